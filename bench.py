@@ -1,0 +1,220 @@
+#!/usr/bin/env python3
+"""Draft-head projection benchmark on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--config 2] [--path auto|valu|mfma]
+
+A step is one draft_project_argmax call (projection + fused argmax + d2t map)
+over one hidden block, with every input already resident in HBM.  The
+default workload is the full-vocabulary draft step: M = 1 hidden row of
+width K = 2,560 against all N = 248,320 rows of a bf16 LM head (synthetic,
+seeded).  Prints ONE JSON line with calls/s, the kernel's achieved
+algorithmic HBM bandwidth against the 8 TB/s MI355X peak, and the fp64
+CPU oracle timed on a bounded sample of the same workload.
+
+Other configs (--config 1, 3, 4, 5) are for exploration; shortlist configs
+rotate through enough W_trim copies to exceed the 256 MB Infinity Cache.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+METRIC = "draft-head calls/sec + achieved HBM GB/s (% of peak), M=1 K=2560 N=248,320"
+PEAK_HBM_GBPS = 8000.0          # MI355X HBM3E, published
+MALL_BYTES = 256 * 2 ** 20      # Infinity Cache
+KERNEL_SOURCE = os.path.join(ROOT, "vocab_shortlisted_lm_amd", "csrc", "lmhead.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def weight_bytes(rows: int, k: int) -> int:
+    """bf16 weight bytes streamed by one projection over `rows` head rows."""
+    return rows * k * 2
+
+
+def algorithmic_bytes(m: int, rows: int, k: int, with_d2t: bool) -> int:
+    """Bytes one call must move at least: every weight row once, the hidden
+    rows once, the d2t entries of the winners and the two outputs."""
+    return weight_bytes(rows, k) + m * k * 2 + (4 * m if with_d2t else 0) + 8 * m
+
+
+def source_digest() -> str:
+    with open(KERNEL_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic(kernel: str, workload: str):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if they
+    were taken on the current kernel source; else None."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            table = json.load(f)
+    except (OSError, ValueError):
+        return None
+    for e in table.get("entries", []):
+        if e.get("kernel") == kernel and e.get("workload") == workload:
+            if e.get("source_sha256_16") != source_digest():
+                return None
+            return e.get("bytes_per_launch")
+    return None
+
+
+def cpu_baseline(h_np, w_np, d2t_np, budget_s: float):
+    """The fp64 oracle timed on host cores over whole calls until `budget_s`."""
+    import oracle
+    from threadpoolctl import threadpool_info
+    threads = max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
+    calls = 0
+    t0 = time.perf_counter()
+    while True:
+        oracle.oracle_project_argmax(h_np, w_np, d2t_np)
+        calls += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s or calls >= 50:
+            break
+    return {"value": calls / el, "unit": "calls/s", "cores": threads, "kind": "oracle",
+            "sample": f"{calls} whole oracle calls (fp64, M={h_np.shape[0]}, {w_np.shape[0]} rows "
+                      f"x K={w_np.shape[1]}) in {el:.1f} s; numpy + BLAS with {threads} threads"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=500)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4, 5])
+    ap.add_argument("--m", type=int, default=None, help="hidden rows (default: the config's first)")
+    ap.add_argument("--full", action="store_true", help="project the full head even for a shortlist config")
+    ap.add_argument("--path", default="auto", choices=["auto", "valu", "mfma"])
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--stream-read", action="store_true",
+                    help="also time the plain streaming-read kernel over W (practical ceiling)")
+    a = ap.parse_args()
+
+    if a.gpus != 1:
+        print(f"bench.py: this build measures one GPU; --gpus {a.gpus} is not supported "
+              "(the projection shards by vocabulary rows with one small all-reduce, "
+              "which is not built here)", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    sys.path.insert(0, ROOT)
+    import synth
+    from vocab_shortlisted_lm_amd import lmhead as L
+
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        return 1
+    L.lib()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    inp = synth.make_config(a.config)
+    c = inp["config"]
+    m = a.m if a.m is not None else c.ms[0]
+    h_np = inp["h"][m] if m in inp["h"] else synth.hidden(c.h_seed[0], 0, m, c.k)
+    w_np = inp["W"]
+    ids = inp["ids"]
+    trimmed = ids is not None and not a.full
+    path = {"auto": L.LMH_PATH_AUTO, "valu": L.LMH_PATH_VALU, "mfma": L.LMH_PATH_MFMA}[a.path]
+    chosen = L.draft_project_auto_path(m, c.k) if path == L.LMH_PATH_AUTO else path
+    kname = {L.LMH_PATH_VALU: "proj_argmax_valu", L.LMH_PATH_MFMA: "proj_argmax_mfma"}[chosen]
+
+    w_full = torch.from_numpy(w_np.view(np.int16)).to(dev)
+    h = torch.from_numpy(h_np.view(np.int16)).to(dev)
+    if trimmed:
+        d2t = torch.from_numpy(ids.astype(np.int32)).to(dev)
+        copies = max(1, -(-2 * MALL_BYTES // weight_bytes(ids.size, c.k)) + 1)
+        heads = [L.lmhead_trim(w_full, d2t) for _ in range(copies)]
+        del w_full
+        rows = ids.size
+        workload = f"{c.name}: M={m} K={c.k} trimmed to {rows} rows ({copies} rotated copies)"
+    else:
+        d2t = None
+        heads = [w_full]
+        rows = c.n
+        workload = (f"full-vocab draft step M={m} K={c.k} N={c.n}" if a.config == 2
+                    else f"{c.name}: M={m} K={c.k} full head N={c.n}")
+    torch.cuda.synchronize()
+
+    ws = L.new_workspace(dev)
+    out_id = torch.empty(m, dtype=torch.int32, device=dev)
+    out_logit = torch.empty(m, dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step(i):
+        L.draft_project_argmax_path(h, heads[i % len(heads)], d2t, path, out_id, out_logit, ws,
+                                    stream)
+
+    for i in range(a.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    wall0 = time.perf_counter()
+    t_start.record(stream)
+    for i in range(a.steps):
+        step(i)
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_total = t_start.elapsed_time(t_end)
+    ms_per_step = ms_total / a.steps
+    calls_per_s = a.steps / (ms_total / 1e3)
+
+    abytes = algorithmic_bytes(m, rows, c.k, d2t is not None)
+    achieved = abytes / (ms_per_step / 1e3) / 1e9
+    traffic = measured_traffic(kname, workload)
+    extra = {}
+    if a.stream_read:
+        sink = torch.zeros(L.lmhead_bench_sink_words(), dtype=torch.int32, device=dev)
+        buf = heads[0]
+        for _ in range(3):
+            L.lmhead_bench_stream_read(buf, sink)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(20):
+            L.lmhead_bench_stream_read(buf, sink)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        nb = buf.numel() * buf.element_size()
+        extra["stream_read_gbps"] = round(nb / (e0.elapsed_time(e1) / 20 / 1e3) / 1e9, 1)
+
+    result = {
+        "metric": METRIC,
+        "value": round(calls_per_s, 2),
+        "unit": "calls/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": round(ms_per_step, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded bf16 W ~ N(0, 0.02), h ~ N(0, 1))",
+        "config": {"workload": workload, "M": m, "K": c.k, "rows": rows,
+                   "kernel": kname, "d2t": d2t is not None, "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS,
+                     "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBPS, 4),
+                     "traffic": traffic, "algorithmic_bytes_per_launch": abytes},
+        "wall_s": round(wall, 3),
+    }
+    result.update(extra)
+    if not a.no_cpu_baseline:
+        hb = h_np
+        wb = w_np[ids] if trimmed else w_np
+        result["cpu_baseline"] = cpu_baseline(hb, wb, ids if trimmed else None, a.cpu_seconds)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

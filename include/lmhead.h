@@ -1,0 +1,169 @@
+/*
+ * lmhead.h -- skinny draft-head vocabulary projection for AMD Instinct MI355X
+ * (gfx950): load-time shortlist row gather, and a fused projection + argmax +
+ * d2t id map for a handful of hidden rows.
+ *
+ * The operation.  A speculative-decoding draft head scores a bf16 hidden
+ * state of width K against every row of the bf16 LM-head weight and proposes
+ * the best-scoring token ("What I was testing", krisbailey.com/articles/
+ * shortlist-mtp: hidden width 2,560, 248,320 head rows, one to three rows per
+ * step).  A shortlisted head scores only the rows of a list of ids, cut from
+ * the full head once at load ("Two ways to run it", zone-1.cobraproject.com
+ * "Masked MTP drafts"); the winning list index goes back to a vocabulary id
+ * through a d2t table, as in EAGLE-3's draft-to-target map (same section).
+ * The argmax is reduced where it is computed instead of gathering logits
+ * ("Re-running the comparison fairly", krisbailey.com).
+ *
+ * Conventions for every call below:
+ *  - bf16 values travel as their raw 16-bit patterns (uint16_t).
+ *  - Every pointer is a DEVICE pointer on the calling thread's current HIP
+ *    device, unless it is documented otherwise.
+ *  - Matrices are row-major and contiguous: element (r, k) of an [R, K]
+ *    matrix is at index r * K + k.
+ *  - `stream` is a hipStream_t passed as void*; NULL means the null stream.
+ *    Work is queued on `stream` and the call returns without waiting, except
+ *    where a call says it synchronizes.
+ *  - The caller owns every buffer.  The library never allocates or frees
+ *    device memory and keeps no device state between calls.
+ *  - Return value: an lmh_status code.  A call that returns LMH_EINVAL,
+ *    LMH_ERANGE or LMH_EWORKSPACE has launched nothing and written nothing.
+ *    LMH_EHIP means a HIP runtime call failed; lmhead_last_error() gives its
+ *    text.  A fault inside a kernel surfaces, as usual in HIP, as an error
+ *    of a later synchronizing call.
+ */
+#ifndef LMHEAD_H
+#define LMHEAD_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  LMH_OK = 0,
+  LMH_EINVAL = 1,      /* bad shape, null or misaligned pointer            */
+  LMH_ERANGE = 2,      /* a shortlist id outside [0, N)                     */
+  LMH_EWORKSPACE = 3,  /* workspace missing, misaligned or too small        */
+  LMH_EHIP = 4         /* a HIP runtime call failed                         */
+} lmh_status;
+
+/* Shape limits.  K must be a multiple of 8 so a row is a whole number of
+ * 16-byte vectors. */
+#define LMH_MAX_M 32
+#define LMH_MIN_K 8
+#define LMH_MAX_K 8192
+#define LMH_MAX_R (1 << 30)
+
+/* Kernel choice for draft_project_argmax_path. */
+#define LMH_PATH_AUTO 0
+#define LMH_PATH_VALU 1  /* hidden rows in registers, packed bf16 dot products */
+#define LMH_PATH_MFMA 2  /* hidden rows in LDS, 16x16x32 bf16 matrix-core tiles */
+
+/*
+ * lmhead_trim -- build the shortlisted head: W_trim[i, :] = W[ids[i], :].
+ *
+ * The head weight is cut once at load from a list of token ids ("Two ways to
+ * run it", zone-1.cobraproject.com "Masked MTP drafts"; the id list file of
+ * "Build the draft vocabulary from your own text", ai-muninn.com).
+ *
+ *  W       [N, K] bf16, 16-byte aligned.
+ *  ids     [S] int32, each in [0, N); order is kept (row i <-> ids[i]);
+ *          duplicates are allowed.  The same array serves as the d2t table
+ *          of draft_project_argmax on W_trim.
+ *  W_trim  [S, K] bf16, 16-byte aligned, written completely (bit copy).
+ *  S = 0 is a no-op.  N >= 1, K as above.
+ *
+ * Synchronizes `stream` once: ids are copied to the host and range-checked
+ * before the gather is queued, so an id outside [0, N) returns LMH_ERANGE
+ * and nothing is read out of bounds.  This is a load-time call.
+ */
+int lmhead_trim(const uint16_t* W, int64_t N, int64_t K,
+                const int32_t* ids, int64_t S,
+                uint16_t* W_trim, void* stream);
+
+/*
+ * draft_project_workspace_bytes -- bytes of workspace draft_project_argmax
+ * needs for M hidden rows (a small constant; 0 if M is out of range).
+ */
+size_t draft_project_workspace_bytes(int64_t M);
+
+/*
+ * draft_project_argmax -- for each hidden row m:
+ *     idx[m]       = the smallest r maximizing  L[m, r] = sum_k h[m, k] * W[r, k]
+ *     out_id[m]    = d2t ? d2t[idx[m]] : idx[m]
+ *     out_logit[m] = L[m, idx[m]]
+ * with bf16 products and fp32 accumulation.  The logit is the raw dot
+ * product (no bias, scale or temperature: greedy drafting).
+ *
+ *  h          [M, K] bf16, 16-byte aligned, 1 <= M <= LMH_MAX_M.
+ *  W          [R, K] bf16, 16-byte aligned: the full head (R = N) or a
+ *             trimmed head from lmhead_trim (R = S).  1 <= R <= 2^30.
+ *  d2t        [R] int32 or NULL.  For a trimmed head pass the ids given to
+ *             lmhead_trim (absolute vocabulary ids); NULL returns row indices.
+ *  out_id     [M] int32.  -1 only if no logit of the row is ordered (NaN).
+ *  out_logit  [M] float.
+ *  workspace  at least draft_project_workspace_bytes(M) bytes, 16-byte
+ *             aligned, ZERO-FILLED by the caller before its first use.  Each
+ *             call leaves it zero-filled again when it completes, so one
+ *             workspace serves any number of calls that are ordered on one
+ *             stream.  Calls that may run concurrently need separate
+ *             workspaces.  After a device fault, zero it again.
+ *
+ * Never synchronizes and never allocates; one kernel launch in the common
+ * case (M * K <= 64 Ki for the matrix-core path; larger M * K splits the
+ * hidden rows over several launches).  Inputs with NaN or Inf give an
+ * unspecified (but in-bounds) result.
+ */
+int draft_project_argmax(const uint16_t* h, int64_t M, int64_t K,
+                         const uint16_t* W, int64_t R,
+                         const int32_t* d2t,
+                         int32_t* out_id, float* out_logit,
+                         void* workspace, size_t workspace_bytes,
+                         void* stream);
+
+/*
+ * draft_project_argmax_path -- draft_project_argmax with the kernel chosen
+ * by the caller (LMH_PATH_*), for tests and measurement.  LMH_PATH_VALU
+ * accepts M <= 4 with M * ceil(K / 512) <= 20; LMH_PATH_MFMA accepts every
+ * shape draft_project_argmax accepts.  Other shapes give LMH_EINVAL.
+ */
+int draft_project_argmax_path(const uint16_t* h, int64_t M, int64_t K,
+                              const uint16_t* W, int64_t R,
+                              const int32_t* d2t,
+                              int32_t* out_id, float* out_logit,
+                              void* workspace, size_t workspace_bytes,
+                              int path, void* stream);
+
+/* Which kernel draft_project_argmax picks for (M, K): an LMH_PATH_* value,
+ * or -1 if the shape is not accepted. */
+int draft_project_auto_path(int64_t M, int64_t K);
+
+/* Static text for a status code. */
+const char* lmhead_status_str(int status);
+
+/* Text of the last HIP error seen by this thread (empty if none). */
+const char* lmhead_last_error(void);
+
+/*
+ * Measurement support (not part of the projection): plain streaming kernels
+ * used to find the practical HBM ceiling and to scale hardware counters.
+ *
+ * lmhead_bench_stream_read: reads `bytes` (a multiple of 16, 16-byte aligned
+ *   `src`) with 16-byte loads and writes one 32-bit checksum word per
+ *   workgroup into `sink` (at least lmhead_bench_sink_words() words).
+ * lmhead_bench_copy: dst[0:bytes] = src[0:bytes] (16-byte multiples/aligned).
+ * `grid` = workgroups to launch (0 = the library's default).
+ */
+int lmhead_bench_sink_words(void);
+int lmhead_bench_stream_read(const void* src, size_t bytes, uint32_t* sink,
+                             int grid, void* stream);
+int lmhead_bench_copy(const void* src, void* dst, size_t bytes, int grid,
+                      void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LMHEAD_H */

@@ -1,0 +1,118 @@
+"""The C-ABI library loads, exports every symbol include/lmhead.h declares,
+and rejects bad arguments on the host before touching the GPU (CPU only:
+every call here returns before the first HIP runtime call)."""
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "lmhead.h")
+
+
+@pytest.fixture(scope="module")
+def L():
+    from vocab_shortlisted_lm_amd import lmhead, build
+    src = build.SRC
+    if (not os.path.exists(lmhead.LIB_PATH)
+            or os.path.getmtime(lmhead.LIB_PATH) < max(os.path.getmtime(src), os.path.getmtime(HEADER))):
+        build.build()
+    return lmhead
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[\w]+\s*\*?\s*(\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for n in ("lmhead_trim", "draft_project_argmax", "draft_project_workspace_bytes",
+              "lmhead_status_str"):
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported(L):
+    lib = L.lib()
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    out = subprocess.run(["nm", "-D", "--defined-only", L.LIB_PATH], capture_output=True,
+                         text=True).stdout
+    exported = set(re.findall(r" T (\w+)$", out, flags=re.M))
+    assert set(declared_functions()) <= exported
+    assert set(L.SIGNATURES) == set(declared_functions())
+
+
+def test_library_targets_gfx950_only(L):
+    data = open(L.LIB_PATH, "rb").read()
+    targets = set(re.findall(rb"amdgcn-amd-amdhsa-[-\w:+]*", data))
+    assert targets == {b"amdgcn-amd-amdhsa--gfx950"}, targets
+
+
+def test_status_strings(L):
+    for c in range(5):
+        assert L.lmhead_status_str(c)
+    assert "range" in L.lmhead_status_str(L.LMH_ERANGE)
+    assert L.lmhead_status_str(99) == "unknown status"
+
+
+def test_workspace_bytes(L):
+    assert L.draft_project_workspace_bytes(0) == 0
+    assert L.draft_project_workspace_bytes(33) == 0
+    for m in (1, 3, 24, 32):
+        ws = L.draft_project_workspace_bytes(m)
+        assert ws >= 8 * m + 4 and ws % 16 == 0
+
+
+def test_auto_path(L):
+    assert L.draft_project_auto_path(1, 2560) == L.LMH_PATH_VALU
+    assert L.draft_project_auto_path(4, 2560) == L.LMH_PATH_VALU
+    assert L.draft_project_auto_path(3, 2560) == L.LMH_PATH_VALU
+    assert L.draft_project_auto_path(5, 2560) == L.LMH_PATH_MFMA
+    assert L.draft_project_auto_path(24, 2560) == L.LMH_PATH_MFMA
+    assert L.draft_project_auto_path(4, 8192) == L.LMH_PATH_MFMA
+    assert L.draft_project_auto_path(1, 8192) == L.LMH_PATH_VALU
+    for m, k in ((0, 2560), (33, 2560), (1, 12), (1, 0), (1, 8200)):
+        assert L.draft_project_auto_path(m, k) == -1
+
+
+# fake, aligned addresses: validation must reject before any device access
+A, B, C, D, E = 0x10000, 0x20000, 0x30000, 0x40000, 0x50000
+
+
+def call(L, h=A, m=1, k=2560, w=B, r=100, d2t=None, oid=C, olog=D, ws=E, wsb=512, path=0):
+    return L.lib().draft_project_argmax_path(h, m, k, w, r, d2t, oid, olog, ws, wsb, path, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(h=None), 1), (dict(w=None), 1), (dict(oid=None), 1), (dict(olog=None), 1),
+    (dict(m=0), 1), (dict(m=33), 1), (dict(k=0), 1), (dict(k=12), 1), (dict(k=8200), 1),
+    (dict(r=0), 1), (dict(r=(1 << 30) + 1), 1), (dict(h=A + 2), 1), (dict(w=B + 8), 1),
+    (dict(path=7), 1), (dict(m=5, path=1), 1), (dict(m=4, k=4096, path=1), 1),
+    (dict(ws=None), 3), (dict(ws=E + 4), 3), (dict(wsb=16), 3), (dict(wsb=0), 3),
+])
+def test_project_rejects_on_host(L, kw, code):
+    assert call(L, **kw) == code
+
+
+def test_trim_rejects_on_host(L):
+    lib = L.lib()
+    assert lib.lmhead_trim(A, 100, 2560, B, 0, C, None) == 0          # S = 0: no-op
+    assert lib.lmhead_trim(A, 100, 2560, B, -1, C, None) == 1
+    assert lib.lmhead_trim(A, 0, 2560, B, 4, C, None) == 1
+    assert lib.lmhead_trim(A, 100, 12, B, 4, C, None) == 1
+    assert lib.lmhead_trim(None, 100, 2560, B, 4, C, None) == 1
+    assert lib.lmhead_trim(A, 100, 2560, None, 4, C, None) == 1
+    assert lib.lmhead_trim(A, 100, 2560, B, 4, None, None) == 1
+    assert lib.lmhead_trim(A + 2, 100, 2560, B, 4, C, None) == 1
+    assert lib.lmhead_trim(A, 100, 2560, B, 4, C + 8, None) == 1
+
+
+def test_bench_kernels_reject_on_host(L):
+    lib = L.lib()
+    assert lib.lmhead_bench_stream_read(A, 1000, B, 0, None) == 1     # not a multiple of 16
+    assert lib.lmhead_bench_stream_read(None, 1024, B, 0, None) == 1
+    assert lib.lmhead_bench_copy(A, B + 4, 1024, 0, None) == 1
+    assert lib.lmhead_bench_sink_words() >= 4096

@@ -1,0 +1,67 @@
+"""Build liblmhead.so (HIP, gfx950) in-tree with hipcc.
+
+    python -m vocab_shortlisted_lm_amd.build [-D NAME=VALUE ...] [-o PATH]
+
+The library is one translation unit, csrc/lmhead.hip, compiled for gfx950
+only.  Packed-fp32 instruction selection is switched off on the device pass
+(`-target-feature -packed-fp32-ops`); the host pass prints a harmless warning
+that it does not know that feature.
+"""
+from __future__ import annotations
+
+import argparse
+import os
+import shutil
+import subprocess
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+SRC = os.path.join(PKG, "csrc", "lmhead.hip")
+INCLUDE = os.path.join(ROOT, "include")
+LIB = os.path.join(PKG, "liblmhead.so")
+ARCH = "gfx950"
+
+
+def hipcc() -> str:
+    for cand in (os.environ.get("HIPCC"), shutil.which("hipcc"), "/opt/rocm/bin/hipcc"):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError("hipcc not found (ROCm is required to build the HIP library)")
+
+
+def command(out: str = LIB, defines: list[str] | None = None) -> list[str]:
+    cmd = [hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-shared", "-fPIC",
+           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+           "-Wall", "-Wno-unused-function", "-I", INCLUDE]
+    for d in defines or []:
+        cmd.append("-D" + d)
+    cmd += [SRC, "-o", out]
+    return cmd
+
+
+def build(out: str = LIB, defines: list[str] | None = None, verbose: bool = False) -> str:
+    """Compile the library; returns its path.  Raises on a compiler error."""
+    tmp = out + ".tmp"
+    cmd = command(tmp, defines)
+    proc = subprocess.run(cmd, capture_output=True, text=True)
+    noise = "is not a recognized feature for this target"
+    err = "\n".join(l for l in proc.stderr.splitlines() if noise not in l)
+    if proc.returncode != 0:
+        raise RuntimeError("hipcc failed:\n" + " ".join(cmd) + "\n" + err)
+    if verbose and err.strip():
+        print(err, file=sys.stderr)
+    os.replace(tmp, out)
+    return out
+
+
+def main() -> None:
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("-D", dest="defines", action="append", default=[])
+    ap.add_argument("-o", dest="out", default=LIB)
+    a = ap.parse_args()
+    print(build(a.out, a.defines, verbose=True))
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,748 @@
+// lmhead.hip -- draft-head projection kernels for MI355X (gfx950) and the
+// C ABI declared in include/lmhead.h.
+//
+// What runs on the device:
+//   gather_rows         load-time shortlist gather, W_trim[i] = W[ids[i]]
+//                       ("Two ways to run it", zone-1.cobraproject.com
+//                       "Masked MTP drafts": the head is trimmed at load).
+//   proj_argmax_valu    M <= 4 hidden rows held in registers; one wave per
+//                       head row, 16-byte buffer loads, packed bf16 dot
+//                       products with fp32 accumulation, DPP row reduction.
+//   proj_argmax_mfma    hidden rows staged in LDS; 16 (or 32) head rows per
+//                       wave tile on 16x16x32 bf16 matrix-core instructions,
+//                       so no cross-lane reduction per row is needed.
+// Both projection kernels fuse the argmax: each wave keeps a running
+// (logit, row) per hidden row, a workgroup folds its waves through LDS, and
+// one 64-bit atomicMax per hidden row per workgroup folds workgroups.  The
+// last workgroup to finish (ticket counter) decodes the winner, maps it
+// through d2t (EAGLE-3 style draft-to-target ids, "Two ways to run it") and
+// re-zeroes the workspace, so a call is a single launch with no memset.
+// The argmax is reduced locally instead of gathering logits, the change the
+// fair re-run on krisbailey.com/articles/shortlist-mtp credits ("Re-running
+// the comparison fairly").
+//
+// The projection is HBM-bound: at M = 1 each head row (5,120 bytes at
+// K = 2,560) is used for 2,560 multiply-adds.  The kernels therefore stream
+// W exactly once with 16-byte non-temporal loads and keep everything else on
+// chip; logits never reach HBM.
+
+#include <hip/hip_runtime.h>
+
+#include <stdint.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <algorithm>
+#include <utility>
+#include <vector>
+
+#include "lmhead.h"
+
+namespace {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+// ---------------------------------------------------------------------------
+// tunables (compile-time)
+// ---------------------------------------------------------------------------
+#ifndef LMH_VALU_ROWS
+#define LMH_VALU_ROWS 2          // head rows per wave per step (VALU path)
+#endif
+#ifndef LMH_VALU_WG_PER_CU
+#define LMH_VALU_WG_PER_CU 8     // cap on resident workgroups per CU (VALU path)
+#endif
+#ifndef LMH_MFMA_WAVES
+#define LMH_MFMA_WAVES 8         // waves per workgroup (matrix-core path)
+#endif
+#ifndef LMH_MFMA_TM
+#define LMH_MFMA_TM 2            // 16-row tiles per wave step (matrix-core path)
+#endif
+#ifndef LMH_MFMA_SB
+#define LMH_MFMA_SB 8            // k-steps of loads issued together
+#endif
+#ifndef LMH_NT_LOADS
+#define LMH_NT_LOADS 1           // non-temporal W loads
+#endif
+
+constexpr int kValuWaves = 4;
+constexpr int kValuThreads = 64 * kValuWaves;
+constexpr int kMfmaThreads = 64 * LMH_MFMA_WAVES;
+// LDS for staged hidden rows in the matrix-core path.  At most one
+// workgroup of that path per CU when it is full; the rest of the 160 KiB is
+// left for the key exchange.
+constexpr int kMfmaLdsBudget = 152 * 1024;
+constexpr int kValuMaxChunksTimesM = 20;   // register budget: 80 VGPRs of h
+constexpr int kWorkspaceBytes = 512;       // 32 keys + ticket counter, padded
+constexpr int64_t kMaxRows = (int64_t)1 << 30;  // keeps row arithmetic in int range
+constexpr uint32_t kBufferWord3 = 0x00020000u;  // gfx9 raw buffer, 32-bit data
+constexpr uint32_t kOobOffset = 0x80000000u;    // any offset >= num_records reads 0
+constexpr int kCachePolicy = LMH_NT_LOADS ? 2 : 0;  // bit 1 = nt
+
+// ---------------------------------------------------------------------------
+// device helpers
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           (int)kBufferWord3);
+}
+
+__device__ __forceinline__ u32x4 load16(__amdgpu_buffer_rsrc_t r, uint32_t voff) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, 0, kCachePolicy);
+}
+
+// acc += sum of the eight bf16 products of one 16-byte chunk (fp32 adds).
+// The pairs are taken with shufflevector from a whole-vector cast: a
+// bit_cast of a single vector component (w.y) is read as component 0 by
+// this compiler.
+__device__ __forceinline__ float dot8(u32x4 w, u32x4 h, float acc) {
+  const bf16x8 a = __builtin_bit_cast(bf16x8, w);
+  const bf16x8 b = __builtin_bit_cast(bf16x8, h);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(a, a, 0, 1),
+                                        __builtin_shufflevector(b, b, 0, 1), acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(a, a, 2, 3),
+                                        __builtin_shufflevector(b, b, 2, 3), acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(a, a, 4, 5),
+                                        __builtin_shufflevector(b, b, 4, 5), acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(a, a, 6, 7),
+                                        __builtin_shufflevector(b, b, 6, 7), acc, false);
+  return acc;
+}
+
+// Wave index inside the workgroup, as a value the compiler knows is uniform
+// (so row bases and buffer descriptors live in scalar registers).
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)); }
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+
+// Sum over the 64 lanes; every lane gets the same result, and the order of
+// additions is fixed, so a row's logit is the same on every call.
+__device__ __forceinline__ float wave_sum(float v) {
+  v += dpp<0xB1>(v);   // quad_perm [1,0,3,2]
+  v += dpp<0x4E>(v);   // quad_perm [2,3,0,1]
+  v += dpp<0x124>(v);  // row_ror:4
+  v += dpp<0x128>(v);  // row_ror:8  -> every lane holds its 16-lane row sum
+  const float a = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 0));
+  const float b = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 16));
+  const float c = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 32));
+  const float d = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 48));
+  return (a + b) + (c + d);
+}
+
+// Running argmax: keep the first row with the largest ordered logit.  A row
+// replaces the best one if it is strictly larger, or if nothing ordered has
+// been seen yet.  Rows reach a lane in increasing order, so this keeps the
+// smallest index among equal logits.
+__device__ __forceinline__ void take_best(float s, int r, float& best, int& bidx) {
+  const bool better = (bidx < 0) ? (s == s) : (s > best);
+  best = better ? s : best;
+  bidx = better ? r : bidx;
+}
+
+// 64-bit key whose unsigned order is (logit ascending, then row descending):
+// the maximum key is the largest logit at its smallest row.  Key 0 is below
+// every real key and means "nothing".
+__device__ __forceinline__ unsigned long long pack_key(float v, int idx) {
+  if (idx < 0) return 0ull;
+  uint32_t b = __builtin_bit_cast(uint32_t, v);
+  if (v == 0.0f) b = 0u;                                  // -0 == +0
+  const uint32_t ord = (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+  return ((unsigned long long)ord << 32) | (unsigned long long)(0xFFFFFFFFu - (uint32_t)idx);
+}
+
+__device__ __forceinline__ void unpack_key(unsigned long long k, float& v, int& idx) {
+  const uint32_t ord = (uint32_t)(k >> 32);
+  const uint32_t b = (ord & 0x80000000u) ? (ord & 0x7FFFFFFFu) : ~ord;
+  v = __builtin_bit_cast(float, b);
+  idx = (int)(0xFFFFFFFFu - (uint32_t)k);
+}
+
+// Workgroup epilogue, run by wave 0 only.  `wg_key[m]` is this workgroup's
+// best key for hidden row m (in LDS).  Folds it into the workspace, takes a
+// ticket, and if this is the last workgroup, writes the results and clears
+// the workspace for the next call on the stream.
+__device__ __forceinline__ void finish_workgroup(unsigned long long key, int lane, int mcount,
+                                                 int m_base, const int32_t* __restrict__ d2t,
+                                                 int32_t* __restrict__ out_id,
+                                                 float* __restrict__ out_logit,
+                                                 unsigned long long* __restrict__ keys,
+                                                 unsigned int* __restrict__ counter) {
+  if (lane < mcount && key != 0ull) atomicMax(&keys[m_base + lane], key);
+  __threadfence();  // release: the key updates are visible before the ticket
+  unsigned int ticket = 0;
+  if (lane == 0) ticket = atomicAdd(counter, 1u);
+  ticket = (unsigned int)__builtin_amdgcn_readfirstlane((int)ticket);
+  if (ticket != gridDim.x - 1) return;
+  __threadfence();  // acquire: every workgroup's key update is visible
+  if (lane < mcount) {
+    const unsigned long long k = atomicExch(&keys[m_base + lane], 0ull);
+    float v;
+    int idx;
+    unpack_key(k, v, idx);
+    if (k == 0ull) {
+      out_id[m_base + lane] = -1;
+      out_logit[m_base + lane] = __builtin_nanf("");
+    } else {
+      out_id[m_base + lane] = d2t ? d2t[idx] : idx;
+      out_logit[m_base + lane] = v;
+    }
+  }
+  if (lane == 0) atomicExch(counter, 0u);
+}
+
+// ---------------------------------------------------------------------------
+// gather: W_trim[i, :] = W[ids[i], :]
+// ---------------------------------------------------------------------------
+__global__ void __launch_bounds__(256)
+gather_rows(const uint16_t* __restrict__ W, int64_t N, int K, const int32_t* __restrict__ ids,
+            int64_t S, uint16_t* __restrict__ out) {
+  const int lane = threadIdx.x & 63;
+  const int64_t wave = (int64_t)blockIdx.x * 4 + wave_id();
+  const int64_t nwave = (int64_t)gridDim.x * 4;
+  const int chunks = K >> 3;
+  for (int64_t i = wave; i < S; i += nwave) {
+    const int32_t id = ids[i];
+    if (id < 0 || (int64_t)id >= N) continue;  // checked on the host too
+    const u32x4* src = reinterpret_cast<const u32x4*>(W + (int64_t)id * K);
+    u32x4* dst = reinterpret_cast<u32x4*>(out + i * K);
+    for (int c = lane; c < chunks; c += 64) {
+      __builtin_nontemporal_store(__builtin_nontemporal_load(src + c), dst + c);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// VALU path: one wave per head row, hidden rows in registers
+// ---------------------------------------------------------------------------
+// Lane `l` owns the 16-byte chunks c = l + 64 j (j < CPL) of every row, so
+// one load instruction moves 1 KiB of a row, fully coalesced.  Chunks past
+// the row end get an out-of-range buffer offset and read as zero.
+template <int M, int CPL, int U>
+__global__ void __launch_bounds__(kValuThreads)
+proj_argmax_valu(const uint16_t* __restrict__ h, const uint16_t* __restrict__ W, int R, int K,
+                 const int32_t* __restrict__ d2t, int32_t* __restrict__ out_id,
+                 float* __restrict__ out_logit, unsigned long long* __restrict__ keys,
+                 unsigned int* __restrict__ counter) {
+  __shared__ unsigned long long s_key[kValuWaves][M];
+  const int lane = threadIdx.x & 63;
+  const int wave = wave_id();
+  const int chunks = K >> 3;
+  const uint32_t row_bytes = (uint32_t)K * 2u;
+
+  uint32_t voff[CPL];
+  u32x4 hf[M][CPL];
+#pragma unroll
+  for (int j = 0; j < CPL; ++j) {
+    const int c = lane + 64 * j;
+    voff[j] = c < chunks ? (uint32_t)c * 16u : kOobOffset;
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+      hf[m][j] = c < chunks ? *reinterpret_cast<const u32x4*>(h + (size_t)m * K + (size_t)c * 8)
+                            : u32x4{0u, 0u, 0u, 0u};
+    }
+  }
+
+  float best[M];
+  int bidx[M];
+#pragma unroll
+  for (int m = 0; m < M; ++m) {
+    best[m] = 0.0f;
+    bidx[m] = -1;
+  }
+
+  const int step = gridDim.x * kValuWaves * U;
+  u32x4 wa[U][CPL], wb[U][CPL];
+
+  auto load_rows = [&](u32x4 (&w)[U][CPL], int r0) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int r = r0 + u;
+      const __amdgpu_buffer_rsrc_t rs =
+          make_rsrc(W + (size_t)(r < R ? r : 0) * (size_t)K, r < R ? row_bytes : 0u);
+#pragma unroll
+      for (int j = 0; j < CPL; ++j) w[u][j] = load16(rs, voff[j]);
+    }
+  };
+  auto score_rows = [&](const u32x4 (&w)[U][CPL], int r0) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+#pragma unroll
+      for (int m = 0; m < M; ++m) {
+        float acc = 0.0f;
+#pragma unroll
+        for (int j = 0; j < CPL; ++j) acc = dot8(w[u][j], hf[m][j], acc);
+        const float s = wave_sum(acc);
+        if (r0 + u < R) take_best(s, r0 + u, best[m], bidx[m]);
+      }
+    }
+  };
+
+  // Two register buffers: the next rows are in flight while these are scored.
+  int r0 = (blockIdx.x * kValuWaves + wave) * U;
+  if (r0 < R) load_rows(wa, r0);
+  while (r0 < R) {
+    const int r1 = r0 + step;
+    if (r1 < R) load_rows(wb, r1);
+    score_rows(wa, r0);
+    if (r1 >= R) break;
+    const int r2 = r1 + step;
+    if (r2 < R) load_rows(wa, r2);
+    score_rows(wb, r1);
+    r0 = r2;
+  }
+
+  if (lane == 0) {
+#pragma unroll
+    for (int m = 0; m < M; ++m) s_key[wave][m] = pack_key(best[m], bidx[m]);
+  }
+  __syncthreads();
+  if (wave != 0) return;
+  unsigned long long key = 0ull;
+  if (lane < M) {
+#pragma unroll
+    for (int w = 0; w < kValuWaves; ++w) key = s_key[w][lane] > key ? s_key[w][lane] : key;
+  }
+  finish_workgroup(key, lane, M, 0, d2t, out_id, out_logit, keys, counter);
+}
+
+// ---------------------------------------------------------------------------
+// matrix-core path: hidden rows in LDS, 16x16x32 bf16 MFMA tiles
+// ---------------------------------------------------------------------------
+// v_mfma_f32_16x16x32_bf16 computes D[i][j] += sum_k A[i][k] B[k][j] with
+// lane l supplying A[l%16][8(l/16) .. +8] and B[8(l/16) .. +8][l%16], and
+// holding D[4(l/16) + v][l%16], v < 4.  The k order inside a dot product is
+// free, so k-slot group g = l/16 of step s is mapped to the 16-byte chunk
+// 4s + g of the row: the four lanes of one head row read 64 contiguous
+// bytes per instruction.  A = 16 head rows, B = 16 hidden rows (columns past
+// the last hidden row repeat it and are ignored), D = their logits, summed
+// over k inside the matrix core.
+template <int NT, int TM>
+__global__ void __launch_bounds__(kMfmaThreads)
+proj_argmax_mfma(const uint16_t* __restrict__ h, const uint16_t* __restrict__ W, int R, int K,
+                 int m_base, int mp, const int32_t* __restrict__ d2t,
+                 int32_t* __restrict__ out_id, float* __restrict__ out_logit,
+                 unsigned long long* __restrict__ keys, unsigned int* __restrict__ counter) {
+  extern __shared__ u32x4 h_lds[];  // [mp][row_chunks], zero past K
+  __shared__ unsigned long long s_key[LMH_MFMA_WAVES][32];
+  const int lane = threadIdx.x & 63;
+  const int wave = wave_id();
+  const int i16 = lane & 15;
+  const int g = lane >> 4;
+  const int chunks = K >> 3;
+  const int steps = (K + 31) >> 5;
+  const int s4 = steps * 4;
+  const int row_chunks = s4 + 1;  // one chunk of padding per row spreads LDS banks
+
+  for (int i = threadIdx.x; i < mp * s4; i += kMfmaThreads) {
+    const int m = i / s4;
+    const int c = i - m * s4;
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (c < chunks) v = *reinterpret_cast<const u32x4*>(h + (size_t)(m_base + m) * K + (size_t)c * 8);
+    h_lds[m * row_chunks + c] = v;
+  }
+  __syncthreads();
+
+  const u32x4* bptr[NT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    const int col = nt * 16 + i16;
+    bptr[nt] = h_lds + (col < mp ? col : mp - 1) * row_chunks + g;
+  }
+
+  float best[NT];
+  int bidx[NT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    best[nt] = 0.0f;
+    bidx[nt] = -1;
+  }
+
+  const uint32_t row_bytes = (uint32_t)K * 2u;
+  const int tile_rows = 16 * TM;
+  const int ntiles = (R + tile_rows - 1) / tile_rows;
+  for (int tile = blockIdx.x * LMH_MFMA_WAVES + wave; tile < ntiles;
+       tile += gridDim.x * LMH_MFMA_WAVES) {
+    const int r0 = tile * tile_rows;
+    const int live = min(tile_rows, R - r0);
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(W + (size_t)r0 * K, (uint32_t)live * row_bytes);
+    uint32_t vrow[TM];
+#pragma unroll
+    for (int t = 0; t < TM; ++t) vrow[t] = (uint32_t)(t * 16 + i16) * row_bytes + (uint32_t)g * 16u;
+
+    f32x4 acc[TM][NT];
+#pragma unroll
+    for (int t = 0; t < TM; ++t)
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) acc[t][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    for (int s0 = 0; s0 < steps; s0 += LMH_MFMA_SB) {
+      u32x4 a[LMH_MFMA_SB][TM];
+#pragma unroll
+      for (int sb = 0; sb < LMH_MFMA_SB; ++sb) {
+        const int s = s0 + sb;
+        const bool ok = s < steps && (s * 4 + g) < chunks;
+#pragma unroll
+        for (int t = 0; t < TM; ++t) a[sb][t] = load16(rs, ok ? vrow[t] + (uint32_t)s * 64u : kOobOffset);
+      }
+#pragma unroll
+      for (int sb = 0; sb < LMH_MFMA_SB; ++sb) {
+        const int s = s0 + sb;
+        if (s < steps) {
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt) {
+            const u32x4 b = bptr[nt][s * 4];
+#pragma unroll
+            for (int t = 0; t < TM; ++t)
+              acc[t][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                  __builtin_bit_cast(bf16x8, a[sb][t]), __builtin_bit_cast(bf16x8, b), acc[t][nt], 0,
+                  0, 0);
+          }
+        }
+      }
+    }
+
+#pragma unroll
+    for (int t = 0; t < TM; ++t)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int r = r0 + t * 16 + 4 * g + v;
+        if (r < R) {
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt) take_best(acc[t][nt][v], r, best[nt], bidx[nt]);
+        }
+      }
+  }
+
+  // fold the four lanes (g = 0..3) that hold the same hidden row
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    unsigned long long k = pack_key(best[nt], bidx[nt]);
+#pragma unroll
+    for (int x = 16; x <= 32; x <<= 1) {
+      const uint32_t lo = (uint32_t)__shfl_xor((int)(uint32_t)k, x);
+      const uint32_t hi = (uint32_t)__shfl_xor((int)(uint32_t)(k >> 32), x);
+      const unsigned long long o = ((unsigned long long)hi << 32) | lo;
+      k = o > k ? o : k;
+    }
+    const int col = nt * 16 + i16;
+    if (g == 0 && col < 32) s_key[wave][col] = k;
+  }
+  __syncthreads();
+  if (wave != 0) return;
+  unsigned long long key = 0ull;
+  if (lane < mp) {
+#pragma unroll
+    for (int w = 0; w < LMH_MFMA_WAVES; ++w) key = s_key[w][lane] > key ? s_key[w][lane] : key;
+  }
+  finish_workgroup(key, lane, mp, m_base, d2t, out_id, out_logit, keys, counter);
+}
+
+// ---------------------------------------------------------------------------
+// measurement kernels
+// ---------------------------------------------------------------------------
+constexpr int kBenchThreads = 256;
+constexpr int kBenchSinkWords = 65536;
+
+__global__ void __launch_bounds__(kBenchThreads)
+stream_read(const u32x4* __restrict__ src, size_t n16, uint32_t* __restrict__ sink) {
+  uint32_t x = 0;
+  const size_t stride = (size_t)gridDim.x * kBenchThreads;
+  size_t i = (size_t)blockIdx.x * kBenchThreads + threadIdx.x;
+  for (; i + 3 * stride < n16; i += 4 * stride) {
+    const u32x4 a = __builtin_nontemporal_load(src + i);
+    const u32x4 b = __builtin_nontemporal_load(src + i + stride);
+    const u32x4 c = __builtin_nontemporal_load(src + i + 2 * stride);
+    const u32x4 d = __builtin_nontemporal_load(src + i + 3 * stride);
+    x ^= a.x ^ a.y ^ a.z ^ a.w ^ b.x ^ b.y ^ b.z ^ b.w ^ c.x ^ c.y ^ c.z ^ c.w ^ d.x ^ d.y ^ d.z ^ d.w;
+  }
+  for (; i < n16; i += stride) {
+    const u32x4 a = __builtin_nontemporal_load(src + i);
+    x ^= a.x ^ a.y ^ a.z ^ a.w;
+  }
+  // one word per workgroup (xor of its lanes through LDS-free DPP-less path)
+  __shared__ uint32_t s[kBenchThreads];
+  s[threadIdx.x] = x;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t y = 0;
+    for (int t = 0; t < kBenchThreads; ++t) y ^= s[t];
+    sink[blockIdx.x] = y;
+  }
+}
+
+__global__ void __launch_bounds__(kBenchThreads)
+copy16(const u32x4* __restrict__ src, u32x4* __restrict__ dst, size_t n16) {
+  const size_t stride = (size_t)gridDim.x * kBenchThreads;
+  for (size_t i = (size_t)blockIdx.x * kBenchThreads + threadIdx.x; i < n16; i += stride)
+    __builtin_nontemporal_store(__builtin_nontemporal_load(src + i), dst + i);
+}
+
+// ---------------------------------------------------------------------------
+// host side
+// ---------------------------------------------------------------------------
+thread_local char g_last_error[256] = "";
+
+int hip_fail(hipError_t e, const char* what) {
+  snprintf(g_last_error, sizeof g_last_error, "%s: %s", what, hipGetErrorString(e));
+  return LMH_EHIP;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool k_ok(int64_t K) { return K >= LMH_MIN_K && K <= LMH_MAX_K && (K % 8) == 0; }
+
+int cu_count(int* out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  e = hipDeviceGetAttribute(out, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return hip_fail(e, "hipDeviceGetAttribute");
+  if (*out < 1) *out = 1;
+  return LMH_OK;
+}
+
+// Workgroups of kernel `f` that can be resident on one CU at once.  The
+// projection kernels are persistent (each workgroup strides over rows), so
+// the grid is sized to what is resident: a second, partial round of
+// workgroups would double the tail.
+int resident_per_cu(const void* f, int threads, size_t lds, int* out) {
+  int n = 0;
+  const hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, f, threads, lds);
+  if (e != hipSuccess) return hip_fail(e, "hipOccupancyMaxActiveBlocksPerMultiprocessor");
+  *out = n < 1 ? 1 : n;
+  return LMH_OK;
+}
+
+int chunks_per_lane(int64_t K) { return (int)((K / 8 + 63) / 64); }
+
+bool valu_ok(int64_t M, int64_t K) {
+  return M >= 1 && M <= 4 && k_ok(K) && M * chunks_per_lane(K) <= kValuMaxChunksTimesM;
+}
+
+int mfma_row_bytes(int64_t K) { return (int)((((K + 31) / 32) * 4 + 1) * 16); }
+
+// hidden rows per launch of the matrix-core path
+int mfma_rows_per_pass(int64_t K) {
+  return std::min<int64_t>(LMH_MAX_M, kMfmaLdsBudget / mfma_row_bytes(K));
+}
+
+typedef void (*valu_fn)(const uint16_t*, const uint16_t*, int, int, const int32_t*, int32_t*, float*,
+                        unsigned long long*, unsigned int*);
+
+template <int M, int CPL>
+valu_fn valu_entry() {
+  if constexpr (M * CPL <= kValuMaxChunksTimesM) {
+    // rows per step: keep each of the two row buffers at <= 10 chunks/lane
+    constexpr int U = CPL * LMH_VALU_ROWS <= 10 ? LMH_VALU_ROWS : (CPL <= 10 ? 10 / CPL : 1);
+    return proj_argmax_valu<M, CPL, (U < 1 ? 1 : U)>;
+  } else {
+    return nullptr;
+  }
+}
+
+template <int M, int... C>
+valu_fn valu_pick_cpl(int cpl, std::integer_sequence<int, C...>) {
+  valu_fn f = nullptr;
+  ((cpl == C + 1 ? (f = valu_entry<M, C + 1>(), 0) : 0), ...);
+  return f;
+}
+
+valu_fn valu_kernel(int M, int cpl) {
+  using seq = std::make_integer_sequence<int, 16>;
+  switch (M) {
+    case 1: return valu_pick_cpl<1>(cpl, seq{});
+    case 2: return valu_pick_cpl<2>(cpl, seq{});
+    case 3: return valu_pick_cpl<3>(cpl, seq{});
+    case 4: return valu_pick_cpl<4>(cpl, seq{});
+    default: return nullptr;
+  }
+}
+
+int launch_valu(const uint16_t* h, int M, int K, const uint16_t* W, int R, const int32_t* d2t,
+                int32_t* out_id, float* out_logit, unsigned long long* keys, unsigned int* counter,
+                hipStream_t stream) {
+  valu_fn f = valu_kernel(M, chunks_per_lane(K));
+  if (!f) return LMH_EINVAL;
+  int cus = 0;
+  int st = cu_count(&cus);
+  if (st != LMH_OK) return st;
+  int per_cu = 0;
+  st = resident_per_cu((const void*)f, kValuThreads, 0, &per_cu);
+  if (st != LMH_OK) return st;
+  const int64_t rows_per_wg = (int64_t)kValuWaves * LMH_VALU_ROWS;
+  const int64_t need = (R + rows_per_wg - 1) / rows_per_wg;
+  const int grid = (int)std::max<int64_t>(
+      1, std::min<int64_t>(need, (int64_t)cus * std::min(per_cu, LMH_VALU_WG_PER_CU)));
+  hipLaunchKernelGGL(f, dim3(grid), dim3(kValuThreads), 0, stream, h, W, R, K, d2t, out_id, out_logit,
+                     keys, counter);
+  const hipError_t e = hipGetLastError();
+  return e == hipSuccess ? LMH_OK : hip_fail(e, "launch proj_argmax_valu");
+}
+
+template <int NT>
+int launch_mfma_nt(const uint16_t* h, int K, int m_base, int mp, const uint16_t* W, int R,
+                   const int32_t* d2t, int32_t* out_id, float* out_logit, unsigned long long* keys,
+                   unsigned int* counter, int cus, hipStream_t stream) {
+  auto f = proj_argmax_mfma<NT, LMH_MFMA_TM>;
+  const size_t lds = (size_t)mp * mfma_row_bytes(K);
+  static bool attr_done = false;  // one-time kernel attribute, same value every call
+  if (!attr_done) {
+    // Best effort: if the runtime does not take the attribute, the launch
+    // itself reports an LDS request it cannot meet.
+    if (hipFuncSetAttribute((const void*)f, hipFuncAttributeMaxDynamicSharedMemorySize, kMfmaLdsBudget) !=
+        hipSuccess)
+      (void)hipGetLastError();
+    attr_done = true;
+  }
+  int per_cu = 0;
+  const int st = resident_per_cu((const void*)f, kMfmaThreads, lds, &per_cu);
+  if (st != LMH_OK) return st;
+  const int64_t tile_rows = 16 * LMH_MFMA_TM;
+  const int64_t tiles = (R + tile_rows - 1) / tile_rows;
+  const int64_t need = (tiles + LMH_MFMA_WAVES - 1) / LMH_MFMA_WAVES;
+  const int grid = (int)std::max<int64_t>(1, std::min<int64_t>(need, (int64_t)cus * per_cu));
+  hipLaunchKernelGGL(f, dim3(grid), dim3(kMfmaThreads), lds, stream, h, W, R, K, m_base, mp, d2t,
+                     out_id, out_logit, keys, counter);
+  const hipError_t e = hipGetLastError();
+  return e == hipSuccess ? LMH_OK : hip_fail(e, "launch proj_argmax_mfma");
+}
+
+int launch_mfma(const uint16_t* h, int M, int K, const uint16_t* W, int R, const int32_t* d2t,
+                int32_t* out_id, float* out_logit, unsigned long long* keys, unsigned int* counter,
+                hipStream_t stream) {
+  int cus = 0;
+  int st = cu_count(&cus);
+  if (st != LMH_OK) return st;
+  const int cap = mfma_rows_per_pass(K);
+  const int passes = (M + cap - 1) / cap;
+  const int per = (M + passes - 1) / passes;
+  for (int m0 = 0; m0 < M; m0 += per) {
+    const int mp = std::min(per, M - m0);
+    st = mp <= 16 ? launch_mfma_nt<1>(h, K, m0, mp, W, R, d2t, out_id, out_logit, keys, counter, cus, stream)
+                  : launch_mfma_nt<2>(h, K, m0, mp, W, R, d2t, out_id, out_logit, keys, counter, cus, stream);
+    if (st != LMH_OK) return st;
+  }
+  return LMH_OK;
+}
+
+int project(const uint16_t* h, int64_t M, int64_t K, const uint16_t* W, int64_t R, const int32_t* d2t,
+            int32_t* out_id, float* out_logit, void* workspace, size_t workspace_bytes, int path,
+            void* stream) {
+  if (!h || !W || !out_id || !out_logit) return LMH_EINVAL;
+  if (M < 1 || M > LMH_MAX_M || !k_ok(K)) return LMH_EINVAL;
+  if (R < 1 || R > kMaxRows) return LMH_EINVAL;
+  if (!aligned16(h) || !aligned16(W)) return LMH_EINVAL;
+  if (path == LMH_PATH_AUTO) path = draft_project_auto_path(M, K);
+  if (path == LMH_PATH_VALU && !valu_ok(M, K)) return LMH_EINVAL;
+  if (path != LMH_PATH_VALU && path != LMH_PATH_MFMA) return LMH_EINVAL;
+  if (!workspace || !aligned16(workspace)) return LMH_EWORKSPACE;
+  if (workspace_bytes < draft_project_workspace_bytes(M)) return LMH_EWORKSPACE;
+  auto* keys = static_cast<unsigned long long*>(workspace);
+  auto* counter = reinterpret_cast<unsigned int*>(static_cast<char*>(workspace) + 8 * LMH_MAX_M);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (path == LMH_PATH_VALU)
+    return launch_valu(h, (int)M, (int)K, W, (int)R, d2t, out_id, out_logit, keys, counter, s);
+  return launch_mfma(h, (int)M, (int)K, W, (int)R, d2t, out_id, out_logit, keys, counter, s);
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// C ABI
+// ---------------------------------------------------------------------------
+extern "C" {
+
+int lmhead_trim(const uint16_t* W, int64_t N, int64_t K, const int32_t* ids, int64_t S,
+                uint16_t* W_trim, void* stream) {
+  if (S < 0 || N < 1 || N > (int64_t)0x7FFFFFFF || !k_ok(K)) return LMH_EINVAL;
+  if (S == 0) return LMH_OK;
+  if (!W || !ids || !W_trim || !aligned16(W) || !aligned16(W_trim)) return LMH_EINVAL;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  std::vector<int32_t> host((size_t)S);
+  hipError_t e = hipMemcpyAsync(host.data(), ids, (size_t)S * sizeof(int32_t), hipMemcpyDeviceToHost, s);
+  if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync(ids)");
+  e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return hip_fail(e, "hipStreamSynchronize");
+  for (int32_t id : host)
+    if (id < 0 || (int64_t)id >= N) return LMH_ERANGE;
+  int cus = 0;
+  int st = cu_count(&cus);
+  if (st != LMH_OK) return st;
+  const int64_t need = (S + 3) / 4;
+  const int grid = (int)std::max<int64_t>(1, std::min<int64_t>(need, (int64_t)cus * 16));
+  hipLaunchKernelGGL(gather_rows, dim3(grid), dim3(256), 0, s, W, N, (int)K, ids, S, W_trim);
+  e = hipGetLastError();
+  return e == hipSuccess ? LMH_OK : hip_fail(e, "launch gather_rows");
+}
+
+size_t draft_project_workspace_bytes(int64_t M) {
+  return (M >= 1 && M <= LMH_MAX_M) ? (size_t)kWorkspaceBytes : 0;
+}
+
+int draft_project_auto_path(int64_t M, int64_t K) {
+  if (M < 1 || M > LMH_MAX_M || !k_ok(K)) return -1;
+  return valu_ok(M, K) ? LMH_PATH_VALU : LMH_PATH_MFMA;
+}
+
+int draft_project_argmax(const uint16_t* h, int64_t M, int64_t K, const uint16_t* W, int64_t R,
+                         const int32_t* d2t, int32_t* out_id, float* out_logit, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+  return project(h, M, K, W, R, d2t, out_id, out_logit, workspace, workspace_bytes, LMH_PATH_AUTO,
+                 stream);
+}
+
+int draft_project_argmax_path(const uint16_t* h, int64_t M, int64_t K, const uint16_t* W, int64_t R,
+                              const int32_t* d2t, int32_t* out_id, float* out_logit, void* workspace,
+                              size_t workspace_bytes, int path, void* stream) {
+  if (path != LMH_PATH_AUTO && path != LMH_PATH_VALU && path != LMH_PATH_MFMA) return LMH_EINVAL;
+  return project(h, M, K, W, R, d2t, out_id, out_logit, workspace, workspace_bytes, path, stream);
+}
+
+const char* lmhead_status_str(int status) {
+  switch (status) {
+    case LMH_OK: return "ok";
+    case LMH_EINVAL: return "invalid argument (shape, null or misaligned pointer)";
+    case LMH_ERANGE: return "shortlist id out of range [0, N)";
+    case LMH_EWORKSPACE: return "workspace missing, misaligned or too small";
+    case LMH_EHIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+const char* lmhead_last_error(void) { return g_last_error; }
+
+int lmhead_bench_sink_words(void) { return kBenchSinkWords; }
+
+int lmhead_bench_stream_read(const void* src, size_t bytes, uint32_t* sink, int grid, void* stream) {
+  if (!src || !sink || (bytes % 16) != 0 || !aligned16(src) || grid < 0 || grid > kBenchSinkWords)
+    return LMH_EINVAL;
+  int cus = 0;
+  int st = cu_count(&cus);
+  if (st != LMH_OK) return st;
+  if (grid == 0) grid = cus * 8;
+  grid = std::min(grid, kBenchSinkWords);
+  hipLaunchKernelGGL(stream_read, dim3(grid), dim3(kBenchThreads), 0, static_cast<hipStream_t>(stream),
+                     static_cast<const u32x4*>(src), bytes / 16, sink);
+  const hipError_t e = hipGetLastError();
+  return e == hipSuccess ? LMH_OK : hip_fail(e, "launch stream_read");
+}
+
+int lmhead_bench_copy(const void* src, void* dst, size_t bytes, int grid, void* stream) {
+  if (!src || !dst || (bytes % 16) != 0 || !aligned16(src) || !aligned16(dst) || grid < 0) return LMH_EINVAL;
+  int cus = 0;
+  int st = cu_count(&cus);
+  if (st != LMH_OK) return st;
+  if (grid == 0) grid = cus * 8;
+  hipLaunchKernelGGL(copy16, dim3(grid), dim3(kBenchThreads), 0, static_cast<hipStream_t>(stream),
+                     static_cast<const u32x4*>(src), static_cast<u32x4*>(dst), bytes / 16);
+  const hipError_t e = hipGetLastError();
+  return e == hipSuccess ? LMH_OK : hip_fail(e, "launch copy16");
+}
+
+}  // extern "C"

@@ -1,0 +1,218 @@
+"""ctypes binding of liblmhead.so (include/lmhead.h).
+
+Argument marshalling only: every step of the projection runs in the HIP
+kernels of the library.  torch supplies device memory and streams.  The
+functions keep the C names; they take torch tensors, pass their device
+pointers, and raise LmheadError on a nonzero status.  If the library has
+not been built, loading it raises -- there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+import torch
+
+__all__ = [
+    "LmheadError", "lib", "LMH_OK", "LMH_EINVAL", "LMH_ERANGE", "LMH_EWORKSPACE",
+    "LMH_EHIP", "LMH_MAX_M", "LMH_MIN_K", "LMH_MAX_K", "LMH_PATH_AUTO", "LMH_PATH_VALU",
+    "LMH_PATH_MFMA", "lmhead_trim", "draft_project_workspace_bytes", "draft_project_argmax",
+    "draft_project_argmax_path", "draft_project_auto_path", "lmhead_status_str",
+    "lmhead_last_error", "lmhead_bench_sink_words", "lmhead_bench_stream_read",
+    "lmhead_bench_copy", "new_workspace",
+]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "liblmhead.so")
+
+LMH_OK, LMH_EINVAL, LMH_ERANGE, LMH_EWORKSPACE, LMH_EHIP = 0, 1, 2, 3, 4
+LMH_MAX_M, LMH_MIN_K, LMH_MAX_K = 32, 8, 8192
+LMH_PATH_AUTO, LMH_PATH_VALU, LMH_PATH_MFMA = 0, 1, 2
+
+_P = ctypes.c_void_p
+_I64 = ctypes.c_int64
+_SZ = ctypes.c_size_t
+_INT = ctypes.c_int
+
+# name -> (restype, argtypes); mirrors include/lmhead.h
+SIGNATURES = {
+    "lmhead_trim": (_INT, [_P, _I64, _I64, _P, _I64, _P, _P]),
+    "draft_project_workspace_bytes": (_SZ, [_I64]),
+    "draft_project_argmax": (_INT, [_P, _I64, _I64, _P, _I64, _P, _P, _P, _P, _SZ, _P]),
+    "draft_project_argmax_path": (_INT, [_P, _I64, _I64, _P, _I64, _P, _P, _P, _P, _SZ, _INT, _P]),
+    "draft_project_auto_path": (_INT, [_I64, _I64]),
+    "lmhead_status_str": (ctypes.c_char_p, [_INT]),
+    "lmhead_last_error": (ctypes.c_char_p, []),
+    "lmhead_bench_sink_words": (_INT, []),
+    "lmhead_bench_stream_read": (_INT, [_P, _SZ, _P, _INT, _P]),
+    "lmhead_bench_copy": (_INT, [_P, _P, _SZ, _INT, _P]),
+}
+
+_lib = None
+_lock = threading.Lock()
+
+
+class LmheadError(RuntimeError):
+    def __init__(self, code: int, where: str):
+        self.code = code
+        text = lib().lmhead_status_str(code).decode()
+        if code == LMH_EHIP:
+            text += ": " + lib().lmhead_last_error().decode()
+        super().__init__(f"{where}: status {code} ({text})")
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library.  Raises if it was not built."""
+    global _lib
+    if _lib is None:
+        with _lock:
+            if _lib is None:
+                if not os.path.exists(LIB_PATH):
+                    raise RuntimeError(
+                        f"{LIB_PATH} is missing: build it with "
+                        "`python -m vocab_shortlisted_lm_amd.build` (hipcc, gfx950)")
+                dll = ctypes.CDLL(LIB_PATH)
+                for name, (res, args) in SIGNATURES.items():
+                    fn = getattr(dll, name)
+                    fn.restype = res
+                    fn.argtypes = args
+                _lib = dll
+    return _lib
+
+
+def _check(code: int, where: str) -> None:
+    if code != LMH_OK:
+        raise LmheadError(code, where)
+
+
+_BF16_LIKE = (torch.bfloat16, torch.int16, torch.uint16)
+
+
+def _dev_tensor(t: torch.Tensor, name: str, dtypes, ndim: int) -> None:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a device tensor")
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected one of {dtypes}")
+    if t.dim() != ndim or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous {ndim}-d tensor")
+
+
+def _stream(stream, device) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return int(stream.cuda_stream) if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def lmhead_trim(W: torch.Tensor, ids: torch.Tensor, out: torch.Tensor | None = None,
+                stream=None) -> torch.Tensor:
+    """W_trim[i] = W[ids[i]] (bf16 [S, K]).  Synchronizes `stream` once."""
+    _dev_tensor(W, "W", _BF16_LIKE, 2)
+    _dev_tensor(ids, "ids", (torch.int32,), 1)
+    n, k = W.shape
+    s = ids.shape[0]
+    if out is None:
+        out = torch.empty((s, k), dtype=W.dtype, device=W.device)
+    _dev_tensor(out, "out", _BF16_LIKE, 2)
+    if tuple(out.shape) != (s, k):
+        raise ValueError("out must be [S, K]")
+    _check(lib().lmhead_trim(W.data_ptr(), n, k, ids.data_ptr(), s, out.data_ptr(),
+                             _stream(stream, W.device)), "lmhead_trim")
+    return out
+
+
+def draft_project_workspace_bytes(M: int) -> int:
+    return int(lib().draft_project_workspace_bytes(M))
+
+
+def draft_project_auto_path(M: int, K: int) -> int:
+    return int(lib().draft_project_auto_path(M, K))
+
+
+def new_workspace(device=None) -> torch.Tensor:
+    """A zero-filled workspace for any M <= LMH_MAX_M."""
+    nbytes = draft_project_workspace_bytes(LMH_MAX_M)
+    return torch.zeros(nbytes, dtype=torch.uint8, device=device or "cuda")
+
+
+_ws_cache: dict = {}
+
+
+def _default_workspace(device, stream_handle: int) -> torch.Tensor:
+    key = (torch.device(device).index, stream_handle)
+    ws = _ws_cache.get(key)
+    if ws is None:
+        ws = new_workspace(device)
+        _ws_cache[key] = ws
+    return ws
+
+
+def draft_project_argmax_path(h: torch.Tensor, W: torch.Tensor, d2t: torch.Tensor | None,
+                              path: int, out_id: torch.Tensor | None = None,
+                              out_logit: torch.Tensor | None = None,
+                              workspace: torch.Tensor | None = None, stream=None):
+    """(out_id int32 [M], out_logit float32 [M]) for the best row of W per
+    hidden row, mapped through d2t.  Queues one call; never synchronizes."""
+    _dev_tensor(h, "h", _BF16_LIKE, 2)
+    _dev_tensor(W, "W", _BF16_LIKE, 2)
+    m, k = h.shape
+    r, k2 = W.shape
+    if k != k2:
+        raise ValueError("h and W must have the same K")
+    if d2t is not None:
+        _dev_tensor(d2t, "d2t", (torch.int32,), 1)
+        if d2t.shape[0] != r:
+            raise ValueError("d2t must have one entry per row of W")
+    if out_id is None:
+        out_id = torch.empty(m, dtype=torch.int32, device=h.device)
+    if out_logit is None:
+        out_logit = torch.empty(m, dtype=torch.float32, device=h.device)
+    _dev_tensor(out_id, "out_id", (torch.int32,), 1)
+    _dev_tensor(out_logit, "out_logit", (torch.float32,), 1)
+    if out_id.shape[0] < m or out_logit.shape[0] < m:
+        raise ValueError("outputs must hold M entries")
+    st = _stream(stream, h.device)
+    if workspace is None:
+        workspace = _default_workspace(h.device, st)
+    code = lib().draft_project_argmax_path(
+        h.data_ptr(), m, k, W.data_ptr(), r, d2t.data_ptr() if d2t is not None else None,
+        out_id.data_ptr(), out_logit.data_ptr(), workspace.data_ptr(),
+        workspace.numel() * workspace.element_size(), path, st)
+    _check(code, "draft_project_argmax")
+    return out_id, out_logit
+
+
+def draft_project_argmax(h, W, d2t=None, out_id=None, out_logit=None, workspace=None,
+                         stream=None):
+    """draft_project_argmax_path with the library's own kernel choice."""
+    return draft_project_argmax_path(h, W, d2t, LMH_PATH_AUTO, out_id, out_logit, workspace,
+                                     stream)
+
+
+def lmhead_status_str(code: int) -> str:
+    return lib().lmhead_status_str(code).decode()
+
+
+def lmhead_last_error() -> str:
+    return lib().lmhead_last_error().decode()
+
+
+def lmhead_bench_sink_words() -> int:
+    return int(lib().lmhead_bench_sink_words())
+
+
+def lmhead_bench_stream_read(buf: torch.Tensor, sink: torch.Tensor, grid: int = 0,
+                             stream=None) -> None:
+    nbytes = buf.numel() * buf.element_size()
+    _check(lib().lmhead_bench_stream_read(buf.data_ptr(), nbytes, sink.data_ptr(), grid,
+                                          _stream(stream, buf.device)),
+           "lmhead_bench_stream_read")
+
+
+def lmhead_bench_copy(src: torch.Tensor, dst: torch.Tensor, grid: int = 0, stream=None) -> None:
+    nbytes = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() < nbytes:
+        raise ValueError("dst too small")
+    _check(lib().lmhead_bench_copy(src.data_ptr(), dst.data_ptr(), nbytes, grid,
+                                   _stream(stream, src.device)), "lmhead_bench_copy")
