@@ -47,7 +47,7 @@ def source_digest() -> str:
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def measured_traffic(kernel: str, workload: str):
+def measured_traffic(path: str, workload: str):
     """HBM bytes per launch from committed rocprofv3 counter runs, if they
     were taken on the current kernel source; else None."""
     try:
@@ -56,7 +56,7 @@ def measured_traffic(kernel: str, workload: str):
     except (OSError, ValueError):
         return None
     for e in table.get("entries", []):
-        if e.get("kernel") == kernel and e.get("workload") == workload:
+        if e.get("path") == path and e.get("workload") == workload:
             if e.get("source_sha256_16") != source_digest():
                 return None
             return e.get("bytes_per_launch")
@@ -94,6 +94,9 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--stream-read", action="store_true",
                     help="also time the plain streaming-read kernel over W (practical ceiling)")
+    ap.add_argument("--calibrate", action="store_true",
+                    help="after the timed region, run the plain copy and read kernels over 1 GiB "
+                         "(known bytes, for scaling hardware counters)")
     a = ap.parse_args()
 
     if a.gpus != 1:
@@ -125,7 +128,8 @@ def main() -> int:
     trimmed = ids is not None and not a.full
     path = {"auto": L.LMH_PATH_AUTO, "valu": L.LMH_PATH_VALU, "mfma": L.LMH_PATH_MFMA}[a.path]
     chosen = L.draft_project_auto_path(m, c.k) if path == L.LMH_PATH_AUTO else path
-    kname = {L.LMH_PATH_VALU: "proj_argmax_valu", L.LMH_PATH_MFMA: "proj_argmax_mfma"}[chosen]
+    kpath = {L.LMH_PATH_VALU: "valu", L.LMH_PATH_MFMA: "mfma"}[chosen]
+    kname = {"valu": "proj_argmax_valu", "mfma": "proj_argmax_mfma"}[kpath]
 
     w_full = torch.from_numpy(w_np.view(np.int16)).to(dev)
     h = torch.from_numpy(h_np.view(np.int16)).to(dev)
@@ -171,7 +175,7 @@ def main() -> int:
 
     abytes = algorithmic_bytes(m, rows, c.k, d2t is not None)
     achieved = abytes / (ms_per_step / 1e3) / 1e9
-    traffic = measured_traffic(kname, workload)
+    traffic = measured_traffic(kpath, workload)
     extra = {}
     if a.stream_read:
         sink = torch.zeros(L.lmhead_bench_sink_words(), dtype=torch.int32, device=dev)
@@ -186,6 +190,20 @@ def main() -> int:
         torch.cuda.synchronize()
         nb = buf.numel() * buf.element_size()
         extra["stream_read_gbps"] = round(nb / (e0.elapsed_time(e1) / 20 / 1e3) / 1e9, 1)
+
+    if a.calibrate:
+        nb = 1 << 30
+        src = torch.empty(nb // 4, dtype=torch.int32, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        sink = torch.zeros(L.lmhead_bench_sink_words(), dtype=torch.int32, device=dev)
+        for _ in range(3):
+            L.lmhead_bench_copy(src, dst)
+        for _ in range(3):
+            L.lmhead_bench_stream_read(src, sink)
+        torch.cuda.synchronize()
+        extra["calibration"] = {"copy_bytes_read": nb, "copy_bytes_written": nb, "read_bytes": nb,
+                                "dispatches": "3 x copy16, then 3 x stream_read"}
+        del src, dst
 
     result = {
         "metric": METRIC,

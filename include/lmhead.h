@@ -85,7 +85,8 @@ int lmhead_trim(const uint16_t* W, int64_t N, int64_t K,
 
 /*
  * draft_project_workspace_bytes -- bytes of workspace draft_project_argmax
- * needs for M hidden rows (a small constant; 0 if M is out of range).
+ * needs for M hidden rows: one 8-byte slot per hidden row per workgroup of
+ * the projection kernel (M * 8 KiB; 0 if M is out of range).
  */
 size_t draft_project_workspace_bytes(int64_t M);
 
@@ -105,16 +106,18 @@ size_t draft_project_workspace_bytes(int64_t M);
  *  out_id     [M] int32.  -1 only if no logit of the row is ordered (NaN).
  *  out_logit  [M] float.
  *  workspace  at least draft_project_workspace_bytes(M) bytes, 16-byte
- *             aligned, ZERO-FILLED by the caller before its first use.  Each
- *             call leaves it zero-filled again when it completes, so one
- *             workspace serves any number of calls that are ordered on one
- *             stream.  Calls that may run concurrently need separate
- *             workspaces.  After a device fault, zero it again.
+ *             aligned.  Scratch for one call: its contents on entry do not
+ *             matter and are undefined afterwards.  Calls ordered on one
+ *             stream may share a workspace; calls that may run concurrently
+ *             need separate ones.
  *
- * Never synchronizes and never allocates; one kernel launch in the common
- * case (M * K <= 64 Ki for the matrix-core path; larger M * K splits the
- * hidden rows over several launches).  Inputs with NaN or Inf give an
- * unspecified (but in-bounds) result.
+ * Never synchronizes and never allocates.  Queues two kernels: the fused
+ * projection + running argmax, whose workgroups each leave their best
+ * (logit, row) per hidden row in the workspace, and a small kernel that
+ * folds those, maps the winner through d2t and writes the outputs.  When the
+ * matrix-core path cannot hold all M hidden rows in LDS at once (M * K above
+ * about 75 Ki at K = 2,560) the rows are split over several such pairs.
+ * Inputs with NaN or Inf give an unspecified (but in-bounds) result.
  */
 int draft_project_argmax(const uint16_t* h, int64_t M, int64_t K,
                          const uint16_t* W, int64_t R,
@@ -126,7 +129,7 @@ int draft_project_argmax(const uint16_t* h, int64_t M, int64_t K,
 /*
  * draft_project_argmax_path -- draft_project_argmax with the kernel chosen
  * by the caller (LMH_PATH_*), for tests and measurement.  LMH_PATH_VALU
- * accepts M <= 4 with M * ceil(K / 512) <= 20; LMH_PATH_MFMA accepts every
+ * accepts M <= 8 with M * ceil(K / 512) <= 40; LMH_PATH_MFMA accepts every
  * shape draft_project_argmax accepts.  Other shapes give LMH_EINVAL.
  */
 int draft_project_argmax_path(const uint16_t* h, int64_t M, int64_t K,

@@ -63,16 +63,19 @@ def test_workspace_bytes(L):
     assert L.draft_project_workspace_bytes(33) == 0
     for m in (1, 3, 24, 32):
         ws = L.draft_project_workspace_bytes(m)
-        assert ws >= 8 * m + 4 and ws % 16 == 0
+        assert ws == m * 1024 * 8 and ws % 16 == 0
 
 
 def test_auto_path(L):
     assert L.draft_project_auto_path(1, 2560) == L.LMH_PATH_VALU
     assert L.draft_project_auto_path(4, 2560) == L.LMH_PATH_VALU
     assert L.draft_project_auto_path(3, 2560) == L.LMH_PATH_VALU
-    assert L.draft_project_auto_path(5, 2560) == L.LMH_PATH_MFMA
+    assert L.draft_project_auto_path(5, 2560) == L.LMH_PATH_VALU
+    assert L.draft_project_auto_path(8, 2560) == L.LMH_PATH_VALU
+    assert L.draft_project_auto_path(9, 2560) == L.LMH_PATH_MFMA
     assert L.draft_project_auto_path(24, 2560) == L.LMH_PATH_MFMA
     assert L.draft_project_auto_path(4, 8192) == L.LMH_PATH_MFMA
+    assert L.draft_project_auto_path(2, 8192) == L.LMH_PATH_VALU
     assert L.draft_project_auto_path(1, 8192) == L.LMH_PATH_VALU
     for m, k in ((0, 2560), (33, 2560), (1, 12), (1, 0), (1, 8200)):
         assert L.draft_project_auto_path(m, k) == -1
@@ -82,7 +85,7 @@ def test_auto_path(L):
 A, B, C, D, E = 0x10000, 0x20000, 0x30000, 0x40000, 0x50000
 
 
-def call(L, h=A, m=1, k=2560, w=B, r=100, d2t=None, oid=C, olog=D, ws=E, wsb=512, path=0):
+def call(L, h=A, m=1, k=2560, w=B, r=100, d2t=None, oid=C, olog=D, ws=E, wsb=1 << 20, path=0):
     return L.lib().draft_project_argmax_path(h, m, k, w, r, d2t, oid, olog, ws, wsb, path, None)
 
 
@@ -90,8 +93,9 @@ def call(L, h=A, m=1, k=2560, w=B, r=100, d2t=None, oid=C, olog=D, ws=E, wsb=512
     (dict(h=None), 1), (dict(w=None), 1), (dict(oid=None), 1), (dict(olog=None), 1),
     (dict(m=0), 1), (dict(m=33), 1), (dict(k=0), 1), (dict(k=12), 1), (dict(k=8200), 1),
     (dict(r=0), 1), (dict(r=(1 << 30) + 1), 1), (dict(h=A + 2), 1), (dict(w=B + 8), 1),
-    (dict(path=7), 1), (dict(m=5, path=1), 1), (dict(m=4, k=4096, path=1), 1),
+    (dict(path=7), 1), (dict(m=9, path=1), 1), (dict(m=4, k=8192, path=1), 1), (dict(m=8, k=4096, path=1), 1),
     (dict(ws=None), 3), (dict(ws=E + 4), 3), (dict(wsb=16), 3), (dict(wsb=0), 3),
+    (dict(m=2, wsb=8 * 1024 * 2 - 8), 3),
 ])
 def test_project_rejects_on_host(L, kw, code):
     assert call(L, **kw) == code
@@ -116,3 +120,10 @@ def test_bench_kernels_reject_on_host(L):
     assert lib.lmhead_bench_stream_read(None, 1024, B, 0, None) == 1
     assert lib.lmhead_bench_copy(A, B + 4, 1024, 0, None) == 1
     assert lib.lmhead_bench_sink_words() >= 4096
+
+
+def test_read_id_list(L, tmp_path):
+    p = tmp_path / "ranks.txt"
+    p.write_text("17\n3\n\n248319\n0\n")
+    ids = L.read_id_list(str(p))
+    assert ids.dtype.name == "int32" and ids.tolist() == [17, 3, 248319, 0]

@@ -41,8 +41,10 @@ def dev_i32(a):
 
 
 def paths_for(L, m, k):
+    """Every kernel that accepts (m, k): the VALU path takes M <= 8 with
+    M * ceil(K / 512) <= 40 (include/lmhead.h); the matrix-core path takes all."""
     ps = [L.LMH_PATH_MFMA]
-    if L.draft_project_auto_path(m, k) == L.LMH_PATH_VALU:
+    if m <= 8 and m * ((k // 8 + 63) // 64) <= 40:
         ps.insert(0, L.LMH_PATH_VALU)
     return ps
 
@@ -187,21 +189,21 @@ def test_config5_m24_full_and_52k(L):
 # determinism and workspace contract
 # --------------------------------------------------------------------------
 
-def test_repeated_calls_bit_identical_and_workspace_cleared(L):
+def test_repeated_calls_bit_identical_any_workspace_contents(L):
+    """Results do not depend on what the workspace held before the call."""
     w_dev = device_weights(2)
     c = synth.CONFIGS[2]
     ws = L.new_workspace()
     for m in (1, 3, 24):
         h = dev_bf16(synth.hidden(777, 0, m, c.k))
         first = None
-        for _ in range(4):
+        for fill in (0xFF, 0x00, 0x5A, 0xFF):
+            ws.fill_(fill)
             i, l = L.draft_project_argmax(h, w_dev, workspace=ws)
             got = (i.cpu().numpy().copy(), l.cpu().numpy().view(np.uint32).copy())
             if first is None:
                 first = got
             assert np.array_equal(got[0], first[0]) and np.array_equal(got[1], first[1])
-        torch.cuda.synchronize()
-        assert int(ws.count_nonzero()) == 0, "workspace not left zero-filled"
 
 
 def test_separate_stream_and_workspace(L):
@@ -224,7 +226,7 @@ def test_separate_stream_and_workspace(L):
 EDGE = [
     (1, 8, 1), (1, 8, 2), (1, 16, 3), (2, 24, 63), (3, 256, 64), (4, 264, 65),
     (1, 520, 1000), (1, 2560, 1), (1, 2560, 7), (4, 2560, 4097), (2, 4096, 333),
-    (1, 8192, 1501), (5, 264, 129), (8, 2560, 33), (16, 2560, 517), (17, 256, 700),
+    (1, 8192, 1501), (5, 264, 129), (8, 2560, 33), (6, 2560, 777), (7, 3072, 50), (16, 2560, 517), (17, 256, 700),
     (24, 2560, 1031), (31, 520, 99), (32, 2560, 2050), (32, 8192, 300), (13, 8, 77),
 ]
 
@@ -298,12 +300,13 @@ def test_rejected_calls_write_nothing(L):
         dict(m=0), dict(m=33), dict(k=12), dict(r=0), dict(hp=h.data_ptr() + 2),
         dict(wsb=8), dict(wsp=ws.data_ptr() + 4), dict(path=9),
     ]
+    ws_before = ws.clone()
     for cs in cases:
         code = lib.draft_project_argmax_path(
             cs.get("hp", h.data_ptr()), cs.get("m", 2), cs.get("k", 256), w.data_ptr(),
             cs.get("r", 100), None, oid.data_ptr(), olog.data_ptr(), cs.get("wsp", ws.data_ptr()),
-            cs.get("wsb", 512), cs.get("path", 0), None)
+            cs.get("wsb", ws.numel()), cs.get("path", 0), None)
         assert code in (L.LMH_EINVAL, L.LMH_EWORKSPACE), cs
     torch.cuda.synchronize()
     assert bool((oid == 77).all()) and bool((olog == 5.0).all())
-    assert int(ws.count_nonzero()) == 0
+    assert torch.equal(ws, ws_before)

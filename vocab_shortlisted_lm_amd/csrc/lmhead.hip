@@ -12,11 +12,13 @@
 //                       wave tile on 16x16x32 bf16 matrix-core instructions,
 //                       so no cross-lane reduction per row is needed.
 // Both projection kernels fuse the argmax: each wave keeps a running
-// (logit, row) per hidden row, a workgroup folds its waves through LDS, and
-// one 64-bit atomicMax per hidden row per workgroup folds workgroups.  The
-// last workgroup to finish (ticket counter) decodes the winner, maps it
-// through d2t (EAGLE-3 style draft-to-target ids, "Two ways to run it") and
-// re-zeroes the workspace, so a call is a single launch with no memset.
+// (logit, row) per hidden row as a 64-bit key, a workgroup folds its waves
+// through LDS and stores one key per hidden row into its own workspace slot.
+//   finalize_argmax     one workgroup per hidden row folds the slots, decodes
+//                       the winner and maps it through d2t (EAGLE-3 style
+//                       draft-to-target ids, "Two ways to run it").
+// The two kernels are ordered by the stream; no atomics, fences or memsets
+// are needed, and the workspace needs no initial contents.
 // The argmax is reduced locally instead of gathering logits, the change the
 // fair re-run on krisbailey.com/articles/shortlist-mtp credits ("Re-running
 // the comparison fairly").
@@ -33,6 +35,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <type_traits>
 #include <utility>
 #include <vector>
 
@@ -52,34 +55,55 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 #define LMH_VALU_ROWS 2          // head rows per wave per step (VALU path)
 #endif
 #ifndef LMH_VALU_WG_PER_CU
-#define LMH_VALU_WG_PER_CU 8     // cap on resident workgroups per CU (VALU path)
+#define LMH_VALU_WG_PER_CU 1     // cap on resident workgroups per CU (VALU path)
 #endif
 #ifndef LMH_MFMA_WAVES
 #define LMH_MFMA_WAVES 8         // waves per workgroup (matrix-core path)
 #endif
 #ifndef LMH_MFMA_TM
-#define LMH_MFMA_TM 2            // 16-row tiles per wave step (matrix-core path)
+#define LMH_MFMA_TM 1            // 16-row tiles per wave step (matrix-core path)
 #endif
 #ifndef LMH_MFMA_SB
-#define LMH_MFMA_SB 8            // k-steps of loads issued together
+#define LMH_MFMA_SB 4            // k-steps of loads issued together
+#endif
+#ifndef LMH_VALU_TILE_ROWS
+#define LMH_VALU_TILE_ROWS 4     // rows per tile of the tiled VALU kernel (M = 1); 0 = row order
+#endif
+#ifndef LMH_VALU_PREFETCH
+#define LMH_VALU_PREFETCH 1      // double-buffer rows in registers (VALU path)
 #endif
 #ifndef LMH_NT_LOADS
-#define LMH_NT_LOADS 1           // non-temporal W loads
+#define LMH_NT_LOADS 1           // non-temporal W loads (VALU path)
+#endif
+#ifndef LMH_MFMA_NT_LOADS
+#define LMH_MFMA_NT_LOADS 0      // non-temporal W loads (matrix-core path)
 #endif
 
-constexpr int kValuWaves = 4;
-constexpr int kValuThreads = 64 * kValuWaves;
+#ifndef LMH_VALU_WAVES
+#define LMH_VALU_WAVES 4          // waves per workgroup (VALU path)
+#endif
 constexpr int kMfmaThreads = 64 * LMH_MFMA_WAVES;
 // LDS for staged hidden rows in the matrix-core path.  At most one
 // workgroup of that path per CU when it is full; the rest of the 160 KiB is
 // left for the key exchange.
 constexpr int kMfmaLdsBudget = 152 * 1024;
-constexpr int kValuMaxChunksTimesM = 20;   // register budget: 80 VGPRs of h
-constexpr int kWorkspaceBytes = 512;       // 32 keys + ticket counter, padded
+constexpr int kValuMaxM = 8;
+constexpr int kValuMaxChunksTimesM = 40;   // register budget: 160 VGPRs of h
+#ifndef LMH_VALU_AUTO_MAX_M
+#define LMH_VALU_AUTO_MAX_M 8     // largest M the default choice sends to the VALU path
+#endif
+// Workgroup slots per hidden row in the workspace; grids are clamped to it.
+constexpr int kMaxGrid = 1024;
 constexpr int64_t kMaxRows = (int64_t)1 << 30;  // keeps row arithmetic in int range
 constexpr uint32_t kBufferWord3 = 0x00020000u;  // gfx9 raw buffer, 32-bit data
 constexpr uint32_t kOobOffset = 0x80000000u;    // any offset >= num_records reads 0
-constexpr int kCachePolicy = LMH_NT_LOADS ? 2 : 0;  // bit 1 = nt
+// cache-policy operand of buffer loads: bit 1 = nt (streaming).  The VALU
+// path reads whole 1 KiB row pieces per instruction and streams best with
+// nt; the matrix-core path reads 64-byte pieces of 16 rows per instruction,
+// whose 128-byte lines are completed by the next k-step, so it keeps them
+// cacheable.
+constexpr int kPolicyValu = LMH_NT_LOADS ? 2 : 0;
+constexpr int kPolicyMfma = LMH_MFMA_NT_LOADS ? 2 : 0;
 
 // ---------------------------------------------------------------------------
 // device helpers
@@ -89,8 +113,9 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
                                            (int)kBufferWord3);
 }
 
+template <int POLICY = kPolicyValu>
 __device__ __forceinline__ u32x4 load16(__amdgpu_buffer_rsrc_t r, uint32_t voff) {
-  return __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, 0, kCachePolicy);
+  return __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, 0, POLICY);
 }
 
 // acc += sum of the eight bf16 products of one 16-byte chunk (fp32 adds).
@@ -163,37 +188,50 @@ __device__ __forceinline__ void unpack_key(unsigned long long k, float& v, int& 
   idx = (int)(0xFFFFFFFFu - (uint32_t)k);
 }
 
-// Workgroup epilogue, run by wave 0 only.  `wg_key[m]` is this workgroup's
-// best key for hidden row m (in LDS).  Folds it into the workspace, takes a
-// ticket, and if this is the last workgroup, writes the results and clears
-// the workspace for the next call on the stream.
-__device__ __forceinline__ void finish_workgroup(unsigned long long key, int lane, int mcount,
-                                                 int m_base, const int32_t* __restrict__ d2t,
-                                                 int32_t* __restrict__ out_id,
-                                                 float* __restrict__ out_logit,
-                                                 unsigned long long* __restrict__ keys,
-                                                 unsigned int* __restrict__ counter) {
-  if (lane < mcount && key != 0ull) atomicMax(&keys[m_base + lane], key);
-  __threadfence();  // release: the key updates are visible before the ticket
-  unsigned int ticket = 0;
-  if (lane == 0) ticket = atomicAdd(counter, 1u);
-  ticket = (unsigned int)__builtin_amdgcn_readfirstlane((int)ticket);
-  if (ticket != gridDim.x - 1) return;
-  __threadfence();  // acquire: every workgroup's key update is visible
-  if (lane < mcount) {
-    const unsigned long long k = atomicExch(&keys[m_base + lane], 0ull);
-    float v;
-    int idx;
-    unpack_key(k, v, idx);
-    if (k == 0ull) {
-      out_id[m_base + lane] = -1;
-      out_logit[m_base + lane] = __builtin_nanf("");
-    } else {
-      out_id[m_base + lane] = d2t ? d2t[idx] : idx;
-      out_logit[m_base + lane] = v;
-    }
+// Workgroup epilogue, run by wave 0 only: lane m < mcount publishes this
+// workgroup's best key for hidden row m_base + m into its own slot.  Slots
+// are laid out [hidden row][workgroup], so the finalize kernel reads each
+// hidden row's keys contiguously.  Plain stores: the end of the kernel
+// orders them before the finalize kernel on the same stream.
+__device__ __forceinline__ void publish_workgroup(unsigned long long key, int lane, int mcount, int m_base,
+                                                  unsigned long long* __restrict__ slots) {
+  if (lane < mcount) slots[(size_t)(m_base + lane) * kMaxGrid + blockIdx.x] = key;
+}
+
+// One workgroup per hidden row: fold the `nslots` workgroup keys, decode
+// the winner, map it through d2t and write the outputs.
+__global__ void __launch_bounds__(256)
+finalize_argmax(const unsigned long long* __restrict__ slots, int nslots, int m_base,
+                const int32_t* __restrict__ d2t, int32_t* __restrict__ out_id,
+                float* __restrict__ out_logit) {
+  __shared__ unsigned long long s_wave[4];
+  const int m = m_base + blockIdx.x;
+  const unsigned long long* row = slots + (size_t)m * kMaxGrid;
+  unsigned long long k = 0ull;
+  for (int i = threadIdx.x; i < nslots; i += 256) k = row[i] > k ? row[i] : k;
+#pragma unroll
+  for (int x = 32; x >= 1; x >>= 1) {
+    const uint32_t lo = (uint32_t)__shfl_xor((int)(uint32_t)k, x);
+    const uint32_t hi = (uint32_t)__shfl_xor((int)(uint32_t)(k >> 32), x);
+    const unsigned long long o = ((unsigned long long)hi << 32) | lo;
+    k = o > k ? o : k;
   }
-  if (lane == 0) atomicExch(counter, 0u);
+  if ((threadIdx.x & 63) == 0) s_wave[threadIdx.x >> 6] = k;
+  __syncthreads();
+  if (threadIdx.x != 0) return;
+  k = s_wave[0];
+#pragma unroll
+  for (int w = 1; w < 4; ++w) k = s_wave[w] > k ? s_wave[w] : k;
+  if (k == 0ull) {
+    out_id[m] = -1;
+    out_logit[m] = __builtin_nanf("");
+    return;
+  }
+  float v;
+  int idx;
+  unpack_key(k, v, idx);
+  out_id[m] = d2t ? d2t[idx] : idx;
+  out_logit[m] = v;
 }
 
 // ---------------------------------------------------------------------------
@@ -223,13 +261,11 @@ gather_rows(const uint16_t* __restrict__ W, int64_t N, int K, const int32_t* __r
 // Lane `l` owns the 16-byte chunks c = l + 64 j (j < CPL) of every row, so
 // one load instruction moves 1 KiB of a row, fully coalesced.  Chunks past
 // the row end get an out-of-range buffer offset and read as zero.
-template <int M, int CPL, int U>
-__global__ void __launch_bounds__(kValuThreads)
+template <int M, int CPL, int U, int WV>
+__global__ void __launch_bounds__(64 * WV)
 proj_argmax_valu(const uint16_t* __restrict__ h, const uint16_t* __restrict__ W, int R, int K,
-                 const int32_t* __restrict__ d2t, int32_t* __restrict__ out_id,
-                 float* __restrict__ out_logit, unsigned long long* __restrict__ keys,
-                 unsigned int* __restrict__ counter) {
-  __shared__ unsigned long long s_key[kValuWaves][M];
+                 unsigned long long* __restrict__ slots) {
+  __shared__ unsigned long long s_key[WV][M];
   const int lane = threadIdx.x & 63;
   const int wave = wave_id();
   const int chunks = K >> 3;
@@ -256,7 +292,7 @@ proj_argmax_valu(const uint16_t* __restrict__ h, const uint16_t* __restrict__ W,
     bidx[m] = -1;
   }
 
-  const int step = gridDim.x * kValuWaves * U;
+  const int step = gridDim.x * WV * U;
   u32x4 wa[U][CPL], wb[U][CPL];
 
   auto load_rows = [&](u32x4 (&w)[U][CPL], int r0) {
@@ -283,18 +319,25 @@ proj_argmax_valu(const uint16_t* __restrict__ h, const uint16_t* __restrict__ W,
     }
   };
 
-  // Two register buffers: the next rows are in flight while these are scored.
-  int r0 = (blockIdx.x * kValuWaves + wave) * U;
-  if (r0 < R) load_rows(wa, r0);
-  while (r0 < R) {
-    const int r1 = r0 + step;
-    if (r1 < R) load_rows(wb, r1);
-    score_rows(wa, r0);
-    if (r1 >= R) break;
-    const int r2 = r1 + step;
-    if (r2 < R) load_rows(wa, r2);
-    score_rows(wb, r1);
-    r0 = r2;
+  int r0 = (blockIdx.x * WV + wave) * U;
+  if constexpr (LMH_VALU_PREFETCH) {
+    // Two register buffers: the next rows are in flight while these are scored.
+    if (r0 < R) load_rows(wa, r0);
+    while (r0 < R) {
+      const int r1 = r0 + step;
+      if (r1 < R) load_rows(wb, r1);
+      score_rows(wa, r0);
+      if (r1 >= R) break;
+      const int r2 = r1 + step;
+      if (r2 < R) load_rows(wa, r2);
+      score_rows(wb, r1);
+      r0 = r2;
+    }
+  } else {
+    for (; r0 < R; r0 += step) {
+      load_rows(wa, r0);
+      score_rows(wa, r0);
+    }
   }
 
   if (lane == 0) {
@@ -306,9 +349,128 @@ proj_argmax_valu(const uint16_t* __restrict__ h, const uint16_t* __restrict__ W,
   unsigned long long key = 0ull;
   if (lane < M) {
 #pragma unroll
-    for (int w = 0; w < kValuWaves; ++w) key = s_key[w][lane] > key ? s_key[w][lane] : key;
+    for (int w = 0; w < WV; ++w) key = s_key[w][lane] > key ? s_key[w][lane] : key;
   }
-  finish_workgroup(key, lane, M, 0, d2t, out_id, out_logit, keys, counter);
+  publish_workgroup(key, lane, M, 0, slots);
+}
+
+// VALU path, tiled order: a wave owns tiles of TR consecutive head rows and
+// walks each tile in 1 KiB column stripes (stripe j = chunks 64 j .. 64 j + 63
+// of every row of the tile), keeping one fp32 partial sum per (row, hidden
+// row) in its lanes.  One batch is TR rows x 1 KiB; the next batch is in
+// flight while this one is scored.  Hidden rows live in LDS, zero-padded to
+// whole stripes, so the batch loop is a plain runtime loop.
+template <int M, int TR, int WV>
+__global__ void __launch_bounds__(64 * WV)
+proj_argmax_valu_tiled(const uint16_t* __restrict__ h, const uint16_t* __restrict__ W, int R, int K,
+                       unsigned long long* __restrict__ slots) {
+  extern __shared__ u32x4 h_stripes[];  // [M][nb * 64] chunks, zero past K
+  __shared__ unsigned long long s_key[WV][M];
+  const int lane = threadIdx.x & 63;
+  const int wave = wave_id();
+  const int chunks = K >> 3;
+  const int nb = (chunks + 63) >> 6;  // stripes per row
+  const int hc = nb * 64;
+  const uint32_t row_bytes = (uint32_t)K * 2u;
+
+  for (int i = threadIdx.x; i < M * hc; i += (64 * WV)) {
+    const int m = i / hc;
+    const int c = i - m * hc;
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (c < chunks) v = *reinterpret_cast<const u32x4*>(h + (size_t)m * K + (size_t)c * 8);
+    h_stripes[i] = v;
+  }
+  __syncthreads();
+
+  float best[M];
+  int bidx[M];
+#pragma unroll
+  for (int m = 0; m < M; ++m) {
+    best[m] = 0.0f;
+    bidx[m] = -1;
+  }
+  float acc[TR][M];
+#pragma unroll
+  for (int q = 0; q < TR; ++q)
+#pragma unroll
+    for (int m = 0; m < M; ++m) acc[q][m] = 0.0f;
+
+  const int ntiles = (R + TR - 1) / TR;
+  const int tstride = gridDim.x * WV;
+
+  // One descriptor per tile covering its live rows: offsets of rows past R
+  // (and of chunks past K) are >= num_records and read as zero.
+  auto issue = [&](u32x4 (&w)[TR], int tile, int j) {
+    const int c = lane + 64 * j;
+    const int r0 = tile * TR;
+    const int live = min(TR, R - r0);
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(W + (size_t)r0 * (size_t)K, (uint32_t)live * row_bytes);
+    const uint32_t off = c < chunks ? (uint32_t)c * 16u : kOobOffset;
+#pragma unroll
+    for (int q = 0; q < TR; ++q) w[q] = load16(rs, off + (uint32_t)q * row_bytes);
+  };
+  auto consume = [&](const u32x4 (&w)[TR], int tile, int j) {
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+      const u32x4 hv = h_stripes[m * hc + j * 64 + lane];
+#pragma unroll
+      for (int q = 0; q < TR; ++q) acc[q][m] = dot8(w[q], hv, acc[q][m]);
+    }
+    if (j == nb - 1) {
+      const int r0 = tile * TR;
+#pragma unroll
+      for (int q = 0; q < TR; ++q)
+#pragma unroll
+        for (int m = 0; m < M; ++m) {
+          const float sum = wave_sum(acc[q][m]);
+          acc[q][m] = 0.0f;
+          if (r0 + q < R) take_best(sum, r0 + q, best[m], bidx[m]);
+        }
+    }
+  };
+  auto advance = [&](int& tile, int& j) {
+    if (++j == nb) {
+      j = 0;
+      tile += tstride;
+    }
+  };
+
+  int tile = blockIdx.x * WV + wave;
+  int j = 0;
+  u32x4 wa[TR], wb[TR];
+  if (tile < ntiles) {
+    issue(wa, tile, 0);
+    while (true) {
+      int t1 = tile, j1 = j;
+      advance(t1, j1);
+      bool more = t1 < ntiles;
+      if (more) issue(wb, t1, j1);
+      consume(wa, tile, j);
+      if (!more) break;
+      tile = t1;
+      j = j1;
+      advance(t1, j1);
+      more = t1 < ntiles;
+      if (more) issue(wa, t1, j1);
+      consume(wb, tile, j);
+      if (!more) break;
+      tile = t1;
+      j = j1;
+    }
+  }
+
+  if (lane == 0) {
+#pragma unroll
+    for (int m = 0; m < M; ++m) s_key[wave][m] = pack_key(best[m], bidx[m]);
+  }
+  __syncthreads();
+  if (wave != 0) return;
+  unsigned long long key = 0ull;
+  if (lane < M) {
+#pragma unroll
+    for (int w = 0; w < WV; ++w) key = s_key[w][lane] > key ? s_key[w][lane] : key;
+  }
+  publish_workgroup(key, lane, M, 0, slots);
 }
 
 // ---------------------------------------------------------------------------
@@ -322,12 +484,10 @@ proj_argmax_valu(const uint16_t* __restrict__ h, const uint16_t* __restrict__ W,
 // bytes per instruction.  A = 16 head rows, B = 16 hidden rows (columns past
 // the last hidden row repeat it and are ignored), D = their logits, summed
 // over k inside the matrix core.
-template <int NT, int TM>
+template <int NT, int TM, int SB>
 __global__ void __launch_bounds__(kMfmaThreads)
 proj_argmax_mfma(const uint16_t* __restrict__ h, const uint16_t* __restrict__ W, int R, int K,
-                 int m_base, int mp, const int32_t* __restrict__ d2t,
-                 int32_t* __restrict__ out_id, float* __restrict__ out_logit,
-                 unsigned long long* __restrict__ keys, unsigned int* __restrict__ counter) {
+                 int m_base, int mp, unsigned long long* __restrict__ slots) {
   extern __shared__ u32x4 h_lds[];  // [mp][row_chunks], zero past K
   __shared__ unsigned long long s_key[LMH_MFMA_WAVES][32];
   const int lane = threadIdx.x & 63;
@@ -366,47 +526,49 @@ proj_argmax_mfma(const uint16_t* __restrict__ h, const uint16_t* __restrict__ W,
   const uint32_t row_bytes = (uint32_t)K * 2u;
   const int tile_rows = 16 * TM;
   const int ntiles = (R + tile_rows - 1) / tile_rows;
-  for (int tile = blockIdx.x * LMH_MFMA_WAVES + wave; tile < ntiles;
-       tile += gridDim.x * LMH_MFMA_WAVES) {
+  const int nbatch = (steps + SB - 1) / SB;   // k-batches per tile
+  uint32_t vrow[TM];
+#pragma unroll
+  for (int t = 0; t < TM; ++t) vrow[t] = (uint32_t)(t * 16 + i16) * row_bytes + (uint32_t)g * 16u;
+
+  f32x4 acc[TM][NT];
+#pragma unroll
+  for (int t = 0; t < TM; ++t)
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) acc[t][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // Loads for k-batch `b` of `tile`: SB steps x TM row tiles, 16 B per lane.
+  auto issue = [&](u32x4 (&buf)[SB][TM], int tile, int b) {
     const int r0 = tile * tile_rows;
     const int live = min(tile_rows, R - r0);
     const __amdgpu_buffer_rsrc_t rs = make_rsrc(W + (size_t)r0 * K, (uint32_t)live * row_bytes);
-    uint32_t vrow[TM];
 #pragma unroll
-    for (int t = 0; t < TM; ++t) vrow[t] = (uint32_t)(t * 16 + i16) * row_bytes + (uint32_t)g * 16u;
-
-    f32x4 acc[TM][NT];
+    for (int sb = 0; sb < SB; ++sb) {
+      const int s = b * SB + sb;
+      const bool ok = s < steps && (s * 4 + g) < chunks;
 #pragma unroll
-    for (int t = 0; t < TM; ++t)
+      for (int t = 0; t < TM; ++t)
+        buf[sb][t] = load16<kPolicyMfma>(rs, ok ? vrow[t] + (uint32_t)s * 64u : kOobOffset);
+    }
+  };
+  auto consume = [&](const u32x4 (&buf)[SB][TM], int b) {
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt) acc[t][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-    for (int s0 = 0; s0 < steps; s0 += LMH_MFMA_SB) {
-      u32x4 a[LMH_MFMA_SB][TM];
+    for (int sb = 0; sb < SB; ++sb) {
+      const int s = b * SB + sb;
+      if (s < steps) {
 #pragma unroll
-      for (int sb = 0; sb < LMH_MFMA_SB; ++sb) {
-        const int s = s0 + sb;
-        const bool ok = s < steps && (s * 4 + g) < chunks;
+        for (int nt = 0; nt < NT; ++nt) {
+          const u32x4 bf = bptr[nt][s * 4];
 #pragma unroll
-        for (int t = 0; t < TM; ++t) a[sb][t] = load16(rs, ok ? vrow[t] + (uint32_t)s * 64u : kOobOffset);
-      }
-#pragma unroll
-      for (int sb = 0; sb < LMH_MFMA_SB; ++sb) {
-        const int s = s0 + sb;
-        if (s < steps) {
-#pragma unroll
-          for (int nt = 0; nt < NT; ++nt) {
-            const u32x4 b = bptr[nt][s * 4];
-#pragma unroll
-            for (int t = 0; t < TM; ++t)
-              acc[t][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                  __builtin_bit_cast(bf16x8, a[sb][t]), __builtin_bit_cast(bf16x8, b), acc[t][nt], 0,
-                  0, 0);
-          }
+          for (int t = 0; t < TM; ++t)
+            acc[t][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                __builtin_bit_cast(bf16x8, buf[sb][t]), __builtin_bit_cast(bf16x8, bf), acc[t][nt], 0, 0, 0);
         }
       }
     }
-
+  };
+  auto finish_tile = [&](int tile) {
+    const int r0 = tile * tile_rows;
 #pragma unroll
     for (int t = 0; t < TM; ++t)
 #pragma unroll
@@ -417,6 +579,41 @@ proj_argmax_mfma(const uint16_t* __restrict__ h, const uint16_t* __restrict__ W,
           for (int nt = 0; nt < NT; ++nt) take_best(acc[t][nt][v], r, best[nt], bidx[nt]);
         }
       }
+#pragma unroll
+    for (int t = 0; t < TM; ++t)
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) acc[t][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  };
+
+  // The wave walks (tile, batch) pairs in order; the loads of the next pair
+  // are in flight while the current pair feeds the matrix cores.
+  const int tstride = gridDim.x * LMH_MFMA_WAVES;
+  int tile = blockIdx.x * LMH_MFMA_WAVES + wave;
+  int b = 0;
+  u32x4 bufa[SB][TM], bufb[SB][TM];
+  if (tile < ntiles) {
+    issue(bufa, tile, 0);
+    while (true) {
+      int nt_ = tile, nb_ = b + 1;
+      if (nb_ == nbatch) { nb_ = 0; nt_ += tstride; }
+      bool more = nt_ < ntiles;
+      if (more) issue(bufb, nt_, nb_);
+      consume(bufa, b);
+      if (b == nbatch - 1) finish_tile(tile);
+      if (!more) break;
+      tile = nt_;
+      b = nb_;
+      nt_ = tile;
+      nb_ = b + 1;
+      if (nb_ == nbatch) { nb_ = 0; nt_ += tstride; }
+      more = nt_ < ntiles;
+      if (more) issue(bufa, nt_, nb_);
+      consume(bufb, b);
+      if (b == nbatch - 1) finish_tile(tile);
+      if (!more) break;
+      tile = nt_;
+      b = nb_;
+    }
   }
 
   // fold the four lanes (g = 0..3) that hold the same hidden row
@@ -440,7 +637,7 @@ proj_argmax_mfma(const uint16_t* __restrict__ h, const uint16_t* __restrict__ W,
 #pragma unroll
     for (int w = 0; w < LMH_MFMA_WAVES; ++w) key = s_key[w][lane] > key ? s_key[w][lane] : key;
   }
-  finish_workgroup(key, lane, mp, m_base, d2t, out_id, out_logit, keys, counter);
+  publish_workgroup(key, lane, mp, m_base, slots);
 }
 
 // ---------------------------------------------------------------------------
@@ -522,7 +719,7 @@ int resident_per_cu(const void* f, int threads, size_t lds, int* out) {
 int chunks_per_lane(int64_t K) { return (int)((K / 8 + 63) / 64); }
 
 bool valu_ok(int64_t M, int64_t K) {
-  return M >= 1 && M <= 4 && k_ok(K) && M * chunks_per_lane(K) <= kValuMaxChunksTimesM;
+  return M >= 1 && M <= kValuMaxM && k_ok(K) && M * chunks_per_lane(K) <= kValuMaxChunksTimesM;
 }
 
 int mfma_row_bytes(int64_t K) { return (int)((((K + 31) / 32) * 4 + 1) * 16); }
@@ -532,64 +729,98 @@ int mfma_rows_per_pass(int64_t K) {
   return std::min<int64_t>(LMH_MAX_M, kMfmaLdsBudget / mfma_row_bytes(K));
 }
 
-typedef void (*valu_fn)(const uint16_t*, const uint16_t*, int, int, const int32_t*, int32_t*, float*,
-                        unsigned long long*, unsigned int*);
+typedef void (*valu_fn)(const uint16_t*, const uint16_t*, int, int, unsigned long long*);
 
-template <int M, int CPL>
-valu_fn valu_entry() {
+// One VALU launch shape: kernel, waves per workgroup, head rows a wave takes
+// per step, LDS bytes.  The choice per M comes from measurement on MI355X
+// (full 248,320 x 2,560 head): M = 1 streams fastest in 4-row tiles; M = 2..4
+// in row order with one 4-wave workgroup per CU; M = 5..8 need the 256-VGPR
+// budget of 8-wave workgroups.
+struct ValuPlan {
+  valu_fn fn = nullptr;
+  int waves = 0;
+  int rows_per_wave = 0;
+  size_t lds = 0;
+};
+
+template <int M, int CPL, int WV>
+void row_plan(ValuPlan& p) {
   if constexpr (M * CPL <= kValuMaxChunksTimesM) {
     // rows per step: keep each of the two row buffers at <= 10 chunks/lane
-    constexpr int U = CPL * LMH_VALU_ROWS <= 10 ? LMH_VALU_ROWS : (CPL <= 10 ? 10 / CPL : 1);
-    return proj_argmax_valu<M, CPL, (U < 1 ? 1 : U)>;
-  } else {
-    return nullptr;
+    constexpr int U0 = CPL * LMH_VALU_ROWS <= 10 ? LMH_VALU_ROWS : (CPL <= 10 ? 10 / CPL : 1);
+    constexpr int U = U0 < 1 ? 1 : U0;
+    p.fn = proj_argmax_valu<M, CPL, U, WV>;
+    p.waves = WV;
+    p.rows_per_wave = U;
+    p.lds = 0;
   }
 }
 
 template <int M, int... C>
-valu_fn valu_pick_cpl(int cpl, std::integer_sequence<int, C...>) {
-  valu_fn f = nullptr;
-  ((cpl == C + 1 ? (f = valu_entry<M, C + 1>(), 0) : 0), ...);
-  return f;
+void row_plan_cpl(ValuPlan& p, int cpl, std::integer_sequence<int, C...>) {
+  constexpr int WV = M <= 4 ? LMH_VALU_WAVES : 2 * LMH_VALU_WAVES;
+  ((cpl == C + 1 ? (row_plan<M, C + 1, WV>(p), 0) : 0), ...);
 }
 
-valu_fn valu_kernel(int M, int cpl) {
+ValuPlan valu_plan(int M, int K) {
+  ValuPlan p;
+  const int cpl = chunks_per_lane(K);
+  if (M == 1 && LMH_VALU_TILE_ROWS > 0) {
+    p.fn = proj_argmax_valu_tiled<1, LMH_VALU_TILE_ROWS, LMH_VALU_WAVES>;
+    p.waves = LMH_VALU_WAVES;
+    p.rows_per_wave = LMH_VALU_TILE_ROWS;
+    p.lds = (size_t)cpl * 64 * 16;
+    return p;
+  }
   using seq = std::make_integer_sequence<int, 16>;
   switch (M) {
-    case 1: return valu_pick_cpl<1>(cpl, seq{});
-    case 2: return valu_pick_cpl<2>(cpl, seq{});
-    case 3: return valu_pick_cpl<3>(cpl, seq{});
-    case 4: return valu_pick_cpl<4>(cpl, seq{});
-    default: return nullptr;
+    case 1: row_plan_cpl<1>(p, cpl, seq{}); break;
+    case 2: row_plan_cpl<2>(p, cpl, seq{}); break;
+    case 3: row_plan_cpl<3>(p, cpl, seq{}); break;
+    case 4: row_plan_cpl<4>(p, cpl, seq{}); break;
+    case 5: row_plan_cpl<5>(p, cpl, seq{}); break;
+    case 6: row_plan_cpl<6>(p, cpl, seq{}); break;
+    case 7: row_plan_cpl<7>(p, cpl, seq{}); break;
+    case 8: row_plan_cpl<8>(p, cpl, seq{}); break;
+    default: break;
   }
+  return p;
+}
+
+int launch_finalize(unsigned long long* slots, int nslots, int m_base, int mcount, const int32_t* d2t,
+                    int32_t* out_id, float* out_logit, hipStream_t stream) {
+  hipLaunchKernelGGL(finalize_argmax, dim3(mcount), dim3(256), 0, stream, slots, nslots, m_base, d2t, out_id,
+                     out_logit);
+  const hipError_t e = hipGetLastError();
+  return e == hipSuccess ? LMH_OK : hip_fail(e, "launch finalize_argmax");
+}
+
+int clamp_grid(int64_t need, int cus, int per_cu) {
+  return (int)std::max<int64_t>(1, std::min<int64_t>({need, (int64_t)cus * per_cu, (int64_t)kMaxGrid}));
 }
 
 int launch_valu(const uint16_t* h, int M, int K, const uint16_t* W, int R, const int32_t* d2t,
-                int32_t* out_id, float* out_logit, unsigned long long* keys, unsigned int* counter,
-                hipStream_t stream) {
-  valu_fn f = valu_kernel(M, chunks_per_lane(K));
-  if (!f) return LMH_EINVAL;
+                int32_t* out_id, float* out_logit, unsigned long long* slots, hipStream_t stream) {
+  const ValuPlan p = valu_plan(M, K);
+  if (!p.fn) return LMH_EINVAL;
   int cus = 0;
   int st = cu_count(&cus);
   if (st != LMH_OK) return st;
   int per_cu = 0;
-  st = resident_per_cu((const void*)f, kValuThreads, 0, &per_cu);
+  st = resident_per_cu((const void*)p.fn, 64 * p.waves, p.lds, &per_cu);
   if (st != LMH_OK) return st;
-  const int64_t rows_per_wg = (int64_t)kValuWaves * LMH_VALU_ROWS;
-  const int64_t need = (R + rows_per_wg - 1) / rows_per_wg;
-  const int grid = (int)std::max<int64_t>(
-      1, std::min<int64_t>(need, (int64_t)cus * std::min(per_cu, LMH_VALU_WG_PER_CU)));
-  hipLaunchKernelGGL(f, dim3(grid), dim3(kValuThreads), 0, stream, h, W, R, K, d2t, out_id, out_logit,
-                     keys, counter);
+  const int64_t rows_per_wg = (int64_t)p.waves * p.rows_per_wave;
+  const int grid = clamp_grid((R + rows_per_wg - 1) / rows_per_wg, cus, std::min(per_cu, LMH_VALU_WG_PER_CU));
+  hipLaunchKernelGGL(p.fn, dim3(grid), dim3(64 * p.waves), p.lds, stream, h, W, R, K, slots);
   const hipError_t e = hipGetLastError();
-  return e == hipSuccess ? LMH_OK : hip_fail(e, "launch proj_argmax_valu");
+  if (e != hipSuccess) return hip_fail(e, "launch proj_argmax_valu");
+  return launch_finalize(slots, grid, 0, M, d2t, out_id, out_logit, stream);
 }
 
 template <int NT>
 int launch_mfma_nt(const uint16_t* h, int K, int m_base, int mp, const uint16_t* W, int R,
-                   const int32_t* d2t, int32_t* out_id, float* out_logit, unsigned long long* keys,
-                   unsigned int* counter, int cus, hipStream_t stream) {
-  auto f = proj_argmax_mfma<NT, LMH_MFMA_TM>;
+                   unsigned long long* slots, int cus, hipStream_t stream, int* grid_out) {
+  auto f = proj_argmax_mfma<NT, LMH_MFMA_TM, LMH_MFMA_SB>;
   const size_t lds = (size_t)mp * mfma_row_bytes(K);
   static bool attr_done = false;  // one-time kernel attribute, same value every call
   if (!attr_done) {
@@ -605,17 +836,16 @@ int launch_mfma_nt(const uint16_t* h, int K, int m_base, int mp, const uint16_t*
   if (st != LMH_OK) return st;
   const int64_t tile_rows = 16 * LMH_MFMA_TM;
   const int64_t tiles = (R + tile_rows - 1) / tile_rows;
-  const int64_t need = (tiles + LMH_MFMA_WAVES - 1) / LMH_MFMA_WAVES;
-  const int grid = (int)std::max<int64_t>(1, std::min<int64_t>(need, (int64_t)cus * per_cu));
-  hipLaunchKernelGGL(f, dim3(grid), dim3(kMfmaThreads), lds, stream, h, W, R, K, m_base, mp, d2t,
-                     out_id, out_logit, keys, counter);
+  const int grid = clamp_grid((tiles + LMH_MFMA_WAVES - 1) / LMH_MFMA_WAVES, cus, per_cu);
+  hipLaunchKernelGGL(f, dim3(grid), dim3(kMfmaThreads), lds, stream, h, W, R, K, m_base, mp, slots);
   const hipError_t e = hipGetLastError();
-  return e == hipSuccess ? LMH_OK : hip_fail(e, "launch proj_argmax_mfma");
+  if (e != hipSuccess) return hip_fail(e, "launch proj_argmax_mfma");
+  *grid_out = grid;
+  return LMH_OK;
 }
 
 int launch_mfma(const uint16_t* h, int M, int K, const uint16_t* W, int R, const int32_t* d2t,
-                int32_t* out_id, float* out_logit, unsigned long long* keys, unsigned int* counter,
-                hipStream_t stream) {
+                int32_t* out_id, float* out_logit, unsigned long long* slots, hipStream_t stream) {
   int cus = 0;
   int st = cu_count(&cus);
   if (st != LMH_OK) return st;
@@ -624,8 +854,11 @@ int launch_mfma(const uint16_t* h, int M, int K, const uint16_t* W, int R, const
   const int per = (M + passes - 1) / passes;
   for (int m0 = 0; m0 < M; m0 += per) {
     const int mp = std::min(per, M - m0);
-    st = mp <= 16 ? launch_mfma_nt<1>(h, K, m0, mp, W, R, d2t, out_id, out_logit, keys, counter, cus, stream)
-                  : launch_mfma_nt<2>(h, K, m0, mp, W, R, d2t, out_id, out_logit, keys, counter, cus, stream);
+    int grid = 0;
+    st = mp <= 16 ? launch_mfma_nt<1>(h, K, m0, mp, W, R, slots, cus, stream, &grid)
+                  : launch_mfma_nt<2>(h, K, m0, mp, W, R, slots, cus, stream, &grid);
+    if (st != LMH_OK) return st;
+    st = launch_finalize(slots, grid, m0, mp, d2t, out_id, out_logit, stream);
     if (st != LMH_OK) return st;
   }
   return LMH_OK;
@@ -643,12 +876,10 @@ int project(const uint16_t* h, int64_t M, int64_t K, const uint16_t* W, int64_t 
   if (path != LMH_PATH_VALU && path != LMH_PATH_MFMA) return LMH_EINVAL;
   if (!workspace || !aligned16(workspace)) return LMH_EWORKSPACE;
   if (workspace_bytes < draft_project_workspace_bytes(M)) return LMH_EWORKSPACE;
-  auto* keys = static_cast<unsigned long long*>(workspace);
-  auto* counter = reinterpret_cast<unsigned int*>(static_cast<char*>(workspace) + 8 * LMH_MAX_M);
+  auto* slots = static_cast<unsigned long long*>(workspace);
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (path == LMH_PATH_VALU)
-    return launch_valu(h, (int)M, (int)K, W, (int)R, d2t, out_id, out_logit, keys, counter, s);
-  return launch_mfma(h, (int)M, (int)K, W, (int)R, d2t, out_id, out_logit, keys, counter, s);
+  if (path == LMH_PATH_VALU) return launch_valu(h, (int)M, (int)K, W, (int)R, d2t, out_id, out_logit, slots, s);
+  return launch_mfma(h, (int)M, (int)K, W, (int)R, d2t, out_id, out_logit, slots, s);
 }
 
 }  // namespace
@@ -682,12 +913,12 @@ int lmhead_trim(const uint16_t* W, int64_t N, int64_t K, const int32_t* ids, int
 }
 
 size_t draft_project_workspace_bytes(int64_t M) {
-  return (M >= 1 && M <= LMH_MAX_M) ? (size_t)kWorkspaceBytes : 0;
+  return (M >= 1 && M <= LMH_MAX_M) ? (size_t)M * kMaxGrid * sizeof(unsigned long long) : 0;
 }
 
 int draft_project_auto_path(int64_t M, int64_t K) {
   if (M < 1 || M > LMH_MAX_M || !k_ok(K)) return -1;
-  return valu_ok(M, K) ? LMH_PATH_VALU : LMH_PATH_MFMA;
+  return (M <= LMH_VALU_AUTO_MAX_M && valu_ok(M, K)) ? LMH_PATH_VALU : LMH_PATH_MFMA;
 }
 
 int draft_project_argmax(const uint16_t* h, int64_t M, int64_t K, const uint16_t* W, int64_t R,

@@ -20,7 +20,7 @@ __all__ = [
     "LMH_PATH_MFMA", "lmhead_trim", "draft_project_workspace_bytes", "draft_project_argmax",
     "draft_project_argmax_path", "draft_project_auto_path", "lmhead_status_str",
     "lmhead_last_error", "lmhead_bench_sink_words", "lmhead_bench_stream_read",
-    "lmhead_bench_copy", "new_workspace",
+    "lmhead_bench_copy", "new_workspace", "read_id_list",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "liblmhead.so")
@@ -130,10 +130,10 @@ def draft_project_auto_path(M: int, K: int) -> int:
     return int(lib().draft_project_auto_path(M, K))
 
 
-def new_workspace(device=None) -> torch.Tensor:
-    """A zero-filled workspace for any M <= LMH_MAX_M."""
-    nbytes = draft_project_workspace_bytes(LMH_MAX_M)
-    return torch.zeros(nbytes, dtype=torch.uint8, device=device or "cuda")
+def new_workspace(device=None, M: int = LMH_MAX_M) -> torch.Tensor:
+    """A workspace for calls with up to M hidden rows (contents irrelevant)."""
+    nbytes = draft_project_workspace_bytes(M)
+    return torch.empty(nbytes, dtype=torch.uint8, device=device or "cuda")
 
 
 _ws_cache: dict = {}
@@ -188,6 +188,16 @@ def draft_project_argmax(h, W, d2t=None, out_id=None, out_logit=None, workspace=
     """draft_project_argmax_path with the library's own kernel choice."""
     return draft_project_argmax_path(h, W, d2t, LMH_PATH_AUTO, out_id, out_logit, workspace,
                                      stream)
+
+
+def read_id_list(path: str):
+    """Token ids of a shortlist file: one integer id per line (blank lines
+    ignored), in file order -- the ranks / draft-vocabulary list format the
+    head is trimmed from at load.  Returns an int32 numpy array."""
+    import numpy as np
+    with open(path) as f:
+        vals = [int(tok) for tok in (line.strip() for line in f) if tok]
+    return np.asarray(vals, dtype=np.int32)
 
 
 def lmhead_status_str(code: int) -> str:
