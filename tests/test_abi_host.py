@@ -70,12 +70,13 @@ def test_auto_path(L):
     assert L.draft_project_auto_path(1, 2560) == L.LMH_PATH_VALU
     assert L.draft_project_auto_path(4, 2560) == L.LMH_PATH_VALU
     assert L.draft_project_auto_path(3, 2560) == L.LMH_PATH_VALU
-    assert L.draft_project_auto_path(5, 2560) == L.LMH_PATH_VALU
-    assert L.draft_project_auto_path(8, 2560) == L.LMH_PATH_VALU
+    assert L.draft_project_auto_path(5, 2560) == L.LMH_PATH_MFMA
+    assert L.draft_project_auto_path(8, 2560) == L.LMH_PATH_MFMA
     assert L.draft_project_auto_path(9, 2560) == L.LMH_PATH_MFMA
     assert L.draft_project_auto_path(24, 2560) == L.LMH_PATH_MFMA
     assert L.draft_project_auto_path(4, 8192) == L.LMH_PATH_MFMA
     assert L.draft_project_auto_path(2, 8192) == L.LMH_PATH_VALU
+    assert L.draft_project_auto_path(4, 4096) == L.LMH_PATH_VALU
     assert L.draft_project_auto_path(1, 8192) == L.LMH_PATH_VALU
     for m, k in ((0, 2560), (33, 2560), (1, 12), (1, 0), (1, 8200)):
         assert L.draft_project_auto_path(m, k) == -1
@@ -127,3 +128,18 @@ def test_read_id_list(L, tmp_path):
     p.write_text("17\n3\n\n248319\n0\n")
     ids = L.read_id_list(str(p))
     assert ids.dtype.name == "int32" and ids.tolist() == [17, 3, 248319, 0]
+
+
+def test_build_has_no_scratch_spills():
+    """Every kernel of the default build keeps its state in registers/LDS."""
+    from vocab_shortlisted_lm_amd import build
+    import tempfile
+    with tempfile.TemporaryDirectory() as d:
+        out = os.path.join(d, "lib.so")
+        proc = subprocess.run(build.command(out), capture_output=True, text=True)
+        assert proc.returncode == 0, proc.stderr[-2000:]
+        usage = build.kernel_resources(proc.stderr)
+    assert any("proj_argmax_valu_tiled" in k for k in usage)
+    assert any("proj_argmax_mfma_lds" in k for k in usage)
+    spills = {k: v["ScratchSize"] for k, v in usage.items() if v.get("ScratchSize", 0)}
+    assert not spills, spills

@@ -11,6 +11,7 @@ from __future__ import annotations
 
 import argparse
 import os
+import re
 import shutil
 import subprocess
 import sys
@@ -31,8 +32,9 @@ def hipcc() -> str:
 
 
 def command(out: str = LIB, defines: list[str] | None = None) -> list[str]:
-    cmd = [hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-shared", "-fPIC",
+    cmd = [hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++20", "-shared", "-fPIC",
            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+           "-Rpass-analysis=kernel-resource-usage", "-fno-caret-diagnostics",
            "-Wall", "-Wno-unused-function", "-I", INCLUDE]
     for d in defines or []:
         cmd.append("-D" + d)
@@ -40,15 +42,42 @@ def command(out: str = LIB, defines: list[str] | None = None) -> list[str]:
     return cmd
 
 
-def build(out: str = LIB, defines: list[str] | None = None, verbose: bool = False) -> str:
-    """Compile the library; returns its path.  Raises on a compiler error."""
+def kernel_resources(stderr: str) -> dict[str, dict[str, int]]:
+    """Per-kernel resource usage from the compiler's kernel-resource-usage
+    remarks: {mangled name: {"ScratchSize": bytes/lane, "VGPRs": n, ...}}."""
+    usage: dict[str, dict[str, int]] = {}
+    name = None
+    for line in stderr.splitlines():
+        m = re.search(r"remark: Function Name: (\S+)", line)
+        if m:
+            name = m.group(1)
+            usage[name] = {}
+            continue
+        m = re.search(r"remark:\s+(\w+)(?: \[[^\]]*\])?: (\d+)", line)
+        if m and name:
+            usage[name][m.group(1)] = int(m.group(2))
+    return usage
+
+
+def build(out: str = LIB, defines: list[str] | None = None, verbose: bool = False,
+          allow_scratch: bool = False) -> str:
+    """Compile the library; returns its path.  Raises on a compiler error,
+    and -- unless allow_scratch -- if any kernel spills to scratch memory
+    (a spill in a streaming kernel costs far more than the register it saves)."""
     tmp = out + ".tmp"
     cmd = command(tmp, defines)
     proc = subprocess.run(cmd, capture_output=True, text=True)
     noise = "is not a recognized feature for this target"
-    err = "\n".join(l for l in proc.stderr.splitlines() if noise not in l)
+    lines = [l for l in proc.stderr.splitlines() if noise not in l]
+    err = "\n".join(l for l in lines if "kernel-resource-usage" not in l)
     if proc.returncode != 0:
         raise RuntimeError("hipcc failed:\n" + " ".join(cmd) + "\n" + err)
+    spills = {k: v["ScratchSize"] for k, v in kernel_resources(proc.stderr).items()
+              if v.get("ScratchSize", 0) > 0}
+    if spills and not allow_scratch:
+        os.remove(tmp)
+        raise RuntimeError("kernels spill to scratch: " + ", ".join(f"{k} ({v} B/lane)"
+                                                                   for k, v in spills.items()))
     if verbose and err.strip():
         print(err, file=sys.stderr)
     os.replace(tmp, out)
@@ -59,8 +88,9 @@ def main() -> None:
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("-D", dest="defines", action="append", default=[])
     ap.add_argument("-o", dest="out", default=LIB)
+    ap.add_argument("--allow-scratch", action="store_true")
     a = ap.parse_args()
-    print(build(a.out, a.defines, verbose=True))
+    print(build(a.out, a.defines, verbose=True, allow_scratch=a.allow_scratch))
 
 
 if __name__ == "__main__":

@@ -2,24 +2,28 @@
 // C ABI declared in include/lmhead.h.
 //
 // What runs on the device:
-//   gather_rows         load-time shortlist gather, W_trim[i] = W[ids[i]]
-//                       ("Two ways to run it", zone-1.cobraproject.com
-//                       "Masked MTP drafts": the head is trimmed at load).
-//   proj_argmax_valu    M <= 4 hidden rows held in registers; one wave per
-//                       head row, 16-byte buffer loads, packed bf16 dot
-//                       products with fp32 accumulation, DPP row reduction.
-//   proj_argmax_mfma    hidden rows staged in LDS; 16 (or 32) head rows per
-//                       wave tile on 16x16x32 bf16 matrix-core instructions,
-//                       so no cross-lane reduction per row is needed.
-// Both projection kernels fuse the argmax: each wave keeps a running
+//   gather_rows             load-time shortlist gather, W_trim[i] = W[ids[i]]
+//                           ("Two ways to run it", zone-1.cobraproject.com
+//                           "Masked MTP drafts": the head is trimmed at load).
+//   proj_argmax_valu_tiled  M = 1: a wave walks tiles of 4 head rows in 1 KiB
+//                           column stripes; packed bf16 dot products with
+//                           fp32 accumulation, DPP reduction per row.
+//   proj_argmax_valu        M = 2..8: one wave per head row, hidden rows in
+//                           registers, two rows per step double-buffered.
+//   proj_argmax_mfma_lds    M > 4 (default): coalesced 16-byte loads of
+//                           16-row tiles, transposed through a wave-private
+//                           LDS stage into 16x16x32 bf16 matrix-core operands;
+//                           hidden rows staged in LDS.
+// Every projection kernel fuses the argmax: each wave keeps a running
 // (logit, row) per hidden row as a 64-bit key, a workgroup folds its waves
 // through LDS and stores one key per hidden row into its own workspace slot.
-//   finalize_argmax     one workgroup per hidden row folds the slots, decodes
-//                       the winner and maps it through d2t (EAGLE-3 style
-//                       draft-to-target ids, "Two ways to run it").
+//   finalize_argmax         one workgroup per hidden row folds the slots,
+//                           decodes the winner and maps it through d2t
+//                           (EAGLE-3 style draft-to-target ids, "Two ways to
+//                           run it").
 // The two kernels are ordered by the stream; no atomics, fences or memsets
-// are needed, and the workspace needs no initial contents.
-// The argmax is reduced locally instead of gathering logits, the change the
+// are needed, and the workspace needs no initial contents.  The argmax is
+// reduced where it is computed instead of gathering logits, the change the
 // fair re-run on krisbailey.com/articles/shortlist-mtp credits ("Re-running
 // the comparison fairly").
 //
@@ -57,15 +61,6 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 #ifndef LMH_VALU_WG_PER_CU
 #define LMH_VALU_WG_PER_CU 1     // cap on resident workgroups per CU (VALU path)
 #endif
-#ifndef LMH_MFMA_WAVES
-#define LMH_MFMA_WAVES 8         // waves per workgroup (matrix-core path)
-#endif
-#ifndef LMH_MFMA_TM
-#define LMH_MFMA_TM 1            // 16-row tiles per wave step (matrix-core path)
-#endif
-#ifndef LMH_MFMA_SB
-#define LMH_MFMA_SB 4            // k-steps of loads issued together
-#endif
 #ifndef LMH_VALU_TILE_ROWS
 #define LMH_VALU_TILE_ROWS 4     // rows per tile of the tiled VALU kernel (M = 1); 0 = row order
 #endif
@@ -73,37 +68,32 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 #define LMH_VALU_PREFETCH 1      // double-buffer rows in registers (VALU path)
 #endif
 #ifndef LMH_NT_LOADS
-#define LMH_NT_LOADS 1           // non-temporal W loads (VALU path)
+#define LMH_NT_LOADS 1           // non-temporal W loads
 #endif
-#ifndef LMH_MFMA_NT_LOADS
-#define LMH_MFMA_NT_LOADS 0      // non-temporal W loads (matrix-core path)
+#ifndef LMH_MFMA_LDS_SB
+#define LMH_MFMA_LDS_SB 4        // k-steps per batch of the coalesced matrix-core kernel
+#endif
+#ifndef LMH_MFMA_RING
+#define LMH_MFMA_RING 3          // batches in the register ring of the coalesced matrix-core kernel
 #endif
 
 #ifndef LMH_VALU_WAVES
 #define LMH_VALU_WAVES 4          // waves per workgroup (VALU path)
 #endif
-constexpr int kMfmaThreads = 64 * LMH_MFMA_WAVES;
-// LDS for staged hidden rows in the matrix-core path.  At most one
-// workgroup of that path per CU when it is full; the rest of the 160 KiB is
-// left for the key exchange.
-constexpr int kMfmaLdsBudget = 152 * 1024;
 constexpr int kValuMaxM = 8;
 constexpr int kValuMaxChunksTimesM = 40;   // register budget: 160 VGPRs of h
 #ifndef LMH_VALU_AUTO_MAX_M
-#define LMH_VALU_AUTO_MAX_M 8     // largest M the default choice sends to the VALU path
+#define LMH_VALU_AUTO_MAX_M 4     // largest M the default choice sends to the VALU path
 #endif
 // Workgroup slots per hidden row in the workspace; grids are clamped to it.
 constexpr int kMaxGrid = 1024;
 constexpr int64_t kMaxRows = (int64_t)1 << 30;  // keeps row arithmetic in int range
 constexpr uint32_t kBufferWord3 = 0x00020000u;  // gfx9 raw buffer, 32-bit data
 constexpr uint32_t kOobOffset = 0x80000000u;    // any offset >= num_records reads 0
-// cache-policy operand of buffer loads: bit 1 = nt (streaming).  The VALU
-// path reads whole 1 KiB row pieces per instruction and streams best with
-// nt; the matrix-core path reads 64-byte pieces of 16 rows per instruction,
-// whose 128-byte lines are completed by the next k-step, so it keeps them
-// cacheable.
-constexpr int kPolicyValu = LMH_NT_LOADS ? 2 : 0;
-constexpr int kPolicyMfma = LMH_MFMA_NT_LOADS ? 2 : 0;
+// cache-policy operand of buffer loads: bit 1 = nt (streaming).  Every
+// projection kernel reads whole row pieces per instruction and streams W
+// once, which HBM serves best as non-temporal reads.
+constexpr int kPolicyStream = LMH_NT_LOADS ? 2 : 0;
 
 // ---------------------------------------------------------------------------
 // device helpers
@@ -113,7 +103,7 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
                                            (int)kBufferWord3);
 }
 
-template <int POLICY = kPolicyValu>
+template <int POLICY = kPolicyStream>
 __device__ __forceinline__ u32x4 load16(__amdgpu_buffer_rsrc_t r, uint32_t voff) {
   return __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, 0, POLICY);
 }
@@ -474,22 +464,27 @@ proj_argmax_valu_tiled(const uint16_t* __restrict__ h, const uint16_t* __restric
 }
 
 // ---------------------------------------------------------------------------
-// matrix-core path: hidden rows in LDS, 16x16x32 bf16 MFMA tiles
+// matrix-core path
 // ---------------------------------------------------------------------------
-// v_mfma_f32_16x16x32_bf16 computes D[i][j] += sum_k A[i][k] B[k][j] with
-// lane l supplying A[l%16][8(l/16) .. +8] and B[8(l/16) .. +8][l%16], and
-// holding D[4(l/16) + v][l%16], v < 4.  The k order inside a dot product is
-// free, so k-slot group g = l/16 of step s is mapped to the 16-byte chunk
-// 4s + g of the row: the four lanes of one head row read 64 contiguous
-// bytes per instruction.  A = 16 head rows, B = 16 hidden rows (columns past
-// the last hidden row repeat it and are ignored), D = their logits, summed
-// over k inside the matrix core.
-template <int NT, int TM, int SB>
-__global__ void __launch_bounds__(kMfmaThreads)
-proj_argmax_mfma(const uint16_t* __restrict__ h, const uint16_t* __restrict__ W, int R, int K,
-                 int m_base, int mp, unsigned long long* __restrict__ slots) {
-  extern __shared__ u32x4 h_lds[];  // [mp][row_chunks], zero past K
-  __shared__ unsigned long long s_key[LMH_MFMA_WAVES][32];
+// Matrix-core path with coalesced loads.  The MFMA operand layout wants the
+// 16 lanes of a k-group to hold 16 different head rows, which makes every
+// load instruction touch 16 rows x 64 bytes; HBM streams such loads at
+// about 6 TB/s against 7 TB/s for whole row pieces.  Here each wave loads a
+// batch of its 16-row tile with coalesced instructions (lane l: chunk l % BC
+// of row l / BC, BC = 4 SB chunks = SB k-steps), writes it to a private LDS
+// stage, and reads the A operands back in MFMA layout.  Hidden rows are in
+// LDS as in proj_argmax_mfma.  The stage is private to the wave, so the
+// exchange needs only wave-level ordering, not a workgroup barrier.
+template <int NT, int SB, int WV, int D>
+__global__ void __launch_bounds__(64 * WV)
+proj_argmax_mfma_lds(const uint16_t* __restrict__ h, const uint16_t* __restrict__ W, int R, int K,
+                     int m_base, int mp, unsigned long long* __restrict__ slots) {
+  static_assert(SB == 4 || SB == 8 || SB == 16, "a load instruction covers whole row pieces");
+  constexpr int BC = 4 * SB;    // 16-byte chunks per row per batch
+  constexpr int SC = BC + 1;    // stage row stride in chunks (padded against bank conflicts)
+  constexpr int RPI = 64 / BC;  // rows per load instruction
+  extern __shared__ u32x4 lds[];  // [mp][row_chunks] hidden rows, then [WV][16][SC] stages
+  __shared__ unsigned long long s_key[WV][32];
   const int lane = threadIdx.x & 63;
   const int wave = wave_id();
   const int i16 = lane & 15;
@@ -497,22 +492,23 @@ proj_argmax_mfma(const uint16_t* __restrict__ h, const uint16_t* __restrict__ W,
   const int chunks = K >> 3;
   const int steps = (K + 31) >> 5;
   const int s4 = steps * 4;
-  const int row_chunks = s4 + 1;  // one chunk of padding per row spreads LDS banks
+  const int row_chunks = s4 + 1;
 
-  for (int i = threadIdx.x; i < mp * s4; i += kMfmaThreads) {
+  for (int i = threadIdx.x; i < mp * s4; i += 64 * WV) {
     const int m = i / s4;
     const int c = i - m * s4;
     u32x4 v = {0u, 0u, 0u, 0u};
     if (c < chunks) v = *reinterpret_cast<const u32x4*>(h + (size_t)(m_base + m) * K + (size_t)c * 8);
-    h_lds[m * row_chunks + c] = v;
+    lds[m * row_chunks + c] = v;
   }
   __syncthreads();
 
+  u32x4* stage = lds + mp * row_chunks + wave * 16 * SC;
   const u32x4* bptr[NT];
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
     const int col = nt * 16 + i16;
-    bptr[nt] = h_lds + (col < mp ? col : mp - 1) * row_chunks + g;
+    bptr[nt] = lds + (col < mp ? col : mp - 1) * row_chunks + g;
   }
 
   float best[NT];
@@ -522,101 +518,122 @@ proj_argmax_mfma(const uint16_t* __restrict__ h, const uint16_t* __restrict__ W,
     best[nt] = 0.0f;
     bidx[nt] = -1;
   }
+  f32x4 acc[NT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   const uint32_t row_bytes = (uint32_t)K * 2u;
-  const int tile_rows = 16 * TM;
-  const int ntiles = (R + tile_rows - 1) / tile_rows;
-  const int nbatch = (steps + SB - 1) / SB;   // k-batches per tile
-  uint32_t vrow[TM];
-#pragma unroll
-  for (int t = 0; t < TM; ++t) vrow[t] = (uint32_t)(t * 16 + i16) * row_bytes + (uint32_t)g * 16u;
+  const int ntiles = (R + 15) >> 4;
+  const int nbatch = (steps + SB - 1) / SB;
+  const int lrow = lane / BC;  // row of this lane within a load instruction
+  const int lc = lane % BC;    // chunk of this lane within the batch
 
-  f32x4 acc[TM][NT];
+  uint32_t rowoff[SB];
 #pragma unroll
-  for (int t = 0; t < TM; ++t)
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) acc[t][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int q = 0; q < SB; ++q) rowoff[q] = (uint32_t)(q * RPI + lrow) * row_bytes;
 
-  // Loads for k-batch `b` of `tile`: SB steps x TM row tiles, 16 B per lane.
-  auto issue = [&](u32x4 (&buf)[SB][TM], int tile, int b) {
-    const int r0 = tile * tile_rows;
-    const int live = min(tile_rows, R - r0);
+  // Positions past the last tile get a descriptor with no records, so their
+  // loads read zero without touching memory (live is clamped at 0).
+  auto issue = [&](u32x4 (&buf)[SB], int tile, int b) {
+    const int r0 = tile < ntiles ? tile * 16 : 0;
+    const int live = tile < ntiles ? min(16, R - r0) : 0;
     const __amdgpu_buffer_rsrc_t rs = make_rsrc(W + (size_t)r0 * K, (uint32_t)live * row_bytes);
+    // Column offset of this lane, or an offset past num_records for chunks
+    // beyond K.  Selected once per batch so the loads themselves carry no
+    // condition (and stay countable for the wait counters).
+    const int cg = b * BC + lc;
+    const uint32_t cbase = cg < chunks ? (uint32_t)cg * 16u : kOobOffset;
 #pragma unroll
-    for (int sb = 0; sb < SB; ++sb) {
-      const int s = b * SB + sb;
-      const bool ok = s < steps && (s * 4 + g) < chunks;
+    for (int q = 0; q < SB; ++q) buf[q] = load16<kPolicyStream>(rs, cbase + rowoff[q]);
+  };
+  auto mma_step = [&](const u32x4& a, int s) {
 #pragma unroll
-      for (int t = 0; t < TM; ++t)
-        buf[sb][t] = load16<kPolicyMfma>(rs, ok ? vrow[t] + (uint32_t)s * 64u : kOobOffset);
+    for (int nt = 0; nt < NT; ++nt) {
+      const u32x4 bf = bptr[nt][s * 4];
+      acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                        __builtin_bit_cast(bf16x8, bf), acc[nt], 0, 0, 0);
     }
   };
-  auto consume = [&](const u32x4 (&buf)[SB][TM], int b) {
+  auto consume = [&](const u32x4 (&buf)[SB], int b) {
 #pragma unroll
-    for (int sb = 0; sb < SB; ++sb) {
-      const int s = b * SB + sb;
-      if (s < steps) {
+    for (int q = 0; q < SB; ++q) stage[(q * RPI + lrow) * SC + lc] = buf[q];
+    // lanes of this wave exchange data through the stage
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    if ((b + 1) * SB <= steps) {
+      // whole batch: all operand reads first, then the matrix instructions
+      u32x4 a[SB];
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt) {
-          const u32x4 bf = bptr[nt][s * 4];
+      for (int sb = 0; sb < SB; ++sb) a[sb] = stage[i16 * SC + 4 * sb + g];
 #pragma unroll
-          for (int t = 0; t < TM; ++t)
-            acc[t][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                __builtin_bit_cast(bf16x8, buf[sb][t]), __builtin_bit_cast(bf16x8, bf), acc[t][nt], 0, 0, 0);
-        }
+      for (int sb = 0; sb < SB; ++sb) mma_step(a[sb], b * SB + sb);
+    } else {
+#pragma unroll
+      for (int sb = 0; sb < SB; ++sb) {
+        const int s = b * SB + sb;
+        if (s < steps) mma_step(stage[i16 * SC + 4 * sb + g], s);
       }
     }
+    // the next batch overwrites the stage only after these reads
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   };
   auto finish_tile = [&](int tile) {
-    const int r0 = tile * tile_rows;
+    const int r0 = tile * 16;
 #pragma unroll
-    for (int t = 0; t < TM; ++t)
+    for (int v = 0; v < 4; ++v) {
+      const int r = r0 + 4 * g + v;
+      if (r < R) {
 #pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int r = r0 + t * 16 + 4 * g + v;
-        if (r < R) {
-#pragma unroll
-          for (int nt = 0; nt < NT; ++nt) take_best(acc[t][nt][v], r, best[nt], bidx[nt]);
-        }
+        for (int nt = 0; nt < NT; ++nt) take_best(acc[nt][v], r, best[nt], bidx[nt]);
       }
+    }
 #pragma unroll
-    for (int t = 0; t < TM; ++t)
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt) acc[t][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int nt = 0; nt < NT; ++nt) acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
   };
 
-  // The wave walks (tile, batch) pairs in order; the loads of the next pair
-  // are in flight while the current pair feeds the matrix cores.
-  const int tstride = gridDim.x * LMH_MFMA_WAVES;
-  int tile = blockIdx.x * LMH_MFMA_WAVES + wave;
-  int b = 0;
-  u32x4 bufa[SB][TM], bufb[SB][TM];
-  if (tile < ntiles) {
-    issue(bufa, tile, 0);
-    while (true) {
-      int nt_ = tile, nb_ = b + 1;
-      if (nb_ == nbatch) { nb_ = 0; nt_ += tstride; }
-      bool more = nt_ < ntiles;
-      if (more) issue(bufb, nt_, nb_);
-      consume(bufa, b);
-      if (b == nbatch - 1) finish_tile(tile);
-      if (!more) break;
-      tile = nt_;
-      b = nb_;
-      nt_ = tile;
-      nb_ = b + 1;
-      if (nb_ == nbatch) { nb_ = 0; nt_ += tstride; }
-      more = nt_ < ntiles;
-      if (more) issue(bufa, nt_, nb_);
-      consume(bufb, b);
-      if (b == nbatch - 1) finish_tile(tile);
-      if (!more) break;
-      tile = nt_;
-      b = nb_;
+  // The wave walks (tile, batch) pairs in order with a ring of D register
+  // buffers: D - 1 batches are in flight while one is transposed and fed to
+  // the matrix cores.  The loop is unrolled D times so ring slots are static.
+  const int tstride = gridDim.x * WV;
+  int ti = blockIdx.x * WV + wave, bi = 0;  // next pair to issue
+  int tc = ti, bc = 0;                      // next pair to consume
+  auto advance = [&](int& t, int& bb) {
+    if (++bb == nbatch) {
+      bb = 0;
+      t += tstride;
     }
+  };
+  // Number of (tile, batch) pairs this wave consumes.
+  const int my_tiles = tc < ntiles ? (ntiles - 1 - tc) / tstride + 1 : 0;
+  const int count = my_tiles * nbatch;
+  u32x4 ring[D][SB];
+#pragma unroll
+  for (int j = 0; j < D - 1; ++j) {
+    issue(ring[j], ti, bi);
+    advance(ti, bi);
   }
+  auto step = [&](auto jc) {
+    constexpr int j = decltype(jc)::value;
+    issue(ring[(j + D - 1) % D], ti, bi);
+    advance(ti, bi);
+    consume(ring[j], bc);
+    if (bc == nbatch - 1) finish_tile(tc);
+    advance(tc, bc);
+  };
+  int n = 0;
+  // steady state: every slot issues and consumes, no conditions on loads
+  for (; n + D <= count; n += D) {
+    [&]<int... J>(std::integer_sequence<int, J...>) { (step(std::integral_constant<int, J>{}), ...); }(
+        std::make_integer_sequence<int, D>{});
+  }
+  // last partial round
+  [&]<int... J>(std::integer_sequence<int, J...>) {
+    ((n + J < count ? (step(std::integral_constant<int, J>{}), 0) : 0), ...);
+  }(std::make_integer_sequence<int, D>{});
 
-  // fold the four lanes (g = 0..3) that hold the same hidden row
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
     unsigned long long k = pack_key(best[nt], bidx[nt]);
@@ -635,7 +652,7 @@ proj_argmax_mfma(const uint16_t* __restrict__ h, const uint16_t* __restrict__ W,
   unsigned long long key = 0ull;
   if (lane < mp) {
 #pragma unroll
-    for (int w = 0; w < LMH_MFMA_WAVES; ++w) key = s_key[w][lane] > key ? s_key[w][lane] : key;
+    for (int w = 0; w < WV; ++w) key = s_key[w][lane] > key ? s_key[w][lane] : key;
   }
   publish_workgroup(key, lane, mp, m_base, slots);
 }
@@ -724,10 +741,6 @@ bool valu_ok(int64_t M, int64_t K) {
 
 int mfma_row_bytes(int64_t K) { return (int)((((K + 31) / 32) * 4 + 1) * 16); }
 
-// hidden rows per launch of the matrix-core path
-int mfma_rows_per_pass(int64_t K) {
-  return std::min<int64_t>(LMH_MAX_M, kMfmaLdsBudget / mfma_row_bytes(K));
-}
 
 typedef void (*valu_fn)(const uint16_t*, const uint16_t*, int, int, unsigned long long*);
 
@@ -746,8 +759,9 @@ struct ValuPlan {
 template <int M, int CPL, int WV>
 void row_plan(ValuPlan& p) {
   if constexpr (M * CPL <= kValuMaxChunksTimesM) {
-    // rows per step: keep each of the two row buffers at <= 10 chunks/lane
-    constexpr int U0 = CPL * LMH_VALU_ROWS <= 10 ? LMH_VALU_ROWS : (CPL <= 10 ? 10 / CPL : 1);
+    // rows per step: keep each of the two row buffers at <= 10 chunks/lane,
+    // and one row per step once h alone takes more than 80 registers
+    constexpr int U0 = M * CPL > 20 ? 1 : (CPL * LMH_VALU_ROWS <= 10 ? LMH_VALU_ROWS : (CPL <= 10 ? 10 / CPL : 1));
     constexpr int U = U0 < 1 ? 1 : U0;
     p.fn = proj_argmax_valu<M, CPL, U, WV>;
     p.waves = WV;
@@ -817,31 +831,62 @@ int launch_valu(const uint16_t* h, int M, int K, const uint16_t* W, int R, const
   return launch_finalize(slots, grid, 0, M, d2t, out_id, out_logit, stream);
 }
 
-template <int NT>
-int launch_mfma_nt(const uint16_t* h, int K, int m_base, int mp, const uint16_t* W, int R,
-                   unsigned long long* slots, int cus, hipStream_t stream, int* grid_out) {
-  auto f = proj_argmax_mfma<NT, LMH_MFMA_TM, LMH_MFMA_SB>;
-  const size_t lds = (size_t)mp * mfma_row_bytes(K);
+constexpr int kLdsPerWorkgroup = 160 * 1024;
+
+// Hidden rows one launch of the coalesced matrix-core kernel can stage for
+// K, with `waves` waves (each with its own 16-row stage).
+int mfma_lds_rows_fit(int64_t K, int waves) {
+  const int64_t stage = (int64_t)waves * 16 * (4 * LMH_MFMA_LDS_SB + 1) * 16;
+  const int64_t fixed = stage + (int64_t)waves * 32 * 8 + 512;
+  const int64_t rows = (kLdsPerWorkgroup - fixed) / mfma_row_bytes(K);
+  return (int)std::max<int64_t>(0, std::min<int64_t>(LMH_MAX_M, rows));
+}
+
+template <typename F>
+int launch_persistent(F f, int threads, size_t lds, int64_t units, int units_per_wg, int cus, hipStream_t stream,
+                      const char* what, int* grid_out, const uint16_t* h, const uint16_t* W, int R, int K,
+                      int m_base, int mp, unsigned long long* slots) {
   static bool attr_done = false;  // one-time kernel attribute, same value every call
   if (!attr_done) {
     // Best effort: if the runtime does not take the attribute, the launch
     // itself reports an LDS request it cannot meet.
-    if (hipFuncSetAttribute((const void*)f, hipFuncAttributeMaxDynamicSharedMemorySize, kMfmaLdsBudget) !=
+    if (hipFuncSetAttribute((const void*)f, hipFuncAttributeMaxDynamicSharedMemorySize, kLdsPerWorkgroup) !=
         hipSuccess)
       (void)hipGetLastError();
     attr_done = true;
   }
   int per_cu = 0;
-  const int st = resident_per_cu((const void*)f, kMfmaThreads, lds, &per_cu);
+  const int st = resident_per_cu((const void*)f, threads, lds, &per_cu);
   if (st != LMH_OK) return st;
-  const int64_t tile_rows = 16 * LMH_MFMA_TM;
-  const int64_t tiles = (R + tile_rows - 1) / tile_rows;
-  const int grid = clamp_grid((tiles + LMH_MFMA_WAVES - 1) / LMH_MFMA_WAVES, cus, per_cu);
-  hipLaunchKernelGGL(f, dim3(grid), dim3(kMfmaThreads), lds, stream, h, W, R, K, m_base, mp, slots);
+  const int grid = clamp_grid((units + units_per_wg - 1) / units_per_wg, cus, per_cu);
+  hipLaunchKernelGGL(f, dim3(grid), dim3(threads), lds, stream, h, W, R, K, m_base, mp, slots);
   const hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return hip_fail(e, "launch proj_argmax_mfma");
+  if (e != hipSuccess) return hip_fail(e, what);
   *grid_out = grid;
   return LMH_OK;
+}
+
+// One pass of the matrix-core path over hidden rows [m_base, m_base + mp):
+// 8 waves per workgroup when the hidden rows and eight stages fit the LDS,
+// else 4; two 16-column tiles when mp > 16.
+int launch_mfma_pass(const uint16_t* h, int K, int m_base, int mp, const uint16_t* W, int R,
+                     unsigned long long* slots, int cus, hipStream_t stream, int* grid_out) {
+  constexpr int SB = LMH_MFMA_LDS_SB;
+  constexpr int D = LMH_MFMA_RING;
+  const size_t hbytes = (size_t)mp * mfma_row_bytes(K);
+  const int64_t tiles = (R + 15) / 16;
+  const bool eight = mp <= mfma_lds_rows_fit(K, 8);
+  const size_t lds = hbytes + (size_t)(eight ? 8 : 4) * 16 * (4 * SB + 1) * 16;
+  const char* what = "launch proj_argmax_mfma_lds";
+  if (mp <= 16)
+    return eight ? launch_persistent(proj_argmax_mfma_lds<1, SB, 8, D>, 512, lds, tiles, 8, cus, stream, what,
+                                     grid_out, h, W, R, K, m_base, mp, slots)
+                 : launch_persistent(proj_argmax_mfma_lds<1, SB, 4, D>, 256, lds, tiles, 4, cus, stream, what,
+                                     grid_out, h, W, R, K, m_base, mp, slots);
+  return eight ? launch_persistent(proj_argmax_mfma_lds<2, SB, 8, D>, 512, lds, tiles, 8, cus, stream, what,
+                                   grid_out, h, W, R, K, m_base, mp, slots)
+               : launch_persistent(proj_argmax_mfma_lds<2, SB, 4, D>, 256, lds, tiles, 4, cus, stream, what,
+                                   grid_out, h, W, R, K, m_base, mp, slots);
 }
 
 int launch_mfma(const uint16_t* h, int M, int K, const uint16_t* W, int R, const int32_t* d2t,
@@ -849,14 +894,14 @@ int launch_mfma(const uint16_t* h, int M, int K, const uint16_t* W, int R, const
   int cus = 0;
   int st = cu_count(&cus);
   if (st != LMH_OK) return st;
-  const int cap = mfma_rows_per_pass(K);
+  const int cap = mfma_lds_rows_fit(K, 4);
+  if (cap < 1) return LMH_EINVAL;
   const int passes = (M + cap - 1) / cap;
   const int per = (M + passes - 1) / passes;
   for (int m0 = 0; m0 < M; m0 += per) {
     const int mp = std::min(per, M - m0);
     int grid = 0;
-    st = mp <= 16 ? launch_mfma_nt<1>(h, K, m0, mp, W, R, slots, cus, stream, &grid)
-                  : launch_mfma_nt<2>(h, K, m0, mp, W, R, slots, cus, stream, &grid);
+    st = launch_mfma_pass(h, K, m0, mp, W, R, slots, cus, stream, &grid);
     if (st != LMH_OK) return st;
     st = launch_finalize(slots, grid, m0, mp, d2t, out_id, out_logit, stream);
     if (st != LMH_OK) return st;
