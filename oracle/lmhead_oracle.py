@@ -45,7 +45,10 @@ __all__ = [
     "oracle_trim",
     "oracle_logits",
     "oracle_project_argmax",
+    "oracle_project_topk",
+    "oracle_scatter_logits",
     "OracleResult",
+    "TopkResult",
 ]
 
 # Rows of W decoded to fp64 at a time (bounds memory: 8,192 x 2,560 x 8 B).
@@ -149,3 +152,68 @@ def oracle_project_argmax(h_bits: np.ndarray, w_bits: np.ndarray,
     abs_sum = np.abs(h * w_win).sum(axis=1)
     return OracleResult(ids, idx.astype(np.int64), best, gap, abs_sum,
                         logits if keep_logits else None)
+
+
+@dataclass
+class TopkResult:
+    """Per hidden row m, the k best projected rows in order: ``idx[m, j]``
+    the row, ``id[m, j]`` its vocabulary id, ``logit[m, j]`` its fp64 logit;
+    ``sorted_logits[m]`` every projected logit in the same order (so gaps
+    around any position can be read off); ``logits`` the unsorted [M, R]."""
+    id: np.ndarray
+    idx: np.ndarray
+    logit: np.ndarray
+    sorted_logits: np.ndarray
+    logits: np.ndarray
+
+
+def oracle_project_topk(h_bits: np.ndarray, w_bits: np.ndarray,
+                        d2t: np.ndarray | None, k: int) -> TopkResult:
+    """The k highest-scoring projected rows per hidden row, best first.
+
+    Several draft candidates per position (for sampling or a draft tree)
+    are the top of the same scores whose argmax is the greedy draft; ties
+    are broken by the smaller row index, as for the argmax.  Rows are
+    mapped through d2t as in "Two ways to run it" (zone-1.cobraproject.com
+    "Masked MTP drafts").  If fewer than k rows exist, positions past R hold
+    id -1 and logit -inf."""
+    logits = oracle_logits(h_bits, w_bits)
+    m, r = logits.shape
+    if k < 1:
+        raise ValueError("k must be at least 1")
+    # stable sort on -logit keeps the smaller index first among equal logits
+    order = np.argsort(-logits, axis=1, kind="stable")
+    srt = np.take_along_axis(logits, order, axis=1)
+    kk = min(k, r)
+    idx = np.full((m, k), -1, dtype=np.int64)
+    lg = np.full((m, k), -np.inf)
+    idx[:, :kk] = order[:, :kk]
+    lg[:, :kk] = srt[:, :kk]
+    if d2t is None:
+        ids = idx.copy()
+    else:
+        d2t = np.asarray(d2t)
+        if d2t.shape != (r,):
+            raise ValueError("d2t must have one entry per projected row")
+        ids = np.where(idx >= 0, d2t[np.clip(idx, 0, r - 1)], -1).astype(np.int64)
+    return TopkResult(ids, idx, lg, srt, logits)
+
+
+def oracle_scatter_logits(h_bits: np.ndarray, w_bits: np.ndarray,
+                          d2t: np.ndarray | None, n: int | None = None) -> np.ndarray:
+    """Logits in vocabulary space, scatter-after-matmul.
+
+    With a d2t table the shortlist's logits are placed at their vocabulary
+    ids in an [M, n] array whose other entries are -inf, the EAGLE-3 style
+    map named in "Two ways to run it" (zone-1.cobraproject.com "Masked MTP
+    drafts"); ids off the list can never win.  Without d2t the result is the
+    [M, R] logits themselves."""
+    logits = oracle_logits(h_bits, w_bits)
+    if d2t is None:
+        return logits
+    d2t = np.asarray(d2t).astype(np.int64)
+    if n is None or d2t.size and (d2t.min() < 0 or d2t.max() >= n):
+        raise ValueError("d2t ids must lie in [0, n)")
+    out = np.full((logits.shape[0], n), -np.inf)
+    out[:, d2t] = logits
+    return out

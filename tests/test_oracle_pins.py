@@ -250,11 +250,66 @@ def pin_rows_independent(m):
     assert np.array_equal(t.id[ok], tp.id[ok])
 
 
+def pin_topk_bruteforce(m):
+    """Small-integer logits are exact; sort by (value desc, row asc) by hand."""
+    rng = _rng(41)
+    for (mm, k, r, kk) in [(1, 16, 40, 5), (3, 64, 200, 8), (2, 8, 7, 10)]:
+        hi = rng.integers(-3, 4, size=(mm, k))
+        wi = rng.integers(-3, 4, size=(r, k))
+        exact = (hi.astype(np.int64) @ wi.astype(np.int64).T).tolist()
+        res = m.oracle_project_topk(_bf16_of(hi.astype(np.float32)),
+                                    _bf16_of(wi.astype(np.float32)), None, kk)
+        assert res.idx.shape == (mm, kk)
+        for i in range(mm):
+            order = sorted(range(r), key=lambda j: (-exact[i][j], j))
+            for j in range(kk):
+                if j < r:
+                    assert res.idx[i, j] == order[j] and res.id[i, j] == order[j]
+                    assert res.logit[i, j] == exact[i][order[j]]
+                else:
+                    assert res.idx[i, j] == -1 and res.id[i, j] == -1
+                    assert res.logit[i, j] == -np.inf
+
+
+def pin_topk_ties_and_d2t(m):
+    h = _bf16_of(np.ones((1, 4), np.float32))
+    # row sums: 2, 4, 4, 1, 4, 3
+    rows = [[1, 1, 0, 0], [2, 2, 0, 0], [1, 1, 1, 1], [1, 0, 0, 0], [4, 0, 0, 0], [3, 0, 0, 0]]
+    w = _bf16_of(np.array(rows, np.float32))
+    res = m.oracle_project_topk(h, w, None, 4)
+    assert res.idx[0].tolist() == [1, 2, 4, 5]
+    assert res.logit[0].tolist() == [4.0, 4.0, 4.0, 3.0]
+    d2t = np.array([50, 40, 30, 20, 10, 0], np.int32)
+    assert m.oracle_project_topk(h, w, d2t, 4).id[0].tolist() == [40, 30, 10, 0]
+    one = m.oracle_project_topk(h, w, d2t, 1)
+    arg = m.oracle_project_argmax(h, w, d2t)
+    assert one.id[0, 0] == arg.id[0] and one.logit[0, 0] == arg.logit[0]
+
+
+def pin_scatter_logits(m):
+    w, ids, hs = _tiny_inputs(draws=4)
+    n = w.shape[0]
+    full = m.oracle_logits(hs, w)
+    sc = m.oracle_scatter_logits(hs, m.oracle_trim(w, ids), ids, n)
+    assert sc.shape == (hs.shape[0], n)
+    off = np.ones(n, bool)
+    off[ids] = False
+    assert np.all(sc[:, off] == -np.inf)
+    assert np.array_equal(sc[:, ids], full[:, ids])
+    # argmax of the scattered vector is the shortlist draft
+    arg = m.oracle_project_argmax(hs, m.oracle_trim(w, ids), d2t=ids)
+    assert np.array_equal(np.argmax(sc, axis=1), arg.id)
+    assert np.array_equal(m.oracle_scatter_logits(hs, w, None), full)
+    with pytest.raises(ValueError):
+        m.oracle_scatter_logits(hs, w[:10], np.arange(10), 5)
+
+
 PINS = [pin_decode_known, pin_decode_all_vs_torch, pin_bruteforce_fsum,
         pin_integer_exact, pin_one_hot, pin_planted_winner,
         pin_ties_first_occurrence, pin_gap_and_single_row, pin_trim_rows,
         pin_restriction_invariant, pin_scatter_equivalence, pin_identity_list,
-        pin_rows_independent]
+        pin_rows_independent, pin_topk_bruteforce, pin_topk_ties_and_d2t,
+        pin_scatter_logits]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
@@ -270,6 +325,8 @@ _orig_decode = lo.bf16_bits_to_f64
 _orig_logits = lo.oracle_logits
 _orig_project = lo.oracle_project_argmax
 _orig_trim = lo.oracle_trim
+_orig_topk = lo.oracle_project_topk
+_orig_scatter = lo.oracle_scatter_logits
 
 
 def _mut_decode_fp16(bits):
@@ -368,7 +425,55 @@ def _mut_trim_no_check(w, ids):
     return w[np.asarray(ids, np.int64) % w.shape[0]].copy()
 
 
+def _mut_topk_ties_large_first(h, w, d2t, k):
+    res = _orig_topk(h, w, d2t, k)
+    lg = res.logits
+    order = np.lexsort((-np.arange(lg.shape[1])[None, :].repeat(lg.shape[0], 0), -lg), axis=1)
+    kk = min(k, lg.shape[1])
+    res.idx[:, :kk] = order[:, :kk]
+    res.id = res.idx.copy() if d2t is None else np.where(res.idx >= 0, np.asarray(d2t)[np.clip(res.idx, 0, None)], -1)
+    return res
+
+
+def _mut_topk_ascending(h, w, d2t, k):
+    res = _orig_topk(h, w, d2t, k)
+    res.idx = res.idx[:, ::-1].copy()
+    res.id = res.id[:, ::-1].copy()
+    res.logit = res.logit[:, ::-1].copy()
+    return res
+
+
+def _mut_topk_ignores_d2t(h, w, d2t, k):
+    return _orig_topk(h, w, None, k)
+
+
+def _mut_topk_pads_zero(h, w, d2t, k):
+    res = _orig_topk(h, w, d2t, k)
+    res.logit = np.where(np.isinf(res.logit), 0.0, res.logit)
+    return res
+
+
+def _mut_scatter_zero_fill(h, w, d2t, n=None):
+    out = _orig_scatter(h, w, d2t, n)
+    return np.where(np.isinf(out), 0.0, out)
+
+
+def _mut_scatter_by_position(h, w, d2t, n=None):
+    logits = _orig_logits(h, w)
+    if d2t is None:
+        return logits
+    out = np.full((logits.shape[0], n), -np.inf)
+    out[:, :logits.shape[1]] = logits
+    return out
+
+
 MUTANTS = {
+    "topk_ties_larger_first": ("oracle_project_topk", _mut_topk_ties_large_first),
+    "topk_ascending": ("oracle_project_topk", _mut_topk_ascending),
+    "topk_ignores_d2t": ("oracle_project_topk", _mut_topk_ignores_d2t),
+    "topk_pads_zero": ("oracle_project_topk", _mut_topk_pads_zero),
+    "scatter_zero_fill": ("oracle_scatter_logits", _mut_scatter_zero_fill),
+    "scatter_by_position": ("oracle_scatter_logits", _mut_scatter_by_position),
     "decode_as_fp16": ("bf16_bits_to_f64", _mut_decode_fp16),
     "decode_shift15": ("bf16_bits_to_f64", _mut_decode_shift15),
     "logits_drop_last_k": ("oracle_logits", _mut_logits_drop_last),
