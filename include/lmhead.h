@@ -55,6 +55,7 @@ typedef enum {
 #define LMH_MIN_K 8
 #define LMH_MAX_K 8192
 #define LMH_MAX_R (1 << 30)
+#define LMH_MAX_TOPK 16
 
 /* Kernel choice for draft_project_argmax_path. */
 #define LMH_PATH_AUTO 0
@@ -138,6 +139,47 @@ int draft_project_argmax_path(const uint16_t* h, int64_t M, int64_t K,
                               int32_t* out_id, float* out_logit,
                               void* workspace, size_t workspace_bytes,
                               int path, void* stream);
+
+/*
+ * draft_project_topk -- the `topk` best rows per hidden row instead of one:
+ * several draft candidates per position, for sampling or a draft tree.  They
+ * are the top of the same scores whose argmax is the greedy draft.
+ *
+ *  out_id     [M, topk] int32: d2t[row] (or row), best first; among equal
+ *             logits the smaller row comes first.  Positions past R hold -1.
+ *  out_logit  [M, topk] float, matching; -inf past R.
+ *  topk       1 .. LMH_MAX_TOPK.
+ *  workspace  draft_project_topk_workspace_bytes(M, topk) bytes, 16-byte
+ *             aligned; contents irrelevant, as for draft_project_argmax.
+ *  path       LMH_PATH_AUTO, or LMH_PATH_VALU (M <= 4) / LMH_PATH_MFMA.
+ * Other arguments, synchronization and errors as for draft_project_argmax.
+ */
+size_t draft_project_topk_workspace_bytes(int64_t M, int64_t topk);
+int draft_project_topk(const uint16_t* h, int64_t M, int64_t K,
+                       const uint16_t* W, int64_t R,
+                       const int32_t* d2t, int64_t topk,
+                       int32_t* out_id, float* out_logit,
+                       void* workspace, size_t workspace_bytes,
+                       int path, void* stream);
+
+/*
+ * draft_project_logits -- every logit, for consumers that sample or rescore.
+ * Without d2t: out is [M, R], out[m * R + r] = L[m, r].  With d2t (the
+ * shortlist's vocabulary ids), the logits are scattered into vocabulary
+ * space: out is [M, N], out[m * N + d2t[r]] = L[m, r] and every other entry
+ * is -inf, so an id off the list can never be chosen -- EAGLE-3's d2t map,
+ * scatter-after-matmul ("Two ways to run it", zone-1.cobraproject.com
+ * "Masked MTP drafts").  d2t entries outside [0, N) are skipped; with
+ * duplicate ids one of the rows' logits is kept.
+ *
+ *  out   float, 4-byte aligned, [M, R] or [M, N] as above.  No workspace.
+ *  path  as for draft_project_topk.
+ * Queues a -inf fill (with d2t) and the projection; never synchronizes.
+ */
+int draft_project_logits(const uint16_t* h, int64_t M, int64_t K,
+                         const uint16_t* W, int64_t R,
+                         const int32_t* d2t, int64_t N, float* out,
+                         int path, void* stream);
 
 /* Which kernel draft_project_argmax picks for (M, K): an LMH_PATH_* value,
  * or -1 if the shape is not accepted. */

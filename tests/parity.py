@@ -91,3 +91,91 @@ def check(h_bits, w_bits, d2t, gpu_id, gpu_logit, res=None) -> ParityStats:
             assert res.logit[i] - lg <= LOGIT_TOL
             st.exempt += 1
     return st
+
+
+def row_bounds(h_bits, w_bits, rows=None) -> np.ndarray:
+    """(K+1) * 2**-24 * sum_k |h[m,k] W[r,k]| for every (m, r) (or the given
+    rows): the fp32 error bound of any summation order, as in check()."""
+    h = np.abs(oracle.bf16_bits_to_f64(np.asarray(h_bits)))
+    w_bits = np.asarray(w_bits)
+    if rows is not None:
+        w_bits = w_bits[rows]
+    k = h.shape[1]
+    out = np.empty((h.shape[0], w_bits.shape[0]))
+    for r0 in range(0, w_bits.shape[0], 8192):
+        wb = np.abs(oracle.bf16_bits_to_f64(w_bits[r0:r0 + 8192]))
+        out[:, r0:r0 + wb.shape[0]] = h @ wb.T
+    return (k + 1) * U32 * out + 1e-30
+
+
+def check_topk(h_bits, w_bits, d2t, gpu_ids, gpu_logits, res=None) -> ParityStats:
+    """Top-k rule: per position j the GPU logit is within the fp32 bound of
+    the oracle logit of the GPU's row and within 2e-2 of the oracle's j-th
+    logit; the id at j must equal the oracle's wherever both neighbouring
+    gaps exceed 1e-2 (or twice the fp32 bound); logits are non-increasing,
+    rows are distinct, and positions past R hold -1 / -inf."""
+    h_bits = np.asarray(h_bits)
+    w_bits = np.asarray(w_bits)
+    gpu_ids = np.asarray(gpu_ids).astype(np.int64)
+    gpu_logits = np.asarray(gpu_logits).astype(np.float64)
+    m, k = gpu_ids.shape
+    r = w_bits.shape[0]
+    if res is None:
+        res = oracle.oracle_project_topk(h_bits, w_bits, d2t, k)
+    if d2t is None:
+        to_row = lambda ids: ids
+    else:
+        d2t = np.asarray(d2t).astype(np.int64)
+        pos = np.full(int(d2t.max()) + 1, -1, dtype=np.int64)
+        pos[d2t] = np.arange(r)
+        to_row = lambda ids: np.where((ids >= 0) & (ids < pos.size), pos[np.clip(ids, 0, pos.size - 1)], -1)
+    kk = min(k, r)
+    st = ParityStats(rows=m * kk)
+    for i in range(m):
+        assert np.all(gpu_ids[i, kk:] == -1) and np.all(np.isneginf(gpu_logits[i, kk:]))
+        rows = to_row(gpu_ids[i, :kk])
+        assert np.all(rows >= 0), f"row {i}: id not in the projected set"
+        assert np.unique(rows).size == kk, f"row {i}: repeated candidates"
+        gl = gpu_logits[i, :kk]
+        assert np.all(gl[:-1] >= gl[1:]), f"row {i}: logits not in descending order"
+        bnd = row_bounds(h_bits[i:i + 1], w_bits, rows)[0]
+        bnd_ref = row_bounds(h_bits[i:i + 1], w_bits, res.idx[i, :kk])[0]
+        srt = res.sorted_logits[i]
+        bmax = 2 * float(max(bnd.max(), bnd_ref.max()))
+        for j in range(kk):
+            lg = res.logits[i, rows[j]]
+            err = abs(gl[j] - lg)
+            st.max_err = max(st.max_err, err)
+            st.max_err_over_bound = max(st.max_err_over_bound, err / bnd[j])
+            assert err <= bnd[j], f"row {i} pos {j}: error {err:.3e} > bound {bnd[j]:.3e}"
+            assert abs(gl[j] - res.logit[i, j]) <= LOGIT_TOL
+            hi = srt[j - 1] - srt[j] if j > 0 else np.inf
+            lo = srt[j] - srt[j + 1] if j + 1 < r else np.inf
+            if min(hi, lo) > min(GAP_EXEMPT, bmax):
+                assert gpu_ids[i, j] == res.id[i, j], (i, j, gpu_ids[i, j], res.id[i, j])
+            elif gpu_ids[i, j] != res.id[i, j]:
+                st.exempt += 1
+    return st
+
+
+def check_logits(h_bits, w_bits, d2t, n, gpu_out) -> ParityStats:
+    """Every logit within the fp32 bound (and 2e-2) of the oracle; with d2t,
+    entries off the list are exactly -inf (scatter-after-matmul)."""
+    gpu_out = np.asarray(gpu_out).astype(np.float64)
+    want = oracle.oracle_scatter_logits(h_bits, w_bits, d2t, n)
+    bnd = row_bounds(h_bits, w_bits)
+    st = ParityStats(rows=gpu_out.shape[0])
+    if d2t is None:
+        got, ref = gpu_out, want
+    else:
+        d2t = np.asarray(d2t).astype(np.int64)
+        off = np.ones(n, dtype=bool)
+        off[d2t] = False
+        assert np.all(np.isneginf(gpu_out[:, off])), "entries off the list must be -inf"
+        got, ref = gpu_out[:, d2t], want[:, d2t]
+    err = np.abs(got - ref)
+    assert np.all(err <= bnd), f"max error/bound {float((err / bnd).max()):.3f}"
+    assert np.all(err <= LOGIT_TOL)
+    st.max_err = float(err.max())
+    st.max_err_over_bound = float((err / bnd).max())
+    return st

@@ -102,6 +102,39 @@ def test_project_rejects_on_host(L, kw, code):
     assert call(L, **kw) == code
 
 
+def topk_call(L, h=A, m=2, k=2560, w=B, r=100, d2t=None, topk=4, oid=C, olog=D, ws=E,
+              wsb=1 << 24, path=0):
+    return L.lib().draft_project_topk(h, m, k, w, r, d2t, topk, oid, olog, ws, wsb, path, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(topk=0), 1), (dict(topk=17), 1), (dict(oid=None), 1), (dict(olog=None), 1),
+    (dict(h=None), 1), (dict(m=0), 1), (dict(k=12), 1), (dict(r=0), 1), (dict(w=B + 2), 1),
+    (dict(m=5, path=1), 1), (dict(path=3), 1), (dict(ws=None), 3), (dict(ws=E + 8), 3),
+    (dict(wsb=2 * 1024 * 4 * 8 - 1), 3),
+])
+def test_topk_rejects_on_host(L, kw, code):
+    assert topk_call(L, **kw) == code
+
+
+def test_topk_workspace_bytes(L):
+    assert L.draft_project_topk_workspace_bytes(1, 1) == 8 * 1024
+    assert L.draft_project_topk_workspace_bytes(2, 3) == 2 * 1024 * 4 * 8
+    assert L.draft_project_topk_workspace_bytes(24, 16) == 24 * 1024 * 16 * 8
+    assert L.draft_project_topk_workspace_bytes(1, 17) == 0
+    assert L.draft_project_topk_workspace_bytes(33, 4) == 0
+
+
+def test_logits_rejects_on_host(L):
+    lib = L.lib()
+    f = lib.draft_project_logits
+    assert f(A, 1, 2560, B, 100, None, 0, None, 0, None) == 1          # no output
+    assert f(A, 1, 2560, B, 100, None, 0, C + 2, 0, None) == 1         # misaligned output
+    assert f(A, 1, 2560, B, 100, D, 0, C, 0, None) == 1                # d2t needs N >= 1
+    assert f(A, 5, 2560, B, 100, None, 0, C, 1, None) == 1             # VALU epilogues: M <= 4
+    assert f(A, 1, 12, B, 100, None, 0, C, 0, None) == 1
+
+
 def test_trim_rejects_on_host(L):
     lib = L.lib()
     assert lib.lmhead_trim(A, 100, 2560, B, 0, C, None) == 0          # S = 0: no-op
@@ -139,7 +172,7 @@ def test_build_has_no_scratch_spills():
         proc = subprocess.run(build.command(out), capture_output=True, text=True)
         assert proc.returncode == 0, proc.stderr[-2000:]
         usage = build.kernel_resources(proc.stderr)
-    assert any("proj_argmax_valu_tiled" in k for k in usage)
-    assert any("proj_argmax_mfma_lds" in k for k in usage)
+    for kernel in ("proj_valu_tiled", "proj_valu_rows", "proj_mfma", "finalize_topk"):
+        assert any(kernel in k for k in usage), kernel
     spills = {k: v["ScratchSize"] for k, v in usage.items() if v.get("ScratchSize", 0)}
     assert not spills, spills

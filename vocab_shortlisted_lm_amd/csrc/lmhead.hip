@@ -39,6 +39,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <mutex>
 #include <type_traits>
 #include <utility>
 #include <vector>
@@ -87,6 +88,8 @@ constexpr int kValuMaxChunksTimesM = 40;   // register budget: 160 VGPRs of h
 #endif
 // Workgroup slots per hidden row in the workspace; grids are clamped to it.
 constexpr int kMaxGrid = 1024;
+// LDS one workgroup may use on gfx950.
+constexpr int kLdsPerWorkgroup = 160 * 1024;
 constexpr int64_t kMaxRows = (int64_t)1 << 30;  // keeps row arithmetic in int range
 constexpr uint32_t kBufferWord3 = 0x00020000u;  // gfx9 raw buffer, 32-bit data
 constexpr uint32_t kOobOffset = 0x80000000u;    // any offset >= num_records reads 0
@@ -178,6 +181,47 @@ __device__ __forceinline__ void unpack_key(unsigned long long k, float& v, int& 
   idx = (int)(0xFFFFFFFFu - (uint32_t)k);
 }
 
+__device__ __forceinline__ unsigned long long max_u64(unsigned long long a, unsigned long long b) {
+  return a > b ? a : b;
+}
+__device__ __forceinline__ unsigned long long min_u64(unsigned long long a, unsigned long long b) {
+  return a < b ? a : b;
+}
+
+__device__ __forceinline__ unsigned long long shfl_xor_u64(unsigned long long k, int x) {
+  const uint32_t lo = (uint32_t)__shfl_xor((int)(uint32_t)k, x);
+  const uint32_t hi = (uint32_t)__shfl_xor((int)(uint32_t)(k >> 32), x);
+  return ((unsigned long long)hi << 32) | lo;
+}
+
+// A lane's running top-TK: keys in descending order, 0 = empty slot.
+// push() inserts without branches over the list: position j takes
+// max(old[j], min(old[j - 1], x)), which shifts every key below x down one
+// place.  Keys are unique (the row is in the low bits), so the list holds
+// the TK best rows seen, with the smaller row first among equal logits.
+template <int TK>
+struct KeyList {
+  unsigned long long k[TK];
+  __device__ __forceinline__ void clear() {
+#pragma unroll
+    for (int j = 0; j < TK; ++j) k[j] = 0ull;
+  }
+  __device__ __forceinline__ void push(unsigned long long x) {
+    if (x <= k[TK - 1]) return;  // the common case once the list is full
+#pragma unroll
+    for (int j = TK - 1; j >= 1; --j) k[j] = max_u64(k[j], min_u64(k[j - 1], x));
+    k[0] = max_u64(k[0], x);
+  }
+  // fold in the list of lane (this lane ^ x)
+  __device__ __forceinline__ void merge_xor(int x) {
+    unsigned long long o[TK];
+#pragma unroll
+    for (int j = 0; j < TK; ++j) o[j] = shfl_xor_u64(k[j], x);
+#pragma unroll
+    for (int j = 0; j < TK; ++j) push(o[j]);
+  }
+};
+
 // Workgroup epilogue, run by wave 0 only: lane m < mcount publishes this
 // workgroup's best key for hidden row m_base + m into its own slot.  Slots
 // are laid out [hidden row][workgroup], so the finalize kernel reads each
@@ -186,6 +230,47 @@ __device__ __forceinline__ void unpack_key(unsigned long long k, float& v, int& 
 __device__ __forceinline__ void publish_workgroup(unsigned long long key, int lane, int mcount, int m_base,
                                                   unsigned long long* __restrict__ slots) {
   if (lane < mcount) slots[(size_t)(m_base + lane) * kMaxGrid + blockIdx.x] = key;
+}
+
+// What a projection kernel does with each (head row, hidden row) logit.
+//   TK >= 1, !LOGITS: keep the TK best keys; each workgroup leaves them in
+//                     slots[(hidden row * kMaxGrid + workgroup) * TK + j].
+//   LOGITS:           write the logit to logits[hidden row * ld + col], col
+//                     = d2t[row] (skipped unless 0 <= col < ncols) or row.
+struct Epi {
+  unsigned long long* slots;
+  float* logits;
+  const int32_t* d2t;
+  int64_t ld;
+  int64_t ncols;
+};
+
+__device__ __forceinline__ void store_logit(const Epi& e, int m, int r, float v) {
+  int64_t col = r;
+  if (e.d2t) {
+    col = e.d2t[r];
+    if (col < 0 || col >= e.ncols) return;
+  }
+  e.logits[(int64_t)m * e.ld + col] = v;
+}
+
+// Workgroup epilogue for TK > 1, run by wave 0: lane m < mcount merges the
+// per-wave lists lists[(w * ms + m) * TK + j] (in LDS) and publishes the
+// workgroup's TK keys.
+template <int TK, int WV>
+__device__ __forceinline__ void publish_lists(const unsigned long long* lists, int ms, int lane, int mcount,
+                                              int m_base, unsigned long long* __restrict__ slots) {
+  if (lane >= mcount) return;
+  KeyList<TK> l;
+#pragma unroll
+  for (int j = 0; j < TK; ++j) l.k[j] = lists[lane * TK + j];
+#pragma unroll
+  for (int w = 1; w < WV; ++w)
+#pragma unroll
+    for (int j = 0; j < TK; ++j) l.push(lists[(w * ms + lane) * TK + j]);
+  unsigned long long* dst = slots + ((size_t)(m_base + lane) * kMaxGrid + blockIdx.x) * TK;
+#pragma unroll
+  for (int j = 0; j < TK; ++j) dst[j] = l.k[j];
 }
 
 // One workgroup per hidden row: fold the `nslots` workgroup keys, decode
@@ -224,6 +309,52 @@ finalize_argmax(const unsigned long long* __restrict__ slots, int nslots, int m_
   out_logit[m] = v;
 }
 
+// Top-TK version: one workgroup per hidden row merges the TK keys of each
+// of `nslots` workgroups (slots laid out [hidden row][workgroup][TK]) and
+// writes the best `topk` rows, mapped through d2t, best first.  Positions
+// with no row (R < topk) get id -1 and logit -inf.
+template <int TK>
+__global__ void __launch_bounds__(256)
+finalize_topk(const unsigned long long* __restrict__ slots, int nslots, int m_base, int topk,
+              const int32_t* __restrict__ d2t, int32_t* __restrict__ out_id, float* __restrict__ out_logit) {
+  __shared__ unsigned long long s_list[256][TK];
+  const int m = m_base + blockIdx.x;
+  const unsigned long long* row = slots + (size_t)m * kMaxGrid * TK;
+  KeyList<TK> l;
+  l.clear();
+  for (int i = threadIdx.x; i < nslots * TK; i += 256) l.push(row[i]);
+#pragma unroll
+  for (int j = 0; j < TK; ++j) s_list[threadIdx.x][j] = l.k[j];
+  __syncthreads();
+  for (int half = 128; half >= 1; half >>= 1) {
+    if (threadIdx.x < half) {
+#pragma unroll
+      for (int j = 0; j < TK; ++j) l.push(s_list[threadIdx.x + half][j]);
+#pragma unroll
+      for (int j = 0; j < TK; ++j) s_list[threadIdx.x][j] = l.k[j];
+    }
+    __syncthreads();
+  }
+  if (threadIdx.x != 0) return;
+#pragma unroll
+  for (int j = 0; j < TK; ++j) {
+    if (j < topk) {
+      const unsigned long long k = l.k[j];
+      float v = -__builtin_inff();
+      int idx = -1;
+      if (k != 0ull) unpack_key(k, v, idx);
+      out_id[(size_t)m * topk + j] = idx < 0 ? -1 : (d2t ? d2t[idx] : idx);
+      out_logit[(size_t)m * topk + j] = v;
+    }
+  }
+}
+
+// Fill for scatter-after-matmul: every entry of [M, N] starts at -inf.
+__global__ void __launch_bounds__(256) fill_neg_inf(float* __restrict__ out, size_t n) {
+  const float ninf = -__builtin_inff();
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256) out[i] = ninf;
+}
+
 // ---------------------------------------------------------------------------
 // gather: W_trim[i, :] = W[ids[i], :]
 // ---------------------------------------------------------------------------
@@ -253,8 +384,7 @@ gather_rows(const uint16_t* __restrict__ W, int64_t N, int K, const int32_t* __r
 // the row end get an out-of-range buffer offset and read as zero.
 template <int M, int CPL, int U, int WV>
 __global__ void __launch_bounds__(64 * WV)
-proj_argmax_valu(const uint16_t* __restrict__ h, const uint16_t* __restrict__ W, int R, int K,
-                 unsigned long long* __restrict__ slots) {
+proj_valu_rows(const uint16_t* __restrict__ h, const uint16_t* __restrict__ W, int R, int K, Epi epi) {
   __shared__ unsigned long long s_key[WV][M];
   const int lane = threadIdx.x & 63;
   const int wave = wave_id();
@@ -341,7 +471,7 @@ proj_argmax_valu(const uint16_t* __restrict__ h, const uint16_t* __restrict__ W,
 #pragma unroll
     for (int w = 0; w < WV; ++w) key = s_key[w][lane] > key ? s_key[w][lane] : key;
   }
-  publish_workgroup(key, lane, M, 0, slots);
+  publish_workgroup(key, lane, M, 0, epi.slots);
 }
 
 // VALU path, tiled order: a wave owns tiles of TR consecutive head rows and
@@ -349,13 +479,12 @@ proj_argmax_valu(const uint16_t* __restrict__ h, const uint16_t* __restrict__ W,
 // of every row of the tile), keeping one fp32 partial sum per (row, hidden
 // row) in its lanes.  One batch is TR rows x 1 KiB; the next batch is in
 // flight while this one is scored.  Hidden rows live in LDS, zero-padded to
-// whole stripes, so the batch loop is a plain runtime loop.
-template <int M, int TR, int WV>
+// whole stripes, so the batch loop is a plain runtime loop.  The epilogue
+// (argmax, top-TK or every logit) is chosen by TK and LOGITS.
+template <int M, int TR, int WV, int TK, bool LOGITS>
 __global__ void __launch_bounds__(64 * WV)
-proj_argmax_valu_tiled(const uint16_t* __restrict__ h, const uint16_t* __restrict__ W, int R, int K,
-                       unsigned long long* __restrict__ slots) {
+proj_valu_tiled(const uint16_t* __restrict__ h, const uint16_t* __restrict__ W, int R, int K, Epi epi) {
   extern __shared__ u32x4 h_stripes[];  // [M][nb * 64] chunks, zero past K
-  __shared__ unsigned long long s_key[WV][M];
   const int lane = threadIdx.x & 63;
   const int wave = wave_id();
   const int chunks = K >> 3;
@@ -372,13 +501,17 @@ proj_argmax_valu_tiled(const uint16_t* __restrict__ h, const uint16_t* __restric
   }
   __syncthreads();
 
+  // epilogue state: the running best row (TK == 1) or the TK best keys
   float best[M];
   int bidx[M];
+  KeyList<TK> lists[(TK > 1 && !LOGITS) ? M : 1];
 #pragma unroll
   for (int m = 0; m < M; ++m) {
     best[m] = 0.0f;
     bidx[m] = -1;
   }
+#pragma unroll
+  for (int m = 0; m < ((TK > 1 && !LOGITS) ? M : 1); ++m) lists[m].clear();
   float acc[TR][M];
 #pragma unroll
   for (int q = 0; q < TR; ++q)
@@ -414,7 +547,15 @@ proj_argmax_valu_tiled(const uint16_t* __restrict__ h, const uint16_t* __restric
         for (int m = 0; m < M; ++m) {
           const float sum = wave_sum(acc[q][m]);
           acc[q][m] = 0.0f;
-          if (r0 + q < R) take_best(sum, r0 + q, best[m], bidx[m]);
+          if (r0 + q < R) {
+            if constexpr (LOGITS) {
+              if (lane == 0) store_logit(epi, m, r0 + q, sum);
+            } else if constexpr (TK == 1) {
+              take_best(sum, r0 + q, best[m], bidx[m]);
+            } else {
+              lists[m].push(pack_key(sum, r0 + q));
+            }
+          }
         }
     }
   };
@@ -449,18 +590,34 @@ proj_argmax_valu_tiled(const uint16_t* __restrict__ h, const uint16_t* __restric
     }
   }
 
-  if (lane == 0) {
+  if constexpr (LOGITS) {
+    return;
+  } else if constexpr (TK == 1) {
+    __shared__ unsigned long long s_key[WV][M];
+    if (lane == 0) {
 #pragma unroll
-    for (int m = 0; m < M; ++m) s_key[wave][m] = pack_key(best[m], bidx[m]);
-  }
-  __syncthreads();
-  if (wave != 0) return;
-  unsigned long long key = 0ull;
-  if (lane < M) {
+      for (int m = 0; m < M; ++m) s_key[wave][m] = pack_key(best[m], bidx[m]);
+    }
+    __syncthreads();
+    if (wave != 0) return;
+    unsigned long long key = 0ull;
+    if (lane < M) {
 #pragma unroll
-    for (int w = 0; w < WV; ++w) key = s_key[w][lane] > key ? s_key[w][lane] : key;
+      for (int w = 0; w < WV; ++w) key = s_key[w][lane] > key ? s_key[w][lane] : key;
+    }
+    publish_workgroup(key, lane, M, 0, epi.slots);
+  } else {
+    __shared__ unsigned long long s_list[WV * M * TK];
+    if (lane == 0) {
+#pragma unroll
+      for (int m = 0; m < M; ++m)
+#pragma unroll
+        for (int jj = 0; jj < TK; ++jj) s_list[(wave * M + m) * TK + jj] = lists[m].k[jj];
+    }
+    __syncthreads();
+    if (wave != 0) return;
+    publish_lists<TK, WV>(s_list, M, lane, M, 0, epi.slots);
   }
-  publish_workgroup(key, lane, M, 0, slots);
 }
 
 // ---------------------------------------------------------------------------
@@ -475,16 +632,16 @@ proj_argmax_valu_tiled(const uint16_t* __restrict__ h, const uint16_t* __restric
 // stage, and reads the A operands back in MFMA layout.  Hidden rows are in
 // LDS as in proj_argmax_mfma.  The stage is private to the wave, so the
 // exchange needs only wave-level ordering, not a workgroup barrier.
-template <int NT, int SB, int WV, int D>
+template <int NT, int SB, int WV, int D, int TK, bool LOGITS>
 __global__ void __launch_bounds__(64 * WV)
-proj_argmax_mfma_lds(const uint16_t* __restrict__ h, const uint16_t* __restrict__ W, int R, int K,
-                     int m_base, int mp, unsigned long long* __restrict__ slots) {
+proj_mfma(const uint16_t* __restrict__ h, const uint16_t* __restrict__ W, int R, int K, int m_base, int mp,
+          Epi epi) {
   static_assert(SB == 4 || SB == 8 || SB == 16, "a load instruction covers whole row pieces");
   constexpr int BC = 4 * SB;    // 16-byte chunks per row per batch
   constexpr int SC = BC + 1;    // stage row stride in chunks (padded against bank conflicts)
   constexpr int RPI = 64 / BC;  // rows per load instruction
   extern __shared__ u32x4 lds[];  // [mp][row_chunks] hidden rows, then [WV][16][SC] stages
-  __shared__ unsigned long long s_key[WV][32];
+  __shared__ unsigned long long s_key[TK == 1 && !LOGITS ? WV : 1][32];
   const int lane = threadIdx.x & 63;
   const int wave = wave_id();
   const int i16 = lane & 15;
@@ -511,13 +668,18 @@ proj_argmax_mfma_lds(const uint16_t* __restrict__ h, const uint16_t* __restrict_
     bptr[nt] = lds + (col < mp ? col : mp - 1) * row_chunks + g;
   }
 
+  // epilogue state of this lane's column (hidden row) in each 16-column
+  // tile: the running best row (TK == 1) or the TK best keys
   float best[NT];
   int bidx[NT];
+  KeyList<TK> lists[(TK > 1 && !LOGITS) ? NT : 1];
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
     best[nt] = 0.0f;
     bidx[nt] = -1;
   }
+#pragma unroll
+  for (int nt = 0; nt < ((TK > 1 && !LOGITS) ? NT : 1); ++nt) lists[nt].clear();
   f32x4 acc[NT];
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -587,7 +749,16 @@ proj_argmax_mfma_lds(const uint16_t* __restrict__ h, const uint16_t* __restrict_
       const int r = r0 + 4 * g + v;
       if (r < R) {
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt) take_best(acc[nt][v], r, best[nt], bidx[nt]);
+        for (int nt = 0; nt < NT; ++nt) {
+          if constexpr (LOGITS) {
+            const int col = nt * 16 + i16;
+            if (col < mp) store_logit(epi, m_base + col, r, acc[nt][v]);
+          } else if constexpr (TK == 1) {
+            take_best(acc[nt][v], r, best[nt], bidx[nt]);
+          } else {
+            lists[nt].push(pack_key(acc[nt][v], r));
+          }
+        }
       }
     }
 #pragma unroll
@@ -634,27 +805,47 @@ proj_argmax_mfma_lds(const uint16_t* __restrict__ h, const uint16_t* __restrict_
     ((n + J < count ? (step(std::integral_constant<int, J>{}), 0) : 0), ...);
   }(std::make_integer_sequence<int, D>{});
 
+  if constexpr (LOGITS) {
+    return;
+  } else if constexpr (TK == 1) {
 #pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
-    unsigned long long k = pack_key(best[nt], bidx[nt]);
-#pragma unroll
-    for (int x = 16; x <= 32; x <<= 1) {
-      const uint32_t lo = (uint32_t)__shfl_xor((int)(uint32_t)k, x);
-      const uint32_t hi = (uint32_t)__shfl_xor((int)(uint32_t)(k >> 32), x);
-      const unsigned long long o = ((unsigned long long)hi << 32) | lo;
-      k = o > k ? o : k;
+    for (int nt = 0; nt < NT; ++nt) {
+      unsigned long long k = pack_key(best[nt], bidx[nt]);
+      // fold the four lanes (g = 0..3) that hold the same hidden row
+      k = max_u64(k, shfl_xor_u64(k, 16));
+      k = max_u64(k, shfl_xor_u64(k, 32));
+      const int col = nt * 16 + i16;
+      if (g == 0 && col < 32) s_key[wave][col] = k;
     }
-    const int col = nt * 16 + i16;
-    if (g == 0 && col < 32) s_key[wave][col] = k;
-  }
-  __syncthreads();
-  if (wave != 0) return;
-  unsigned long long key = 0ull;
-  if (lane < mp) {
+    __syncthreads();
+    if (wave != 0) return;
+    unsigned long long key = 0ull;
+    if (lane < mp) {
 #pragma unroll
-    for (int w = 0; w < WV; ++w) key = s_key[w][lane] > key ? s_key[w][lane] : key;
+      for (int w = 0; w < WV; ++w) key = s_key[w][lane] > key ? s_key[w][lane] : key;
+    }
+    publish_workgroup(key, lane, mp, m_base, epi.slots);
+  } else {
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      lists[nt].merge_xor(16);
+      lists[nt].merge_xor(32);
+    }
+    // every wave is past its main loop: the stage area is free for the lists
+    __syncthreads();
+    unsigned long long* s_list = reinterpret_cast<unsigned long long*>(lds + mp * row_chunks);
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      const int col = nt * 16 + i16;
+      if (g == 0 && col < mp) {
+#pragma unroll
+        for (int j = 0; j < TK; ++j) s_list[(wave * 32 + col) * TK + j] = lists[nt].k[j];
+      }
+    }
+    __syncthreads();
+    if (wave != 0) return;
+    publish_lists<TK, WV>(s_list, 32, lane, mp, m_base, epi.slots);
   }
-  publish_workgroup(key, lane, mp, m_base, slots);
 }
 
 // ---------------------------------------------------------------------------
@@ -742,15 +933,15 @@ bool valu_ok(int64_t M, int64_t K) {
 int mfma_row_bytes(int64_t K) { return (int)((((K + 31) / 32) * 4 + 1) * 16); }
 
 
-typedef void (*valu_fn)(const uint16_t*, const uint16_t*, int, int, unsigned long long*);
+typedef void (*proj_fn)(const uint16_t*, const uint16_t*, int, int, Epi);
 
 // One VALU launch shape: kernel, waves per workgroup, head rows a wave takes
-// per step, LDS bytes.  The choice per M comes from measurement on MI355X
-// (full 248,320 x 2,560 head): M = 1 streams fastest in 4-row tiles; M = 2..4
-// in row order with one 4-wave workgroup per CU; M = 5..8 need the 256-VGPR
-// budget of 8-wave workgroups.
+// per step, LDS bytes.  For the argmax the choice per M comes from
+// measurement on MI355X (full 248,320 x 2,560 head): M = 1 streams fastest
+// in 4-row tiles; M = 2..4 in row order with one 4-wave workgroup per CU.
+// The top-k and logits epilogues use the tiled kernel for every M <= 4.
 struct ValuPlan {
-  valu_fn fn = nullptr;
+  proj_fn fn = nullptr;
   int waves = 0;
   int rows_per_wave = 0;
   size_t lds = 0;
@@ -763,7 +954,7 @@ void row_plan(ValuPlan& p) {
     // and one row per step once h alone takes more than 80 registers
     constexpr int U0 = M * CPL > 20 ? 1 : (CPL * LMH_VALU_ROWS <= 10 ? LMH_VALU_ROWS : (CPL <= 10 ? 10 / CPL : 1));
     constexpr int U = U0 < 1 ? 1 : U0;
-    p.fn = proj_argmax_valu<M, CPL, U, WV>;
+    p.fn = proj_valu_rows<M, CPL, U, WV>;
     p.waves = WV;
     p.rows_per_wave = U;
     p.lds = 0;
@@ -776,16 +967,20 @@ void row_plan_cpl(ValuPlan& p, int cpl, std::integer_sequence<int, C...>) {
   ((cpl == C + 1 ? (row_plan<M, C + 1, WV>(p), 0) : 0), ...);
 }
 
-ValuPlan valu_plan(int M, int K) {
+template <int M, int TK, bool LOGITS>
+ValuPlan tiled_plan(int K) {
   ValuPlan p;
+  p.fn = proj_valu_tiled<M, LMH_VALU_TILE_ROWS, LMH_VALU_WAVES, TK, LOGITS>;
+  p.waves = LMH_VALU_WAVES;
+  p.rows_per_wave = LMH_VALU_TILE_ROWS;
+  p.lds = (size_t)M * chunks_per_lane(K) * 64 * 16;
+  return p;
+}
+
+ValuPlan valu_argmax_plan(int M, int K) {
+  ValuPlan p;
+  if (M == 1 && LMH_VALU_TILE_ROWS > 0) return tiled_plan<1, 1, false>(K);
   const int cpl = chunks_per_lane(K);
-  if (M == 1 && LMH_VALU_TILE_ROWS > 0) {
-    p.fn = proj_argmax_valu_tiled<1, LMH_VALU_TILE_ROWS, LMH_VALU_WAVES>;
-    p.waves = LMH_VALU_WAVES;
-    p.rows_per_wave = LMH_VALU_TILE_ROWS;
-    p.lds = (size_t)cpl * 64 * 16;
-    return p;
-  }
   using seq = std::make_integer_sequence<int, 16>;
   switch (M) {
     case 1: row_plan_cpl<1>(p, cpl, seq{}); break;
@@ -801,40 +996,60 @@ ValuPlan valu_plan(int M, int K) {
   return p;
 }
 
-int launch_finalize(unsigned long long* slots, int nslots, int m_base, int mcount, const int32_t* d2t,
-                    int32_t* out_id, float* out_logit, hipStream_t stream) {
-  hipLaunchKernelGGL(finalize_argmax, dim3(mcount), dim3(256), 0, stream, slots, nslots, m_base, d2t, out_id,
-                     out_logit);
-  const hipError_t e = hipGetLastError();
-  return e == hipSuccess ? LMH_OK : hip_fail(e, "launch finalize_argmax");
+template <int TK, bool LOGITS>
+ValuPlan valu_epi_plan(int M, int K) {
+  switch (M) {
+    case 1: return tiled_plan<1, TK, LOGITS>(K);
+    case 2: return tiled_plan<2, TK, LOGITS>(K);
+    case 3: return tiled_plan<3, TK, LOGITS>(K);
+    case 4: return tiled_plan<4, TK, LOGITS>(K);
+    default: return ValuPlan{};
+  }
+}
+
+// Lets kernel `f` request the whole LDS of a workgroup, once per kernel.
+// Best effort: if the runtime does not take the attribute, the launch
+// itself reports an LDS request it cannot meet.
+void allow_full_lds(const void* f) {
+  static std::mutex mu;
+  static std::vector<const void*> done;
+  std::lock_guard<std::mutex> lock(mu);
+  if (std::find(done.begin(), done.end(), f) != done.end()) return;
+  if (hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, kLdsPerWorkgroup) != hipSuccess)
+    (void)hipGetLastError();
+  done.push_back(f);
 }
 
 int clamp_grid(int64_t need, int cus, int per_cu) {
   return (int)std::max<int64_t>(1, std::min<int64_t>({need, (int64_t)cus * per_cu, (int64_t)kMaxGrid}));
 }
 
-int launch_valu(const uint16_t* h, int M, int K, const uint16_t* W, int R, const int32_t* d2t,
-                int32_t* out_id, float* out_logit, unsigned long long* slots, hipStream_t stream) {
-  const ValuPlan p = valu_plan(M, K);
-  if (!p.fn) return LMH_EINVAL;
-  int cus = 0;
-  int st = cu_count(&cus);
-  if (st != LMH_OK) return st;
+// Persistent launch: as many workgroups as are resident (at most one round).
+template <typename F, typename... Args>
+int launch_persistent(F f, int threads, size_t lds, int64_t units, int units_per_wg, int cap_per_cu, int cus,
+                      hipStream_t stream, const char* what, int* grid_out, Args... args) {
+  allow_full_lds((const void*)f);
   int per_cu = 0;
-  st = resident_per_cu((const void*)p.fn, 64 * p.waves, p.lds, &per_cu);
+  const int st = resident_per_cu((const void*)f, threads, lds, &per_cu);
   if (st != LMH_OK) return st;
-  const int64_t rows_per_wg = (int64_t)p.waves * p.rows_per_wave;
-  const int grid = clamp_grid((R + rows_per_wg - 1) / rows_per_wg, cus, std::min(per_cu, LMH_VALU_WG_PER_CU));
-  hipLaunchKernelGGL(p.fn, dim3(grid), dim3(64 * p.waves), p.lds, stream, h, W, R, K, slots);
+  const int grid = clamp_grid((units + units_per_wg - 1) / units_per_wg, cus, std::min(per_cu, cap_per_cu));
+  hipLaunchKernelGGL(f, dim3(grid), dim3(threads), lds, stream, args...);
   const hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return hip_fail(e, "launch proj_argmax_valu");
-  return launch_finalize(slots, grid, 0, M, d2t, out_id, out_logit, stream);
+  if (e != hipSuccess) return hip_fail(e, what);
+  *grid_out = grid;
+  return LMH_OK;
 }
 
-constexpr int kLdsPerWorkgroup = 160 * 1024;
+int launch_valu(const ValuPlan& p, const uint16_t* h, int K, const uint16_t* W, int R, const Epi& epi, int cus,
+                hipStream_t stream, int* grid_out) {
+  if (!p.fn) return LMH_EINVAL;
+  return launch_persistent(p.fn, 64 * p.waves, p.lds, R, p.waves * p.rows_per_wave, LMH_VALU_WG_PER_CU, cus,
+                           stream, "launch VALU projection", grid_out, h, W, R, K, epi);
+}
 
-// Hidden rows one launch of the coalesced matrix-core kernel can stage for
-// K, with `waves` waves (each with its own 16-row stage).
+// Hidden rows one launch of the matrix-core kernel can stage for K with
+// `waves` waves (each with its own 16-row stage); the static key array of
+// the argmax epilogue is counted too.
 int mfma_lds_rows_fit(int64_t K, int waves) {
   const int64_t stage = (int64_t)waves * 16 * (4 * LMH_MFMA_LDS_SB + 1) * 16;
   const int64_t fixed = stage + (int64_t)waves * 32 * 8 + 512;
@@ -842,89 +1057,124 @@ int mfma_lds_rows_fit(int64_t K, int waves) {
   return (int)std::max<int64_t>(0, std::min<int64_t>(LMH_MAX_M, rows));
 }
 
-template <typename F>
-int launch_persistent(F f, int threads, size_t lds, int64_t units, int units_per_wg, int cus, hipStream_t stream,
-                      const char* what, int* grid_out, const uint16_t* h, const uint16_t* W, int R, int K,
-                      int m_base, int mp, unsigned long long* slots) {
-  static bool attr_done = false;  // one-time kernel attribute, same value every call
-  if (!attr_done) {
-    // Best effort: if the runtime does not take the attribute, the launch
-    // itself reports an LDS request it cannot meet.
-    if (hipFuncSetAttribute((const void*)f, hipFuncAttributeMaxDynamicSharedMemorySize, kLdsPerWorkgroup) !=
-        hipSuccess)
-      (void)hipGetLastError();
-    attr_done = true;
-  }
-  int per_cu = 0;
-  const int st = resident_per_cu((const void*)f, threads, lds, &per_cu);
-  if (st != LMH_OK) return st;
-  const int grid = clamp_grid((units + units_per_wg - 1) / units_per_wg, cus, per_cu);
-  hipLaunchKernelGGL(f, dim3(grid), dim3(threads), lds, stream, h, W, R, K, m_base, mp, slots);
-  const hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return hip_fail(e, what);
-  *grid_out = grid;
-  return LMH_OK;
-}
+// Largest top-k list a lane can keep for two 16-column tiles without
+// spilling; larger lists run 16 hidden rows per pass.
+constexpr int kMfmaMaxTkTwoTiles = 4;
 
 // One pass of the matrix-core path over hidden rows [m_base, m_base + mp):
 // 8 waves per workgroup when the hidden rows and eight stages fit the LDS,
 // else 4; two 16-column tiles when mp > 16.
-int launch_mfma_pass(const uint16_t* h, int K, int m_base, int mp, const uint16_t* W, int R,
-                     unsigned long long* slots, int cus, hipStream_t stream, int* grid_out) {
+template <int TK, bool LOGITS>
+int launch_mfma_pass(const uint16_t* h, int K, int m_base, int mp, const uint16_t* W, int R, const Epi& epi,
+                     int cus, hipStream_t stream, int* grid_out) {
   constexpr int SB = LMH_MFMA_LDS_SB;
   constexpr int D = LMH_MFMA_RING;
   const size_t hbytes = (size_t)mp * mfma_row_bytes(K);
   const int64_t tiles = (R + 15) / 16;
   const bool eight = mp <= mfma_lds_rows_fit(K, 8);
   const size_t lds = hbytes + (size_t)(eight ? 8 : 4) * 16 * (4 * SB + 1) * 16;
-  const char* what = "launch proj_argmax_mfma_lds";
+  const char* what = "launch matrix-core projection";
   if (mp <= 16)
-    return eight ? launch_persistent(proj_argmax_mfma_lds<1, SB, 8, D>, 512, lds, tiles, 8, cus, stream, what,
-                                     grid_out, h, W, R, K, m_base, mp, slots)
-                 : launch_persistent(proj_argmax_mfma_lds<1, SB, 4, D>, 256, lds, tiles, 4, cus, stream, what,
-                                     grid_out, h, W, R, K, m_base, mp, slots);
-  return eight ? launch_persistent(proj_argmax_mfma_lds<2, SB, 8, D>, 512, lds, tiles, 8, cus, stream, what,
-                                   grid_out, h, W, R, K, m_base, mp, slots)
-               : launch_persistent(proj_argmax_mfma_lds<2, SB, 4, D>, 256, lds, tiles, 4, cus, stream, what,
-                                   grid_out, h, W, R, K, m_base, mp, slots);
+    return eight ? launch_persistent(proj_mfma<1, SB, 8, D, TK, LOGITS>, 512, lds, tiles, 8, 1 << 20, cus, stream,
+                                     what, grid_out, h, W, R, K, m_base, mp, epi)
+                 : launch_persistent(proj_mfma<1, SB, 4, D, TK, LOGITS>, 256, lds, tiles, 4, 1 << 20, cus, stream,
+                                     what, grid_out, h, W, R, K, m_base, mp, epi);
+  if constexpr (TK <= kMfmaMaxTkTwoTiles) {
+    return eight ? launch_persistent(proj_mfma<2, SB, 8, D, TK, LOGITS>, 512, lds, tiles, 8, 1 << 20, cus, stream,
+                                     what, grid_out, h, W, R, K, m_base, mp, epi)
+                 : launch_persistent(proj_mfma<2, SB, 4, D, TK, LOGITS>, 256, lds, tiles, 4, 1 << 20, cus, stream,
+                                     what, grid_out, h, W, R, K, m_base, mp, epi);
+  } else {
+    return LMH_EINVAL;  // run() keeps such passes to 16 hidden rows
+  }
 }
 
-int launch_mfma(const uint16_t* h, int M, int K, const uint16_t* W, int R, const int32_t* d2t,
-                int32_t* out_id, float* out_logit, unsigned long long* slots, hipStream_t stream) {
+int launch_finalize_argmax(unsigned long long* slots, int nslots, int m_base, int mcount, const int32_t* d2t,
+                           int32_t* out_id, float* out_logit, hipStream_t stream) {
+  hipLaunchKernelGGL(finalize_argmax, dim3(mcount), dim3(256), 0, stream, slots, nslots, m_base, d2t, out_id,
+                     out_logit);
+  const hipError_t e = hipGetLastError();
+  return e == hipSuccess ? LMH_OK : hip_fail(e, "launch finalize_argmax");
+}
+
+template <int TK>
+int launch_finalize_topk(unsigned long long* slots, int nslots, int m_base, int mcount, int topk,
+                         const int32_t* d2t, int32_t* out_id, float* out_logit, hipStream_t stream) {
+  hipLaunchKernelGGL(finalize_topk<TK>, dim3(mcount), dim3(256), 0, stream, slots, nslots, m_base, topk, d2t,
+                     out_id, out_logit);
+  const hipError_t e = hipGetLastError();
+  return e == hipSuccess ? LMH_OK : hip_fail(e, "launch finalize_topk");
+}
+
+// What one call asks for.
+struct Call {
+  const uint16_t* h;
+  int M;
+  int K;
+  const uint16_t* W;
+  int R;
+  const int32_t* d2t;
+  int path;
+  hipStream_t stream;
+};
+
+// Argmax (TK == 1 with the argmax finalizer), top-TK, or every logit.
+// MODE: 0 = argmax, 1 = top-k, 2 = logits.
+template <int MODE, int TK>
+int run(const Call& c, const Epi& epi, int topk, int32_t* out_id, float* out_logit) {
+  constexpr bool LOGITS = MODE == 2;
   int cus = 0;
   int st = cu_count(&cus);
   if (st != LMH_OK) return st;
-  const int cap = mfma_lds_rows_fit(K, 4);
-  if (cap < 1) return LMH_EINVAL;
-  const int passes = (M + cap - 1) / cap;
-  const int per = (M + passes - 1) / passes;
-  for (int m0 = 0; m0 < M; m0 += per) {
-    const int mp = std::min(per, M - m0);
+  auto finalize = [&](int grid, int m_base, int mcount) -> int {
+    if constexpr (MODE == 0)
+      return launch_finalize_argmax(epi.slots, grid, m_base, mcount, c.d2t, out_id, out_logit, c.stream);
+    else if constexpr (MODE == 1)
+      return launch_finalize_topk<TK>(epi.slots, grid, m_base, mcount, topk, c.d2t, out_id, out_logit, c.stream);
+    else
+      return LMH_OK;
+  };
+  if (c.path == LMH_PATH_VALU) {
+    const ValuPlan p = MODE == 0 ? valu_argmax_plan(c.M, c.K) : valu_epi_plan<TK, LOGITS>(c.M, c.K);
     int grid = 0;
-    st = launch_mfma_pass(h, K, m0, mp, W, R, slots, cus, stream, &grid);
+    st = launch_valu(p, c.h, c.K, c.W, c.R, epi, cus, c.stream, &grid);
     if (st != LMH_OK) return st;
-    st = launch_finalize(slots, grid, m0, mp, d2t, out_id, out_logit, stream);
+    return finalize(grid, 0, c.M);
+  }
+  int cap = mfma_lds_rows_fit(c.K, 4);
+  if (MODE == 1 && TK > kMfmaMaxTkTwoTiles) cap = std::min(cap, 16);
+  if (cap < 1) return LMH_EINVAL;
+  const int passes = (c.M + cap - 1) / cap;
+  const int per = (c.M + passes - 1) / passes;
+  for (int m0 = 0; m0 < c.M; m0 += per) {
+    const int mp = std::min(per, c.M - m0);
+    int grid = 0;
+    st = launch_mfma_pass<TK, LOGITS>(c.h + (size_t)0, c.K, m0, mp, c.W, c.R, epi, cus, c.stream, &grid);
+    if (st != LMH_OK) return st;
+    st = finalize(grid, m0, mp);
     if (st != LMH_OK) return st;
   }
   return LMH_OK;
 }
 
-int project(const uint16_t* h, int64_t M, int64_t K, const uint16_t* W, int64_t R, const int32_t* d2t,
-            int32_t* out_id, float* out_logit, void* workspace, size_t workspace_bytes, int path,
-            void* stream) {
-  if (!h || !W || !out_id || !out_logit) return LMH_EINVAL;
+bool valu_epi_ok(int64_t M, int64_t K) { return M >= 1 && M <= 4 && k_ok(K); }
+
+// Shared argument checks; returns LMH_OK and the resolved path, or a status.
+int check_common(const uint16_t* h, int64_t M, int64_t K, const uint16_t* W, int64_t R, int mode, int* path) {
+  if (!h || !W) return LMH_EINVAL;
   if (M < 1 || M > LMH_MAX_M || !k_ok(K)) return LMH_EINVAL;
   if (R < 1 || R > kMaxRows) return LMH_EINVAL;
   if (!aligned16(h) || !aligned16(W)) return LMH_EINVAL;
-  if (path == LMH_PATH_AUTO) path = draft_project_auto_path(M, K);
-  if (path == LMH_PATH_VALU && !valu_ok(M, K)) return LMH_EINVAL;
-  if (path != LMH_PATH_VALU && path != LMH_PATH_MFMA) return LMH_EINVAL;
-  if (!workspace || !aligned16(workspace)) return LMH_EWORKSPACE;
-  if (workspace_bytes < draft_project_workspace_bytes(M)) return LMH_EWORKSPACE;
-  auto* slots = static_cast<unsigned long long*>(workspace);
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  if (path == LMH_PATH_VALU) return launch_valu(h, (int)M, (int)K, W, (int)R, d2t, out_id, out_logit, slots, s);
-  return launch_mfma(h, (int)M, (int)K, W, (int)R, d2t, out_id, out_logit, slots, s);
+  if (*path != LMH_PATH_AUTO && *path != LMH_PATH_VALU && *path != LMH_PATH_MFMA) return LMH_EINVAL;
+  if (*path == LMH_PATH_AUTO)
+    *path = (M <= LMH_VALU_AUTO_MAX_M && (mode == 0 ? valu_ok(M, K) : valu_epi_ok(M, K))) ? LMH_PATH_VALU
+                                                                                           : LMH_PATH_MFMA;
+  if (*path == LMH_PATH_VALU && !(mode == 0 ? valu_ok(M, K) : valu_epi_ok(M, K))) return LMH_EINVAL;
+  return LMH_OK;
+}
+
+int topk_width(int64_t topk) {
+  return topk <= 1 ? 1 : topk <= 2 ? 2 : topk <= 4 ? 4 : topk <= 8 ? 8 : 16;
 }
 
 }  // namespace
@@ -966,18 +1216,72 @@ int draft_project_auto_path(int64_t M, int64_t K) {
   return (M <= LMH_VALU_AUTO_MAX_M && valu_ok(M, K)) ? LMH_PATH_VALU : LMH_PATH_MFMA;
 }
 
-int draft_project_argmax(const uint16_t* h, int64_t M, int64_t K, const uint16_t* W, int64_t R,
-                         const int32_t* d2t, int32_t* out_id, float* out_logit, void* workspace,
-                         size_t workspace_bytes, void* stream) {
-  return project(h, M, K, W, R, d2t, out_id, out_logit, workspace, workspace_bytes, LMH_PATH_AUTO,
-                 stream);
-}
-
 int draft_project_argmax_path(const uint16_t* h, int64_t M, int64_t K, const uint16_t* W, int64_t R,
                               const int32_t* d2t, int32_t* out_id, float* out_logit, void* workspace,
                               size_t workspace_bytes, int path, void* stream) {
-  if (path != LMH_PATH_AUTO && path != LMH_PATH_VALU && path != LMH_PATH_MFMA) return LMH_EINVAL;
-  return project(h, M, K, W, R, d2t, out_id, out_logit, workspace, workspace_bytes, path, stream);
+  int st = check_common(h, M, K, W, R, 0, &path);
+  if (st != LMH_OK) return st;
+  if (!out_id || !out_logit) return LMH_EINVAL;
+  if (!workspace || !aligned16(workspace)) return LMH_EWORKSPACE;
+  if (workspace_bytes < draft_project_workspace_bytes(M)) return LMH_EWORKSPACE;
+  const Call c{h, (int)M, (int)K, W, (int)R, d2t, path, static_cast<hipStream_t>(stream)};
+  const Epi epi{static_cast<unsigned long long*>(workspace), nullptr, nullptr, 0, 0};
+  return run<0, 1>(c, epi, 1, out_id, out_logit);
+}
+
+int draft_project_argmax(const uint16_t* h, int64_t M, int64_t K, const uint16_t* W, int64_t R,
+                         const int32_t* d2t, int32_t* out_id, float* out_logit, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+  return draft_project_argmax_path(h, M, K, W, R, d2t, out_id, out_logit, workspace, workspace_bytes,
+                                   LMH_PATH_AUTO, stream);
+}
+
+size_t draft_project_topk_workspace_bytes(int64_t M, int64_t topk) {
+  if (M < 1 || M > LMH_MAX_M || topk < 1 || topk > LMH_MAX_TOPK) return 0;
+  return (size_t)M * kMaxGrid * topk_width(topk) * sizeof(unsigned long long);
+}
+
+int draft_project_topk(const uint16_t* h, int64_t M, int64_t K, const uint16_t* W, int64_t R,
+                       const int32_t* d2t, int64_t topk, int32_t* out_id, float* out_logit, void* workspace,
+                       size_t workspace_bytes, int path, void* stream) {
+  int st = check_common(h, M, K, W, R, 1, &path);
+  if (st != LMH_OK) return st;
+  if (topk < 1 || topk > LMH_MAX_TOPK || !out_id || !out_logit) return LMH_EINVAL;
+  if (!workspace || !aligned16(workspace)) return LMH_EWORKSPACE;
+  if (workspace_bytes < draft_project_topk_workspace_bytes(M, topk)) return LMH_EWORKSPACE;
+  const Call c{h, (int)M, (int)K, W, (int)R, d2t, path, static_cast<hipStream_t>(stream)};
+  const Epi epi{static_cast<unsigned long long*>(workspace), nullptr, nullptr, 0, 0};
+  switch (topk_width(topk)) {
+    case 1: return run<1, 1>(c, epi, (int)topk, out_id, out_logit);
+    case 2: return run<1, 2>(c, epi, (int)topk, out_id, out_logit);
+    case 4: return run<1, 4>(c, epi, (int)topk, out_id, out_logit);
+    case 8: return run<1, 8>(c, epi, (int)topk, out_id, out_logit);
+    default: return run<1, 16>(c, epi, (int)topk, out_id, out_logit);
+  }
+}
+
+int draft_project_logits(const uint16_t* h, int64_t M, int64_t K, const uint16_t* W, int64_t R,
+                         const int32_t* d2t, int64_t N, float* out, int path, void* stream) {
+  int st = check_common(h, M, K, W, R, 2, &path);
+  if (st != LMH_OK) return st;
+  if (!out || (reinterpret_cast<uintptr_t>(out) & 3u) != 0) return LMH_EINVAL;
+  const int64_t ncols = d2t ? N : R;
+  if (ncols < 1 || ncols > kMaxRows) return LMH_EINVAL;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (d2t) {
+    // scatter-after-matmul: columns the list does not reach stay -inf
+    int cus = 0;
+    st = cu_count(&cus);
+    if (st != LMH_OK) return st;
+    const size_t n = (size_t)M * (size_t)ncols;
+    const int grid = (int)std::max<int64_t>(1, std::min<int64_t>((int64_t)((n + 255) / 256), (int64_t)cus * 8));
+    hipLaunchKernelGGL(fill_neg_inf, dim3(grid), dim3(256), 0, s, out, n);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return hip_fail(e, "launch fill_neg_inf");
+  }
+  const Call c{h, (int)M, (int)K, W, (int)R, d2t, path, s};
+  const Epi epi{nullptr, out, d2t, ncols, ncols};
+  return run<2, 1>(c, epi, 0, nullptr, nullptr);
 }
 
 const char* lmhead_status_str(int status) {

@@ -20,13 +20,14 @@ __all__ = [
     "LMH_PATH_MFMA", "lmhead_trim", "draft_project_workspace_bytes", "draft_project_argmax",
     "draft_project_argmax_path", "draft_project_auto_path", "lmhead_status_str",
     "lmhead_last_error", "lmhead_bench_sink_words", "lmhead_bench_stream_read",
-    "lmhead_bench_copy", "new_workspace", "read_id_list",
+    "lmhead_bench_copy", "new_workspace", "read_id_list", "LMH_MAX_TOPK",
+    "draft_project_topk_workspace_bytes", "draft_project_topk", "draft_project_logits",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "liblmhead.so")
 
 LMH_OK, LMH_EINVAL, LMH_ERANGE, LMH_EWORKSPACE, LMH_EHIP = 0, 1, 2, 3, 4
-LMH_MAX_M, LMH_MIN_K, LMH_MAX_K = 32, 8, 8192
+LMH_MAX_M, LMH_MIN_K, LMH_MAX_K, LMH_MAX_TOPK = 32, 8, 8192, 16
 LMH_PATH_AUTO, LMH_PATH_VALU, LMH_PATH_MFMA = 0, 1, 2
 
 _P = ctypes.c_void_p
@@ -41,6 +42,9 @@ SIGNATURES = {
     "draft_project_argmax": (_INT, [_P, _I64, _I64, _P, _I64, _P, _P, _P, _P, _SZ, _P]),
     "draft_project_argmax_path": (_INT, [_P, _I64, _I64, _P, _I64, _P, _P, _P, _P, _SZ, _INT, _P]),
     "draft_project_auto_path": (_INT, [_I64, _I64]),
+    "draft_project_topk_workspace_bytes": (_SZ, [_I64, _I64]),
+    "draft_project_topk": (_INT, [_P, _I64, _I64, _P, _I64, _P, _I64, _P, _P, _P, _SZ, _INT, _P]),
+    "draft_project_logits": (_INT, [_P, _I64, _I64, _P, _I64, _P, _I64, _P, _INT, _P]),
     "lmhead_status_str": (ctypes.c_char_p, [_INT]),
     "lmhead_last_error": (ctypes.c_char_p, []),
     "lmhead_bench_sink_words": (_INT, []),
@@ -188,6 +192,74 @@ def draft_project_argmax(h, W, d2t=None, out_id=None, out_logit=None, workspace=
     """draft_project_argmax_path with the library's own kernel choice."""
     return draft_project_argmax_path(h, W, d2t, LMH_PATH_AUTO, out_id, out_logit, workspace,
                                      stream)
+
+
+def draft_project_topk_workspace_bytes(M: int, topk: int) -> int:
+    return int(lib().draft_project_topk_workspace_bytes(M, topk))
+
+
+def _check_hw(h, W, d2t):
+    _dev_tensor(h, "h", _BF16_LIKE, 2)
+    _dev_tensor(W, "W", _BF16_LIKE, 2)
+    m, k = h.shape
+    r, k2 = W.shape
+    if k != k2:
+        raise ValueError("h and W must have the same K")
+    if d2t is not None:
+        _dev_tensor(d2t, "d2t", (torch.int32,), 1)
+        if d2t.shape[0] != r:
+            raise ValueError("d2t must have one entry per row of W")
+    return m, k, r
+
+
+def draft_project_topk(h: torch.Tensor, W: torch.Tensor, d2t: torch.Tensor | None, topk: int,
+                       out_id: torch.Tensor | None = None, out_logit: torch.Tensor | None = None,
+                       workspace: torch.Tensor | None = None, path: int = LMH_PATH_AUTO,
+                       stream=None):
+    """(ids int32 [M, topk], logits float32 [M, topk]): the topk best rows of
+    W per hidden row, best first, mapped through d2t.  Never synchronizes."""
+    m, k, r = _check_hw(h, W, d2t)
+    if out_id is None:
+        out_id = torch.empty((m, topk), dtype=torch.int32, device=h.device)
+    if out_logit is None:
+        out_logit = torch.empty((m, topk), dtype=torch.float32, device=h.device)
+    _dev_tensor(out_id, "out_id", (torch.int32,), 2)
+    _dev_tensor(out_logit, "out_logit", (torch.float32,), 2)
+    if tuple(out_id.shape) != (m, topk) or tuple(out_logit.shape) != (m, topk):
+        raise ValueError("outputs must be [M, topk]")
+    st = _stream(stream, h.device)
+    if workspace is None:
+        nbytes = draft_project_topk_workspace_bytes(m, topk)
+        if nbytes == 0:
+            raise LmheadError(LMH_EINVAL, "draft_project_topk")
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=h.device)
+    code = lib().draft_project_topk(
+        h.data_ptr(), m, k, W.data_ptr(), r, d2t.data_ptr() if d2t is not None else None, topk,
+        out_id.data_ptr(), out_logit.data_ptr(), workspace.data_ptr(),
+        workspace.numel() * workspace.element_size(), path, st)
+    _check(code, "draft_project_topk")
+    return out_id, out_logit
+
+
+def draft_project_logits(h: torch.Tensor, W: torch.Tensor, d2t: torch.Tensor | None = None,
+                         n: int | None = None, out: torch.Tensor | None = None,
+                         path: int = LMH_PATH_AUTO, stream=None) -> torch.Tensor:
+    """float32 logits: [M, R] without d2t; with d2t, [M, n] with the list's
+    logits at their vocabulary ids and -inf elsewhere.  Never synchronizes."""
+    m, k, r = _check_hw(h, W, d2t)
+    cols = r if d2t is None else n
+    if cols is None:
+        raise ValueError("n (vocabulary size) is required with d2t")
+    if out is None:
+        out = torch.empty((m, cols), dtype=torch.float32, device=h.device)
+    _dev_tensor(out, "out", (torch.float32,), 2)
+    if tuple(out.shape) != (m, cols):
+        raise ValueError(f"out must be [{m}, {cols}]")
+    code = lib().draft_project_logits(
+        h.data_ptr(), m, k, W.data_ptr(), r, d2t.data_ptr() if d2t is not None else None,
+        cols if d2t is not None else 0, out.data_ptr(), path, _stream(stream, h.device))
+    _check(code, "draft_project_logits")
+    return out
 
 
 def read_id_list(path: str):
