@@ -90,6 +90,9 @@ constexpr int kValuMaxChunksTimesM = 40;   // register budget: 160 VGPRs of h
 constexpr int kMaxGrid = 1024;
 // LDS one workgroup may use on gfx950.
 constexpr int kLdsPerWorkgroup = 160 * 1024;
+// Largest top-k a matrix-core lane keeps in its own registers; larger k
+// keep each column's best 16 over its four lanes.
+constexpr int kLaneListMaxTk = 4;
 constexpr int64_t kMaxRows = (int64_t)1 << 30;  // keeps row arithmetic in int range
 constexpr uint32_t kBufferWord3 = 0x00020000u;  // gfx9 raw buffer, 32-bit data
 constexpr uint32_t kOobOffset = 0x80000000u;    // any offset >= num_records reads 0
@@ -199,6 +202,10 @@ __device__ __forceinline__ unsigned long long shfl_xor_u64(unsigned long long k,
 // max(old[j], min(old[j - 1], x)), which shifts every key below x down one
 // place.  Keys are unique (the row is in the low bits), so the list holds
 // the TK best rows seen, with the smaller row first among equal logits.
+// merge() folds in another sorted list with a bitonic network: the
+// element-wise maximum of one list and the other reversed holds the TK
+// best of both as a bitonic sequence, which log2(TK) half-cleaner stages
+// sort.
 template <int TK>
 struct KeyList {
   unsigned long long k[TK];
@@ -212,15 +219,95 @@ struct KeyList {
     for (int j = TK - 1; j >= 1; --j) k[j] = max_u64(k[j], min_u64(k[j - 1], x));
     k[0] = max_u64(k[0], x);
   }
+  __device__ __forceinline__ void merge(const unsigned long long (&o)[TK]) {
+#pragma unroll
+    for (int j = 0; j < TK; ++j) k[j] = max_u64(k[j], o[TK - 1 - j]);
+#pragma unroll
+    for (int st = TK / 2; st >= 1; st >>= 1)
+#pragma unroll
+      for (int j = 0; j < TK; ++j)
+        if ((j & st) == 0) {
+          const unsigned long long a = k[j], b = k[j + st];
+          k[j] = max_u64(a, b);
+          k[j + st] = min_u64(a, b);
+        }
+  }
   // fold in the list of lane (this lane ^ x)
   __device__ __forceinline__ void merge_xor(int x) {
     unsigned long long o[TK];
 #pragma unroll
     for (int j = 0; j < TK; ++j) o[j] = shfl_xor_u64(k[j], x);
-#pragma unroll
-    for (int j = 0; j < TK; ++j) push(o[j]);
+    merge(o);
   }
 };
+
+// Top-16 of one hidden row spread over the 16 lanes of a DPP row: lane j of
+// the row holds the j-th best key.  Inserting a key x (which may differ per
+// row): a lane whose key is below x takes the smaller of x and the key one
+// lane up, so keys below x move down one lane; the first lane of a row
+// sees all ones from above (bound_ctrl off keeps the old value).
+__device__ __forceinline__ void row_push(unsigned long long& k, unsigned long long x) {
+  const uint32_t plo = (uint32_t)__builtin_amdgcn_update_dpp(-1, (int)(uint32_t)k, 0x111, 0xF, 0xF, false);
+  const uint32_t phi =
+      (uint32_t)__builtin_amdgcn_update_dpp(-1, (int)(uint32_t)(k >> 32), 0x111, 0xF, 0xF, false);
+  const unsigned long long p = ((unsigned long long)phi << 32) | plo;
+  k = x > k ? min_u64(x, p) : k;
+}
+
+// Top-16 of one hidden row in the matrix-core output layout: the 4 lanes
+// g = 0..3 that hold a column each keep 4 keys, element e = 4 g + v of the
+// list in register v of lane g (so lanes differ by 16 g).  Bitonic networks
+// compare elements e and e ^ s: within a lane for s = 1, 2 and with the lane
+// 16 s / 4 away for s = 4, 8.
+template <bool ASC, int SIZE, int S>
+__device__ __forceinline__ void col_cx(unsigned long long (&c)[4], int g) {
+  // direction of the block of SIZE elements containing e: descending
+  // where (e & SIZE) == 0, flipped for an ascending sort
+  if constexpr (S >= 4) {
+    constexpr int kLaneXor = 16 * (S / 4);
+    const bool lower = (g & (S / 4)) == 0;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const bool desc = (((4 * g + v) & SIZE) == 0) != ASC;
+      const unsigned long long o = shfl_xor_u64(c[v], kLaneXor);
+      c[v] = (lower == desc) ? max_u64(c[v], o) : min_u64(c[v], o);
+    }
+  } else {
+#pragma unroll
+    for (int v = 0; v < 4; ++v)
+      if ((v & S) == 0) {
+        const bool desc = (((4 * g + v) & SIZE) == 0) != ASC;
+        const unsigned long long a = c[v], b = c[v + S];
+        const unsigned long long hi = max_u64(a, b), lo = min_u64(a, b);
+        c[v] = desc ? hi : lo;
+        c[v + S] = desc ? lo : hi;
+      }
+  }
+}
+
+// the half-cleaner stages S, S / 2, ..., 1 of a block of SIZE elements
+template <bool ASC, int SIZE, int S>
+__device__ __forceinline__ void col_stages(unsigned long long (&c)[4], int g) {
+  col_cx<ASC, SIZE, S>(c, g);
+  if constexpr (S > 1) col_stages<ASC, SIZE, S / 2>(c, g);
+}
+
+// bitonic sort of the 16 elements, ascending, built up from blocks of SIZE
+template <int SIZE>
+__device__ __forceinline__ void col_sort_asc(unsigned long long (&c)[4], int g) {
+  col_stages<true, SIZE, SIZE / 2>(c, g);
+  if constexpr (SIZE < 16) col_sort_asc<SIZE * 2>(c, g);
+}
+
+// list (descending) := best 16 of list and the 16 candidates c (any order)
+__device__ __forceinline__ void col_merge(unsigned long long (&list)[4], unsigned long long (&c)[4], int g) {
+  col_sort_asc<2>(c, g);
+  // descending list against ascending candidates: the element-wise maximum
+  // is bitonic and holds the best 16; sort it descending
+#pragma unroll
+  for (int v = 0; v < 4; ++v) list[v] = max_u64(list[v], c[v]);
+  col_stages<false, 16, 8>(list, g);
+}
 
 // Workgroup epilogue, run by wave 0 only: lane m < mcount publishes this
 // workgroup's best key for hidden row m_base + m into its own slot.  Slots
@@ -255,19 +342,22 @@ __device__ __forceinline__ void store_logit(const Epi& e, int m, int r, float v)
 }
 
 // Workgroup epilogue for TK > 1, run by wave 0: lane m < mcount merges the
-// per-wave lists lists[(w * ms + m) * TK + j] (in LDS) and publishes the
-// workgroup's TK keys.
-template <int TK, int WV>
+// per-wave sorted lists lists[(w * ms + m) * LS + j], j < TK (in LDS), and
+// publishes the workgroup's TK best keys, sorted.
+template <int TK, int WV, int LS>
 __device__ __forceinline__ void publish_lists(const unsigned long long* lists, int ms, int lane, int mcount,
                                               int m_base, unsigned long long* __restrict__ slots) {
   if (lane >= mcount) return;
   KeyList<TK> l;
 #pragma unroll
-  for (int j = 0; j < TK; ++j) l.k[j] = lists[lane * TK + j];
+  for (int j = 0; j < TK; ++j) l.k[j] = lists[lane * LS + j];
 #pragma unroll
-  for (int w = 1; w < WV; ++w)
+  for (int w = 1; w < WV; ++w) {
+    unsigned long long o[TK];
 #pragma unroll
-    for (int j = 0; j < TK; ++j) l.push(lists[(w * ms + lane) * TK + j]);
+    for (int j = 0; j < TK; ++j) o[j] = lists[(w * ms + lane) * LS + j];
+    l.merge(o);
+  }
   unsigned long long* dst = slots + ((size_t)(m_base + lane) * kMaxGrid + blockIdx.x) * TK;
 #pragma unroll
   for (int j = 0; j < TK; ++j) dst[j] = l.k[j];
@@ -309,10 +399,11 @@ finalize_argmax(const unsigned long long* __restrict__ slots, int nslots, int m_
   out_logit[m] = v;
 }
 
-// Top-TK version: one workgroup per hidden row merges the TK keys of each
-// of `nslots` workgroups (slots laid out [hidden row][workgroup][TK]) and
-// writes the best `topk` rows, mapped through d2t, best first.  Positions
-// with no row (R < topk) get id -1 and logit -inf.
+// Top-TK version: one workgroup per hidden row merges the sorted TK-key
+// lists of `nslots` workgroups (slots laid out [hidden row][workgroup][TK])
+// in a tree of bitonic merges and writes the best `topk` rows, mapped
+// through d2t, best first.  Positions with no row (R < topk) get id -1 and
+// logit -inf.
 template <int TK>
 __global__ void __launch_bounds__(256)
 finalize_topk(const unsigned long long* __restrict__ slots, int nslots, int m_base, int topk,
@@ -322,14 +413,21 @@ finalize_topk(const unsigned long long* __restrict__ slots, int nslots, int m_ba
   const unsigned long long* row = slots + (size_t)m * kMaxGrid * TK;
   KeyList<TK> l;
   l.clear();
-  for (int i = threadIdx.x; i < nslots * TK; i += 256) l.push(row[i]);
+  for (int i = threadIdx.x; i < nslots; i += 256) {
+    unsigned long long o[TK];
+#pragma unroll
+    for (int j = 0; j < TK; ++j) o[j] = row[(size_t)i * TK + j];
+    l.merge(o);
+  }
 #pragma unroll
   for (int j = 0; j < TK; ++j) s_list[threadIdx.x][j] = l.k[j];
   __syncthreads();
   for (int half = 128; half >= 1; half >>= 1) {
     if (threadIdx.x < half) {
+      unsigned long long o[TK];
 #pragma unroll
-      for (int j = 0; j < TK; ++j) l.push(s_list[threadIdx.x + half][j]);
+      for (int j = 0; j < TK; ++j) o[j] = s_list[threadIdx.x + half][j];
+      l.merge(o);
 #pragma unroll
       for (int j = 0; j < TK; ++j) s_list[threadIdx.x][j] = l.k[j];
     }
@@ -501,17 +599,18 @@ proj_valu_tiled(const uint16_t* __restrict__ h, const uint16_t* __restrict__ W, 
   }
   __syncthreads();
 
-  // epilogue state: the running best row (TK == 1) or the TK best keys
+  // epilogue state: the running best row (TK == 1), or for TK > 1 the
+  // best 16 keys of hidden row rho = lane / 16 spread over that DPP row
+  static_assert(TK == 1 || LOGITS || (M <= 4 && TK <= 16), "a DPP row holds one hidden row's top 16");
   float best[M];
   int bidx[M];
-  KeyList<TK> lists[(TK > 1 && !LOGITS) ? M : 1];
 #pragma unroll
   for (int m = 0; m < M; ++m) {
     best[m] = 0.0f;
     bidx[m] = -1;
   }
-#pragma unroll
-  for (int m = 0; m < ((TK > 1 && !LOGITS) ? M : 1); ++m) lists[m].clear();
+  unsigned long long rkey = 0ull;
+  const int rho = lane >> 4;
   float acc[TR][M];
 #pragma unroll
   for (int q = 0; q < TR; ++q)
@@ -542,21 +641,30 @@ proj_valu_tiled(const uint16_t* __restrict__ h, const uint16_t* __restrict__ W, 
     if (j == nb - 1) {
       const int r0 = tile * TR;
 #pragma unroll
-      for (int q = 0; q < TR; ++q)
+      for (int q = 0; q < TR; ++q) {
+        float sum[M];
 #pragma unroll
         for (int m = 0; m < M; ++m) {
-          const float sum = wave_sum(acc[q][m]);
+          sum[m] = wave_sum(acc[q][m]);
           acc[q][m] = 0.0f;
-          if (r0 + q < R) {
-            if constexpr (LOGITS) {
-              if (lane == 0) store_logit(epi, m, r0 + q, sum);
-            } else if constexpr (TK == 1) {
-              take_best(sum, r0 + q, best[m], bidx[m]);
-            } else {
-              lists[m].push(pack_key(sum, r0 + q));
+        }
+        if (r0 + q < R) {
+          if constexpr (LOGITS) {
+            if (lane == 0) {
+#pragma unroll
+              for (int m = 0; m < M; ++m) store_logit(epi, m, r0 + q, sum[m]);
             }
+          } else if constexpr (TK == 1) {
+#pragma unroll
+            for (int m = 0; m < M; ++m) take_best(sum[m], r0 + q, best[m], bidx[m]);
+          } else {
+            float x = sum[0];
+#pragma unroll
+            for (int m = 1; m < M; ++m) x = rho == m ? sum[m] : x;
+            row_push(rkey, pack_key(x, r0 + q));
           }
         }
+      }
     }
   };
   auto advance = [&](int& tile, int& j) {
@@ -607,16 +715,11 @@ proj_valu_tiled(const uint16_t* __restrict__ h, const uint16_t* __restrict__ W, 
     }
     publish_workgroup(key, lane, M, 0, epi.slots);
   } else {
-    __shared__ unsigned long long s_list[WV * M * TK];
-    if (lane == 0) {
-#pragma unroll
-      for (int m = 0; m < M; ++m)
-#pragma unroll
-        for (int jj = 0; jj < TK; ++jj) s_list[(wave * M + m) * TK + jj] = lists[m].k[jj];
-    }
+    __shared__ unsigned long long s_list[WV * M * 16];
+    if (rho < M) s_list[(wave * M + rho) * 16 + (lane & 15)] = rkey;
     __syncthreads();
     if (wave != 0) return;
-    publish_lists<TK, WV>(s_list, M, lane, M, 0, epi.slots);
+    publish_lists<TK, WV, 16>(s_list, M, lane, M, 0, epi.slots);
   }
 }
 
@@ -669,17 +772,27 @@ proj_mfma(const uint16_t* __restrict__ h, const uint16_t* __restrict__ W, int R,
   }
 
   // epilogue state of this lane's column (hidden row) in each 16-column
-  // tile: the running best row (TK == 1) or the TK best keys
+  // tile: the running best row (TK == 1); for TK <= 4 the TK best keys of
+  // the rows this lane saw; for larger TK the column's best 16 spread over
+  // its 4 lanes (col_merge)
+  constexpr bool kLaneLists = TK > 1 && TK <= kLaneListMaxTk && !LOGITS;
+  constexpr bool kColLists = TK > kLaneListMaxTk && !LOGITS;
+  static_assert(TK <= 16, "a column list holds 16 keys");
   float best[NT];
   int bidx[NT];
-  KeyList<TK> lists[(TK > 1 && !LOGITS) ? NT : 1];
+  KeyList<TK> lists[kLaneLists ? NT : 1];
+  unsigned long long clist[kColLists ? NT : 1][4];
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
     best[nt] = 0.0f;
     bidx[nt] = -1;
   }
 #pragma unroll
-  for (int nt = 0; nt < ((TK > 1 && !LOGITS) ? NT : 1); ++nt) lists[nt].clear();
+  for (int nt = 0; nt < (kLaneLists ? NT : 1); ++nt) lists[nt].clear();
+#pragma unroll
+  for (int nt = 0; nt < (kColLists ? NT : 1); ++nt)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) clist[nt][v] = 0ull;
   f32x4 acc[NT];
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -742,7 +855,7 @@ proj_mfma(const uint16_t* __restrict__ h, const uint16_t* __restrict__ W, int R,
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   };
-  auto finish_tile = [&](int tile) {
+  auto finish_tile = [&](int tile) __attribute__((always_inline)) {
     const int r0 = tile * 16;
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
@@ -755,10 +868,22 @@ proj_mfma(const uint16_t* __restrict__ h, const uint16_t* __restrict__ W, int R,
             if (col < mp) store_logit(epi, m_base + col, r, acc[nt][v]);
           } else if constexpr (TK == 1) {
             take_best(acc[nt][v], r, best[nt], bidx[nt]);
-          } else {
+          } else if constexpr (kLaneLists) {
             lists[nt].push(pack_key(acc[nt][v], r));
           }
         }
+      }
+    }
+    if constexpr (kColLists) {
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        unsigned long long c[4];
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const int r = r0 + 4 * g + v;
+          c[v] = r < R ? pack_key(acc[nt][v], r) : 0ull;
+        }
+        col_merge(clist[nt], c, g);
       }
     }
 #pragma unroll
@@ -786,7 +911,7 @@ proj_mfma(const uint16_t* __restrict__ h, const uint16_t* __restrict__ W, int R,
     issue(ring[j], ti, bi);
     advance(ti, bi);
   }
-  auto step = [&](auto jc) {
+  auto step = [&](auto jc) __attribute__((always_inline)) {
     constexpr int j = decltype(jc)::value;
     issue(ring[(j + D - 1) % D], ti, bi);
     advance(ti, bi);
@@ -825,6 +950,21 @@ proj_mfma(const uint16_t* __restrict__ h, const uint16_t* __restrict__ W, int R,
       for (int w = 0; w < WV; ++w) key = s_key[w][lane] > key ? s_key[w][lane] : key;
     }
     publish_workgroup(key, lane, mp, m_base, epi.slots);
+  } else if constexpr (kColLists) {
+    // every wave is past its main loop: the stage area is free for the lists
+    __syncthreads();
+    unsigned long long* s_list = reinterpret_cast<unsigned long long*>(lds + mp * row_chunks);
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      const int col = nt * 16 + i16;
+      if (col < mp) {
+#pragma unroll
+        for (int v = 0; v < 4; ++v) s_list[(wave * 32 + col) * 16 + 4 * g + v] = clist[nt][v];
+      }
+    }
+    __syncthreads();
+    if (wave != 0) return;
+    publish_lists<TK, WV, 16>(s_list, 32, lane, mp, m_base, epi.slots);
   } else {
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
@@ -844,7 +984,7 @@ proj_mfma(const uint16_t* __restrict__ h, const uint16_t* __restrict__ W, int R,
     }
     __syncthreads();
     if (wave != 0) return;
-    publish_lists<TK, WV>(s_list, 32, lane, mp, m_base, epi.slots);
+    publish_lists<TK, WV, TK>(s_list, 32, lane, mp, m_base, epi.slots);
   }
 }
 
@@ -1057,10 +1197,6 @@ int mfma_lds_rows_fit(int64_t K, int waves) {
   return (int)std::max<int64_t>(0, std::min<int64_t>(LMH_MAX_M, rows));
 }
 
-// Largest top-k list a lane can keep for two 16-column tiles without
-// spilling; larger lists run 16 hidden rows per pass.
-constexpr int kMfmaMaxTkTwoTiles = 4;
-
 // One pass of the matrix-core path over hidden rows [m_base, m_base + mp):
 // 8 waves per workgroup when the hidden rows and eight stages fit the LDS,
 // else 4; two 16-column tiles when mp > 16.
@@ -1079,14 +1215,10 @@ int launch_mfma_pass(const uint16_t* h, int K, int m_base, int mp, const uint16_
                                      what, grid_out, h, W, R, K, m_base, mp, epi)
                  : launch_persistent(proj_mfma<1, SB, 4, D, TK, LOGITS>, 256, lds, tiles, 4, 1 << 20, cus, stream,
                                      what, grid_out, h, W, R, K, m_base, mp, epi);
-  if constexpr (TK <= kMfmaMaxTkTwoTiles) {
-    return eight ? launch_persistent(proj_mfma<2, SB, 8, D, TK, LOGITS>, 512, lds, tiles, 8, 1 << 20, cus, stream,
-                                     what, grid_out, h, W, R, K, m_base, mp, epi)
-                 : launch_persistent(proj_mfma<2, SB, 4, D, TK, LOGITS>, 256, lds, tiles, 4, 1 << 20, cus, stream,
-                                     what, grid_out, h, W, R, K, m_base, mp, epi);
-  } else {
-    return LMH_EINVAL;  // run() keeps such passes to 16 hidden rows
-  }
+  return eight ? launch_persistent(proj_mfma<2, SB, 8, D, TK, LOGITS>, 512, lds, tiles, 8, 1 << 20, cus, stream,
+                                   what, grid_out, h, W, R, K, m_base, mp, epi)
+               : launch_persistent(proj_mfma<2, SB, 4, D, TK, LOGITS>, 256, lds, tiles, 4, 1 << 20, cus, stream,
+                                   what, grid_out, h, W, R, K, m_base, mp, epi);
 }
 
 int launch_finalize_argmax(unsigned long long* slots, int nslots, int m_base, int mcount, const int32_t* d2t,
@@ -1141,8 +1273,7 @@ int run(const Call& c, const Epi& epi, int topk, int32_t* out_id, float* out_log
     if (st != LMH_OK) return st;
     return finalize(grid, 0, c.M);
   }
-  int cap = mfma_lds_rows_fit(c.K, 4);
-  if (MODE == 1 && TK > kMfmaMaxTkTwoTiles) cap = std::min(cap, 16);
+  const int cap = mfma_lds_rows_fit(c.K, 4);
   if (cap < 1) return LMH_EINVAL;
   const int passes = (c.M + cap - 1) / cap;
   const int per = (c.M + passes - 1) / passes;
