@@ -151,7 +151,8 @@ int draft_project_argmax_path(const uint16_t* h, int64_t M, int64_t K,
  *  topk       1 .. LMH_MAX_TOPK.
  *  workspace  draft_project_topk_workspace_bytes(M, topk) bytes, 16-byte
  *             aligned; contents irrelevant, as for draft_project_argmax.
- *  path       LMH_PATH_AUTO, or LMH_PATH_VALU (M <= 4) / LMH_PATH_MFMA.
+ *  path       LMH_PATH_AUTO, or LMH_PATH_VALU (M <= 4 with
+ *             M * ceil(K / 512) <= 40) / LMH_PATH_MFMA.
  * Other arguments, synchronization and errors as for draft_project_argmax.
  */
 size_t draft_project_topk_workspace_bytes(int64_t M, int64_t topk);

@@ -132,6 +132,7 @@ def test_logits_rejects_on_host(L):
     assert f(A, 1, 2560, B, 100, None, 0, C + 2, 0, None) == 1         # misaligned output
     assert f(A, 1, 2560, B, 100, D, 0, C, 0, None) == 1                # d2t needs N >= 1
     assert f(A, 5, 2560, B, 100, None, 0, C, 1, None) == 1             # VALU epilogues: M <= 4
+    assert f(A, 3, 8192, B, 100, None, 0, C, 1, None) == 1             # and M * ceil(K / 512) <= 40
     assert f(A, 1, 12, B, 100, None, 0, C, 0, None) == 1
 
 

@@ -20,10 +20,11 @@ def L():
     return lmhead
 
 
-def epi_paths(L, m):
-    """The top-k / logits epilogues run on the tiled VALU kernel for M <= 4
-    and on the matrix-core kernel for any M."""
-    return [L.LMH_PATH_VALU, L.LMH_PATH_MFMA] if m <= 4 else [L.LMH_PATH_MFMA]
+def epi_paths(L, m, k=2560):
+    """The top-k / logits epilogues run on the VALU kernels for M <= 4 with
+    M * ceil(K / 512) <= 40, and on the matrix-core kernel for any M."""
+    valu = m <= 4 and m * ((k // 8 + 63) // 64) <= 40
+    return [L.LMH_PATH_VALU, L.LMH_PATH_MFMA] if valu else [L.LMH_PATH_MFMA]
 
 
 def run_topk(L, hs, w_np, w_dev, d2t_np, k, tag):
@@ -88,7 +89,7 @@ def test_topk_edges(L, m, k, r, topk):
     h_np = synth.hidden(4000 + k, m, m, k)
     d2t = (np.arange(r, dtype=np.int32)[::-1] * 3 + 1).copy()
     w_dev = dev_bf16(w_np)
-    for p in epi_paths(L, m):
+    for p in epi_paths(L, m, k):
         for dd in (None, d2t):
             i, l = L.draft_project_topk(dev_bf16(h_np), w_dev, dev_i32(dd) if dd is not None else None,
                                         topk, path=p)
@@ -197,7 +198,7 @@ def test_logits_edges(L, m, k, r):
     n = 3 * r + 5
     d2t = (np.arange(r, dtype=np.int32) * 3 + 2)
     w_dev = dev_bf16(w_np)
-    for p in epi_paths(L, m):
+    for p in epi_paths(L, m, k):
         out = L.draft_project_logits(dev_bf16(h_np), w_dev, None, path=p)
         check_logits(h_np, w_np, None, None, out.cpu().numpy())
         sc = L.draft_project_logits(dev_bf16(h_np), w_dev, dev_i32(d2t), n=n, path=p)

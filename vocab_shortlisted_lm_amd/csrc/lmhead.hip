@@ -241,17 +241,55 @@ struct KeyList {
   }
 };
 
-// Top-16 of one hidden row spread over the 16 lanes of a DPP row: lane j of
-// the row holds the j-th best key.  Inserting a key x (which may differ per
-// row): a lane whose key is below x takes the smaller of x and the key one
-// lane up, so keys below x move down one lane; the first lane of a row
-// sees all ones from above (bound_ctrl off keeps the old value).
-__device__ __forceinline__ void row_push(unsigned long long& k, unsigned long long x) {
-  const uint32_t plo = (uint32_t)__builtin_amdgcn_update_dpp(-1, (int)(uint32_t)k, 0x111, 0xF, 0xF, false);
-  const uint32_t phi =
-      (uint32_t)__builtin_amdgcn_update_dpp(-1, (int)(uint32_t)(k >> 32), 0x111, 0xF, 0xF, false);
-  const unsigned long long p = ((unsigned long long)phi << 32) | plo;
-  k = x > k ? min_u64(x, p) : k;
+// Top-16 of each hidden row m < M (<= 4) spread over the 16 lanes of DPP
+// row m: lane j of the row holds the j-th best (logit, row) pair, an empty
+// place (-inf, -1).  The VALU kernels hand a wave its head rows in
+// increasing order, so a new row r loses every tie with the rows already
+// held: in key order (larger logit, then smaller row) it beats a held pair
+// exactly when its logit is larger, and plain fp32 compares decide.
+// Inserting: a lane whose pair is below the new one takes the smaller of
+// the new pair and the pair one lane up, so pairs below it move down one
+// lane; the first lane of a row sees +inf from above (bound_ctrl off keeps
+// the old value).  pack_key turns a pair into the 64-bit key.
+struct RowTop16 {
+  float val;
+  int row;
+  __device__ __forceinline__ void clear() {
+    val = -__builtin_inff();
+    row = -1;
+  }
+  template <int M>
+  __device__ __forceinline__ void push(const float (&sum)[M], int r, int rho) {
+    const float pv = __builtin_bit_cast(
+        float, __builtin_amdgcn_update_dpp(0x7F800000, __builtin_bit_cast(int, val), 0x111, 0xF, 0xF, false));
+    const int pr = __builtin_amdgcn_update_dpp(-1, row, 0x111, 0xF, 0xF, false);
+    float nv = val;
+    int nr = row;
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+      if (rho == m && sum[m] > val) {  // selects, no branch
+        const bool here = sum[m] <= pv;
+        nv = here ? sum[m] : pv;
+        nr = here ? r : pr;
+      }
+    }
+    val = nv;
+    row = nr;
+  }
+};
+
+// Best 16 of two lists each laid out over the 16 lanes of a DPP row (lane
+// j = element j, descending): the element-wise maximum of a and b mirrored
+// is bitonic and holds the best 16, which four half-cleaner stages sort.
+// j = lane % 16.  Every lane of the row must take part.
+__device__ __forceinline__ unsigned long long row_merge(unsigned long long a, unsigned long long b, int j) {
+  unsigned long long c = max_u64(a, shfl_xor_u64(b, 15));
+#pragma unroll
+  for (int s = 8; s >= 1; s >>= 1) {
+    const unsigned long long o = shfl_xor_u64(c, s);
+    c = (j & s) == 0 ? max_u64(c, o) : min_u64(c, o);
+  }
+  return c;
 }
 
 // Top-16 of one hidden row in the matrix-core output layout: the 4 lanes
@@ -341,26 +379,24 @@ __device__ __forceinline__ void store_logit(const Epi& e, int m, int r, float v)
   e.logits[(int64_t)m * e.ld + col] = v;
 }
 
-// Workgroup epilogue for TK > 1, run by wave 0: lane m < mcount merges the
-// per-wave sorted lists lists[(w * ms + m) * LS + j], j < TK (in LDS), and
-// publishes the workgroup's TK best keys, sorted.
+// Workgroup epilogue for TK > 1, run by every thread after a barrier: the
+// sorted per-wave lists of hidden row c are in LDS at lists[(w * ms + c) *
+// LS + j], j < LS (LS = 16, or TK for shorter lists).  Each DPP row of the
+// workgroup merges the WV lists of one hidden row (row_merge) and
+// publishes its TK best keys, sorted, into the workgroup's slot.
 template <int TK, int WV, int LS>
-__device__ __forceinline__ void publish_lists(const unsigned long long* lists, int ms, int lane, int mcount,
-                                              int m_base, unsigned long long* __restrict__ slots) {
-  if (lane >= mcount) return;
-  KeyList<TK> l;
+__device__ __forceinline__ void publish_rows(const unsigned long long* lists, int ms, int mcount, int m_base,
+                                             unsigned long long* __restrict__ slots) {
+  const int j = threadIdx.x & 15;
+  const int row = threadIdx.x >> 4;
+  for (int c0 = 0; c0 < mcount; c0 += (int)(blockDim.x >> 4)) {
+    const int col = c0 + row;
+    const int cc = col < mcount ? col : 0;  // a row with no hidden row merges row 0 and drops it
+    unsigned long long k = j < LS ? lists[cc * LS + j] : 0ull;
 #pragma unroll
-  for (int j = 0; j < TK; ++j) l.k[j] = lists[lane * LS + j];
-#pragma unroll
-  for (int w = 1; w < WV; ++w) {
-    unsigned long long o[TK];
-#pragma unroll
-    for (int j = 0; j < TK; ++j) o[j] = lists[(w * ms + lane) * LS + j];
-    l.merge(o);
+    for (int w = 1; w < WV; ++w) k = row_merge(k, j < LS ? lists[(w * ms + cc) * LS + j] : 0ull, j);
+    if (col < mcount && j < TK) slots[((size_t)(m_base + col) * kMaxGrid + blockIdx.x) * TK + j] = k;
   }
-  unsigned long long* dst = slots + ((size_t)(m_base + lane) * kMaxGrid + blockIdx.x) * TK;
-#pragma unroll
-  for (int j = 0; j < TK; ++j) dst[j] = l.k[j];
 }
 
 // One workgroup per hidden row: fold the `nslots` workgroup keys, decode
@@ -400,50 +436,50 @@ finalize_argmax(const unsigned long long* __restrict__ slots, int nslots, int m_
 }
 
 // Top-TK version: one workgroup per hidden row merges the sorted TK-key
-// lists of `nslots` workgroups (slots laid out [hidden row][workgroup][TK])
-// in a tree of bitonic merges and writes the best `topk` rows, mapped
-// through d2t, best first.  Positions with no row (R < topk) get id -1 and
-// logit -inf.
+// lists of `nslots` (<= kMaxGrid) workgroups (slots laid out [hidden row]
+// [workgroup][TK]) and writes the best `topk` rows, mapped through d2t, best
+// first.  Each of the 64 DPP rows of the workgroup loads its lists (every
+// 64th) at once and folds them (row_merge); a tree through LDS folds the 64
+// rows.  Positions with no row (R < topk) get id -1 and logit -inf.
+constexpr int kFinalizeTopkThreads = 1024;
+constexpr int kFinalizeTopkRows = kFinalizeTopkThreads / 16;
+constexpr int kFinalizeTopkPerRow = kMaxGrid / kFinalizeTopkRows;
+
 template <int TK>
-__global__ void __launch_bounds__(256)
+__global__ void __launch_bounds__(kFinalizeTopkThreads)
 finalize_topk(const unsigned long long* __restrict__ slots, int nslots, int m_base, int topk,
               const int32_t* __restrict__ d2t, int32_t* __restrict__ out_id, float* __restrict__ out_logit) {
-  __shared__ unsigned long long s_list[256][TK];
+  __shared__ unsigned long long s_rows[kFinalizeTopkRows][16];
   const int m = m_base + blockIdx.x;
-  const unsigned long long* row = slots + (size_t)m * kMaxGrid * TK;
-  KeyList<TK> l;
-  l.clear();
-  for (int i = threadIdx.x; i < nslots; i += 256) {
-    unsigned long long o[TK];
+  const unsigned long long* lists = slots + (size_t)m * kMaxGrid * TK;
+  const int j = threadIdx.x & 15;
+  const int rr = threadIdx.x >> 4;
+  unsigned long long x[kFinalizeTopkPerRow];
 #pragma unroll
-    for (int j = 0; j < TK; ++j) o[j] = row[(size_t)i * TK + j];
-    l.merge(o);
+  for (int u = 0; u < kFinalizeTopkPerRow; ++u) {
+    const int i = rr + kFinalizeTopkRows * u;
+    x[u] = (i < nslots && j < TK) ? lists[(size_t)i * TK + j] : 0ull;
   }
+  unsigned long long k = x[0];
 #pragma unroll
-  for (int j = 0; j < TK; ++j) s_list[threadIdx.x][j] = l.k[j];
+  for (int u = 1; u < kFinalizeTopkPerRow; ++u)
+    if (kFinalizeTopkRows * u < nslots) k = row_merge(k, x[u], j);  // uniform condition
+  s_rows[rr][j] = k;
   __syncthreads();
-  for (int half = 128; half >= 1; half >>= 1) {
-    if (threadIdx.x < half) {
-      unsigned long long o[TK];
 #pragma unroll
-      for (int j = 0; j < TK; ++j) o[j] = s_list[threadIdx.x + half][j];
-      l.merge(o);
-#pragma unroll
-      for (int j = 0; j < TK; ++j) s_list[threadIdx.x][j] = l.k[j];
+  for (int half = kFinalizeTopkRows / 2; half >= 1; half >>= 1) {
+    if (rr < half) {
+      k = row_merge(k, s_rows[rr + half][j], j);
+      s_rows[rr][j] = k;
     }
     __syncthreads();
   }
-  if (threadIdx.x != 0) return;
-#pragma unroll
-  for (int j = 0; j < TK; ++j) {
-    if (j < topk) {
-      const unsigned long long k = l.k[j];
-      float v = -__builtin_inff();
-      int idx = -1;
-      if (k != 0ull) unpack_key(k, v, idx);
-      out_id[(size_t)m * topk + j] = idx < 0 ? -1 : (d2t ? d2t[idx] : idx);
-      out_logit[(size_t)m * topk + j] = v;
-    }
+  if (rr == 0 && j < topk) {
+    float v = -__builtin_inff();
+    int idx = -1;
+    if (k != 0ull) unpack_key(k, v, idx);
+    out_id[(size_t)m * topk + j] = idx < 0 ? -1 : (d2t ? d2t[idx] : idx);
+    out_logit[(size_t)m * topk + j] = v;
   }
 }
 
@@ -474,16 +510,76 @@ gather_rows(const uint16_t* __restrict__ W, int64_t N, int K, const int32_t* __r
   }
 }
 
+// Epilogue of the VALU kernels, where every row sum is wave-uniform after
+// the DPP reduction: the running best row per hidden row (TK == 1), the
+// best 16 keys of hidden row rho = lane / 16 over that DPP row (TK > 1,
+// M <= 4), or the logit itself stored by lane 0 (LOGITS).
+template <int M, int WV, int TK, bool LOGITS>
+struct ValuEpilogue {
+  static_assert(TK == 1 || LOGITS || (M <= 4 && TK <= 16), "a DPP row holds one hidden row's top 16");
+  float best[M];
+  int bidx[M];
+  RowTop16 top;
+
+  __device__ __forceinline__ void init() {
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+      best[m] = 0.0f;
+      bidx[m] = -1;
+    }
+    top.clear();
+  }
+  // head row r (< R) has logit sum[m] against hidden row m
+  __device__ __forceinline__ void row(const float (&sum)[M], int r, int lane, const Epi& e) {
+    if constexpr (LOGITS) {
+      if (lane == 0) {
+#pragma unroll
+        for (int m = 0; m < M; ++m) store_logit(e, m, r, sum[m]);
+      }
+    } else if constexpr (TK == 1) {
+#pragma unroll
+      for (int m = 0; m < M; ++m) take_best(sum[m], r, best[m], bidx[m]);
+    } else {
+      top.push<M>(sum, r, lane >> 4);
+    }
+  }
+  // fold the waves of the workgroup and publish its keys
+  __device__ __forceinline__ void finish(int lane, int wave, const Epi& e) {
+    if constexpr (LOGITS) {
+      return;
+    } else if constexpr (TK == 1) {
+      __shared__ unsigned long long s_key[WV][M];
+      if (lane == 0) {
+#pragma unroll
+        for (int m = 0; m < M; ++m) s_key[wave][m] = pack_key(best[m], bidx[m]);
+      }
+      __syncthreads();
+      if (wave != 0) return;
+      unsigned long long key = 0ull;
+      if (lane < M) {
+#pragma unroll
+        for (int w = 0; w < WV; ++w) key = s_key[w][lane] > key ? s_key[w][lane] : key;
+      }
+      publish_workgroup(key, lane, M, 0, e.slots);
+    } else {
+      __shared__ unsigned long long s_list[WV * M * 16];
+      const int rho = lane >> 4;
+      if (rho < M) s_list[(wave * M + rho) * 16 + (lane & 15)] = pack_key(top.val, top.row);
+      __syncthreads();
+      publish_rows<TK, WV, 16>(s_list, M, M, 0, e.slots);
+    }
+  }
+};
+
 // ---------------------------------------------------------------------------
 // VALU path: one wave per head row, hidden rows in registers
 // ---------------------------------------------------------------------------
 // Lane `l` owns the 16-byte chunks c = l + 64 j (j < CPL) of every row, so
 // one load instruction moves 1 KiB of a row, fully coalesced.  Chunks past
 // the row end get an out-of-range buffer offset and read as zero.
-template <int M, int CPL, int U, int WV>
+template <int M, int CPL, int U, int WV, int TK, bool LOGITS>
 __global__ void __launch_bounds__(64 * WV)
 proj_valu_rows(const uint16_t* __restrict__ h, const uint16_t* __restrict__ W, int R, int K, Epi epi) {
-  __shared__ unsigned long long s_key[WV][M];
   const int lane = threadIdx.x & 63;
   const int wave = wave_id();
   const int chunks = K >> 3;
@@ -502,13 +598,8 @@ proj_valu_rows(const uint16_t* __restrict__ h, const uint16_t* __restrict__ W, i
     }
   }
 
-  float best[M];
-  int bidx[M];
-#pragma unroll
-  for (int m = 0; m < M; ++m) {
-    best[m] = 0.0f;
-    bidx[m] = -1;
-  }
+  ValuEpilogue<M, WV, TK, LOGITS> ep;
+  ep.init();
 
   const int step = gridDim.x * WV * U;
   u32x4 wa[U][CPL], wb[U][CPL];
@@ -526,14 +617,15 @@ proj_valu_rows(const uint16_t* __restrict__ h, const uint16_t* __restrict__ W, i
   auto score_rows = [&](const u32x4 (&w)[U][CPL], int r0) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
+      float sum[M];
 #pragma unroll
       for (int m = 0; m < M; ++m) {
         float acc = 0.0f;
 #pragma unroll
         for (int j = 0; j < CPL; ++j) acc = dot8(w[u][j], hf[m][j], acc);
-        const float s = wave_sum(acc);
-        if (r0 + u < R) take_best(s, r0 + u, best[m], bidx[m]);
+        sum[m] = wave_sum(acc);
       }
+      if (r0 + u < R) ep.row(sum, r0 + u, lane, epi);
     }
   };
 
@@ -558,18 +650,7 @@ proj_valu_rows(const uint16_t* __restrict__ h, const uint16_t* __restrict__ W, i
     }
   }
 
-  if (lane == 0) {
-#pragma unroll
-    for (int m = 0; m < M; ++m) s_key[wave][m] = pack_key(best[m], bidx[m]);
-  }
-  __syncthreads();
-  if (wave != 0) return;
-  unsigned long long key = 0ull;
-  if (lane < M) {
-#pragma unroll
-    for (int w = 0; w < WV; ++w) key = s_key[w][lane] > key ? s_key[w][lane] : key;
-  }
-  publish_workgroup(key, lane, M, 0, epi.slots);
+  ep.finish(lane, wave, epi);
 }
 
 // VALU path, tiled order: a wave owns tiles of TR consecutive head rows and
@@ -599,18 +680,8 @@ proj_valu_tiled(const uint16_t* __restrict__ h, const uint16_t* __restrict__ W, 
   }
   __syncthreads();
 
-  // epilogue state: the running best row (TK == 1), or for TK > 1 the
-  // best 16 keys of hidden row rho = lane / 16 spread over that DPP row
-  static_assert(TK == 1 || LOGITS || (M <= 4 && TK <= 16), "a DPP row holds one hidden row's top 16");
-  float best[M];
-  int bidx[M];
-#pragma unroll
-  for (int m = 0; m < M; ++m) {
-    best[m] = 0.0f;
-    bidx[m] = -1;
-  }
-  unsigned long long rkey = 0ull;
-  const int rho = lane >> 4;
+  ValuEpilogue<M, WV, TK, LOGITS> ep;
+  ep.init();
   float acc[TR][M];
 #pragma unroll
   for (int q = 0; q < TR; ++q)
@@ -648,22 +719,7 @@ proj_valu_tiled(const uint16_t* __restrict__ h, const uint16_t* __restrict__ W, 
           sum[m] = wave_sum(acc[q][m]);
           acc[q][m] = 0.0f;
         }
-        if (r0 + q < R) {
-          if constexpr (LOGITS) {
-            if (lane == 0) {
-#pragma unroll
-              for (int m = 0; m < M; ++m) store_logit(epi, m, r0 + q, sum[m]);
-            }
-          } else if constexpr (TK == 1) {
-#pragma unroll
-            for (int m = 0; m < M; ++m) take_best(sum[m], r0 + q, best[m], bidx[m]);
-          } else {
-            float x = sum[0];
-#pragma unroll
-            for (int m = 1; m < M; ++m) x = rho == m ? sum[m] : x;
-            row_push(rkey, pack_key(x, r0 + q));
-          }
-        }
+        if (r0 + q < R) ep.row(sum, r0 + q, lane, epi);
       }
     }
   };
@@ -698,29 +754,7 @@ proj_valu_tiled(const uint16_t* __restrict__ h, const uint16_t* __restrict__ W, 
     }
   }
 
-  if constexpr (LOGITS) {
-    return;
-  } else if constexpr (TK == 1) {
-    __shared__ unsigned long long s_key[WV][M];
-    if (lane == 0) {
-#pragma unroll
-      for (int m = 0; m < M; ++m) s_key[wave][m] = pack_key(best[m], bidx[m]);
-    }
-    __syncthreads();
-    if (wave != 0) return;
-    unsigned long long key = 0ull;
-    if (lane < M) {
-#pragma unroll
-      for (int w = 0; w < WV; ++w) key = s_key[w][lane] > key ? s_key[w][lane] : key;
-    }
-    publish_workgroup(key, lane, M, 0, epi.slots);
-  } else {
-    __shared__ unsigned long long s_list[WV * M * 16];
-    if (rho < M) s_list[(wave * M + rho) * 16 + (lane & 15)] = rkey;
-    __syncthreads();
-    if (wave != 0) return;
-    publish_lists<TK, WV, 16>(s_list, M, lane, M, 0, epi.slots);
-  }
+  ep.finish(lane, wave, epi);
 }
 
 // ---------------------------------------------------------------------------
@@ -855,8 +889,22 @@ proj_mfma(const uint16_t* __restrict__ h, const uint16_t* __restrict__ W, int R,
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   };
+  // Logits without d2t: lane (g, i16) holds head rows 4 g .. 4 g + 3 of its
+  // column, one 16-byte store where the row block is whole and aligned.
+  const bool vec_logits =
+      LOGITS && !epi.d2t && (epi.ld & 3) == 0 && (reinterpret_cast<uintptr_t>(epi.logits) & 15) == 0;
   auto finish_tile = [&](int tile) __attribute__((always_inline)) {
     const int r0 = tile * 16;
+    if (LOGITS && vec_logits && r0 + 4 * g + 3 < R) {
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        const int col = nt * 16 + i16;
+        if (col < mp)
+          *reinterpret_cast<f32x4*>(epi.logits + (int64_t)(m_base + col) * epi.ld + r0 + 4 * g) = acc[nt];
+        acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+      return;
+    }
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
       const int r = r0 + 4 * g + v;
@@ -963,8 +1011,7 @@ proj_mfma(const uint16_t* __restrict__ h, const uint16_t* __restrict__ W, int R,
       }
     }
     __syncthreads();
-    if (wave != 0) return;
-    publish_lists<TK, WV, 16>(s_list, 32, lane, mp, m_base, epi.slots);
+    publish_rows<TK, WV, 16>(s_list, 32, mp, m_base, epi.slots);
   } else {
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
@@ -983,8 +1030,7 @@ proj_mfma(const uint16_t* __restrict__ h, const uint16_t* __restrict__ W, int R,
       }
     }
     __syncthreads();
-    if (wave != 0) return;
-    publish_lists<TK, WV, TK>(s_list, 32, lane, mp, m_base, epi.slots);
+    publish_rows<TK, WV, TK>(s_list, 32, mp, m_base, epi.slots);
   }
 }
 
@@ -1076,10 +1122,11 @@ int mfma_row_bytes(int64_t K) { return (int)((((K + 31) / 32) * 4 + 1) * 16); }
 typedef void (*proj_fn)(const uint16_t*, const uint16_t*, int, int, Epi);
 
 // One VALU launch shape: kernel, waves per workgroup, head rows a wave takes
-// per step, LDS bytes.  For the argmax the choice per M comes from
-// measurement on MI355X (full 248,320 x 2,560 head): M = 1 streams fastest
-// in 4-row tiles; M = 2..4 in row order with one 4-wave workgroup per CU.
-// The top-k and logits epilogues use the tiled kernel for every M <= 4.
+// per step, LDS bytes.  The choice per M comes from measurement on MI355X
+// (full 248,320 x 2,560 head): M = 1 streams fastest in 4-row tiles; M = 2..8
+// in row order with one workgroup per CU (4 waves up to M = 4, else 8).
+// Every epilogue (argmax, top-k, logits) uses the same shapes; top-k and
+// logits take M <= 4.
 struct ValuPlan {
   proj_fn fn = nullptr;
   int waves = 0;
@@ -1087,24 +1134,24 @@ struct ValuPlan {
   size_t lds = 0;
 };
 
-template <int M, int CPL, int WV>
+template <int M, int CPL, int WV, int TK, bool LOGITS>
 void row_plan(ValuPlan& p) {
   if constexpr (M * CPL <= kValuMaxChunksTimesM) {
     // rows per step: keep each of the two row buffers at <= 10 chunks/lane,
     // and one row per step once h alone takes more than 80 registers
     constexpr int U0 = M * CPL > 20 ? 1 : (CPL * LMH_VALU_ROWS <= 10 ? LMH_VALU_ROWS : (CPL <= 10 ? 10 / CPL : 1));
     constexpr int U = U0 < 1 ? 1 : U0;
-    p.fn = proj_valu_rows<M, CPL, U, WV>;
+    p.fn = proj_valu_rows<M, CPL, U, WV, TK, LOGITS>;
     p.waves = WV;
     p.rows_per_wave = U;
     p.lds = 0;
   }
 }
 
-template <int M, int... C>
+template <int M, int TK, bool LOGITS, int... C>
 void row_plan_cpl(ValuPlan& p, int cpl, std::integer_sequence<int, C...>) {
   constexpr int WV = M <= 4 ? LMH_VALU_WAVES : 2 * LMH_VALU_WAVES;
-  ((cpl == C + 1 ? (row_plan<M, C + 1, WV>(p), 0) : 0), ...);
+  ((cpl == C + 1 ? (row_plan<M, C + 1, WV, TK, LOGITS>(p), 0) : 0), ...);
 }
 
 template <int M, int TK, bool LOGITS>
@@ -1117,34 +1164,30 @@ ValuPlan tiled_plan(int K) {
   return p;
 }
 
-ValuPlan valu_argmax_plan(int M, int K) {
+template <int TK, bool LOGITS>
+ValuPlan valu_plan(int M, int K) {
   ValuPlan p;
-  if (M == 1 && LMH_VALU_TILE_ROWS > 0) return tiled_plan<1, 1, false>(K);
+  if (M == 1 && LMH_VALU_TILE_ROWS > 0) return tiled_plan<1, TK, LOGITS>(K);
   const int cpl = chunks_per_lane(K);
   using seq = std::make_integer_sequence<int, 16>;
   switch (M) {
-    case 1: row_plan_cpl<1>(p, cpl, seq{}); break;
-    case 2: row_plan_cpl<2>(p, cpl, seq{}); break;
-    case 3: row_plan_cpl<3>(p, cpl, seq{}); break;
-    case 4: row_plan_cpl<4>(p, cpl, seq{}); break;
-    case 5: row_plan_cpl<5>(p, cpl, seq{}); break;
-    case 6: row_plan_cpl<6>(p, cpl, seq{}); break;
-    case 7: row_plan_cpl<7>(p, cpl, seq{}); break;
-    case 8: row_plan_cpl<8>(p, cpl, seq{}); break;
-    default: break;
+    case 1: row_plan_cpl<1, TK, LOGITS>(p, cpl, seq{}); break;
+    case 2: row_plan_cpl<2, TK, LOGITS>(p, cpl, seq{}); break;
+    case 3: row_plan_cpl<3, TK, LOGITS>(p, cpl, seq{}); break;
+    case 4: row_plan_cpl<4, TK, LOGITS>(p, cpl, seq{}); break;
+    default:
+      if constexpr (TK == 1 && !LOGITS) {
+        switch (M) {
+          case 5: row_plan_cpl<5, 1, false>(p, cpl, seq{}); break;
+          case 6: row_plan_cpl<6, 1, false>(p, cpl, seq{}); break;
+          case 7: row_plan_cpl<7, 1, false>(p, cpl, seq{}); break;
+          case 8: row_plan_cpl<8, 1, false>(p, cpl, seq{}); break;
+          default: break;
+        }
+      }
+      break;
   }
   return p;
-}
-
-template <int TK, bool LOGITS>
-ValuPlan valu_epi_plan(int M, int K) {
-  switch (M) {
-    case 1: return tiled_plan<1, TK, LOGITS>(K);
-    case 2: return tiled_plan<2, TK, LOGITS>(K);
-    case 3: return tiled_plan<3, TK, LOGITS>(K);
-    case 4: return tiled_plan<4, TK, LOGITS>(K);
-    default: return ValuPlan{};
-  }
 }
 
 // Lets kernel `f` request the whole LDS of a workgroup, once per kernel.
@@ -1232,8 +1275,8 @@ int launch_finalize_argmax(unsigned long long* slots, int nslots, int m_base, in
 template <int TK>
 int launch_finalize_topk(unsigned long long* slots, int nslots, int m_base, int mcount, int topk,
                          const int32_t* d2t, int32_t* out_id, float* out_logit, hipStream_t stream) {
-  hipLaunchKernelGGL(finalize_topk<TK>, dim3(mcount), dim3(256), 0, stream, slots, nslots, m_base, topk, d2t,
-                     out_id, out_logit);
+  hipLaunchKernelGGL(finalize_topk<TK>, dim3(mcount), dim3(kFinalizeTopkThreads), 0, stream, slots, nslots, m_base,
+                     topk, d2t, out_id, out_logit);
   const hipError_t e = hipGetLastError();
   return e == hipSuccess ? LMH_OK : hip_fail(e, "launch finalize_topk");
 }
@@ -1267,7 +1310,7 @@ int run(const Call& c, const Epi& epi, int topk, int32_t* out_id, float* out_log
       return LMH_OK;
   };
   if (c.path == LMH_PATH_VALU) {
-    const ValuPlan p = MODE == 0 ? valu_argmax_plan(c.M, c.K) : valu_epi_plan<TK, LOGITS>(c.M, c.K);
+    const ValuPlan p = valu_plan<TK, LOGITS>(c.M, c.K);
     int grid = 0;
     st = launch_valu(p, c.h, c.K, c.W, c.R, epi, cus, c.stream, &grid);
     if (st != LMH_OK) return st;
@@ -1288,7 +1331,7 @@ int run(const Call& c, const Epi& epi, int topk, int32_t* out_id, float* out_log
   return LMH_OK;
 }
 
-bool valu_epi_ok(int64_t M, int64_t K) { return M >= 1 && M <= 4 && k_ok(K); }
+bool valu_epi_ok(int64_t M, int64_t K) { return M <= 4 && valu_ok(M, K); }
 
 // Shared argument checks; returns LMH_OK and the resolved path, or a status.
 int check_common(const uint16_t* h, int64_t M, int64_t K, const uint16_t* W, int64_t R, int mode, int* path) {
