@@ -7,9 +7,12 @@ A step is one draft_project_argmax call (projection + fused argmax + d2t map)
 over one hidden block, with every input already resident in HBM.  The
 default workload is the full-vocabulary draft step: M = 1 hidden row of
 width K = 2,560 against all N = 248,320 rows of a bf16 LM head (synthetic,
-seeded).  Prints ONE JSON line with calls/s, the kernel's achieved
-algorithmic HBM bandwidth against the 8 TB/s MI355X peak, and the fp64
-CPU oracle timed on a bounded sample of the same workload.
+seeded).  Prints ONE JSON line with calls/s over the timed steps, the
+projection kernel's achieved algorithmic HBM bandwidth against the 8 TB/s
+MI355X peak (its mean duration from two HIP events the library records
+around as many projection launches again, back to back on the same stream,
+right after the timed region), and the fp64 CPU oracle timed on a bounded
+sample of the same workload.
 
 Other configs (--config 1, 3, 4, 5) are for exploration; shortlist configs
 rotate through enough W_trim copies to exceed the 256 MB Infinity Cache.
@@ -37,9 +40,15 @@ def weight_bytes(rows: int, k: int) -> int:
 
 
 def algorithmic_bytes(m: int, rows: int, k: int, with_d2t: bool) -> int:
-    """Bytes one call must move at least: every weight row once, the hidden
-    rows once, the d2t entries of the winners and the two outputs."""
+    """Bytes one whole call must move at least: every weight row once, the
+    hidden rows once, the d2t entries of the winners and the two outputs."""
     return weight_bytes(rows, k) + m * k * 2 + (4 * m if with_d2t else 0) + 8 * m
+
+
+def projection_bytes(m: int, rows: int, k: int) -> int:
+    """Bytes the projection kernel itself must move: every weight row once
+    and the hidden rows once (the fold and the d2t map run afterwards)."""
+    return weight_bytes(rows, k) + m * k * 2
 
 
 def source_digest() -> str:
@@ -47,9 +56,38 @@ def source_digest() -> str:
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
+def kernel_name(path: str, m: int) -> str:
+    """The projection kernel a call runs (the plan in the library's host code)."""
+    if path == "mfma":
+        return "proj_mfma"
+    return "proj_valu_tiled" if m == 1 else "proj_valu_rows"
+
+
+def describe(a, synth, L):
+    """Everything about the workload that needs no GPU."""
+    inp = synth.make_config(a.config)
+    c = inp["config"]
+    m = a.m if a.m is not None else c.ms[0]
+    ids = inp["ids"]
+    trimmed = ids is not None and not a.full
+    path = {"auto": L.LMH_PATH_AUTO, "valu": L.LMH_PATH_VALU, "mfma": L.LMH_PATH_MFMA}[a.path]
+    chosen = L.draft_project_auto_path(m, c.k) if path == L.LMH_PATH_AUTO else path
+    kpath = {L.LMH_PATH_VALU: "valu", L.LMH_PATH_MFMA: "mfma"}[chosen]
+    if trimmed:
+        rows = ids.size
+        copies = max(1, -(-2 * MALL_BYTES // weight_bytes(rows, c.k)) + 1)
+        workload = f"{c.name}: M={m} K={c.k} trimmed to {rows} rows ({copies} rotated copies)"
+    else:
+        rows, copies = c.n, 1
+        workload = (f"full-vocab draft step M={m} K={c.k} N={c.n}" if a.config == 2
+                    else f"{c.name}: M={m} K={c.k} full head N={c.n}")
+    return dict(inp=inp, c=c, m=m, ids=ids, trimmed=trimmed, path=path, kpath=kpath, rows=rows,
+                copies=copies, workload=workload, kname=kernel_name(kpath, m))
+
+
 def measured_traffic(path: str, workload: str):
-    """HBM bytes per launch from committed rocprofv3 counter runs, if they
-    were taken on the current kernel source; else None."""
+    """HBM bytes per projection launch from committed rocprofv3 counter
+    runs, if they were taken on the current kernel source; else None."""
     try:
         with open(TRAFFIC_FILE) as f:
             table = json.load(f)
@@ -59,8 +97,78 @@ def measured_traffic(path: str, workload: str):
         if e.get("path") == path and e.get("workload") == workload:
             if e.get("source_sha256_16") != source_digest():
                 return None
-            return e.get("bytes_per_launch")
+            return e.get("bytes_projection_kernel")
     return None
+
+
+def _counter_medians(csv_path: str, counter: str) -> dict:
+    """Median counter value (KiB per dispatch) by kernel, from a rocprofv3
+    --pmc ... --output-format csv counter_collection file."""
+    import csv
+    import statistics
+    vals: dict = {}
+    with open(csv_path, newline="") as f:
+        for row in csv.DictReader(f):
+            if row["Counter_Name"] != counter:
+                continue
+            name = row["Kernel_Name"].replace("(anonymous namespace)::", "")
+            name = name.split("(")[0].replace("void ", "").strip()
+            vals.setdefault(name, []).append(float(row["Counter_Value"]))
+    return {k: statistics.median(v) for k, v in vals.items()}
+
+
+def _pick(med: dict, prefix: str):
+    hits = [(k, v) for k, v in med.items() if k.startswith(prefix)]
+    if len(hits) != 1:
+        raise SystemExit(f"bench.py: expected one kernel named {prefix}*, found {[k for k, _ in hits]}")
+    return hits[0]
+
+
+def record_traffic(a, d, fetch_csv: str, write_csv: str) -> int:
+    """Turn two counter runs of `bench.py --calibrate` (FETCH_SIZE, then
+    WRITE_SIZE) into the entry of profiles/traffic.json for this workload.
+    FETCH_SIZE and WRITE_SIZE are scaled by what they read for copy16 over
+    1 GiB (1 GiB read, 1 GiB written) in the same process."""
+    fm = _counter_medians(fetch_csv, "FETCH_SIZE")
+    wm = _counter_medians(write_csv, "WRITE_SIZE")
+    kname, fk = _pick(fm, d["kname"])
+    _, wk = _pick(wm, d["kname"])
+    _, ffin = _pick(fm, "finalize_argmax")
+    _, wfin = _pick(wm, "finalize_argmax")
+    _, fcopy = _pick(fm, "copy16")
+    _, wcopy = _pick(wm, "copy16")
+    gib = float(1 << 30)
+    fs, ws = gib / (fcopy * 1024), gib / (wcopy * 1024)
+    proj = fk * 1024 * fs + wk * 1024 * ws
+    fin = ffin * 1024 * fs + wfin * 1024 * ws
+    entry = {
+        "path": d["kpath"], "kernel": kname, "workload": d["workload"],
+        "source_sha256_16": source_digest(),
+        "fetch_kib_per_dispatch": fk, "write_kib_per_dispatch": wk,
+        "finalize_fetch_kib": ffin, "finalize_write_kib": wfin,
+        "copy16_fetch_kib": fcopy, "copy16_write_kib": wcopy,
+        "fetch_scale": round(fs, 5), "write_scale": round(ws, 5),
+        "bytes_projection_kernel": int(round(proj)), "bytes_finalize_kernel": int(round(fin)),
+        "algorithmic_bytes_projection_kernel": projection_bytes(d["m"], d["rows"], d["c"].k),
+    }
+    try:
+        with open(TRAFFIC_FILE) as f:
+            table = json.load(f)
+    except (OSError, ValueError):
+        table = {}
+    table["about"] = ("HBM bytes per launch of the projection kernel from rocprofv3 --pmc FETCH_SIZE and "
+                      "WRITE_SIZE runs of bench.py --calibrate, each scaled by what the counter reads for "
+                      "copy16 over 1 GiB in the same process; valid only for the kernel source with this "
+                      "digest")
+    entries = [e for e in table.get("entries", [])
+               if not (e.get("path") == entry["path"] and e.get("workload") == entry["workload"])]
+    entries.append(entry)
+    table["entries"] = entries
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(table, f, indent=1)
+        f.write("\n")
+    print(json.dumps(entry))
+    return 0
 
 
 def cpu_baseline(h_np, w_np, d2t_np, budget_s: float):
@@ -97,6 +205,10 @@ def main() -> int:
     ap.add_argument("--calibrate", action="store_true",
                     help="after the timed region, run the plain copy and read kernels over 1 GiB "
                          "(known bytes, for scaling hardware counters)")
+    ap.add_argument("--record-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="no GPU: write this workload's entry of profiles/traffic.json from the "
+                         "counter_collection.csv files of two rocprofv3 --pmc runs (FETCH_SIZE, "
+                         "WRITE_SIZE) of bench.py --calibrate with the same workload options")
     a = ap.parse_args()
 
     if a.gpus != 1:
@@ -112,40 +224,30 @@ def main() -> int:
     import synth
     from vocab_shortlisted_lm_amd import lmhead as L
 
+    L.lib()
+    d = describe(a, synth, L)
+    if a.record_traffic:
+        return record_traffic(a, d, *a.record_traffic)
     if not torch.cuda.is_available():
         print("bench.py: no GPU visible", file=sys.stderr)
         return 1
-    L.lib()
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
 
-    inp = synth.make_config(a.config)
-    c = inp["config"]
-    m = a.m if a.m is not None else c.ms[0]
+    inp, c, m, ids, trimmed, path = d["inp"], d["c"], d["m"], d["ids"], d["trimmed"], d["path"]
+    rows, workload, kpath = d["rows"], d["workload"], d["kpath"]
     h_np = inp["h"][m] if m in inp["h"] else synth.hidden(c.h_seed[0], 0, m, c.k)
     w_np = inp["W"]
-    ids = inp["ids"]
-    trimmed = ids is not None and not a.full
-    path = {"auto": L.LMH_PATH_AUTO, "valu": L.LMH_PATH_VALU, "mfma": L.LMH_PATH_MFMA}[a.path]
-    chosen = L.draft_project_auto_path(m, c.k) if path == L.LMH_PATH_AUTO else path
-    kpath = {L.LMH_PATH_VALU: "valu", L.LMH_PATH_MFMA: "mfma"}[chosen]
-    kname = {"valu": "proj_argmax_valu", "mfma": "proj_argmax_mfma"}[kpath]
 
     w_full = torch.from_numpy(w_np.view(np.int16)).to(dev)
     h = torch.from_numpy(h_np.view(np.int16)).to(dev)
     if trimmed:
         d2t = torch.from_numpy(ids.astype(np.int32)).to(dev)
-        copies = max(1, -(-2 * MALL_BYTES // weight_bytes(ids.size, c.k)) + 1)
-        heads = [L.lmhead_trim(w_full, d2t) for _ in range(copies)]
+        heads = [L.lmhead_trim(w_full, d2t) for _ in range(d["copies"])]
         del w_full
-        rows = ids.size
-        workload = f"{c.name}: M={m} K={c.k} trimmed to {rows} rows ({copies} rotated copies)"
     else:
         d2t = None
         heads = [w_full]
-        rows = c.n
-        workload = (f"full-vocab draft step M={m} K={c.k} N={c.n}" if a.config == 2
-                    else f"{c.name}: M={m} K={c.k} full head N={c.n}")
     torch.cuda.synchronize()
 
     ws = L.new_workspace(dev)
@@ -173,8 +275,12 @@ def main() -> int:
     ms_per_step = ms_total / a.steps
     calls_per_s = a.steps / (ms_total / 1e3)
 
+    # The projection kernel alone: as many launches again, back to back on
+    # this stream between two HIP events the library records (no fold).
+    proj_ms = L.lmhead_bench_time_argmax(h, heads, d2t, path, a.steps, out_id, out_logit, ws, stream)
+    pbytes = projection_bytes(m, rows, c.k)
+    achieved = pbytes / (proj_ms / 1e3) / 1e9
     abytes = algorithmic_bytes(m, rows, c.k, d2t is not None)
-    achieved = abytes / (ms_per_step / 1e3) / 1e9
     traffic = measured_traffic(kpath, workload)
     extra = {}
     if a.stream_read:
@@ -219,10 +325,14 @@ def main() -> int:
         "dtype": "bf16",
         "data": "synthetic (seeded bf16 W ~ N(0, 0.02), h ~ N(0, 1))",
         "config": {"workload": workload, "M": m, "K": c.k, "rows": rows,
-                   "kernel": kname, "d2t": d2t is not None, "parallelism": "single GPU"},
+                   "kernel": d["kname"], "d2t": d2t is not None, "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS,
                      "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBPS, 4),
-                     "traffic": traffic, "algorithmic_bytes_per_launch": abytes},
+                     "traffic": traffic, "kernel": d["kname"],
+                     "kernel_avg_us": round(proj_ms * 1e3, 2),
+                     "algorithmic_bytes_per_launch": pbytes,
+                     "step_gbps": round(abytes / (ms_per_step / 1e3) / 1e9, 1),
+                     "algorithmic_bytes_per_step": abytes},
         "wall_s": round(wall, 3),
     }
     result.update(extra)

@@ -208,6 +208,25 @@ int lmhead_bench_stream_read(const void* src, size_t bytes, uint32_t* sink,
 int lmhead_bench_copy(const void* src, void* dst, size_t bytes, int grid,
                       void* stream);
 
+/*
+ * lmhead_bench_time_argmax: mean duration of the projection kernel of
+ *   draft_project_argmax_path.  Between two HIP events on `stream` the
+ *   library launches that kernel `calls` times back to back, launch i over
+ *   heads[i % nheads] (a host array of device pointers, each [R, K]), with
+ *   no fold in between; *proj_ms = elapsed milliseconds / calls.  Then one
+ *   whole call over heads[0] writes out_id / out_logit.  Only shapes that
+ *   take a single projection launch are accepted (LMH_EINVAL otherwise).
+ *   Synchronizes; for measurement, not for the decode loop.  Other
+ *   arguments as for draft_project_argmax_path.
+ */
+int lmhead_bench_time_argmax(const uint16_t* h, int64_t M, int64_t K,
+                             const uint16_t* const* heads, int nheads,
+                             int64_t R, const int32_t* d2t,
+                             int32_t* out_id, float* out_logit,
+                             void* workspace, size_t workspace_bytes,
+                             int path, int calls, double* proj_ms,
+                             void* stream);
+
 #ifdef __cplusplus
 }
 #endif

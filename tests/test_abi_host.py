@@ -136,6 +136,19 @@ def test_logits_rejects_on_host(L):
     assert f(A, 1, 12, B, 100, None, 0, C, 0, None) == 1
 
 
+def test_bench_time_rejects_on_host(L):
+    import ctypes
+    f = L.lib().lmhead_bench_time_argmax
+    one = (ctypes.c_void_p * 1)(B)
+    out = ctypes.c_double(0.0)
+    ws = L.draft_project_workspace_bytes(1)
+    assert f(A, 1, 2560, None, 1, 100, None, C, D, E, ws, 0, 5, ctypes.byref(out), None) == 1  # no heads
+    assert f(A, 1, 2560, one, 0, 100, None, C, D, E, ws, 0, 5, ctypes.byref(out), None) == 1   # nheads 0
+    assert f(A, 1, 2560, one, 1, 100, None, C, D, E, ws, 0, 0, ctypes.byref(out), None) == 1   # calls 0
+    assert f(A, 1, 2560, one, 1, 100, None, C, D, E, ws, 0, 5, None, None) == 1                # no output
+    assert f(A, 1, 2560, one, 1, 100, None, C, D, E, 8, 0, 5, ctypes.byref(out), None) == 3    # workspace
+
+
 def test_trim_rejects_on_host(L):
     lib = L.lib()
     assert lib.lmhead_trim(A, 100, 2560, B, 0, C, None) == 0          # S = 0: no-op

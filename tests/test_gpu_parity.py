@@ -310,3 +310,22 @@ def test_rejected_calls_write_nothing(L):
     torch.cuda.synchronize()
     assert bool((oid == 77).all()) and bool((olog == 5.0).all())
     assert torch.equal(ws, ws_before)
+
+
+# --------------------------------------------------------------------------
+# the measurement helper runs the same kernels
+# --------------------------------------------------------------------------
+
+def test_bench_time_argmax_matches_call(L):
+    inp = config_inputs(1)
+    c = inp["config"]
+    w_dev = device_weights(1)
+    h = dev_bf16(inp["h"][1])
+    want_id, want_lg = L.draft_project_argmax(h, w_dev, None)
+    ws = L.new_workspace()
+    oid = torch.empty(1, dtype=torch.int32, device="cuda")
+    olg = torch.empty(1, dtype=torch.float32, device="cuda")
+    for p in paths_for(L, 1, c.k):
+        ms = L.lmhead_bench_time_argmax(h, [w_dev, w_dev], None, p, 7, oid, olg, ws)
+        assert 0.0 < ms < 100.0
+        assert torch.equal(oid, want_id) and torch.equal(olg, want_lg)

@@ -1291,7 +1291,13 @@ struct Call {
   const int32_t* d2t;
   int path;
   hipStream_t stream;
+  bool projection_only = false;  // measurement: skip the fold (outputs untouched)
 };
+
+int record(hipEvent_t e, hipStream_t s) {
+  const hipError_t r = hipEventRecord(e, s);
+  return r == hipSuccess ? LMH_OK : hip_fail(r, "hipEventRecord");
+}
 
 // Argmax (TK == 1 with the argmax finalizer), top-TK, or every logit.
 // MODE: 0 = argmax, 1 = top-k, 2 = logits.
@@ -1302,6 +1308,7 @@ int run(const Call& c, const Epi& epi, int topk, int32_t* out_id, float* out_log
   int st = cu_count(&cus);
   if (st != LMH_OK) return st;
   auto finalize = [&](int grid, int m_base, int mcount) -> int {
+    if (c.projection_only) return LMH_OK;
     if constexpr (MODE == 0)
       return launch_finalize_argmax(epi.slots, grid, m_base, mcount, c.d2t, out_id, out_logit, c.stream);
     else if constexpr (MODE == 1)
@@ -1311,6 +1318,7 @@ int run(const Call& c, const Epi& epi, int topk, int32_t* out_id, float* out_log
   };
   if (c.path == LMH_PATH_VALU) {
     const ValuPlan p = valu_plan<TK, LOGITS>(c.M, c.K);
+    if (!p.fn) return LMH_EINVAL;
     int grid = 0;
     st = launch_valu(p, c.h, c.K, c.W, c.R, epi, cus, c.stream, &grid);
     if (st != LMH_OK) return st;
@@ -1323,7 +1331,7 @@ int run(const Call& c, const Epi& epi, int topk, int32_t* out_id, float* out_log
   for (int m0 = 0; m0 < c.M; m0 += per) {
     const int mp = std::min(per, c.M - m0);
     int grid = 0;
-    st = launch_mfma_pass<TK, LOGITS>(c.h + (size_t)0, c.K, m0, mp, c.W, c.R, epi, cus, c.stream, &grid);
+    st = launch_mfma_pass<TK, LOGITS>(c.h, c.K, m0, mp, c.W, c.R, epi, cus, c.stream, &grid);
     if (st != LMH_OK) return st;
     st = finalize(grid, m0, mp);
     if (st != LMH_OK) return st;
@@ -1485,6 +1493,59 @@ int lmhead_bench_stream_read(const void* src, size_t bytes, uint32_t* sink, int 
                      static_cast<const u32x4*>(src), bytes / 16, sink);
   const hipError_t e = hipGetLastError();
   return e == hipSuccess ? LMH_OK : hip_fail(e, "launch stream_read");
+}
+
+int lmhead_bench_time_argmax(const uint16_t* h, int64_t M, int64_t K, const uint16_t* const* heads, int nheads,
+                             int64_t R, const int32_t* d2t, int32_t* out_id, float* out_logit, void* workspace,
+                             size_t workspace_bytes, int path, int calls, double* proj_ms, void* stream) {
+  if (!heads || nheads < 1 || calls < 1 || !proj_ms) return LMH_EINVAL;
+  const int path_in = path;
+  int st = LMH_OK;
+  for (int i = 0; i < nheads; ++i) {
+    path = path_in;
+    if ((st = check_common(h, M, K, heads[i], R, 0, &path)) != LMH_OK) return st;
+  }
+  if (!out_id || !out_logit) return LMH_EINVAL;
+  if (!workspace || !aligned16(workspace)) return LMH_EWORKSPACE;
+  if (workspace_bytes < draft_project_workspace_bytes(M)) return LMH_EWORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipEvent_t ev[2] = {nullptr, nullptr};
+  for (auto& e : ev) {
+    const hipError_t r = hipEventCreate(&e);
+    if (r != hipSuccess) {
+      e = nullptr;
+      st = hip_fail(r, "hipEventCreate");
+      break;
+    }
+  }
+  const Epi epi{static_cast<unsigned long long*>(workspace), nullptr, nullptr, 0, 0};
+  // single-pass shapes only: the events must bracket projection kernels alone
+  const int cap = mfma_lds_rows_fit(K, 4);
+  if (st == LMH_OK && path == LMH_PATH_MFMA && (cap < 1 || M > cap)) st = LMH_EINVAL;
+  if (st == LMH_OK) st = record(ev[0], s);
+  for (int i = 0; i < calls && st == LMH_OK; ++i) {
+    Call c{h, (int)M, (int)K, heads[i % nheads], (int)R, d2t, path, s};
+    c.projection_only = true;
+    st = run<0, 1>(c, epi, 1, out_id, out_logit);
+  }
+  if (st == LMH_OK) st = record(ev[1], s);
+  if (st == LMH_OK) {  // one whole call, so the outputs hold a result
+    const Call c{h, (int)M, (int)K, heads[0], (int)R, d2t, path, s};
+    st = run<0, 1>(c, epi, 1, out_id, out_logit);
+  }
+  if (st == LMH_OK) {
+    const hipError_t r = hipStreamSynchronize(s);
+    if (r != hipSuccess) st = hip_fail(r, "hipStreamSynchronize");
+  }
+  float ms = 0.0f;
+  if (st == LMH_OK) {
+    const hipError_t r = hipEventElapsedTime(&ms, ev[0], ev[1]);
+    if (r != hipSuccess) st = hip_fail(r, "hipEventElapsedTime");
+  }
+  for (hipEvent_t e : ev)
+    if (e) (void)hipEventDestroy(e);
+  if (st == LMH_OK) *proj_ms = (double)ms / calls;
+  return st;
 }
 
 int lmhead_bench_copy(const void* src, void* dst, size_t bytes, int grid, void* stream) {

@@ -22,6 +22,7 @@ __all__ = [
     "lmhead_last_error", "lmhead_bench_sink_words", "lmhead_bench_stream_read",
     "lmhead_bench_copy", "new_workspace", "read_id_list", "LMH_MAX_TOPK",
     "draft_project_topk_workspace_bytes", "draft_project_topk", "draft_project_logits",
+    "lmhead_bench_time_argmax",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "liblmhead.so")
@@ -50,6 +51,8 @@ SIGNATURES = {
     "lmhead_bench_sink_words": (_INT, []),
     "lmhead_bench_stream_read": (_INT, [_P, _SZ, _P, _INT, _P]),
     "lmhead_bench_copy": (_INT, [_P, _P, _SZ, _INT, _P]),
+    "lmhead_bench_time_argmax": (_INT, [_P, _I64, _I64, _P, _INT, _I64, _P, _P, _P, _P, _SZ, _INT, _INT,
+                                        ctypes.POINTER(ctypes.c_double), _P]),
 }
 
 _lib = None
@@ -298,3 +301,26 @@ def lmhead_bench_copy(src: torch.Tensor, dst: torch.Tensor, grid: int = 0, strea
         raise ValueError("dst too small")
     _check(lib().lmhead_bench_copy(src.data_ptr(), dst.data_ptr(), nbytes, grid,
                                    _stream(stream, src.device)), "lmhead_bench_copy")
+
+
+def lmhead_bench_time_argmax(h: torch.Tensor, heads: list, d2t: torch.Tensor | None, path: int,
+                             calls: int, out_id: torch.Tensor, out_logit: torch.Tensor,
+                             workspace: torch.Tensor, stream=None) -> float:
+    """Mean duration (ms) of the projection kernel over `calls` back-to-back
+    argmax calls rotating through `heads`, from HIP events the library
+    records around each projection launch.  Synchronizes."""
+    _dev_tensor(h, "h", _BF16_LIKE, 2)
+    m, k = h.shape
+    for w in heads:
+        _dev_tensor(w, "W", _BF16_LIKE, 2)
+        if w.shape != heads[0].shape or w.shape[1] != k:
+            raise ValueError("every head must be [R, K] with the same R and K")
+    r = heads[0].shape[0]
+    ptrs = (ctypes.c_void_p * len(heads))(*[w.data_ptr() for w in heads])
+    out = ctypes.c_double(0.0)
+    _check(lib().lmhead_bench_time_argmax(
+        h.data_ptr(), m, k, ptrs, len(heads), r, d2t.data_ptr() if d2t is not None else None,
+        out_id.data_ptr(), out_logit.data_ptr(), workspace.data_ptr(),
+        workspace.numel() * workspace.element_size(), path, calls, ctypes.byref(out),
+        _stream(stream, h.device)), "lmhead_bench_time_argmax")
+    return out.value
