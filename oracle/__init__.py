@@ -1,10 +1,15 @@
 """fp64 CPU oracle: test infrastructure only (tests, the smoke check and the
 benchmark's CPU-baseline leg).  The product path never imports it."""
-from .lmhead_oracle import (OracleResult, TopkResult, bf16_bits_to_f64,
-                            oracle_logits, oracle_project_argmax,
-                            oracle_project_topk, oracle_scatter_logits,
-                            oracle_trim)
+from .fp8_head import (E4M3_MAX, e4m3_decode, e4m3_encode, oracle_dequant_fp8,
+                       oracle_logits_fp8, oracle_project_argmax_fp8,
+                       oracle_quantize_fp8)
+from .lmhead_oracle import (OracleResult, TopkResult, argmax_of_logits,
+                            bf16_bits_to_f64, oracle_logits,
+                            oracle_project_argmax, oracle_project_topk,
+                            oracle_scatter_logits, oracle_trim)
 
-__all__ = ["OracleResult", "TopkResult", "bf16_bits_to_f64", "oracle_logits",
-           "oracle_project_argmax", "oracle_project_topk",
-           "oracle_scatter_logits", "oracle_trim"]
+__all__ = ["OracleResult", "TopkResult", "argmax_of_logits", "bf16_bits_to_f64",
+           "oracle_logits", "oracle_project_argmax", "oracle_project_topk",
+           "oracle_scatter_logits", "oracle_trim", "E4M3_MAX", "e4m3_decode",
+           "e4m3_encode", "oracle_quantize_fp8", "oracle_dequant_fp8",
+           "oracle_logits_fp8", "oracle_project_argmax_fp8"]

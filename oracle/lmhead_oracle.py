@@ -47,6 +47,7 @@ __all__ = [
     "oracle_project_argmax",
     "oracle_project_topk",
     "oracle_scatter_logits",
+    "argmax_of_logits",
     "OracleResult",
     "TopkResult",
 ]
@@ -128,6 +129,17 @@ def oracle_project_argmax(h_bits: np.ndarray, w_bits: np.ndarray,
     zone-1.cobraproject.com); the index-to-id map is the d2t table of
     "Two ways to run it" on the same page."""
     logits = oracle_logits(h_bits, w_bits)
+    ids, idx, best, gap = argmax_of_logits(logits, d2t)
+    h = bf16_bits_to_f64(h_bits)
+    w_win = bf16_bits_to_f64(np.asarray(w_bits)[idx])
+    abs_sum = np.abs(h * w_win).sum(axis=1)
+    return OracleResult(ids, idx, best, gap, abs_sum, logits if keep_logits else None)
+
+
+def argmax_of_logits(logits: np.ndarray, d2t: np.ndarray | None):
+    """(id, idx, logit, gap) per hidden row of an [M, R] logit array: idx is
+    the first row holding the maximum, id = d2t[idx] (or idx), gap = the
+    maximum minus the best other row (+inf when R = 1)."""
     m, r = logits.shape
     if r < 1:
         raise ValueError("need at least one projected row")
@@ -147,11 +159,7 @@ def oracle_project_argmax(h_bits: np.ndarray, w_bits: np.ndarray,
         if d2t.shape != (r,):
             raise ValueError("d2t must have one entry per projected row")
         ids = d2t[idx].astype(np.int64)
-    h = bf16_bits_to_f64(h_bits)
-    w_win = bf16_bits_to_f64(np.asarray(w_bits)[idx])
-    abs_sum = np.abs(h * w_win).sum(axis=1)
-    return OracleResult(ids, idx.astype(np.int64), best, gap, abs_sum,
-                        logits if keep_logits else None)
+    return ids, idx.astype(np.int64), best, gap
 
 
 @dataclass
