@@ -39,16 +39,18 @@ def weight_bytes(rows: int, k: int) -> int:
     return rows * k * 2
 
 
-def algorithmic_bytes(m: int, rows: int, k: int, with_d2t: bool) -> int:
+def algorithmic_bytes(m: int, rows: int, k: int, with_d2t: bool, fp8: bool = False) -> int:
     """Bytes one whole call must move at least: every weight row once, the
     hidden rows once, the d2t entries of the winners and the two outputs."""
-    return weight_bytes(rows, k) + m * k * 2 + (4 * m if with_d2t else 0) + 8 * m
+    return projection_bytes(m, rows, k, fp8) + (4 * m if with_d2t else 0) + 8 * m
 
 
-def projection_bytes(m: int, rows: int, k: int) -> int:
+def projection_bytes(m: int, rows: int, k: int, fp8: bool = False) -> int:
     """Bytes the projection kernel itself must move: every weight row once
-    and the hidden rows once (the fold and the d2t map run afterwards)."""
-    return weight_bytes(rows, k) + m * k * 2
+    (bf16, or E4M3 codes plus one fp32 scale per row) and the hidden rows
+    once (the fold and the d2t map run afterwards)."""
+    w = rows * k + rows * 4 if fp8 else weight_bytes(rows, k)
+    return w + m * k * 2
 
 
 def source_digest() -> str:
@@ -71,7 +73,10 @@ def describe(a, synth, L):
     ids = inp["ids"]
     trimmed = ids is not None and not a.full
     path = {"auto": L.LMH_PATH_AUTO, "valu": L.LMH_PATH_VALU, "mfma": L.LMH_PATH_MFMA}[a.path]
-    chosen = L.draft_project_auto_path(m, c.k) if path == L.LMH_PATH_AUTO else path
+    if a.fp8:
+        chosen = L.LMH_PATH_MFMA if path == L.LMH_PATH_AUTO else path   # the library's FP8 default
+    else:
+        chosen = L.draft_project_auto_path(m, c.k) if path == L.LMH_PATH_AUTO else path
     kpath = {L.LMH_PATH_VALU: "valu", L.LMH_PATH_MFMA: "mfma"}[chosen]
     if trimmed:
         rows = ids.size
@@ -81,8 +86,14 @@ def describe(a, synth, L):
         rows, copies = c.n, 1
         workload = (f"full-vocab draft step M={m} K={c.k} N={c.n}" if a.config == 2
                     else f"{c.name}: M={m} K={c.k} full head N={c.n}")
+    if a.fp8:
+        if trimmed:
+            copies = max(1, -(-2 * MALL_BYTES // (rows * c.k)) + 1)
+            workload = f"{c.name}: M={m} K={c.k} trimmed to {rows} rows ({copies} rotated copies)"
+        workload += ", FP8 E4M3 head (fp32 row scale)"
+    kname = kernel_name(kpath, m) if not a.fp8 else ("proj_mfma" if kpath == "mfma" else "proj_valu_fp8")
     return dict(inp=inp, c=c, m=m, ids=ids, trimmed=trimmed, path=path, kpath=kpath, rows=rows,
-                copies=copies, workload=workload, kname=kernel_name(kpath, m))
+                copies=copies, workload=workload, kname=kname)
 
 
 def measured_traffic(path: str, workload: str):
@@ -149,7 +160,7 @@ def record_traffic(a, d, fetch_csv: str, write_csv: str) -> int:
         "copy16_fetch_kib": fcopy, "copy16_write_kib": wcopy,
         "fetch_scale": round(fs, 5), "write_scale": round(ws, 5),
         "bytes_projection_kernel": int(round(proj)), "bytes_finalize_kernel": int(round(fin)),
-        "algorithmic_bytes_projection_kernel": projection_bytes(d["m"], d["rows"], d["c"].k),
+        "algorithmic_bytes_projection_kernel": projection_bytes(d["m"], d["rows"], d["c"].k, a.fp8),
     }
     try:
         with open(TRAFFIC_FILE) as f:
@@ -205,6 +216,9 @@ def main() -> int:
     ap.add_argument("--calibrate", action="store_true",
                     help="after the timed region, run the plain copy and read kernels over 1 GiB "
                          "(known bytes, for scaling hardware counters)")
+    ap.add_argument("--fp8", action="store_true",
+                    help="quantize the head (or shortlist) to FP8 E4M3 with one scale per row at load "
+                         "and time draft_project_argmax_fp8 (no CPU baseline)")
     ap.add_argument("--record-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="no GPU: write this workload's entry of profiles/traffic.json from the "
                          "counter_collection.csv files of two rocprofv3 --pmc runs (FETCH_SIZE, "
@@ -248,6 +262,13 @@ def main() -> int:
     else:
         d2t = None
         heads = [w_full]
+    if a.fp8:
+        qheads = []
+        for w in heads:
+            qheads.append(L.lmhead_quantize_fp8(w))
+            torch.cuda.synchronize()
+        del heads, w
+        heads = qheads
     torch.cuda.synchronize()
 
     ws = L.new_workspace(dev)
@@ -256,8 +277,12 @@ def main() -> int:
     stream = torch.cuda.current_stream(dev)
 
     def step(i):
-        L.draft_project_argmax_path(h, heads[i % len(heads)], d2t, path, out_id, out_logit, ws,
-                                    stream)
+        if a.fp8:
+            q, sc = heads[i % len(heads)]
+            L.draft_project_argmax_fp8(h, q, sc, d2t, path, out_id, out_logit, ws, stream)
+        else:
+            L.draft_project_argmax_path(h, heads[i % len(heads)], d2t, path, out_id, out_logit, ws,
+                                        stream)
 
     for i in range(a.warmup):
         step(i)
@@ -277,15 +302,18 @@ def main() -> int:
 
     # The projection kernel alone: as many launches again, back to back on
     # this stream between two HIP events the library records (no fold).
-    proj_ms = L.lmhead_bench_time_argmax(h, heads, d2t, path, a.steps, out_id, out_logit, ws, stream)
-    pbytes = projection_bytes(m, rows, c.k)
+    if a.fp8:
+        proj_ms = L.lmhead_bench_time_argmax_fp8(h, heads, d2t, path, a.steps, out_id, out_logit, ws, stream)
+    else:
+        proj_ms = L.lmhead_bench_time_argmax(h, heads, d2t, path, a.steps, out_id, out_logit, ws, stream)
+    pbytes = projection_bytes(m, rows, c.k, a.fp8)
     achieved = pbytes / (proj_ms / 1e3) / 1e9
-    abytes = algorithmic_bytes(m, rows, c.k, d2t is not None)
+    abytes = algorithmic_bytes(m, rows, c.k, d2t is not None, a.fp8)
     traffic = measured_traffic(kpath, workload)
     extra = {}
     if a.stream_read:
         sink = torch.zeros(L.lmhead_bench_sink_words(), dtype=torch.int32, device=dev)
-        buf = heads[0]
+        buf = heads[0][0] if a.fp8 else heads[0]
         for _ in range(3):
             L.lmhead_bench_stream_read(buf, sink)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -322,7 +350,7 @@ def main() -> int:
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "e4m3 W x bf16 h, fp32 accumulate" if a.fp8 else "bf16",
         "data": "synthetic (seeded bf16 W ~ N(0, 0.02), h ~ N(0, 1))",
         "config": {"workload": workload, "M": m, "K": c.k, "rows": rows,
                    "kernel": d["kname"], "d2t": d2t is not None, "parallelism": "single GPU"},
@@ -336,7 +364,7 @@ def main() -> int:
         "wall_s": round(wall, 3),
     }
     result.update(extra)
-    if not a.no_cpu_baseline:
+    if not a.no_cpu_baseline and not a.fp8:
         hb = h_np
         wb = w_np[ids] if trimmed else w_np
         result["cpu_baseline"] = cpu_baseline(hb, wb, ids if trimmed else None, a.cpu_seconds)

@@ -182,6 +182,48 @@ int draft_project_logits(const uint16_t* h, int64_t M, int64_t K,
                          const int32_t* d2t, int64_t N, float* out,
                          int path, void* stream);
 
+/*
+ * lmhead_quantize_fp8 -- load-time FP8 copy of a bf16 head (W or W_trim),
+ * one scale per row.  The pages convert weights that every decode step
+ * reads to FP8 E4M3 at load, which halves the bytes read (ai-muninn.com
+ * "Qwen3.8-Flash-Next on two DGX Sparks": "The costs: a 69% smaller KV pool
+ * and FP8 GDN weights", and the kernel notes under "Decode runs at 80-87%
+ * of memory bandwidth").  Granularity and rounding are readings:
+ *   scale[r] = max_k |W[r, k]| / 448 in fp32, or 1 for an all-zero row;
+ *   Wq[r, k] = the OCP E4M3 code nearest to W[r, k] / scale[r] (fp32
+ *   division), ties to the even code, magnitudes above 448 saturating.
+ * The quantized head stands for decode(Wq[r, k]) * scale[r].
+ *
+ *  W      [R, K] bf16 (device, 16-byte aligned).  K a multiple of 16.
+ *  Wq     [R, K] uint8 (device, 16-byte aligned, caller-allocated).
+ *  scale  [R] float (device, 4-byte aligned, caller-allocated).
+ * R = 0 is a no-op.  Asynchronous on `stream`; allocates nothing.
+ * Returns LMH_EINVAL for a bad shape, a null or misaligned pointer.
+ */
+int lmhead_quantize_fp8(const uint16_t* W, int64_t R, int64_t K,
+                        uint8_t* Wq, float* scale, void* stream);
+
+/*
+ * draft_project_argmax_fp8 -- draft_project_argmax over an FP8 head from
+ * lmhead_quantize_fp8: out_logit[m] = max_r scale[r] * sum_k h[m, k] *
+ * decode(Wq[r, k]), fp32 sums of exact products, then one multiply by the
+ * row's scale; out_id as for draft_project_argmax (first row among equal
+ * maxima, mapped through d2t).  The head streams at 1 byte per weight.
+ *
+ *  Wq, scale  as written by lmhead_quantize_fp8 (R rows).  K a multiple
+ *             of 16, Wq 16-byte aligned, scale 4-byte aligned.
+ *  path       LMH_PATH_AUTO (matrix cores for every M), LMH_PATH_VALU
+ *             (M <= 4) or LMH_PATH_MFMA.
+ * Other arguments, workspace, synchronization and errors as for
+ * draft_project_argmax_path.
+ */
+int draft_project_argmax_fp8(const uint16_t* h, int64_t M, int64_t K,
+                             const uint8_t* Wq, const float* scale, int64_t R,
+                             const int32_t* d2t,
+                             int32_t* out_id, float* out_logit,
+                             void* workspace, size_t workspace_bytes,
+                             int path, void* stream);
+
 /* Which kernel draft_project_argmax picks for (M, K): an LMH_PATH_* value,
  * or -1 if the shape is not accepted. */
 int draft_project_auto_path(int64_t M, int64_t K);
@@ -226,6 +268,19 @@ int lmhead_bench_time_argmax(const uint16_t* h, int64_t M, int64_t K,
                              void* workspace, size_t workspace_bytes,
                              int path, int calls, double* proj_ms,
                              void* stream);
+
+/*
+ * lmhead_bench_time_argmax_fp8: the same over FP8 heads (draft_project_
+ *   argmax_fp8): launch i uses heads[i % nheads] with scales[i % nheads].
+ */
+int lmhead_bench_time_argmax_fp8(const uint16_t* h, int64_t M, int64_t K,
+                                 const uint8_t* const* heads,
+                                 const float* const* scales, int nheads,
+                                 int64_t R, const int32_t* d2t,
+                                 int32_t* out_id, float* out_logit,
+                                 void* workspace, size_t workspace_bytes,
+                                 int path, int calls, double* proj_ms,
+                                 void* stream);
 
 #ifdef __cplusplus
 }

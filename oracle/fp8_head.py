@@ -37,6 +37,7 @@ __all__ = ["E4M3_MAX", "e4m3_decode", "e4m3_encode", "oracle_quantize_fp8",
 
 E4M3_MAX = 448.0
 BLOCK_ROWS = 8192
+QUANT_BLOCK_ROWS = 256
 
 
 def _e4m3_value(code: int) -> float:
@@ -79,17 +80,23 @@ def e4m3_encode(x: np.ndarray) -> np.ndarray:
 
 
 def oracle_quantize_fp8(w_bits: np.ndarray):
-    """(codes uint8 [R, K], scale float32 [R]) of a bf16 head, row by row."""
+    """(codes uint8 [R, K], scale float32 [R]) of a bf16 head, row by row
+    (in blocks of QUANT_BLOCK_ROWS rows, which bounds the temporaries)."""
     w_bits = np.asarray(w_bits, dtype=np.uint16)
     if w_bits.ndim != 2:
         raise ValueError("W must be [R, K]")
-    w = bf16_bits_to_f64(w_bits).astype(np.float32)       # exact
-    if not np.all(np.isfinite(w)):
-        raise ValueError("non-finite weight value")
-    amax = np.abs(w).max(axis=1) if w.shape[1] else np.zeros(w.shape[0], np.float32)
-    scale = np.where(amax > 0, amax / np.float32(E4M3_MAX), np.float32(1.0)).astype(np.float32)
-    q = (w / scale[:, None]).astype(np.float32)           # fp32 division, nearest even
-    return e4m3_encode(q), scale
+    codes = np.empty(w_bits.shape, dtype=np.uint8)
+    scale = np.empty(w_bits.shape[0], dtype=np.float32)
+    for r0 in range(0, w_bits.shape[0], QUANT_BLOCK_ROWS):
+        w = bf16_bits_to_f64(w_bits[r0:r0 + QUANT_BLOCK_ROWS]).astype(np.float32)   # exact
+        if not np.all(np.isfinite(w)):
+            raise ValueError("non-finite weight value")
+        amax = np.abs(w).max(axis=1) if w.shape[1] else np.zeros(w.shape[0], np.float32)
+        s = np.where(amax > 0, amax / np.float32(E4M3_MAX), np.float32(1.0)).astype(np.float32)
+        q = (w / s[:, None]).astype(np.float32)           # fp32 division, nearest even
+        codes[r0:r0 + w.shape[0]] = e4m3_encode(q)
+        scale[r0:r0 + w.shape[0]] = s
+    return codes, scale
 
 
 def oracle_dequant_fp8(codes: np.ndarray, scale: np.ndarray) -> np.ndarray:

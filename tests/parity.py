@@ -15,6 +15,9 @@ Two bars are applied to every hidden row:
    bound for row r: the GPU logit of its row r_g is within B(r_g) of the
    oracle's, the GPU's row can trail the true maximum by at most
    B(r_g) + B(r_best), and if the gap exceeds that sum the ids must match.
+   Over an FP8 head the products are exact too (bf16 x E4M3) and one more
+   rounding multiplies by the row's scale: (K + 2) * 2**-24 * sum_k
+   |h_k w_k| with w the dequantized values.
 """
 from __future__ import annotations
 
@@ -43,20 +46,37 @@ class ParityStats:
         self.max_err_over_bound = max(self.max_err_over_bound, other.max_err_over_bound)
 
 
-def _row_bound(h_row: np.ndarray, w_row: np.ndarray, k: int) -> float:
-    return (k + 1) * U32 * float(np.abs(h_row * w_row).sum()) + 1e-30
+def _row_bound(h_row: np.ndarray, w_row: np.ndarray, k: int, extra: int = 1) -> float:
+    return (k + extra) * U32 * float(np.abs(h_row * w_row).sum()) + 1e-30
 
 
 def check(h_bits, w_bits, d2t, gpu_id, gpu_logit, res=None) -> ParityStats:
-    """Assert the parity rule for one call; returns statistics."""
-    h_bits = np.asarray(h_bits)
+    """Assert the parity rule for one call over a bf16 head; returns statistics."""
     w_bits = np.asarray(w_bits)
+    if res is None or res.logits is None:
+        res = oracle.oracle_project_argmax(h_bits, w_bits, d2t, keep_logits=True)
+    return _check_core(h_bits, lambda rows: oracle.bf16_bits_to_f64(w_bits[rows]), w_bits.shape[0], d2t,
+                       gpu_id, gpu_logit, res, extra=1)
+
+
+def check_fp8(h_bits, codes, scale, d2t, gpu_id, gpu_logit, res=None) -> ParityStats:
+    """The same rule over an FP8 head (codes [R, K], scale [R]).  The GPU
+    sums exact bf16 x E4M3 products in fp32 and multiplies by the row's
+    scale once, so the derived bound carries K + 2 roundings against the
+    dequantized values decode(code) * scale."""
+    codes = np.asarray(codes)
+    scale = np.asarray(scale)
+    if res is None or res.logits is None:
+        res = oracle.oracle_project_argmax_fp8(h_bits, codes, scale, d2t, keep_logits=True)
+    return _check_core(h_bits, lambda rows: oracle.oracle_dequant_fp8(codes[rows], scale[rows]),
+                       codes.shape[0], d2t, gpu_id, gpu_logit, res, extra=2)
+
+
+def _check_core(h_bits, w_rows, r, d2t, gpu_id, gpu_logit, res, extra) -> ParityStats:
+    h_bits = np.asarray(h_bits)
     gpu_id = np.asarray(gpu_id).astype(np.int64)
     gpu_logit = np.asarray(gpu_logit).astype(np.float64)
     m, k = h_bits.shape
-    r = w_bits.shape[0]
-    if res is None or res.logits is None:
-        res = oracle.oracle_project_argmax(h_bits, w_bits, d2t, keep_logits=True)
     if d2t is None:
         rows = gpu_id.copy()
     else:
@@ -70,10 +90,10 @@ def check(h_bits, w_bits, d2t, gpu_id, gpu_logit, res=None) -> ParityStats:
     for i in range(m):
         assert 0 <= rows[i] < r, f"row {i}: GPU id {gpu_id[i]} is not a projected row"
         lg = res.logits[i, rows[i]]
-        wg = oracle.bf16_bits_to_f64(w_bits[rows[i]])
-        wb = oracle.bf16_bits_to_f64(w_bits[res.idx[i]])
-        b_g = _row_bound(h[i], wg, k)
-        b_best = _row_bound(h[i], wb, k)
+        wg = w_rows(np.array([rows[i]]))[0]
+        wb = w_rows(np.array([res.idx[i]]))[0]
+        b_g = _row_bound(h[i], wg, k, extra)
+        b_best = _row_bound(h[i], wb, k, extra)
         err = abs(gpu_logit[i] - lg)
         st.max_err = max(st.max_err, err)
         st.max_err_over_bound = max(st.max_err_over_bound, err / b_g)

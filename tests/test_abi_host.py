@@ -149,6 +149,26 @@ def test_bench_time_rejects_on_host(L):
     assert f(A, 1, 2560, one, 1, 100, None, C, D, E, 8, 0, 5, ctypes.byref(out), None) == 3    # workspace
 
 
+def test_fp8_rejects_on_host(L):
+    lib = L.lib()
+    q = lib.lmhead_quantize_fp8
+    assert q(A, 0, 2560, B, C, None) == 0                        # R = 0: no-op
+    assert q(A, 10, 2568, B, C, None) == 1                       # K not a multiple of 16
+    assert q(A, 10, 2560, B + 8, C, None) == 1                   # Wq misaligned
+    assert q(A, 10, 2560, B, C + 2, None) == 1                   # scale misaligned
+    assert q(None, 10, 2560, B, C, None) == 1
+    assert q(A, -1, 2560, B, C, None) == 1
+    f = lib.draft_project_argmax_fp8
+    ws = L.draft_project_workspace_bytes(4)
+    assert f(A, 4, 2568, B, C, 100, None, D, E, E, ws, 0, None) == 1   # K % 16
+    assert f(A, 5, 2560, B, C, 100, None, D, E, E, ws, 1, None) == 1   # VALU takes M <= 4
+    assert f(A, 1, 2560, B, None, 100, None, D, E, E, ws, 0, None) == 1  # no scale
+    assert f(A, 1, 2560, B, C + 1, 100, None, D, E, E, ws, 0, None) == 1
+    assert f(A, 33, 2560, B, C, 100, None, D, E, E, ws, 0, None) == 1
+    assert f(A, 1, 2560, B, C, 0, None, D, E, E, ws, 0, None) == 1     # R = 0
+    assert f(A, 4, 2560, B, C, 100, None, D, E, E, 8, 0, None) == 3    # workspace
+
+
 def test_trim_rejects_on_host(L):
     lib = L.lib()
     assert lib.lmhead_trim(A, 100, 2560, B, 0, C, None) == 0          # S = 0: no-op
@@ -186,7 +206,8 @@ def test_build_has_no_scratch_spills():
         proc = subprocess.run(build.command(out), capture_output=True, text=True)
         assert proc.returncode == 0, proc.stderr[-2000:]
         usage = build.kernel_resources(proc.stderr)
-    for kernel in ("proj_valu_tiled", "proj_valu_rows", "proj_mfma", "finalize_topk"):
+    for kernel in ("proj_valu_tiled", "proj_valu_rows", "proj_mfma", "finalize_topk", "proj_valu_fp8",
+                   "quantize_rows_fp8"):
         assert any(kernel in k for k in usage), kernel
     spills = {k: v["ScratchSize"] for k, v in usage.items() if v.get("ScratchSize", 0)}
     assert not spills, spills

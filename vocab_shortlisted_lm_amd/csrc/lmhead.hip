@@ -132,6 +132,47 @@ __device__ __forceinline__ float dot8(u32x4 w, u32x4 h, float acc) {
   return acc;
 }
 
+// Eight E4M3 codes (bytes 0..7 of lo:hi) as eight bf16 values, exactly
+// (every E4M3 value, subnormals included, is a bf16 number).  The gfx950
+// conversion takes two codes from one 16-bit half of a dword; its scale
+// operand is 1.
+__device__ __forceinline__ u32x4 fp8x8_to_bf16x8(uint32_t lo, uint32_t hi) {
+  const bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, false);
+  const bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, true);
+  const bf16x2 c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, false);
+  const bf16x2 d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, true);
+  return u32x4{__builtin_bit_cast(uint32_t, a), __builtin_bit_cast(uint32_t, b), __builtin_bit_cast(uint32_t, c),
+               __builtin_bit_cast(uint32_t, d)};
+}
+
+// E4M3 code of an fp32 value (OCP FP8 E4M3: bias 7, 3 mantissa bits,
+// subnormals m * 2^-9, largest finite 448): the nearest value, ties to the
+// even code, magnitudes from 448 up saturating to 448; the sign bit is the
+// input's.  Written from the format: below 2^-6 the step is 2^-9, so the
+// code is the magnitude in units of 2^-9 rounded to nearest even; above,
+// the fp32 fraction is rounded to 3 bits and a carry moves the exponent.
+__device__ __forceinline__ uint32_t e4m3_encode(float q) {
+  const uint32_t bits = __builtin_bit_cast(uint32_t, q);
+  const uint32_t sign = (bits >> 24) & 0x80u;
+  const float a = __builtin_fabsf(q);
+  uint32_t code;
+  if (!(a < 448.0f)) {
+    code = 0x7Eu;
+  } else if (a < 0.015625f) {
+    code = (uint32_t)__builtin_rintf(a * 512.0f);  // exact scaling; 8 lands on 2^-6 = code 0x08
+  } else {
+    const uint32_t ab = __builtin_bit_cast(uint32_t, a);
+    const uint32_t e = (ab >> 23) - 127u + 7u;  // 1 .. 15
+    const uint32_t frac = ab & 0x7FFFFFu;
+    uint32_t keep = frac >> 20;
+    const uint32_t rest = frac & 0xFFFFFu;
+    if (rest > 0x80000u || (rest == 0x80000u && (keep & 1u))) ++keep;
+    code = (e << 3) + keep;  // keep == 8 carries into the exponent
+    if (code > 0x7Eu) code = 0x7Eu;
+  }
+  return sign | code;
+}
+
 // Wave index inside the workgroup, as a value the compiler knows is uniform
 // (so row bases and buffer descriptors live in scalar registers).
 __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)); }
@@ -510,6 +551,56 @@ gather_rows(const uint16_t* __restrict__ W, int64_t N, int K, const int32_t* __r
   }
 }
 
+// FP8 copy of a bf16 head, one wave per row: scale = fp32(max |W[r, :]| /
+// 448) (1 for an all-zero row), code = e4m3_encode(W / scale) with both
+// divisions correctly rounded.  The row stays in registers between the two
+// passes (K <= 8192: at most 16 chunks of 8 values per lane).
+constexpr int kQuantMaxChunksPerLane = 16;
+
+__global__ void __launch_bounds__(256)
+quantize_rows_fp8(const uint16_t* __restrict__ W, int R, int K, uint8_t* __restrict__ Wq,
+                  float* __restrict__ scale) {
+  const int lane = threadIdx.x & 63;
+  const int chunks = K >> 3;
+  const int nwaves = gridDim.x * 4;
+  for (int r = blockIdx.x * 4 + wave_id(); r < R; r += nwaves) {
+    const u32x4* row = reinterpret_cast<const u32x4*>(W + (size_t)r * K);
+    u32x4 v[kQuantMaxChunksPerLane];
+    float amax = 0.0f;
+#pragma unroll
+    for (int j = 0; j < kQuantMaxChunksPerLane; ++j) {
+      const int c = lane + 64 * j;
+      v[j] = c < chunks ? row[c] : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float x0 = __builtin_bit_cast(float, v[j][e] << 16);
+        const float x1 = __builtin_bit_cast(float, v[j][e] & 0xFFFF0000u);
+        amax = __builtin_fmaxf(amax, __builtin_fmaxf(__builtin_fabsf(x0), __builtin_fabsf(x1)));
+      }
+    }
+#pragma unroll
+    for (int x = 32; x >= 1; x >>= 1) amax = __builtin_fmaxf(amax, __shfl_xor(amax, x));
+    const float sc = amax > 0.0f ? __fdiv_rn(amax, 448.0f) : 1.0f;
+    if (lane == 0) scale[r] = sc;
+    uint2* out = reinterpret_cast<uint2*>(Wq + (size_t)r * K);
+#pragma unroll
+    for (int j = 0; j < kQuantMaxChunksPerLane; ++j) {
+      const int c = lane + 64 * j;
+      if (c < chunks) {
+        uint32_t b[2] = {0u, 0u};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float x0 = __builtin_bit_cast(float, v[j][e] << 16);
+          const float x1 = __builtin_bit_cast(float, v[j][e] & 0xFFFF0000u);
+          const uint32_t pair = e4m3_encode(__fdiv_rn(x0, sc)) | (e4m3_encode(__fdiv_rn(x1, sc)) << 8);
+          b[e >> 1] |= pair << (16 * (e & 1));
+        }
+        out[c] = uint2{b[0], b[1]};
+      }
+    }
+  }
+}
+
 // Epilogue of the VALU kernels, where every row sum is wave-uniform after
 // the DPP reduction: the running best row per hidden row (TK == 1), the
 // best 16 keys of hidden row rho = lane / 16 over that DPP row (TK > 1,
@@ -757,6 +848,126 @@ proj_valu_tiled(const uint16_t* __restrict__ h, const uint16_t* __restrict__ W, 
   ep.finish(lane, wave, epi);
 }
 
+// VALU path over an FP8 head (E4M3 codes, one fp32 scale per row), tiled
+// like proj_valu_tiled: a wave owns tiles of TR consecutive head rows and
+// walks them in 1 KiB column stripes, now 1,024 codes per stripe, so lane l
+// takes codes 16 l .. 16 l + 15 and the hidden rows' matching 32 bytes from
+// LDS.  Codes become bf16 in registers (exact) and meet the hidden rows in
+// packed bf16 dot products with fp32 accumulation; a row's sum is then
+// multiplied by its scale.  The tile's scales are read with scalar loads one
+// tile ahead (the wave's next tile), so they never wait on the W stream.
+template <int M, int TR, int WV, int TK, bool LOGITS>
+__global__ void __launch_bounds__(64 * WV)
+proj_valu_fp8(const uint16_t* __restrict__ h, const uint8_t* __restrict__ W, const float* __restrict__ wscale,
+              int R, int K, Epi epi) {
+  extern __shared__ u32x4 h_stripes[];  // [M][nb * 128] chunks of 8 bf16, zero past K
+  const int lane = threadIdx.x & 63;
+  const int wave = wave_id();
+  const int hchunks = K >> 3;
+  const int wchunks = K >> 4;
+  const int nb = (wchunks + 63) >> 6;  // stripes per row
+  const int hc = nb * 128;
+  const uint32_t row_bytes = (uint32_t)K;
+
+  for (int i = threadIdx.x; i < M * hc; i += (64 * WV)) {
+    const int m = i / hc;
+    const int c = i - m * hc;
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (c < hchunks) v = *reinterpret_cast<const u32x4*>(h + (size_t)m * K + (size_t)c * 8);
+    h_stripes[i] = v;
+  }
+  __syncthreads();
+
+  ValuEpilogue<M, WV, TK, LOGITS> ep;
+  ep.init();
+  float acc[TR][M];
+#pragma unroll
+  for (int q = 0; q < TR; ++q)
+#pragma unroll
+    for (int m = 0; m < M; ++m) acc[q][m] = 0.0f;
+
+  const int ntiles = (R + TR - 1) / TR;
+  const int tstride = gridDim.x * WV;
+  float sc[TR];
+  auto load_scales = [&](int tile) {
+    const int r0 = tile * TR;
+#pragma unroll
+    for (int q = 0; q < TR; ++q) sc[q] = wscale[min(r0 + q, R - 1)];
+  };
+
+  auto issue = [&](u32x4 (&w)[TR], int tile, int j) {
+    const int c = lane + 64 * j;
+    const int r0 = tile * TR;
+    const int live = min(TR, R - r0);
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(W + (size_t)r0 * (size_t)K, (uint32_t)live * row_bytes);
+    const uint32_t off = c < wchunks ? (uint32_t)c * 16u : kOobOffset;
+#pragma unroll
+    for (int q = 0; q < TR; ++q) w[q] = load16(rs, off + (uint32_t)q * row_bytes);
+  };
+  auto consume = [&](const u32x4 (&w)[TR], int tile, int j) {
+    u32x4 lo[TR], hi[TR];
+#pragma unroll
+    for (int q = 0; q < TR; ++q) {
+      lo[q] = fp8x8_to_bf16x8(w[q].x, w[q].y);
+      hi[q] = fp8x8_to_bf16x8(w[q].z, w[q].w);
+    }
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+      const u32x4 h0 = h_stripes[m * hc + j * 128 + 2 * lane];
+      const u32x4 h1 = h_stripes[m * hc + j * 128 + 2 * lane + 1];
+#pragma unroll
+      for (int q = 0; q < TR; ++q) acc[q][m] = dot8(hi[q], h1, dot8(lo[q], h0, acc[q][m]));
+    }
+    if (j == nb - 1) {
+      const int r0 = tile * TR;
+#pragma unroll
+      for (int q = 0; q < TR; ++q) {
+        float sum[M];
+#pragma unroll
+        for (int m = 0; m < M; ++m) {
+          sum[m] = wave_sum(acc[q][m]) * sc[q];
+          acc[q][m] = 0.0f;
+        }
+        if (r0 + q < R) ep.row(sum, r0 + q, lane, epi);
+      }
+      load_scales(tile + tstride);  // the next tile this wave finishes
+    }
+  };
+  auto advance = [&](int& tile, int& j) {
+    if (++j == nb) {
+      j = 0;
+      tile += tstride;
+    }
+  };
+
+  int tile = blockIdx.x * WV + wave;
+  int j = 0;
+  u32x4 wa[TR], wb[TR];
+  if (tile < ntiles) {
+    load_scales(tile);
+    issue(wa, tile, 0);
+    while (true) {
+      int t1 = tile, j1 = j;
+      advance(t1, j1);
+      bool more = t1 < ntiles;
+      if (more) issue(wb, t1, j1);
+      consume(wa, tile, j);
+      if (!more) break;
+      tile = t1;
+      j = j1;
+      advance(t1, j1);
+      more = t1 < ntiles;
+      if (more) issue(wa, t1, j1);
+      consume(wb, tile, j);
+      if (!more) break;
+      tile = t1;
+      j = j1;
+    }
+  }
+
+  ep.finish(lane, wave, epi);
+}
+
 // ---------------------------------------------------------------------------
 // matrix-core path
 // ---------------------------------------------------------------------------
@@ -769,21 +980,28 @@ proj_valu_tiled(const uint16_t* __restrict__ h, const uint16_t* __restrict__ W, 
 // stage, and reads the A operands back in MFMA layout.  Hidden rows are in
 // LDS as in proj_argmax_mfma.  The stage is private to the wave, so the
 // exchange needs only wave-level ordering, not a workgroup barrier.
-template <int NT, int SB, int WV, int D, int TK, bool LOGITS>
+template <int NT, int SB, int WV, int D, int TK, bool LOGITS, bool FP8>
 __global__ void __launch_bounds__(64 * WV)
-proj_mfma(const uint16_t* __restrict__ h, const uint16_t* __restrict__ W, int R, int K, int m_base, int mp,
-          Epi epi) {
-  static_assert(SB == 4 || SB == 8 || SB == 16, "a load instruction covers whole row pieces");
-  constexpr int BC = 4 * SB;    // 16-byte chunks per row per batch
-  constexpr int SC = BC + 1;    // stage row stride in chunks (padded against bank conflicts)
-  constexpr int RPI = 64 / BC;  // rows per load instruction
+proj_mfma(const uint16_t* __restrict__ h, const void* __restrict__ Wv, const float* __restrict__ wscale, int R,
+          int K, int m_base, int mp, Epi epi) {
+  // A k-step is 32 head-row elements: four 16-byte chunks of bf16, or two of
+  // E4M3 codes (FP8: codes become bf16 when read from the stage, and a
+  // row's sum is multiplied by its fp32 scale).
+  constexpr int CPS = FP8 ? 2 : 4;  // 16-byte chunks per k-step
+  constexpr int BC = CPS * SB;      // 16-byte chunks per row per batch
+  static_assert(BC == 16 || BC == 32 || BC == 64, "a load instruction covers whole row pieces");
+  constexpr int SC = BC + 1;        // stage row stride in chunks (padded against bank conflicts)
+  constexpr int RPI = 64 / BC;      // rows per load instruction
+  constexpr int LPB = 16 / RPI;     // load instructions per batch
+  const uint8_t* W = static_cast<const uint8_t*>(Wv);
   extern __shared__ u32x4 lds[];  // [mp][row_chunks] hidden rows, then [WV][16][SC] stages
   __shared__ unsigned long long s_key[TK == 1 && !LOGITS ? WV : 1][32];
   const int lane = threadIdx.x & 63;
   const int wave = wave_id();
   const int i16 = lane & 15;
   const int g = lane >> 4;
-  const int chunks = K >> 3;
+  const int chunks = K >> 3;                         // 16-byte chunks of a hidden row
+  const int wchunks = FP8 ? (K >> 4) : (K >> 3);     // 16-byte chunks of a head row
   const int steps = (K + 31) >> 5;
   const int s4 = steps * 4;
   const int row_chunks = s4 + 1;
@@ -831,29 +1049,50 @@ proj_mfma(const uint16_t* __restrict__ h, const uint16_t* __restrict__ W, int R,
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  const uint32_t row_bytes = (uint32_t)K * 2u;
+  const uint32_t row_bytes = FP8 ? (uint32_t)K : (uint32_t)K * 2u;
   const int ntiles = (R + 15) >> 4;
   const int nbatch = (steps + SB - 1) / SB;
   const int lrow = lane / BC;  // row of this lane within a load instruction
   const int lc = lane % BC;    // chunk of this lane within the batch
 
-  uint32_t rowoff[SB];
+  const int tstride = gridDim.x * WV;  // tiles between a wave's consecutive tiles
+  uint32_t rowoff[LPB];
 #pragma unroll
-  for (int q = 0; q < SB; ++q) rowoff[q] = (uint32_t)(q * RPI + lrow) * row_bytes;
+  for (int q = 0; q < LPB; ++q) rowoff[q] = (uint32_t)(q * RPI + lrow) * row_bytes;
+
+  // FP8: scales of head rows r0 .. r0 + 15 of a tile, read with scalar
+  // loads one tile ahead (the wave's next tile), clamped to the last row.
+  float sc[FP8 ? 16 : 1];
+  auto load_scales = [&](int tile) {
+    if constexpr (FP8) {
+      const int r0 = tile * 16;
+#pragma unroll
+      for (int j = 0; j < 16; ++j) sc[j] = wscale[min(r0 + j, R - 1)];
+    }
+  };
 
   // Positions past the last tile get a descriptor with no records, so their
   // loads read zero without touching memory (live is clamped at 0).
-  auto issue = [&](u32x4 (&buf)[SB], int tile, int b) {
+  auto issue = [&](u32x4 (&buf)[LPB], int tile, int b) {
     const int r0 = tile < ntiles ? tile * 16 : 0;
     const int live = tile < ntiles ? min(16, R - r0) : 0;
-    const __amdgpu_buffer_rsrc_t rs = make_rsrc(W + (size_t)r0 * K, (uint32_t)live * row_bytes);
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(W + (size_t)r0 * row_bytes, (uint32_t)live * row_bytes);
     // Column offset of this lane, or an offset past num_records for chunks
     // beyond K.  Selected once per batch so the loads themselves carry no
     // condition (and stay countable for the wait counters).
     const int cg = b * BC + lc;
-    const uint32_t cbase = cg < chunks ? (uint32_t)cg * 16u : kOobOffset;
+    const uint32_t cbase = cg < wchunks ? (uint32_t)cg * 16u : kOobOffset;
 #pragma unroll
-    for (int q = 0; q < SB; ++q) buf[q] = load16<kPolicyStream>(rs, cbase + rowoff[q]);
+    for (int q = 0; q < LPB; ++q) buf[q] = load16<kPolicyStream>(rs, cbase + rowoff[q]);
+  };
+  // A operand of k-step sb of the staged batch: 8 elements of row i16
+  auto a_operand = [&](int sb) -> u32x4 {
+    if constexpr (FP8) {
+      const uint2 raw = reinterpret_cast<const uint2*>(stage)[(i16 * SC + 2 * sb) * 2 + g];
+      return fp8x8_to_bf16x8(raw.x, raw.y);
+    } else {
+      return stage[i16 * SC + 4 * sb + g];
+    }
   };
   auto mma_step = [&](const u32x4& a, int s) {
 #pragma unroll
@@ -863,9 +1102,9 @@ proj_mfma(const uint16_t* __restrict__ h, const uint16_t* __restrict__ W, int R,
                                                         __builtin_bit_cast(bf16x8, bf), acc[nt], 0, 0, 0);
     }
   };
-  auto consume = [&](const u32x4 (&buf)[SB], int b) {
+  auto consume = [&](const u32x4 (&buf)[LPB], int b) {
 #pragma unroll
-    for (int q = 0; q < SB; ++q) stage[(q * RPI + lrow) * SC + lc] = buf[q];
+    for (int q = 0; q < LPB; ++q) stage[(q * RPI + lrow) * SC + lc] = buf[q];
     // lanes of this wave exchange data through the stage
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
@@ -874,14 +1113,14 @@ proj_mfma(const uint16_t* __restrict__ h, const uint16_t* __restrict__ W, int R,
       // whole batch: all operand reads first, then the matrix instructions
       u32x4 a[SB];
 #pragma unroll
-      for (int sb = 0; sb < SB; ++sb) a[sb] = stage[i16 * SC + 4 * sb + g];
+      for (int sb = 0; sb < SB; ++sb) a[sb] = a_operand(sb);
 #pragma unroll
       for (int sb = 0; sb < SB; ++sb) mma_step(a[sb], b * SB + sb);
     } else {
 #pragma unroll
       for (int sb = 0; sb < SB; ++sb) {
         const int s = b * SB + sb;
-        if (s < steps) mma_step(stage[i16 * SC + 4 * sb + g], s);
+        if (s < steps) mma_step(a_operand(sb), s);
       }
     }
     // the next batch overwrites the stage only after these reads
@@ -895,6 +1134,20 @@ proj_mfma(const uint16_t* __restrict__ h, const uint16_t* __restrict__ W, int R,
       LOGITS && !epi.d2t && (epi.ld & 3) == 0 && (reinterpret_cast<uintptr_t>(epi.logits) & 15) == 0;
   auto finish_tile = [&](int tile) __attribute__((always_inline)) {
     const int r0 = tile * 16;
+    if constexpr (FP8) {
+      // this lane's rows are 4 g + v: pick their scales, then prefetch.
+      // The pick is a sum with 0 / 1 weights (exact for finite scales): a
+      // select chain would become an indexed array in scratch memory.
+      const float w0 = g == 0 ? 1.0f : 0.0f, w1 = g == 1 ? 1.0f : 0.0f;
+      const float w2 = g == 2 ? 1.0f : 0.0f, w3 = g == 3 ? 1.0f : 0.0f;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const float s = (sc[v] * w0 + sc[4 + v] * w1) + (sc[8 + v] * w2 + sc[12 + v] * w3);
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) acc[nt][v] *= s;
+      }
+      load_scales(tile + tstride);
+    }
     if (LOGITS && vec_logits && r0 + 4 * g + 3 < R) {
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
@@ -941,7 +1194,6 @@ proj_mfma(const uint16_t* __restrict__ h, const uint16_t* __restrict__ W, int R,
   // The wave walks (tile, batch) pairs in order with a ring of D register
   // buffers: D - 1 batches are in flight while one is transposed and fed to
   // the matrix cores.  The loop is unrolled D times so ring slots are static.
-  const int tstride = gridDim.x * WV;
   int ti = blockIdx.x * WV + wave, bi = 0;  // next pair to issue
   int tc = ti, bc = 0;                      // next pair to consume
   auto advance = [&](int& t, int& bb) {
@@ -953,7 +1205,8 @@ proj_mfma(const uint16_t* __restrict__ h, const uint16_t* __restrict__ W, int R,
   // Number of (tile, batch) pairs this wave consumes.
   const int my_tiles = tc < ntiles ? (ntiles - 1 - tc) / tstride + 1 : 0;
   const int count = my_tiles * nbatch;
-  u32x4 ring[D][SB];
+  u32x4 ring[D][LPB];
+  load_scales(ti);
 #pragma unroll
   for (int j = 0; j < D - 1; ++j) {
     issue(ring[j], ti, bi);
@@ -1243,25 +1496,48 @@ int mfma_lds_rows_fit(int64_t K, int waves) {
 // One pass of the matrix-core path over hidden rows [m_base, m_base + mp):
 // 8 waves per workgroup when the hidden rows and eight stages fit the LDS,
 // else 4; two 16-column tiles when mp > 16.
-template <int TK, bool LOGITS>
-int launch_mfma_pass(const uint16_t* h, int K, int m_base, int mp, const uint16_t* W, int R, const Epi& epi,
-                     int cus, hipStream_t stream, int* grid_out) {
-  constexpr int SB = LMH_MFMA_LDS_SB;
+// FP8 heads take twice the k-steps per batch, so a batch moves the same
+// bytes (and the stage has the same size) as for bf16.
+template <int TK, bool LOGITS, bool FP8>
+int launch_mfma_pass(const uint16_t* h, int K, int m_base, int mp, const void* W, const float* wscale, int R,
+                     const Epi& epi, int cus, hipStream_t stream, int* grid_out) {
+  constexpr int SB = FP8 ? 2 * LMH_MFMA_LDS_SB : LMH_MFMA_LDS_SB;
   constexpr int D = LMH_MFMA_RING;
   const size_t hbytes = (size_t)mp * mfma_row_bytes(K);
   const int64_t tiles = (R + 15) / 16;
   const bool eight = mp <= mfma_lds_rows_fit(K, 8);
-  const size_t lds = hbytes + (size_t)(eight ? 8 : 4) * 16 * (4 * SB + 1) * 16;
+  const size_t lds = hbytes + (size_t)(eight ? 8 : 4) * 16 * (4 * LMH_MFMA_LDS_SB + 1) * 16;
   const char* what = "launch matrix-core projection";
   if (mp <= 16)
-    return eight ? launch_persistent(proj_mfma<1, SB, 8, D, TK, LOGITS>, 512, lds, tiles, 8, 1 << 20, cus, stream,
-                                     what, grid_out, h, W, R, K, m_base, mp, epi)
-                 : launch_persistent(proj_mfma<1, SB, 4, D, TK, LOGITS>, 256, lds, tiles, 4, 1 << 20, cus, stream,
-                                     what, grid_out, h, W, R, K, m_base, mp, epi);
-  return eight ? launch_persistent(proj_mfma<2, SB, 8, D, TK, LOGITS>, 512, lds, tiles, 8, 1 << 20, cus, stream,
-                                   what, grid_out, h, W, R, K, m_base, mp, epi)
-               : launch_persistent(proj_mfma<2, SB, 4, D, TK, LOGITS>, 256, lds, tiles, 4, 1 << 20, cus, stream,
-                                   what, grid_out, h, W, R, K, m_base, mp, epi);
+    return eight ? launch_persistent(proj_mfma<1, SB, 8, D, TK, LOGITS, FP8>, 512, lds, tiles, 8, 1 << 20, cus,
+                                     stream, what, grid_out, h, W, wscale, R, K, m_base, mp, epi)
+                 : launch_persistent(proj_mfma<1, SB, 4, D, TK, LOGITS, FP8>, 256, lds, tiles, 4, 1 << 20, cus,
+                                     stream, what, grid_out, h, W, wscale, R, K, m_base, mp, epi);
+  return eight ? launch_persistent(proj_mfma<2, SB, 8, D, TK, LOGITS, FP8>, 512, lds, tiles, 8, 1 << 20, cus,
+                                   stream, what, grid_out, h, W, wscale, R, K, m_base, mp, epi)
+               : launch_persistent(proj_mfma<2, SB, 4, D, TK, LOGITS, FP8>, 256, lds, tiles, 4, 1 << 20, cus,
+                                   stream, what, grid_out, h, W, wscale, R, K, m_base, mp, epi);
+}
+
+// VALU path over an FP8 head: the tiled kernel for every M <= 4.
+typedef void (*proj_fp8_fn)(const uint16_t*, const uint8_t*, const float*, int, int, Epi);
+
+int launch_valu_fp8(const uint16_t* h, int M, int K, const uint8_t* Wq, const float* wscale, int R,
+                    const Epi& epi, int cus, hipStream_t stream, int* grid_out) {
+  constexpr int TR = LMH_VALU_TILE_ROWS > 0 ? LMH_VALU_TILE_ROWS : 4;
+  constexpr int WV = LMH_VALU_WAVES;
+  proj_fp8_fn fn = nullptr;
+  switch (M) {
+    case 1: fn = proj_valu_fp8<1, TR, WV, 1, false>; break;
+    case 2: fn = proj_valu_fp8<2, TR, WV, 1, false>; break;
+    case 3: fn = proj_valu_fp8<3, TR, WV, 1, false>; break;
+    case 4: fn = proj_valu_fp8<4, TR, WV, 1, false>; break;
+    default: return LMH_EINVAL;
+  }
+  const int nb = (K / 16 + 63) / 64;
+  const size_t lds = (size_t)M * nb * 128 * 16;
+  return launch_persistent(fn, 64 * WV, lds, R, WV * TR, LMH_VALU_WG_PER_CU, cus, stream,
+                           "launch VALU FP8 projection", grid_out, h, Wq, wscale, R, K, epi);
 }
 
 int launch_finalize_argmax(unsigned long long* slots, int nslots, int m_base, int mcount, const int32_t* d2t,
@@ -1281,17 +1557,19 @@ int launch_finalize_topk(unsigned long long* slots, int nslots, int m_base, int 
   return e == hipSuccess ? LMH_OK : hip_fail(e, "launch finalize_topk");
 }
 
-// What one call asks for.
+// What one call asks for.  With `wscale` set, W holds E4M3 codes and
+// wscale one fp32 scale per row (argmax only).
 struct Call {
   const uint16_t* h;
   int M;
   int K;
-  const uint16_t* W;
+  const void* W;
   int R;
   const int32_t* d2t;
   int path;
   hipStream_t stream;
   bool projection_only = false;  // measurement: skip the fold (outputs untouched)
+  const float* wscale = nullptr;
 };
 
 int record(hipEvent_t e, hipStream_t s) {
@@ -1316,11 +1594,18 @@ int run(const Call& c, const Epi& epi, int topk, int32_t* out_id, float* out_log
     else
       return LMH_OK;
   };
+  const bool fp8 = c.wscale != nullptr;
+  if (fp8 && MODE != 0) return LMH_EINVAL;
   if (c.path == LMH_PATH_VALU) {
-    const ValuPlan p = valu_plan<TK, LOGITS>(c.M, c.K);
-    if (!p.fn) return LMH_EINVAL;
     int grid = 0;
-    st = launch_valu(p, c.h, c.K, c.W, c.R, epi, cus, c.stream, &grid);
+    if (fp8) {
+      st = launch_valu_fp8(c.h, c.M, c.K, static_cast<const uint8_t*>(c.W), c.wscale, c.R, epi, cus, c.stream,
+                           &grid);
+    } else {
+      const ValuPlan p = valu_plan<TK, LOGITS>(c.M, c.K);
+      if (!p.fn) return LMH_EINVAL;
+      st = launch_valu(p, c.h, c.K, static_cast<const uint16_t*>(c.W), c.R, epi, cus, c.stream, &grid);
+    }
     if (st != LMH_OK) return st;
     return finalize(grid, 0, c.M);
   }
@@ -1331,7 +1616,13 @@ int run(const Call& c, const Epi& epi, int topk, int32_t* out_id, float* out_log
   for (int m0 = 0; m0 < c.M; m0 += per) {
     const int mp = std::min(per, c.M - m0);
     int grid = 0;
-    st = launch_mfma_pass<TK, LOGITS>(c.h, c.K, m0, mp, c.W, c.R, epi, cus, c.stream, &grid);
+    if constexpr (MODE == 0) {
+      st = fp8 ? launch_mfma_pass<TK, LOGITS, true>(c.h, c.K, m0, mp, c.W, c.wscale, c.R, epi, cus, c.stream, &grid)
+               : launch_mfma_pass<TK, LOGITS, false>(c.h, c.K, m0, mp, c.W, nullptr, c.R, epi, cus, c.stream,
+                                                     &grid);
+    } else {
+      st = launch_mfma_pass<TK, LOGITS, false>(c.h, c.K, m0, mp, c.W, nullptr, c.R, epi, cus, c.stream, &grid);
+    }
     if (st != LMH_OK) return st;
     st = finalize(grid, m0, mp);
     if (st != LMH_OK) return st;
@@ -1353,6 +1644,70 @@ int check_common(const uint16_t* h, int64_t M, int64_t K, const uint16_t* W, int
                                                                                            : LMH_PATH_MFMA;
   if (*path == LMH_PATH_VALU && !(mode == 0 ? valu_ok(M, K) : valu_epi_ok(M, K))) return LMH_EINVAL;
   return LMH_OK;
+}
+
+// Checks for a call over an FP8 head: as check_common, plus K a multiple
+// of 16 (16-byte aligned rows of codes) and a 4-byte aligned scale array.
+int check_fp8(const uint16_t* h, int64_t M, int64_t K, const uint8_t* Wq, const float* wscale, int64_t R,
+              int* path) {
+  if (!h || !Wq || !wscale || (reinterpret_cast<uintptr_t>(wscale) & 3u) != 0) return LMH_EINVAL;
+  if (M < 1 || M > LMH_MAX_M || !k_ok(K) || (K % 16) != 0) return LMH_EINVAL;
+  if (R < 1 || R > kMaxRows) return LMH_EINVAL;
+  if (!aligned16(h) || !aligned16(Wq)) return LMH_EINVAL;
+  if (*path != LMH_PATH_AUTO && *path != LMH_PATH_VALU && *path != LMH_PATH_MFMA) return LMH_EINVAL;
+  // Measured on MI355X (full 248,320 x 2,560 head): the matrix-core kernel
+  // is faster for every M (98 us at M = 1 against 126 us for VALU, whose
+  // code conversions and dot products make it ALU-bound at 1 byte/weight).
+  if (*path == LMH_PATH_AUTO) *path = LMH_PATH_MFMA;
+  if (*path == LMH_PATH_VALU && M > 4) return LMH_EINVAL;
+  return LMH_OK;
+}
+
+// Mean projection-kernel time over `calls` back-to-back launches between two
+// events, then one whole call so the outputs hold a result (bench helpers).
+int time_projection(Call c, int nheads, const void* const* heads, const float* const* scales, const Epi& epi,
+                    int32_t* out_id, float* out_logit, int calls, double* proj_ms) {
+  hipEvent_t ev[2] = {nullptr, nullptr};
+  int st = LMH_OK;
+  for (auto& e : ev) {
+    const hipError_t r = hipEventCreate(&e);
+    if (r != hipSuccess) {
+      e = nullptr;
+      st = hip_fail(r, "hipEventCreate");
+      break;
+    }
+  }
+  // single-pass shapes only: the events must bracket projection kernels alone
+  const int cap = mfma_lds_rows_fit(c.K, 4);
+  if (st == LMH_OK && c.path == LMH_PATH_MFMA && (cap < 1 || c.M > cap)) st = LMH_EINVAL;
+  if (st == LMH_OK) st = record(ev[0], c.stream);
+  for (int i = 0; i < calls && st == LMH_OK; ++i) {
+    Call ci = c;
+    ci.W = heads[i % nheads];
+    ci.wscale = scales ? scales[i % nheads] : nullptr;
+    ci.projection_only = true;
+    st = run<0, 1>(ci, epi, 1, out_id, out_logit);
+  }
+  if (st == LMH_OK) st = record(ev[1], c.stream);
+  if (st == LMH_OK) {
+    Call c0 = c;
+    c0.W = heads[0];
+    c0.wscale = scales ? scales[0] : nullptr;
+    st = run<0, 1>(c0, epi, 1, out_id, out_logit);
+  }
+  if (st == LMH_OK) {
+    const hipError_t r = hipStreamSynchronize(c.stream);
+    if (r != hipSuccess) st = hip_fail(r, "hipStreamSynchronize");
+  }
+  float ms = 0.0f;
+  if (st == LMH_OK) {
+    const hipError_t r = hipEventElapsedTime(&ms, ev[0], ev[1]);
+    if (r != hipSuccess) st = hip_fail(r, "hipEventElapsedTime");
+  }
+  for (hipEvent_t e : ev)
+    if (e) (void)hipEventDestroy(e);
+  if (st == LMH_OK) *proj_ms = (double)ms / calls;
+  return st;
 }
 
 int topk_width(int64_t topk) {
@@ -1466,6 +1821,35 @@ int draft_project_logits(const uint16_t* h, int64_t M, int64_t K, const uint16_t
   return run<2, 1>(c, epi, 0, nullptr, nullptr);
 }
 
+int lmhead_quantize_fp8(const uint16_t* W, int64_t R, int64_t K, uint8_t* Wq, float* scale, void* stream) {
+  if (R < 0 || R > kMaxRows || !k_ok(K) || (K % 16) != 0) return LMH_EINVAL;
+  if (R == 0) return LMH_OK;
+  if (!W || !Wq || !scale || !aligned16(W) || !aligned16(Wq) || (reinterpret_cast<uintptr_t>(scale) & 3u) != 0)
+    return LMH_EINVAL;
+  int cus = 0;
+  const int st = cu_count(&cus);
+  if (st != LMH_OK) return st;
+  const int grid = (int)std::max<int64_t>(1, std::min<int64_t>((R + 3) / 4, (int64_t)cus * 16));
+  hipLaunchKernelGGL(quantize_rows_fp8, dim3(grid), dim3(256), 0, static_cast<hipStream_t>(stream), W, (int)R,
+                     (int)K, Wq, scale);
+  const hipError_t e = hipGetLastError();
+  return e == hipSuccess ? LMH_OK : hip_fail(e, "launch quantize_rows_fp8");
+}
+
+int draft_project_argmax_fp8(const uint16_t* h, int64_t M, int64_t K, const uint8_t* Wq, const float* scale,
+                             int64_t R, const int32_t* d2t, int32_t* out_id, float* out_logit, void* workspace,
+                             size_t workspace_bytes, int path, void* stream) {
+  int st = check_fp8(h, M, K, Wq, scale, R, &path);
+  if (st != LMH_OK) return st;
+  if (!out_id || !out_logit) return LMH_EINVAL;
+  if (!workspace || !aligned16(workspace)) return LMH_EWORKSPACE;
+  if (workspace_bytes < draft_project_workspace_bytes(M)) return LMH_EWORKSPACE;
+  Call c{h, (int)M, (int)K, Wq, (int)R, d2t, path, static_cast<hipStream_t>(stream)};
+  c.wscale = scale;
+  const Epi epi{static_cast<unsigned long long*>(workspace), nullptr, nullptr, 0, 0};
+  return run<0, 1>(c, epi, 1, out_id, out_logit);
+}
+
 const char* lmhead_status_str(int status) {
   switch (status) {
     case LMH_OK: return "ok";
@@ -1508,44 +1892,31 @@ int lmhead_bench_time_argmax(const uint16_t* h, int64_t M, int64_t K, const uint
   if (!out_id || !out_logit) return LMH_EINVAL;
   if (!workspace || !aligned16(workspace)) return LMH_EWORKSPACE;
   if (workspace_bytes < draft_project_workspace_bytes(M)) return LMH_EWORKSPACE;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  hipEvent_t ev[2] = {nullptr, nullptr};
-  for (auto& e : ev) {
-    const hipError_t r = hipEventCreate(&e);
-    if (r != hipSuccess) {
-      e = nullptr;
-      st = hip_fail(r, "hipEventCreate");
-      break;
-    }
-  }
+  const Call c{h, (int)M, (int)K, heads[0], (int)R, d2t, path, static_cast<hipStream_t>(stream)};
   const Epi epi{static_cast<unsigned long long*>(workspace), nullptr, nullptr, 0, 0};
-  // single-pass shapes only: the events must bracket projection kernels alone
-  const int cap = mfma_lds_rows_fit(K, 4);
-  if (st == LMH_OK && path == LMH_PATH_MFMA && (cap < 1 || M > cap)) st = LMH_EINVAL;
-  if (st == LMH_OK) st = record(ev[0], s);
-  for (int i = 0; i < calls && st == LMH_OK; ++i) {
-    Call c{h, (int)M, (int)K, heads[i % nheads], (int)R, d2t, path, s};
-    c.projection_only = true;
-    st = run<0, 1>(c, epi, 1, out_id, out_logit);
+  return time_projection(c, nheads, reinterpret_cast<const void* const*>(heads), nullptr, epi, out_id, out_logit,
+                         calls, proj_ms);
+}
+
+int lmhead_bench_time_argmax_fp8(const uint16_t* h, int64_t M, int64_t K, const uint8_t* const* heads,
+                                 const float* const* scales, int nheads, int64_t R, const int32_t* d2t,
+                                 int32_t* out_id, float* out_logit, void* workspace, size_t workspace_bytes,
+                                 int path, int calls, double* proj_ms, void* stream) {
+  if (!heads || !scales || nheads < 1 || calls < 1 || !proj_ms) return LMH_EINVAL;
+  const int path_in = path;
+  int st = LMH_OK;
+  for (int i = 0; i < nheads; ++i) {
+    path = path_in;
+    if ((st = check_fp8(h, M, K, heads[i], scales[i], R, &path)) != LMH_OK) return st;
   }
-  if (st == LMH_OK) st = record(ev[1], s);
-  if (st == LMH_OK) {  // one whole call, so the outputs hold a result
-    const Call c{h, (int)M, (int)K, heads[0], (int)R, d2t, path, s};
-    st = run<0, 1>(c, epi, 1, out_id, out_logit);
-  }
-  if (st == LMH_OK) {
-    const hipError_t r = hipStreamSynchronize(s);
-    if (r != hipSuccess) st = hip_fail(r, "hipStreamSynchronize");
-  }
-  float ms = 0.0f;
-  if (st == LMH_OK) {
-    const hipError_t r = hipEventElapsedTime(&ms, ev[0], ev[1]);
-    if (r != hipSuccess) st = hip_fail(r, "hipEventElapsedTime");
-  }
-  for (hipEvent_t e : ev)
-    if (e) (void)hipEventDestroy(e);
-  if (st == LMH_OK) *proj_ms = (double)ms / calls;
-  return st;
+  if (!out_id || !out_logit) return LMH_EINVAL;
+  if (!workspace || !aligned16(workspace)) return LMH_EWORKSPACE;
+  if (workspace_bytes < draft_project_workspace_bytes(M)) return LMH_EWORKSPACE;
+  Call c{h, (int)M, (int)K, heads[0], (int)R, d2t, path, static_cast<hipStream_t>(stream)};
+  c.wscale = scales[0];
+  const Epi epi{static_cast<unsigned long long*>(workspace), nullptr, nullptr, 0, 0};
+  return time_projection(c, nheads, reinterpret_cast<const void* const*>(heads), scales, epi, out_id, out_logit,
+                         calls, proj_ms);
 }
 
 int lmhead_bench_copy(const void* src, void* dst, size_t bytes, int grid, void* stream) {

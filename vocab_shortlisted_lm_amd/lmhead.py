@@ -22,7 +22,8 @@ __all__ = [
     "lmhead_last_error", "lmhead_bench_sink_words", "lmhead_bench_stream_read",
     "lmhead_bench_copy", "new_workspace", "read_id_list", "LMH_MAX_TOPK",
     "draft_project_topk_workspace_bytes", "draft_project_topk", "draft_project_logits",
-    "lmhead_bench_time_argmax",
+    "lmhead_bench_time_argmax", "lmhead_quantize_fp8", "draft_project_argmax_fp8",
+    "lmhead_bench_time_argmax_fp8",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "liblmhead.so")
@@ -53,6 +54,10 @@ SIGNATURES = {
     "lmhead_bench_copy": (_INT, [_P, _P, _SZ, _INT, _P]),
     "lmhead_bench_time_argmax": (_INT, [_P, _I64, _I64, _P, _INT, _I64, _P, _P, _P, _P, _SZ, _INT, _INT,
                                         ctypes.POINTER(ctypes.c_double), _P]),
+    "lmhead_quantize_fp8": (_INT, [_P, _I64, _I64, _P, _P, _P]),
+    "draft_project_argmax_fp8": (_INT, [_P, _I64, _I64, _P, _P, _I64, _P, _P, _P, _P, _SZ, _INT, _P]),
+    "lmhead_bench_time_argmax_fp8": (_INT, [_P, _I64, _I64, _P, _P, _INT, _I64, _P, _P, _P, _P, _SZ, _INT, _INT,
+                                            ctypes.POINTER(ctypes.c_double), _P]),
 }
 
 _lib = None
@@ -323,4 +328,85 @@ def lmhead_bench_time_argmax(h: torch.Tensor, heads: list, d2t: torch.Tensor | N
         out_id.data_ptr(), out_logit.data_ptr(), workspace.data_ptr(),
         workspace.numel() * workspace.element_size(), path, calls, ctypes.byref(out),
         _stream(stream, h.device)), "lmhead_bench_time_argmax")
+    return out.value
+
+
+def lmhead_quantize_fp8(W: torch.Tensor, out: torch.Tensor | None = None,
+                        scale: torch.Tensor | None = None, stream=None):
+    """(Wq uint8 [R, K] E4M3 codes, scale float32 [R]) of a bf16 head, one
+    scale per row.  Queues one kernel; never synchronizes."""
+    _dev_tensor(W, "W", _BF16_LIKE, 2)
+    r, k = W.shape
+    if out is None:
+        out = torch.empty((r, k), dtype=torch.uint8, device=W.device)
+    if scale is None:
+        scale = torch.empty(r, dtype=torch.float32, device=W.device)
+    _dev_tensor(out, "Wq", (torch.uint8,), 2)
+    _dev_tensor(scale, "scale", (torch.float32,), 1)
+    if tuple(out.shape) != (r, k) or scale.shape[0] < r:
+        raise ValueError("Wq must be [R, K] and scale hold R entries")
+    _check(lib().lmhead_quantize_fp8(W.data_ptr(), r, k, out.data_ptr(), scale.data_ptr(),
+                                     _stream(stream, W.device)), "lmhead_quantize_fp8")
+    return out, scale
+
+
+def _check_fp8_head(h, Wq, scale, d2t):
+    _dev_tensor(h, "h", _BF16_LIKE, 2)
+    _dev_tensor(Wq, "Wq", (torch.uint8,), 2)
+    _dev_tensor(scale, "scale", (torch.float32,), 1)
+    m, k = h.shape
+    r, k2 = Wq.shape
+    if k != k2:
+        raise ValueError("h and Wq must have the same K")
+    if scale.shape[0] != r:
+        raise ValueError("scale must have one entry per row of Wq")
+    if d2t is not None:
+        _dev_tensor(d2t, "d2t", (torch.int32,), 1)
+        if d2t.shape[0] != r:
+            raise ValueError("d2t must have one entry per row of Wq")
+    return m, k, r
+
+
+def draft_project_argmax_fp8(h: torch.Tensor, Wq: torch.Tensor, scale: torch.Tensor,
+                             d2t: torch.Tensor | None = None, path: int = LMH_PATH_AUTO,
+                             out_id: torch.Tensor | None = None, out_logit: torch.Tensor | None = None,
+                             workspace: torch.Tensor | None = None, stream=None):
+    """(out_id int32 [M], out_logit float32 [M]) for the best row of the
+    dequantized FP8 head per hidden row, mapped through d2t.  Never
+    synchronizes."""
+    m, k, r = _check_fp8_head(h, Wq, scale, d2t)
+    if out_id is None:
+        out_id = torch.empty(m, dtype=torch.int32, device=h.device)
+    if out_logit is None:
+        out_logit = torch.empty(m, dtype=torch.float32, device=h.device)
+    st = _stream(stream, h.device)
+    if workspace is None:
+        workspace = _default_workspace(h.device, st)
+    _check(lib().draft_project_argmax_fp8(
+        h.data_ptr(), m, k, Wq.data_ptr(), scale.data_ptr(), r,
+        d2t.data_ptr() if d2t is not None else None, out_id.data_ptr(), out_logit.data_ptr(),
+        workspace.data_ptr(), workspace.numel() * workspace.element_size(), path, st),
+        "draft_project_argmax_fp8")
+    return out_id, out_logit
+
+
+def lmhead_bench_time_argmax_fp8(h: torch.Tensor, heads: list, d2t: torch.Tensor | None, path: int,
+                                 calls: int, out_id: torch.Tensor, out_logit: torch.Tensor,
+                                 workspace: torch.Tensor, stream=None) -> float:
+    """lmhead_bench_time_argmax over FP8 heads: `heads` is a list of
+    (Wq, scale) pairs.  Synchronizes."""
+    m, k, r = _check_fp8_head(h, heads[0][0], heads[0][1], d2t)
+    for wq, sc in heads:
+        if tuple(wq.shape) != (r, k) or sc.shape[0] != r:
+            raise ValueError("every head must have the same shape")
+        _dev_tensor(wq, "Wq", (torch.uint8,), 2)
+        _dev_tensor(sc, "scale", (torch.float32,), 1)
+    qp = (ctypes.c_void_p * len(heads))(*[wq.data_ptr() for wq, _ in heads])
+    sp = (ctypes.c_void_p * len(heads))(*[sc.data_ptr() for _, sc in heads])
+    out = ctypes.c_double(0.0)
+    _check(lib().lmhead_bench_time_argmax_fp8(
+        h.data_ptr(), m, k, qp, sp, len(heads), r, d2t.data_ptr() if d2t is not None else None,
+        out_id.data_ptr(), out_logit.data_ptr(), workspace.data_ptr(),
+        workspace.numel() * workspace.element_size(), path, calls, ctypes.byref(out),
+        _stream(stream, h.device)), "lmhead_bench_time_argmax_fp8")
     return out.value
