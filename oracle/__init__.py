@@ -3,6 +3,7 @@ benchmark's CPU-baseline leg).  The product path never imports it."""
 from .fp8_head import (E4M3_MAX, e4m3_decode, e4m3_encode, oracle_dequant_fp8,
                        oracle_logits_fp8, oracle_project_argmax_fp8,
                        oracle_quantize_fp8)
+from .shortlist import oracle_overwrite_rows, oracle_union
 from .lmhead_oracle import (OracleResult, TopkResult, argmax_of_logits,
                             bf16_bits_to_f64, oracle_logits,
                             oracle_project_argmax, oracle_project_topk,
@@ -12,4 +13,5 @@ __all__ = ["OracleResult", "TopkResult", "argmax_of_logits", "bf16_bits_to_f64",
            "oracle_logits", "oracle_project_argmax", "oracle_project_topk",
            "oracle_scatter_logits", "oracle_trim", "E4M3_MAX", "e4m3_decode",
            "e4m3_encode", "oracle_quantize_fp8", "oracle_dequant_fp8",
-           "oracle_logits_fp8", "oracle_project_argmax_fp8"]
+           "oracle_logits_fp8", "oracle_project_argmax_fp8", "oracle_overwrite_rows",
+           "oracle_union"]
