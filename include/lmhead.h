@@ -56,6 +56,8 @@ typedef enum {
 #define LMH_MAX_K 8192
 #define LMH_MAX_R (1 << 30)
 #define LMH_MAX_TOPK 16
+#define LMH_MAX_OVERWRITE 65536      /* entries per lmhead_shortlist_overwrite call */
+#define LMH_MAX_UNION_VOCAB 524288   /* N of lmhead_shortlist_union (two LDS bitmaps) */
 
 /* Kernel choice for draft_project_argmax_path. */
 #define LMH_PATH_AUTO 0
@@ -223,6 +225,49 @@ int draft_project_argmax_fp8(const uint16_t* h, int64_t M, int64_t K,
                              int32_t* out_id, float* out_logit,
                              void* workspace, size_t workspace_bytes,
                              int path, void* stream);
+
+/*
+ * lmhead_shortlist_overwrite -- refresh rows of a trimmed head in place:
+ * for each entry i, W_trim[rows[i], :] = W[ids[i], :] and d2t[rows[i]] =
+ * ids[i].  This is how escaped ids are learned into spare head rows, the
+ * pages' fix for a static trim that misses tokens (krisbailey.com/articles/
+ * shortlist-mtp, the update in "Re-running the comparison fairly"): keep
+ * W_trim and d2t with room for `cap` rows, project over the first R, write
+ * newly seen ids into rows R, R + 1, ... and project over the grown prefix.
+ *
+ *  W       [N, K] bf16 (device, 16-byte aligned), not overlapping W_trim.
+ *  W_trim  [cap, K] bf16 (device, 16-byte aligned), written in place.
+ *  d2t     [cap] int32 (device), written in place.
+ *  rows, ids  [n] int32 (device), 0 <= n <= LMH_MAX_OVERWRITE.
+ * An entry with rows[i] outside [0, cap) or ids[i] outside [0, N) is
+ * skipped.  When several valid entries name the same row, the last one
+ * wins.  Asynchronous on `stream`; allocates nothing.  Order it against
+ * projections that read W_trim on other streams.  LMH_EINVAL for bad
+ * sizes, null or misaligned pointers, or overlapping W and W_trim.
+ */
+int lmhead_shortlist_overwrite(const uint16_t* W, int64_t N, int64_t K,
+                               uint16_t* W_trim, int32_t* d2t, int64_t cap,
+                               const int32_t* rows, const int32_t* ids,
+                               int64_t n, void* stream);
+
+/*
+ * lmhead_shortlist_union -- the sorted union of two id lists, on the
+ * device (the pages widen a list by merging candidates into it: ai-muninn.com
+ * "Qwen3.8-Flash-Next on two DGX Sparks", "Build the draft vocabulary from
+ * your own text", where 47,149 ids and 9,749 candidates, 5,606 of them new,
+ * give 52,755).
+ *
+ *  a [na], b [nb]  int32 ids (device), any order, duplicates allowed; ids
+ *                  outside [0, N) are ignored.  N <= LMH_MAX_UNION_VOCAB.
+ *  out    int32 (device), room for out_cap >= na + nb entries: receives
+ *         the union in ascending order, each id once.
+ *  counts int32[4] (device): |set a|, |set b|, |set b minus set a|, and
+ *         the union's size (the number of entries written to out).
+ * Asynchronous on `stream` (one workgroup); allocates nothing.
+ */
+int lmhead_shortlist_union(const int32_t* a, int64_t na, const int32_t* b,
+                           int64_t nb, int64_t N, int32_t* out,
+                           int64_t out_cap, int32_t* counts, void* stream);
 
 /* Which kernel draft_project_argmax picks for (M, K): an LMH_PATH_* value,
  * or -1 if the shape is not accepted. */

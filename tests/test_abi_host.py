@@ -169,6 +169,27 @@ def test_fp8_rejects_on_host(L):
     assert f(A, 4, 2560, B, C, 100, None, D, E, E, 8, 0, None) == 3    # workspace
 
 
+def test_shortlist_ops_reject_on_host(L):
+    lib = L.lib()
+    f = lib.lmhead_shortlist_overwrite
+    assert f(A, 100, 256, B, C, 50, D, E, 0, None) == 0                 # n = 0: no-op
+    assert f(A, 100, 256, B, C, 50, D, E, 65537, None) == 1             # n > LMH_MAX_OVERWRITE
+    assert f(A, 0, 256, B, C, 50, D, E, 4, None) == 1                   # N = 0
+    assert f(A, 100, 12, B, C, 50, D, E, 4, None) == 1                  # K
+    assert f(A, 100, 256, B, C, 0, D, E, 4, None) == 1                  # cap = 0
+    assert f(A, 100, 256, A + 512, C, 50, D, E, 4, None) == 1           # W_trim overlaps W
+    assert f(A, 100, 256, B + 8, C, 50, D, E, 4, None) == 1             # misaligned W_trim
+    assert f(A, 100, 256, B, None, 50, D, E, 4, None) == 1
+    assert f(A, 100, 256, B, C, 50, None, E, 4, None) == 1
+    u = lib.lmhead_shortlist_union
+    assert u(A, 10, B, 10, 1 << 19 | 1, C, 20, D, None) == 1            # N > LMH_MAX_UNION_VOCAB
+    assert u(A, 10, B, 10, 0, C, 20, D, None) == 1
+    assert u(A, 10, B, 10, 100, C, 19, D, None) == 1                    # out too small
+    assert u(A, 10, B, 10, 100, C, 20, None, None) == 1                 # no counts
+    assert u(None, 10, B, 10, 100, C, 20, D, None) == 1
+    assert u(A, -1, B, 10, 100, C, 20, D, None) == 1
+
+
 def test_trim_rejects_on_host(L):
     lib = L.lib()
     assert lib.lmhead_trim(A, 100, 2560, B, 0, C, None) == 0          # S = 0: no-op

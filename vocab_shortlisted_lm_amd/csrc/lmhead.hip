@@ -551,6 +551,106 @@ gather_rows(const uint16_t* __restrict__ W, int64_t N, int K, const int32_t* __r
   }
 }
 
+// In-place refresh of a trimmed head: entry i writes row ids[i] of W into
+// row rows[i] of W_trim and ids[i] into d2t[rows[i]].  One wave per entry;
+// an entry with a row outside [0, cap) or an id outside [0, N) is skipped,
+// and an entry is dropped when a later valid entry names the same row (the
+// last one wins), so every row has exactly one writer.  Escaped ids learned
+// into spare rows are the pages' fix for a static trim that misses
+// (Shortlist-MTP, the update in "Re-running the comparison fairly").
+__global__ void __launch_bounds__(256)
+overwrite_rows(const uint16_t* __restrict__ W, int64_t N, int K, uint16_t* __restrict__ W_trim, int32_t* d2t,
+               int64_t cap, const int32_t* __restrict__ rows, const int32_t* __restrict__ ids, int n) {
+  const int lane = threadIdx.x & 63;
+  const int chunks = K >> 3;
+  const int nwaves = gridDim.x * 4;
+  for (int i = blockIdx.x * 4 + wave_id(); i < n; i += nwaves) {
+    const int32_t r = rows[i];
+    const int32_t id = ids[i];
+    if (r < 0 || (int64_t)r >= cap || id < 0 || (int64_t)id >= N) continue;
+    bool later = false;
+    for (int j = i + 1 + lane; j < n; j += 64) {
+      const int32_t jd = ids[j];
+      later |= rows[j] == r && jd >= 0 && (int64_t)jd < N;
+    }
+    if (__any(later)) continue;
+    const u32x4* src = reinterpret_cast<const u32x4*>(W + (int64_t)id * K);
+    u32x4* dst = reinterpret_cast<u32x4*>(W_trim + (int64_t)r * K);
+    for (int c = lane; c < chunks; c += 64) dst[c] = src[c];
+    if (lane == 0) d2t[r] = id;
+  }
+}
+
+// Sorted union of two id lists in one workgroup: a bitmap per list in LDS,
+// counts of |A|, |B|, |B \ A| and |A u B| from them, then the union's ids in
+// ascending order through a block-wide prefix sum of per-thread popcounts
+// (the pages merge two lists this way: Two Sparks, "Build the draft
+// vocabulary from your own text").  Ids outside [0, N) are ignored.
+constexpr int kUnionThreads = 1024;
+constexpr int kUnionMaxVocab = 1 << 19;   // two bitmaps of 64 KiB
+
+__global__ void __launch_bounds__(kUnionThreads)
+union_ids(const int32_t* __restrict__ a, int na, const int32_t* __restrict__ b, int nb, int N,
+          int32_t* __restrict__ out, int32_t* __restrict__ counts) {
+  extern __shared__ uint32_t bits[];  // [2][words]
+  __shared__ uint32_t s_scan[kUnionThreads];
+  __shared__ uint32_t s_cnt[4];
+  const int t = threadIdx.x;
+  const int words = (N + 31) >> 5;
+  uint32_t* ba = bits;
+  uint32_t* bb = bits + words;
+  for (int w = t; w < 2 * words; w += kUnionThreads) bits[w] = 0u;
+  if (t < 4) s_cnt[t] = 0u;
+  __syncthreads();
+  for (int i = t; i < na; i += kUnionThreads) {
+    const int32_t x = a[i];
+    if (x >= 0 && x < N) atomicOr(&ba[x >> 5], 1u << (x & 31));
+  }
+  for (int i = t; i < nb; i += kUnionThreads) {
+    const int32_t x = b[i];
+    if (x >= 0 && x < N) atomicOr(&bb[x >> 5], 1u << (x & 31));
+  }
+  __syncthreads();
+  // each thread owns a contiguous run of words, so its ids come out in order
+  const int per = (words + kUnionThreads - 1) / kUnionThreads;
+  const int w0 = min(words, t * per), w1 = min(words, w0 + per);
+  uint32_t ca = 0, cb = 0, cnew = 0, cu = 0;
+  for (int w = w0; w < w1; ++w) {
+    ca += __popc(ba[w]);
+    cb += __popc(bb[w]);
+    cnew += __popc(bb[w] & ~ba[w]);
+    cu += __popc(ba[w] | bb[w]);
+  }
+  atomicAdd(&s_cnt[0], ca);
+  atomicAdd(&s_cnt[1], cb);
+  atomicAdd(&s_cnt[2], cnew);
+  // inclusive scan of cu over the workgroup (Hillis-Steele in LDS)
+  s_scan[t] = cu;
+  __syncthreads();
+  for (int d = 1; d < kUnionThreads; d <<= 1) {
+    const uint32_t v = t >= d ? s_scan[t - d] : 0u;
+    __syncthreads();
+    s_scan[t] += v;
+    __syncthreads();
+  }
+  uint32_t pos = s_scan[t] - cu;
+  for (int w = w0; w < w1; ++w) {
+    uint32_t m = ba[w] | bb[w];
+    while (m) {
+      const int bit = __builtin_ctz(m);
+      out[pos++] = (w << 5) + bit;
+      m &= m - 1u;
+    }
+  }
+  __syncthreads();
+  if (t == 0) {
+    counts[0] = (int32_t)s_cnt[0];
+    counts[1] = (int32_t)s_cnt[1];
+    counts[2] = (int32_t)s_cnt[2];
+    counts[3] = (int32_t)s_scan[kUnionThreads - 1];
+  }
+}
+
 // FP8 copy of a bf16 head, one wave per row: scale = fp32(max |W[r, :]| /
 // 448) (1 for an all-zero row), code = e4m3_encode(W / scale) with both
 // divisions correctly rounded.  The row stays in registers between the two
@@ -1819,6 +1919,39 @@ int draft_project_logits(const uint16_t* h, int64_t M, int64_t K, const uint16_t
   const Call c{h, (int)M, (int)K, W, (int)R, d2t, path, s};
   const Epi epi{nullptr, out, d2t, ncols, ncols};
   return run<2, 1>(c, epi, 0, nullptr, nullptr);
+}
+
+int lmhead_shortlist_overwrite(const uint16_t* W, int64_t N, int64_t K, uint16_t* W_trim, int32_t* d2t,
+                               int64_t cap, const int32_t* rows, const int32_t* ids, int64_t n, void* stream) {
+  if (n < 0 || n > LMH_MAX_OVERWRITE || N < 1 || N > (int64_t)0x7FFFFFFF || cap < 1 || cap > kMaxRows ||
+      !k_ok(K))
+    return LMH_EINVAL;
+  if (n == 0) return LMH_OK;
+  if (!W || !W_trim || !d2t || !rows || !ids || !aligned16(W) || !aligned16(W_trim)) return LMH_EINVAL;
+  const uintptr_t w0 = reinterpret_cast<uintptr_t>(W), t0 = reinterpret_cast<uintptr_t>(W_trim);
+  const uintptr_t w1 = w0 + (uintptr_t)N * (uintptr_t)K * 2u, t1 = t0 + (uintptr_t)cap * (uintptr_t)K * 2u;
+  if (t0 < w1 && w0 < t1) return LMH_EINVAL;  // W_trim must not overlap W
+  int cus = 0;
+  const int st = cu_count(&cus);
+  if (st != LMH_OK) return st;
+  const int grid = (int)std::max<int64_t>(1, std::min<int64_t>((n + 3) / 4, (int64_t)cus * 16));
+  hipLaunchKernelGGL(overwrite_rows, dim3(grid), dim3(256), 0, static_cast<hipStream_t>(stream), W, N, (int)K,
+                     W_trim, d2t, cap, rows, ids, (int)n);
+  const hipError_t e = hipGetLastError();
+  return e == hipSuccess ? LMH_OK : hip_fail(e, "launch overwrite_rows");
+}
+
+int lmhead_shortlist_union(const int32_t* a, int64_t na, const int32_t* b, int64_t nb, int64_t N, int32_t* out,
+                           int64_t out_cap, int32_t* counts, void* stream) {
+  if (na < 0 || nb < 0 || na > kMaxRows || nb > kMaxRows || N < 1 || N > kUnionMaxVocab) return LMH_EINVAL;
+  if (!counts || (na > 0 && !a) || (nb > 0 && !b) || ((na + nb) > 0 && !out) || out_cap < na + nb)
+    return LMH_EINVAL;
+  const size_t lds = (size_t)2 * (size_t)((N + 31) / 32) * 4;
+  allow_full_lds((const void*)union_ids);
+  hipLaunchKernelGGL(union_ids, dim3(1), dim3(kUnionThreads), lds, static_cast<hipStream_t>(stream), a, (int)na, b,
+                     (int)nb, (int)N, out, counts);
+  const hipError_t e = hipGetLastError();
+  return e == hipSuccess ? LMH_OK : hip_fail(e, "launch union_ids");
 }
 
 int lmhead_quantize_fp8(const uint16_t* W, int64_t R, int64_t K, uint8_t* Wq, float* scale, void* stream) {

@@ -23,7 +23,8 @@ __all__ = [
     "lmhead_bench_copy", "new_workspace", "read_id_list", "LMH_MAX_TOPK",
     "draft_project_topk_workspace_bytes", "draft_project_topk", "draft_project_logits",
     "lmhead_bench_time_argmax", "lmhead_quantize_fp8", "draft_project_argmax_fp8",
-    "lmhead_bench_time_argmax_fp8",
+    "lmhead_bench_time_argmax_fp8", "lmhead_shortlist_overwrite", "lmhead_shortlist_union",
+    "LMH_MAX_OVERWRITE", "LMH_MAX_UNION_VOCAB",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "liblmhead.so")
@@ -31,6 +32,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "liblmhead.s
 LMH_OK, LMH_EINVAL, LMH_ERANGE, LMH_EWORKSPACE, LMH_EHIP = 0, 1, 2, 3, 4
 LMH_MAX_M, LMH_MIN_K, LMH_MAX_K, LMH_MAX_TOPK = 32, 8, 8192, 16
 LMH_PATH_AUTO, LMH_PATH_VALU, LMH_PATH_MFMA = 0, 1, 2
+LMH_MAX_OVERWRITE, LMH_MAX_UNION_VOCAB = 65536, 524288
 
 _P = ctypes.c_void_p
 _I64 = ctypes.c_int64
@@ -55,6 +57,8 @@ SIGNATURES = {
     "lmhead_bench_time_argmax": (_INT, [_P, _I64, _I64, _P, _INT, _I64, _P, _P, _P, _P, _SZ, _INT, _INT,
                                         ctypes.POINTER(ctypes.c_double), _P]),
     "lmhead_quantize_fp8": (_INT, [_P, _I64, _I64, _P, _P, _P]),
+    "lmhead_shortlist_overwrite": (_INT, [_P, _I64, _I64, _P, _P, _I64, _P, _P, _I64, _P]),
+    "lmhead_shortlist_union": (_INT, [_P, _I64, _P, _I64, _I64, _P, _I64, _P, _P]),
     "draft_project_argmax_fp8": (_INT, [_P, _I64, _I64, _P, _P, _I64, _P, _P, _P, _P, _SZ, _INT, _P]),
     "lmhead_bench_time_argmax_fp8": (_INT, [_P, _I64, _I64, _P, _P, _INT, _I64, _P, _P, _P, _P, _SZ, _INT, _INT,
                                             ctypes.POINTER(ctypes.c_double), _P]),
@@ -410,3 +414,41 @@ def lmhead_bench_time_argmax_fp8(h: torch.Tensor, heads: list, d2t: torch.Tensor
         workspace.numel() * workspace.element_size(), path, calls, ctypes.byref(out),
         _stream(stream, h.device)), "lmhead_bench_time_argmax_fp8")
     return out.value
+
+
+def lmhead_shortlist_overwrite(W: torch.Tensor, W_trim: torch.Tensor, d2t: torch.Tensor,
+                               rows: torch.Tensor, ids: torch.Tensor, stream=None) -> None:
+    """W_trim[rows[i]] = W[ids[i]], d2t[rows[i]] = ids[i] in place (invalid
+    entries skipped, the last entry for a row wins).  Never synchronizes."""
+    _dev_tensor(W, "W", _BF16_LIKE, 2)
+    _dev_tensor(W_trim, "W_trim", _BF16_LIKE, 2)
+    _dev_tensor(d2t, "d2t", (torch.int32,), 1)
+    _dev_tensor(rows, "rows", (torch.int32,), 1)
+    _dev_tensor(ids, "ids", (torch.int32,), 1)
+    n, k = W.shape
+    cap, k2 = W_trim.shape
+    if k != k2 or d2t.shape[0] != cap or rows.shape[0] != ids.shape[0]:
+        raise ValueError("W [N, K], W_trim [cap, K], d2t [cap], rows and ids of one length")
+    _check(lib().lmhead_shortlist_overwrite(W.data_ptr(), n, k, W_trim.data_ptr(), d2t.data_ptr(), cap,
+                                            rows.data_ptr(), ids.data_ptr(), rows.shape[0],
+                                            _stream(stream, W.device)), "lmhead_shortlist_overwrite")
+
+
+def lmhead_shortlist_union(a: torch.Tensor, b: torch.Tensor, n_vocab: int, out: torch.Tensor | None = None,
+                           counts: torch.Tensor | None = None, stream=None):
+    """(out int32 [na + nb], counts int32 [4]): out[:counts[3]] is the
+    ascending union of a and b; counts = (|set a|, |set b|, |b - a|, |a u b|).
+    Never synchronizes."""
+    _dev_tensor(a, "a", (torch.int32,), 1)
+    _dev_tensor(b, "b", (torch.int32,), 1)
+    na, nb = a.shape[0], b.shape[0]
+    if out is None:
+        out = torch.empty(max(1, na + nb), dtype=torch.int32, device=a.device)
+    if counts is None:
+        counts = torch.empty(4, dtype=torch.int32, device=a.device)
+    _dev_tensor(out, "out", (torch.int32,), 1)
+    _dev_tensor(counts, "counts", (torch.int32,), 1)
+    _check(lib().lmhead_shortlist_union(a.data_ptr(), na, b.data_ptr(), nb, n_vocab, out.data_ptr(),
+                                        out.shape[0], counts.data_ptr(), _stream(stream, a.device)),
+           "lmhead_shortlist_union")
+    return out, counts
