@@ -6,7 +6,8 @@ from .fp8_head import (E4M3_MAX, e4m3_decode, e4m3_encode, oracle_dequant_fp8,
 from .shortlist import oracle_overwrite_rows, oracle_union
 from .lmhead_oracle import (OracleResult, TopkResult, argmax_of_logits,
                             bf16_bits_to_f64, oracle_logits,
-                            oracle_project_argmax, oracle_project_topk,
+                            oracle_project_argmax, oracle_project_argmax_indexed,
+                            oracle_project_topk,
                             oracle_scatter_logits, oracle_trim)
 
 __all__ = ["OracleResult", "TopkResult", "argmax_of_logits", "bf16_bits_to_f64",
@@ -14,4 +15,4 @@ __all__ = ["OracleResult", "TopkResult", "argmax_of_logits", "bf16_bits_to_f64",
            "oracle_scatter_logits", "oracle_trim", "E4M3_MAX", "e4m3_decode",
            "e4m3_encode", "oracle_quantize_fp8", "oracle_dequant_fp8",
            "oracle_logits_fp8", "oracle_project_argmax_fp8", "oracle_overwrite_rows",
-           "oracle_union"]
+           "oracle_union", "oracle_project_argmax_indexed"]

@@ -47,6 +47,7 @@ __all__ = [
     "oracle_project_argmax",
     "oracle_project_topk",
     "oracle_scatter_logits",
+    "oracle_project_argmax_indexed",
     "argmax_of_logits",
     "OracleResult",
     "TopkResult",
@@ -225,3 +226,19 @@ def oracle_scatter_logits(h_bits: np.ndarray, w_bits: np.ndarray,
     out = np.full((logits.shape[0], n), -np.inf)
     out[:, d2t] = logits
     return out
+
+
+def oracle_project_argmax_indexed(h_bits: np.ndarray, w_bits: np.ndarray, ids: np.ndarray,
+                                  keep_logits: bool = False) -> OracleResult:
+    """Greedy draft over the rows W[ids[i]] read in place, without a trimmed
+    copy: the same result as trimming the head to the list and projecting
+    with d2t = ids ("Two ways to run it", zone-1.cobraproject.com "Masked MTP
+    drafts": the list picks the head rows; the d2t map gives their ids).
+    Entries whose id lies outside [0, N) are skipped; idx is the position in
+    the list of the remaining entries, ties go to the earlier position."""
+    w_bits = np.asarray(w_bits)
+    ids = np.asarray(ids).astype(np.int64)
+    valid = ids[(ids >= 0) & (ids < w_bits.shape[0])]
+    if valid.size == 0:
+        raise ValueError("no listed row is a row of W")
+    return oracle_project_argmax(h_bits, oracle_trim(w_bits, valid), valid, keep_logits)

@@ -217,6 +217,33 @@ def pin_restriction_invariant(m):
         assert res.logit[i] == masked[i].max()
 
 
+def pin_indexed_restriction(m):
+    """Rows read through a list: the maximum of the full logits over the
+    listed ids, ties to the earlier list position, with invalid entries
+    (outside [0, N)) skipped."""
+    w, ids, hs = _tiny_inputs()
+    rng = np.random.default_rng(29)
+    lst = ids[rng.permutation(ids.size)].astype(np.int64)
+    lst = np.insert(lst, [0, 7, 100, lst.size], [-1, w.shape[0], w.shape[0] + 9, -20])
+    # exact ties: copies of one row under two listed ids, the later one first in the list
+    w = w.copy()
+    a, b = int(lst[5]), int(lst[40])
+    w[a] = w[b]
+    res = m.oracle_project_argmax_indexed(hs, w, lst)
+    full = m.oracle_logits(hs, w)
+    valid = lst[(lst >= 0) & (lst < w.shape[0])]
+    for i in range(hs.shape[0]):
+        vals = full[i, valid]
+        j = int(np.flatnonzero(vals == vals.max())[0])
+        assert res.idx[i] == j and res.id[i] == valid[j] and res.logit[i] == vals.max()
+    # every hidden row whose maximum is the duplicated row takes the earlier position (id a)
+    hs2 = synth.bf16_from_f32(lo.bf16_bits_to_f64(w[[a]]).astype(np.float32))
+    r2 = m.oracle_project_argmax_indexed(hs2, w, lst)
+    assert r2.id[0] == a
+    with pytest.raises(ValueError):
+        m.oracle_project_argmax_indexed(hs, w, np.array([-1, w.shape[0]]))
+
+
 def pin_scatter_equivalence(m):
     w, ids, hs = _tiny_inputs()
     perm = np.random.default_rng(23).permutation(ids.size)
@@ -309,7 +336,7 @@ PINS = [pin_decode_known, pin_decode_all_vs_torch, pin_bruteforce_fsum,
         pin_ties_first_occurrence, pin_gap_and_single_row, pin_trim_rows,
         pin_restriction_invariant, pin_scatter_equivalence, pin_identity_list,
         pin_rows_independent, pin_topk_bruteforce, pin_topk_ties_and_d2t,
-        pin_scatter_logits]
+        pin_scatter_logits, pin_indexed_restriction]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
@@ -327,6 +354,17 @@ _orig_project = lo.oracle_project_argmax
 _orig_trim = lo.oracle_trim
 _orig_topk = lo.oracle_project_topk
 _orig_scatter = lo.oracle_scatter_logits
+_orig_indexed = lo.oracle_project_argmax_indexed
+
+
+def _mut_indexed_wraps(h, w, ids, keep_logits=False):
+    n = np.asarray(w).shape[0]
+    return _orig_indexed(h, w, np.mod(np.asarray(ids), n), keep_logits)
+
+
+def _mut_indexed_ties_by_id(h, w, ids, keep_logits=False):
+    ids = np.asarray(ids)
+    return _orig_indexed(h, w, np.sort(ids[(ids >= 0) & (ids < np.asarray(w).shape[0])]), keep_logits)
 
 
 def _mut_decode_fp16(bits):
@@ -474,6 +512,8 @@ MUTANTS = {
     "topk_pads_zero": ("oracle_project_topk", _mut_topk_pads_zero),
     "scatter_zero_fill": ("oracle_scatter_logits", _mut_scatter_zero_fill),
     "scatter_by_position": ("oracle_scatter_logits", _mut_scatter_by_position),
+    "indexed_wraps_ids": ("oracle_project_argmax_indexed", _mut_indexed_wraps),
+    "indexed_sorted_list": ("oracle_project_argmax_indexed", _mut_indexed_ties_by_id),
     "decode_as_fp16": ("bf16_bits_to_f64", _mut_decode_fp16),
     "decode_shift15": ("bf16_bits_to_f64", _mut_decode_shift15),
     "logits_drop_last_k": ("oracle_logits", _mut_logits_drop_last),
