@@ -39,18 +39,20 @@ def weight_bytes(rows: int, k: int) -> int:
     return rows * k * 2
 
 
-def algorithmic_bytes(m: int, rows: int, k: int, with_d2t: bool, fp8: bool = False) -> int:
+def algorithmic_bytes(m: int, rows: int, k: int, with_d2t: bool, fp8: bool = False,
+                      indexed: bool = False) -> int:
     """Bytes one whole call must move at least: every weight row once, the
     hidden rows once, the d2t entries of the winners and the two outputs."""
-    return projection_bytes(m, rows, k, fp8) + (4 * m if with_d2t else 0) + 8 * m
+    return projection_bytes(m, rows, k, fp8, indexed) + (4 * m if with_d2t else 0) + 8 * m
 
 
-def projection_bytes(m: int, rows: int, k: int, fp8: bool = False) -> int:
+def projection_bytes(m: int, rows: int, k: int, fp8: bool = False, indexed: bool = False) -> int:
     """Bytes the projection kernel itself must move: every weight row once
-    (bf16, or E4M3 codes plus one fp32 scale per row) and the hidden rows
-    once (the fold and the d2t map run afterwards)."""
+    (bf16, or E4M3 codes plus one fp32 scale per row), the id list when the
+    rows are read in place from the full head (4 bytes per entry), and the
+    hidden rows once (the fold and the d2t map run afterwards)."""
     w = rows * k + rows * 4 if fp8 else weight_bytes(rows, k)
-    return w + m * k * 2
+    return w + (rows * 4 if indexed else 0) + m * k * 2
 
 
 def source_digest() -> str:
@@ -86,6 +88,11 @@ def describe(a, synth, L):
         rows, copies = c.n, 1
         workload = (f"full-vocab draft step M={m} K={c.k} N={c.n}" if a.config == 2
                     else f"{c.name}: M={m} K={c.k} full head N={c.n}")
+    if a.indexed:
+        if ids is None or a.full or a.fp8:
+            raise SystemExit("bench.py: --indexed needs a shortlist config (1, 3, 4, 5), without --full or --fp8")
+        workload = (f"{c.name}: M={m} K={c.k} {rows} listed rows read in place from the full head "
+                    f"N={c.n} ({copies} rotated copies of W)")
     if a.fp8:
         if trimmed:
             copies = max(1, -(-2 * MALL_BYTES // (rows * c.k)) + 1)
@@ -182,22 +189,27 @@ def record_traffic(a, d, fetch_csv: str, write_csv: str) -> int:
     return 0
 
 
-def cpu_baseline(h_np, w_np, d2t_np, budget_s: float):
-    """The fp64 oracle timed on host cores over whole calls until `budget_s`."""
+def cpu_baseline(h_np, w_np, d2t_np, budget_s: float, indexed: bool = False):
+    """The fp64 oracle timed on host cores over whole calls until `budget_s`
+    (indexed: the oracle reads the listed rows of the full head in place)."""
     import oracle
     from threadpoolctl import threadpool_info
     threads = max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
     calls = 0
     t0 = time.perf_counter()
     while True:
-        oracle.oracle_project_argmax(h_np, w_np, d2t_np)
+        if indexed:
+            oracle.oracle_project_argmax_indexed(h_np, w_np, d2t_np)
+        else:
+            oracle.oracle_project_argmax(h_np, w_np, d2t_np)
         calls += 1
         el = time.perf_counter() - t0
         if el >= budget_s or calls >= 50:
             break
     return {"value": calls / el, "unit": "calls/s", "cores": threads, "kind": "oracle",
-            "sample": f"{calls} whole oracle calls (fp64, M={h_np.shape[0]}, {w_np.shape[0]} rows "
-                      f"x K={w_np.shape[1]}) in {el:.1f} s; numpy + BLAS with {threads} threads"}
+            "sample": f"{calls} whole oracle calls (fp64, M={h_np.shape[0]}, "
+                      f"{d2t_np.size if indexed else w_np.shape[0]} rows x K={w_np.shape[1]}) in {el:.1f} s; "
+                      f"numpy + BLAS with {threads} threads"}
 
 
 def main() -> int:
@@ -219,6 +231,9 @@ def main() -> int:
     ap.add_argument("--fp8", action="store_true",
                     help="quantize the head (or shortlist) to FP8 E4M3 with one scale per row at load "
                          "and time draft_project_argmax_fp8 (no CPU baseline)")
+    ap.add_argument("--indexed", action="store_true",
+                    help="read the shortlist's rows in place from the full head "
+                         "(draft_project_argmax_indexed), rotating copies of W past the Infinity Cache")
     ap.add_argument("--record-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="no GPU: write this workload's entry of profiles/traffic.json from the "
                          "counter_collection.csv files of two rocprofv3 --pmc runs (FETCH_SIZE, "
@@ -255,7 +270,10 @@ def main() -> int:
 
     w_full = torch.from_numpy(w_np.view(np.int16)).to(dev)
     h = torch.from_numpy(h_np.view(np.int16)).to(dev)
-    if trimmed:
+    if a.indexed:
+        d2t = torch.from_numpy(ids.astype(np.int32)).to(dev)
+        heads = [w_full] + [w_full.clone() for _ in range(d["copies"] - 1)]
+    elif trimmed:
         d2t = torch.from_numpy(ids.astype(np.int32)).to(dev)
         heads = [L.lmhead_trim(w_full, d2t) for _ in range(d["copies"])]
         del w_full
@@ -277,7 +295,9 @@ def main() -> int:
     stream = torch.cuda.current_stream(dev)
 
     def step(i):
-        if a.fp8:
+        if a.indexed:
+            L.draft_project_argmax_indexed(h, heads[i % len(heads)], d2t, path, out_id, out_logit, ws, stream)
+        elif a.fp8:
             q, sc = heads[i % len(heads)]
             L.draft_project_argmax_fp8(h, q, sc, d2t, path, out_id, out_logit, ws, stream)
         else:
@@ -302,13 +322,15 @@ def main() -> int:
 
     # The projection kernel alone: as many launches again, back to back on
     # this stream between two HIP events the library records (no fold).
-    if a.fp8:
+    if a.indexed:
+        proj_ms = L.lmhead_bench_time_argmax_indexed(h, heads, d2t, path, a.steps, out_id, out_logit, ws, stream)
+    elif a.fp8:
         proj_ms = L.lmhead_bench_time_argmax_fp8(h, heads, d2t, path, a.steps, out_id, out_logit, ws, stream)
     else:
         proj_ms = L.lmhead_bench_time_argmax(h, heads, d2t, path, a.steps, out_id, out_logit, ws, stream)
-    pbytes = projection_bytes(m, rows, c.k, a.fp8)
+    pbytes = projection_bytes(m, rows, c.k, a.fp8, a.indexed)
     achieved = pbytes / (proj_ms / 1e3) / 1e9
-    abytes = algorithmic_bytes(m, rows, c.k, d2t is not None, a.fp8)
+    abytes = algorithmic_bytes(m, rows, c.k, d2t is not None, a.fp8, a.indexed)
     traffic = measured_traffic(kpath, workload)
     extra = {}
     if a.stream_read:
@@ -352,7 +374,7 @@ def main() -> int:
         "vs_baseline": None,
         "dtype": "e4m3 W x bf16 h, fp32 accumulate" if a.fp8 else "bf16",
         "data": "synthetic (seeded bf16 W ~ N(0, 0.02), h ~ N(0, 1))",
-        "config": {"workload": workload, "M": m, "K": c.k, "rows": rows,
+        "config": {"workload": workload, "M": m, "K": c.k, "rows": rows, "indexed": a.indexed,
                    "kernel": d["kname"], "d2t": d2t is not None, "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS,
                      "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBPS, 4),
@@ -366,8 +388,11 @@ def main() -> int:
     result.update(extra)
     if not a.no_cpu_baseline and not a.fp8:
         hb = h_np
-        wb = w_np[ids] if trimmed else w_np
-        result["cpu_baseline"] = cpu_baseline(hb, wb, ids if trimmed else None, a.cpu_seconds)
+        if a.indexed:
+            result["cpu_baseline"] = cpu_baseline(hb, w_np, ids, a.cpu_seconds, indexed=True)
+        else:
+            wb = w_np[ids] if trimmed else w_np
+            result["cpu_baseline"] = cpu_baseline(hb, wb, ids if trimmed else None, a.cpu_seconds)
     print(json.dumps(result), flush=True)
     return 0
 

@@ -227,6 +227,42 @@ int draft_project_argmax_fp8(const uint16_t* h, int64_t M, int64_t K,
                              int path, void* stream);
 
 /*
+ * draft_project_argmax_indexed -- the shortlisted argmax read straight from
+ * the full head: for each hidden row m, over the list entries i with
+ * ids[i] in [0, N),
+ *     best[m]      = the smallest i maximizing  L[m, i] = sum_k h[m, k] *
+ *                    W[ids[i], k]   (bf16 products, fp32 sums)
+ *     out_id[m]    = ids[best[m]]
+ *     out_logit[m] = L[m, best[m]]
+ * This is exactly draft_project_argmax over lmhead_trim(W, ids) with d2t =
+ * ids, without the trimmed copy: a shortlisted head only picks which head
+ * rows the draft scores, and the d2t map gives their ids ("Two ways to run
+ * it", zone-1.cobraproject.com "Masked MTP drafts").  It serves when the
+ * full head must stay resident anyway (the verifier reads it) and the S x K
+ * copy would be extra memory, or when the list changes often; each listed
+ * row is still one contiguous K x 2-byte read.
+ *
+ *  h          [M, K] bf16 (device, 16-byte aligned), 1 <= M <= LMH_MAX_M.
+ *  W          [N, K] bf16 (device, 16-byte aligned), the full head;
+ *             1 <= N <= 2^31 - 1.
+ *  ids        [S] int32 (device, 4-byte aligned), 1 <= S <= 2^30, any
+ *             order, duplicates allowed.  An entry outside [0, N) is
+ *             skipped (never read); if every entry is skipped, out_id = -1
+ *             and out_logit is NaN.
+ *  out_id, out_logit, workspace: as for draft_project_argmax.
+ *  path       LMH_PATH_AUTO, LMH_PATH_VALU (M <= 8 with M * ceil(K / 512)
+ *             <= 40) or LMH_PATH_MFMA.
+ * Never synchronizes and never allocates.  Errors as for
+ * draft_project_argmax_path.
+ */
+int draft_project_argmax_indexed(const uint16_t* h, int64_t M, int64_t K,
+                                 const uint16_t* W, int64_t N,
+                                 const int32_t* ids, int64_t S,
+                                 int32_t* out_id, float* out_logit,
+                                 void* workspace, size_t workspace_bytes,
+                                 int path, void* stream);
+
+/*
  * lmhead_shortlist_overwrite -- refresh rows of a trimmed head in place:
  * for each entry i, W_trim[rows[i], :] = W[ids[i], :] and d2t[rows[i]] =
  * ids[i].  This is how escaped ids are learned into spare head rows, the
@@ -326,6 +362,19 @@ int lmhead_bench_time_argmax_fp8(const uint16_t* h, int64_t M, int64_t K,
                                  void* workspace, size_t workspace_bytes,
                                  int path, int calls, double* proj_ms,
                                  void* stream);
+
+/*
+ * lmhead_bench_time_argmax_indexed: the same for draft_project_argmax_
+ *   indexed: launch i reads full head heads[i % nheads] ([N, K] each)
+ *   through the one id list `ids`.
+ */
+int lmhead_bench_time_argmax_indexed(const uint16_t* h, int64_t M, int64_t K,
+                                     const uint16_t* const* heads, int nheads,
+                                     int64_t N, const int32_t* ids, int64_t S,
+                                     int32_t* out_id, float* out_logit,
+                                     void* workspace, size_t workspace_bytes,
+                                     int path, int calls, double* proj_ms,
+                                     void* stream);
 
 #ifdef __cplusplus
 }

@@ -169,6 +169,29 @@ def test_fp8_rejects_on_host(L):
     assert f(A, 4, 2560, B, C, 100, None, D, E, E, 8, 0, None) == 3    # workspace
 
 
+def test_indexed_rejects_on_host(L):
+    import ctypes
+    f = L.lib().draft_project_argmax_indexed
+    ws = L.draft_project_workspace_bytes(3)
+    assert f(A, 3, 2560, B, 0, C, 100, D, E, E, ws, 0, None) == 1      # N = 0
+    assert f(A, 3, 2560, B, 1 << 31, C, 100, D, E, E, ws, 0, None) == 1  # N >= 2^31
+    assert f(A, 3, 2560, B, 1000, None, 100, D, E, E, ws, 0, None) == 1  # no ids
+    assert f(A, 3, 2560, B, 1000, C + 2, 100, D, E, E, ws, 0, None) == 1  # ids misaligned
+    assert f(A, 3, 2560, B, 1000, C, 0, D, E, E, ws, 0, None) == 1     # S = 0
+    assert f(A, 3, 2560, B, 1000, C, (1 << 30) + 1, D, E, E, ws, 0, None) == 1
+    assert f(A, 33, 2560, B, 1000, C, 100, D, E, E, ws, 0, None) == 1  # M
+    assert f(A, 3, 2560, B + 8, 1000, C, 100, D, E, E, ws, 0, None) == 1  # W misaligned
+    assert f(A, 9, 2560, B, 1000, C, 100, D, E, E, ws, 1, None) == 1   # VALU takes M <= 8
+    assert f(A, 3, 2560, B, 1000, C, 100, None, E, E, ws, 0, None) == 1  # no output
+    assert f(A, 3, 2560, B, 1000, C, 100, D, E, E, 8, 0, None) == 3    # workspace
+    t = L.lib().lmhead_bench_time_argmax_indexed
+    one = (ctypes.c_void_p * 1)(B)
+    out = ctypes.c_double(0.0)
+    assert t(A, 1, 2560, None, 1, 1000, C, 100, D, E, E, ws, 0, 5, ctypes.byref(out), None) == 1
+    assert t(A, 1, 2560, one, 1, 1000, None, 100, D, E, E, ws, 0, 5, ctypes.byref(out), None) == 1
+    assert t(A, 1, 2560, one, 1, 1000, C, 100, D, E, E, ws, 0, 0, ctypes.byref(out), None) == 1
+
+
 def test_shortlist_ops_reject_on_host(L):
     lib = L.lib()
     f = lib.lmhead_shortlist_overwrite

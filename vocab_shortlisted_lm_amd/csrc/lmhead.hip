@@ -78,6 +78,9 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 #define LMH_MFMA_RING 3          // batches in the register ring of the coalesced matrix-core kernel
 #endif
 
+#ifndef LMH_UNCOND_ISSUE
+#define LMH_UNCOND_ISSUE 0       // VALU kernels issue the next loads unconditionally (zero-record past the end)
+#endif
 #ifndef LMH_VALU_WAVES
 #define LMH_VALU_WAVES 4          // waves per workgroup (VALU path)
 #endif
@@ -403,13 +406,33 @@ __device__ __forceinline__ void publish_workgroup(unsigned long long key, int la
 //                     slots[(hidden row * kMaxGrid + workgroup) * TK + j].
 //   LOGITS:           write the logit to logits[hidden row * ld + col], col
 //                     = d2t[row] (skipped unless 0 <= col < ncols) or row.
+//
+// Indexed kernels (template flag IDX) also read the head through a row map:
+// head row r of the projection is row rowmap[r] of W, which has nw rows; a
+// row whose id lies outside [0, nw) is never read and takes no part in the
+// result.
 struct Epi {
   unsigned long long* slots;
   float* logits;
   const int32_t* d2t;
   int64_t ld;
   int64_t ncols;
+  const int32_t* rowmap = nullptr;
+  int nw = 0;
 };
+
+// Id of list entry r for an indexed kernel, as a plain (unconditional)
+// buffer load; entries past the list (r >= R) read 0, so the caller checks
+// r < R where it uses the id.  Nothing may consume the value right after
+// the load: the wait would then cover every load in flight.
+__device__ __forceinline__ int load_row_id(const int32_t* rowmap, int R, int r) {
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(rowmap, (uint32_t)R * 4u);
+  const uint32_t off = r < R ? (uint32_t)r * 4u : kOobOffset;
+  return __builtin_amdgcn_raw_buffer_load_b32(rs, (int)off, 0, 0);
+}
+
+// List entry r (< R) with id `id` takes part if the id is a row of W.
+__device__ __forceinline__ bool row_id_ok(int id, int nw) { return id >= 0 && id < nw; }
 
 __device__ __forceinline__ void store_logit(const Epi& e, int m, int r, float v) {
   int64_t col = r;
@@ -768,9 +791,16 @@ struct ValuEpilogue {
 // Lane `l` owns the 16-byte chunks c = l + 64 j (j < CPL) of every row, so
 // one load instruction moves 1 KiB of a row, fully coalesced.  Chunks past
 // the row end get an out-of-range buffer offset and read as zero.
-template <int M, int CPL, int U, int WV, int TK, bool LOGITS>
+//
+// IDX: row r is row epi.rowmap[r] of W.  The ids of the rows two steps
+// ahead are fetched with a vector load (lane u < U: row u of that step)
+// when a step's rows are issued, so they have arrived (loads complete in
+// order) by the time their own rows are issued; a row whose id is outside
+// [0, nw) reads nothing and is left out.
+template <int M, int CPL, int U, int WV, int TK, bool LOGITS, bool IDX = false>
 __global__ void __launch_bounds__(64 * WV)
 proj_valu_rows(const uint16_t* __restrict__ h, const uint16_t* __restrict__ W, int R, int K, Epi epi) {
+  static_assert(!IDX || (TK == 1 && !LOGITS && U <= 64), "indexed rows: argmax epilogue");
   const int lane = threadIdx.x & 63;
   const int wave = wave_id();
   const int chunks = K >> 3;
@@ -795,17 +825,34 @@ proj_valu_rows(const uint16_t* __restrict__ h, const uint16_t* __restrict__ W, i
   const int step = gridDim.x * WV * U;
   u32x4 wa[U][CPL], wb[U][CPL];
 
-  auto load_rows = [&](u32x4 (&w)[U][CPL], int r0) {
+  // IDX: ids of the rows of the next two steps, one per lane u < U.
+  int vid1 = -1, vid2 = -1;
+  auto fetch_ids = [&](int r0) { return load_row_id(epi.rowmap, R, r0 + (lane < U ? lane : 0)); };
+
+  // `live` gets bit u for each row that takes part.
+  auto load_rows = [&](u32x4 (&w)[U][CPL], int& live, int r0) {
+    int bits = 0;
+    int rid[U];
+    if constexpr (IDX) {
+#pragma unroll
+      for (int u = 0; u < U; ++u) rid[u] = __builtin_amdgcn_readlane(vid1, u);
+      vid1 = vid2;
+      vid2 = fetch_ids(r0 + 2 * step);
+    }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int r = r0 + u;
+      const bool ok = r < R && (!IDX || row_id_ok(rid[u], epi.nw));
+      const int src = IDX ? rid[u] : r;
+      bits |= ok ? (1 << u) : 0;
       const __amdgpu_buffer_rsrc_t rs =
-          make_rsrc(W + (size_t)(r < R ? r : 0) * (size_t)K, r < R ? row_bytes : 0u);
+          make_rsrc(W + (size_t)(ok ? src : 0) * (size_t)K, ok ? row_bytes : 0u);
 #pragma unroll
       for (int j = 0; j < CPL; ++j) w[u][j] = load16(rs, voff[j]);
     }
+    live = bits;
   };
-  auto score_rows = [&](const u32x4 (&w)[U][CPL], int r0) {
+  auto score_rows = [&](const u32x4 (&w)[U][CPL], int live, int r0) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       float sum[M];
@@ -816,28 +863,35 @@ proj_valu_rows(const uint16_t* __restrict__ h, const uint16_t* __restrict__ W, i
         for (int j = 0; j < CPL; ++j) acc = dot8(w[u][j], hf[m][j], acc);
         sum[m] = wave_sum(acc);
       }
-      if (r0 + u < R) ep.row(sum, r0 + u, lane, epi);
+      if (r0 + u < R && (!IDX || ((live >> u) & 1))) ep.row(sum, r0 + u, lane, epi);
     }
   };
 
   int r0 = (blockIdx.x * WV + wave) * U;
+  int la = 0, lb = 0;
+  if constexpr (IDX) {
+    vid1 = fetch_ids(r0);
+    vid2 = fetch_ids(r0 + step);
+  }
   if constexpr (LMH_VALU_PREFETCH) {
     // Two register buffers: the next rows are in flight while these are scored.
-    if (r0 < R) load_rows(wa, r0);
+    // Rows past R get descriptors with no records: their loads read zero
+    // without touching memory, so the loads may be issued unconditionally.
+    if (LMH_UNCOND_ISSUE || r0 < R) load_rows(wa, la, r0);
     while (r0 < R) {
       const int r1 = r0 + step;
-      if (r1 < R) load_rows(wb, r1);
-      score_rows(wa, r0);
+      if (LMH_UNCOND_ISSUE || r1 < R) load_rows(wb, lb, r1);
+      score_rows(wa, la, r0);
       if (r1 >= R) break;
       const int r2 = r1 + step;
-      if (r2 < R) load_rows(wa, r2);
-      score_rows(wb, r1);
+      if (LMH_UNCOND_ISSUE || r2 < R) load_rows(wa, la, r2);
+      score_rows(wb, lb, r1);
       r0 = r2;
     }
   } else {
     for (; r0 < R; r0 += step) {
-      load_rows(wa, r0);
-      score_rows(wa, r0);
+      load_rows(wa, la, r0);
+      score_rows(wa, la, r0);
     }
   }
 
@@ -851,9 +905,16 @@ proj_valu_rows(const uint16_t* __restrict__ h, const uint16_t* __restrict__ W, i
 // flight while this one is scored.  Hidden rows live in LDS, zero-padded to
 // whole stripes, so the batch loop is a plain runtime loop.  The epilogue
 // (argmax, top-TK or every logit) is chosen by TK and LOGITS.
-template <int M, int TR, int WV, int TK, bool LOGITS>
+//
+// IDX: the tile's rows are list entries; row q of a tile is row
+// epi.rowmap[tile * TR + q] of W, each with its own descriptor.  The ids of
+// the wave's next tile are fetched with a vector load when a tile starts,
+// so they have long arrived (loads complete in order) when that tile starts;
+// a row with an id outside [0, nw) reads nothing and is left out.
+template <int M, int TR, int WV, int TK, bool LOGITS, bool IDX = false>
 __global__ void __launch_bounds__(64 * WV)
 proj_valu_tiled(const uint16_t* __restrict__ h, const uint16_t* __restrict__ W, int R, int K, Epi epi) {
+  static_assert(!IDX || (TK == 1 && !LOGITS && TR <= 64), "indexed rows: argmax epilogue");
   extern __shared__ u32x4 h_stripes[];  // [M][nb * 64] chunks, zero past K
   const int lane = threadIdx.x & 63;
   const int wave = wave_id();
@@ -882,18 +943,48 @@ proj_valu_tiled(const uint16_t* __restrict__ h, const uint16_t* __restrict__ W, 
   const int ntiles = (R + TR - 1) / TR;
   const int tstride = gridDim.x * WV;
 
+  // IDX: ids of the rows being issued (wave-uniform) and, in lane q < TR,
+  // the id of row q of the wave's next tile.
+  int rid[IDX ? TR : 1];
+  int vnext = -1;
+  auto fetch_next_ids = [&](int tile) {
+    vnext = load_row_id(epi.rowmap, R, tile * TR + (lane < TR ? lane : 0));
+  };
+
   // One descriptor per tile covering its live rows: offsets of rows past R
-  // (and of chunks past K) are >= num_records and read as zero.
-  auto issue = [&](u32x4 (&w)[TR], int tile, int j) {
+  // (and of chunks past K) are >= num_records and read as zero.  IDX: one
+  // descriptor per row; `live` gets bit q for each row that takes part.
+  auto issue = [&](u32x4 (&w)[TR], int& live, int tile, int j) {
     const int c = lane + 64 * j;
     const int r0 = tile * TR;
-    const int live = min(TR, R - r0);
-    const __amdgpu_buffer_rsrc_t rs = make_rsrc(W + (size_t)r0 * (size_t)K, (uint32_t)live * row_bytes);
     const uint32_t off = c < chunks ? (uint32_t)c * 16u : kOobOffset;
+    if constexpr (IDX) {
+      if (j == 0) {
 #pragma unroll
-    for (int q = 0; q < TR; ++q) w[q] = load16(rs, off + (uint32_t)q * row_bytes);
+        for (int q = 0; q < TR; ++q) rid[q] = __builtin_amdgcn_readlane(vnext, q);
+        fetch_next_ids(tile + tstride);
+      }
+      int bits = 0;
+#pragma unroll
+      for (int q = 0; q < TR; ++q) {
+        const bool ok = r0 + q < R && row_id_ok(rid[q], epi.nw);
+        bits |= ok ? (1 << q) : 0;
+        const __amdgpu_buffer_rsrc_t rs =
+            make_rsrc(W + (size_t)(ok ? rid[q] : 0) * (size_t)K, ok ? row_bytes : 0u);
+        w[q] = load16(rs, off);
+      }
+      live = bits;
+    } else {
+      // past the last tile (unconditional issue) the descriptor has no records
+      const int nlive = LMH_UNCOND_ISSUE ? __builtin_amdgcn_readfirstlane(max(0, min(TR, R - r0))) : min(TR, R - r0);
+      const int rbase = LMH_UNCOND_ISSUE ? __builtin_amdgcn_readfirstlane(nlive == 0 ? 0 : r0) : r0;
+      const __amdgpu_buffer_rsrc_t rs = make_rsrc(W + (size_t)rbase * (size_t)K, (uint32_t)nlive * row_bytes);
+#pragma unroll
+      for (int q = 0; q < TR; ++q) w[q] = load16(rs, off + (uint32_t)q * row_bytes);
+      live = (1 << TR) - 1;
+    }
   };
-  auto consume = [&](const u32x4 (&w)[TR], int tile, int j) {
+  auto consume = [&](const u32x4 (&w)[TR], int live, int tile, int j) {
 #pragma unroll
     for (int m = 0; m < M; ++m) {
       const u32x4 hv = h_stripes[m * hc + j * 64 + lane];
@@ -910,7 +1001,7 @@ proj_valu_tiled(const uint16_t* __restrict__ h, const uint16_t* __restrict__ W, 
           sum[m] = wave_sum(acc[q][m]);
           acc[q][m] = 0.0f;
         }
-        if (r0 + q < R) ep.row(sum, r0 + q, lane, epi);
+        if (r0 + q < R && (!IDX || ((live >> q) & 1))) ep.row(sum, r0 + q, lane, epi);
       }
     }
   };
@@ -924,21 +1015,23 @@ proj_valu_tiled(const uint16_t* __restrict__ h, const uint16_t* __restrict__ W, 
   int tile = blockIdx.x * WV + wave;
   int j = 0;
   u32x4 wa[TR], wb[TR];
+  int la = 0, lb = 0;
   if (tile < ntiles) {
-    issue(wa, tile, 0);
+    if constexpr (IDX) fetch_next_ids(tile);
+    issue(wa, la, tile, 0);
     while (true) {
       int t1 = tile, j1 = j;
       advance(t1, j1);
       bool more = t1 < ntiles;
-      if (more) issue(wb, t1, j1);
-      consume(wa, tile, j);
+      if (LMH_UNCOND_ISSUE || more) issue(wb, lb, t1, j1);
+      consume(wa, la, tile, j);
       if (!more) break;
       tile = t1;
       j = j1;
       advance(t1, j1);
       more = t1 < ntiles;
-      if (more) issue(wa, t1, j1);
-      consume(wb, tile, j);
+      if (LMH_UNCOND_ISSUE || more) issue(wa, la, t1, j1);
+      consume(wb, lb, tile, j);
       if (!more) break;
       tile = t1;
       j = j1;
@@ -1080,10 +1173,19 @@ proj_valu_fp8(const uint16_t* __restrict__ h, const uint8_t* __restrict__ W, con
 // stage, and reads the A operands back in MFMA layout.  Hidden rows are in
 // LDS as in proj_argmax_mfma.  The stage is private to the wave, so the
 // exchange needs only wave-level ordering, not a workgroup barrier.
-template <int NT, int SB, int WV, int D, int TK, bool LOGITS, bool FP8>
+//
+// IDX: the tile's 16 rows are list entries; row i of a tile is row
+// epi.rowmap[tile * 16 + i] of W.  The 16 ids of the wave's next tile are
+// read with scalar loads when a tile starts (one tile ahead), each lane
+// forms 64-bit addresses of its rows, and the loads are plain global loads
+// (past the row end, or for a row whose id is outside [0, nw), they read
+// row 0 and the values are dropped).  A 16-bit mask of the rows that take
+// part travels with the tile in a short history until the tile finishes.
+template <int NT, int SB, int WV, int D, int TK, bool LOGITS, bool FP8, bool IDX = false>
 __global__ void __launch_bounds__(64 * WV)
 proj_mfma(const uint16_t* __restrict__ h, const void* __restrict__ Wv, const float* __restrict__ wscale, int R,
           int K, int m_base, int mp, Epi epi) {
+  static_assert(!IDX || (TK == 1 && !LOGITS && !FP8), "indexed rows: bf16 argmax epilogue");
   // A k-step is 32 head-row elements: four 16-byte chunks of bf16, or two of
   // E4M3 codes (FP8: codes become bf16 when read from the stage, and a
   // row's sum is multiplied by its fp32 scale).
@@ -1171,9 +1273,62 @@ proj_mfma(const uint16_t* __restrict__ h, const void* __restrict__ Wv, const flo
     }
   };
 
+  // IDX state: ids of the tile being issued (snext holds the next tile's,
+  // fetched one tile ahead), this lane's row addresses in it, and the
+  // masks of rows that take part in the last few tiles issued (16 bits per
+  // tile, newest lowest; `pushed` is the newest tile's index).
+  int snext[IDX ? 16 : 1];
+  const uint8_t* vrow[IDX ? LPB : 1];
+  unsigned long long hist = 0ull;
+  int pushed = 0;
+  auto fetch_tile_ids = [&](int tile) {
+    if constexpr (IDX) {
+      const int r0 = tile * 16;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) snext[i] = epi.rowmap[min(r0 + i, R - 1)];  // checked against R when used
+    }
+  };
+  auto start_issue_tile = [&](int tile) {
+    if constexpr (IDX) {
+      int scur[16];
+      uint32_t mask = 0u;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const bool ok = tile * 16 + i < R && row_id_ok(snext[i], epi.nw);
+        scur[i] = ok ? snext[i] : -1;
+        mask |= ok ? (1u << i) : 0u;
+      }
+#pragma unroll
+      for (int q = 0; q < LPB; ++q) {
+        int id = scur[q * RPI];
+#pragma unroll
+        for (int l = 1; l < RPI; ++l) id = lrow == l ? scur[q * RPI + l] : id;
+        vrow[q] = W + (size_t)(row_id_ok(id, epi.nw) ? id : 0) * row_bytes;
+      }
+      hist = (hist << 16) | mask;
+      pushed = tile;
+      fetch_tile_ids(tile + tstride);
+    }
+  };
+  // Rows of tile `tile` (issued at most three tiles ago) that take part,
+  // bit i for row i of the tile.
+  auto tile_mask = [&](int tile) -> uint32_t {
+    const int d = (pushed - tile) / tstride;
+    return (uint32_t)(hist >> (16 * d)) & 0xFFFFu;
+  };
+
   // Positions past the last tile get a descriptor with no records, so their
   // loads read zero without touching memory (live is clamped at 0).
   auto issue = [&](u32x4 (&buf)[LPB], int tile, int b) {
+    if constexpr (IDX) {
+      if (b == 0) start_issue_tile(tile);
+      const int cg = b * BC + lc;
+      const size_t coff = (size_t)(cg < wchunks ? cg : 0) * 16u;
+#pragma unroll
+      for (int q = 0; q < LPB; ++q)
+        buf[q] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vrow[q] + coff));
+      return;
+    }
     const int r0 = tile < ntiles ? tile * 16 : 0;
     const int live = tile < ntiles ? min(16, R - r0) : 0;
     const __amdgpu_buffer_rsrc_t rs = make_rsrc(W + (size_t)r0 * row_bytes, (uint32_t)live * row_bytes);
@@ -1203,8 +1358,10 @@ proj_mfma(const uint16_t* __restrict__ h, const void* __restrict__ Wv, const flo
     }
   };
   auto consume = [&](const u32x4 (&buf)[LPB], int b) {
+    // IDX: chunks past the row end were loaded from column 0; zero them
+    const bool in_row = !IDX || b * BC + lc < wchunks;
 #pragma unroll
-    for (int q = 0; q < LPB; ++q) stage[(q * RPI + lrow) * SC + lc] = buf[q];
+    for (int q = 0; q < LPB; ++q) stage[(q * RPI + lrow) * SC + lc] = in_row ? buf[q] : u32x4{0u, 0u, 0u, 0u};
     // lanes of this wave exchange data through the stage
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
@@ -1258,10 +1415,11 @@ proj_mfma(const uint16_t* __restrict__ h, const void* __restrict__ Wv, const flo
       }
       return;
     }
+    const uint32_t live = IDX ? tile_mask(tile) >> (4 * g) : 0xFu;
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
       const int r = r0 + 4 * g + v;
-      if (r < R) {
+      if (r < R && ((live >> v) & 1u)) {
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
           if constexpr (LOGITS) {
@@ -1307,6 +1465,7 @@ proj_mfma(const uint16_t* __restrict__ h, const void* __restrict__ Wv, const flo
   const int count = my_tiles * nbatch;
   u32x4 ring[D][LPB];
   load_scales(ti);
+  fetch_tile_ids(ti);
 #pragma unroll
   for (int j = 0; j < D - 1; ++j) {
     issue(ring[j], ti, bi);
@@ -1487,54 +1646,54 @@ struct ValuPlan {
   size_t lds = 0;
 };
 
-template <int M, int CPL, int WV, int TK, bool LOGITS>
+template <int M, int CPL, int WV, int TK, bool LOGITS, bool IDX>
 void row_plan(ValuPlan& p) {
   if constexpr (M * CPL <= kValuMaxChunksTimesM) {
     // rows per step: keep each of the two row buffers at <= 10 chunks/lane,
     // and one row per step once h alone takes more than 80 registers
     constexpr int U0 = M * CPL > 20 ? 1 : (CPL * LMH_VALU_ROWS <= 10 ? LMH_VALU_ROWS : (CPL <= 10 ? 10 / CPL : 1));
     constexpr int U = U0 < 1 ? 1 : U0;
-    p.fn = proj_valu_rows<M, CPL, U, WV, TK, LOGITS>;
+    p.fn = proj_valu_rows<M, CPL, U, WV, TK, LOGITS, IDX>;
     p.waves = WV;
     p.rows_per_wave = U;
     p.lds = 0;
   }
 }
 
-template <int M, int TK, bool LOGITS, int... C>
+template <int M, int TK, bool LOGITS, bool IDX, int... C>
 void row_plan_cpl(ValuPlan& p, int cpl, std::integer_sequence<int, C...>) {
   constexpr int WV = M <= 4 ? LMH_VALU_WAVES : 2 * LMH_VALU_WAVES;
-  ((cpl == C + 1 ? (row_plan<M, C + 1, WV, TK, LOGITS>(p), 0) : 0), ...);
+  ((cpl == C + 1 ? (row_plan<M, C + 1, WV, TK, LOGITS, IDX>(p), 0) : 0), ...);
 }
 
-template <int M, int TK, bool LOGITS>
+template <int M, int TK, bool LOGITS, bool IDX>
 ValuPlan tiled_plan(int K) {
   ValuPlan p;
-  p.fn = proj_valu_tiled<M, LMH_VALU_TILE_ROWS, LMH_VALU_WAVES, TK, LOGITS>;
+  p.fn = proj_valu_tiled<M, LMH_VALU_TILE_ROWS, LMH_VALU_WAVES, TK, LOGITS, IDX>;
   p.waves = LMH_VALU_WAVES;
   p.rows_per_wave = LMH_VALU_TILE_ROWS;
   p.lds = (size_t)M * chunks_per_lane(K) * 64 * 16;
   return p;
 }
 
-template <int TK, bool LOGITS>
+template <int TK, bool LOGITS, bool IDX = false>
 ValuPlan valu_plan(int M, int K) {
   ValuPlan p;
-  if (M == 1 && LMH_VALU_TILE_ROWS > 0) return tiled_plan<1, TK, LOGITS>(K);
+  if (M == 1 && LMH_VALU_TILE_ROWS > 0) return tiled_plan<1, TK, LOGITS, IDX>(K);
   const int cpl = chunks_per_lane(K);
   using seq = std::make_integer_sequence<int, 16>;
   switch (M) {
-    case 1: row_plan_cpl<1, TK, LOGITS>(p, cpl, seq{}); break;
-    case 2: row_plan_cpl<2, TK, LOGITS>(p, cpl, seq{}); break;
-    case 3: row_plan_cpl<3, TK, LOGITS>(p, cpl, seq{}); break;
-    case 4: row_plan_cpl<4, TK, LOGITS>(p, cpl, seq{}); break;
+    case 1: row_plan_cpl<1, TK, LOGITS, IDX>(p, cpl, seq{}); break;
+    case 2: row_plan_cpl<2, TK, LOGITS, IDX>(p, cpl, seq{}); break;
+    case 3: row_plan_cpl<3, TK, LOGITS, IDX>(p, cpl, seq{}); break;
+    case 4: row_plan_cpl<4, TK, LOGITS, IDX>(p, cpl, seq{}); break;
     default:
       if constexpr (TK == 1 && !LOGITS) {
         switch (M) {
-          case 5: row_plan_cpl<5, 1, false>(p, cpl, seq{}); break;
-          case 6: row_plan_cpl<6, 1, false>(p, cpl, seq{}); break;
-          case 7: row_plan_cpl<7, 1, false>(p, cpl, seq{}); break;
-          case 8: row_plan_cpl<8, 1, false>(p, cpl, seq{}); break;
+          case 5: row_plan_cpl<5, 1, false, IDX>(p, cpl, seq{}); break;
+          case 6: row_plan_cpl<6, 1, false, IDX>(p, cpl, seq{}); break;
+          case 7: row_plan_cpl<7, 1, false, IDX>(p, cpl, seq{}); break;
+          case 8: row_plan_cpl<8, 1, false, IDX>(p, cpl, seq{}); break;
           default: break;
         }
       }
@@ -1598,7 +1757,7 @@ int mfma_lds_rows_fit(int64_t K, int waves) {
 // else 4; two 16-column tiles when mp > 16.
 // FP8 heads take twice the k-steps per batch, so a batch moves the same
 // bytes (and the stage has the same size) as for bf16.
-template <int TK, bool LOGITS, bool FP8>
+template <int TK, bool LOGITS, bool FP8, bool IDX = false>
 int launch_mfma_pass(const uint16_t* h, int K, int m_base, int mp, const void* W, const float* wscale, int R,
                      const Epi& epi, int cus, hipStream_t stream, int* grid_out) {
   constexpr int SB = FP8 ? 2 * LMH_MFMA_LDS_SB : LMH_MFMA_LDS_SB;
@@ -1609,13 +1768,13 @@ int launch_mfma_pass(const uint16_t* h, int K, int m_base, int mp, const void* W
   const size_t lds = hbytes + (size_t)(eight ? 8 : 4) * 16 * (4 * LMH_MFMA_LDS_SB + 1) * 16;
   const char* what = "launch matrix-core projection";
   if (mp <= 16)
-    return eight ? launch_persistent(proj_mfma<1, SB, 8, D, TK, LOGITS, FP8>, 512, lds, tiles, 8, 1 << 20, cus,
+    return eight ? launch_persistent(proj_mfma<1, SB, 8, D, TK, LOGITS, FP8, IDX>, 512, lds, tiles, 8, 1 << 20, cus,
                                      stream, what, grid_out, h, W, wscale, R, K, m_base, mp, epi)
-                 : launch_persistent(proj_mfma<1, SB, 4, D, TK, LOGITS, FP8>, 256, lds, tiles, 4, 1 << 20, cus,
+                 : launch_persistent(proj_mfma<1, SB, 4, D, TK, LOGITS, FP8, IDX>, 256, lds, tiles, 4, 1 << 20, cus,
                                      stream, what, grid_out, h, W, wscale, R, K, m_base, mp, epi);
-  return eight ? launch_persistent(proj_mfma<2, SB, 8, D, TK, LOGITS, FP8>, 512, lds, tiles, 8, 1 << 20, cus,
+  return eight ? launch_persistent(proj_mfma<2, SB, 8, D, TK, LOGITS, FP8, IDX>, 512, lds, tiles, 8, 1 << 20, cus,
                                    stream, what, grid_out, h, W, wscale, R, K, m_base, mp, epi)
-               : launch_persistent(proj_mfma<2, SB, 4, D, TK, LOGITS, FP8>, 256, lds, tiles, 4, 1 << 20, cus,
+               : launch_persistent(proj_mfma<2, SB, 4, D, TK, LOGITS, FP8, IDX>, 256, lds, tiles, 4, 1 << 20, cus,
                                    stream, what, grid_out, h, W, wscale, R, K, m_base, mp, epi);
 }
 
@@ -1670,6 +1829,7 @@ struct Call {
   hipStream_t stream;
   bool projection_only = false;  // measurement: skip the fold (outputs untouched)
   const float* wscale = nullptr;
+  bool indexed = false;          // W is the whole head, read through epi.rowmap (argmax only)
 };
 
 int record(hipEvent_t e, hipStream_t s) {
@@ -1696,13 +1856,17 @@ int run(const Call& c, const Epi& epi, int topk, int32_t* out_id, float* out_log
   };
   const bool fp8 = c.wscale != nullptr;
   if (fp8 && MODE != 0) return LMH_EINVAL;
+  constexpr bool kIdxOk = MODE == 0 && TK == 1;
+  if (c.indexed && (!kIdxOk || fp8 || !epi.rowmap)) return LMH_EINVAL;
   if (c.path == LMH_PATH_VALU) {
     int grid = 0;
     if (fp8) {
       st = launch_valu_fp8(c.h, c.M, c.K, static_cast<const uint8_t*>(c.W), c.wscale, c.R, epi, cus, c.stream,
                            &grid);
     } else {
-      const ValuPlan p = valu_plan<TK, LOGITS>(c.M, c.K);
+      ValuPlan p;
+      if constexpr (kIdxOk) p = c.indexed ? valu_plan<TK, LOGITS, true>(c.M, c.K) : valu_plan<TK, LOGITS>(c.M, c.K);
+      else p = valu_plan<TK, LOGITS>(c.M, c.K);
       if (!p.fn) return LMH_EINVAL;
       st = launch_valu(p, c.h, c.K, static_cast<const uint16_t*>(c.W), c.R, epi, cus, c.stream, &grid);
     }
@@ -1716,7 +1880,14 @@ int run(const Call& c, const Epi& epi, int topk, int32_t* out_id, float* out_log
   for (int m0 = 0; m0 < c.M; m0 += per) {
     const int mp = std::min(per, c.M - m0);
     int grid = 0;
-    if constexpr (MODE == 0) {
+    if constexpr (kIdxOk) {
+      st = fp8 ? launch_mfma_pass<TK, LOGITS, true>(c.h, c.K, m0, mp, c.W, c.wscale, c.R, epi, cus, c.stream, &grid)
+           : c.indexed
+               ? launch_mfma_pass<TK, LOGITS, false, true>(c.h, c.K, m0, mp, c.W, nullptr, c.R, epi, cus, c.stream,
+                                                           &grid)
+               : launch_mfma_pass<TK, LOGITS, false>(c.h, c.K, m0, mp, c.W, nullptr, c.R, epi, cus, c.stream,
+                                                     &grid);
+    } else if constexpr (MODE == 0) {
       st = fp8 ? launch_mfma_pass<TK, LOGITS, true>(c.h, c.K, m0, mp, c.W, c.wscale, c.R, epi, cus, c.stream, &grid)
                : launch_mfma_pass<TK, LOGITS, false>(c.h, c.K, m0, mp, c.W, nullptr, c.R, epi, cus, c.stream,
                                                      &grid);
@@ -1871,6 +2042,23 @@ int draft_project_argmax(const uint16_t* h, int64_t M, int64_t K, const uint16_t
                          size_t workspace_bytes, void* stream) {
   return draft_project_argmax_path(h, M, K, W, R, d2t, out_id, out_logit, workspace, workspace_bytes,
                                    LMH_PATH_AUTO, stream);
+}
+
+int draft_project_argmax_indexed(const uint16_t* h, int64_t M, int64_t K, const uint16_t* W, int64_t N,
+                                 const int32_t* ids, int64_t S, int32_t* out_id, float* out_logit, void* workspace,
+                                 size_t workspace_bytes, int path, void* stream) {
+  int st = check_common(h, M, K, W, S, 0, &path);
+  if (st != LMH_OK) return st;
+  if (N < 1 || N > (int64_t)0x7FFFFFFF || !ids || (reinterpret_cast<uintptr_t>(ids) & 3u) != 0) return LMH_EINVAL;
+  if (!out_id || !out_logit) return LMH_EINVAL;
+  if (!workspace || !aligned16(workspace)) return LMH_EWORKSPACE;
+  if (workspace_bytes < draft_project_workspace_bytes(M)) return LMH_EWORKSPACE;
+  Call c{h, (int)M, (int)K, W, (int)S, ids, path, static_cast<hipStream_t>(stream)};
+  c.indexed = true;
+  Epi epi{static_cast<unsigned long long*>(workspace), nullptr, nullptr, 0, 0};
+  epi.rowmap = ids;
+  epi.nw = (int)N;
+  return run<0, 1>(c, epi, 1, out_id, out_logit);
 }
 
 size_t draft_project_topk_workspace_bytes(int64_t M, int64_t topk) {
@@ -2049,6 +2237,30 @@ int lmhead_bench_time_argmax_fp8(const uint16_t* h, int64_t M, int64_t K, const 
   c.wscale = scales[0];
   const Epi epi{static_cast<unsigned long long*>(workspace), nullptr, nullptr, 0, 0};
   return time_projection(c, nheads, reinterpret_cast<const void* const*>(heads), scales, epi, out_id, out_logit,
+                         calls, proj_ms);
+}
+
+int lmhead_bench_time_argmax_indexed(const uint16_t* h, int64_t M, int64_t K, const uint16_t* const* heads,
+                                     int nheads, int64_t N, const int32_t* ids, int64_t S, int32_t* out_id,
+                                     float* out_logit, void* workspace, size_t workspace_bytes, int path, int calls,
+                                     double* proj_ms, void* stream) {
+  if (!heads || nheads < 1 || calls < 1 || !proj_ms) return LMH_EINVAL;
+  const int path_in = path;
+  int st = LMH_OK;
+  for (int i = 0; i < nheads; ++i) {
+    path = path_in;
+    if ((st = check_common(h, M, K, heads[i], S, 0, &path)) != LMH_OK) return st;
+  }
+  if (N < 1 || N > (int64_t)0x7FFFFFFF || !ids || (reinterpret_cast<uintptr_t>(ids) & 3u) != 0) return LMH_EINVAL;
+  if (!out_id || !out_logit) return LMH_EINVAL;
+  if (!workspace || !aligned16(workspace)) return LMH_EWORKSPACE;
+  if (workspace_bytes < draft_project_workspace_bytes(M)) return LMH_EWORKSPACE;
+  Call c{h, (int)M, (int)K, heads[0], (int)S, ids, path, static_cast<hipStream_t>(stream)};
+  c.indexed = true;
+  Epi epi{static_cast<unsigned long long*>(workspace), nullptr, nullptr, 0, 0};
+  epi.rowmap = ids;
+  epi.nw = (int)N;
+  return time_projection(c, nheads, reinterpret_cast<const void* const*>(heads), nullptr, epi, out_id, out_logit,
                          calls, proj_ms);
 }
 

@@ -24,7 +24,8 @@ __all__ = [
     "draft_project_topk_workspace_bytes", "draft_project_topk", "draft_project_logits",
     "lmhead_bench_time_argmax", "lmhead_quantize_fp8", "draft_project_argmax_fp8",
     "lmhead_bench_time_argmax_fp8", "lmhead_shortlist_overwrite", "lmhead_shortlist_union",
-    "LMH_MAX_OVERWRITE", "LMH_MAX_UNION_VOCAB",
+    "LMH_MAX_OVERWRITE", "LMH_MAX_UNION_VOCAB", "draft_project_argmax_indexed",
+    "lmhead_bench_time_argmax_indexed",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "liblmhead.so")
@@ -62,6 +63,9 @@ SIGNATURES = {
     "draft_project_argmax_fp8": (_INT, [_P, _I64, _I64, _P, _P, _I64, _P, _P, _P, _P, _SZ, _INT, _P]),
     "lmhead_bench_time_argmax_fp8": (_INT, [_P, _I64, _I64, _P, _P, _INT, _I64, _P, _P, _P, _P, _SZ, _INT, _INT,
                                             ctypes.POINTER(ctypes.c_double), _P]),
+    "draft_project_argmax_indexed": (_INT, [_P, _I64, _I64, _P, _I64, _P, _I64, _P, _P, _P, _SZ, _INT, _P]),
+    "lmhead_bench_time_argmax_indexed": (_INT, [_P, _I64, _I64, _P, _INT, _I64, _P, _I64, _P, _P, _P, _SZ, _INT,
+                                                _INT, ctypes.POINTER(ctypes.c_double), _P]),
 }
 
 _lib = None
@@ -452,3 +456,58 @@ def lmhead_shortlist_union(a: torch.Tensor, b: torch.Tensor, n_vocab: int, out: 
                                         out.shape[0], counts.data_ptr(), _stream(stream, a.device)),
            "lmhead_shortlist_union")
     return out, counts
+
+
+def draft_project_argmax_indexed(h: torch.Tensor, W: torch.Tensor, ids: torch.Tensor,
+                                 path: int = LMH_PATH_AUTO, out_id: torch.Tensor | None = None,
+                                 out_logit: torch.Tensor | None = None,
+                                 workspace: torch.Tensor | None = None, stream=None):
+    """(out_id int32 [M], out_logit float32 [M]): the best listed row per
+    hidden row, reading rows W[ids[i]] of the full head in place (no trimmed
+    copy); out_id is the winning entry's id.  Entries outside [0, N) are
+    skipped.  Never synchronizes."""
+    _dev_tensor(h, "h", _BF16_LIKE, 2)
+    _dev_tensor(W, "W", _BF16_LIKE, 2)
+    _dev_tensor(ids, "ids", (torch.int32,), 1)
+    m, k = h.shape
+    n, k2 = W.shape
+    if k != k2:
+        raise ValueError("h and W must have the same K")
+    if out_id is None:
+        out_id = torch.empty(m, dtype=torch.int32, device=h.device)
+    if out_logit is None:
+        out_logit = torch.empty(m, dtype=torch.float32, device=h.device)
+    _dev_tensor(out_id, "out_id", (torch.int32,), 1)
+    _dev_tensor(out_logit, "out_logit", (torch.float32,), 1)
+    if out_id.shape[0] < m or out_logit.shape[0] < m:
+        raise ValueError("outputs must hold M entries")
+    st = _stream(stream, h.device)
+    if workspace is None:
+        workspace = _default_workspace(h.device, st)
+    _check(lib().draft_project_argmax_indexed(
+        h.data_ptr(), m, k, W.data_ptr(), n, ids.data_ptr(), ids.shape[0], out_id.data_ptr(),
+        out_logit.data_ptr(), workspace.data_ptr(), workspace.numel() * workspace.element_size(), path, st),
+        "draft_project_argmax_indexed")
+    return out_id, out_logit
+
+
+def lmhead_bench_time_argmax_indexed(h: torch.Tensor, heads: list, ids: torch.Tensor, path: int,
+                                     calls: int, out_id: torch.Tensor, out_logit: torch.Tensor,
+                                     workspace: torch.Tensor, stream=None) -> float:
+    """lmhead_bench_time_argmax for draft_project_argmax_indexed: `heads`
+    are full heads [N, K] read through the same id list.  Synchronizes."""
+    _dev_tensor(h, "h", _BF16_LIKE, 2)
+    _dev_tensor(ids, "ids", (torch.int32,), 1)
+    m, k = h.shape
+    for w in heads:
+        _dev_tensor(w, "W", _BF16_LIKE, 2)
+        if w.shape != heads[0].shape or w.shape[1] != k:
+            raise ValueError("every head must be [N, K] with the same N and K")
+    n = heads[0].shape[0]
+    ptrs = (ctypes.c_void_p * len(heads))(*[w.data_ptr() for w in heads])
+    out = ctypes.c_double(0.0)
+    _check(lib().lmhead_bench_time_argmax_indexed(
+        h.data_ptr(), m, k, ptrs, len(heads), n, ids.data_ptr(), ids.shape[0], out_id.data_ptr(),
+        out_logit.data_ptr(), workspace.data_ptr(), workspace.numel() * workspace.element_size(), path, calls,
+        ctypes.byref(out), _stream(stream, h.device)), "lmhead_bench_time_argmax_indexed")
+    return out.value
