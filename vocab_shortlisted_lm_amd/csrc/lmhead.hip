@@ -78,13 +78,30 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 #define LMH_MFMA_RING 3          // batches in the register ring of the coalesced matrix-core kernel
 #endif
 
-#ifndef LMH_UNCOND_ISSUE
-#define LMH_UNCOND_ISSUE 0       // VALU kernels issue the next loads unconditionally (zero-record past the end)
+#ifndef LMH_RING_MAX_ROWS
+#define LMH_RING_MAX_ROWS 131072  // VALU argmax over fewer head rows than this uses the ring loop
 #endif
 #ifndef LMH_VALU_WAVES
 #define LMH_VALU_WAVES 4          // waves per workgroup (VALU path)
 #endif
 constexpr int kValuMaxM = 8;
+// Load loop of the VALU kernels (template parameter LOOP):
+//   kLoopPair    two register buffers; the next batch is issued only if it
+//                exists, which makes the compiler's wait counts cover the
+//                just-issued batch too (each step drains the loads);
+//   kLoopUncond  the same, issuing every batch (past the end through
+//                descriptors with no records), so a step waits only for the
+//                batch it scores;
+//   kLoopRing    a branch-free ring of kRingDepth batches, unrolled so the
+//                slots are static: exact waits, one batch always in flight.
+// Measured on MI355X (interleaved runs, same box): on the full 248,320-row
+// head the draining loop is best for M = 2..4 and the unconditional one for
+// M = 1 (174.6 against 177.7 us); on shortlists of 16k-53k rows the ring
+// is 3-16% faster than either (the ramp and tail dominate there).
+constexpr int kLoopPair = 0;
+constexpr int kLoopUncond = 1;
+constexpr int kLoopRing = 2;
+constexpr int kRingDepth = 2;
 constexpr int kValuMaxChunksTimesM = 40;   // register budget: 160 VGPRs of h
 #ifndef LMH_VALU_AUTO_MAX_M
 #define LMH_VALU_AUTO_MAX_M 4     // largest M the default choice sends to the VALU path
@@ -797,7 +814,7 @@ struct ValuEpilogue {
 // when a step's rows are issued, so they have arrived (loads complete in
 // order) by the time their own rows are issued; a row whose id is outside
 // [0, nw) reads nothing and is left out.
-template <int M, int CPL, int U, int WV, int TK, bool LOGITS, bool IDX = false>
+template <int M, int CPL, int U, int WV, int TK, bool LOGITS, bool IDX = false, int LOOP = kLoopPair>
 __global__ void __launch_bounds__(64 * WV)
 proj_valu_rows(const uint16_t* __restrict__ h, const uint16_t* __restrict__ W, int R, int K, Epi epi) {
   static_assert(!IDX || (TK == 1 && !LOGITS && U <= 64), "indexed rows: argmax epilogue");
@@ -867,6 +884,77 @@ proj_valu_rows(const uint16_t* __restrict__ h, const uint16_t* __restrict__ W, i
     }
   };
 
+  static_assert(LOOP != kLoopUncond, "row-order kernel: pair or ring loop");
+  if constexpr (LOOP == kLoopRing) {
+    // The wave's steps (U rows each) in order with a ring of D batches, as
+    // in proj_valu_tiled: a branch-free steady state unrolled D times, rows
+    // past R read through descriptors with no records.  IDX: ring slot S
+    // keeps, in lane u < U, the ids of the rows of its next step.
+    constexpr int D = kRingDepth;
+    const int rw = (blockIdx.x * WV + wave) * U;
+    const int count = rw < R ? (R - 1 - rw) / step + 1 : 0;
+    if (count > 0) {
+      u32x4 ring[D][U][CPL];
+      int live[D];
+      int vid[IDX ? D : 1];
+      int ri = rw, ra = rw, rc = rw;
+      if constexpr (IDX) {
+#pragma unroll
+        for (int q = 0; q < D; ++q) {
+          vid[q] = fetch_ids(ra);
+          ra += step;
+        }
+      }
+      auto issue_at = [&](auto slot) __attribute__((always_inline)) {
+        constexpr int S = decltype(slot)::value;
+        int bits = 0;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const int r = ri + u;
+          bool ok = r < R;
+          int src = r;
+          if constexpr (IDX) {
+            src = __builtin_amdgcn_readlane(vid[S], u);
+            ok = ok && row_id_ok(src, epi.nw);
+          }
+          bits |= ok ? (1 << u) : 0;
+          const __amdgpu_buffer_rsrc_t rs = make_rsrc(W + (size_t)(ok ? src : 0) * (size_t)K, ok ? row_bytes : 0u);
+#pragma unroll
+          for (int j = 0; j < CPL; ++j) ring[S][u][j] = load16(rs, voff[j]);
+        }
+        live[S] = bits;
+        if constexpr (IDX) {
+          vid[S] = fetch_ids(ra);
+          ra += step;
+        }
+        ri += step;
+      };
+      auto consume_at = [&](auto slot) __attribute__((always_inline)) {
+        constexpr int S = decltype(slot)::value;
+        score_rows(ring[S], live[S], rc);
+        rc += step;
+      };
+      [&]<int... J>(std::integer_sequence<int, J...>) {
+        (issue_at(std::integral_constant<int, J>{}), ...);
+      }(std::make_integer_sequence<int, D - 1>{});
+      int n = 0;
+      for (; n + D <= count; n += D) {
+        [&]<int... J>(std::integer_sequence<int, J...>) {
+          ((issue_at(std::integral_constant<int, (J + D - 1) % D>{}), consume_at(std::integral_constant<int, J>{})),
+           ...);
+        }(std::make_integer_sequence<int, D>{});
+      }
+      [&]<int... J>(std::integer_sequence<int, J...>) {
+        ((n + J < count ? (issue_at(std::integral_constant<int, (J + D - 1) % D>{}),
+                           consume_at(std::integral_constant<int, J>{}), 0)
+                        : 0),
+         ...);
+      }(std::make_integer_sequence<int, D>{});
+    }
+    ep.finish(lane, wave, epi);
+    return;
+  }
+
   int r0 = (blockIdx.x * WV + wave) * U;
   int la = 0, lb = 0;
   if constexpr (IDX) {
@@ -875,16 +963,14 @@ proj_valu_rows(const uint16_t* __restrict__ h, const uint16_t* __restrict__ W, i
   }
   if constexpr (LMH_VALU_PREFETCH) {
     // Two register buffers: the next rows are in flight while these are scored.
-    // Rows past R get descriptors with no records: their loads read zero
-    // without touching memory, so the loads may be issued unconditionally.
-    if (LMH_UNCOND_ISSUE || r0 < R) load_rows(wa, la, r0);
+    if (r0 < R) load_rows(wa, la, r0);
     while (r0 < R) {
       const int r1 = r0 + step;
-      if (LMH_UNCOND_ISSUE || r1 < R) load_rows(wb, lb, r1);
+      if (r1 < R) load_rows(wb, lb, r1);
       score_rows(wa, la, r0);
       if (r1 >= R) break;
       const int r2 = r1 + step;
-      if (LMH_UNCOND_ISSUE || r2 < R) load_rows(wa, la, r2);
+      if (r2 < R) load_rows(wa, la, r2);
       score_rows(wb, lb, r1);
       r0 = r2;
     }
@@ -911,7 +997,7 @@ proj_valu_rows(const uint16_t* __restrict__ h, const uint16_t* __restrict__ W, i
 // the wave's next tile are fetched with a vector load when a tile starts,
 // so they have long arrived (loads complete in order) when that tile starts;
 // a row with an id outside [0, nw) reads nothing and is left out.
-template <int M, int TR, int WV, int TK, bool LOGITS, bool IDX = false>
+template <int M, int TR, int WV, int TK, bool LOGITS, bool IDX = false, int LOOP = kLoopPair>
 __global__ void __launch_bounds__(64 * WV)
 proj_valu_tiled(const uint16_t* __restrict__ h, const uint16_t* __restrict__ W, int R, int K, Epi epi) {
   static_assert(!IDX || (TK == 1 && !LOGITS && TR <= 64), "indexed rows: argmax epilogue");
@@ -976,8 +1062,9 @@ proj_valu_tiled(const uint16_t* __restrict__ h, const uint16_t* __restrict__ W, 
       live = bits;
     } else {
       // past the last tile (unconditional issue) the descriptor has no records
-      const int nlive = LMH_UNCOND_ISSUE ? __builtin_amdgcn_readfirstlane(max(0, min(TR, R - r0))) : min(TR, R - r0);
-      const int rbase = LMH_UNCOND_ISSUE ? __builtin_amdgcn_readfirstlane(nlive == 0 ? 0 : r0) : r0;
+      constexpr bool kUncond = LOOP == kLoopUncond;
+      const int nlive = kUncond ? __builtin_amdgcn_readfirstlane(max(0, min(TR, R - r0))) : min(TR, R - r0);
+      const int rbase = kUncond ? __builtin_amdgcn_readfirstlane(nlive == 0 ? 0 : r0) : r0;
       const __amdgpu_buffer_rsrc_t rs = make_rsrc(W + (size_t)rbase * (size_t)K, (uint32_t)nlive * row_bytes);
 #pragma unroll
       for (int q = 0; q < TR; ++q) w[q] = load16(rs, off + (uint32_t)q * row_bytes);
@@ -1012,6 +1099,87 @@ proj_valu_tiled(const uint16_t* __restrict__ h, const uint16_t* __restrict__ W, 
     }
   };
 
+  if constexpr (LOOP == kLoopRing) {
+    // The wave's (tile, stripe) positions in order, with a ring of D
+    // batches: D - 1 are in flight while one is scored.  The steady state is
+    // unrolled D times so ring slots are static and every slot issues and
+    // consumes without conditions; positions past the wave's last one read
+    // through descriptors with no records (nothing is fetched).  IDX: ring
+    // slot S also keeps, in lane q < TR, the ids of the tile its next
+    // position will read, loaded D positions ahead.
+    constexpr int D = kRingDepth;
+    const int tile0 = blockIdx.x * WV + wave;
+    const int my_tiles = tile0 < ntiles ? (ntiles - 1 - tile0) / tstride + 1 : 0;
+    const int count = my_tiles * nb;
+    if (count > 0) {
+      u32x4 ring[D][TR];
+      int live[D];
+      int vid[IDX ? D : 1];
+      int ti = tile0, ji = 0;  // next position to issue
+      int ta = tile0, ja = 0;  // position D ahead of it (IDX ids)
+      int tc = tile0, jc = 0;  // next position to consume
+      auto id_lane = [&](int tile) { return load_row_id(epi.rowmap, R, tile * TR + (lane < TR ? lane : 0)); };
+      if constexpr (IDX) {
+#pragma unroll
+        for (int q = 0; q < D; ++q) {
+          vid[q] = id_lane(ta);
+          advance(ta, ja);
+        }
+      }
+      auto issue_at = [&](auto slot) __attribute__((always_inline)) {
+        constexpr int S = decltype(slot)::value;
+        const int c = lane + 64 * ji;
+        const uint32_t off = c < chunks ? (uint32_t)c * 16u : kOobOffset;
+        const int r0 = ti * TR;
+        if constexpr (IDX) {
+          int bits = 0;
+#pragma unroll
+          for (int q = 0; q < TR; ++q) {
+            const int id = __builtin_amdgcn_readlane(vid[S], q);
+            const bool ok = r0 + q < R && row_id_ok(id, epi.nw);
+            bits |= ok ? (1 << q) : 0;
+            const __amdgpu_buffer_rsrc_t rs = make_rsrc(W + (size_t)(ok ? id : 0) * (size_t)K, ok ? row_bytes : 0u);
+            ring[S][q] = load16(rs, off);
+          }
+          live[S] = bits;
+          vid[S] = id_lane(ta);
+          advance(ta, ja);
+        } else {
+          const int nlive = __builtin_amdgcn_readfirstlane(max(0, min(TR, R - r0)));
+          const int rbase = __builtin_amdgcn_readfirstlane(nlive > 0 ? r0 : 0);
+          const __amdgpu_buffer_rsrc_t rs = make_rsrc(W + (size_t)rbase * (size_t)K, (uint32_t)nlive * row_bytes);
+#pragma unroll
+          for (int q = 0; q < TR; ++q) ring[S][q] = load16(rs, off + (uint32_t)q * row_bytes);
+          live[S] = (1 << TR) - 1;
+        }
+        advance(ti, ji);
+      };
+      auto consume_at = [&](auto slot) __attribute__((always_inline)) {
+        constexpr int S = decltype(slot)::value;
+        consume(ring[S], live[S], tc, jc);
+        advance(tc, jc);
+      };
+      [&]<int... J>(std::integer_sequence<int, J...>) {
+        (issue_at(std::integral_constant<int, J>{}), ...);
+      }(std::make_integer_sequence<int, D - 1>{});
+      int n = 0;
+      for (; n + D <= count; n += D) {
+        [&]<int... J>(std::integer_sequence<int, J...>) {
+          ((issue_at(std::integral_constant<int, (J + D - 1) % D>{}), consume_at(std::integral_constant<int, J>{})),
+           ...);
+        }(std::make_integer_sequence<int, D>{});
+      }
+      [&]<int... J>(std::integer_sequence<int, J...>) {
+        ((n + J < count ? (issue_at(std::integral_constant<int, (J + D - 1) % D>{}),
+                           consume_at(std::integral_constant<int, J>{}), 0)
+                        : 0),
+         ...);
+      }(std::make_integer_sequence<int, D>{});
+    }
+    ep.finish(lane, wave, epi);
+    return;
+  }
+
   int tile = blockIdx.x * WV + wave;
   int j = 0;
   u32x4 wa[TR], wb[TR];
@@ -1023,14 +1191,14 @@ proj_valu_tiled(const uint16_t* __restrict__ h, const uint16_t* __restrict__ W, 
       int t1 = tile, j1 = j;
       advance(t1, j1);
       bool more = t1 < ntiles;
-      if (LMH_UNCOND_ISSUE || more) issue(wb, lb, t1, j1);
+      if (LOOP == kLoopUncond || more) issue(wb, lb, t1, j1);
       consume(wa, la, tile, j);
       if (!more) break;
       tile = t1;
       j = j1;
       advance(t1, j1);
       more = t1 < ntiles;
-      if (LMH_UNCOND_ISSUE || more) issue(wa, la, t1, j1);
+      if (LOOP == kLoopUncond || more) issue(wa, la, t1, j1);
       consume(wb, lb, tile, j);
       if (!more) break;
       tile = t1;
@@ -1646,54 +1814,75 @@ struct ValuPlan {
   size_t lds = 0;
 };
 
-template <int M, int CPL, int WV, int TK, bool LOGITS, bool IDX>
+template <int M, int CPL, int WV, int TK, bool LOGITS, bool IDX, int LOOP>
 void row_plan(ValuPlan& p) {
   if constexpr (M * CPL <= kValuMaxChunksTimesM) {
     // rows per step: keep each of the two row buffers at <= 10 chunks/lane,
     // and one row per step once h alone takes more than 80 registers
     constexpr int U0 = M * CPL > 20 ? 1 : (CPL * LMH_VALU_ROWS <= 10 ? LMH_VALU_ROWS : (CPL <= 10 ? 10 / CPL : 1));
     constexpr int U = U0 < 1 ? 1 : U0;
-    p.fn = proj_valu_rows<M, CPL, U, WV, TK, LOGITS, IDX>;
+    p.fn = proj_valu_rows<M, CPL, U, WV, TK, LOGITS, IDX, LOOP>;
     p.waves = WV;
     p.rows_per_wave = U;
     p.lds = 0;
   }
 }
 
-template <int M, int TK, bool LOGITS, bool IDX, int... C>
+template <int M, int TK, bool LOGITS, bool IDX, int LOOP, int... C>
 void row_plan_cpl(ValuPlan& p, int cpl, std::integer_sequence<int, C...>) {
   constexpr int WV = M <= 4 ? LMH_VALU_WAVES : 2 * LMH_VALU_WAVES;
-  ((cpl == C + 1 ? (row_plan<M, C + 1, WV, TK, LOGITS, IDX>(p), 0) : 0), ...);
+  ((cpl == C + 1 ? (row_plan<M, C + 1, WV, TK, LOGITS, IDX, LOOP>(p), 0) : 0), ...);
 }
 
-template <int M, int TK, bool LOGITS, bool IDX>
+template <int M, int TK, bool LOGITS, bool IDX, int LOOP>
 ValuPlan tiled_plan(int K) {
   ValuPlan p;
-  p.fn = proj_valu_tiled<M, LMH_VALU_TILE_ROWS, LMH_VALU_WAVES, TK, LOGITS, IDX>;
+  p.fn = proj_valu_tiled<M, LMH_VALU_TILE_ROWS, LMH_VALU_WAVES, TK, LOGITS, IDX, LOOP>;
   p.waves = LMH_VALU_WAVES;
   p.rows_per_wave = LMH_VALU_TILE_ROWS;
   p.lds = (size_t)M * chunks_per_lane(K) * 64 * 16;
   return p;
 }
 
+// Row-order plan for M = 1..4 with the argmax loop chosen by the head's row
+// count (the ring below LMH_RING_MAX_ROWS rows); other epilogues keep the
+// two-buffer loop.
+template <int M, int TK, bool LOGITS, bool IDX>
+void row_plan_m(ValuPlan& p, int cpl, int64_t R) {
+  using seq = std::make_integer_sequence<int, 16>;
+  if constexpr (TK == 1 && !LOGITS) {
+    if (R < LMH_RING_MAX_ROWS) {
+      row_plan_cpl<M, TK, LOGITS, IDX, kLoopRing>(p, cpl, seq{});
+      return;
+    }
+  }
+  row_plan_cpl<M, TK, LOGITS, IDX, kLoopPair>(p, cpl, seq{});
+}
+
 template <int TK, bool LOGITS, bool IDX = false>
-ValuPlan valu_plan(int M, int K) {
+ValuPlan valu_plan(int M, int K, int64_t R) {
   ValuPlan p;
-  if (M == 1 && LMH_VALU_TILE_ROWS > 0) return tiled_plan<1, TK, LOGITS, IDX>(K);
+  if (M == 1 && LMH_VALU_TILE_ROWS > 0) {
+    if constexpr (TK == 1 && !LOGITS)
+      return R < LMH_RING_MAX_ROWS ? tiled_plan<1, TK, LOGITS, IDX, kLoopRing>(K)
+                                   : tiled_plan<1, TK, LOGITS, IDX, kLoopUncond>(K);
+    else
+      return tiled_plan<1, TK, LOGITS, IDX, kLoopPair>(K);
+  }
   const int cpl = chunks_per_lane(K);
   using seq = std::make_integer_sequence<int, 16>;
   switch (M) {
-    case 1: row_plan_cpl<1, TK, LOGITS, IDX>(p, cpl, seq{}); break;
-    case 2: row_plan_cpl<2, TK, LOGITS, IDX>(p, cpl, seq{}); break;
-    case 3: row_plan_cpl<3, TK, LOGITS, IDX>(p, cpl, seq{}); break;
-    case 4: row_plan_cpl<4, TK, LOGITS, IDX>(p, cpl, seq{}); break;
+    case 1: row_plan_m<1, TK, LOGITS, IDX>(p, cpl, R); break;
+    case 2: row_plan_m<2, TK, LOGITS, IDX>(p, cpl, R); break;
+    case 3: row_plan_m<3, TK, LOGITS, IDX>(p, cpl, R); break;
+    case 4: row_plan_m<4, TK, LOGITS, IDX>(p, cpl, R); break;
     default:
       if constexpr (TK == 1 && !LOGITS) {
         switch (M) {
-          case 5: row_plan_cpl<5, 1, false, IDX>(p, cpl, seq{}); break;
-          case 6: row_plan_cpl<6, 1, false, IDX>(p, cpl, seq{}); break;
-          case 7: row_plan_cpl<7, 1, false, IDX>(p, cpl, seq{}); break;
-          case 8: row_plan_cpl<8, 1, false, IDX>(p, cpl, seq{}); break;
+          case 5: row_plan_cpl<5, 1, false, IDX, kLoopPair>(p, cpl, seq{}); break;
+          case 6: row_plan_cpl<6, 1, false, IDX, kLoopPair>(p, cpl, seq{}); break;
+          case 7: row_plan_cpl<7, 1, false, IDX, kLoopPair>(p, cpl, seq{}); break;
+          case 8: row_plan_cpl<8, 1, false, IDX, kLoopPair>(p, cpl, seq{}); break;
           default: break;
         }
       }
@@ -1865,8 +2054,10 @@ int run(const Call& c, const Epi& epi, int topk, int32_t* out_id, float* out_log
                            &grid);
     } else {
       ValuPlan p;
-      if constexpr (kIdxOk) p = c.indexed ? valu_plan<TK, LOGITS, true>(c.M, c.K) : valu_plan<TK, LOGITS>(c.M, c.K);
-      else p = valu_plan<TK, LOGITS>(c.M, c.K);
+      if constexpr (kIdxOk)
+        p = c.indexed ? valu_plan<TK, LOGITS, true>(c.M, c.K, c.R) : valu_plan<TK, LOGITS>(c.M, c.K, c.R);
+      else
+        p = valu_plan<TK, LOGITS>(c.M, c.K, c.R);
       if (!p.fn) return LMH_EINVAL;
       st = launch_valu(p, c.h, c.K, static_cast<const uint16_t*>(c.W), c.R, epi, cus, c.stream, &grid);
     }
