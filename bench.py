@@ -212,6 +212,62 @@ def cpu_baseline(h_np, w_np, d2t_np, budget_s: float, indexed: bool = False):
                       f"numpy + BLAS with {threads} threads"}
 
 
+def shortlist_ops(synth, L, torch, np, dev) -> dict:
+    """Load-time and maintenance calls on the shortlisted-head workloads:
+    the gather of each list (whole lmhead_trim call, host range check
+    included), the device union of the two lists behind the 52,755-id list,
+    and 600 escaped ids written into spare rows of the 32,768-id head."""
+    stream = torch.cuda.current_stream(dev)
+    w_np = synth.make_config(2)["W"]
+    w = torch.from_numpy(w_np.view(np.int16)).to(dev)
+    k = w.shape[1]
+    out = {"mode": "shortlist-ops", "K": k, "N": w.shape[0]}
+
+    def events(fn, reps):
+        for _ in range(3):
+            fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps * 1e3  # us
+
+    for cfg in (3, 4, 5):
+        ids = torch.from_numpy(synth.make_config(cfg)["ids"].astype(np.int32)).to(dev)
+        dst = torch.empty((ids.shape[0], k), dtype=w.dtype, device=dev)
+        L.lmhead_trim(w, ids, dst)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        reps = 5
+        for _ in range(reps):
+            L.lmhead_trim(w, ids, dst)
+        torch.cuda.synchronize()
+        us = (time.perf_counter() - t0) / reps * 1e6
+        out[f"trim_{ids.shape[0]}_us"] = round(us, 1)
+        out[f"trim_{ids.shape[0]}_gbps"] = round(2 * ids.shape[0] * k * 2 / (us / 1e6) / 1e9, 1)
+        del dst
+    a, b, _ = synth.union_parts()
+    ad, bd = torch.from_numpy(a).to(dev), torch.from_numpy(b).to(dev)
+    uo = torch.empty(a.size + b.size, dtype=torch.int32, device=dev)
+    uc = torch.empty(4, dtype=torch.int32, device=dev)
+    out["union_us"] = round(events(lambda: L.lmhead_shortlist_union(ad, bd, w.shape[0], uo, uc), 50), 2)
+    out["union_counts"] = [int(x) for x in uc.cpu().tolist()]
+    ids32 = synth.make_config(4)["ids"]
+    spare = 1024
+    cap_ids = torch.from_numpy(np.concatenate([ids32, np.zeros(spare, np.int32)]).astype(np.int32)).to(dev)
+    wt = L.lmhead_trim(w, cap_ids)
+    rng = np.random.default_rng(70)
+    esc = np.setdiff1d(rng.integers(0, w.shape[0], size=800), ids32)[:600].astype(np.int32)
+    rows = torch.from_numpy((ids32.size + np.arange(esc.size)).astype(np.int32)).to(dev)
+    escd = torch.from_numpy(esc).to(dev)
+    us = events(lambda: L.lmhead_shortlist_overwrite(w, wt, cap_ids, rows, escd), 50)
+    out["overwrite_600_us"] = round(us, 2)
+    out["overwrite_600_gbps"] = round(2 * esc.size * k * 2 / (us / 1e6) / 1e9, 1)
+    return out
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -234,6 +290,9 @@ def main() -> int:
     ap.add_argument("--indexed", action="store_true",
                     help="read the shortlist's rows in place from the full head "
                          "(draft_project_argmax_indexed), rotating copies of W past the Infinity Cache")
+    ap.add_argument("--shortlist-ops", action="store_true",
+                    help="instead of the projection: time the list gathers, the device union of two lists "
+                         "and 600 escaped ids written into spare rows (one JSON line)")
     ap.add_argument("--record-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="no GPU: write this workload's entry of profiles/traffic.json from the "
                          "counter_collection.csv files of two rocprofv3 --pmc runs (FETCH_SIZE, "
@@ -262,6 +321,9 @@ def main() -> int:
         return 1
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if a.shortlist_ops:
+        print(json.dumps(shortlist_ops(synth, L, torch, np, dev)), flush=True)
+        return 0
 
     inp, c, m, ids, trimmed, path = d["inp"], d["c"], d["m"], d["ids"], d["trimmed"], d["path"]
     rows, workload, kpath = d["rows"], d["workload"], d["kpath"]

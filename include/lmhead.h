@@ -319,9 +319,11 @@ const char* lmhead_last_error(void);
  * Measurement support (not part of the projection): plain streaming kernels
  * used to find the practical HBM ceiling and to scale hardware counters.
  *
- * lmhead_bench_stream_read: reads `bytes` (a multiple of 16, 16-byte aligned
- *   `src`) with 16-byte loads and writes one 32-bit checksum word per
+ * lmhead_bench_stream_read: reads `bytes` (a nonzero multiple of 16,
+ *   16-byte aligned `src`) with 16-byte non-temporal loads, two groups of
+ *   four in flight per lane, and writes one 32-bit checksum word per
  *   workgroup into `sink` (at least lmhead_bench_sink_words() words).
+ *   grid 0 = one 256-thread workgroup per CU, the fastest shape measured.
  * lmhead_bench_copy: dst[0:bytes] = src[0:bytes] (16-byte multiples/aligned).
  * `grid` = workgroups to launch (0 = the library's default).
  */

@@ -230,6 +230,7 @@ def test_bench_kernels_reject_on_host(L):
     lib = L.lib()
     assert lib.lmhead_bench_stream_read(A, 1000, B, 0, None) == 1     # not a multiple of 16
     assert lib.lmhead_bench_stream_read(None, 1024, B, 0, None) == 1
+    assert lib.lmhead_bench_stream_read(A, 0, B, 0, None) == 1        # nothing to read
     assert lib.lmhead_bench_copy(A, B + 4, 1024, 0, None) == 1
     assert lib.lmhead_bench_sink_words() >= 4096
 
