@@ -258,3 +258,19 @@ def test_indexed_bench_helper_matches_call(L):
         assert 0.0 < ms < 100.0
         want_id, want_lg = L.draft_project_argmax_indexed(h, w_dev, ids, p)
         assert torch.equal(oid, want_id) and torch.equal(olg, want_lg)
+
+
+@pytest.mark.parametrize("m", [1, 3, 24])
+def test_indexed_long_list_takes_the_large_head_loops(L, m):
+    """A list of at least 131,072 entries takes the loops chosen for large
+    heads (unconditional issue at M = 1, the two-buffer loop at M = 2-4):
+    a shuffled 150,000-id list of the full head, with a few invalid ids."""
+    inp = config_inputs(2)
+    c = inp["config"]
+    rng = np.random.default_rng(91 + m)
+    ids = rng.permutation(c.n)[:150_000].astype(np.int32)
+    ids[rng.choice(ids.size, 50, replace=False)] = -3
+    hs = [synth.hidden(92 + m, d, m, c.k) for d in range(2 if m < 24 else 1)]
+    log(f"[indexed long] M={m} S={ids.size}")
+    run_indexed(L, hs, inp["W"], dev_bf16(inp["W"]), ids, paths_for(L, m, c.k), f"long list M={m}",
+                compare_trim=False)

@@ -228,6 +228,8 @@ EDGE = [
     (1, 520, 1000), (1, 2560, 1), (1, 2560, 7), (4, 2560, 4097), (2, 4096, 333),
     (1, 8192, 1501), (5, 264, 129), (8, 2560, 33), (6, 2560, 777), (7, 3072, 50), (16, 2560, 517), (17, 256, 700),
     (24, 2560, 1031), (31, 520, 99), (32, 2560, 2050), (32, 8192, 300), (13, 8, 77),
+    # either side of the head size where the VALU argmax switches load loops
+    (1, 264, 131_071), (1, 264, 131_072), (3, 264, 131_071), (4, 264, 131_072),
 ]
 
 

@@ -78,6 +78,9 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 #define LMH_MFMA_RING 3          // batches in the register ring of the coalesced matrix-core kernel
 #endif
 
+#ifndef LMH_WAVE_MAJOR
+#define LMH_WAVE_MAJOR 0          // 1: hand out work units wave-major (see first_unit)
+#endif
 #ifndef LMH_RING_MAX_ROWS
 #define LMH_RING_MAX_ROWS 131072  // VALU argmax over fewer head rows than this uses the ring loop
 #endif
@@ -196,6 +199,15 @@ __device__ __forceinline__ uint32_t e4m3_encode(float q) {
 // Wave index inside the workgroup, as a value the compiler knows is uniform
 // (so row bases and buffer descriptors live in scalar registers).
 __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)); }
+
+// First work unit (tile or step) of this wave; a wave then strides by
+// gridDim.x * WV units.  Units go out wave-major: the first gridDim.x units
+// to wave 0 of every workgroup, the next to wave 1, and so on, so a head
+// with fewer units than waves (or a last partial round) still spreads over
+// every CU instead of filling the first workgroups.
+__device__ __forceinline__ int first_unit(int wave, int wv) {
+  return LMH_WAVE_MAJOR ? wave * (int)gridDim.x + (int)blockIdx.x : (int)blockIdx.x * wv + wave;
+}
 
 template <int CTRL>
 __device__ __forceinline__ float dpp(float v) {
@@ -891,7 +903,7 @@ proj_valu_rows(const uint16_t* __restrict__ h, const uint16_t* __restrict__ W, i
     // past R read through descriptors with no records.  IDX: ring slot S
     // keeps, in lane u < U, the ids of the rows of its next step.
     constexpr int D = kRingDepth;
-    const int rw = (blockIdx.x * WV + wave) * U;
+    const int rw = first_unit(wave, WV) * U;
     const int count = rw < R ? (R - 1 - rw) / step + 1 : 0;
     if (count > 0) {
       u32x4 ring[D][U][CPL];
@@ -955,7 +967,7 @@ proj_valu_rows(const uint16_t* __restrict__ h, const uint16_t* __restrict__ W, i
     return;
   }
 
-  int r0 = (blockIdx.x * WV + wave) * U;
+  int r0 = first_unit(wave, WV) * U;
   int la = 0, lb = 0;
   if constexpr (IDX) {
     vid1 = fetch_ids(r0);
@@ -1108,7 +1120,7 @@ proj_valu_tiled(const uint16_t* __restrict__ h, const uint16_t* __restrict__ W, 
     // slot S also keeps, in lane q < TR, the ids of the tile its next
     // position will read, loaded D positions ahead.
     constexpr int D = kRingDepth;
-    const int tile0 = blockIdx.x * WV + wave;
+    const int tile0 = first_unit(wave, WV);
     const int my_tiles = tile0 < ntiles ? (ntiles - 1 - tile0) / tstride + 1 : 0;
     const int count = my_tiles * nb;
     if (count > 0) {
@@ -1180,7 +1192,7 @@ proj_valu_tiled(const uint16_t* __restrict__ h, const uint16_t* __restrict__ W, 
     return;
   }
 
-  int tile = blockIdx.x * WV + wave;
+  int tile = first_unit(wave, WV);
   int j = 0;
   u32x4 wa[TR], wb[TR];
   int la = 0, lb = 0;
@@ -1301,7 +1313,7 @@ proj_valu_fp8(const uint16_t* __restrict__ h, const uint8_t* __restrict__ W, con
     }
   };
 
-  int tile = blockIdx.x * WV + wave;
+  int tile = first_unit(wave, WV);
   int j = 0;
   u32x4 wa[TR], wb[TR];
   if (tile < ntiles) {
@@ -1620,7 +1632,7 @@ proj_mfma(const uint16_t* __restrict__ h, const void* __restrict__ Wv, const flo
   // The wave walks (tile, batch) pairs in order with a ring of D register
   // buffers: D - 1 batches are in flight while one is transposed and fed to
   // the matrix cores.  The loop is unrolled D times so ring slots are static.
-  int ti = blockIdx.x * WV + wave, bi = 0;  // next pair to issue
+  int ti = first_unit(wave, WV), bi = 0;  // next pair to issue
   int tc = ti, bc = 0;                      // next pair to consume
   auto advance = [&](int& t, int& bb) {
     if (++bb == nbatch) {
