@@ -39,20 +39,29 @@ def weight_bytes(rows: int, k: int) -> int:
     return rows * k * 2
 
 
-def algorithmic_bytes(m: int, rows: int, k: int, with_d2t: bool, fp8: bool = False,
+def algorithmic_bytes(m: int, rows: int, k: int, with_d2t: bool, fmt: str = "bf16",
                       indexed: bool = False) -> int:
     """Bytes one whole call must move at least: every weight row once, the
     hidden rows once, the d2t entries of the winners and the two outputs."""
-    return projection_bytes(m, rows, k, fp8, indexed) + (4 * m if with_d2t else 0) + 8 * m
+    return projection_bytes(m, rows, k, fmt, indexed) + (4 * m if with_d2t else 0) + 8 * m
 
 
-def projection_bytes(m: int, rows: int, k: int, fp8: bool = False, indexed: bool = False) -> int:
+def head_bytes(rows: int, k: int, fmt: str = "bf16") -> int:
+    """Bytes of the head: bf16; E4M3 codes plus one fp32 scale per row; or
+    MXFP4 codes (two per byte) plus one E8M0 scale byte per 32 elements."""
+    if fmt == "fp8":
+        return rows * k + rows * 4
+    if fmt == "mxfp4":
+        return rows * (k // 2) + rows * (k // 32)
+    return weight_bytes(rows, k)
+
+
+def projection_bytes(m: int, rows: int, k: int, fmt: str = "bf16", indexed: bool = False) -> int:
     """Bytes the projection kernel itself must move: every weight row once
-    (bf16, or E4M3 codes plus one fp32 scale per row), the id list when the
-    rows are read in place from the full head (4 bytes per entry), and the
-    hidden rows once (the fold and the d2t map run afterwards)."""
-    w = rows * k + rows * 4 if fp8 else weight_bytes(rows, k)
-    return w + (rows * 4 if indexed else 0) + m * k * 2
+    (in the head's format), the id list when the rows are read in place from
+    the full head (4 bytes per entry), and the hidden rows once (the fold and
+    the d2t map run afterwards)."""
+    return head_bytes(rows, k, fmt) + (rows * 4 if indexed else 0) + m * k * 2
 
 
 def source_digest() -> str:
@@ -75,8 +84,8 @@ def describe(a, synth, L):
     ids = inp["ids"]
     trimmed = ids is not None and not a.full
     path = {"auto": L.LMH_PATH_AUTO, "valu": L.LMH_PATH_VALU, "mfma": L.LMH_PATH_MFMA}[a.path]
-    if a.fp8:
-        chosen = L.LMH_PATH_MFMA if path == L.LMH_PATH_AUTO else path   # the library's FP8 default
+    if a.fp8 or a.mxfp4:
+        chosen = L.LMH_PATH_MFMA if path == L.LMH_PATH_AUTO else path   # the library's FP8 / MXFP4 default
     else:
         chosen = L.draft_project_auto_path(m, c.k) if path == L.LMH_PATH_AUTO else path
     kpath = {L.LMH_PATH_VALU: "valu", L.LMH_PATH_MFMA: "mfma"}[chosen]
@@ -88,9 +97,12 @@ def describe(a, synth, L):
         rows, copies = c.n, 1
         workload = (f"full-vocab draft step M={m} K={c.k} N={c.n}" if a.config == 2
                     else f"{c.name}: M={m} K={c.k} full head N={c.n}")
+    if a.fp8 and a.mxfp4:
+        raise SystemExit("bench.py: --fp8 and --mxfp4 exclude each other")
     if a.indexed:
-        if ids is None or a.full or a.fp8:
-            raise SystemExit("bench.py: --indexed needs a shortlist config (1, 3, 4, 5), without --full or --fp8")
+        if ids is None or a.full or a.fp8 or a.mxfp4:
+            raise SystemExit("bench.py: --indexed needs a shortlist config (1, 3, 4, 5), without --full, "
+                             "--fp8 or --mxfp4")
         workload = (f"{c.name}: M={m} K={c.k} {rows} listed rows read in place from the full head "
                     f"N={c.n} ({copies} rotated copies of W)")
     if a.fp8:
@@ -98,9 +110,17 @@ def describe(a, synth, L):
             copies = max(1, -(-2 * MALL_BYTES // (rows * c.k)) + 1)
             workload = f"{c.name}: M={m} K={c.k} trimmed to {rows} rows ({copies} rotated copies)"
         workload += ", FP8 E4M3 head (fp32 row scale)"
-    kname = kernel_name(kpath, m) if not a.fp8 else ("proj_mfma" if kpath == "mfma" else "proj_valu_fp8")
+    if a.mxfp4:
+        if kpath != "mfma":
+            raise SystemExit("bench.py: MXFP4 heads run on the matrix-core path only")
+        if trimmed:
+            copies = max(1, -(-2 * MALL_BYTES // head_bytes(rows, c.k, "mxfp4")) + 1)
+            workload = f"{c.name}: M={m} K={c.k} trimmed to {rows} rows ({copies} rotated copies)"
+        workload += ", MXFP4 head (E2M1, E8M0 scale per 32)"
+    fmt = "fp8" if a.fp8 else ("mxfp4" if a.mxfp4 else "bf16")
+    kname = kernel_name(kpath, m) if fmt == "bf16" else ("proj_mfma" if kpath == "mfma" else "proj_valu_fp8")
     return dict(inp=inp, c=c, m=m, ids=ids, trimmed=trimmed, path=path, kpath=kpath, rows=rows,
-                copies=copies, workload=workload, kname=kname)
+                copies=copies, workload=workload, kname=kname, fmt=fmt)
 
 
 def measured_traffic(path: str, workload: str):
@@ -167,7 +187,7 @@ def record_traffic(a, d, fetch_csv: str, write_csv: str) -> int:
         "copy16_fetch_kib": fcopy, "copy16_write_kib": wcopy,
         "fetch_scale": round(fs, 5), "write_scale": round(ws, 5),
         "bytes_projection_kernel": int(round(proj)), "bytes_finalize_kernel": int(round(fin)),
-        "algorithmic_bytes_projection_kernel": projection_bytes(d["m"], d["rows"], d["c"].k, a.fp8),
+        "algorithmic_bytes_projection_kernel": projection_bytes(d["m"], d["rows"], d["c"].k, d["fmt"], a.indexed),
     }
     try:
         with open(TRAFFIC_FILE) as f:
@@ -287,6 +307,9 @@ def main() -> int:
     ap.add_argument("--fp8", action="store_true",
                     help="quantize the head (or shortlist) to FP8 E4M3 with one scale per row at load "
                          "and time draft_project_argmax_fp8 (no CPU baseline)")
+    ap.add_argument("--mxfp4", action="store_true",
+                    help="quantize the head (or shortlist) to MXFP4 at load and time "
+                         "draft_project_argmax_mxfp4 (no CPU baseline)")
     ap.add_argument("--indexed", action="store_true",
                     help="read the shortlist's rows in place from the full head "
                          "(draft_project_argmax_indexed), rotating copies of W past the Infinity Cache")
@@ -349,6 +372,13 @@ def main() -> int:
             torch.cuda.synchronize()
         del heads, w
         heads = qheads
+    if a.mxfp4:
+        qheads = []
+        for w in heads:
+            qheads.append(L.lmhead_quantize_mxfp4(w))
+            torch.cuda.synchronize()
+        del heads, w
+        heads = qheads
     torch.cuda.synchronize()
 
     ws = L.new_workspace(dev)
@@ -362,6 +392,9 @@ def main() -> int:
         elif a.fp8:
             q, sc = heads[i % len(heads)]
             L.draft_project_argmax_fp8(h, q, sc, d2t, path, out_id, out_logit, ws, stream)
+        elif a.mxfp4:
+            q, sc = heads[i % len(heads)]
+            L.draft_project_argmax_mxfp4(h, q, sc, d2t, path, out_id, out_logit, ws, stream)
         else:
             L.draft_project_argmax_path(h, heads[i % len(heads)], d2t, path, out_id, out_logit, ws,
                                         stream)
@@ -388,16 +421,18 @@ def main() -> int:
         proj_ms = L.lmhead_bench_time_argmax_indexed(h, heads, d2t, path, a.steps, out_id, out_logit, ws, stream)
     elif a.fp8:
         proj_ms = L.lmhead_bench_time_argmax_fp8(h, heads, d2t, path, a.steps, out_id, out_logit, ws, stream)
+    elif a.mxfp4:
+        proj_ms = L.lmhead_bench_time_argmax_mxfp4(h, heads, d2t, path, a.steps, out_id, out_logit, ws, stream)
     else:
         proj_ms = L.lmhead_bench_time_argmax(h, heads, d2t, path, a.steps, out_id, out_logit, ws, stream)
-    pbytes = projection_bytes(m, rows, c.k, a.fp8, a.indexed)
+    pbytes = projection_bytes(m, rows, c.k, d["fmt"], a.indexed)
     achieved = pbytes / (proj_ms / 1e3) / 1e9
-    abytes = algorithmic_bytes(m, rows, c.k, d2t is not None, a.fp8, a.indexed)
+    abytes = algorithmic_bytes(m, rows, c.k, d2t is not None, d["fmt"], a.indexed)
     traffic = measured_traffic(kpath, workload)
     extra = {}
     if a.stream_read:
         sink = torch.zeros(L.lmhead_bench_sink_words(), dtype=torch.int32, device=dev)
-        buf = heads[0][0] if a.fp8 else heads[0]
+        buf = heads[0][0] if d["fmt"] != "bf16" else heads[0]
         for _ in range(3):
             L.lmhead_bench_stream_read(buf, sink)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -434,7 +469,8 @@ def main() -> int:
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "e4m3 W x bf16 h, fp32 accumulate" if a.fp8 else "bf16",
+        "dtype": {"fp8": "e4m3 W x bf16 h, fp32 accumulate", "mxfp4": "mxfp4 (e2m1 + e8m0) W x bf16 h, fp32 accumulate",
+                  "bf16": "bf16"}[d["fmt"]],
         "data": "synthetic (seeded bf16 W ~ N(0, 0.02), h ~ N(0, 1))",
         "config": {"workload": workload, "M": m, "K": c.k, "rows": rows, "indexed": a.indexed,
                    "kernel": d["kname"], "d2t": d2t is not None, "parallelism": "single GPU"},
@@ -448,7 +484,7 @@ def main() -> int:
         "wall_s": round(wall, 3),
     }
     result.update(extra)
-    if not a.no_cpu_baseline and not a.fp8:
+    if not a.no_cpu_baseline and d["fmt"] == "bf16":
         hb = h_np
         if a.indexed:
             result["cpu_baseline"] = cpu_baseline(hb, w_np, ids, a.cpu_seconds, indexed=True)

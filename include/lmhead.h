@@ -227,6 +227,53 @@ int draft_project_argmax_fp8(const uint16_t* h, int64_t M, int64_t K,
                              int path, void* stream);
 
 /*
+ * lmhead_quantize_mxfp4 -- load-time 4-bit copy of a bf16 head (W or W_trim)
+ * in OCP MXFP4: E2M1 elements in blocks of 32 consecutive elements of a
+ * row, each block with one power-of-two scale stored as an E8M0 code.  The
+ * pages requantize the trimmed draft head to a 4-bit format at no measured
+ * acceptance cost (zone-1.cobraproject.com "Masked MTP drafts", the section
+ * of that name); their format is NVFP4, the 4-bit format of their GPUs,
+ * and MXFP4 is the one MI355X converts in hardware.  Rounding and scale
+ * follow the MX specification's conversion:
+ *   s = floor(log2(max |block|)) - 2, clamped to [-127, 127], 0 for a block
+ *       of zeros; scales[r, b] = s + 127;
+ *   code = the E2M1 value (0, 0.5, 1, 1.5, 2, 3, 4, 6 and negatives)
+ *       nearest to W / 2^s, ties to the even code, above 6 saturating.
+ * The quantized head stands for decode(code) * 2^s.
+ *
+ *  W       [R, K] bf16 (device, 16-byte aligned); K a multiple of 32.
+ *  Wq      [R, K / 2] uint8 (device, 16-byte aligned): two codes per byte,
+ *          element 2i in the low nibble of byte i.
+ *  scales  [R, K / 32] uint8 (device).
+ * R = 0 is a no-op.  Asynchronous on `stream`; allocates nothing.
+ * Returns LMH_EINVAL for a bad shape, a null or misaligned pointer.
+ */
+int lmhead_quantize_mxfp4(const uint16_t* W, int64_t R, int64_t K,
+                          uint8_t* Wq, uint8_t* scales, void* stream);
+
+/*
+ * draft_project_argmax_mxfp4 -- draft_project_argmax over an MXFP4 head
+ * from lmhead_quantize_mxfp4: out_logit[m] = max_r sum_k h[m, k] *
+ * decode(Wq[r, k]) * 2^(scales[r, k / 32] - 127), fp32 sums of exact
+ * products (every E2M1 value times a power of two is a bf16 number); out_id
+ * as for draft_project_argmax (first row among equal maxima, mapped
+ * through d2t).  The head streams at 0.53 bytes per weight (codes and
+ * scales).  The matrix cores take every M.
+ *
+ *  Wq, scales as written by lmhead_quantize_mxfp4 (R rows); K a multiple
+ *             of 512; Wq and scales 16-byte aligned.
+ *  path       LMH_PATH_AUTO or LMH_PATH_MFMA.
+ * Other arguments, workspace, synchronization and errors as for
+ * draft_project_argmax_path.
+ */
+int draft_project_argmax_mxfp4(const uint16_t* h, int64_t M, int64_t K,
+                               const uint8_t* Wq, const uint8_t* scales,
+                               int64_t R, const int32_t* d2t,
+                               int32_t* out_id, float* out_logit,
+                               void* workspace, size_t workspace_bytes,
+                               int path, void* stream);
+
+/*
  * draft_project_argmax_indexed -- the shortlisted argmax read straight from
  * the full head: for each hidden row m, over the list entries i with
  * ids[i] in [0, N),
@@ -364,6 +411,19 @@ int lmhead_bench_time_argmax_fp8(const uint16_t* h, int64_t M, int64_t K,
                                  void* workspace, size_t workspace_bytes,
                                  int path, int calls, double* proj_ms,
                                  void* stream);
+
+/*
+ * lmhead_bench_time_argmax_mxfp4: the same over MXFP4 heads (draft_project_
+ *   argmax_mxfp4): launch i uses heads[i % nheads] with scales[i % nheads].
+ */
+int lmhead_bench_time_argmax_mxfp4(const uint16_t* h, int64_t M, int64_t K,
+                                   const uint8_t* const* heads,
+                                   const uint8_t* const* scales, int nheads,
+                                   int64_t R, const int32_t* d2t,
+                                   int32_t* out_id, float* out_logit,
+                                   void* workspace, size_t workspace_bytes,
+                                   int path, int calls, double* proj_ms,
+                                   void* stream);
 
 /*
  * lmhead_bench_time_argmax_indexed: the same for draft_project_argmax_

@@ -17,7 +17,8 @@ Two bars are applied to every hidden row:
    B(r_g) + B(r_best), and if the gap exceeds that sum the ids must match.
    Over an FP8 head the products are exact too (bf16 x E4M3) and one more
    rounding multiplies by the row's scale: (K + 2) * 2**-24 * sum_k
-   |h_k w_k| with w the dequantized values.
+   |h_k w_k| with w the dequantized values.  Over an MXFP4 head every
+   dequantized value is a bf16 number and the bf16 bound applies unchanged.
 """
 from __future__ import annotations
 
@@ -70,6 +71,19 @@ def check_fp8(h_bits, codes, scale, d2t, gpu_id, gpu_logit, res=None) -> ParityS
         res = oracle.oracle_project_argmax_fp8(h_bits, codes, scale, d2t, keep_logits=True)
     return _check_core(h_bits, lambda rows: oracle.oracle_dequant_fp8(codes[rows], scale[rows]),
                        codes.shape[0], d2t, gpu_id, gpu_logit, res, extra=2)
+
+
+def check_mxfp4(h_bits, codes, scales, d2t, gpu_id, gpu_logit, res=None) -> ParityStats:
+    """The same rule over an MXFP4 head (codes [R, K / 2], scales [R, K / 32]).
+    Every E2M1 value times its block's power of two is a bf16 number, so the
+    GPU's products are exact as over a bf16 head and the derived bound is
+    the bf16 one (K + 1 roundings) against the dequantized values."""
+    codes = np.asarray(codes)
+    scales = np.asarray(scales)
+    if res is None or res.logits is None:
+        res = oracle.oracle_project_argmax_mxfp4(h_bits, codes, scales, d2t, keep_logits=True)
+    return _check_core(h_bits, lambda rows: oracle.oracle_dequant_mxfp4(codes[rows], scales[rows]),
+                       codes.shape[0], d2t, gpu_id, gpu_logit, res, extra=1)
 
 
 def _check_core(h_bits, w_rows, r, d2t, gpu_id, gpu_logit, res, extra) -> ParityStats:

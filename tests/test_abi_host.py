@@ -192,6 +192,25 @@ def test_indexed_rejects_on_host(L):
     assert t(A, 1, 2560, one, 1, 1000, C, 100, D, E, E, ws, 0, 0, ctypes.byref(out), None) == 1
 
 
+def test_mxfp4_rejects_on_host(L):
+    lib = L.lib()
+    q = lib.lmhead_quantize_mxfp4
+    assert q(A, 0, 2560, B, C, None) == 0                        # R = 0: no-op
+    assert q(A, 10, 2576, B, C, None) == 1                       # K not a multiple of 32
+    assert q(A, 10, 2560, B + 8, C, None) == 1                   # Wq misaligned
+    assert q(None, 10, 2560, B, C, None) == 1
+    assert q(A, 10, 2560, B, None, None) == 1
+    f = lib.draft_project_argmax_mxfp4
+    ws = L.draft_project_workspace_bytes(4)
+    assert f(A, 4, 2592, B, C, 100, None, D, E, E, ws, 0, None) == 1   # K % 512
+    assert f(A, 4, 2560, B, C, 100, None, D, E, E, ws, 1, None) == 1   # no VALU path
+    assert f(A, 4, 2560, B, C + 4, 100, None, D, E, E, ws, 0, None) == 1  # scales misaligned
+    assert f(A, 4, 2560, B, None, 100, None, D, E, E, ws, 0, None) == 1
+    assert f(A, 33, 2560, B, C, 100, None, D, E, E, ws, 0, None) == 1
+    assert f(A, 1, 2560, B, C, 0, None, D, E, E, ws, 0, None) == 1     # R = 0
+    assert f(A, 4, 2560, B, C, 100, None, D, E, E, 8, 0, None) == 3    # workspace
+
+
 def test_shortlist_ops_reject_on_host(L):
     lib = L.lib()
     f = lib.lmhead_shortlist_overwrite
@@ -252,7 +271,7 @@ def test_build_has_no_scratch_spills():
         assert proc.returncode == 0, proc.stderr[-2000:]
         usage = build.kernel_resources(proc.stderr)
     for kernel in ("proj_valu_tiled", "proj_valu_rows", "proj_mfma", "finalize_topk", "proj_valu_fp8",
-                   "quantize_rows_fp8"):
+                   "quantize_rows_fp8", "quantize_rows_mxfp4"):
         assert any(kernel in k for k in usage), kernel
     spills = {k: v["ScratchSize"] for k, v in usage.items() if v.get("ScratchSize", 0)}
     assert not spills, spills

@@ -101,6 +101,10 @@ constexpr int kValuMaxM = 8;
 // head the draining loop is best for M = 2..4 and the unconditional one for
 // M = 1 (174.6 against 177.7 us); on shortlists of 16k-53k rows the ring
 // is 3-16% faster than either (the ramp and tail dominate there).
+// Weight formats of the matrix-core kernel (template parameter FMT).
+constexpr int kFmtBf16 = 0;  // bf16 head
+constexpr int kFmtFp8 = 1;   // E4M3 codes, one fp32 scale per row
+constexpr int kFmtMx4 = 2;   // MXFP4: E2M1 codes, one E8M0 scale per 32 elements
 constexpr int kLoopPair = 0;
 constexpr int kLoopUncond = 1;
 constexpr int kLoopRing = 2;
@@ -166,6 +170,33 @@ __device__ __forceinline__ u32x4 fp8x8_to_bf16x8(uint32_t lo, uint32_t hi) {
   const bf16x2 d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, true);
   return u32x4{__builtin_bit_cast(uint32_t, a), __builtin_bit_cast(uint32_t, b), __builtin_bit_cast(uint32_t, c),
                __builtin_bit_cast(uint32_t, d)};
+}
+
+// Eight E2M1 codes (the nibbles of `packed`, element 2i in the low nibble of
+// byte i) as eight bf16 values times the block scale 2^(e - 127), e the
+// block's E8M0 code.  The gfx950 conversion multiplies by an fp32 scale;
+// every E2M1 value times a power of two in bf16 range is a bf16 number, so
+// the result is exact.  Code 0 is 2^-127 (an fp32 subnormal).
+__device__ __forceinline__ u32x4 fp4x8_to_bf16x8(uint32_t packed, uint32_t e) {
+  const float sc = __builtin_bit_cast(float, e != 0u ? e << 23 : 0x00400000u);
+  const bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(packed, sc, 0);
+  const bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(packed, sc, 1);
+  const bf16x2 c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(packed, sc, 2);
+  const bf16x2 d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(packed, sc, 3);
+  return u32x4{__builtin_bit_cast(uint32_t, a), __builtin_bit_cast(uint32_t, b), __builtin_bit_cast(uint32_t, c),
+               __builtin_bit_cast(uint32_t, d)};
+}
+
+// E2M1 code (OCP MX FP4: bias 1, 1 mantissa bit, subnormal 0.5) of an
+// fp32 value: the magnitude is the number of rounding thresholds it
+// passes, the midpoints between neighbouring values 0, 0.5, 1, 1.5, 2, 3, 4,
+// 6, strict where the upper neighbour's code is odd (a tie goes to the even
+// code) and inclusive where it is even; 6 and above saturate to code 7.
+__device__ __forceinline__ uint32_t e2m1_encode(float q) {
+  const float a = __builtin_fabsf(q);
+  const uint32_t mag = (uint32_t)(a > 0.25f) + (uint32_t)(a >= 0.75f) + (uint32_t)(a > 1.25f) +
+                       (uint32_t)(a >= 1.75f) + (uint32_t)(a > 2.5f) + (uint32_t)(a >= 3.5f) + (uint32_t)(a > 5.0f);
+  return ((__builtin_bit_cast(uint32_t, q) >> 28) & 0x8u) | mag;
 }
 
 // E4M3 code of an fp32 value (OCP FP8 E4M3: bias 7, 3 mantissa bits,
@@ -749,6 +780,50 @@ quantize_rows_fp8(const uint16_t* __restrict__ W, int R, int K, uint8_t* __restr
         }
         out[c] = uint2{b[0], b[1]};
       }
+    }
+  }
+}
+
+// MXFP4 copy of a bf16 head, one wave per row, one 32-element block per lane
+// at a time: the block's scale exponent s = floor(log2 amax) - 2 (2 is the
+// exponent of the largest E2M1 value, 6 = 1.5 x 2^2), clamped to the E8M0
+// range, 0 for a block of zeros; its elements scaled by 2^-s (exact) and
+// encoded to the nearest E2M1 code, ties to the even code, saturating at 6.
+// Codes are packed two per byte, element 2i in the low nibble of byte i;
+// the block's 16 code bytes are one 16-byte store, its scale code one byte.
+__global__ void __launch_bounds__(256)
+quantize_rows_mxfp4(const uint16_t* __restrict__ W, int R, int K, uint8_t* __restrict__ Wq,
+                    uint8_t* __restrict__ scales) {
+  const int lane = threadIdx.x & 63;
+  const int blocks = K >> 5;
+  const int nwaves = gridDim.x * 4;
+  for (int r = blockIdx.x * 4 + wave_id(); r < R; r += nwaves) {
+    const u32x4* row = reinterpret_cast<const u32x4*>(W + (size_t)r * K);
+    for (int blk = lane; blk < blocks; blk += 64) {
+      float x[32];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const u32x4 v = row[blk * 4 + j];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          x[8 * j + 2 * e] = __builtin_bit_cast(float, v[e] << 16);
+          x[8 * j + 2 * e + 1] = __builtin_bit_cast(float, v[e] & 0xFFFF0000u);
+        }
+      }
+      float amax = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 32; ++i) amax = __builtin_fmaxf(amax, __builtin_fabsf(x[i]));
+      int s = 0;
+      if (amax > 0.0f) {
+        int ex = 0;
+        (void)__builtin_frexpf(amax, &ex);  // amax = f * 2^ex, f in [0.5, 1)
+        s = min(127, max(-127, ex - 1 - 2));
+      }
+      uint32_t packed[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int i = 0; i < 32; ++i) packed[i >> 3] |= e2m1_encode(__builtin_ldexpf(x[i], -s)) << (4 * (i & 7));
+      reinterpret_cast<u32x4*>(Wq + (size_t)r * (K >> 1))[blk] = u32x4{packed[0], packed[1], packed[2], packed[3]};
+      scales[(size_t)r * blocks + blk] = (uint8_t)(s + 127);
     }
   }
 }
@@ -1361,15 +1436,24 @@ proj_valu_fp8(const uint16_t* __restrict__ h, const uint8_t* __restrict__ W, con
 // (past the row end, or for a row whose id is outside [0, nw), they read
 // row 0 and the values are dropped).  A 16-bit mask of the rows that take
 // part travels with the tile in a short history until the tile finishes.
-template <int NT, int SB, int WV, int D, int TK, bool LOGITS, bool FP8, bool IDX = false>
+//
+// FMT selects the head's format.  A k-step is 32 head-row elements: four
+// 16-byte chunks of bf16; two of E4M3 codes (kFmtFp8: codes become bf16
+// when read from the stage, and a row's sum is multiplied by its fp32
+// scale); or one of E2M1 codes (kFmtMx4: one E8M0 scale per k-step and row;
+// each batch also loads the 16 scale bytes of each of its 16 rows, staged
+// beside the codes, and the codes become bf16 times the scale, exactly).
+template <int NT, int SB, int WV, int D, int TK, bool LOGITS, int FMT, bool IDX = false>
 __global__ void __launch_bounds__(64 * WV)
-proj_mfma(const uint16_t* __restrict__ h, const void* __restrict__ Wv, const float* __restrict__ wscale, int R,
+proj_mfma(const uint16_t* __restrict__ h, const void* __restrict__ Wv, const void* __restrict__ wsc, int R,
           int K, int m_base, int mp, Epi epi) {
-  static_assert(!IDX || (TK == 1 && !LOGITS && !FP8), "indexed rows: bf16 argmax epilogue");
-  // A k-step is 32 head-row elements: four 16-byte chunks of bf16, or two of
-  // E4M3 codes (FP8: codes become bf16 when read from the stage, and a
-  // row's sum is multiplied by its fp32 scale).
-  constexpr int CPS = FP8 ? 2 : 4;  // 16-byte chunks per k-step
+  constexpr bool FP8 = FMT == kFmtFp8;
+  constexpr bool MX4 = FMT == kFmtMx4;
+  static_assert(!IDX || (TK == 1 && !LOGITS && FMT == kFmtBf16), "indexed rows: bf16 argmax epilogue");
+  static_assert(!MX4 || SB == 16, "MXFP4: a batch is 16 k-steps, one scale chunk per row");
+  const float* wscale = static_cast<const float*>(wsc);     // FP8: [R] fp32
+  const uint8_t* mxscale = static_cast<const uint8_t*>(wsc);  // MX4: [R, K / 32] E8M0 codes
+  constexpr int CPS = FP8 ? 2 : (MX4 ? 1 : 4);  // 16-byte chunks per k-step
   constexpr int BC = CPS * SB;      // 16-byte chunks per row per batch
   static_assert(BC == 16 || BC == 32 || BC == 64, "a load instruction covers whole row pieces");
   constexpr int SC = BC + 1;        // stage row stride in chunks (padded against bank conflicts)
@@ -1383,7 +1467,7 @@ proj_mfma(const uint16_t* __restrict__ h, const void* __restrict__ Wv, const flo
   const int i16 = lane & 15;
   const int g = lane >> 4;
   const int chunks = K >> 3;                         // 16-byte chunks of a hidden row
-  const int wchunks = FP8 ? (K >> 4) : (K >> 3);     // 16-byte chunks of a head row
+  const int wchunks = FP8 ? (K >> 4) : (MX4 ? (K >> 5) : (K >> 3));  // 16-byte chunks of a head row
   const int steps = (K + 31) >> 5;
   const int s4 = steps * 4;
   const int row_chunks = s4 + 1;
@@ -1398,6 +1482,8 @@ proj_mfma(const uint16_t* __restrict__ h, const void* __restrict__ Wv, const flo
   __syncthreads();
 
   u32x4* stage = lds + mp * row_chunks + wave * 16 * SC;
+  // MX4: this wave's scale stage, one 16-byte chunk (16 k-steps) per row
+  u32x4* sstage = lds + mp * row_chunks + WV * 16 * SC + wave * 16;
   const u32x4* bptr[NT];
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
@@ -1431,7 +1517,8 @@ proj_mfma(const uint16_t* __restrict__ h, const void* __restrict__ Wv, const flo
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  const uint32_t row_bytes = FP8 ? (uint32_t)K : (uint32_t)K * 2u;
+  const uint32_t row_bytes = FP8 ? (uint32_t)K : (MX4 ? (uint32_t)K / 2u : (uint32_t)K * 2u);
+  const uint32_t sc_row_bytes = (uint32_t)K / 32u;  // MX4: scale bytes per row
   const int ntiles = (R + 15) >> 4;
   const int nbatch = (steps + SB - 1) / SB;
   const int lrow = lane / BC;  // row of this lane within a load instruction
@@ -1499,7 +1586,7 @@ proj_mfma(const uint16_t* __restrict__ h, const void* __restrict__ Wv, const flo
 
   // Positions past the last tile get a descriptor with no records, so their
   // loads read zero without touching memory (live is clamped at 0).
-  auto issue = [&](u32x4 (&buf)[LPB], int tile, int b) {
+  auto issue = [&](u32x4 (&buf)[LPB], u32x4& sbuf, int tile, int b) {
     if constexpr (IDX) {
       if (b == 0) start_issue_tile(tile);
       const int cg = b * BC + lc;
@@ -1519,12 +1606,25 @@ proj_mfma(const uint16_t* __restrict__ h, const void* __restrict__ Wv, const flo
     const uint32_t cbase = cg < wchunks ? (uint32_t)cg * 16u : kOobOffset;
 #pragma unroll
     for (int q = 0; q < LPB; ++q) buf[q] = load16<kPolicyStream>(rs, cbase + rowoff[q]);
+    if constexpr (MX4) {
+      // lane i16 of the first 16 lanes: scale bytes of k-steps b*16 .. b*16 + 15 of row i16
+      const __amdgpu_buffer_rsrc_t ss =
+          make_rsrc(mxscale + (size_t)r0 * sc_row_bytes, (uint32_t)live * sc_row_bytes);
+      const uint32_t soff = g == 0 ? (uint32_t)i16 * sc_row_bytes + (uint32_t)b * 16u : kOobOffset;
+      sbuf = load16<kPolicyStream>(ss, soff);
+    } else {
+      (void)sbuf;
+    }
   };
   // A operand of k-step sb of the staged batch: 8 elements of row i16
   auto a_operand = [&](int sb) -> u32x4 {
     if constexpr (FP8) {
       const uint2 raw = reinterpret_cast<const uint2*>(stage)[(i16 * SC + 2 * sb) * 2 + g];
       return fp8x8_to_bf16x8(raw.x, raw.y);
+    } else if constexpr (MX4) {
+      const uint32_t codes = reinterpret_cast<const uint32_t*>(stage)[(i16 * SC + sb) * 4 + g];
+      const uint32_t e = reinterpret_cast<const uint8_t*>(sstage)[i16 * 16 + sb];
+      return fp4x8_to_bf16x8(codes, e);
     } else {
       return stage[i16 * SC + 4 * sb + g];
     }
@@ -1537,22 +1637,31 @@ proj_mfma(const uint16_t* __restrict__ h, const void* __restrict__ Wv, const flo
                                                         __builtin_bit_cast(bf16x8, bf), acc[nt], 0, 0, 0);
     }
   };
-  auto consume = [&](const u32x4 (&buf)[LPB], int b) {
+  auto consume = [&](const u32x4 (&buf)[LPB], const u32x4& sbuf, int b) {
     // IDX: chunks past the row end were loaded from column 0; zero them
     const bool in_row = !IDX || b * BC + lc < wchunks;
 #pragma unroll
     for (int q = 0; q < LPB; ++q) stage[(q * RPI + lrow) * SC + lc] = in_row ? buf[q] : u32x4{0u, 0u, 0u, 0u};
+    if constexpr (MX4) {
+      if (g == 0) sstage[i16] = sbuf;
+    }
     // lanes of this wave exchange data through the stage
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    if ((b + 1) * SB <= steps) {
-      // whole batch: all operand reads first, then the matrix instructions
-      u32x4 a[SB];
+    if (MX4 || (b + 1) * SB <= steps) {  // MXFP4 heads hold whole batches (K % 512 == 0)
+      // whole batch: operand reads first, then the matrix instructions, in
+      // groups of CH k-steps (MXFP4's 16 k-steps at once would not fit the
+      // registers)
+      constexpr int CH = MX4 ? 4 : SB;
 #pragma unroll
-      for (int sb = 0; sb < SB; ++sb) a[sb] = a_operand(sb);
+      for (int c0 = 0; c0 < SB; c0 += CH) {
+        u32x4 a[CH];
 #pragma unroll
-      for (int sb = 0; sb < SB; ++sb) mma_step(a[sb], b * SB + sb);
+        for (int sb = 0; sb < CH; ++sb) a[sb] = a_operand(c0 + sb);
+#pragma unroll
+        for (int sb = 0; sb < CH; ++sb) mma_step(a[sb], b * SB + c0 + sb);
+      }
     } else {
 #pragma unroll
       for (int sb = 0; sb < SB; ++sb) {
@@ -1644,18 +1753,19 @@ proj_mfma(const uint16_t* __restrict__ h, const void* __restrict__ Wv, const flo
   const int my_tiles = tc < ntiles ? (ntiles - 1 - tc) / tstride + 1 : 0;
   const int count = my_tiles * nbatch;
   u32x4 ring[D][LPB];
+  u32x4 sring[D];  // MX4: the scale chunk of each batch in flight
   load_scales(ti);
   fetch_tile_ids(ti);
 #pragma unroll
   for (int j = 0; j < D - 1; ++j) {
-    issue(ring[j], ti, bi);
+    issue(ring[j], sring[j], ti, bi);
     advance(ti, bi);
   }
   auto step = [&](auto jc) __attribute__((always_inline)) {
     constexpr int j = decltype(jc)::value;
-    issue(ring[(j + D - 1) % D], ti, bi);
+    issue(ring[(j + D - 1) % D], sring[(j + D - 1) % D], ti, bi);
     advance(ti, bi);
-    consume(ring[j], bc);
+    consume(ring[j], sring[j], bc);
     if (bc == nbatch - 1) finish_tile(tc);
     advance(tc, bc);
   };
@@ -1962,11 +2072,17 @@ int launch_valu(const ValuPlan& p, const uint16_t* h, int K, const uint16_t* W, 
                            stream, "launch VALU projection", grid_out, h, W, R, K, epi);
 }
 
+// LDS of the per-wave stages of the matrix-core kernel: a 16-row code
+// stage (and for MXFP4 a 16-chunk scale stage) per wave.
+size_t mfma_stage_bytes(int waves, int fmt) {
+  return (size_t)waves * 16 * (4 * LMH_MFMA_LDS_SB + 1) * 16 + (fmt == kFmtMx4 ? (size_t)waves * 16 * 16 : 0);
+}
+
 // Hidden rows one launch of the matrix-core kernel can stage for K with
-// `waves` waves (each with its own 16-row stage); the static key array of
-// the argmax epilogue is counted too.
-int mfma_lds_rows_fit(int64_t K, int waves) {
-  const int64_t stage = (int64_t)waves * 16 * (4 * LMH_MFMA_LDS_SB + 1) * 16;
+// `waves` waves (each with its own stages); the static key array of the
+// argmax epilogue is counted too.
+int mfma_lds_rows_fit(int64_t K, int waves, int fmt = kFmtBf16) {
+  const int64_t stage = (int64_t)mfma_stage_bytes(waves, fmt);
   const int64_t fixed = stage + (int64_t)waves * 32 * 8 + 512;
   const int64_t rows = (kLdsPerWorkgroup - fixed) / mfma_row_bytes(K);
   return (int)std::max<int64_t>(0, std::min<int64_t>(LMH_MAX_M, rows));
@@ -1975,26 +2091,28 @@ int mfma_lds_rows_fit(int64_t K, int waves) {
 // One pass of the matrix-core path over hidden rows [m_base, m_base + mp):
 // 8 waves per workgroup when the hidden rows and eight stages fit the LDS,
 // else 4; two 16-column tiles when mp > 16.
-// FP8 heads take twice the k-steps per batch, so a batch moves the same
-// bytes (and the stage has the same size) as for bf16.
-template <int TK, bool LOGITS, bool FP8, bool IDX = false>
-int launch_mfma_pass(const uint16_t* h, int K, int m_base, int mp, const void* W, const float* wscale, int R,
+// FP8 heads take twice the k-steps per batch and MXFP4 heads four times, so
+// a batch moves the same code bytes (and the stage has the same size) as for
+// bf16.  `wsc` is the FP8 row scales or the MXFP4 block scales.
+template <int TK, bool LOGITS, int FMT, bool IDX = false>
+int launch_mfma_pass(const uint16_t* h, int K, int m_base, int mp, const void* W, const void* wsc, int R,
                      const Epi& epi, int cus, hipStream_t stream, int* grid_out) {
-  constexpr int SB = FP8 ? 2 * LMH_MFMA_LDS_SB : LMH_MFMA_LDS_SB;
+  constexpr int SB = FMT == kFmtFp8 ? 2 * LMH_MFMA_LDS_SB : (FMT == kFmtMx4 ? 4 * LMH_MFMA_LDS_SB : LMH_MFMA_LDS_SB);
   constexpr int D = LMH_MFMA_RING;
+  const void* wscale = wsc;
   const size_t hbytes = (size_t)mp * mfma_row_bytes(K);
   const int64_t tiles = (R + 15) / 16;
-  const bool eight = mp <= mfma_lds_rows_fit(K, 8);
-  const size_t lds = hbytes + (size_t)(eight ? 8 : 4) * 16 * (4 * LMH_MFMA_LDS_SB + 1) * 16;
+  const bool eight = mp <= mfma_lds_rows_fit(K, 8, FMT);
+  const size_t lds = hbytes + mfma_stage_bytes(eight ? 8 : 4, FMT);
   const char* what = "launch matrix-core projection";
   if (mp <= 16)
-    return eight ? launch_persistent(proj_mfma<1, SB, 8, D, TK, LOGITS, FP8, IDX>, 512, lds, tiles, 8, 1 << 20, cus,
+    return eight ? launch_persistent(proj_mfma<1, SB, 8, D, TK, LOGITS, FMT, IDX>, 512, lds, tiles, 8, 1 << 20, cus,
                                      stream, what, grid_out, h, W, wscale, R, K, m_base, mp, epi)
-                 : launch_persistent(proj_mfma<1, SB, 4, D, TK, LOGITS, FP8, IDX>, 256, lds, tiles, 4, 1 << 20, cus,
+                 : launch_persistent(proj_mfma<1, SB, 4, D, TK, LOGITS, FMT, IDX>, 256, lds, tiles, 4, 1 << 20, cus,
                                      stream, what, grid_out, h, W, wscale, R, K, m_base, mp, epi);
-  return eight ? launch_persistent(proj_mfma<2, SB, 8, D, TK, LOGITS, FP8, IDX>, 512, lds, tiles, 8, 1 << 20, cus,
+  return eight ? launch_persistent(proj_mfma<2, SB, 8, D, TK, LOGITS, FMT, IDX>, 512, lds, tiles, 8, 1 << 20, cus,
                                    stream, what, grid_out, h, W, wscale, R, K, m_base, mp, epi)
-               : launch_persistent(proj_mfma<2, SB, 4, D, TK, LOGITS, FP8, IDX>, 256, lds, tiles, 4, 1 << 20, cus,
+               : launch_persistent(proj_mfma<2, SB, 4, D, TK, LOGITS, FMT, IDX>, 256, lds, tiles, 4, 1 << 20, cus,
                                    stream, what, grid_out, h, W, wscale, R, K, m_base, mp, epi);
 }
 
@@ -2036,8 +2154,9 @@ int launch_finalize_topk(unsigned long long* slots, int nslots, int m_base, int 
   return e == hipSuccess ? LMH_OK : hip_fail(e, "launch finalize_topk");
 }
 
-// What one call asks for.  With `wscale` set, W holds E4M3 codes and
-// wscale one fp32 scale per row (argmax only).
+// What one call asks for.  `fmt` is the head's format: bf16, or (argmax
+// only) E4M3 codes with one fp32 scale per row in `wscale`, or MXFP4 codes
+// with one E8M0 scale per 32 elements in `wscale`.
 struct Call {
   const uint16_t* h;
   int M;
@@ -2048,7 +2167,8 @@ struct Call {
   int path;
   hipStream_t stream;
   bool projection_only = false;  // measurement: skip the fold (outputs untouched)
-  const float* wscale = nullptr;
+  const void* wscale = nullptr;
+  int fmt = kFmtBf16;
   bool indexed = false;          // W is the whole head, read through epi.rowmap (argmax only)
 };
 
@@ -2074,15 +2194,18 @@ int run(const Call& c, const Epi& epi, int topk, int32_t* out_id, float* out_log
     else
       return LMH_OK;
   };
-  const bool fp8 = c.wscale != nullptr;
-  if (fp8 && MODE != 0) return LMH_EINVAL;
+  const bool fp8 = c.fmt == kFmtFp8;
+  const bool mx4 = c.fmt == kFmtMx4;
+  if ((fp8 || mx4) && MODE != 0) return LMH_EINVAL;
+  if ((fp8 || mx4) && !c.wscale) return LMH_EINVAL;
   constexpr bool kIdxOk = MODE == 0 && TK == 1;
-  if (c.indexed && (!kIdxOk || fp8 || !epi.rowmap)) return LMH_EINVAL;
+  if (c.indexed && (!kIdxOk || c.fmt != kFmtBf16 || !epi.rowmap)) return LMH_EINVAL;
   if (c.path == LMH_PATH_VALU) {
     int grid = 0;
+    if (mx4) return LMH_EINVAL;  // MXFP4 heads take the matrix cores only
     if (fp8) {
-      st = launch_valu_fp8(c.h, c.M, c.K, static_cast<const uint8_t*>(c.W), c.wscale, c.R, epi, cus, c.stream,
-                           &grid);
+      st = launch_valu_fp8(c.h, c.M, c.K, static_cast<const uint8_t*>(c.W), static_cast<const float*>(c.wscale),
+                           c.R, epi, cus, c.stream, &grid);
     } else {
       ValuPlan p;
       if constexpr (kIdxOk)
@@ -2095,7 +2218,7 @@ int run(const Call& c, const Epi& epi, int topk, int32_t* out_id, float* out_log
     if (st != LMH_OK) return st;
     return finalize(grid, 0, c.M);
   }
-  const int cap = mfma_lds_rows_fit(c.K, 4);
+  const int cap = mfma_lds_rows_fit(c.K, 4, c.fmt);
   if (cap < 1) return LMH_EINVAL;
   const int passes = (c.M + cap - 1) / cap;
   const int per = (c.M + passes - 1) / passes;
@@ -2103,18 +2226,17 @@ int run(const Call& c, const Epi& epi, int topk, int32_t* out_id, float* out_log
     const int mp = std::min(per, c.M - m0);
     int grid = 0;
     if constexpr (kIdxOk) {
-      st = fp8 ? launch_mfma_pass<TK, LOGITS, true>(c.h, c.K, m0, mp, c.W, c.wscale, c.R, epi, cus, c.stream, &grid)
-           : c.indexed
-               ? launch_mfma_pass<TK, LOGITS, false, true>(c.h, c.K, m0, mp, c.W, nullptr, c.R, epi, cus, c.stream,
-                                                           &grid)
-               : launch_mfma_pass<TK, LOGITS, false>(c.h, c.K, m0, mp, c.W, nullptr, c.R, epi, cus, c.stream,
-                                                     &grid);
-    } else if constexpr (MODE == 0) {
-      st = fp8 ? launch_mfma_pass<TK, LOGITS, true>(c.h, c.K, m0, mp, c.W, c.wscale, c.R, epi, cus, c.stream, &grid)
-               : launch_mfma_pass<TK, LOGITS, false>(c.h, c.K, m0, mp, c.W, nullptr, c.R, epi, cus, c.stream,
-                                                     &grid);
+      if (fp8)
+        st = launch_mfma_pass<TK, LOGITS, kFmtFp8>(c.h, c.K, m0, mp, c.W, c.wscale, c.R, epi, cus, c.stream, &grid);
+      else if (mx4)
+        st = launch_mfma_pass<TK, LOGITS, kFmtMx4>(c.h, c.K, m0, mp, c.W, c.wscale, c.R, epi, cus, c.stream, &grid);
+      else if (c.indexed)
+        st = launch_mfma_pass<TK, LOGITS, kFmtBf16, true>(c.h, c.K, m0, mp, c.W, nullptr, c.R, epi, cus, c.stream,
+                                                          &grid);
+      else
+        st = launch_mfma_pass<TK, LOGITS, kFmtBf16>(c.h, c.K, m0, mp, c.W, nullptr, c.R, epi, cus, c.stream, &grid);
     } else {
-      st = launch_mfma_pass<TK, LOGITS, false>(c.h, c.K, m0, mp, c.W, nullptr, c.R, epi, cus, c.stream, &grid);
+      st = launch_mfma_pass<TK, LOGITS, kFmtBf16>(c.h, c.K, m0, mp, c.W, nullptr, c.R, epi, cus, c.stream, &grid);
     }
     if (st != LMH_OK) return st;
     st = finalize(grid, m0, mp);
@@ -2156,9 +2278,25 @@ int check_fp8(const uint16_t* h, int64_t M, int64_t K, const uint8_t* Wq, const 
   return LMH_OK;
 }
 
+// Checks for a call over an MXFP4 head: as check_common, plus K a multiple
+// of 512 (a batch of the matrix-core kernel is 512 elements, and the scale
+// row is a whole number of 16-byte chunks) and a 16-byte aligned scale
+// array.  The matrix cores take every M.
+int check_mx4(const uint16_t* h, int64_t M, int64_t K, const uint8_t* Wq, const uint8_t* scales, int64_t R,
+              int* path) {
+  if (!h || !Wq || !scales) return LMH_EINVAL;
+  if (M < 1 || M > LMH_MAX_M || !k_ok(K) || (K % 512) != 0) return LMH_EINVAL;
+  if (R < 1 || R > kMaxRows) return LMH_EINVAL;
+  if (!aligned16(h) || !aligned16(Wq) || !aligned16(scales)) return LMH_EINVAL;
+  if (*path != LMH_PATH_AUTO && *path != LMH_PATH_MFMA) return LMH_EINVAL;
+  *path = LMH_PATH_MFMA;
+  return LMH_OK;
+}
+
 // Mean projection-kernel time over `calls` back-to-back launches between two
 // events, then one whole call so the outputs hold a result (bench helpers).
-int time_projection(Call c, int nheads, const void* const* heads, const float* const* scales, const Epi& epi,
+// `scales[i]` goes with `heads[i]` for FP8 and MXFP4 heads.
+int time_projection(Call c, int nheads, const void* const* heads, const void* const* scales, const Epi& epi,
                     int32_t* out_id, float* out_logit, int calls, double* proj_ms) {
   hipEvent_t ev[2] = {nullptr, nullptr};
   int st = LMH_OK;
@@ -2171,7 +2309,7 @@ int time_projection(Call c, int nheads, const void* const* heads, const float* c
     }
   }
   // single-pass shapes only: the events must bracket projection kernels alone
-  const int cap = mfma_lds_rows_fit(c.K, 4);
+  const int cap = mfma_lds_rows_fit(c.K, 4, c.fmt);
   if (st == LMH_OK && c.path == LMH_PATH_MFMA && (cap < 1 || c.M > cap)) st = LMH_EINVAL;
   if (st == LMH_OK) st = record(ev[0], c.stream);
   for (int i = 0; i < calls && st == LMH_OK; ++i) {
@@ -2389,6 +2527,36 @@ int draft_project_argmax_fp8(const uint16_t* h, int64_t M, int64_t K, const uint
   if (workspace_bytes < draft_project_workspace_bytes(M)) return LMH_EWORKSPACE;
   Call c{h, (int)M, (int)K, Wq, (int)R, d2t, path, static_cast<hipStream_t>(stream)};
   c.wscale = scale;
+  c.fmt = kFmtFp8;
+  const Epi epi{static_cast<unsigned long long*>(workspace), nullptr, nullptr, 0, 0};
+  return run<0, 1>(c, epi, 1, out_id, out_logit);
+}
+
+int lmhead_quantize_mxfp4(const uint16_t* W, int64_t R, int64_t K, uint8_t* Wq, uint8_t* scales, void* stream) {
+  if (R < 0 || R > kMaxRows || !k_ok(K) || (K % 32) != 0) return LMH_EINVAL;
+  if (R == 0) return LMH_OK;
+  if (!W || !Wq || !scales || !aligned16(W) || !aligned16(Wq)) return LMH_EINVAL;
+  int cus = 0;
+  const int st = cu_count(&cus);
+  if (st != LMH_OK) return st;
+  const int grid = (int)std::max<int64_t>(1, std::min<int64_t>((R + 3) / 4, (int64_t)cus * 16));
+  hipLaunchKernelGGL(quantize_rows_mxfp4, dim3(grid), dim3(256), 0, static_cast<hipStream_t>(stream), W, (int)R,
+                     (int)K, Wq, scales);
+  const hipError_t e = hipGetLastError();
+  return e == hipSuccess ? LMH_OK : hip_fail(e, "launch quantize_rows_mxfp4");
+}
+
+int draft_project_argmax_mxfp4(const uint16_t* h, int64_t M, int64_t K, const uint8_t* Wq, const uint8_t* scales,
+                               int64_t R, const int32_t* d2t, int32_t* out_id, float* out_logit, void* workspace,
+                               size_t workspace_bytes, int path, void* stream) {
+  int st = check_mx4(h, M, K, Wq, scales, R, &path);
+  if (st != LMH_OK) return st;
+  if (!out_id || !out_logit) return LMH_EINVAL;
+  if (!workspace || !aligned16(workspace)) return LMH_EWORKSPACE;
+  if (workspace_bytes < draft_project_workspace_bytes(M)) return LMH_EWORKSPACE;
+  Call c{h, (int)M, (int)K, Wq, (int)R, d2t, path, static_cast<hipStream_t>(stream)};
+  c.wscale = scales;
+  c.fmt = kFmtMx4;
   const Epi epi{static_cast<unsigned long long*>(workspace), nullptr, nullptr, 0, 0};
   return run<0, 1>(c, epi, 1, out_id, out_logit);
 }
@@ -2457,9 +2625,32 @@ int lmhead_bench_time_argmax_fp8(const uint16_t* h, int64_t M, int64_t K, const 
   if (workspace_bytes < draft_project_workspace_bytes(M)) return LMH_EWORKSPACE;
   Call c{h, (int)M, (int)K, heads[0], (int)R, d2t, path, static_cast<hipStream_t>(stream)};
   c.wscale = scales[0];
+  c.fmt = kFmtFp8;
   const Epi epi{static_cast<unsigned long long*>(workspace), nullptr, nullptr, 0, 0};
-  return time_projection(c, nheads, reinterpret_cast<const void* const*>(heads), scales, epi, out_id, out_logit,
-                         calls, proj_ms);
+  return time_projection(c, nheads, reinterpret_cast<const void* const*>(heads),
+                         reinterpret_cast<const void* const*>(scales), epi, out_id, out_logit, calls, proj_ms);
+}
+
+int lmhead_bench_time_argmax_mxfp4(const uint16_t* h, int64_t M, int64_t K, const uint8_t* const* heads,
+                                   const uint8_t* const* scales, int nheads, int64_t R, const int32_t* d2t,
+                                   int32_t* out_id, float* out_logit, void* workspace, size_t workspace_bytes,
+                                   int path, int calls, double* proj_ms, void* stream) {
+  if (!heads || !scales || nheads < 1 || calls < 1 || !proj_ms) return LMH_EINVAL;
+  const int path_in = path;
+  int st = LMH_OK;
+  for (int i = 0; i < nheads; ++i) {
+    path = path_in;
+    if ((st = check_mx4(h, M, K, heads[i], scales[i], R, &path)) != LMH_OK) return st;
+  }
+  if (!out_id || !out_logit) return LMH_EINVAL;
+  if (!workspace || !aligned16(workspace)) return LMH_EWORKSPACE;
+  if (workspace_bytes < draft_project_workspace_bytes(M)) return LMH_EWORKSPACE;
+  Call c{h, (int)M, (int)K, heads[0], (int)R, d2t, path, static_cast<hipStream_t>(stream)};
+  c.wscale = scales[0];
+  c.fmt = kFmtMx4;
+  const Epi epi{static_cast<unsigned long long*>(workspace), nullptr, nullptr, 0, 0};
+  return time_projection(c, nheads, reinterpret_cast<const void* const*>(heads),
+                         reinterpret_cast<const void* const*>(scales), epi, out_id, out_logit, calls, proj_ms);
 }
 
 int lmhead_bench_time_argmax_indexed(const uint16_t* h, int64_t M, int64_t K, const uint16_t* const* heads,

@@ -25,7 +25,8 @@ __all__ = [
     "lmhead_bench_time_argmax", "lmhead_quantize_fp8", "draft_project_argmax_fp8",
     "lmhead_bench_time_argmax_fp8", "lmhead_shortlist_overwrite", "lmhead_shortlist_union",
     "LMH_MAX_OVERWRITE", "LMH_MAX_UNION_VOCAB", "draft_project_argmax_indexed",
-    "lmhead_bench_time_argmax_indexed",
+    "lmhead_bench_time_argmax_indexed", "lmhead_quantize_mxfp4", "draft_project_argmax_mxfp4",
+    "lmhead_bench_time_argmax_mxfp4",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "liblmhead.so")
@@ -66,6 +67,10 @@ SIGNATURES = {
     "draft_project_argmax_indexed": (_INT, [_P, _I64, _I64, _P, _I64, _P, _I64, _P, _P, _P, _SZ, _INT, _P]),
     "lmhead_bench_time_argmax_indexed": (_INT, [_P, _I64, _I64, _P, _INT, _I64, _P, _I64, _P, _P, _P, _SZ, _INT,
                                                 _INT, ctypes.POINTER(ctypes.c_double), _P]),
+    "lmhead_quantize_mxfp4": (_INT, [_P, _I64, _I64, _P, _P, _P]),
+    "draft_project_argmax_mxfp4": (_INT, [_P, _I64, _I64, _P, _P, _I64, _P, _P, _P, _P, _SZ, _INT, _P]),
+    "lmhead_bench_time_argmax_mxfp4": (_INT, [_P, _I64, _I64, _P, _P, _INT, _I64, _P, _P, _P, _P, _SZ, _INT, _INT,
+                                              ctypes.POINTER(ctypes.c_double), _P]),
 }
 
 _lib = None
@@ -510,4 +515,87 @@ def lmhead_bench_time_argmax_indexed(h: torch.Tensor, heads: list, ids: torch.Te
         h.data_ptr(), m, k, ptrs, len(heads), n, ids.data_ptr(), ids.shape[0], out_id.data_ptr(),
         out_logit.data_ptr(), workspace.data_ptr(), workspace.numel() * workspace.element_size(), path, calls,
         ctypes.byref(out), _stream(stream, h.device)), "lmhead_bench_time_argmax_indexed")
+    return out.value
+
+
+def lmhead_quantize_mxfp4(W: torch.Tensor, out: torch.Tensor | None = None,
+                          scales: torch.Tensor | None = None, stream=None):
+    """(Wq uint8 [R, K / 2] packed E2M1 codes, scales uint8 [R, K / 32] E8M0
+    codes) of a bf16 head, one scale per 32 elements.  Queues one kernel;
+    never synchronizes."""
+    _dev_tensor(W, "W", _BF16_LIKE, 2)
+    r, k = W.shape
+    if k % 32:
+        raise ValueError("K must be a multiple of 32")
+    if out is None:
+        out = torch.empty((r, k // 2), dtype=torch.uint8, device=W.device)
+    if scales is None:
+        scales = torch.empty((r, k // 32), dtype=torch.uint8, device=W.device)
+    _dev_tensor(out, "Wq", (torch.uint8,), 2)
+    _dev_tensor(scales, "scales", (torch.uint8,), 2)
+    if tuple(out.shape) != (r, k // 2) or tuple(scales.shape) != (r, k // 32):
+        raise ValueError("Wq must be [R, K / 2] and scales [R, K / 32]")
+    _check(lib().lmhead_quantize_mxfp4(W.data_ptr(), r, k, out.data_ptr(), scales.data_ptr(),
+                                       _stream(stream, W.device)), "lmhead_quantize_mxfp4")
+    return out, scales
+
+
+def _check_mx4_head(h, Wq, scales, d2t):
+    _dev_tensor(h, "h", _BF16_LIKE, 2)
+    _dev_tensor(Wq, "Wq", (torch.uint8,), 2)
+    _dev_tensor(scales, "scales", (torch.uint8,), 2)
+    m, k = h.shape
+    r, half = Wq.shape
+    if k != 2 * half:
+        raise ValueError("Wq must be [R, K / 2] for h [M, K]")
+    if tuple(scales.shape) != (r, k // 32):
+        raise ValueError("scales must be [R, K / 32]")
+    if d2t is not None:
+        _dev_tensor(d2t, "d2t", (torch.int32,), 1)
+        if d2t.shape[0] != r:
+            raise ValueError("d2t must have one entry per row of Wq")
+    return m, k, r
+
+
+def draft_project_argmax_mxfp4(h: torch.Tensor, Wq: torch.Tensor, scales: torch.Tensor,
+                               d2t: torch.Tensor | None = None, path: int = LMH_PATH_AUTO,
+                               out_id: torch.Tensor | None = None, out_logit: torch.Tensor | None = None,
+                               workspace: torch.Tensor | None = None, stream=None):
+    """(out_id int32 [M], out_logit float32 [M]) for the best row of the
+    dequantized MXFP4 head per hidden row, mapped through d2t.  Never
+    synchronizes."""
+    m, k, r = _check_mx4_head(h, Wq, scales, d2t)
+    if out_id is None:
+        out_id = torch.empty(m, dtype=torch.int32, device=h.device)
+    if out_logit is None:
+        out_logit = torch.empty(m, dtype=torch.float32, device=h.device)
+    st = _stream(stream, h.device)
+    if workspace is None:
+        workspace = _default_workspace(h.device, st)
+    _check(lib().draft_project_argmax_mxfp4(
+        h.data_ptr(), m, k, Wq.data_ptr(), scales.data_ptr(), r,
+        d2t.data_ptr() if d2t is not None else None, out_id.data_ptr(), out_logit.data_ptr(),
+        workspace.data_ptr(), workspace.numel() * workspace.element_size(), path, st),
+        "draft_project_argmax_mxfp4")
+    return out_id, out_logit
+
+
+def lmhead_bench_time_argmax_mxfp4(h: torch.Tensor, heads: list, d2t: torch.Tensor | None, path: int,
+                                   calls: int, out_id: torch.Tensor, out_logit: torch.Tensor,
+                                   workspace: torch.Tensor, stream=None) -> float:
+    """lmhead_bench_time_argmax over MXFP4 heads: `heads` is a list of
+    (Wq, scales) pairs.  Synchronizes."""
+    m, k, r = _check_mx4_head(h, heads[0][0], heads[0][1], d2t)
+    for wq, sc in heads:
+        _check_mx4_head(h, wq, sc, d2t)
+        if wq.shape[0] != r:
+            raise ValueError("every head must have the same shape")
+    qp = (ctypes.c_void_p * len(heads))(*[wq.data_ptr() for wq, _ in heads])
+    sp = (ctypes.c_void_p * len(heads))(*[sc.data_ptr() for _, sc in heads])
+    out = ctypes.c_double(0.0)
+    _check(lib().lmhead_bench_time_argmax_mxfp4(
+        h.data_ptr(), m, k, qp, sp, len(heads), r, d2t.data_ptr() if d2t is not None else None,
+        out_id.data_ptr(), out_logit.data_ptr(), workspace.data_ptr(),
+        workspace.numel() * workspace.element_size(), path, calls, ctypes.byref(out),
+        _stream(stream, h.device)), "lmhead_bench_time_argmax_mxfp4")
     return out.value
