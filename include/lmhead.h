@@ -236,7 +236,7 @@ int draft_project_argmax_fp8(const uint16_t* h, int64_t M, int64_t K,
  * and MXFP4 is the one MI355X converts in hardware.  Rounding and scale
  * follow the MX specification's conversion:
  *   s = floor(log2(max |block|)) - 2, clamped to [-127, 127], 0 for a block
- *       of zeros; scales[r, b] = s + 127;
+ *       of zeros; the stored code is s + 127;
  *   code = the E2M1 value (0, 0.5, 1, 1.5, 2, 3, 4, 6 and negatives)
  *       nearest to W / 2^s, ties to the even code, above 6 saturating.
  * The quantized head stands for decode(code) * 2^s.
@@ -244,7 +244,13 @@ int draft_project_argmax_fp8(const uint16_t* h, int64_t M, int64_t K,
  *  W       [R, K] bf16 (device, 16-byte aligned); K a multiple of 32.
  *  Wq      [R, K / 2] uint8 (device, 16-byte aligned): two codes per byte,
  *          element 2i in the low nibble of byte i.
- *  scales  [R, K / 32] uint8 (device).
+ *  scales  lmhead_mxfp4_scale_bytes(R, K) bytes (device) in the tiled scale
+ *          layout: with nb = ceil(K / 512), the scale of row r, block j
+ *          (elements 32 j .. 32 j + 31) is byte
+ *            ((r / 16 * nb + j / 16) * 16 + r % 16) * 16 + j % 16,
+ *          so that the scales one 16-row tile needs for 512 elements are
+ *          256 contiguous bytes.  Bytes of the padding (rows R .. up to a
+ *          multiple of 16, blocks past K / 32) are not written.
  * R = 0 is a no-op.  Asynchronous on `stream`; allocates nothing.
  * Returns LMH_EINVAL for a bad shape, a null or misaligned pointer.
  */
@@ -252,16 +258,39 @@ int lmhead_quantize_mxfp4(const uint16_t* W, int64_t R, int64_t K,
                           uint8_t* Wq, uint8_t* scales, void* stream);
 
 /*
+ * lmhead_mxfp4_scale_bytes -- size in bytes of the tiled scale array of an
+ * [R, K] MXFP4 head: ceil(R / 16) * ceil(K / 512) * 256.  Host only; -1 for
+ * a bad shape (R outside [0, 2^31 - 1), K not a positive multiple of 32 up
+ * to the library's limit).
+ */
+int64_t lmhead_mxfp4_scale_bytes(int64_t R, int64_t K);
+
+/*
+ * lmhead_mxfp4_tile_scales -- row-major E8M0 block scales [R, K / 32] (the
+ * order of the MX specification, for a head quantized elsewhere) into the
+ * tiled scale layout of lmhead_quantize_mxfp4.
+ *
+ *  src     [R, K / 32] uint8 (device).
+ *  scales  lmhead_mxfp4_scale_bytes(R, K) bytes (device); padding bytes are
+ *          not written.
+ * R = 0 is a no-op.  Asynchronous on `stream`; allocates nothing.
+ * Returns LMH_EINVAL for a bad shape or a null pointer.
+ */
+int lmhead_mxfp4_tile_scales(const uint8_t* src, int64_t R, int64_t K, uint8_t* scales, void* stream);
+
+/*
  * draft_project_argmax_mxfp4 -- draft_project_argmax over an MXFP4 head
  * from lmhead_quantize_mxfp4: out_logit[m] = max_r sum_k h[m, k] *
- * decode(Wq[r, k]) * 2^(scales[r, k / 32] - 127), fp32 sums of exact
+ * decode(Wq[r, k]) * 2^(s[r, k / 32]), fp32 sums of exact
  * products (every E2M1 value times a power of two is a bf16 number); out_id
  * as for draft_project_argmax (first row among equal maxima, mapped
  * through d2t).  The head streams at 0.53 bytes per weight (codes and
  * scales).  The matrix cores take every M.
  *
- *  Wq, scales as written by lmhead_quantize_mxfp4 (R rows); K a multiple
- *             of 512; Wq and scales 16-byte aligned.
+ *  Wq, scales as written by lmhead_quantize_mxfp4 (R rows; scales in the
+ *             tiled layout, lmhead_mxfp4_scale_bytes(R, K) bytes, all of
+ *             which may be read); K a multiple of 512; Wq and scales
+ *             16-byte aligned.
  *  path       LMH_PATH_AUTO or LMH_PATH_MFMA.
  * Other arguments, workspace, synchronization and errors as for
  * draft_project_argmax_path.

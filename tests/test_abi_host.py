@@ -192,6 +192,21 @@ def test_indexed_rejects_on_host(L):
     assert t(A, 1, 2560, one, 1, 1000, C, 100, D, E, E, ws, 0, 0, ctypes.byref(out), None) == 1
 
 
+def test_mxfp4_scale_bytes_and_tiling_rejects(L):
+    lib = L.lib()
+    sb = lib.lmhead_mxfp4_scale_bytes
+    assert sb(248320, 2560) == 15520 * 5 * 256 == 248320 * 80
+    assert sb(1, 32) == 256 and sb(17, 544) == 2 * 2 * 256 and sb(0, 2560) == 0
+    assert sb(10, 48) == -1 and sb(-1, 512) == -1 and sb(10, 0) == -1
+    assert L.mxfp4_scale_shape(17, 544) == (2, 2, 16, 16)
+    t = lib.lmhead_mxfp4_tile_scales
+    assert t(A, 0, 2560, B, None) == 0                           # R = 0: no-op
+    assert t(A, 10, 48, B, None) == 1
+    assert t(None, 10, 512, B, None) == 1
+    assert t(A, 10, 512, None, None) == 1
+    assert t(A, -3, 512, B, None) == 1
+
+
 def test_mxfp4_rejects_on_host(L):
     lib = L.lib()
     q = lib.lmhead_quantize_mxfp4
@@ -271,7 +286,7 @@ def test_build_has_no_scratch_spills():
         assert proc.returncode == 0, proc.stderr[-2000:]
         usage = build.kernel_resources(proc.stderr)
     for kernel in ("proj_valu_tiled", "proj_valu_rows", "proj_mfma", "finalize_topk", "proj_valu_fp8",
-                   "quantize_rows_fp8", "quantize_rows_mxfp4"):
+                   "quantize_rows_fp8", "quantize_rows_mxfp4", "tile_mxfp4_scales"):
         assert any(kernel in k for k in usage), kernel
     spills = {k: v["ScratchSize"] for k, v in usage.items() if v.get("ScratchSize", 0)}
     assert not spills, spills

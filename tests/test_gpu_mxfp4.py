@@ -8,6 +8,11 @@ tests upload, so no expected value and no argmax input comes from the GPU.
 Rows are quantized independently: the oracle runs over row blocks in a
 thread pool, and a shortlisted head is the oracle's full-head codes at the
 listed rows.
+
+The library keeps the block scales in a tiled layout (16-row tiles, groups
+of 16 blocks, 256 bytes per tile and group); tile_scales / untile_scales
+below rearrange the oracle's row-major scales to and from it, following the
+layout the header documents.
 """
 import os
 from concurrent.futures import ThreadPoolExecutor
@@ -34,6 +39,22 @@ def L():
 
 def dev_u8(a):
     return torch.from_numpy(np.ascontiguousarray(a, dtype=np.uint8)).cuda()
+
+
+def tile_scales(sc, fill=0):
+    """Row-major scales [R, B] -> the tiled layout [ceil(R/16), ceil(B/16),
+    16, 16]: element [t, g, i, j] is the scale of row 16 t + i, block 16 g + j
+    (padding = fill)."""
+    r, nblk = sc.shape
+    t, nb = (r + 15) // 16, (nblk + 15) // 16
+    pad = np.full((t * 16, nb * 16), fill, dtype=np.uint8)
+    pad[:r, :nblk] = sc
+    return np.ascontiguousarray(pad.reshape(t, 16, nb, 16).transpose(0, 2, 1, 3))
+
+
+def untile_scales(tiled, r, nblk):
+    t, nb = tiled.shape[:2]
+    return np.ascontiguousarray(tiled.transpose(0, 2, 1, 3).reshape(t * 16, nb * 16)[:r, :nblk])
 
 
 def oracle_quantize_rows(w_bits, block=2048):
@@ -78,7 +99,7 @@ def run_and_check(L, hs, codes, scales, d2t_np, tag, q_dev=None, s_dev=None):
     stack = np.concatenate(hs)
     res = oracle.oracle_project_argmax_mxfp4(stack, codes, scales, d2t_np, keep_logits=True)
     if q_dev is None:
-        q_dev, s_dev = dev_u8(codes), dev_u8(scales)
+        q_dev, s_dev = dev_u8(codes), dev_u8(tile_scales(scales))
     d2t_dev = dev_i32(d2t_np) if d2t_np is not None else None
     for p in (L.LMH_PATH_AUTO, L.LMH_PATH_MFMA):
         ids, lgs = [], []
@@ -136,19 +157,22 @@ def test_quantize_bit_exact(L, k):
     w = _special_head(rng, k)
     q, s = gpu_quantize(L, dev_bf16(w))
     codes, scales = oracle.oracle_quantize_mxfp4(w)
-    qn, sn = q.cpu().numpy(), s.cpu().numpy()
+    qn, sn = q.cpu().numpy(), untile_scales(s.cpu().numpy(), *scales.shape)
     bad = np.nonzero((qn != codes).any(axis=1) | (sn != scales).any(axis=1))[0]
     assert bad.size == 0, f"rows differing from the oracle: {bad[:10]}"
+    # padding of the tiled array (rows up to a multiple of 16, blocks up to a
+    # multiple of 16) is left as the binding allocated it: zero
+    assert np.array_equal(s.cpu().numpy(), tile_scales(scales))
 
 
 def test_quantize_ragged_row_counts(L):
     """Row counts around the launch's rows per workgroup, K = 2,560."""
-    for r in (1, 3, 4, 5, 63, 64, 65, 1000):
+    for r in (1, 3, 4, 5, 15, 16, 17, 63, 64, 65, 1000):
         w = synth.normal_bf16(40 + r, r, 2560, 0.02)
         q, s = gpu_quantize(L, dev_bf16(w))
         codes, scales = oracle.oracle_quantize_mxfp4(w)
         assert np.array_equal(q.cpu().numpy(), codes), r
-        assert np.array_equal(s.cpu().numpy(), scales), r
+        assert np.array_equal(s.cpu().numpy(), tile_scales(scales)), r
 
 
 def test_quantize_full_head_every_row(L):
@@ -156,20 +180,46 @@ def test_quantize_full_head_every_row(L):
     codes, scales = oracle_full_head()
     q, s = gpu_quantize(L, device_weights(2))
     qn, sn = q.cpu().numpy(), s.cpu().numpy()
-    assert np.array_equal(sn, scales)
+    assert np.array_equal(untile_scales(sn, *scales.shape), scales)
     assert np.array_equal(qn, codes)
 
 
 def test_quantize_rejects_and_writes_nothing(L):
     w = dev_bf16(synth.normal_bf16(3, 10, 48, 0.02))          # K = 48 is not a multiple of 32
     q = torch.full((10, 24), 7, dtype=torch.uint8, device="cuda")
-    s = torch.full((10, 2), 3, dtype=torch.uint8, device="cuda")
+    s = torch.full((1, 1, 16, 16), 3, dtype=torch.uint8, device="cuda")
     code = L.lib().lmhead_quantize_mxfp4(w.data_ptr(), 10, 48, q.data_ptr(), s.data_ptr(), None)
     assert code == L.LMH_EINVAL
     torch.cuda.synchronize()
     assert bool((q == 7).all()) and bool((s == 3).all())
     with pytest.raises(ValueError):
         L.lmhead_quantize_mxfp4(w)
+
+
+@pytest.mark.parametrize("r,k", [(1, 32), (5, 96), (16, 512), (17, 544), (1000, 2560), (4099, 8192)])
+def test_tile_scales_matches_layout(L, r, k):
+    """lmhead_mxfp4_tile_scales puts every row-major scale at its place in
+    the tiled layout and leaves the padding alone."""
+    rng = np.random.default_rng(r * 7 + k)
+    sc = rng.integers(0, 256, size=(r, k // 32)).astype(np.uint8)
+    out = torch.full(L.mxfp4_scale_shape(r, k), 0xEE, dtype=torch.uint8, device="cuda")
+    L.lmhead_mxfp4_tile_scales(dev_u8(sc), out)
+    torch.cuda.synchronize()
+    assert np.array_equal(out.cpu().numpy(), tile_scales(sc, fill=0xEE))
+
+
+def test_tile_scales_of_oracle_quantization_drive_the_argmax(L):
+    """Scales written row-major (as the oracle writes them), tiled on the
+    GPU, give the same argmax as the quantizer's own tiled scales."""
+    w = synth.normal_bf16(61, 3001, 2560, 0.02)
+    codes, scales = oracle.oracle_quantize_mxfp4(w)
+    s_dev = L.lmhead_mxfp4_tile_scales(dev_u8(scales))
+    q_dev, s_q = gpu_quantize(L, dev_bf16(w))
+    assert torch.equal(s_dev, s_q)
+    h = dev_bf16(synth.hidden(62, 0, 5, 2560))
+    a = L.draft_project_argmax_mxfp4(h, dev_u8(codes), s_dev)
+    b = L.draft_project_argmax_mxfp4(h, q_dev, s_q)
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
 
 
 # --------------------------------------------------------------------------
@@ -200,7 +250,8 @@ def test_mxfp4_argmax_on_gpu_quantized_head(L):
     del w_dev
     codes, scales = oracle_full_head()
     codes, scales = codes[inp["ids"]], scales[inp["ids"]]
-    assert np.array_equal(q_dev.cpu().numpy(), codes) and np.array_equal(s_dev.cpu().numpy(), scales)
+    assert np.array_equal(q_dev.cpu().numpy(), codes)
+    assert np.array_equal(s_dev.cpu().numpy(), tile_scales(scales))
     hs = draws(inp["config"], 4, 2)
     run_and_check(L, hs, codes, scales, inp["ids"].astype(np.int32), "mxfp4 gpu-quantized list M=4",
                   q_dev, s_dev)
@@ -277,7 +328,7 @@ def test_mxfp4_exact_ties_first_row(L, m):
     codes, scales = oracle.oracle_quantize_mxfp4(w)
     assert np.all(scales == 127)
     res = oracle.oracle_project_argmax_mxfp4(h, codes, scales)
-    q_dev, s_dev = dev_u8(codes), dev_u8(scales)
+    q_dev, s_dev = dev_u8(codes), dev_u8(tile_scales(scales))
     for p in (L.LMH_PATH_AUTO, L.LMH_PATH_MFMA):
         i, lg = L.draft_project_argmax_mxfp4(dev_bf16(h), q_dev, s_dev, None, p)
         assert np.array_equal(i.cpu().numpy(), res.id), (p, i.cpu().numpy(), res.id)
@@ -287,7 +338,7 @@ def test_mxfp4_exact_ties_first_row(L, m):
 def test_mxfp4_repeat_bit_identical_and_rejects(L):
     w = synth.normal_bf16(155, 5000, 2560, 0.02)
     codes, scales = oracle.oracle_quantize_mxfp4(w)
-    q_dev, s_dev = dev_u8(codes), dev_u8(scales)
+    q_dev, s_dev = dev_u8(codes), dev_u8(tile_scales(scales))
     h = dev_bf16(synth.hidden(156, 0, 6, 2560))
     ws = L.new_workspace()
     a = L.draft_project_argmax_mxfp4(h, q_dev, s_dev, workspace=ws)
@@ -314,7 +365,7 @@ def test_mxfp4_repeat_bit_identical_and_rejects(L):
 def test_mxfp4_bench_helper_matches_call(L):
     w = synth.normal_bf16(255, 20000, 2560, 0.02)
     codes, scales = oracle.oracle_quantize_mxfp4(w)
-    heads = [(dev_u8(codes), dev_u8(scales)), (dev_u8(codes), dev_u8(scales))]
+    heads = [(dev_u8(codes), dev_u8(tile_scales(scales))) for _ in range(2)]
     h = dev_bf16(synth.hidden(256, 0, 4, 2560))
     ws = L.new_workspace()
     oid = torch.empty(4, dtype=torch.int32, device="cuda")

@@ -784,13 +784,37 @@ quantize_rows_fp8(const uint16_t* __restrict__ W, int R, int K, uint8_t* __restr
   }
 }
 
+// Place of the E8M0 scale of row r, block j (elements 32 j .. 32 j + 31) in
+// the tiled scale layout: rows in tiles of 16 and blocks in groups of 16
+// (one matrix-core batch), each (tile, group) a 256-byte piece of 16 rows x
+// 16 bytes, the pieces of a tile in group order and the tiles in row order.
+// With nb = ceil(blocks / 16) groups per row the array holds ceil(R / 16) x
+// nb x 256 bytes; a tile's part starts at r0 x blocks when blocks % 16 == 0.
+__device__ __forceinline__ size_t mx_scale_index(int r, int j, int blocks) {
+  const int nb = (blocks + 15) >> 4;
+  return (((size_t)(r >> 4) * nb + (j >> 4)) * 16 + (r & 15)) * 16 + (j & 15);
+}
+
+// Row-major E8M0 scales [R, blocks] into the tiled scale layout, one byte per
+// thread (a load-time conversion of scales written elsewhere).
+__global__ void __launch_bounds__(256)
+tile_mxfp4_scales(const uint8_t* __restrict__ src, int R, int blocks, uint8_t* __restrict__ dst) {
+  const int64_t n = (int64_t)R * blocks;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) {
+    const int r = (int)(i / blocks);
+    const int j = (int)(i - (int64_t)r * blocks);
+    dst[mx_scale_index(r, j, blocks)] = src[i];
+  }
+}
+
 // MXFP4 copy of a bf16 head, one wave per row, one 32-element block per lane
 // at a time: the block's scale exponent s = floor(log2 amax) - 2 (2 is the
 // exponent of the largest E2M1 value, 6 = 1.5 x 2^2), clamped to the E8M0
 // range, 0 for a block of zeros; its elements scaled by 2^-s (exact) and
 // encoded to the nearest E2M1 code, ties to the even code, saturating at 6.
 // Codes are packed two per byte, element 2i in the low nibble of byte i;
-// the block's 16 code bytes are one 16-byte store, its scale code one byte.
+// the block's 16 code bytes are one 16-byte store, its scale code one byte
+// at its place in the tiled scale layout (mx_scale_index).
 __global__ void __launch_bounds__(256)
 quantize_rows_mxfp4(const uint16_t* __restrict__ W, int R, int K, uint8_t* __restrict__ Wq,
                     uint8_t* __restrict__ scales) {
@@ -823,7 +847,7 @@ quantize_rows_mxfp4(const uint16_t* __restrict__ W, int R, int K, uint8_t* __res
 #pragma unroll
       for (int i = 0; i < 32; ++i) packed[i >> 3] |= e2m1_encode(__builtin_ldexpf(x[i], -s)) << (4 * (i & 7));
       reinterpret_cast<u32x4*>(Wq + (size_t)r * (K >> 1))[blk] = u32x4{packed[0], packed[1], packed[2], packed[3]};
-      scales[(size_t)r * blocks + blk] = (uint8_t)(s + 127);
+      scales[mx_scale_index(r, blk, blocks)] = (uint8_t)(s + 127);
     }
   }
 }
@@ -1518,7 +1542,7 @@ proj_mfma(const uint16_t* __restrict__ h, const void* __restrict__ Wv, const voi
   for (int nt = 0; nt < NT; ++nt) acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   const uint32_t row_bytes = FP8 ? (uint32_t)K : (MX4 ? (uint32_t)K / 2u : (uint32_t)K * 2u);
-  const uint32_t sc_row_bytes = (uint32_t)K / 32u;  // MX4: scale bytes per row
+  const uint32_t sc_row_bytes = (uint32_t)K / 32u;  // MX4: scale bytes per row (a tile holds 16 rows' worth)
   const int ntiles = (R + 15) >> 4;
   const int nbatch = (steps + SB - 1) / SB;
   const int lrow = lane / BC;  // row of this lane within a load instruction
@@ -1607,10 +1631,12 @@ proj_mfma(const uint16_t* __restrict__ h, const void* __restrict__ Wv, const voi
 #pragma unroll
     for (int q = 0; q < LPB; ++q) buf[q] = load16<kPolicyStream>(rs, cbase + rowoff[q]);
     if constexpr (MX4) {
-      // lane i16 of the first 16 lanes: scale bytes of k-steps b*16 .. b*16 + 15 of row i16
+      // lane i16 of the first 16 lanes: scale bytes of k-steps b*16 .. b*16 + 15
+      // of row i16, 16 bytes at (b * 16 + i16) * 16 in the tile's part of the
+      // tiled scale layout (whole 16-row tiles, so one 256-byte piece per batch)
       const __amdgpu_buffer_rsrc_t ss =
-          make_rsrc(mxscale + (size_t)r0 * sc_row_bytes, (uint32_t)live * sc_row_bytes);
-      const uint32_t soff = g == 0 ? (uint32_t)i16 * sc_row_bytes + (uint32_t)b * 16u : kOobOffset;
+          make_rsrc(mxscale + (size_t)r0 * sc_row_bytes, live > 0 ? 16u * sc_row_bytes : 0u);
+      const uint32_t soff = g == 0 && i16 < live ? ((uint32_t)b * 16u + (uint32_t)i16) * 16u : kOobOffset;
       sbuf = load16<kPolicyStream>(ss, soff);
     } else {
       (void)sbuf;
@@ -2530,6 +2556,26 @@ int draft_project_argmax_fp8(const uint16_t* h, int64_t M, int64_t K, const uint
   c.fmt = kFmtFp8;
   const Epi epi{static_cast<unsigned long long*>(workspace), nullptr, nullptr, 0, 0};
   return run<0, 1>(c, epi, 1, out_id, out_logit);
+}
+
+int64_t lmhead_mxfp4_scale_bytes(int64_t R, int64_t K) {
+  if (R < 0 || R > kMaxRows || !k_ok(K) || (K % 32) != 0) return -1;
+  return (R + 15) / 16 * ((K / 32 + 15) / 16) * 256;
+}
+
+int lmhead_mxfp4_tile_scales(const uint8_t* src, int64_t R, int64_t K, uint8_t* scales, void* stream) {
+  if (R < 0 || R > kMaxRows || !k_ok(K) || (K % 32) != 0) return LMH_EINVAL;
+  if (R == 0) return LMH_OK;
+  if (!src || !scales) return LMH_EINVAL;
+  int cus = 0;
+  const int st = cu_count(&cus);
+  if (st != LMH_OK) return st;
+  const int64_t n = R * (K / 32);
+  const int grid = (int)std::max<int64_t>(1, std::min<int64_t>((n + 255) / 256, (int64_t)cus * 16));
+  hipLaunchKernelGGL(tile_mxfp4_scales, dim3(grid), dim3(256), 0, static_cast<hipStream_t>(stream), src, (int)R,
+                     (int)(K / 32), scales);
+  const hipError_t e = hipGetLastError();
+  return e == hipSuccess ? LMH_OK : hip_fail(e, "launch tile_mxfp4_scales");
 }
 
 int lmhead_quantize_mxfp4(const uint16_t* W, int64_t R, int64_t K, uint8_t* Wq, uint8_t* scales, void* stream) {

@@ -26,7 +26,8 @@ __all__ = [
     "lmhead_bench_time_argmax_fp8", "lmhead_shortlist_overwrite", "lmhead_shortlist_union",
     "LMH_MAX_OVERWRITE", "LMH_MAX_UNION_VOCAB", "draft_project_argmax_indexed",
     "lmhead_bench_time_argmax_indexed", "lmhead_quantize_mxfp4", "draft_project_argmax_mxfp4",
-    "lmhead_bench_time_argmax_mxfp4",
+    "lmhead_bench_time_argmax_mxfp4", "lmhead_mxfp4_scale_bytes", "lmhead_mxfp4_tile_scales",
+    "mxfp4_scale_shape",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "liblmhead.so")
@@ -68,6 +69,8 @@ SIGNATURES = {
     "lmhead_bench_time_argmax_indexed": (_INT, [_P, _I64, _I64, _P, _INT, _I64, _P, _I64, _P, _P, _P, _SZ, _INT,
                                                 _INT, ctypes.POINTER(ctypes.c_double), _P]),
     "lmhead_quantize_mxfp4": (_INT, [_P, _I64, _I64, _P, _P, _P]),
+    "lmhead_mxfp4_scale_bytes": (_I64, [_I64, _I64]),
+    "lmhead_mxfp4_tile_scales": (_INT, [_P, _I64, _I64, _P, _P]),
     "draft_project_argmax_mxfp4": (_INT, [_P, _I64, _I64, _P, _P, _I64, _P, _P, _P, _P, _SZ, _INT, _P]),
     "lmhead_bench_time_argmax_mxfp4": (_INT, [_P, _I64, _I64, _P, _P, _INT, _I64, _P, _P, _P, _P, _SZ, _INT, _INT,
                                               ctypes.POINTER(ctypes.c_double), _P]),
@@ -518,11 +521,25 @@ def lmhead_bench_time_argmax_indexed(h: torch.Tensor, heads: list, ids: torch.Te
     return out.value
 
 
+def lmhead_mxfp4_scale_bytes(R: int, K: int) -> int:
+    """Bytes of the tiled scale array of an [R, K] MXFP4 head (-1: bad shape)."""
+    return int(lib().lmhead_mxfp4_scale_bytes(R, K))
+
+
+def mxfp4_scale_shape(r: int, k: int) -> tuple:
+    """Shape of the tiled scale array of an [R, K] MXFP4 head:
+    (ceil(R / 16), ceil(K / 512), 16, 16) bytes -- [tile][group of 16 blocks]
+    [row in tile][block in group]."""
+    if k % 32 or k <= 0 or r < 0:
+        raise ValueError("K must be a positive multiple of 32")
+    return ((r + 15) // 16, (k // 32 + 15) // 16, 16, 16)
+
+
 def lmhead_quantize_mxfp4(W: torch.Tensor, out: torch.Tensor | None = None,
                           scales: torch.Tensor | None = None, stream=None):
-    """(Wq uint8 [R, K / 2] packed E2M1 codes, scales uint8 [R, K / 32] E8M0
-    codes) of a bf16 head, one scale per 32 elements.  Queues one kernel;
-    never synchronizes."""
+    """(Wq uint8 [R, K / 2] packed E2M1 codes, scales uint8 in the tiled
+    layout, shape mxfp4_scale_shape(R, K)) of a bf16 head, one E8M0 scale per
+    32 elements.  Queues one kernel; never synchronizes."""
     _dev_tensor(W, "W", _BF16_LIKE, 2)
     r, k = W.shape
     if k % 32:
@@ -530,26 +547,42 @@ def lmhead_quantize_mxfp4(W: torch.Tensor, out: torch.Tensor | None = None,
     if out is None:
         out = torch.empty((r, k // 2), dtype=torch.uint8, device=W.device)
     if scales is None:
-        scales = torch.empty((r, k // 32), dtype=torch.uint8, device=W.device)
+        scales = torch.zeros(mxfp4_scale_shape(r, k), dtype=torch.uint8, device=W.device)
     _dev_tensor(out, "Wq", (torch.uint8,), 2)
-    _dev_tensor(scales, "scales", (torch.uint8,), 2)
-    if tuple(out.shape) != (r, k // 2) or tuple(scales.shape) != (r, k // 32):
-        raise ValueError("Wq must be [R, K / 2] and scales [R, K / 32]")
+    _dev_tensor(scales, "scales", (torch.uint8,), 4)
+    if tuple(out.shape) != (r, k // 2) or tuple(scales.shape) != mxfp4_scale_shape(r, k):
+        raise ValueError("Wq must be [R, K / 2] and scales of shape mxfp4_scale_shape(R, K)")
     _check(lib().lmhead_quantize_mxfp4(W.data_ptr(), r, k, out.data_ptr(), scales.data_ptr(),
                                        _stream(stream, W.device)), "lmhead_quantize_mxfp4")
     return out, scales
 
 
+def lmhead_mxfp4_tile_scales(src: torch.Tensor, out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """Row-major E8M0 scales [R, K / 32] (a head quantized elsewhere) into
+    the tiled layout.  Queues one kernel; never synchronizes."""
+    _dev_tensor(src, "src", (torch.uint8,), 2)
+    r, nblk = src.shape
+    k = nblk * 32
+    if out is None:
+        out = torch.zeros(mxfp4_scale_shape(r, k), dtype=torch.uint8, device=src.device)
+    _dev_tensor(out, "scales", (torch.uint8,), 4)
+    if tuple(out.shape) != mxfp4_scale_shape(r, k):
+        raise ValueError("scales must have shape mxfp4_scale_shape(R, K)")
+    _check(lib().lmhead_mxfp4_tile_scales(src.data_ptr(), r, k, out.data_ptr(), _stream(stream, src.device)),
+           "lmhead_mxfp4_tile_scales")
+    return out
+
+
 def _check_mx4_head(h, Wq, scales, d2t):
     _dev_tensor(h, "h", _BF16_LIKE, 2)
     _dev_tensor(Wq, "Wq", (torch.uint8,), 2)
-    _dev_tensor(scales, "scales", (torch.uint8,), 2)
+    _dev_tensor(scales, "scales", (torch.uint8,), 4)
     m, k = h.shape
     r, half = Wq.shape
     if k != 2 * half:
         raise ValueError("Wq must be [R, K / 2] for h [M, K]")
-    if tuple(scales.shape) != (r, k // 32):
-        raise ValueError("scales must be [R, K / 32]")
+    if tuple(scales.shape) != mxfp4_scale_shape(r, k):
+        raise ValueError("scales must have shape mxfp4_scale_shape(R, K) (the tiled layout)")
     if d2t is not None:
         _dev_tensor(d2t, "d2t", (torch.int32,), 1)
         if d2t.shape[0] != r:
