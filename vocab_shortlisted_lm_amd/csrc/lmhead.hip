@@ -2115,8 +2115,9 @@ int mfma_lds_rows_fit(int64_t K, int waves, int fmt = kFmtBf16) {
 }
 
 // One pass of the matrix-core path over hidden rows [m_base, m_base + mp):
-// 8 waves per workgroup when the hidden rows and eight stages fit the LDS,
-// else 4; two 16-column tiles when mp > 16.
+// 8 waves per workgroup when the hidden rows and eight stages fit the LDS
+// and the head has at least 8 tiles per CU, else 4; two 16-column tiles
+// when mp > 16.
 // FP8 heads take twice the k-steps per batch and MXFP4 heads four times, so
 // a batch moves the same code bytes (and the stage has the same size) as for
 // bf16.  `wsc` is the FP8 row scales or the MXFP4 block scales.
@@ -2128,7 +2129,10 @@ int launch_mfma_pass(const uint16_t* h, int K, int m_base, int mp, const void* W
   const void* wscale = wsc;
   const size_t hbytes = (size_t)mp * mfma_row_bytes(K);
   const int64_t tiles = (R + 15) / 16;
-  const bool eight = mp <= mfma_lds_rows_fit(K, 8, FMT);
+  // 8 waves per workgroup only when there are tiles for 8 waves on every CU:
+  // a shorter head in 8-wave workgroups would leave CUs idle (a 16,000-row
+  // list has 1,000 tiles, 125 such workgroups)
+  const bool eight = mp <= mfma_lds_rows_fit(K, 8, FMT) && tiles >= 8LL * cus;
   const size_t lds = hbytes + mfma_stage_bytes(eight ? 8 : 4, FMT);
   const char* what = "launch matrix-core projection";
   if (mp <= 16)
