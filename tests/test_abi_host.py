@@ -269,6 +269,31 @@ def test_bench_kernels_reject_on_host(L):
     assert lib.lmhead_bench_sink_words() >= 4096
 
 
+def test_binding_rejects_host_tensors_before_any_call(L):
+    """Every wrapper refuses host tensors before the library sees a pointer
+    (a host address in a kernel would fault the GPU)."""
+    import torch
+    h = torch.zeros(2, 512, dtype=torch.bfloat16)
+    W = torch.zeros(64, 512, dtype=torch.bfloat16)
+    ids = torch.zeros(4, dtype=torch.int32)
+    calls = [
+        lambda: L.draft_project_argmax(h, W),
+        lambda: L.draft_project_topk(h, W, None, 4),
+        lambda: L.draft_project_logits(h, W),
+        lambda: L.lmhead_trim(W, ids),
+        lambda: L.lmhead_quantize_fp8(W),
+        lambda: L.lmhead_quantize_mxfp4(W),
+        lambda: L.draft_project_argmax_indexed(h, W, ids),
+        lambda: L.lmhead_shortlist_union(ids, ids, 100),
+        lambda: L.lmhead_bench_stream_read(W, ids),
+        lambda: L.lmhead_bench_copy(W, W),
+        lambda: L.lmhead_mxfp4_tile_scales(torch.zeros(64, 16, dtype=torch.uint8)),
+    ]
+    for i, call in enumerate(calls):
+        with pytest.raises(ValueError, match="device tensor"):
+            call()
+
+
 def test_read_id_list(L, tmp_path):
     p = tmp_path / "ranks.txt"
     p.write_text("17\n3\n\n248319\n0\n")

@@ -318,6 +318,34 @@ def test_rejected_calls_write_nothing(L):
 # the measurement helper runs the same kernels
 # --------------------------------------------------------------------------
 
+def test_binding_rejects_host_and_short_buffers(L):
+    """The binding refuses a host workspace or host outputs next to device
+    inputs, and outputs or a d2t of the wrong size, before any launch."""
+    h = dev_bf16(synth.hidden(7, 0, 3, 512))
+    W = dev_bf16(synth.normal_bf16(8, 100, 512, 0.02))
+    ws_host = torch.empty(L.draft_project_workspace_bytes(32), dtype=torch.uint8)
+    bad = [
+        dict(workspace=ws_host),
+        dict(out_id=torch.empty(3, dtype=torch.int32)),
+        dict(out_logit=torch.empty(3, dtype=torch.float32)),
+        dict(out_id=torch.empty(2, dtype=torch.int32, device="cuda")),
+        dict(out_logit=torch.empty(3, dtype=torch.float64, device="cuda")),
+    ]
+    for kw in bad:
+        with pytest.raises((ValueError, TypeError)):
+            L.draft_project_argmax(h, W, **kw)
+    with pytest.raises(ValueError):
+        L.draft_project_argmax(h, W, torch.arange(99, dtype=torch.int32, device="cuda"))
+    with pytest.raises(ValueError):
+        L.draft_project_argmax(h, W, torch.arange(100, dtype=torch.int32))
+    q, sc = L.lmhead_quantize_fp8(W)
+    with pytest.raises(ValueError):
+        L.draft_project_argmax_fp8(h, q, sc, workspace=ws_host)
+    with pytest.raises(ValueError):
+        L.draft_project_argmax_fp8(h, q, sc, out_id=torch.empty(1, dtype=torch.int32, device="cuda"))
+    torch.cuda.synchronize()
+
+
 def test_bench_time_argmax_matches_call(L):
     inp = config_inputs(1)
     c = inp["config"]

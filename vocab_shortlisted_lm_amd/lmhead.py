@@ -116,15 +116,55 @@ def _check(code: int, where: str) -> None:
 _BF16_LIKE = (torch.bfloat16, torch.int16, torch.uint16)
 
 
-def _dev_tensor(t: torch.Tensor, name: str, dtypes, ndim: int) -> None:
+def _dev_tensor(t: torch.Tensor, name: str, dtypes, ndim: int, device=None) -> None:
+    """A contiguous device tensor of one of `dtypes` with `ndim` dimensions
+    (any dtype / rank if None), on `device` when given.  Every pointer the
+    library receives goes through here: a host tensor's address in a
+    kernel would fault the GPU."""
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch.Tensor")
     if t.device.type != "cuda":
         raise ValueError(f"{name} must be a device tensor")
-    if t.dtype not in dtypes:
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, the call runs on {device}")
+    if dtypes is not None and t.dtype not in dtypes:
         raise TypeError(f"{name} has dtype {t.dtype}, expected one of {dtypes}")
-    if t.dim() != ndim or not t.is_contiguous():
-        raise ValueError(f"{name} must be a contiguous {ndim}-d tensor")
+    if (ndim is not None and t.dim() != ndim) or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous {ndim}-d tensor" if ndim is not None
+                         else f"{name} must be contiguous")
+
+
+def _nbytes(t: torch.Tensor) -> int:
+    return t.numel() * t.element_size()
+
+
+def _outputs(m: int, out_id, out_logit, device):
+    """(out_id int32, out_logit float32) of at least m entries on `device`,
+    allocated when not given."""
+    if out_id is None:
+        out_id = torch.empty(m, dtype=torch.int32, device=device)
+    if out_logit is None:
+        out_logit = torch.empty(m, dtype=torch.float32, device=device)
+    _dev_tensor(out_id, "out_id", (torch.int32,), 1, device)
+    _dev_tensor(out_logit, "out_logit", (torch.float32,), 1, device)
+    if out_id.shape[0] < m or out_logit.shape[0] < m:
+        raise ValueError("outputs must hold M entries")
+    return out_id, out_logit
+
+
+def _workspace(workspace, device, stream_handle: int) -> torch.Tensor:
+    """The caller's workspace (checked), or a cached one per device and stream."""
+    if workspace is None:
+        return _default_workspace(device, stream_handle)
+    _dev_tensor(workspace, "workspace", None, None, device)
+    return workspace
+
+
+def _d2t(d2t, r: int, device, rows_of: str = "W"):
+    if d2t is not None:
+        _dev_tensor(d2t, "d2t", (torch.int32,), 1, device)
+        if d2t.shape[0] != r:
+            raise ValueError(f"d2t must have one entry per row of {rows_of}")
 
 
 def _stream(stream, device) -> int:
@@ -137,12 +177,12 @@ def lmhead_trim(W: torch.Tensor, ids: torch.Tensor, out: torch.Tensor | None = N
                 stream=None) -> torch.Tensor:
     """W_trim[i] = W[ids[i]] (bf16 [S, K]).  Synchronizes `stream` once."""
     _dev_tensor(W, "W", _BF16_LIKE, 2)
-    _dev_tensor(ids, "ids", (torch.int32,), 1)
+    _dev_tensor(ids, "ids", (torch.int32,), 1, W.device)
     n, k = W.shape
     s = ids.shape[0]
     if out is None:
         out = torch.empty((s, k), dtype=W.dtype, device=W.device)
-    _dev_tensor(out, "out", _BF16_LIKE, 2)
+    _dev_tensor(out, "out", _BF16_LIKE, 2, W.device)
     if tuple(out.shape) != (s, k):
         raise ValueError("out must be [S, K]")
     _check(lib().lmhead_trim(W.data_ptr(), n, k, ids.data_ptr(), s, out.data_ptr(),
@@ -182,31 +222,13 @@ def draft_project_argmax_path(h: torch.Tensor, W: torch.Tensor, d2t: torch.Tenso
                               workspace: torch.Tensor | None = None, stream=None):
     """(out_id int32 [M], out_logit float32 [M]) for the best row of W per
     hidden row, mapped through d2t.  Queues one call; never synchronizes."""
-    _dev_tensor(h, "h", _BF16_LIKE, 2)
-    _dev_tensor(W, "W", _BF16_LIKE, 2)
-    m, k = h.shape
-    r, k2 = W.shape
-    if k != k2:
-        raise ValueError("h and W must have the same K")
-    if d2t is not None:
-        _dev_tensor(d2t, "d2t", (torch.int32,), 1)
-        if d2t.shape[0] != r:
-            raise ValueError("d2t must have one entry per row of W")
-    if out_id is None:
-        out_id = torch.empty(m, dtype=torch.int32, device=h.device)
-    if out_logit is None:
-        out_logit = torch.empty(m, dtype=torch.float32, device=h.device)
-    _dev_tensor(out_id, "out_id", (torch.int32,), 1)
-    _dev_tensor(out_logit, "out_logit", (torch.float32,), 1)
-    if out_id.shape[0] < m or out_logit.shape[0] < m:
-        raise ValueError("outputs must hold M entries")
+    m, k, r = _check_hw(h, W, d2t)
+    out_id, out_logit = _outputs(m, out_id, out_logit, h.device)
     st = _stream(stream, h.device)
-    if workspace is None:
-        workspace = _default_workspace(h.device, st)
+    workspace = _workspace(workspace, h.device, st)
     code = lib().draft_project_argmax_path(
         h.data_ptr(), m, k, W.data_ptr(), r, d2t.data_ptr() if d2t is not None else None,
-        out_id.data_ptr(), out_logit.data_ptr(), workspace.data_ptr(),
-        workspace.numel() * workspace.element_size(), path, st)
+        out_id.data_ptr(), out_logit.data_ptr(), workspace.data_ptr(), _nbytes(workspace), path, st)
     _check(code, "draft_project_argmax")
     return out_id, out_logit
 
@@ -224,15 +246,12 @@ def draft_project_topk_workspace_bytes(M: int, topk: int) -> int:
 
 def _check_hw(h, W, d2t):
     _dev_tensor(h, "h", _BF16_LIKE, 2)
-    _dev_tensor(W, "W", _BF16_LIKE, 2)
+    _dev_tensor(W, "W", _BF16_LIKE, 2, h.device)
     m, k = h.shape
     r, k2 = W.shape
     if k != k2:
         raise ValueError("h and W must have the same K")
-    if d2t is not None:
-        _dev_tensor(d2t, "d2t", (torch.int32,), 1)
-        if d2t.shape[0] != r:
-            raise ValueError("d2t must have one entry per row of W")
+    _d2t(d2t, r, h.device)
     return m, k, r
 
 
@@ -247,8 +266,8 @@ def draft_project_topk(h: torch.Tensor, W: torch.Tensor, d2t: torch.Tensor | Non
         out_id = torch.empty((m, topk), dtype=torch.int32, device=h.device)
     if out_logit is None:
         out_logit = torch.empty((m, topk), dtype=torch.float32, device=h.device)
-    _dev_tensor(out_id, "out_id", (torch.int32,), 2)
-    _dev_tensor(out_logit, "out_logit", (torch.float32,), 2)
+    _dev_tensor(out_id, "out_id", (torch.int32,), 2, h.device)
+    _dev_tensor(out_logit, "out_logit", (torch.float32,), 2, h.device)
     if tuple(out_id.shape) != (m, topk) or tuple(out_logit.shape) != (m, topk):
         raise ValueError("outputs must be [M, topk]")
     st = _stream(stream, h.device)
@@ -257,10 +276,10 @@ def draft_project_topk(h: torch.Tensor, W: torch.Tensor, d2t: torch.Tensor | Non
         if nbytes == 0:
             raise LmheadError(LMH_EINVAL, "draft_project_topk")
         workspace = torch.empty(nbytes, dtype=torch.uint8, device=h.device)
+    _dev_tensor(workspace, "workspace", None, None, h.device)
     code = lib().draft_project_topk(
         h.data_ptr(), m, k, W.data_ptr(), r, d2t.data_ptr() if d2t is not None else None, topk,
-        out_id.data_ptr(), out_logit.data_ptr(), workspace.data_ptr(),
-        workspace.numel() * workspace.element_size(), path, st)
+        out_id.data_ptr(), out_logit.data_ptr(), workspace.data_ptr(), _nbytes(workspace), path, st)
     _check(code, "draft_project_topk")
     return out_id, out_logit
 
@@ -276,7 +295,7 @@ def draft_project_logits(h: torch.Tensor, W: torch.Tensor, d2t: torch.Tensor | N
         raise ValueError("n (vocabulary size) is required with d2t")
     if out is None:
         out = torch.empty((m, cols), dtype=torch.float32, device=h.device)
-    _dev_tensor(out, "out", (torch.float32,), 2)
+    _dev_tensor(out, "out", (torch.float32,), 2, h.device)
     if tuple(out.shape) != (m, cols):
         raise ValueError(f"out must be [{m}, {cols}]")
     code = lib().draft_project_logits(
@@ -310,15 +329,21 @@ def lmhead_bench_sink_words() -> int:
 
 def lmhead_bench_stream_read(buf: torch.Tensor, sink: torch.Tensor, grid: int = 0,
                              stream=None) -> None:
-    nbytes = buf.numel() * buf.element_size()
+    _dev_tensor(buf, "buf", None, None)
+    _dev_tensor(sink, "sink", (torch.int32,), 1, buf.device)
+    if sink.numel() < lmhead_bench_sink_words():
+        raise ValueError("sink must hold lmhead_bench_sink_words() int32 words")
+    nbytes = _nbytes(buf)
     _check(lib().lmhead_bench_stream_read(buf.data_ptr(), nbytes, sink.data_ptr(), grid,
                                           _stream(stream, buf.device)),
            "lmhead_bench_stream_read")
 
 
 def lmhead_bench_copy(src: torch.Tensor, dst: torch.Tensor, grid: int = 0, stream=None) -> None:
-    nbytes = src.numel() * src.element_size()
-    if dst.numel() * dst.element_size() < nbytes:
+    _dev_tensor(src, "src", None, None)
+    _dev_tensor(dst, "dst", None, None, src.device)
+    nbytes = _nbytes(src)
+    if _nbytes(dst) < nbytes:
         raise ValueError("dst too small")
     _check(lib().lmhead_bench_copy(src.data_ptr(), dst.data_ptr(), nbytes, grid,
                                    _stream(stream, src.device)), "lmhead_bench_copy")
@@ -332,18 +357,23 @@ def lmhead_bench_time_argmax(h: torch.Tensor, heads: list, d2t: torch.Tensor | N
     records around each projection launch.  Synchronizes."""
     _dev_tensor(h, "h", _BF16_LIKE, 2)
     m, k = h.shape
+    if not heads:
+        raise ValueError("at least one head")
     for w in heads:
-        _dev_tensor(w, "W", _BF16_LIKE, 2)
+        _dev_tensor(w, "W", _BF16_LIKE, 2, h.device)
         if w.shape != heads[0].shape or w.shape[1] != k:
             raise ValueError("every head must be [R, K] with the same R and K")
     r = heads[0].shape[0]
+    _d2t(d2t, r, h.device)
+    out_id, out_logit = _outputs(m, out_id, out_logit, h.device)
+    st = _stream(stream, h.device)
+    workspace = _workspace(workspace, h.device, st)
     ptrs = (ctypes.c_void_p * len(heads))(*[w.data_ptr() for w in heads])
     out = ctypes.c_double(0.0)
     _check(lib().lmhead_bench_time_argmax(
         h.data_ptr(), m, k, ptrs, len(heads), r, d2t.data_ptr() if d2t is not None else None,
-        out_id.data_ptr(), out_logit.data_ptr(), workspace.data_ptr(),
-        workspace.numel() * workspace.element_size(), path, calls, ctypes.byref(out),
-        _stream(stream, h.device)), "lmhead_bench_time_argmax")
+        out_id.data_ptr(), out_logit.data_ptr(), workspace.data_ptr(), _nbytes(workspace), path, calls,
+        ctypes.byref(out), st), "lmhead_bench_time_argmax")
     return out.value
 
 
@@ -357,8 +387,8 @@ def lmhead_quantize_fp8(W: torch.Tensor, out: torch.Tensor | None = None,
         out = torch.empty((r, k), dtype=torch.uint8, device=W.device)
     if scale is None:
         scale = torch.empty(r, dtype=torch.float32, device=W.device)
-    _dev_tensor(out, "Wq", (torch.uint8,), 2)
-    _dev_tensor(scale, "scale", (torch.float32,), 1)
+    _dev_tensor(out, "Wq", (torch.uint8,), 2, W.device)
+    _dev_tensor(scale, "scale", (torch.float32,), 1, W.device)
     if tuple(out.shape) != (r, k) or scale.shape[0] < r:
         raise ValueError("Wq must be [R, K] and scale hold R entries")
     _check(lib().lmhead_quantize_fp8(W.data_ptr(), r, k, out.data_ptr(), scale.data_ptr(),
@@ -368,18 +398,15 @@ def lmhead_quantize_fp8(W: torch.Tensor, out: torch.Tensor | None = None,
 
 def _check_fp8_head(h, Wq, scale, d2t):
     _dev_tensor(h, "h", _BF16_LIKE, 2)
-    _dev_tensor(Wq, "Wq", (torch.uint8,), 2)
-    _dev_tensor(scale, "scale", (torch.float32,), 1)
+    _dev_tensor(Wq, "Wq", (torch.uint8,), 2, h.device)
+    _dev_tensor(scale, "scale", (torch.float32,), 1, h.device)
     m, k = h.shape
     r, k2 = Wq.shape
     if k != k2:
         raise ValueError("h and Wq must have the same K")
     if scale.shape[0] != r:
         raise ValueError("scale must have one entry per row of Wq")
-    if d2t is not None:
-        _dev_tensor(d2t, "d2t", (torch.int32,), 1)
-        if d2t.shape[0] != r:
-            raise ValueError("d2t must have one entry per row of Wq")
+    _d2t(d2t, r, h.device, "Wq")
     return m, k, r
 
 
@@ -391,17 +418,13 @@ def draft_project_argmax_fp8(h: torch.Tensor, Wq: torch.Tensor, scale: torch.Ten
     dequantized FP8 head per hidden row, mapped through d2t.  Never
     synchronizes."""
     m, k, r = _check_fp8_head(h, Wq, scale, d2t)
-    if out_id is None:
-        out_id = torch.empty(m, dtype=torch.int32, device=h.device)
-    if out_logit is None:
-        out_logit = torch.empty(m, dtype=torch.float32, device=h.device)
+    out_id, out_logit = _outputs(m, out_id, out_logit, h.device)
     st = _stream(stream, h.device)
-    if workspace is None:
-        workspace = _default_workspace(h.device, st)
+    workspace = _workspace(workspace, h.device, st)
     _check(lib().draft_project_argmax_fp8(
         h.data_ptr(), m, k, Wq.data_ptr(), scale.data_ptr(), r,
         d2t.data_ptr() if d2t is not None else None, out_id.data_ptr(), out_logit.data_ptr(),
-        workspace.data_ptr(), workspace.numel() * workspace.element_size(), path, st),
+        workspace.data_ptr(), _nbytes(workspace), path, st),
         "draft_project_argmax_fp8")
     return out_id, out_logit
 
@@ -411,20 +434,23 @@ def lmhead_bench_time_argmax_fp8(h: torch.Tensor, heads: list, d2t: torch.Tensor
                                  workspace: torch.Tensor, stream=None) -> float:
     """lmhead_bench_time_argmax over FP8 heads: `heads` is a list of
     (Wq, scale) pairs.  Synchronizes."""
+    if not heads:
+        raise ValueError("at least one head")
     m, k, r = _check_fp8_head(h, heads[0][0], heads[0][1], d2t)
     for wq, sc in heads:
-        if tuple(wq.shape) != (r, k) or sc.shape[0] != r:
+        _check_fp8_head(h, wq, sc, None)
+        if tuple(wq.shape) != (r, k):
             raise ValueError("every head must have the same shape")
-        _dev_tensor(wq, "Wq", (torch.uint8,), 2)
-        _dev_tensor(sc, "scale", (torch.float32,), 1)
+    out_id, out_logit = _outputs(m, out_id, out_logit, h.device)
+    st = _stream(stream, h.device)
+    workspace = _workspace(workspace, h.device, st)
     qp = (ctypes.c_void_p * len(heads))(*[wq.data_ptr() for wq, _ in heads])
     sp = (ctypes.c_void_p * len(heads))(*[sc.data_ptr() for _, sc in heads])
     out = ctypes.c_double(0.0)
     _check(lib().lmhead_bench_time_argmax_fp8(
         h.data_ptr(), m, k, qp, sp, len(heads), r, d2t.data_ptr() if d2t is not None else None,
-        out_id.data_ptr(), out_logit.data_ptr(), workspace.data_ptr(),
-        workspace.numel() * workspace.element_size(), path, calls, ctypes.byref(out),
-        _stream(stream, h.device)), "lmhead_bench_time_argmax_fp8")
+        out_id.data_ptr(), out_logit.data_ptr(), workspace.data_ptr(), _nbytes(workspace), path, calls,
+        ctypes.byref(out), st), "lmhead_bench_time_argmax_fp8")
     return out.value
 
 
@@ -433,10 +459,10 @@ def lmhead_shortlist_overwrite(W: torch.Tensor, W_trim: torch.Tensor, d2t: torch
     """W_trim[rows[i]] = W[ids[i]], d2t[rows[i]] = ids[i] in place (invalid
     entries skipped, the last entry for a row wins).  Never synchronizes."""
     _dev_tensor(W, "W", _BF16_LIKE, 2)
-    _dev_tensor(W_trim, "W_trim", _BF16_LIKE, 2)
-    _dev_tensor(d2t, "d2t", (torch.int32,), 1)
-    _dev_tensor(rows, "rows", (torch.int32,), 1)
-    _dev_tensor(ids, "ids", (torch.int32,), 1)
+    _dev_tensor(W_trim, "W_trim", _BF16_LIKE, 2, W.device)
+    _dev_tensor(d2t, "d2t", (torch.int32,), 1, W.device)
+    _dev_tensor(rows, "rows", (torch.int32,), 1, W.device)
+    _dev_tensor(ids, "ids", (torch.int32,), 1, W.device)
     n, k = W.shape
     cap, k2 = W_trim.shape
     if k != k2 or d2t.shape[0] != cap or rows.shape[0] != ids.shape[0]:
@@ -452,14 +478,16 @@ def lmhead_shortlist_union(a: torch.Tensor, b: torch.Tensor, n_vocab: int, out: 
     ascending union of a and b; counts = (|set a|, |set b|, |b - a|, |a u b|).
     Never synchronizes."""
     _dev_tensor(a, "a", (torch.int32,), 1)
-    _dev_tensor(b, "b", (torch.int32,), 1)
+    _dev_tensor(b, "b", (torch.int32,), 1, a.device)
     na, nb = a.shape[0], b.shape[0]
     if out is None:
         out = torch.empty(max(1, na + nb), dtype=torch.int32, device=a.device)
     if counts is None:
         counts = torch.empty(4, dtype=torch.int32, device=a.device)
-    _dev_tensor(out, "out", (torch.int32,), 1)
-    _dev_tensor(counts, "counts", (torch.int32,), 1)
+    _dev_tensor(out, "out", (torch.int32,), 1, a.device)
+    _dev_tensor(counts, "counts", (torch.int32,), 1, a.device)
+    if counts.shape[0] < 4:
+        raise ValueError("counts must hold 4 entries")
     _check(lib().lmhead_shortlist_union(a.data_ptr(), na, b.data_ptr(), nb, n_vocab, out.data_ptr(),
                                         out.shape[0], counts.data_ptr(), _stream(stream, a.device)),
            "lmhead_shortlist_union")
@@ -475,26 +503,18 @@ def draft_project_argmax_indexed(h: torch.Tensor, W: torch.Tensor, ids: torch.Te
     copy); out_id is the winning entry's id.  Entries outside [0, N) are
     skipped.  Never synchronizes."""
     _dev_tensor(h, "h", _BF16_LIKE, 2)
-    _dev_tensor(W, "W", _BF16_LIKE, 2)
-    _dev_tensor(ids, "ids", (torch.int32,), 1)
+    _dev_tensor(W, "W", _BF16_LIKE, 2, h.device)
+    _dev_tensor(ids, "ids", (torch.int32,), 1, h.device)
     m, k = h.shape
     n, k2 = W.shape
     if k != k2:
         raise ValueError("h and W must have the same K")
-    if out_id is None:
-        out_id = torch.empty(m, dtype=torch.int32, device=h.device)
-    if out_logit is None:
-        out_logit = torch.empty(m, dtype=torch.float32, device=h.device)
-    _dev_tensor(out_id, "out_id", (torch.int32,), 1)
-    _dev_tensor(out_logit, "out_logit", (torch.float32,), 1)
-    if out_id.shape[0] < m or out_logit.shape[0] < m:
-        raise ValueError("outputs must hold M entries")
+    out_id, out_logit = _outputs(m, out_id, out_logit, h.device)
     st = _stream(stream, h.device)
-    if workspace is None:
-        workspace = _default_workspace(h.device, st)
+    workspace = _workspace(workspace, h.device, st)
     _check(lib().draft_project_argmax_indexed(
         h.data_ptr(), m, k, W.data_ptr(), n, ids.data_ptr(), ids.shape[0], out_id.data_ptr(),
-        out_logit.data_ptr(), workspace.data_ptr(), workspace.numel() * workspace.element_size(), path, st),
+        out_logit.data_ptr(), workspace.data_ptr(), _nbytes(workspace), path, st),
         "draft_project_argmax_indexed")
     return out_id, out_logit
 
@@ -505,19 +525,24 @@ def lmhead_bench_time_argmax_indexed(h: torch.Tensor, heads: list, ids: torch.Te
     """lmhead_bench_time_argmax for draft_project_argmax_indexed: `heads`
     are full heads [N, K] read through the same id list.  Synchronizes."""
     _dev_tensor(h, "h", _BF16_LIKE, 2)
-    _dev_tensor(ids, "ids", (torch.int32,), 1)
+    _dev_tensor(ids, "ids", (torch.int32,), 1, h.device)
     m, k = h.shape
+    if not heads:
+        raise ValueError("at least one head")
     for w in heads:
-        _dev_tensor(w, "W", _BF16_LIKE, 2)
+        _dev_tensor(w, "W", _BF16_LIKE, 2, h.device)
         if w.shape != heads[0].shape or w.shape[1] != k:
             raise ValueError("every head must be [N, K] with the same N and K")
     n = heads[0].shape[0]
+    out_id, out_logit = _outputs(m, out_id, out_logit, h.device)
+    st = _stream(stream, h.device)
+    workspace = _workspace(workspace, h.device, st)
     ptrs = (ctypes.c_void_p * len(heads))(*[w.data_ptr() for w in heads])
     out = ctypes.c_double(0.0)
     _check(lib().lmhead_bench_time_argmax_indexed(
         h.data_ptr(), m, k, ptrs, len(heads), n, ids.data_ptr(), ids.shape[0], out_id.data_ptr(),
-        out_logit.data_ptr(), workspace.data_ptr(), workspace.numel() * workspace.element_size(), path, calls,
-        ctypes.byref(out), _stream(stream, h.device)), "lmhead_bench_time_argmax_indexed")
+        out_logit.data_ptr(), workspace.data_ptr(), _nbytes(workspace), path, calls,
+        ctypes.byref(out), st), "lmhead_bench_time_argmax_indexed")
     return out.value
 
 
@@ -548,8 +573,8 @@ def lmhead_quantize_mxfp4(W: torch.Tensor, out: torch.Tensor | None = None,
         out = torch.empty((r, k // 2), dtype=torch.uint8, device=W.device)
     if scales is None:
         scales = torch.zeros(mxfp4_scale_shape(r, k), dtype=torch.uint8, device=W.device)
-    _dev_tensor(out, "Wq", (torch.uint8,), 2)
-    _dev_tensor(scales, "scales", (torch.uint8,), 4)
+    _dev_tensor(out, "Wq", (torch.uint8,), 2, W.device)
+    _dev_tensor(scales, "scales", (torch.uint8,), 4, W.device)
     if tuple(out.shape) != (r, k // 2) or tuple(scales.shape) != mxfp4_scale_shape(r, k):
         raise ValueError("Wq must be [R, K / 2] and scales of shape mxfp4_scale_shape(R, K)")
     _check(lib().lmhead_quantize_mxfp4(W.data_ptr(), r, k, out.data_ptr(), scales.data_ptr(),
@@ -565,7 +590,7 @@ def lmhead_mxfp4_tile_scales(src: torch.Tensor, out: torch.Tensor | None = None,
     k = nblk * 32
     if out is None:
         out = torch.zeros(mxfp4_scale_shape(r, k), dtype=torch.uint8, device=src.device)
-    _dev_tensor(out, "scales", (torch.uint8,), 4)
+    _dev_tensor(out, "scales", (torch.uint8,), 4, src.device)
     if tuple(out.shape) != mxfp4_scale_shape(r, k):
         raise ValueError("scales must have shape mxfp4_scale_shape(R, K)")
     _check(lib().lmhead_mxfp4_tile_scales(src.data_ptr(), r, k, out.data_ptr(), _stream(stream, src.device)),
@@ -575,18 +600,15 @@ def lmhead_mxfp4_tile_scales(src: torch.Tensor, out: torch.Tensor | None = None,
 
 def _check_mx4_head(h, Wq, scales, d2t):
     _dev_tensor(h, "h", _BF16_LIKE, 2)
-    _dev_tensor(Wq, "Wq", (torch.uint8,), 2)
-    _dev_tensor(scales, "scales", (torch.uint8,), 4)
+    _dev_tensor(Wq, "Wq", (torch.uint8,), 2, h.device)
+    _dev_tensor(scales, "scales", (torch.uint8,), 4, h.device)
     m, k = h.shape
     r, half = Wq.shape
     if k != 2 * half:
         raise ValueError("Wq must be [R, K / 2] for h [M, K]")
     if tuple(scales.shape) != mxfp4_scale_shape(r, k):
         raise ValueError("scales must have shape mxfp4_scale_shape(R, K) (the tiled layout)")
-    if d2t is not None:
-        _dev_tensor(d2t, "d2t", (torch.int32,), 1)
-        if d2t.shape[0] != r:
-            raise ValueError("d2t must have one entry per row of Wq")
+    _d2t(d2t, r, h.device, "Wq")
     return m, k, r
 
 
@@ -598,17 +620,13 @@ def draft_project_argmax_mxfp4(h: torch.Tensor, Wq: torch.Tensor, scales: torch.
     dequantized MXFP4 head per hidden row, mapped through d2t.  Never
     synchronizes."""
     m, k, r = _check_mx4_head(h, Wq, scales, d2t)
-    if out_id is None:
-        out_id = torch.empty(m, dtype=torch.int32, device=h.device)
-    if out_logit is None:
-        out_logit = torch.empty(m, dtype=torch.float32, device=h.device)
+    out_id, out_logit = _outputs(m, out_id, out_logit, h.device)
     st = _stream(stream, h.device)
-    if workspace is None:
-        workspace = _default_workspace(h.device, st)
+    workspace = _workspace(workspace, h.device, st)
     _check(lib().draft_project_argmax_mxfp4(
         h.data_ptr(), m, k, Wq.data_ptr(), scales.data_ptr(), r,
         d2t.data_ptr() if d2t is not None else None, out_id.data_ptr(), out_logit.data_ptr(),
-        workspace.data_ptr(), workspace.numel() * workspace.element_size(), path, st),
+        workspace.data_ptr(), _nbytes(workspace), path, st),
         "draft_project_argmax_mxfp4")
     return out_id, out_logit
 
@@ -618,17 +636,21 @@ def lmhead_bench_time_argmax_mxfp4(h: torch.Tensor, heads: list, d2t: torch.Tens
                                    workspace: torch.Tensor, stream=None) -> float:
     """lmhead_bench_time_argmax over MXFP4 heads: `heads` is a list of
     (Wq, scales) pairs.  Synchronizes."""
+    if not heads:
+        raise ValueError("at least one head")
     m, k, r = _check_mx4_head(h, heads[0][0], heads[0][1], d2t)
     for wq, sc in heads:
-        _check_mx4_head(h, wq, sc, d2t)
+        _check_mx4_head(h, wq, sc, None)
         if wq.shape[0] != r:
             raise ValueError("every head must have the same shape")
+    out_id, out_logit = _outputs(m, out_id, out_logit, h.device)
+    st = _stream(stream, h.device)
+    workspace = _workspace(workspace, h.device, st)
     qp = (ctypes.c_void_p * len(heads))(*[wq.data_ptr() for wq, _ in heads])
     sp = (ctypes.c_void_p * len(heads))(*[sc.data_ptr() for _, sc in heads])
     out = ctypes.c_double(0.0)
     _check(lib().lmhead_bench_time_argmax_mxfp4(
         h.data_ptr(), m, k, qp, sp, len(heads), r, d2t.data_ptr() if d2t is not None else None,
-        out_id.data_ptr(), out_logit.data_ptr(), workspace.data_ptr(),
-        workspace.numel() * workspace.element_size(), path, calls, ctypes.byref(out),
-        _stream(stream, h.device)), "lmhead_bench_time_argmax_mxfp4")
+        out_id.data_ptr(), out_logit.data_ptr(), workspace.data_ptr(), _nbytes(workspace), path, calls,
+        ctypes.byref(out), st), "lmhead_bench_time_argmax_mxfp4")
     return out.value
