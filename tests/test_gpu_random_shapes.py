@@ -10,7 +10,7 @@ import pytest
 
 import oracle
 import synth
-from parity import ParityStats, check, check_fp8, check_mxfp4
+from parity import ParityStats, check, check_fp8, check_logits, check_mxfp4, check_topk
 from test_gpu_parity import dev_bf16, dev_i32, log, paths_for
 
 pytestmark = pytest.mark.gpu
@@ -120,3 +120,58 @@ def test_random_shape(L, case):
                                    np.concatenate([g[1].cpu().numpy() for g in got]), res))
     log(f"[random {i}] rows={st.rows} exempt={st.exempt} max_err={st.max_err:.2e} "
         f"err/bound={st.max_err_over_bound:.3f}")
+
+
+# --------------------------------------------------------------------------
+# top-k and logits epilogues
+# --------------------------------------------------------------------------
+
+def _epi_cases(n=60, seed=20261203):
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        kind = "topk" if i % 3 else "logits"
+        m = int(rng.choice(MS))
+        k = 8 * int(rng.integers(1, (1024 if rng.random() < 0.5 else 8192) // 8 + 1))
+        rmax = max(1, min(40_000, 12_000_000 // k))
+        r = int(rng.integers(1, min(rmax, 600) + 1)) if rng.random() < 0.5 or rmax <= 600 else \
+            int(np.exp(rng.uniform(np.log(600), np.log(rmax))))
+        with_d2t = bool(rng.random() < 0.5)
+        topk = int(rng.integers(1, 17))
+        out.append((i, kind, m, k, r, with_d2t, topk))
+    return out
+
+
+EPI_CASES = _epi_cases()
+
+
+def _epi_paths(L, m, k):
+    """The top-k / logits epilogues: VALU for M <= 4 with M * ceil(K / 512)
+    <= 40, matrix cores for any M."""
+    valu = m <= 4 and m * ((k // 8 + 63) // 64) <= 40
+    return ([L.LMH_PATH_VALU] if valu else []) + [L.LMH_PATH_MFMA, L.LMH_PATH_AUTO]
+
+
+@pytest.mark.parametrize("case", EPI_CASES,
+                         ids=[f"{c[0]}-{c[1]}-M{c[2]}-K{c[3]}-R{c[4]}{'-d2t' if c[5] else ''}"
+                              f"{'-k' + str(c[6]) if c[1] == 'topk' else ''}" for c in EPI_CASES])
+def test_random_shape_topk_logits(L, case):
+    i, kind, m, k, r, with_d2t, topk = case
+    log(f"[random epilogue {i}] {kind} M={m} K={k} R={r} d2t={with_d2t} topk={topk}")
+    rng = np.random.default_rng(3000 + i)
+    w = synth.normal_bf16(7000 + i, r, k, 0.02)
+    h = synth.hidden(8000 + i, 0, m, k)
+    n = r + int(rng.integers(0, 2 * r + 1))
+    d2t = _ids(rng, r, n) if with_d2t else None
+    w_dev, h_dev = dev_bf16(w), dev_bf16(h)
+    d2t_dev = dev_i32(d2t) if d2t is not None else None
+    if kind == "topk":
+        res = oracle.oracle_project_topk(h, w, d2t, topk)
+        for p in _epi_paths(L, m, k):
+            ids, lgs = L.draft_project_topk(h_dev, w_dev, d2t_dev, topk, path=p)
+            st = check_topk(h, w, d2t, ids.cpu().numpy(), lgs.cpu().numpy(), res)
+    else:
+        for p in _epi_paths(L, m, k):
+            out = L.draft_project_logits(h_dev, w_dev, d2t_dev, n=n if with_d2t else None, path=p)
+            st = check_logits(h, w, d2t, n if with_d2t else None, out.cpu().numpy())
+    log(f"[random epilogue {i}] max_err={st.max_err:.2e} err/bound={st.max_err_over_bound:.3f}")
