@@ -30,10 +30,11 @@ from __future__ import annotations
 
 import numpy as np
 
-from .lmhead_oracle import OracleResult, argmax_of_logits, bf16_bits_to_f64
+from .lmhead_oracle import OracleResult, TopkResult, argmax_of_logits, bf16_bits_to_f64, topk_of_logits
 
 __all__ = ["E4M3_MAX", "e4m3_decode", "e4m3_encode", "oracle_quantize_fp8",
-           "oracle_dequant_fp8", "oracle_logits_fp8", "oracle_project_argmax_fp8"]
+           "oracle_dequant_fp8", "oracle_logits_fp8", "oracle_project_argmax_fp8",
+           "oracle_project_topk_fp8"]
 
 E4M3_MAX = 448.0
 BLOCK_ROWS = 8192
@@ -131,3 +132,12 @@ def oracle_project_argmax_fp8(h_bits, codes, scale, d2t=None, keep_logits: bool 
     w_win = oracle_dequant_fp8(np.asarray(codes)[idx], np.asarray(scale)[idx])
     abs_sum = np.abs(h * w_win).sum(axis=1)
     return OracleResult(ids, idx, best, gap, abs_sum, logits if keep_logits else None)
+
+
+def oracle_project_topk_fp8(h_bits, codes, scale, d2t, k: int) -> TopkResult:
+    """The k best rows of the dequantized FP8 head per hidden row, best
+    first, ties to the smaller row, mapped through d2t: several draft
+    candidates per position taken from a quantized head, as the pages take a
+    drafter's candidates from the target's 4-bit head
+    (zone-1.cobraproject.com "Masked MTP drafts", "Update (November 2026)")."""
+    return topk_of_logits(oracle_logits_fp8(h_bits, codes, scale), d2t, k)

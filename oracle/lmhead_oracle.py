@@ -49,6 +49,7 @@ __all__ = [
     "oracle_scatter_logits",
     "oracle_project_argmax_indexed",
     "argmax_of_logits",
+    "topk_of_logits",
     "OracleResult",
     "TopkResult",
 ]
@@ -186,7 +187,13 @@ def oracle_project_topk(h_bits: np.ndarray, w_bits: np.ndarray,
     mapped through d2t as in "Two ways to run it" (zone-1.cobraproject.com
     "Masked MTP drafts").  If fewer than k rows exist, positions past R hold
     id -1 and logit -inf."""
-    logits = oracle_logits(h_bits, w_bits)
+    return topk_of_logits(oracle_logits(h_bits, w_bits), d2t, k)
+
+
+def topk_of_logits(logits: np.ndarray, d2t: np.ndarray | None, k: int) -> TopkResult:
+    """The k best of [M, R] fp64 logits per row, best first, ties to the
+    smaller row, mapped through d2t (the selection step of
+    oracle_project_topk, shared by the heads of every format)."""
     m, r = logits.shape
     if k < 1:
         raise ValueError("k must be at least 1")

@@ -34,11 +34,11 @@ from __future__ import annotations
 
 import numpy as np
 
-from .lmhead_oracle import OracleResult, argmax_of_logits, bf16_bits_to_f64
+from .lmhead_oracle import OracleResult, TopkResult, argmax_of_logits, bf16_bits_to_f64, topk_of_logits
 
 __all__ = ["MX_BLOCK", "E2M1_MAX", "e2m1_decode", "e2m1_encode", "oracle_quantize_mxfp4",
            "oracle_dequant_mxfp4", "oracle_logits_mxfp4", "oracle_project_argmax_mxfp4",
-           "unpack_nibbles", "pack_nibbles"]
+           "unpack_nibbles", "pack_nibbles", "oracle_project_topk_mxfp4"]
 
 MX_BLOCK = 32
 E2M1_MAX = 6.0
@@ -163,3 +163,11 @@ def oracle_project_argmax_mxfp4(h_bits, codes, scales, d2t=None, keep_logits: bo
     w_win = oracle_dequant_mxfp4(np.asarray(codes)[idx], np.asarray(scales)[idx])
     abs_sum = np.abs(h * w_win).sum(axis=1)
     return OracleResult(ids, idx, best, gap, abs_sum, logits if keep_logits else None)
+
+
+def oracle_project_topk_mxfp4(h_bits, codes, scales, d2t, k: int) -> TopkResult:
+    """The k best rows of the dequantized MXFP4 head per hidden row, best
+    first, ties to the smaller row, mapped through d2t: the candidates a
+    drafter takes from the target's 4-bit head (zone-1.cobraproject.com
+    "Masked MTP drafts", "Update (November 2026)")."""
+    return topk_of_logits(oracle_logits_mxfp4(h_bits, codes, scales), d2t, k)

@@ -197,10 +197,29 @@ def pin_planted_winner_fp8(m):
     assert m.oracle_project_argmax_fp8(h, codes, scale, d2t).id[0] == 900 - 1 - 417
 
 
+def pin_topk_equals_bf16_oracle(m):
+    """Power-of-two row scales make the dequantized head bf16-exact: the top
+    k over the FP8 head is the bf16 oracle's top k."""
+    rng = _rng(21)
+    w = _pow2_head(rng, 500, 128)
+    codes, scale = m.oracle_quantize_fp8(w)
+    w_deq = _bf16_exact(m.oracle_dequant_fp8(codes, scale).astype(np.float32))
+    h = synth.bf16_from_f32(rng.standard_normal((3, 128)).astype(np.float32))
+    d2t = (np.arange(500, dtype=np.int32) * 7 + 2)
+    for k in (1, 4, 16, 503):
+        a = m.oracle_project_topk_fp8(h, codes, scale, d2t, k)
+        b = lo.oracle_project_topk(h, w_deq, d2t, k)
+        assert np.array_equal(a.id, b.id) and np.array_equal(a.logit, b.logit)
+    t = m.oracle_project_topk_fp8(h, codes, scale, d2t, 6)
+    a = m.oracle_project_argmax_fp8(h, codes, scale, d2t)
+    assert np.array_equal(t.id[:, 0], a.id) and np.array_equal(t.logit[:, 0], a.logit)
+
+
 PINS = [pin_decode_known, pin_decode_all_vs_torch, pin_encode_vs_torch,
         pin_encode_nearest_bruteforce, pin_encode_saturates, pin_quantize_invariants,
         pin_quantize_commutes_with_trim, pin_projection_equals_bf16_oracle,
-        pin_projection_fsum, pin_planted_winner_fp8]
+        pin_projection_fsum, pin_planted_winner_fp8,
+        pin_topk_equals_bf16_oracle]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])

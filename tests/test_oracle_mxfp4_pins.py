@@ -172,9 +172,47 @@ def pin_planted_winner(m):
     assert res.id.tolist() == [77 * 3 + 1, 420 * 3 + 1]
 
 
+def pin_topk_equals_bf16_oracle(m):
+    """On a head whose dequantized values are bf16 numbers, the top k over
+    the MXFP4 head is the bf16 oracle's top k (ids, rows and logits),
+    including k past the number of rows."""
+    rng = np.random.default_rng(31)
+    packed, scales, w_bits = _representable_head(rng, 400, 256)
+    h = synth.hidden(32, 0, 3, 256)
+    ids = rng.permutation(1000)[:400].astype(np.int32)
+    for k in (1, 5, 16, 400, 403):
+        a = m.oracle_project_topk_mxfp4(h, packed, scales, ids, k)
+        b = lo.oracle_project_topk(h, w_bits, ids, k)
+        assert np.array_equal(a.id, b.id) and np.array_equal(a.idx, b.idx)
+        assert np.array_equal(a.logit, b.logit)
+
+
+def pin_topk_order_and_first(m):
+    """Best first, the first equal to the argmax, and the k logits are the k
+    largest dot products with the hand-dequantized rows."""
+    w_bits = synth.normal_bf16(33, 300, 512, 0.02)
+    codes, scales = m.oracle_quantize_mxfp4(w_bits)
+    h = synth.hidden(34, 0, 4, 512)
+    ids = (np.arange(300) * 5 + 3).astype(np.int32)
+    t = m.oracle_project_topk_mxfp4(h, codes, scales, ids, 8)
+    a = m.oracle_project_argmax_mxfp4(h, codes, scales, ids)
+    assert np.array_equal(t.id[:, 0], a.id) and np.array_equal(t.logit[:, 0], a.logit)
+    vals = np.array([0, .5, 1, 1.5, 2, 3, 4, 6, -0., -.5, -1, -1.5, -2, -3, -4, -6])
+    lo_nib, hi_nib = codes & 0xF, codes >> 4
+    deq = np.empty((300, 512))
+    deq[:, 0::2], deq[:, 1::2] = vals[lo_nib], vals[hi_nib]
+    deq *= np.repeat(np.ldexp(1.0, scales.astype(np.int64) - 127), 32, axis=1)
+    full = lo.bf16_bits_to_f64(h) @ deq.T
+    for i in range(4):
+        assert np.all(np.diff(t.logit[i]) <= 0)
+        assert np.allclose(t.logit[i], np.sort(full[i])[::-1][:8], rtol=1e-12, atol=1e-15)
+        assert np.array_equal(t.id[i], ids[t.idx[i]])
+
+
 PINS = [pin_decode_table, pin_encode_midpoints, pin_encode_saturates_and_round_trips,
         pin_block_scale_by_hand, pin_quantize_error_bound, pin_quantize_round_trip, pin_zero_block,
-        pin_projection_equals_bf16_oracle, pin_projection_fsum, pin_planted_winner]
+        pin_projection_equals_bf16_oracle, pin_projection_fsum, pin_planted_winner,
+        pin_topk_equals_bf16_oracle, pin_topk_order_and_first]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
@@ -274,7 +312,13 @@ def _mut_project_ignores_d2t(h, codes, scales, d2t=None, keep_logits=False):
     return _orig_project(h, codes, scales, None, keep_logits)
 
 
+def _mut_topk_ascending(h, codes, scales, d2t, k):
+    logits = _orig_logits(h, codes, scales)
+    return mx.topk_of_logits(-logits, d2t, k)
+
+
 MUTANTS = {
+    "topk_ascending": ("oracle_project_topk_mxfp4", _mut_topk_ascending),
     "encode_ties_up": ("e2m1_encode", _mut_encode_ties_up),
     "encode_truncates": ("e2m1_encode", _mut_encode_truncates),
     "encode_overflow_wraps_to_zero": ("e2m1_encode", _mut_encode_wraps),
