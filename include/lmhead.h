@@ -303,6 +303,35 @@ int draft_project_argmax_mxfp4(const uint16_t* h, int64_t M, int64_t K,
                                int path, void* stream);
 
 /*
+ * draft_project_topk_fp8, draft_project_topk_mxfp4 -- draft_project_topk
+ * over a quantized head: the `topk` best rows of the dequantized FP8 or
+ * MXFP4 head per hidden row, best first, mapped through d2t.  The pages
+ * take a drafter's candidates from the target's 4-bit head
+ * (zone-1.cobraproject.com "Masked MTP drafts", "Update (November 2026)");
+ * this is that scoring, several candidates per position.  Logits as for
+ * draft_project_argmax_fp8 / _mxfp4; order, ties and padding (positions
+ * past R hold id -1 and logit -inf) as for draft_project_topk.
+ *
+ *  Wq, scale / scales  the head as for draft_project_argmax_fp8 / _mxfp4.
+ *  topk                1 to LMH_MAX_TOPK.
+ *  workspace           draft_project_topk_workspace_bytes(M, topk) bytes.
+ *  path                LMH_PATH_AUTO or LMH_PATH_MFMA (the matrix cores).
+ * Errors and synchronization as for draft_project_topk.
+ */
+int draft_project_topk_fp8(const uint16_t* h, int64_t M, int64_t K,
+                           const uint8_t* Wq, const float* scale, int64_t R,
+                           const int32_t* d2t, int64_t topk,
+                           int32_t* out_id, float* out_logit,
+                           void* workspace, size_t workspace_bytes,
+                           int path, void* stream);
+int draft_project_topk_mxfp4(const uint16_t* h, int64_t M, int64_t K,
+                             const uint8_t* Wq, const uint8_t* scales,
+                             int64_t R, const int32_t* d2t, int64_t topk,
+                             int32_t* out_id, float* out_logit,
+                             void* workspace, size_t workspace_bytes,
+                             int path, void* stream);
+
+/*
  * draft_project_argmax_indexed -- the shortlisted argmax read straight from
  * the full head: for each hidden row m, over the list entries i with
  * ids[i] in [0, N),

@@ -127,19 +127,21 @@ def _check_core(h_bits, w_rows, r, d2t, gpu_id, gpu_logit, res, extra) -> Parity
     return st
 
 
-def row_bounds(h_bits, w_bits, rows=None) -> np.ndarray:
-    """(K+1) * 2**-24 * sum_k |h[m,k] W[r,k]| for every (m, r) (or the given
-    rows): the fp32 error bound of any summation order, as in check()."""
+def row_bounds(h_bits, w_bits, rows=None, w_rows=None, extra: int = 1) -> np.ndarray:
+    """(K + extra) * 2**-24 * sum_k |h[m,k] W[r,k]| for every (m, r) (or the
+    given rows): the fp32 error bound of any summation order, as in check().
+    `w_rows(rows)` gives fp64 rows of a quantized head instead of w_bits."""
     h = np.abs(oracle.bf16_bits_to_f64(np.asarray(h_bits)))
-    w_bits = np.asarray(w_bits)
-    if rows is not None:
-        w_bits = w_bits[rows]
+    if w_rows is None:
+        w_bits = np.asarray(w_bits)
+        rows = np.arange(w_bits.shape[0]) if rows is None else np.asarray(rows)
+        w_rows = lambda rr: oracle.bf16_bits_to_f64(w_bits[rr])
     k = h.shape[1]
-    out = np.empty((h.shape[0], w_bits.shape[0]))
-    for r0 in range(0, w_bits.shape[0], 8192):
-        wb = np.abs(oracle.bf16_bits_to_f64(w_bits[r0:r0 + 8192]))
+    out = np.empty((h.shape[0], len(rows)))
+    for r0 in range(0, len(rows), 8192):
+        wb = np.abs(w_rows(rows[r0:r0 + 8192]))
         out[:, r0:r0 + wb.shape[0]] = h @ wb.T
-    return (k + 1) * U32 * out + 1e-30
+    return (k + extra) * U32 * out + 1e-30
 
 
 def check_topk(h_bits, w_bits, d2t, gpu_ids, gpu_logits, res=None) -> ParityStats:
@@ -148,14 +150,38 @@ def check_topk(h_bits, w_bits, d2t, gpu_ids, gpu_logits, res=None) -> ParityStat
     logit; the id at j must equal the oracle's wherever both neighbouring
     gaps exceed 1e-2 (or twice the fp32 bound); logits are non-increasing,
     rows are distinct, and positions past R hold -1 / -inf."""
-    h_bits = np.asarray(h_bits)
     w_bits = np.asarray(w_bits)
+    if res is None:
+        res = oracle.oracle_project_topk(h_bits, w_bits, d2t, np.asarray(gpu_ids).shape[1])
+    return _check_topk_core(h_bits, lambda rr: oracle.bf16_bits_to_f64(w_bits[rr]), w_bits.shape[0], d2t,
+                            gpu_ids, gpu_logits, res, extra=1)
+
+
+def check_topk_fp8(h_bits, codes, scale, d2t, gpu_ids, gpu_logits, res=None) -> ParityStats:
+    """The top-k rule over an FP8 head (bound with K + 2 roundings, as in
+    check_fp8)."""
+    codes, scale = np.asarray(codes), np.asarray(scale)
+    if res is None:
+        res = oracle.oracle_project_topk_fp8(h_bits, codes, scale, d2t, np.asarray(gpu_ids).shape[1])
+    return _check_topk_core(h_bits, lambda rr: oracle.oracle_dequant_fp8(codes[rr], scale[rr]), codes.shape[0],
+                            d2t, gpu_ids, gpu_logits, res, extra=2)
+
+
+def check_topk_mxfp4(h_bits, codes, scales, d2t, gpu_ids, gpu_logits, res=None) -> ParityStats:
+    """The top-k rule over an MXFP4 head (the bf16 bound, as in
+    check_mxfp4)."""
+    codes, scales = np.asarray(codes), np.asarray(scales)
+    if res is None:
+        res = oracle.oracle_project_topk_mxfp4(h_bits, codes, scales, d2t, np.asarray(gpu_ids).shape[1])
+    return _check_topk_core(h_bits, lambda rr: oracle.oracle_dequant_mxfp4(codes[rr], scales[rr]),
+                            codes.shape[0], d2t, gpu_ids, gpu_logits, res, extra=1)
+
+
+def _check_topk_core(h_bits, w_rows, r, d2t, gpu_ids, gpu_logits, res, extra) -> ParityStats:
+    h_bits = np.asarray(h_bits)
     gpu_ids = np.asarray(gpu_ids).astype(np.int64)
     gpu_logits = np.asarray(gpu_logits).astype(np.float64)
     m, k = gpu_ids.shape
-    r = w_bits.shape[0]
-    if res is None:
-        res = oracle.oracle_project_topk(h_bits, w_bits, d2t, k)
     if d2t is None:
         to_row = lambda ids: ids
     else:
@@ -172,8 +198,8 @@ def check_topk(h_bits, w_bits, d2t, gpu_ids, gpu_logits, res=None) -> ParityStat
         assert np.unique(rows).size == kk, f"row {i}: repeated candidates"
         gl = gpu_logits[i, :kk]
         assert np.all(gl[:-1] >= gl[1:]), f"row {i}: logits not in descending order"
-        bnd = row_bounds(h_bits[i:i + 1], w_bits, rows)[0]
-        bnd_ref = row_bounds(h_bits[i:i + 1], w_bits, res.idx[i, :kk])[0]
+        bnd = row_bounds(h_bits[i:i + 1], None, rows, w_rows, extra)[0]
+        bnd_ref = row_bounds(h_bits[i:i + 1], None, res.idx[i, :kk], w_rows, extra)[0]
         srt = res.sorted_logits[i]
         bmax = 2 * float(max(bnd.max(), bnd_ref.max()))
         for j in range(kk):

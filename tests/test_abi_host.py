@@ -207,6 +207,28 @@ def test_mxfp4_scale_bytes_and_tiling_rejects(L):
     assert t(A, -3, 512, B, None) == 1
 
 
+def test_quantized_topk_rejects_on_host(L):
+    lib = L.lib()
+    ws = L.draft_project_topk_workspace_bytes(4, 8)
+    f8, f4 = lib.draft_project_topk_fp8, lib.draft_project_topk_mxfp4
+    # FP8: scale pointer 4-byte aligned; K % 16; no VALU path; topk 1-16; workspace
+    assert f8(A, 4, 2560, B, C, 100, None, 8, D, E, E, ws, 1, None) == 1
+    assert f8(A, 4, 2560, B, C, 100, None, 0, D, E, E, ws, 0, None) == 1
+    assert f8(A, 4, 2560, B, C, 100, None, 17, D, E, E, ws, 0, None) == 1
+    assert f8(A, 4, 2568, B, C, 100, None, 8, D, E, E, ws, 0, None) == 1
+    assert f8(A, 4, 2560, B, C + 2, 100, None, 8, D, E, E, ws, 0, None) == 1
+    assert f8(A, 4, 2560, B, C, 100, None, 8, None, E, E, ws, 0, None) == 1
+    assert f8(A, 4, 2560, B, C, 100, None, 8, D, E, E, ws - 1, 0, None) == 3
+    assert f8(A, 4, 2560, B, C, 100, None, 8, D, E, E + 8, ws, 0, None) == 3
+    # MXFP4: K % 512; no VALU path; topk 1-16; workspace
+    assert f4(A, 4, 2560, B, C, 100, None, 8, D, E, E, ws, 1, None) == 1
+    assert f4(A, 4, 2592, B, C, 100, None, 8, D, E, E, ws, 0, None) == 1
+    assert f4(A, 4, 2560, B, C, 100, None, 17, D, E, E, ws, 0, None) == 1
+    assert f4(A, 4, 2560, B, C + 4, 100, None, 8, D, E, E, ws, 0, None) == 1
+    assert f4(A, 33, 2560, B, C, 100, None, 8, D, E, E, ws, 0, None) == 1
+    assert f4(A, 4, 2560, B, C, 100, None, 8, D, E, E, ws - 1, 0, None) == 3
+
+
 def test_mxfp4_rejects_on_host(L):
     lib = L.lib()
     q = lib.lmhead_quantize_mxfp4

@@ -236,3 +236,55 @@ def test_fp8_repeat_bit_identical_and_rejects(L):
         assert code in (L.LMH_EINVAL, L.LMH_EWORKSPACE), cs
     torch.cuda.synchronize()
     assert bool((oid == 77).all()) and bool((olg == 5.0).all())
+
+
+# --------------------------------------------------------------------------
+# top k over the FP8 head
+# --------------------------------------------------------------------------
+
+def run_topk_fp8(L, h, codes, scale, d2t_np, topk, tag):
+    from parity import check_topk_fp8
+    res = oracle.oracle_project_topk_fp8(h, codes, scale, d2t_np, topk)
+    q_dev, s_dev = torch.from_numpy(codes).cuda(), torch.from_numpy(scale).cuda()
+    d2t_dev = dev_i32(d2t_np) if d2t_np is not None else None
+    for p in (L.LMH_PATH_AUTO, L.LMH_PATH_MFMA):
+        i, lg = L.draft_project_topk_fp8(dev_bf16(h), q_dev, s_dev, d2t_dev, topk, path=p)
+        st = check_topk_fp8(h, codes, scale, d2t_np, i.cpu().numpy(), lg.cpu().numpy(), res)
+        log(f"[{tag}] path={p} k={topk} positions={st.rows} exempt={st.exempt} max_err={st.max_err:.2e} "
+            f"err/bound={st.max_err_over_bound:.3f}")
+
+
+@pytest.mark.parametrize("cfg,trimmed,m,topk", [(2, False, 1, 8), (5, False, 24, 16), (3, True, 3, 4),
+                                                (5, True, 24, 8)])
+def test_fp8_topk_configs(L, cfg, trimmed, m, topk):
+    inp = config_inputs(cfg)
+    w, codes, scale = oracle_head(cfg, trimmed)
+    d2t = inp["ids"].astype(np.int32) if trimmed else None
+    h = draws(inp["config"], m, 1)[0]
+    run_topk_fp8(L, h, codes, scale, d2t, topk, f"fp8 top-k config {cfg} M={m}")
+
+
+FP8_TOPK_EDGE = [(1, 16, 1, 16), (3, 48, 5, 4), (17, 272, 1000, 16), (32, 8192, 40, 8), (24, 2560, 3001, 2)]
+
+
+@pytest.mark.parametrize("m,k,r,topk", FP8_TOPK_EDGE, ids=[f"M{m}-K{k}-R{r}-k{t}" for m, k, r, t in FP8_TOPK_EDGE])
+def test_fp8_topk_edges(L, m, k, r, topk):
+    w = synth.normal_bf16(17000 + r, r, k, 0.02)
+    codes, scale = oracle.oracle_quantize_fp8(w)
+    h = synth.hidden(18000 + k, 1, m, k)
+    d2t = (np.arange(r, dtype=np.int32)[::-1] * 5 + 7).copy()
+    run_topk_fp8(L, h, codes, scale, None, topk, f"fp8 top-k edge M={m} K={k} R={r}")
+    run_topk_fp8(L, h, codes, scale, d2t, topk, f"fp8 top-k edge d2t M={m} K={k} R={r}")
+
+
+def test_fp8_topk1_matches_argmax_and_rejects(L):
+    w = synth.normal_bf16(401, 20000, 2560, 0.02)
+    q, s = gpu_quantize(L, dev_bf16(w))
+    for m in (1, 5, 24):
+        h = dev_bf16(synth.hidden(402, m, m, 2560))
+        a = L.draft_project_argmax_fp8(h, q, s, None, L.LMH_PATH_MFMA)
+        t = L.draft_project_topk_fp8(h, q, s, None, 1)
+        assert torch.equal(t[0][:, 0], a[0]) and torch.equal(t[1][:, 0], a[1]), m
+    h = dev_bf16(synth.hidden(403, 0, 2, 2560))
+    with pytest.raises(L.LmheadError):
+        L.draft_project_topk_fp8(h, q, s, None, 4, path=L.LMH_PATH_VALU)

@@ -376,3 +376,97 @@ def test_mxfp4_bench_helper_matches_call(L):
     assert torch.equal(oid, i) and torch.equal(olg, lg)
     res = oracle.oracle_project_argmax_mxfp4(synth.hidden(256, 0, 4, 2560), codes, scales, keep_logits=True)
     check_mxfp4(synth.hidden(256, 0, 4, 2560), codes, scales, None, i.cpu().numpy(), lg.cpu().numpy(), res)
+
+
+# --------------------------------------------------------------------------
+# top k over the MXFP4 head
+# --------------------------------------------------------------------------
+
+def run_topk_mx(L, h, codes, scales, d2t_np, topk, tag):
+    from parity import check_topk_mxfp4
+    res = oracle.oracle_project_topk_mxfp4(h, codes, scales, d2t_np, topk)
+    q_dev, s_dev = dev_u8(codes), dev_u8(tile_scales(scales))
+    d2t_dev = dev_i32(d2t_np) if d2t_np is not None else None
+    for p in (L.LMH_PATH_AUTO, L.LMH_PATH_MFMA):
+        i, lg = L.draft_project_topk_mxfp4(dev_bf16(h), q_dev, s_dev, d2t_dev, topk, path=p)
+        st = check_topk_mxfp4(h, codes, scales, d2t_np, i.cpu().numpy(), lg.cpu().numpy(), res)
+        log(f"[{tag}] path={p} k={topk} positions={st.rows} exempt={st.exempt} max_err={st.max_err:.2e} "
+            f"err/bound={st.max_err_over_bound:.3f}")
+
+
+@pytest.mark.parametrize("cfg,trimmed,m,topk", [
+    (2, False, 1, 8), (2, False, 4, 16), (5, False, 24, 4), (3, True, 3, 16), (4, True, 1, 1), (5, True, 24, 8),
+])
+def test_mxfp4_topk_configs(L, cfg, trimmed, m, topk):
+    """Candidates from the 4-bit head: the full head and the lists."""
+    inp = config_inputs(cfg)
+    codes, scales = oracle_full_head()
+    d2t = None
+    if trimmed:
+        ids = inp["ids"]
+        codes, scales = codes[ids], scales[ids]
+        d2t = ids.astype(np.int32)
+    h = draws(inp["config"], m, 1)[0]
+    run_topk_mx(L, h, codes, scales, d2t, topk, f"mxfp4 top-k config {cfg} M={m}")
+
+
+TOPK_EDGE = [(1, 512, 1, 16), (3, 512, 5, 4), (2, 1024, 17, 16), (17, 1024, 1000, 16), (32, 8192, 40, 8),
+             (24, 2560, 3001, 2), (5, 1536, 4099, 3)]
+
+
+@pytest.mark.parametrize("m,k,r,topk", TOPK_EDGE, ids=[f"M{m}-K{k}-R{r}-k{t}" for m, k, r, t in TOPK_EDGE])
+def test_mxfp4_topk_edges(L, m, k, r, topk):
+    w = synth.normal_bf16(27000 + r, r, k, 0.02)
+    codes, scales = oracle.oracle_quantize_mxfp4(w)
+    h = synth.hidden(28000 + k, 0, m, k)
+    d2t = (np.arange(r, dtype=np.int32)[::-1] * 5 + 7).copy()
+    run_topk_mx(L, h, codes, scales, None, topk, f"mxfp4 top-k edge M={m} K={k} R={r}")
+    run_topk_mx(L, h, codes, scales, d2t, topk, f"mxfp4 top-k edge d2t M={m} K={k} R={r}")
+
+
+def test_mxfp4_topk1_matches_argmax_and_ties(L):
+    """k = 1 gives the argmax call's id and logit bits (same kernel); planted
+    exact ties (E2M1 values, scale 1, integer hidden rows) come out smaller
+    row first, every position equal to the oracle's."""
+    w = synth.normal_bf16(301, 20000, 2560, 0.02)
+    codes, scales = oracle.oracle_quantize_mxfp4(w)
+    q_dev, s_dev = dev_u8(codes), dev_u8(tile_scales(scales))
+    for m in (1, 4, 24):
+        h = dev_bf16(synth.hidden(302, m, m, 2560))
+        a = L.draft_project_argmax_mxfp4(h, q_dev, s_dev)
+        t = L.draft_project_topk_mxfp4(h, q_dev, s_dev, None, 1)
+        assert torch.equal(t[0][:, 0], a[0]) and torch.equal(t[1][:, 0], a[1]), m
+    rng = np.random.default_rng(303)
+    r, k, m = 40_000, 512, 3
+    wi = rng.choice(np.array([-2, -1, 0, 1, 2], dtype=np.float64), size=(r, k))
+    wi[:, ::32] = 4.0
+    hi = rng.integers(-1, 2, size=(m, k)).astype(np.float64)
+    hi[:, ::32] = 0
+    for j in range(m):
+        for rr in (39_001, 5 + j, 20_000, 12_345):
+            wi[rr] = np.where(np.arange(k) % 32 == 0, 4.0, 2.0 * np.sign(hi[j]))
+    wb, hb = synth.bf16_from_f32(wi.astype(np.float32)), synth.bf16_from_f32(hi.astype(np.float32))
+    codes, scales = oracle.oracle_quantize_mxfp4(wb)
+    res = oracle.oracle_project_topk_mxfp4(hb, codes, scales, None, 6)
+    i, lg = L.draft_project_topk_mxfp4(dev_bf16(hb), dev_u8(codes), dev_u8(tile_scales(scales)), None, 6)
+    assert np.array_equal(i.cpu().numpy(), res.id)
+    assert np.array_equal(lg.cpu().numpy().astype(np.float64), res.logit)
+
+
+def test_mxfp4_topk_rejects(L):
+    """No VALU path, topk outside 1-16 rejected; a rejected call writes
+    nothing."""
+    w = synth.normal_bf16(311, 100, 512, 0.02)
+    q, s = gpu_quantize(L, dev_bf16(w))
+    h = dev_bf16(synth.hidden(312, 0, 2, 512))
+    with pytest.raises(L.LmheadError):
+        L.draft_project_topk_mxfp4(h, q, s, None, 4, path=L.LMH_PATH_VALU)
+    oid = torch.full((2, 16), 7, dtype=torch.int32, device="cuda")
+    olg = torch.full((2, 16), 5.0, device="cuda")
+    ws = torch.empty(L.draft_project_topk_workspace_bytes(2, 16), dtype=torch.uint8, device="cuda")
+    for topk in (0, 17):
+        code = L.lib().draft_project_topk_mxfp4(h.data_ptr(), 2, 512, q.data_ptr(), s.data_ptr(), 100, None, topk,
+                                                oid.data_ptr(), olg.data_ptr(), ws.data_ptr(), ws.numel(), 0, None)
+        assert code == L.LMH_EINVAL
+    torch.cuda.synchronize()
+    assert bool((oid == 7).all()) and bool((olg == 5.0).all())

@@ -2185,8 +2185,8 @@ int launch_finalize_topk(unsigned long long* slots, int nslots, int m_base, int 
 }
 
 // What one call asks for.  `fmt` is the head's format: bf16, or (argmax
-// only) E4M3 codes with one fp32 scale per row in `wscale`, or MXFP4 codes
-// with one E8M0 scale per 32 elements in `wscale`.
+// and top k) E4M3 codes with one fp32 scale per row in `wscale`, or MXFP4
+// codes with one E8M0 scale per 32 elements in `wscale`.
 struct Call {
   const uint16_t* h;
   int M;
@@ -2226,7 +2226,7 @@ int run(const Call& c, const Epi& epi, int topk, int32_t* out_id, float* out_log
   };
   const bool fp8 = c.fmt == kFmtFp8;
   const bool mx4 = c.fmt == kFmtMx4;
-  if ((fp8 || mx4) && MODE != 0) return LMH_EINVAL;
+  if ((fp8 || mx4) && MODE == 2) return LMH_EINVAL;  // quantized heads: argmax and top k
   if ((fp8 || mx4) && !c.wscale) return LMH_EINVAL;
   constexpr bool kIdxOk = MODE == 0 && TK == 1;
   if (c.indexed && (!kIdxOk || c.fmt != kFmtBf16 || !epi.rowmap)) return LMH_EINVAL;
@@ -2234,6 +2234,7 @@ int run(const Call& c, const Epi& epi, int topk, int32_t* out_id, float* out_log
     int grid = 0;
     if (mx4) return LMH_EINVAL;  // MXFP4 heads take the matrix cores only
     if (fp8) {
+      if constexpr (MODE != 0) return LMH_EINVAL;  // top k over an FP8 head: matrix cores only
       st = launch_valu_fp8(c.h, c.M, c.K, static_cast<const uint8_t*>(c.W), static_cast<const float*>(c.wscale),
                            c.R, epi, cus, c.stream, &grid);
     } else {
@@ -2255,16 +2256,17 @@ int run(const Call& c, const Epi& epi, int topk, int32_t* out_id, float* out_log
   for (int m0 = 0; m0 < c.M; m0 += per) {
     const int mp = std::min(per, c.M - m0);
     int grid = 0;
-    if constexpr (kIdxOk) {
-      if (fp8)
-        st = launch_mfma_pass<TK, LOGITS, kFmtFp8>(c.h, c.K, m0, mp, c.W, c.wscale, c.R, epi, cus, c.stream, &grid);
-      else if (mx4)
-        st = launch_mfma_pass<TK, LOGITS, kFmtMx4>(c.h, c.K, m0, mp, c.W, c.wscale, c.R, epi, cus, c.stream, &grid);
-      else if (c.indexed)
+    if (fp8 || mx4) {
+      if constexpr (MODE != 2) {
+        st = fp8 ? launch_mfma_pass<TK, LOGITS, kFmtFp8>(c.h, c.K, m0, mp, c.W, c.wscale, c.R, epi, cus, c.stream,
+                                                         &grid)
+                 : launch_mfma_pass<TK, LOGITS, kFmtMx4>(c.h, c.K, m0, mp, c.W, c.wscale, c.R, epi, cus, c.stream,
+                                                         &grid);
+      }
+    } else if (c.indexed) {
+      if constexpr (kIdxOk)
         st = launch_mfma_pass<TK, LOGITS, kFmtBf16, true>(c.h, c.K, m0, mp, c.W, nullptr, c.R, epi, cus, c.stream,
                                                           &grid);
-      else
-        st = launch_mfma_pass<TK, LOGITS, kFmtBf16>(c.h, c.K, m0, mp, c.W, nullptr, c.R, epi, cus, c.stream, &grid);
     } else {
       st = launch_mfma_pass<TK, LOGITS, kFmtBf16>(c.h, c.K, m0, mp, c.W, nullptr, c.R, epi, cus, c.stream, &grid);
     }
@@ -2375,6 +2377,17 @@ int topk_width(int64_t topk) {
   return topk <= 1 ? 1 : topk <= 2 ? 2 : topk <= 4 ? 4 : topk <= 8 ? 8 : 16;
 }
 
+// The top-k run for `topk` (1-16), on the list width that holds it.
+int run_topk(const Call& c, const Epi& epi, int64_t topk, int32_t* out_id, float* out_logit) {
+  switch (topk_width(topk)) {
+    case 1: return run<1, 1>(c, epi, (int)topk, out_id, out_logit);
+    case 2: return run<1, 2>(c, epi, (int)topk, out_id, out_logit);
+    case 4: return run<1, 4>(c, epi, (int)topk, out_id, out_logit);
+    case 8: return run<1, 8>(c, epi, (int)topk, out_id, out_logit);
+    default: return run<1, 16>(c, epi, (int)topk, out_id, out_logit);
+  }
+}
+
 }  // namespace
 
 // ---------------------------------------------------------------------------
@@ -2456,23 +2469,24 @@ size_t draft_project_topk_workspace_bytes(int64_t M, int64_t topk) {
   return (size_t)M * kMaxGrid * topk_width(topk) * sizeof(unsigned long long);
 }
 
+// Output and workspace checks of a top-k call.
+static int check_topk_io(int64_t M, int64_t topk, const int32_t* out_id, const float* out_logit,
+                         const void* workspace, size_t workspace_bytes) {
+  if (topk < 1 || topk > LMH_MAX_TOPK || !out_id || !out_logit) return LMH_EINVAL;
+  if (!workspace || !aligned16(workspace)) return LMH_EWORKSPACE;
+  if (workspace_bytes < draft_project_topk_workspace_bytes(M, topk)) return LMH_EWORKSPACE;
+  return LMH_OK;
+}
+
 int draft_project_topk(const uint16_t* h, int64_t M, int64_t K, const uint16_t* W, int64_t R,
                        const int32_t* d2t, int64_t topk, int32_t* out_id, float* out_logit, void* workspace,
                        size_t workspace_bytes, int path, void* stream) {
   int st = check_common(h, M, K, W, R, 1, &path);
   if (st != LMH_OK) return st;
-  if (topk < 1 || topk > LMH_MAX_TOPK || !out_id || !out_logit) return LMH_EINVAL;
-  if (!workspace || !aligned16(workspace)) return LMH_EWORKSPACE;
-  if (workspace_bytes < draft_project_topk_workspace_bytes(M, topk)) return LMH_EWORKSPACE;
+  if ((st = check_topk_io(M, topk, out_id, out_logit, workspace, workspace_bytes)) != LMH_OK) return st;
   const Call c{h, (int)M, (int)K, W, (int)R, d2t, path, static_cast<hipStream_t>(stream)};
   const Epi epi{static_cast<unsigned long long*>(workspace), nullptr, nullptr, 0, 0};
-  switch (topk_width(topk)) {
-    case 1: return run<1, 1>(c, epi, (int)topk, out_id, out_logit);
-    case 2: return run<1, 2>(c, epi, (int)topk, out_id, out_logit);
-    case 4: return run<1, 4>(c, epi, (int)topk, out_id, out_logit);
-    case 8: return run<1, 8>(c, epi, (int)topk, out_id, out_logit);
-    default: return run<1, 16>(c, epi, (int)topk, out_id, out_logit);
-  }
+  return run_topk(c, epi, topk, out_id, out_logit);
 }
 
 int draft_project_logits(const uint16_t* h, int64_t M, int64_t K, const uint16_t* W, int64_t R,
@@ -2560,6 +2574,33 @@ int draft_project_argmax_fp8(const uint16_t* h, int64_t M, int64_t K, const uint
   c.fmt = kFmtFp8;
   const Epi epi{static_cast<unsigned long long*>(workspace), nullptr, nullptr, 0, 0};
   return run<0, 1>(c, epi, 1, out_id, out_logit);
+}
+
+int draft_project_topk_fp8(const uint16_t* h, int64_t M, int64_t K, const uint8_t* Wq, const float* scale,
+                           int64_t R, const int32_t* d2t, int64_t topk, int32_t* out_id, float* out_logit,
+                           void* workspace, size_t workspace_bytes, int path, void* stream) {
+  int st = check_fp8(h, M, K, Wq, scale, R, &path);
+  if (st != LMH_OK) return st;
+  if (path != LMH_PATH_MFMA) return LMH_EINVAL;  // top k over an FP8 head: matrix cores only
+  if ((st = check_topk_io(M, topk, out_id, out_logit, workspace, workspace_bytes)) != LMH_OK) return st;
+  Call c{h, (int)M, (int)K, Wq, (int)R, d2t, path, static_cast<hipStream_t>(stream)};
+  c.wscale = scale;
+  c.fmt = kFmtFp8;
+  const Epi epi{static_cast<unsigned long long*>(workspace), nullptr, nullptr, 0, 0};
+  return run_topk(c, epi, topk, out_id, out_logit);
+}
+
+int draft_project_topk_mxfp4(const uint16_t* h, int64_t M, int64_t K, const uint8_t* Wq, const uint8_t* scales,
+                             int64_t R, const int32_t* d2t, int64_t topk, int32_t* out_id, float* out_logit,
+                             void* workspace, size_t workspace_bytes, int path, void* stream) {
+  int st = check_mx4(h, M, K, Wq, scales, R, &path);
+  if (st != LMH_OK) return st;
+  if ((st = check_topk_io(M, topk, out_id, out_logit, workspace, workspace_bytes)) != LMH_OK) return st;
+  Call c{h, (int)M, (int)K, Wq, (int)R, d2t, path, static_cast<hipStream_t>(stream)};
+  c.wscale = scales;
+  c.fmt = kFmtMx4;
+  const Epi epi{static_cast<unsigned long long*>(workspace), nullptr, nullptr, 0, 0};
+  return run_topk(c, epi, topk, out_id, out_logit);
 }
 
 int64_t lmhead_mxfp4_scale_bytes(int64_t R, int64_t K) {

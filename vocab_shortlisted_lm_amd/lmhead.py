@@ -27,7 +27,7 @@ __all__ = [
     "LMH_MAX_OVERWRITE", "LMH_MAX_UNION_VOCAB", "draft_project_argmax_indexed",
     "lmhead_bench_time_argmax_indexed", "lmhead_quantize_mxfp4", "draft_project_argmax_mxfp4",
     "lmhead_bench_time_argmax_mxfp4", "lmhead_mxfp4_scale_bytes", "lmhead_mxfp4_tile_scales",
-    "mxfp4_scale_shape",
+    "mxfp4_scale_shape", "draft_project_topk_fp8", "draft_project_topk_mxfp4",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "liblmhead.so")
@@ -74,6 +74,8 @@ SIGNATURES = {
     "draft_project_argmax_mxfp4": (_INT, [_P, _I64, _I64, _P, _P, _I64, _P, _P, _P, _P, _SZ, _INT, _P]),
     "lmhead_bench_time_argmax_mxfp4": (_INT, [_P, _I64, _I64, _P, _P, _INT, _I64, _P, _P, _P, _P, _SZ, _INT, _INT,
                                               ctypes.POINTER(ctypes.c_double), _P]),
+    "draft_project_topk_fp8": (_INT, [_P, _I64, _I64, _P, _P, _I64, _P, _I64, _P, _P, _P, _SZ, _INT, _P]),
+    "draft_project_topk_mxfp4": (_INT, [_P, _I64, _I64, _P, _P, _I64, _P, _I64, _P, _P, _P, _SZ, _INT, _P]),
 }
 
 _lib = None
@@ -654,3 +656,51 @@ def lmhead_bench_time_argmax_mxfp4(h: torch.Tensor, heads: list, d2t: torch.Tens
         out_id.data_ptr(), out_logit.data_ptr(), workspace.data_ptr(), _nbytes(workspace), path, calls,
         ctypes.byref(out), st), "lmhead_bench_time_argmax_mxfp4")
     return out.value
+
+
+def _topk_io(m, topk, out_id, out_logit, workspace, device):
+    if out_id is None:
+        out_id = torch.empty((m, topk), dtype=torch.int32, device=device)
+    if out_logit is None:
+        out_logit = torch.empty((m, topk), dtype=torch.float32, device=device)
+    _dev_tensor(out_id, "out_id", (torch.int32,), 2, device)
+    _dev_tensor(out_logit, "out_logit", (torch.float32,), 2, device)
+    if tuple(out_id.shape) != (m, topk) or tuple(out_logit.shape) != (m, topk):
+        raise ValueError("outputs must be [M, topk]")
+    if workspace is None:
+        nbytes = draft_project_topk_workspace_bytes(m, topk)
+        if nbytes == 0:
+            raise LmheadError(LMH_EINVAL, "top k")
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=device)
+    _dev_tensor(workspace, "workspace", None, None, device)
+    return out_id, out_logit, workspace
+
+
+def draft_project_topk_fp8(h: torch.Tensor, Wq: torch.Tensor, scale: torch.Tensor, d2t: torch.Tensor | None,
+                           topk: int, out_id: torch.Tensor | None = None, out_logit: torch.Tensor | None = None,
+                           workspace: torch.Tensor | None = None, path: int = LMH_PATH_AUTO, stream=None):
+    """(ids int32 [M, topk], logits float32 [M, topk]): the topk best rows of
+    the dequantized FP8 head per hidden row, best first, mapped through d2t.
+    Never synchronizes."""
+    m, k, r = _check_fp8_head(h, Wq, scale, d2t)
+    out_id, out_logit, workspace = _topk_io(m, topk, out_id, out_logit, workspace, h.device)
+    _check(lib().draft_project_topk_fp8(
+        h.data_ptr(), m, k, Wq.data_ptr(), scale.data_ptr(), r, d2t.data_ptr() if d2t is not None else None,
+        topk, out_id.data_ptr(), out_logit.data_ptr(), workspace.data_ptr(), _nbytes(workspace), path,
+        _stream(stream, h.device)), "draft_project_topk_fp8")
+    return out_id, out_logit
+
+
+def draft_project_topk_mxfp4(h: torch.Tensor, Wq: torch.Tensor, scales: torch.Tensor, d2t: torch.Tensor | None,
+                             topk: int, out_id: torch.Tensor | None = None, out_logit: torch.Tensor | None = None,
+                             workspace: torch.Tensor | None = None, path: int = LMH_PATH_AUTO, stream=None):
+    """(ids int32 [M, topk], logits float32 [M, topk]): the topk best rows of
+    the dequantized MXFP4 head per hidden row, best first, mapped through
+    d2t.  Never synchronizes."""
+    m, k, r = _check_mx4_head(h, Wq, scales, d2t)
+    out_id, out_logit, workspace = _topk_io(m, topk, out_id, out_logit, workspace, h.device)
+    _check(lib().draft_project_topk_mxfp4(
+        h.data_ptr(), m, k, Wq.data_ptr(), scales.data_ptr(), r, d2t.data_ptr() if d2t is not None else None,
+        topk, out_id.data_ptr(), out_logit.data_ptr(), workspace.data_ptr(), _nbytes(workspace), path,
+        _stream(stream, h.device)), "draft_project_topk_mxfp4")
+    return out_id, out_logit
