@@ -175,3 +175,48 @@ def test_random_shape_topk_logits(L, case):
             out = L.draft_project_logits(h_dev, w_dev, d2t_dev, n=n if with_d2t else None, path=p)
             st = check_logits(h, w, d2t, n if with_d2t else None, out.cpu().numpy())
     log(f"[random epilogue {i}] max_err={st.max_err:.2e} err/bound={st.max_err_over_bound:.3f}")
+
+
+def _qtopk_cases(n=40, seed=20261204):
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        fmt = "fp8" if i % 2 else "mx4"
+        m = int(rng.choice(MS))
+        kmax = 1024 if rng.random() < 0.5 else 8192
+        k = 512 * int(rng.integers(1, kmax // 512 + 1)) if fmt == "mx4" else 16 * int(rng.integers(1, kmax // 16 + 1))
+        rmax = max(1, min(40_000, 12_000_000 // k))
+        r = int(rng.integers(1, min(rmax, 600) + 1)) if rng.random() < 0.5 or rmax <= 600 else \
+            int(np.exp(rng.uniform(np.log(600), np.log(rmax))))
+        out.append((i, fmt, m, k, r, bool(rng.random() < 0.5), int(rng.integers(1, 17))))
+    return out
+
+
+QTOPK_CASES = _qtopk_cases()
+
+
+@pytest.mark.parametrize("case", QTOPK_CASES,
+                         ids=[f"{c[0]}-{c[1]}-M{c[2]}-K{c[3]}-R{c[4]}{'-d2t' if c[5] else ''}-k{c[6]}"
+                              for c in QTOPK_CASES])
+def test_random_shape_quantized_topk(L, case):
+    from parity import check_topk_fp8, check_topk_mxfp4
+    i, fmt, m, k, r, with_d2t, topk = case
+    log(f"[random quantized top-k {i}] {fmt} M={m} K={k} R={r} d2t={with_d2t} topk={topk}")
+    rng = np.random.default_rng(9000 + i)
+    w = synth.normal_bf16(9100 + i, r, k, 0.02)
+    h = synth.hidden(9200 + i, 0, m, k)
+    d2t = _ids(rng, r, r + int(rng.integers(0, 2 * r + 1))) if with_d2t else None
+    d2t_dev = dev_i32(d2t) if d2t is not None else None
+    if fmt == "fp8":
+        codes, scale = oracle.oracle_quantize_fp8(w)
+        res = oracle.oracle_project_topk_fp8(h, codes, scale, d2t, topk)
+        ids, lgs = L.draft_project_topk_fp8(dev_bf16(h), torch.from_numpy(codes).cuda(),
+                                            torch.from_numpy(scale).cuda(), d2t_dev, topk)
+        st = check_topk_fp8(h, codes, scale, d2t, ids.cpu().numpy(), lgs.cpu().numpy(), res)
+    else:
+        codes, scales = oracle.oracle_quantize_mxfp4(w)
+        res = oracle.oracle_project_topk_mxfp4(h, codes, scales, d2t, topk)
+        ids, lgs = L.draft_project_topk_mxfp4(dev_bf16(h), torch.from_numpy(codes).cuda(),
+                                              torch.from_numpy(_tile_scales(scales)).cuda(), d2t_dev, topk)
+        st = check_topk_mxfp4(h, codes, scales, d2t, ids.cpu().numpy(), lgs.cpu().numpy(), res)
+    log(f"[random quantized top-k {i}] max_err={st.max_err:.2e} err/bound={st.max_err_over_bound:.3f}")
