@@ -298,6 +298,8 @@ def main() -> int:
     ap.add_argument("--full", action="store_true", help="project the full head even for a shortlist config")
     ap.add_argument("--path", default="auto", choices=["auto", "valu", "mfma"])
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--repeats", type=int, default=5,
+                    help="timed regions of --steps calls (the first gives `value`; all give the spread)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--stream-read", action="store_true",
                     help="also time the plain streaming-read kernel over W (practical ceiling)")
@@ -415,6 +417,18 @@ def main() -> int:
     ms_per_step = ms_total / a.steps
     calls_per_s = a.steps / (ms_total / 1e3)
 
+    # The same timed region again, for the spread of the rate (the first
+    # region alone gives `value`).
+    rates = [calls_per_s]
+    for _ in range(max(0, a.repeats - 1)):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(a.steps):
+            step(i)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        rates.append(a.steps / (e0.elapsed_time(e1) / 1e3))
+
     # The projection kernel alone: as many launches again, back to back on
     # this stream between two HIP events the library records (no fold).
     if a.indexed:
@@ -425,6 +439,18 @@ def main() -> int:
         proj_ms = L.lmhead_bench_time_argmax_mxfp4(h, heads, d2t, path, a.steps, out_id, out_logit, ws, stream)
     else:
         proj_ms = L.lmhead_bench_time_argmax(h, heads, d2t, path, a.steps, out_id, out_logit, ws, stream)
+    # a rotated workload also timed on one copy, which the Infinity Cache can hold
+    proj_ms_hot = None
+    if len(heads) > 1:
+        one = heads[:1]
+        if a.indexed:
+            proj_ms_hot = L.lmhead_bench_time_argmax_indexed(h, one, d2t, path, a.steps, out_id, out_logit, ws, stream)
+        elif a.fp8:
+            proj_ms_hot = L.lmhead_bench_time_argmax_fp8(h, one, d2t, path, a.steps, out_id, out_logit, ws, stream)
+        elif a.mxfp4:
+            proj_ms_hot = L.lmhead_bench_time_argmax_mxfp4(h, one, d2t, path, a.steps, out_id, out_logit, ws, stream)
+        else:
+            proj_ms_hot = L.lmhead_bench_time_argmax(h, one, d2t, path, a.steps, out_id, out_logit, ws, stream)
     pbytes = projection_bytes(m, rows, c.k, d["fmt"], a.indexed)
     achieved = pbytes / (proj_ms / 1e3) / 1e9
     abytes = algorithmic_bytes(m, rows, c.k, d2t is not None, d["fmt"], a.indexed)
@@ -482,7 +508,13 @@ def main() -> int:
                      "step_gbps": round(abytes / (ms_per_step / 1e3) / 1e9, 1),
                      "algorithmic_bytes_per_step": abytes},
         "wall_s": round(wall, 3),
+        "repeats": {"n": len(rates), "unit": "calls/s", "median": round(float(np.median(rates)), 2),
+                    "p10": round(float(np.percentile(rates, 10)), 2),
+                    "p90": round(float(np.percentile(rates, 90)), 2)},
     }
+    if proj_ms_hot is not None:
+        result["mall"] = {"copies": len(heads), "kernel_avg_us_rotated": round(proj_ms * 1e3, 2),
+                          "kernel_avg_us_one_copy": round(proj_ms_hot * 1e3, 2)}
     result.update(extra)
     if not a.no_cpu_baseline and d["fmt"] == "bf16":
         hb = h_np
