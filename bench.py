@@ -99,6 +99,14 @@ def describe(a, synth, L):
                     else f"{c.name}: M={m} K={c.k} full head N={c.n}")
     if a.fp8 and a.mxfp4:
         raise SystemExit("bench.py: --fp8 and --mxfp4 exclude each other")
+    if a.topk and a.logits:
+        raise SystemExit("bench.py: --topk and --logits exclude each other")
+    if (a.topk or a.logits) and a.indexed:
+        raise SystemExit("bench.py: --topk and --logits time trimmed or full heads, not --indexed")
+    if a.logits and (a.fp8 or a.mxfp4):
+        raise SystemExit("bench.py: --logits takes a bf16 head")
+    if a.topk and not 1 <= a.topk <= L.LMH_MAX_TOPK:
+        raise SystemExit(f"bench.py: --topk must be 1..{L.LMH_MAX_TOPK}")
     if a.indexed:
         if ids is None or a.full or a.fp8 or a.mxfp4:
             raise SystemExit("bench.py: --indexed needs a shortlist config (1, 3, 4, 5), without --full, "
@@ -315,6 +323,13 @@ def main() -> int:
     ap.add_argument("--indexed", action="store_true",
                     help="read the shortlist's rows in place from the full head "
                          "(draft_project_argmax_indexed), rotating copies of W past the Infinity Cache")
+    ap.add_argument("--topk", type=int, default=0,
+                    help="time the top-k call (draft_project_topk, or its FP8 / MXFP4 form) with this k "
+                         "instead of the argmax; whole calls only")
+    ap.add_argument("--logits", choices=["rows", "vocab"], default=None,
+                    help="time draft_project_logits instead of the argmax: every logit as [M, R] (rows), "
+                         "or scattered through d2t into [M, N] with -inf elsewhere (vocab; the full head "
+                         "takes d2t = 0..N-1); bf16 heads; whole calls only")
     ap.add_argument("--shortlist-ops", action="store_true",
                     help="instead of the projection: time the list gathers, the device union of two lists "
                          "and 600 escaped ids written into spare rows (one JSON line)")
@@ -387,9 +402,34 @@ def main() -> int:
     out_id = torch.empty(m, dtype=torch.int32, device=dev)
     out_logit = torch.empty(m, dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream(dev)
+    out_bytes = 8 * m
+    if a.topk:
+        tk_id = torch.empty((m, a.topk), dtype=torch.int32, device=dev)
+        tk_logit = torch.empty((m, a.topk), dtype=torch.float32, device=dev)
+        tk_ws = torch.empty(L.draft_project_topk_workspace_bytes(m, a.topk), dtype=torch.uint8, device=dev)
+        out_bytes = 8 * m * a.topk
+    if a.logits:
+        lg_d2t = None
+        if a.logits == "vocab":
+            lg_d2t = d2t if d2t is not None else torch.arange(c.n, dtype=torch.int32, device=dev)
+        lg_cols = c.n if lg_d2t is not None else rows
+        lg_out = torch.empty((m, lg_cols), dtype=torch.float32, device=dev)
+        out_bytes = 4 * m * lg_cols
 
     def step(i):
-        if a.indexed:
+        if a.topk:
+            if a.fp8:
+                q, sc = heads[i % len(heads)]
+                L.draft_project_topk_fp8(h, q, sc, d2t, a.topk, tk_id, tk_logit, tk_ws, path, stream)
+            elif a.mxfp4:
+                q, sc = heads[i % len(heads)]
+                L.draft_project_topk_mxfp4(h, q, sc, d2t, a.topk, tk_id, tk_logit, tk_ws, path, stream)
+            else:
+                L.draft_project_topk(h, heads[i % len(heads)], d2t, a.topk, tk_id, tk_logit, tk_ws, path, stream)
+        elif a.logits:
+            L.draft_project_logits(h, heads[i % len(heads)], lg_d2t, c.n if lg_d2t is not None else None,
+                                   lg_out, path, stream)
+        elif a.indexed:
             L.draft_project_argmax_indexed(h, heads[i % len(heads)], d2t, path, out_id, out_logit, ws, stream)
         elif a.fp8:
             q, sc = heads[i % len(heads)]
@@ -428,6 +468,22 @@ def main() -> int:
         e1.record(stream)
         torch.cuda.synchronize()
         rates.append(a.steps / (e0.elapsed_time(e1) / 1e3))
+
+    if a.topk or a.logits:
+        # whole calls only: the kernel-only timer covers the argmax epilogue
+        result = {
+            "mode": f"top-{a.topk}" if a.topk else f"logits ({a.logits})",
+            "workload": workload, "M": m, "K": c.k, "rows": rows, "fmt": d["fmt"], "steps": a.steps,
+            "warmup": a.warmup, "us_per_call": round(ms_per_step * 1e3, 2),
+            "repeats_us_per_call": {"median": round(float(np.median([1e6 / r for r in rates])), 2),
+                                    "p10": round(float(np.percentile([1e6 / r for r in rates], 10)), 2),
+                                    "p90": round(float(np.percentile([1e6 / r for r in rates], 90)), 2),
+                                    "n": len(rates)},
+            "bytes_per_call": projection_bytes(m, rows, c.k, d["fmt"]) + out_bytes,
+        }
+        result["gbps"] = round(result["bytes_per_call"] / (ms_per_step / 1e3) / 1e9, 1)
+        print(json.dumps(result), flush=True)
+        return 0
 
     # The projection kernel alone: as many launches again, back to back on
     # this stream between two HIP events the library records (no fold).

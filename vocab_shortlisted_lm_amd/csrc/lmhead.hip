@@ -451,6 +451,55 @@ __device__ __forceinline__ void col_merge(unsigned long long (&list)[4], unsigne
   col_stages<false, 16, 8>(list, g);
 }
 
+// Copies hidden rows 0 .. mp - 1 of h (K bf16 wide, row-major) into LDS
+// rows of `stride` 16-byte chunks, writing the first `width` chunks of each
+// (zero past K).  Each of the NT threads issues all of its loads of a group
+// (up to kStageLoads) before it stores any, so staging takes one memory
+// round trip per group; a plain load-then-store loop waits for every chunk
+// in turn.  Buffer loads past a row's end or past the block read 0.
+#ifndef LMH_STAGE_LOADS
+#define LMH_STAGE_LOADS 8
+#endif
+constexpr int kStageLoads = LMH_STAGE_LOADS;
+
+template <int NT, int G>
+__device__ __forceinline__ void stage_group(__amdgpu_buffer_rsrc_t hs, int K, int total, int width, int stride,
+                                            u32x4* __restrict__ dst, int i0) {
+  const int chunks = K >> 3;
+  u32x4 v[G];
+  int at[G];
+#pragma unroll
+  for (int j = 0; j < G; ++j) {
+    const int i = i0 + j * NT;
+    const int m = i / width;
+    const int c = i - m * width;
+    at[j] = i < total ? m * stride + c : -1;
+    v[j] = load16<0>(hs, i < total && c < chunks ? (uint32_t)(m * K + c * 8) * 2u : kOobOffset);
+  }
+#pragma unroll
+  for (int j = 0; j < G; ++j)
+    if (at[j] >= 0) dst[at[j]] = v[j];
+}
+
+template <int NT>
+__device__ __forceinline__ void stage_hidden(const uint16_t* __restrict__ h, int K, int mp, int width, int stride,
+                                             u32x4* __restrict__ dst) {
+  const int total = mp * width;
+  const __amdgpu_buffer_rsrc_t hs = make_rsrc(h, (uint32_t)mp * (uint32_t)K * 2u);
+  const int i0 = threadIdx.x;
+  // the smallest group that covers the block, so no thread issues loads
+  // that all read past it
+  if (total <= NT || kStageLoads == 1) {
+    for (int i = i0; i < total; i += NT) stage_group<NT, 1>(hs, K, total, width, stride, dst, i);
+  } else if (total <= 2 * NT || kStageLoads == 2) {
+    for (int i = i0; i < total; i += 2 * NT) stage_group<NT, 2>(hs, K, total, width, stride, dst, i);
+  } else if (total <= 4 * NT || kStageLoads == 4) {
+    for (int i = i0; i < total; i += 4 * NT) stage_group<NT, 4>(hs, K, total, width, stride, dst, i);
+  } else {
+    for (int i = i0; i < total; i += 8 * NT) stage_group<NT, 8>(hs, K, total, width, stride, dst, i);
+  }
+}
+
 // Workgroup epilogue, run by wave 0 only: lane m < mcount publishes this
 // workgroup's best key for hidden row m_base + m into its own slot.  Slots
 // are laid out [hidden row][workgroup], so the finalize kernel reads each
@@ -1120,13 +1169,7 @@ proj_valu_tiled(const uint16_t* __restrict__ h, const uint16_t* __restrict__ W, 
   const int hc = nb * 64;
   const uint32_t row_bytes = (uint32_t)K * 2u;
 
-  for (int i = threadIdx.x; i < M * hc; i += (64 * WV)) {
-    const int m = i / hc;
-    const int c = i - m * hc;
-    u32x4 v = {0u, 0u, 0u, 0u};
-    if (c < chunks) v = *reinterpret_cast<const u32x4*>(h + (size_t)m * K + (size_t)c * 8);
-    h_stripes[i] = v;
-  }
+  stage_hidden<64 * WV>(h, K, M, hc, hc, h_stripes);
   __syncthreads();
 
   ValuEpilogue<M, WV, TK, LOGITS> ep;
@@ -1335,19 +1378,12 @@ proj_valu_fp8(const uint16_t* __restrict__ h, const uint8_t* __restrict__ W, con
   extern __shared__ u32x4 h_stripes[];  // [M][nb * 128] chunks of 8 bf16, zero past K
   const int lane = threadIdx.x & 63;
   const int wave = wave_id();
-  const int hchunks = K >> 3;
   const int wchunks = K >> 4;
   const int nb = (wchunks + 63) >> 6;  // stripes per row
   const int hc = nb * 128;
   const uint32_t row_bytes = (uint32_t)K;
 
-  for (int i = threadIdx.x; i < M * hc; i += (64 * WV)) {
-    const int m = i / hc;
-    const int c = i - m * hc;
-    u32x4 v = {0u, 0u, 0u, 0u};
-    if (c < hchunks) v = *reinterpret_cast<const u32x4*>(h + (size_t)m * K + (size_t)c * 8);
-    h_stripes[i] = v;
-  }
+  stage_hidden<64 * WV>(h, K, M, hc, hc, h_stripes);
   __syncthreads();
 
   ValuEpilogue<M, WV, TK, LOGITS> ep;
@@ -1470,7 +1506,7 @@ proj_valu_fp8(const uint16_t* __restrict__ h, const uint8_t* __restrict__ W, con
 template <int NT, int SB, int WV, int D, int TK, bool LOGITS, int FMT, bool IDX = false>
 __global__ void __launch_bounds__(64 * WV)
 proj_mfma(const uint16_t* __restrict__ h, const void* __restrict__ Wv, const void* __restrict__ wsc, int R,
-          int K, int m_base, int mp, Epi epi) {
+          int K, int m_base, int mp, Epi epi, int early) {
   constexpr bool FP8 = FMT == kFmtFp8;
   constexpr bool MX4 = FMT == kFmtMx4;
   static_assert(!IDX || (TK == 1 && !LOGITS && FMT == kFmtBf16), "indexed rows: bf16 argmax epilogue");
@@ -1490,21 +1526,17 @@ proj_mfma(const uint16_t* __restrict__ h, const void* __restrict__ Wv, const voi
   const int wave = wave_id();
   const int i16 = lane & 15;
   const int g = lane >> 4;
-  const int chunks = K >> 3;                         // 16-byte chunks of a hidden row
   const int wchunks = FP8 ? (K >> 4) : (MX4 ? (K >> 5) : (K >> 3));  // 16-byte chunks of a head row
   const int steps = (K + 31) >> 5;
   const int s4 = steps * 4;
   const int row_chunks = s4 + 1;
 
-  for (int i = threadIdx.x; i < mp * s4; i += 64 * WV) {
-    const int m = i / s4;
-    const int c = i - m * s4;
-    u32x4 v = {0u, 0u, 0u, 0u};
-    if (c < chunks) v = *reinterpret_cast<const u32x4*>(h + (size_t)(m_base + m) * K + (size_t)c * 8);
-    lds[m * row_chunks + c] = v;
+  // The hidden rows go to LDS either first, or (early != 0) once the
+  // wave's first batches are in flight: see mfma_stage_early.
+  if (!early) {
+    stage_hidden<64 * WV>(h + (size_t)m_base * K, K, mp, s4, row_chunks, lds);
+    __syncthreads();
   }
-  __syncthreads();
-
   u32x4* stage = lds + mp * row_chunks + wave * 16 * SC;
   // MX4: this wave's scale stage, one 16-byte chunk (16 k-steps) per row
   u32x4* sstage = lds + mp * row_chunks + WV * 16 * SC + wave * 16;
@@ -1787,6 +1819,12 @@ proj_mfma(const uint16_t* __restrict__ h, const void* __restrict__ Wv, const voi
     issue(ring[j], sring[j], ti, bi);
     advance(ti, bi);
   }
+
+  if (early) {
+    stage_hidden<64 * WV>(h + (size_t)m_base * K, K, mp, s4, row_chunks, lds);
+    __syncthreads();
+  }
+
   auto step = [&](auto jc) __attribute__((always_inline)) {
     constexpr int j = decltype(jc)::value;
     issue(ring[(j + D - 1) % D], sring[(j + D - 1) % D], ti, bi);
@@ -2114,6 +2152,17 @@ int mfma_lds_rows_fit(int64_t K, int waves, int fmt = kFmtBf16) {
   return (int)std::max<int64_t>(0, std::min<int64_t>(LMH_MAX_M, rows));
 }
 
+// Whether the matrix-core kernel stages the hidden rows after issuing its
+// first batches (so the two latencies overlap) rather than before.  Measured
+// on MI355X, interleaved builds on one box: after wins at 16 and more hidden
+// rows (the staging is long: 1-4% at 24 rows on the 52,755-row list) and on
+// the full head in every format; before wins on short quantized lists at a
+// few rows (MXFP4: 3.5% at 1, 3 and 8 rows; FP8: 1% at 1 and 3 rows), where
+// waiting for the early batches delays the start.
+bool mfma_stage_early(int fmt, int mp, int64_t R) {
+  return R >= LMH_RING_MAX_ROWS || mp >= 16 || (mp >= 5 && fmt != kFmtMx4);
+}
+
 // One pass of the matrix-core path over hidden rows [m_base, m_base + mp):
 // 8 waves per workgroup when the hidden rows and eight stages fit the LDS
 // and the head has at least 8 tiles per CU, else 4; two 16-column tiles
@@ -2135,15 +2184,16 @@ int launch_mfma_pass(const uint16_t* h, int K, int m_base, int mp, const void* W
   const bool eight = mp <= mfma_lds_rows_fit(K, 8, FMT) && tiles >= 8LL * cus;
   const size_t lds = hbytes + mfma_stage_bytes(eight ? 8 : 4, FMT);
   const char* what = "launch matrix-core projection";
+  const int early = mfma_stage_early(FMT, mp, R) ? 1 : 0;
   if (mp <= 16)
     return eight ? launch_persistent(proj_mfma<1, SB, 8, D, TK, LOGITS, FMT, IDX>, 512, lds, tiles, 8, 1 << 20, cus,
-                                     stream, what, grid_out, h, W, wscale, R, K, m_base, mp, epi)
+                                     stream, what, grid_out, h, W, wscale, R, K, m_base, mp, epi, early)
                  : launch_persistent(proj_mfma<1, SB, 4, D, TK, LOGITS, FMT, IDX>, 256, lds, tiles, 4, 1 << 20, cus,
-                                     stream, what, grid_out, h, W, wscale, R, K, m_base, mp, epi);
+                                     stream, what, grid_out, h, W, wscale, R, K, m_base, mp, epi, early);
   return eight ? launch_persistent(proj_mfma<2, SB, 8, D, TK, LOGITS, FMT, IDX>, 512, lds, tiles, 8, 1 << 20, cus,
-                                   stream, what, grid_out, h, W, wscale, R, K, m_base, mp, epi)
+                                   stream, what, grid_out, h, W, wscale, R, K, m_base, mp, epi, early)
                : launch_persistent(proj_mfma<2, SB, 4, D, TK, LOGITS, FMT, IDX>, 256, lds, tiles, 4, 1 << 20, cus,
-                                   stream, what, grid_out, h, W, wscale, R, K, m_base, mp, epi);
+                                   stream, what, grid_out, h, W, wscale, R, K, m_base, mp, epi, early);
 }
 
 // VALU path over an FP8 head: the tiled kernel for every M <= 4.
