@@ -1973,13 +1973,39 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 bool k_ok(int64_t K) { return K >= LMH_MIN_K && K <= LMH_MAX_K && (K % 8) == 0; }
 
+// The host-side figures a launch is planned from (CU count, resident
+// workgroups per CU) are fixed per device and kernel shape, so each is
+// asked of the runtime once and kept: an occupancy query costs about as
+// much host time as a launch, and a short call makes two launches.
+struct OccupancyKey {
+  int dev;
+  const void* f;
+  int threads;
+  size_t lds;
+  int per_cu;
+};
+std::mutex g_query_mu;
+std::vector<std::pair<int, int>> g_cu_counts;  // (device, CUs)
+std::vector<OccupancyKey> g_occupancy;
+
 int cu_count(int* out) {
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
-  e = hipDeviceGetAttribute(out, hipDeviceAttributeMultiprocessorCount, dev);
+  {
+    std::lock_guard<std::mutex> lock(g_query_mu);
+    for (const auto& dc : g_cu_counts)
+      if (dc.first == dev) {
+        *out = dc.second;
+        return LMH_OK;
+      }
+  }
+  int n = 0;
+  e = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev);
   if (e != hipSuccess) return hip_fail(e, "hipDeviceGetAttribute");
-  if (*out < 1) *out = 1;
+  *out = n < 1 ? 1 : n;
+  std::lock_guard<std::mutex> lock(g_query_mu);
+  g_cu_counts.emplace_back(dev, *out);
   return LMH_OK;
 }
 
@@ -1988,10 +2014,23 @@ int cu_count(int* out) {
 // the grid is sized to what is resident: a second, partial round of
 // workgroups would double the tail.
 int resident_per_cu(const void* f, int threads, size_t lds, int* out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  {
+    std::lock_guard<std::mutex> lock(g_query_mu);
+    for (const auto& k : g_occupancy)
+      if (k.dev == dev && k.f == f && k.threads == threads && k.lds == lds) {
+        *out = k.per_cu;
+        return LMH_OK;
+      }
+  }
   int n = 0;
-  const hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, f, threads, lds);
+  e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, f, threads, lds);
   if (e != hipSuccess) return hip_fail(e, "hipOccupancyMaxActiveBlocksPerMultiprocessor");
   *out = n < 1 ? 1 : n;
+  std::lock_guard<std::mutex> lock(g_query_mu);
+  g_occupancy.push_back(OccupancyKey{dev, f, threads, lds, *out});
   return LMH_OK;
 }
 

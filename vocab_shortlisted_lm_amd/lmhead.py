@@ -118,16 +118,28 @@ def _check(code: int, where: str) -> None:
 _BF16_LIKE = (torch.bfloat16, torch.int16, torch.uint16)
 
 
+def _index(device) -> int:
+    """Ordinal of a GPU given as a torch.device, an int or a string."""
+    if isinstance(device, int):
+        return device
+    if not isinstance(device, torch.device):
+        device = torch.device(device)
+    return device.index if device.index is not None else torch.cuda.current_device()
+
+
 def _dev_tensor(t: torch.Tensor, name: str, dtypes, ndim: int, device=None) -> None:
     """A contiguous device tensor of one of `dtypes` with `ndim` dimensions
     (any dtype / rank if None), on `device` when given.  Every pointer the
     library receives goes through here: a host tensor's address in a
     kernel would fault the GPU."""
+    # is_cuda and get_device() are the cheap forms of these checks (a
+    # device object's type string costs more than the rest together); the
+    # binding runs them on every tensor of every call
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch.Tensor")
-    if t.device.type != "cuda":
+    if not t.is_cuda:
         raise ValueError(f"{name} must be a device tensor")
-    if device is not None and t.device != device:
+    if device is not None and t.get_device() != _index(device):
         raise ValueError(f"{name} is on {t.device}, the call runs on {device}")
     if dtypes is not None and t.dtype not in dtypes:
         raise TypeError(f"{name} has dtype {t.dtype}, expected one of {dtypes}")
