@@ -73,7 +73,7 @@ def kernel_name(path: str, m: int) -> str:
     """The projection kernel a call runs (the plan in the library's host code)."""
     if path == "mfma":
         return "proj_mfma"
-    return "proj_valu_tiled" if m == 1 else "proj_valu_rows"
+    return "proj_valu_tiled" if m <= 2 else "proj_valu_rows"
 
 
 def describe(a, synth, L):

@@ -152,6 +152,17 @@ def test_config2_full_m1(L):
     run_and_check(L, hs, inp["W"], device_weights(2), None, paths_for(L, 1, c.k), "full M=1")
 
 
+@pytest.mark.parametrize("m", [2, 3])
+def test_full_head_two_and_three_rows(L, m):
+    """The full head at M = 2 (the tiled kernel's unconditional loop) and
+    M = 3 (the row-order kernel's two-buffer loop), on every kernel that
+    takes the shape."""
+    inp = config_inputs(2)
+    c = inp["config"]
+    hs = [synth.hidden(250 + m, d, m, c.k) for d in range(4)]
+    run_and_check(L, hs, inp["W"], device_weights(2), None, paths_for(L, m, c.k), f"full M={m}")
+
+
 def test_config3_16k_m3(L):
     inp = config_inputs(3)
     c = inp["config"]
