@@ -23,6 +23,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -64,9 +65,18 @@ def projection_bytes(m: int, rows: int, k: int, fmt: str = "bf16", indexed: bool
     return head_bytes(rows, k, fmt) + (rows * 4 if indexed else 0) + m * k * 2
 
 
+_CODE_TOKENS = re.compile(r'//[^\n]*|/\*.*?\*/|"(?:\\.|[^"\\\n])*"|\'(?:\\.|[^\'\\\n])*\'', re.S)
+
+
 def source_digest() -> str:
-    with open(KERNEL_SOURCE, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """Digest of the kernel source's code: comments dropped, string and
+    character literals kept, runs of whitespace folded, so that counters
+    taken on a kernel stay valid across edits of its comments only."""
+    with open(KERNEL_SOURCE, encoding="utf-8") as f:
+        text = f.read()
+    code = _CODE_TOKENS.sub(lambda m: " " if m.group(0)[0] == "/" else m.group(0), text)
+    code = " ".join(code.split())
+    return hashlib.sha256(code.encode("utf-8")).hexdigest()[:16]
 
 
 def kernel_name(path: str, m: int) -> str:
@@ -204,8 +214,8 @@ def record_traffic(a, d, fetch_csv: str, write_csv: str) -> int:
         table = {}
     table["about"] = ("HBM bytes per launch of the projection kernel from rocprofv3 --pmc FETCH_SIZE and "
                       "WRITE_SIZE runs of bench.py --calibrate, each scaled by what the counter reads for "
-                      "copy16 over 1 GiB in the same process; valid only for the kernel source with this "
-                      "digest")
+                      "copy16 over 1 GiB in the same process; valid only for the kernel source whose code "
+                      "(comments excluded) has this digest")
     entries = [e for e in table.get("entries", [])
                if not (e.get("path") == entry["path"] and e.get("workload") == entry["workload"])]
     entries.append(entry)

@@ -5,27 +5,43 @@
 //   gather_rows             load-time shortlist gather, W_trim[i] = W[ids[i]]
 //                           ("Two ways to run it", zone-1.cobraproject.com
 //                           "Masked MTP drafts": the head is trimmed at load).
-//   proj_argmax_valu_tiled  M = 1: a wave walks tiles of 4 head rows in 1 KiB
-//                           column stripes; packed bf16 dot products with
-//                           fp32 accumulation, DPP reduction per row.
-//   proj_argmax_valu        M = 2..8: one wave per head row, hidden rows in
-//                           registers, two rows per step double-buffered.
-//   proj_argmax_mfma_lds    M > 4 (default): coalesced 16-byte loads of
-//                           16-row tiles, transposed through a wave-private
-//                           LDS stage into 16x16x32 bf16 matrix-core operands;
-//                           hidden rows staged in LDS.
-// Every projection kernel fuses the argmax: each wave keeps a running
-// (logit, row) per hidden row as a 64-bit key, a workgroup folds its waves
-// through LDS and stores one key per hidden row into its own workspace slot.
+//   proj_valu_tiled         M = 1 (and M = 2 for the argmax): a wave walks
+//                           tiles of 4 head rows in 1 KiB column stripes;
+//                           packed bf16 dot products with fp32 accumulation,
+//                           DPP reduction per row; hidden rows in LDS.
+//   proj_valu_rows          M = 3..4 by default (M = 2 for top k and logits;
+//                           forced: up to 8): one wave per head row, hidden
+//                           rows in registers, two rows per step
+//                           double-buffered.
+//   proj_mfma               M > 4, and every M over an FP8 or MXFP4 head:
+//                           coalesced 16-byte loads of 16-row tiles,
+//                           transposed through a wave-private LDS stage into
+//                           16x16x32 bf16 matrix-core operands; hidden rows
+//                           staged in LDS.
+//   proj_valu_fp8           FP8 head on the VALU path (forced only).
+// Every projection kernel fuses its epilogue: for the argmax each wave keeps
+// a running (logit, row) per hidden row as a 64-bit key, a workgroup folds
+// its waves through LDS and stores one key per hidden row into its own
+// workspace slot (top k keeps sorted key lists the same way; the logits
+// epilogue stores every logit instead).
 //   finalize_argmax         one workgroup per hidden row folds the slots,
 //                           decodes the winner and maps it through d2t
 //                           (EAGLE-3 style draft-to-target ids, "Two ways to
 //                           run it").
-// The two kernels are ordered by the stream; no atomics, fences or memsets
-// are needed, and the workspace needs no initial contents.  The argmax is
-// reduced where it is computed instead of gathering logits, the change the
-// fair re-run on krisbailey.com/articles/shortlist-mtp credits ("Re-running
-// the comparison fairly").
+//   finalize_topk           the same for the top-k lists.
+//   fill_neg_inf            the -inf fill before logits are scattered to
+//                           vocabulary ids.
+//   quantize_rows_fp8, quantize_rows_mxfp4, tile_mxfp4_scales
+//                           load-time copies of a head in FP8 or MXFP4.
+//   overwrite_rows, union_ids
+//                           shortlist maintenance (escaped ids into spare
+//                           rows; the union of two lists).
+// A projection kernel and its fold are ordered by the stream; no atomics,
+// fences or memsets are needed, and the workspace needs no initial
+// contents.  The argmax is reduced where it is computed instead of
+// gathering logits, the change the fair re-run on
+// krisbailey.com/articles/shortlist-mtp credits ("Re-running the comparison
+// fairly").
 //
 // The projection is HBM-bound: at M = 1 each head row (5,120 bytes at
 // K = 2,560) is used for 2,560 multiply-adds.  The kernels therefore stream
