@@ -473,8 +473,10 @@ __device__ __forceinline__ void col_merge(unsigned long long (&list)[4], unsigne
 // (up to kStageLoads) before it stores any, so staging takes one memory
 // round trip per group; a plain load-then-store loop waits for every chunk
 // in turn.  Buffer loads past a row's end or past the block read 0.
+// Groups of 16 (one round trip at 24 hidden rows in 8 waves) measured
+// 0.2-0.7 us faster per launch than groups of 8 at 16 and 24 rows.
 #ifndef LMH_STAGE_LOADS
-#define LMH_STAGE_LOADS 8
+#define LMH_STAGE_LOADS 16
 #endif
 constexpr int kStageLoads = LMH_STAGE_LOADS;
 
@@ -511,8 +513,10 @@ __device__ __forceinline__ void stage_hidden(const uint16_t* __restrict__ h, int
     for (int i = i0; i < total; i += 2 * NT) stage_group<NT, 2>(hs, K, total, width, stride, dst, i);
   } else if (total <= 4 * NT || kStageLoads == 4) {
     for (int i = i0; i < total; i += 4 * NT) stage_group<NT, 4>(hs, K, total, width, stride, dst, i);
-  } else {
+  } else if (total <= 8 * NT || kStageLoads == 8) {
     for (int i = i0; i < total; i += 8 * NT) stage_group<NT, 8>(hs, K, total, width, stride, dst, i);
+  } else {
+    for (int i = i0; i < total; i += 16 * NT) stage_group<NT, 16>(hs, K, total, width, stride, dst, i);
   }
 }
 
