@@ -340,6 +340,9 @@ def main() -> int:
                     help="time draft_project_logits instead of the argmax: every logit as [M, R] (rows), "
                          "or scattered through d2t into [M, N] with -inf elsewhere (vocab; the full head "
                          "takes d2t = 0..N-1); bf16 heads; whole calls only")
+    ap.add_argument("--graph", action="store_true",
+                    help="capture the --steps calls of a timed region in one HIP graph and time its replays "
+                         "(the calls without the host's launch cost)")
     ap.add_argument("--shortlist-ops", action="store_true",
                     help="instead of the projection: time the list gathers, the device union of two lists "
                          "and 600 escaped ids written into spare rows (one JSON line)")
@@ -412,6 +415,7 @@ def main() -> int:
     out_id = torch.empty(m, dtype=torch.int32, device=dev)
     out_logit = torch.empty(m, dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream(dev)
+    launch_on = [stream]   # the stream the calls go to (a capture stream under --graph)
     out_bytes = 8 * m
     if a.topk:
         tk_id = torch.empty((m, a.topk), dtype=torch.int32, device=dev)
@@ -430,36 +434,57 @@ def main() -> int:
         if a.topk:
             if a.fp8:
                 q, sc = heads[i % len(heads)]
-                L.draft_project_topk_fp8(h, q, sc, d2t, a.topk, tk_id, tk_logit, tk_ws, path, stream)
+                L.draft_project_topk_fp8(h, q, sc, d2t, a.topk, tk_id, tk_logit, tk_ws, path, launch_on[0])
             elif a.mxfp4:
                 q, sc = heads[i % len(heads)]
-                L.draft_project_topk_mxfp4(h, q, sc, d2t, a.topk, tk_id, tk_logit, tk_ws, path, stream)
+                L.draft_project_topk_mxfp4(h, q, sc, d2t, a.topk, tk_id, tk_logit, tk_ws, path, launch_on[0])
             else:
-                L.draft_project_topk(h, heads[i % len(heads)], d2t, a.topk, tk_id, tk_logit, tk_ws, path, stream)
+                L.draft_project_topk(h, heads[i % len(heads)], d2t, a.topk, tk_id, tk_logit, tk_ws, path, launch_on[0])
         elif a.logits:
             L.draft_project_logits(h, heads[i % len(heads)], lg_d2t, c.n if lg_d2t is not None else None,
-                                   lg_out, path, stream)
+                                   lg_out, path, launch_on[0])
         elif a.indexed:
-            L.draft_project_argmax_indexed(h, heads[i % len(heads)], d2t, path, out_id, out_logit, ws, stream)
+            L.draft_project_argmax_indexed(h, heads[i % len(heads)], d2t, path, out_id, out_logit, ws, launch_on[0])
         elif a.fp8:
             q, sc = heads[i % len(heads)]
-            L.draft_project_argmax_fp8(h, q, sc, d2t, path, out_id, out_logit, ws, stream)
+            L.draft_project_argmax_fp8(h, q, sc, d2t, path, out_id, out_logit, ws, launch_on[0])
         elif a.mxfp4:
             q, sc = heads[i % len(heads)]
-            L.draft_project_argmax_mxfp4(h, q, sc, d2t, path, out_id, out_logit, ws, stream)
+            L.draft_project_argmax_mxfp4(h, q, sc, d2t, path, out_id, out_logit, ws, launch_on[0])
         else:
             L.draft_project_argmax_path(h, heads[i % len(heads)], d2t, path, out_id, out_logit, ws,
-                                        stream)
+                                        launch_on[0])
 
     for i in range(a.warmup):
         step(i)
     torch.cuda.synchronize()
+
+    graph = None
+    if a.graph:
+        # the timed region's calls, captured once; a region is then one replay
+        cap = torch.cuda.Stream(dev)
+        graph = torch.cuda.CUDAGraph()
+        launch_on[0] = cap
+        with torch.cuda.graph(graph, stream=cap):
+            for i in range(a.steps):
+                step(i)
+        launch_on[0] = stream
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+
+    def region():
+        if graph is not None:
+            graph.replay()
+        else:
+            for i in range(a.steps):
+                step(i)
+
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
     wall0 = time.perf_counter()
     t_start.record(stream)
-    for i in range(a.steps):
-        step(i)
+    region()
     t_end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
@@ -473,8 +498,7 @@ def main() -> int:
     for _ in range(max(0, a.repeats - 1)):
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(stream)
-        for i in range(a.steps):
-            step(i)
+        region()
         e1.record(stream)
         torch.cuda.synchronize()
         rates.append(a.steps / (e0.elapsed_time(e1) / 1e3))
@@ -483,7 +507,8 @@ def main() -> int:
         # whole calls only: the kernel-only timer covers the argmax epilogue
         result = {
             "mode": f"top-{a.topk}" if a.topk else f"logits ({a.logits})",
-            "workload": workload, "M": m, "K": c.k, "rows": rows, "fmt": d["fmt"], "steps": a.steps,
+            "workload": workload, "M": m, "K": c.k, "rows": rows, "fmt": d["fmt"], "graph": a.graph,
+            "steps": a.steps,
             "warmup": a.warmup, "us_per_call": round(ms_per_step * 1e3, 2),
             "repeats_us_per_call": {"median": round(float(np.median([1e6 / r for r in rates])), 2),
                                     "p10": round(float(np.percentile([1e6 / r for r in rates], 10)), 2),
@@ -574,6 +599,7 @@ def main() -> int:
                      "step_gbps": round(abytes / (ms_per_step / 1e3) / 1e9, 1),
                      "algorithmic_bytes_per_step": abytes},
         "wall_s": round(wall, 3),
+        "graph": a.graph,
         "repeats": {"n": len(rates), "unit": "calls/s", "median": round(float(np.median(rates)), 2),
                     "p10": round(float(np.percentile(rates, 10)), 2),
                     "p90": round(float(np.percentile(rates, 90)), 2)},

@@ -22,7 +22,11 @@
  *    matrix is at index r * K + k.
  *  - `stream` is a hipStream_t passed as void*; NULL means the null stream.
  *    Work is queued on `stream` and the call returns without waiting, except
- *    where a call says it synchronizes.
+ *    where a call says it synchronizes.  A call that neither synchronizes
+ *    nor allocates only launches kernels, so it may be captured in a HIP
+ *    graph (stream capture) and replayed; make one eager call with the same
+ *    shapes first, so that the per-kernel launch settings are cached outside
+ *    the capture.
  *  - The caller owns every buffer.  The library never allocates or frees
  *    device memory and keeps no device state between calls.
  *  - Return value: an lmh_status code.  A call that returns LMH_EINVAL,
