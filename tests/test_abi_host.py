@@ -337,3 +337,24 @@ def test_build_has_no_scratch_spills():
         assert any(kernel in k for k in usage), kernel
     spills = {k: v["ScratchSize"] for k, v in usage.items() if v.get("ScratchSize", 0)}
     assert not spills, spills
+
+
+def test_header_is_plain_c(tmp_path):
+    """include/lmhead.h compiles as strict C99 on its own: the boundary has no
+    C++ or torch types."""
+    src = tmp_path / "uses_header.c"
+    src.write_text('#include "lmhead.h"\nint main(void) { return (int)draft_project_workspace_bytes(1) == 0; }\n')
+    proc = subprocess.run(["gcc", "-std=c99", "-pedantic", "-Wall", "-Wextra", "-Werror", "-fsyntax-only",
+                           "-I", os.path.join(ROOT, "include"), str(src)], capture_output=True, text=True)
+    assert proc.returncode == 0, proc.stderr
+
+
+def test_c_consumer_builds_against_the_header_alone(tmp_path):
+    """The C program the boundary test drives (tests/c_consumer) builds with
+    gcc from the header and HIP's C runtime API, and resolves the in-tree
+    library by a path relative to itself."""
+    from vocab_shortlisted_lm_amd import build
+    out = build.build_consumer(str(tmp_path / "consumer"))
+    ldd = subprocess.run(["ldd", out], capture_output=True, text=True, check=True).stdout
+    line = [l for l in ldd.splitlines() if "liblmhead.so" in l]
+    assert line and "not found" not in line[0], ldd

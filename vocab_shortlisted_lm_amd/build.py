@@ -84,6 +84,26 @@ def build(out: str = LIB, defines: list[str] | None = None, verbose: bool = Fals
     return out
 
 
+CONSUMER_SRC = os.path.join(ROOT, "tests", "c_consumer", "lmhead_consumer.c")
+CONSUMER = os.path.join(ROOT, "tests", "c_consumer", "lmhead_consumer")
+
+
+def build_consumer(out: str = CONSUMER) -> str:
+    """Compile the C program that drives the library through the header
+    alone (C11, gcc, HIP's C runtime API), linked against the in-tree
+    library by a path relative to the program."""
+    rocm = os.environ.get("ROCM_PATH", "/opt/rocm")
+    rel = os.path.relpath(PKG, os.path.dirname(out))
+    cmd = ["gcc", "-std=c11", "-O2", "-Wall", "-Wextra", "-Werror", "-D__HIP_PLATFORM_AMD__",
+           "-I", os.path.join(rocm, "include"), "-I", INCLUDE, CONSUMER_SRC, "-o", out,
+           "-L", PKG, "-llmhead", "-L", os.path.join(rocm, "lib"), "-lamdhip64",
+           f"-Wl,-rpath,$ORIGIN/{rel}", "-Wl,-rpath," + os.path.join(rocm, "lib")]
+    proc = subprocess.run(cmd, capture_output=True, text=True)
+    if proc.returncode != 0:
+        raise RuntimeError("gcc failed:\n" + " ".join(cmd) + "\n" + proc.stderr)
+    return out
+
+
 def main() -> None:
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("-D", dest="defines", action="append", default=[])
