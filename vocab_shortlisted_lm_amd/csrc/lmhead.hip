@@ -470,15 +470,15 @@ __device__ __forceinline__ void col_merge(unsigned long long (&list)[4], unsigne
 // Copies hidden rows 0 .. mp - 1 of h (K bf16 wide, row-major) into LDS
 // rows of `stride` 16-byte chunks, writing the first `width` chunks of each
 // (zero past K).  Each of the NT threads issues all of its loads of a group
-// (up to kStageLoads) before it stores any, so staging takes one memory
+// (up to MAXG) before it stores any, so staging takes one memory
 // round trip per group; a plain load-then-store loop waits for every chunk
 // in turn.  Buffer loads past a row's end or past the block read 0.
-// Groups of 16 (one round trip at 24 hidden rows in 8 waves) measured
-// 0.2-0.7 us faster per launch than groups of 8 at 16 and 24 rows.
-#ifndef LMH_STAGE_LOADS
-#define LMH_STAGE_LOADS 16
-#endif
-constexpr int kStageLoads = LMH_STAGE_LOADS;
+// MAXG bounds the group.  The registers of the largest group count towards
+// the kernel's register peak even when a launch never uses it: groups of 16
+// raised the matrix-core argmax kernels from 86-97 to 126-136 VGPRs, one
+// wave per SIMD less, which cost MXFP4 heads their second workgroup per CU
+// at a few hidden rows.  So only kernels whose LDS already holds them to one
+// workgroup per CU (two 16-column tiles, more than 16 hidden rows) take 16.
 
 template <int NT, int G>
 __device__ __forceinline__ void stage_group(__amdgpu_buffer_rsrc_t hs, int K, int total, int width, int stride,
@@ -499,24 +499,25 @@ __device__ __forceinline__ void stage_group(__amdgpu_buffer_rsrc_t hs, int K, in
     if (at[j] >= 0) dst[at[j]] = v[j];
 }
 
-template <int NT>
+template <int NT, int MAXG = 8>
 __device__ __forceinline__ void stage_hidden(const uint16_t* __restrict__ h, int K, int mp, int width, int stride,
                                              u32x4* __restrict__ dst) {
+  static_assert(MAXG == 8 || MAXG == 16, "groups of up to 8 or 16 loads");
   const int total = mp * width;
   const __amdgpu_buffer_rsrc_t hs = make_rsrc(h, (uint32_t)mp * (uint32_t)K * 2u);
   const int i0 = threadIdx.x;
   // the smallest group that covers the block, so no thread issues loads
   // that all read past it
-  if (total <= NT || kStageLoads == 1) {
-    for (int i = i0; i < total; i += NT) stage_group<NT, 1>(hs, K, total, width, stride, dst, i);
-  } else if (total <= 2 * NT || kStageLoads == 2) {
-    for (int i = i0; i < total; i += 2 * NT) stage_group<NT, 2>(hs, K, total, width, stride, dst, i);
-  } else if (total <= 4 * NT || kStageLoads == 4) {
-    for (int i = i0; i < total; i += 4 * NT) stage_group<NT, 4>(hs, K, total, width, stride, dst, i);
-  } else if (total <= 8 * NT || kStageLoads == 8) {
+  if (total <= NT) {
+    stage_group<NT, 1>(hs, K, total, width, stride, dst, i0);
+  } else if (total <= 2 * NT) {
+    stage_group<NT, 2>(hs, K, total, width, stride, dst, i0);
+  } else if (total <= 4 * NT) {
+    stage_group<NT, 4>(hs, K, total, width, stride, dst, i0);
+  } else if (MAXG == 8 || total <= 8 * NT) {
     for (int i = i0; i < total; i += 8 * NT) stage_group<NT, 8>(hs, K, total, width, stride, dst, i);
   } else {
-    for (int i = i0; i < total; i += 16 * NT) stage_group<NT, 16>(hs, K, total, width, stride, dst, i);
+    for (int i = i0; i < total; i += 16 * NT) stage_group<NT, MAXG>(hs, K, total, width, stride, dst, i);
   }
 }
 
@@ -1554,7 +1555,7 @@ proj_mfma(const uint16_t* __restrict__ h, const void* __restrict__ Wv, const voi
   // The hidden rows go to LDS either first, or (early != 0) once the
   // wave's first batches are in flight: see mfma_stage_early.
   if (!early) {
-    stage_hidden<64 * WV>(h + (size_t)m_base * K, K, mp, s4, row_chunks, lds);
+    stage_hidden<64 * WV, NT == 2 ? 16 : 8>(h + (size_t)m_base * K, K, mp, s4, row_chunks, lds);
     __syncthreads();
   }
   u32x4* stage = lds + mp * row_chunks + wave * 16 * SC;
@@ -1841,7 +1842,7 @@ proj_mfma(const uint16_t* __restrict__ h, const void* __restrict__ Wv, const voi
   }
 
   if (early) {
-    stage_hidden<64 * WV>(h + (size_t)m_base * K, K, mp, s4, row_chunks, lds);
+    stage_hidden<64 * WV, NT == 2 ? 16 : 8>(h + (size_t)m_base * K, K, mp, s4, row_chunks, lds);
     __syncthreads();
   }
 
