@@ -337,6 +337,14 @@ def test_build_has_no_scratch_spills():
         assert any(kernel in k for k in usage), kernel
     spills = {k: v["ScratchSize"] for k, v in usage.items() if v.get("ScratchSize", 0)}
     assert not spills, spills
+    # The one-tile matrix-core argmax kernels over FP8 and MXFP4 heads run two
+    # 8-wave workgroups per CU at a few hidden rows (their LDS allows it), so
+    # they must fit 4 waves per SIMD in registers; a larger register peak
+    # silently halves their residency (no parity test can see it)
+    for fmt in (1, 2):
+        name = [k for k in usage if "proj_mfma" in k and f"ILi1ELi{8 * fmt}ELi8ELi3ELi1ELb0ELi{fmt}ELb0E" in k]
+        assert len(name) == 1, (fmt, name)
+        assert usage[name[0]].get("Occupancy", 0) >= 4, (name[0], usage[name[0]])
 
 
 def test_header_is_plain_c(tmp_path):
