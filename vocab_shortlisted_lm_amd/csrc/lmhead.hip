@@ -79,7 +79,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 #define LMH_VALU_WG_PER_CU 1     // cap on resident workgroups per CU (VALU path)
 #endif
 #ifndef LMH_VALU_TILE_ROWS
-#define LMH_VALU_TILE_ROWS 4     // rows per tile of the tiled VALU kernel (M = 1); 0 = row order
+#define LMH_VALU_TILE_ROWS 4     // rows per tile of the tiled VALU kernel (M = 1; M = 2 argmax); 0 = row order
 #endif
 #ifndef LMH_VALU_PREFETCH
 #define LMH_VALU_PREFETCH 1      // double-buffer rows in registers (VALU path)
