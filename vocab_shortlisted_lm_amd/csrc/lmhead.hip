@@ -398,18 +398,52 @@ struct RowTop16 {
   }
 };
 
+// The key of lane j ^ X of this lane's 16-lane row, moved with DPP (a VALU
+// operand modifier) instead of a shuffle through the LDS crossbar:
+// quad_perm for X = 1 and 2, row_ror:8 for 8 (rotating 16 lanes by 8 is the
+// XOR), row_mirror for 15, and for 4 the rotations by 4 and by 12, picked
+// by bit 2 of the lane.  j is the lane's index within its row.
+template <int CTRL>
+__device__ __forceinline__ unsigned long long dpp_u64(unsigned long long k) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)k, CTRL, 0xF, 0xF, false);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(k >> 32), CTRL, 0xF, 0xF, false);
+  return ((unsigned long long)hi << 32) | lo;
+}
+
+template <int X>
+__device__ __forceinline__ unsigned long long row_xor_u64(unsigned long long k, int j) {
+  static_assert(X == 1 || X == 2 || X == 4 || X == 8 || X == 15, "a lane XOR within a 16-lane row");
+  if constexpr (X == 1) {
+    return dpp_u64<0xB1>(k);   // quad_perm [1,0,3,2]
+  } else if constexpr (X == 2) {
+    return dpp_u64<0x4E>(k);   // quad_perm [2,3,0,1]
+  } else if constexpr (X == 8) {
+    return dpp_u64<0x128>(k);  // row_ror:8
+  } else if constexpr (X == 15) {
+    return dpp_u64<0x140>(k);  // row_mirror
+  } else {
+    const unsigned long long by4 = dpp_u64<0x124>(k);   // row_ror:4: from lane j - 4 (mod 16)
+    const unsigned long long by12 = dpp_u64<0x12C>(k);  // row_ror:12: from lane j + 4 (mod 16)
+    return (j & 4) ? by4 : by12;
+  }
+}
+
+template <int S>
+__device__ __forceinline__ unsigned long long row_half_clean(unsigned long long c, int j) {
+  const unsigned long long o = row_xor_u64<S>(c, j);
+  return (j & S) == 0 ? max_u64(c, o) : min_u64(c, o);
+}
+
 // Best 16 of two lists each laid out over the 16 lanes of a DPP row (lane
 // j = element j, descending): the element-wise maximum of a and b mirrored
 // is bitonic and holds the best 16, which four half-cleaner stages sort.
 // j = lane % 16.  Every lane of the row must take part.
 __device__ __forceinline__ unsigned long long row_merge(unsigned long long a, unsigned long long b, int j) {
-  unsigned long long c = max_u64(a, shfl_xor_u64(b, 15));
-#pragma unroll
-  for (int s = 8; s >= 1; s >>= 1) {
-    const unsigned long long o = shfl_xor_u64(c, s);
-    c = (j & s) == 0 ? max_u64(c, o) : min_u64(c, o);
-  }
-  return c;
+  unsigned long long c = max_u64(a, row_xor_u64<15>(b, j));
+  c = row_half_clean<8>(c, j);
+  c = row_half_clean<4>(c, j);
+  c = row_half_clean<2>(c, j);
+  return row_half_clean<1>(c, j);
 }
 
 // Top-16 of one hidden row in the matrix-core output layout: the 4 lanes
