@@ -311,9 +311,28 @@ __device__ __forceinline__ unsigned long long min_u64(unsigned long long a, unsi
   return a < b ? a : b;
 }
 
-__device__ __forceinline__ unsigned long long shfl_xor_u64(unsigned long long k, int x) {
-  const uint32_t lo = (uint32_t)__shfl_xor((int)(uint32_t)k, x);
-  const uint32_t hi = (uint32_t)__shfl_xor((int)(uint32_t)(k >> 32), x);
+// The key of lane ^ X (X = 16 or 32) with gfx950's row-swap instructions,
+// on the VALU instead of a shuffle through the LDS crossbar.  Given the same
+// value twice, v_permlane16_swap leaves in its first result each odd row
+// holding the even row below it, and in its second each even row holding
+// the odd row above it; v_permlane32_swap does the same for the two halves
+// of the wave.  `row` is the lane's 16-lane row (lane / 16).
+template <int X>
+__device__ __forceinline__ uint32_t xrow_u32(uint32_t v, int row) {
+  static_assert(X == 16 || X == 32, "a lane XOR across 16-lane rows");
+  if constexpr (X == 16) {
+    const auto p = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+    return (row & 1) ? p[0] : p[1];
+  } else {
+    const auto q = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+    return (row & 2) ? q[0] : q[1];
+  }
+}
+
+template <int X>
+__device__ __forceinline__ unsigned long long xrow_u64(unsigned long long k, int row) {
+  const uint32_t lo = xrow_u32<X>((uint32_t)k, row);
+  const uint32_t hi = xrow_u32<X>((uint32_t)(k >> 32), row);
   return ((unsigned long long)hi << 32) | lo;
 }
 
@@ -353,10 +372,11 @@ struct KeyList {
         }
   }
   // fold in the list of lane (this lane ^ x)
-  __device__ __forceinline__ void merge_xor(int x) {
+  template <int X>
+  __device__ __forceinline__ void merge_xor(int row) {
     unsigned long long o[TK];
 #pragma unroll
-    for (int j = 0; j < TK; ++j) o[j] = shfl_xor_u64(k[j], x);
+    for (int j = 0; j < TK; ++j) o[j] = xrow_u64<X>(k[j], row);
     merge(o);
   }
 };
@@ -461,7 +481,7 @@ __device__ __forceinline__ void col_cx(unsigned long long (&c)[4], int g) {
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
       const bool desc = (((4 * g + v) & SIZE) == 0) != ASC;
-      const unsigned long long o = shfl_xor_u64(c[v], kLaneXor);
+      const unsigned long long o = xrow_u64<kLaneXor>(c[v], g);
       c[v] = (lower == desc) ? max_u64(c[v], o) : min_u64(c[v], o);
     }
   } else {
@@ -1906,8 +1926,8 @@ proj_mfma(const uint16_t* __restrict__ h, const void* __restrict__ Wv, const voi
     for (int nt = 0; nt < NT; ++nt) {
       unsigned long long k = pack_key(best[nt], bidx[nt]);
       // fold the four lanes (g = 0..3) that hold the same hidden row
-      k = max_u64(k, shfl_xor_u64(k, 16));
-      k = max_u64(k, shfl_xor_u64(k, 32));
+      k = max_u64(k, xrow_u64<16>(k, g));
+      k = max_u64(k, xrow_u64<32>(k, g));
       const int col = nt * 16 + i16;
       if (g == 0 && col < 32) s_key[wave][col] = k;
     }
@@ -1936,8 +1956,8 @@ proj_mfma(const uint16_t* __restrict__ h, const void* __restrict__ Wv, const voi
   } else {
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
-      lists[nt].merge_xor(16);
-      lists[nt].merge_xor(32);
+      lists[nt].template merge_xor<16>(g);
+      lists[nt].template merge_xor<32>(g);
     }
     // every wave is past its main loop: the stage area is free for the lists
     __syncthreads();
