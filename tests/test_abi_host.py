@@ -300,6 +300,7 @@ def test_binding_rejects_host_tensors_before_any_call(L):
     ids = torch.zeros(4, dtype=torch.int32)
     calls = [
         lambda: L.draft_project_argmax(h, W),
+        lambda: L.PreparedArgmax(h, W),
         lambda: L.draft_project_topk(h, W, None, 4),
         lambda: L.draft_project_logits(h, W),
         lambda: L.lmhead_trim(W, ids),

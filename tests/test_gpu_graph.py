@@ -164,3 +164,29 @@ def test_quantized_heads_replay_match_eager(L, head):
             assert np.array_equal(oid.cpu().numpy(), wi), (rep, fmt, h.shape[0])
             assert np.array_equal(olog.cpu().numpy().view(np.uint32), wl.view(np.uint32)), (rep, fmt)
         log(f"[graph] quantized replay {rep}: bit-identical to eager")
+
+
+def test_prepared_argmax_matches_the_call(L, head):
+    """PreparedArgmax (tensors checked once, one C call per step) gives the
+    ordinary call's results bit for bit while the hidden rows are rewritten
+    in place between steps, on each kernel family."""
+    import time
+    w_np, ids = head
+    w = dev_bf16(w_np)
+    d2t = dev_i32(ids)
+    for m in (1, 2, 3, 24):
+        h = torch.empty((m, K), dtype=torch.int16, device="cuda")
+        step = L.PreparedArgmax(h, w, d2t, workspace=L.new_workspace(M=m))
+        for d, h_np in enumerate(hidden_sets(m, 3)):
+            h.copy_(dev_bf16(h_np))
+            i, l = step()
+            wi, wl = L.draft_project_argmax(dev_bf16(h_np), w, d2t)
+            assert np.array_equal(i.cpu().numpy(), wi.cpu().numpy()), (m, d)
+            assert np.array_equal(l.cpu().numpy().view(np.uint32), wl.cpu().numpy().view(np.uint32)), (m, d)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(200):
+            step()
+        host = (time.perf_counter() - t0) / 200 * 1e6
+        torch.cuda.synchronize()
+        log(f"[prepared] M={m}: bit-identical to the call; host time per queued step {host:.1f} us")

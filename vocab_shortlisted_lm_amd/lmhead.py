@@ -27,7 +27,7 @@ __all__ = [
     "LMH_MAX_OVERWRITE", "LMH_MAX_UNION_VOCAB", "draft_project_argmax_indexed",
     "lmhead_bench_time_argmax_indexed", "lmhead_quantize_mxfp4", "draft_project_argmax_mxfp4",
     "lmhead_bench_time_argmax_mxfp4", "lmhead_mxfp4_scale_bytes", "lmhead_mxfp4_tile_scales",
-    "mxfp4_scale_shape", "draft_project_topk_fp8", "draft_project_topk_mxfp4",
+    "mxfp4_scale_shape", "draft_project_topk_fp8", "draft_project_topk_mxfp4", "PreparedArgmax",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "liblmhead.so")
@@ -245,6 +245,37 @@ def draft_project_argmax_path(h: torch.Tensor, W: torch.Tensor, d2t: torch.Tenso
         out_id.data_ptr(), out_logit.data_ptr(), workspace.data_ptr(), _nbytes(workspace), path, st)
     _check(code, "draft_project_argmax")
     return out_id, out_logit
+
+
+class PreparedArgmax:
+    """draft_project_argmax_path with its tensors checked once.
+
+    A decode loop calls the draft head with the same buffers every step:
+    the hidden rows are rewritten in place, the outputs and the workspace
+    stay.  This object runs the binding's checks at construction and then
+    makes one C call per step; the tensors must keep their storage
+    (no resize or reallocation) while it is used, and it holds references so
+    they stay alive.  Calling it queues the step on the stream given here
+    and returns (out_id, out_logit)."""
+
+    def __init__(self, h: torch.Tensor, W: torch.Tensor, d2t: torch.Tensor | None = None,
+                 path: int = LMH_PATH_AUTO, out_id: torch.Tensor | None = None,
+                 out_logit: torch.Tensor | None = None, workspace: torch.Tensor | None = None, stream=None):
+        m, k, r = _check_hw(h, W, d2t)
+        self.out_id, self.out_logit = _outputs(m, out_id, out_logit, h.device)
+        st = _stream(stream, h.device)
+        self.workspace = _workspace(workspace, h.device, st)
+        self._keep = (h, W, d2t)
+        self._fn = lib().draft_project_argmax_path
+        self._args = (h.data_ptr(), m, k, W.data_ptr(), r, d2t.data_ptr() if d2t is not None else None,
+                      self.out_id.data_ptr(), self.out_logit.data_ptr(), self.workspace.data_ptr(),
+                      _nbytes(self.workspace), path, st)
+
+    def __call__(self):
+        code = self._fn(*self._args)
+        if code != LMH_OK:
+            raise LmheadError(code, "draft_project_argmax")
+        return self.out_id, self.out_logit
 
 
 def draft_project_argmax(h, W, d2t=None, out_id=None, out_logit=None, workspace=None,
