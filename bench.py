@@ -97,7 +97,12 @@ def describe(a, synth, L):
     if a.fp8 or a.mxfp4:
         chosen = L.LMH_PATH_MFMA if path == L.LMH_PATH_AUTO else path   # the library's FP8 / MXFP4 default
     else:
-        chosen = L.draft_project_auto_path(m, c.k) if path == L.LMH_PATH_AUTO else path
+        rows_now = c.n if (ids is None or a.full) else ids.size
+        # the library's choice: by head size for an argmax over a trimmed or
+        # full head; indexed, top-k and logits calls keep the full-head rule
+        by_rows = not (a.indexed or a.topk or a.logits)
+        chosen = (path if path != L.LMH_PATH_AUTO else
+                  L.draft_project_auto_path_rows(m, c.k, rows_now) if by_rows else L.draft_project_auto_path(m, c.k))
     kpath = {L.LMH_PATH_VALU: "valu", L.LMH_PATH_MFMA: "mfma"}[chosen]
     if trimmed:
         rows = ids.size

@@ -66,6 +66,19 @@ def test_workspace_bytes(L):
         assert ws == m * 1024 * 8 and ws % 16 == 0
 
 
+def test_auto_path_by_head_size(L):
+    # four hidden rows: matrix cores below 131,072 head rows, VALU above
+    assert L.draft_project_auto_path_rows(4, 2560, 32768) == L.LMH_PATH_MFMA
+    assert L.draft_project_auto_path_rows(4, 2560, 131071) == L.LMH_PATH_MFMA
+    assert L.draft_project_auto_path_rows(4, 2560, 131072) == L.LMH_PATH_VALU
+    assert L.draft_project_auto_path_rows(4, 2560, 248320) == L.LMH_PATH_VALU
+    for m in (1, 2, 3):
+        assert L.draft_project_auto_path_rows(m, 2560, 16000) == L.LMH_PATH_VALU
+    assert L.draft_project_auto_path_rows(5, 2560, 248320) == L.LMH_PATH_MFMA
+    assert L.draft_project_auto_path_rows(4, 2560, 0) == -1
+    assert L.draft_project_auto_path_rows(0, 2560, 100) == -1
+
+
 def test_auto_path(L):
     assert L.draft_project_auto_path(1, 2560) == L.LMH_PATH_VALU
     assert L.draft_project_auto_path(4, 2560) == L.LMH_PATH_VALU

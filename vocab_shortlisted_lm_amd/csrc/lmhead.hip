@@ -2453,15 +2453,30 @@ int run(const Call& c, const Epi& epi, int topk, int32_t* out_id, float* out_log
 bool valu_epi_ok(int64_t M, int64_t K) { return M <= 4 && valu_ok(M, K); }
 
 // Shared argument checks; returns LMH_OK and the resolved path, or a status.
-int check_common(const uint16_t* h, int64_t M, int64_t K, const uint16_t* W, int64_t R, int mode, int* path) {
+// The default kernel of a call with M hidden rows over R head rows (mode 0:
+// argmax, else top k / logits; `indexed`: rows read in place through a
+// list).  VALU up to 4 hidden rows, matrix cores above, measured on the
+// full head.  Exception, measured on the lists: an argmax over 4 hidden
+// rows and a head of fewer than LMH_RING_MAX_ROWS rows runs 1-4% faster on
+// the matrix cores (32,768 rows: 27.24 against 28.37 us; 16,000: 15.39
+// against 15.67; 52,755: 43.09 against 43.60), while on the full head the
+// VALU kernel is 2% faster (179.4 against 183.3 us).  Read in place through
+// a list the matrix cores are slower at 16,000 and 52,755 rows, so indexed
+// calls keep the VALU kernel.
+int default_path(int64_t M, int64_t K, int64_t R, int mode, bool indexed) {
+  if (M > LMH_VALU_AUTO_MAX_M || !(mode == 0 ? valu_ok(M, K) : valu_epi_ok(M, K))) return LMH_PATH_MFMA;
+  if (mode == 0 && !indexed && M == 4 && R < LMH_RING_MAX_ROWS) return LMH_PATH_MFMA;
+  return LMH_PATH_VALU;
+}
+
+int check_common(const uint16_t* h, int64_t M, int64_t K, const uint16_t* W, int64_t R, int mode, int* path,
+                 bool indexed = false) {
   if (!h || !W) return LMH_EINVAL;
   if (M < 1 || M > LMH_MAX_M || !k_ok(K)) return LMH_EINVAL;
   if (R < 1 || R > kMaxRows) return LMH_EINVAL;
   if (!aligned16(h) || !aligned16(W)) return LMH_EINVAL;
   if (*path != LMH_PATH_AUTO && *path != LMH_PATH_VALU && *path != LMH_PATH_MFMA) return LMH_EINVAL;
-  if (*path == LMH_PATH_AUTO)
-    *path = (M <= LMH_VALU_AUTO_MAX_M && (mode == 0 ? valu_ok(M, K) : valu_epi_ok(M, K))) ? LMH_PATH_VALU
-                                                                                           : LMH_PATH_MFMA;
+  if (*path == LMH_PATH_AUTO) *path = default_path(M, K, R, mode, indexed);
   if (*path == LMH_PATH_VALU && !(mode == 0 ? valu_ok(M, K) : valu_epi_ok(M, K))) return LMH_EINVAL;
   return LMH_OK;
 }
@@ -2597,7 +2612,12 @@ size_t draft_project_workspace_bytes(int64_t M) {
 
 int draft_project_auto_path(int64_t M, int64_t K) {
   if (M < 1 || M > LMH_MAX_M || !k_ok(K)) return -1;
-  return (M <= LMH_VALU_AUTO_MAX_M && valu_ok(M, K)) ? LMH_PATH_VALU : LMH_PATH_MFMA;
+  return default_path(M, K, LMH_RING_MAX_ROWS, 0, false);
+}
+
+int draft_project_auto_path_rows(int64_t M, int64_t K, int64_t R) {
+  if (M < 1 || M > LMH_MAX_M || !k_ok(K) || R < 1 || R > kMaxRows) return -1;
+  return default_path(M, K, R, 0, false);
 }
 
 int draft_project_argmax_path(const uint16_t* h, int64_t M, int64_t K, const uint16_t* W, int64_t R,
@@ -2623,7 +2643,7 @@ int draft_project_argmax(const uint16_t* h, int64_t M, int64_t K, const uint16_t
 int draft_project_argmax_indexed(const uint16_t* h, int64_t M, int64_t K, const uint16_t* W, int64_t N,
                                  const int32_t* ids, int64_t S, int32_t* out_id, float* out_logit, void* workspace,
                                  size_t workspace_bytes, int path, void* stream) {
-  int st = check_common(h, M, K, W, S, 0, &path);
+  int st = check_common(h, M, K, W, S, 0, &path, true);
   if (st != LMH_OK) return st;
   if (N < 1 || N > (int64_t)0x7FFFFFFF || !ids || (reinterpret_cast<uintptr_t>(ids) & 3u) != 0) return LMH_EINVAL;
   if (!out_id || !out_logit) return LMH_EINVAL;
@@ -2926,7 +2946,7 @@ int lmhead_bench_time_argmax_indexed(const uint16_t* h, int64_t M, int64_t K, co
   int st = LMH_OK;
   for (int i = 0; i < nheads; ++i) {
     path = path_in;
-    if ((st = check_common(h, M, K, heads[i], S, 0, &path)) != LMH_OK) return st;
+    if ((st = check_common(h, M, K, heads[i], S, 0, &path, true)) != LMH_OK) return st;
   }
   if (N < 1 || N > (int64_t)0x7FFFFFFF || !ids || (reinterpret_cast<uintptr_t>(ids) & 3u) != 0) return LMH_EINVAL;
   if (!out_id || !out_logit) return LMH_EINVAL;

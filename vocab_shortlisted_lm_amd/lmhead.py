@@ -18,7 +18,7 @@ __all__ = [
     "LmheadError", "lib", "LMH_OK", "LMH_EINVAL", "LMH_ERANGE", "LMH_EWORKSPACE",
     "LMH_EHIP", "LMH_MAX_M", "LMH_MIN_K", "LMH_MAX_K", "LMH_PATH_AUTO", "LMH_PATH_VALU",
     "LMH_PATH_MFMA", "lmhead_trim", "draft_project_workspace_bytes", "draft_project_argmax",
-    "draft_project_argmax_path", "draft_project_auto_path", "lmhead_status_str",
+    "draft_project_argmax_path", "draft_project_auto_path", "draft_project_auto_path_rows", "lmhead_status_str",
     "lmhead_last_error", "lmhead_bench_sink_words", "lmhead_bench_stream_read",
     "lmhead_bench_copy", "new_workspace", "read_id_list", "LMH_MAX_TOPK",
     "draft_project_topk_workspace_bytes", "draft_project_topk", "draft_project_logits",
@@ -49,6 +49,7 @@ SIGNATURES = {
     "draft_project_argmax": (_INT, [_P, _I64, _I64, _P, _I64, _P, _P, _P, _P, _SZ, _P]),
     "draft_project_argmax_path": (_INT, [_P, _I64, _I64, _P, _I64, _P, _P, _P, _P, _SZ, _INT, _P]),
     "draft_project_auto_path": (_INT, [_I64, _I64]),
+    "draft_project_auto_path_rows": (_INT, [_I64, _I64, _I64]),
     "draft_project_topk_workspace_bytes": (_SZ, [_I64, _I64]),
     "draft_project_topk": (_INT, [_P, _I64, _I64, _P, _I64, _P, _I64, _P, _P, _P, _SZ, _INT, _P]),
     "draft_project_logits": (_INT, [_P, _I64, _I64, _P, _I64, _P, _I64, _P, _INT, _P]),
@@ -210,6 +211,10 @@ def draft_project_workspace_bytes(M: int) -> int:
 
 def draft_project_auto_path(M: int, K: int) -> int:
     return int(lib().draft_project_auto_path(M, K))
+
+
+def draft_project_auto_path_rows(M: int, K: int, R: int) -> int:
+    return int(lib().draft_project_auto_path_rows(M, K, R))
 
 
 def new_workspace(device=None, M: int = LMH_MAX_M) -> torch.Tensor:
