@@ -163,6 +163,25 @@ def test_full_head_two_and_three_rows(L, m):
     run_and_check(L, hs, inp["W"], device_weights(2), None, paths_for(L, m, c.k), f"full M={m}")
 
 
+@pytest.mark.parametrize("r", [131_071, 131_072])
+def test_four_rows_at_the_head_size_boundary(L, r):
+    """The argmax at M = 4 takes the matrix cores below 131,072 head rows
+    and VALU from there on: on both sides of the boundary the default call
+    matches the oracle and, bit for bit, the kernel that the rule names."""
+    inp = config_inputs(2)
+    c = inp["config"]
+    w_np, w_dev = inp["W"][:r], device_weights(2)[:r]
+    want = L.LMH_PATH_MFMA if r < 131_072 else L.LMH_PATH_VALU
+    assert L.draft_project_auto_path_rows(4, c.k, r) == want
+    hs = [synth.hidden(4040, d, 4, c.k) for d in range(3)]
+    run_and_check(L, hs, w_np, w_dev, None, [L.LMH_PATH_AUTO], f"{r} rows M=4")
+    for h in hs:
+        a = L.draft_project_argmax_path(dev_bf16(h), w_dev, None, L.LMH_PATH_AUTO)
+        b = L.draft_project_argmax_path(dev_bf16(h), w_dev, None, want)
+        assert np.array_equal(a[0].cpu().numpy(), b[0].cpu().numpy())
+        assert np.array_equal(a[1].cpu().numpy().view(np.uint32), b[1].cpu().numpy().view(np.uint32))
+
+
 def test_config3_16k_m3(L):
     inp = config_inputs(3)
     c = inp["config"]
