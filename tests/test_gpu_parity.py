@@ -33,11 +33,14 @@ def L():
 
 
 def dev_bf16(a):
-    return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda()
+    a = np.ascontiguousarray(a)
+    if not a.flags.writeable:      # torch.from_numpy wants a writable buffer
+        a = a.copy()
+    return torch.from_numpy(a.view(np.int16)).cuda()
 
 
 def dev_i32(a):
-    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).cuda()
+    return torch.from_numpy(np.array(a, dtype=np.int32)).cuda()   # a writable copy
 
 
 def paths_for(L, m, k):
