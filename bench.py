@@ -232,12 +232,26 @@ def record_traffic(a, d, fetch_csv: str, write_csv: str) -> int:
     return 0
 
 
+def blas_threads() -> dict:
+    """The BLAS library numpy calls (name and version, from threadpoolctl)
+    and the threads it runs: the cores the oracle's fp64 matrix products
+    actually use."""
+    import numpy  # noqa: F401  (loads the BLAS library threadpoolctl inspects)
+    from threadpoolctl import threadpool_info
+    libs = [d for d in threadpool_info() if d.get("user_api") == "blas"] or threadpool_info()
+    if not libs:
+        return {"library": "unknown", "threads": 1}
+    top = max(libs, key=lambda d: d.get("num_threads", 1))
+    name = f"{top.get('internal_api', top.get('prefix', 'blas'))} {top.get('version') or ''}".strip()
+    return {"library": name, "threads": int(top.get("num_threads", 1))}
+
+
 def cpu_baseline(h_np, w_np, d2t_np, budget_s: float, indexed: bool = False):
     """The fp64 oracle timed on host cores over whole calls until `budget_s`
     (indexed: the oracle reads the listed rows of the full head in place)."""
     import oracle
-    from threadpoolctl import threadpool_info
-    threads = max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
+    blas = blas_threads()
+    threads = blas["threads"]
     calls = 0
     t0 = time.perf_counter()
     while True:
@@ -250,9 +264,11 @@ def cpu_baseline(h_np, w_np, d2t_np, budget_s: float, indexed: bool = False):
         if el >= budget_s or calls >= 50:
             break
     return {"value": calls / el, "unit": "calls/s", "cores": threads, "kind": "oracle",
+            "host_cpus": os.cpu_count(), "host_cpus_usable": len(os.sched_getaffinity(0)),
+            "blas": blas["library"], "blas_threads": threads,
             "sample": f"{calls} whole oracle calls (fp64, M={h_np.shape[0]}, "
                       f"{d2t_np.size if indexed else w_np.shape[0]} rows x K={w_np.shape[1]}) in {el:.1f} s; "
-                      f"numpy + BLAS with {threads} threads"}
+                      f"numpy + {blas['library']} with {threads} threads"}
 
 
 def shortlist_ops(synth, L, torch, np, dev) -> dict:
@@ -262,7 +278,7 @@ def shortlist_ops(synth, L, torch, np, dev) -> dict:
     and 600 escaped ids written into spare rows of the 32,768-id head."""
     stream = torch.cuda.current_stream(dev)
     w_np = synth.make_config(2)["W"]
-    w = torch.from_numpy(w_np.view(np.int16)).to(dev)
+    w = torch.from_numpy(np.array(w_np.view(np.int16))).to(dev)   # a writable copy of the read-only array
     k = w.shape[1]
     out = {"mode": "shortlist-ops", "K": k, "N": w.shape[0]}
 
@@ -388,8 +404,9 @@ def main() -> int:
     h_np = inp["h"][m] if m in inp["h"] else synth.hidden(c.h_seed[0], 0, m, c.k)
     w_np = inp["W"]
 
-    w_full = torch.from_numpy(w_np.view(np.int16)).to(dev)
-    h = torch.from_numpy(h_np.view(np.int16)).to(dev)
+    # writable copies: the seeded arrays are read-only and torch.from_numpy wants a writable buffer
+    w_full = torch.from_numpy(np.array(w_np.view(np.int16))).to(dev)
+    h = torch.from_numpy(np.array(h_np.view(np.int16))).to(dev)
     if a.indexed:
         d2t = torch.from_numpy(ids.astype(np.int32)).to(dev)
         heads = [w_full] + [w_full.clone() for _ in range(d["copies"] - 1)]

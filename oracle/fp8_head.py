@@ -5,11 +5,11 @@ check and the CPU baseline of the benchmark use it; the product path never
 imports it, and it shares no code with the HIP library.
 
 The pages convert weights that are read on every decode step to FP8 E4M3 at
-load to halve the bytes read, and requantize a trimmed head to a 4-bit format
-at no measured acceptance cost (ai-muninn.com "Qwen3.8-Flash-Next on two
-DGX Sparks", "The costs: a 69% smaller KV pool and FP8 GDN weights" and the
-kernel notes under "Decode runs at 80-87% of memory bandwidth";
-krisbailey.com/articles/shortlist-mtp, "Re-running the comparison fairly").
+load to halve the bytes read (ai-muninn.com "Qwen3.8-Flash-Next on two DGX
+Sparks", "The costs: a 69% smaller KV pool and FP8 GDN weights" and the
+kernel notes under "Decode runs at 80-87% of memory bandwidth"), and
+requantize a trimmed head to a 4-bit format at no measured acceptance cost
+(zone-1.cobraproject.com "Masked MTP drafts", section "Masked MTP drafts").
 They do not fix the scaling granularity or the rounding.  Readings taken
 here, each listed in the design notes of the repository:
 

@@ -9,8 +9,9 @@ What is computed, and where it is defined:
 
 * The draft head scores a hidden state of width K against LM-head rows, and
   the greedy draft is the highest-scoring row ("What I was testing" on
-  krisbailey.com/articles/shortlist-mtp; greedy decoding at temperature zero in
-  "Re-running the comparison fairly" there).
+  krisbailey.com/articles/shortlist-mtp; greedy speculative decoding with
+  the trim on, zone-1.cobraproject.com "Masked MTP drafts", section "Update
+  (November 2026)").
 * A shortlisted head is the full head's weight restricted to a list of ids,
   cut at load time ("Two ways to run it" on zone-1.cobraproject.com "Masked
   MTP drafts"); a shortlisted draft can only propose ids on the list

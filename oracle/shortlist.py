@@ -6,10 +6,10 @@ imports it, and it shares no code with the HIP library.
 
 Two operations the pages use to keep a trimmed head useful:
 
-* A static trim can miss tokens the target still emits; a server fixed this
-  by writing the escaped ids into spare rows of the trimmed head
-  (krisbailey.com/articles/shortlist-mtp, the three-months-later update in
-  "Re-running the comparison fairly").  Reading: an overwrite of chosen rows
+* A static trim can miss tokens the target still emits; on one model the
+  server fixed this by learning the escaped ids into spare rows of the
+  trimmed head (zone-1.cobraproject.com "Masked MTP drafts", section "Update
+  (November 2026)", the Gemma 4 31B case).  Reading: an overwrite of chosen rows
   of W_trim with rows of W, and of the same d2t entries with the ids; the
   caller then projects over the grown prefix of rows.
 * A list is widened by the sorted union of two id lists (ai-muninn.com

@@ -31,20 +31,36 @@ import oracle
 LOGIT_TOL = 2e-2
 GAP_EXEMPT = 1e-2
 U32 = 2.0 ** -24
+# Upper bound on the fraction of rows where the GPU may pick another
+# near-tied id.  Rows whose oracle top-2 gap is at most 1e-2 make up about
+# 3-9% of these workloads (Gaussian logits of scale 0.3-1, 4k-248k rows);
+# the GPU can only differ from the oracle on the part of them whose gap is
+# below its fp32 error, far fewer.  A rise past 5% means ties or near ties
+# are being decided wrongly, which the per-row rule alone would let pass.
+EXEMPT_MAX_FRACTION = 0.05
 
 
 @dataclass
 class ParityStats:
     rows: int = 0
     exempt: int = 0          # near-tie rows where the GPU chose another valid id
+    near_ties: int = 0       # rows (or positions) whose oracle gap is at most 1e-2
     max_err: float = 0.0     # max |gpu logit - oracle logit of the GPU's row|
     max_err_over_bound: float = 0.0
 
     def add(self, other: "ParityStats") -> None:
         self.rows += other.rows
         self.exempt += other.exempt
+        self.near_ties += other.near_ties
         self.max_err = max(self.max_err, other.max_err)
         self.max_err_over_bound = max(self.max_err_over_bound, other.max_err_over_bound)
+
+    def assert_exempt_bound(self) -> None:
+        """Exempt rows are a subset of the near ties and stay below
+        EXEMPT_MAX_FRACTION of the rows (plus one, for small samples)."""
+        assert self.exempt <= self.near_ties, (self.exempt, self.near_ties)
+        assert self.exempt <= EXEMPT_MAX_FRACTION * self.rows + 1, (
+            f"{self.exempt} of {self.rows} rows took another near-tied id")
 
 
 def _row_bound(h_row: np.ndarray, w_row: np.ndarray, k: int, extra: int = 1) -> float:
@@ -119,6 +135,7 @@ def _check_core(h_bits, w_rows, r, d2t, gpu_id, gpu_logit, res, extra) -> Parity
             assert gpu_id[i] == res.id[i], f"row {i}: id {gpu_id[i]} != oracle {res.id[i]}"
         # stated bar
         assert abs(gpu_logit[i] - res.logit[i]) <= LOGIT_TOL
+        st.near_ties += int(res.gap[i] <= GAP_EXEMPT)
         if res.gap[i] > GAP_EXEMPT:
             assert gpu_id[i] == res.id[i], f"row {i}: id {gpu_id[i]} != oracle {res.id[i]}"
         elif gpu_id[i] != res.id[i]:
@@ -211,6 +228,7 @@ def _check_topk_core(h_bits, w_rows, r, d2t, gpu_ids, gpu_logits, res, extra) ->
             assert abs(gl[j] - res.logit[i, j]) <= LOGIT_TOL
             hi = srt[j - 1] - srt[j] if j > 0 else np.inf
             lo = srt[j] - srt[j + 1] if j + 1 < r else np.inf
+            st.near_ties += int(min(hi, lo) <= GAP_EXEMPT)
             if min(hi, lo) > min(GAP_EXEMPT, bmax):
                 assert gpu_ids[i, j] == res.id[i, j], (i, j, gpu_ids[i, j], res.id[i, j])
             elif gpu_ids[i, j] != res.id[i, j]:

@@ -124,3 +124,19 @@ def test_record_and_look_up_traffic(tmp_path, monkeypatch):
     src.write_text("int changed;\n")
     monkeypatch.setattr(bench, "KERNEL_SOURCE", str(src))
     assert bench.measured_traffic("valu", "w1") is None
+
+
+def test_cpu_baseline_names_its_cores_and_blas():
+    """The CPU baseline record states the threads the oracle ran on, the
+    host's CPU count and the BLAS library, each as its own field."""
+    import numpy as np
+    import synth
+    inp = synth.make_config(1)
+    h = synth.hidden(101, 0, 1, 256)
+    rec = bench.cpu_baseline(h, inp["W"], None, 0.05)
+    assert rec["kind"] == "oracle" and rec["unit"] == "calls/s" and rec["value"] > 0
+    assert rec["host_cpus"] == os.cpu_count()
+    assert 1 <= rec["host_cpus_usable"] <= os.cpu_count()
+    assert rec["cores"] == rec["blas_threads"] >= 1
+    assert rec["blas"] != "unknown" and rec["blas"] in rec["sample"]
+    assert np.isfinite(rec["value"])

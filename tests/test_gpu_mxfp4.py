@@ -22,6 +22,7 @@ import pytest
 
 import oracle
 import synth
+from devcopy import dev_u8
 from parity import ParityStats, check_mxfp4
 from test_gpu_parity import config_inputs, dev_bf16, dev_i32, device_weights, draws, log
 
@@ -35,10 +36,6 @@ def L():
     from vocab_shortlisted_lm_amd import lmhead
     lmhead.lib()
     return lmhead
-
-
-def dev_u8(a):
-    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.uint8)).cuda()
 
 
 def tile_scales(sc, fill=0):
@@ -109,8 +106,9 @@ def run_and_check(L, hs, codes, scales, d2t_np, tag, q_dev=None, s_dev=None):
             lgs.append(l.cpu().numpy())
         st = ParityStats()
         st.add(check_mxfp4(stack, codes, scales, d2t_np, np.concatenate(ids), np.concatenate(lgs), res))
-        log(f"[{tag}] path={p} rows={st.rows} exempt={st.exempt} max_err={st.max_err:.2e} "
+        log(f"[{tag}] path={p} rows={st.rows} near_ties={st.near_ties} exempt={st.exempt} max_err={st.max_err:.2e} "
             f"err/bound={st.max_err_over_bound:.3f}")
+        st.assert_exempt_bound()
 
 
 # --------------------------------------------------------------------------
@@ -227,7 +225,7 @@ def test_tile_scales_of_oracle_quantization_drive_the_argmax(L):
 # --------------------------------------------------------------------------
 
 @pytest.mark.parametrize("cfg,trimmed,m,n", [
-    (2, False, 1, 6), (3, True, 3, 6), (4, True, 1, 8), (4, True, 4, 4), (5, True, 24, 2), (5, False, 24, 1),
+    (2, False, 1, 16), (3, True, 3, 16), (4, True, 1, 16), (4, True, 4, 16), (5, True, 24, 16), (5, False, 24, 16),
 ])
 def test_mxfp4_argmax_configs(L, cfg, trimmed, m, n):
     inp = config_inputs(cfg)
@@ -390,8 +388,9 @@ def run_topk_mx(L, h, codes, scales, d2t_np, topk, tag):
     for p in (L.LMH_PATH_AUTO, L.LMH_PATH_MFMA):
         i, lg = L.draft_project_topk_mxfp4(dev_bf16(h), q_dev, s_dev, d2t_dev, topk, path=p)
         st = check_topk_mxfp4(h, codes, scales, d2t_np, i.cpu().numpy(), lg.cpu().numpy(), res)
-        log(f"[{tag}] path={p} k={topk} positions={st.rows} exempt={st.exempt} max_err={st.max_err:.2e} "
+        log(f"[{tag}] path={p} k={topk} positions={st.rows} near_ties={st.near_ties} exempt={st.exempt} max_err={st.max_err:.2e} "
             f"err/bound={st.max_err_over_bound:.3f}")
+        st.assert_exempt_bound()
 
 
 @pytest.mark.parametrize("cfg,trimmed,m,topk", [

@@ -118,8 +118,9 @@ def test_random_shape(L, case):
                 got = [L.draft_project_argmax_mxfp4(dev_bf16(h), q_dev, s_dev, d2t_dev, p) for h in hs]
                 st.add(check_mxfp4(stack, codes, scales, d2t, np.concatenate([g[0].cpu().numpy() for g in got]),
                                    np.concatenate([g[1].cpu().numpy() for g in got]), res))
-    log(f"[random {i}] rows={st.rows} exempt={st.exempt} max_err={st.max_err:.2e} "
+    log(f"[random {i}] rows={st.rows} near_ties={st.near_ties} exempt={st.exempt} max_err={st.max_err:.2e} "
         f"err/bound={st.max_err_over_bound:.3f}")
+    st.assert_exempt_bound()
 
 
 # --------------------------------------------------------------------------

@@ -121,4 +121,5 @@ def test_learn_escaped_ids_then_project(L, m):
             gl.append(lg.cpu().numpy())
         st = check(stack, w_live, d2t_np, np.concatenate(gi), np.concatenate(gl), res)
         learned = np.isin(np.concatenate(gi), escaped).sum()
-        log(f"[learn M={m}] path={p} rows={st.rows} exempt={st.exempt} picked a learned id {learned}x")
+        log(f"[learn M={m}] path={p} rows={st.rows} near_ties={st.near_ties} exempt={st.exempt} picked a learned id {learned}x")
+        st.assert_exempt_bound()

@@ -38,8 +38,9 @@ def run_topk(L, hs, w_np, w_dev, d2t_np, k, tag):
             ids.append(i.cpu().numpy())
             lgs.append(l.cpu().numpy())
         st = check_topk(stack, w_np, d2t_np, np.concatenate(ids), np.concatenate(lgs), res)
-        log(f"[{tag}] path={p} k={k} positions={st.rows} exempt={st.exempt} "
+        log(f"[{tag}] path={p} k={k} positions={st.rows} near_ties={st.near_ties} exempt={st.exempt} "
             f"max_err={st.max_err:.2e} err/bound={st.max_err_over_bound:.3f}")
+        st.assert_exempt_bound()
 
 
 @pytest.mark.parametrize("k", [1, 3, 8, 16])
