@@ -48,12 +48,16 @@ def algorithmic_bytes(m: int, rows: int, k: int, with_d2t: bool, fmt: str = "bf1
 
 
 def head_bytes(rows: int, k: int, fmt: str = "bf16") -> int:
-    """Bytes of the head: bf16; E4M3 codes plus one fp32 scale per row; or
-    MXFP4 codes (two per byte) plus one E8M0 scale byte per 32 elements."""
+    """Bytes of the head: bf16; E4M3 codes plus one fp32 scale per row;
+    MXFP4 codes (two per byte) plus one E8M0 scale byte per 32 elements; or
+    NVFP4 codes plus one E4M3 scale byte per 16 elements and the head's fp32
+    scale."""
     if fmt == "fp8":
         return rows * k + rows * 4
     if fmt == "mxfp4":
         return rows * (k // 2) + rows * (k // 32)
+    if fmt == "nvfp4":
+        return rows * (k // 2) + rows * (k // 16) + 4
     return weight_bytes(rows, k)
 
 
@@ -94,8 +98,9 @@ def describe(a, synth, L):
     ids = inp["ids"]
     trimmed = ids is not None and not a.full
     path = {"auto": L.LMH_PATH_AUTO, "valu": L.LMH_PATH_VALU, "mfma": L.LMH_PATH_MFMA}[a.path]
-    if a.fp8 or a.mxfp4:
-        chosen = L.LMH_PATH_MFMA if path == L.LMH_PATH_AUTO else path   # the library's FP8 / MXFP4 default
+    quantized = a.fp8 or a.mxfp4 or a.nvfp4
+    if quantized:
+        chosen = L.LMH_PATH_MFMA if path == L.LMH_PATH_AUTO else path   # the library's quantized-head default
     else:
         rows_now = c.n if (ids is None or a.full) else ids.size
         # the library's choice: by head size for an argmax over a trimmed or
@@ -112,20 +117,22 @@ def describe(a, synth, L):
         rows, copies = c.n, 1
         workload = (f"full-vocab draft step M={m} K={c.k} N={c.n}" if a.config == 2
                     else f"{c.name}: M={m} K={c.k} full head N={c.n}")
-    if a.fp8 and a.mxfp4:
-        raise SystemExit("bench.py: --fp8 and --mxfp4 exclude each other")
+    if (a.fp8 + a.mxfp4 + a.nvfp4) > 1:
+        raise SystemExit("bench.py: --fp8, --mxfp4 and --nvfp4 exclude each other")
     if a.topk and a.logits:
         raise SystemExit("bench.py: --topk and --logits exclude each other")
     if (a.topk or a.logits) and a.indexed:
         raise SystemExit("bench.py: --topk and --logits time trimmed or full heads, not --indexed")
-    if a.logits and (a.fp8 or a.mxfp4):
+    if a.logits and quantized:
         raise SystemExit("bench.py: --logits takes a bf16 head")
+    if a.onepass and (quantized or a.indexed or a.topk or a.logits):
+        raise SystemExit("bench.py: --onepass times the bf16 argmax over a full or trimmed head")
     if a.topk and not 1 <= a.topk <= L.LMH_MAX_TOPK:
         raise SystemExit(f"bench.py: --topk must be 1..{L.LMH_MAX_TOPK}")
     if a.indexed:
-        if ids is None or a.full or a.fp8 or a.mxfp4:
+        if ids is None or a.full or quantized:
             raise SystemExit("bench.py: --indexed needs a shortlist config (1, 3, 4, 5), without --full, "
-                             "--fp8 or --mxfp4")
+                             "--fp8, --mxfp4 or --nvfp4")
         workload = (f"{c.name}: M={m} K={c.k} {rows} listed rows read in place from the full head "
                     f"N={c.n} ({copies} rotated copies of W)")
     if a.fp8:
@@ -140,7 +147,14 @@ def describe(a, synth, L):
             copies = max(1, -(-2 * MALL_BYTES // head_bytes(rows, c.k, "mxfp4")) + 1)
             workload = f"{c.name}: M={m} K={c.k} trimmed to {rows} rows ({copies} rotated copies)"
         workload += ", MXFP4 head (E2M1, E8M0 scale per 32)"
-    fmt = "fp8" if a.fp8 else ("mxfp4" if a.mxfp4 else "bf16")
+    if a.nvfp4:
+        if kpath != "mfma":
+            raise SystemExit("bench.py: NVFP4 heads run on the matrix-core path only")
+        if trimmed:
+            copies = max(1, -(-2 * MALL_BYTES // head_bytes(rows, c.k, "nvfp4")) + 1)
+            workload = f"{c.name}: M={m} K={c.k} trimmed to {rows} rows ({copies} rotated copies)"
+        workload += ", NVFP4 head (E2M1, E4M3 scale per 16, fp32 head scale)"
+    fmt = "fp8" if a.fp8 else ("mxfp4" if a.mxfp4 else ("nvfp4" if a.nvfp4 else "bf16"))
     kname = kernel_name(kpath, m) if fmt == "bf16" else ("proj_mfma" if kpath == "mfma" else "proj_valu_fp8")
     return dict(inp=inp, c=c, m=m, ids=ids, trimmed=trimmed, path=path, kpath=kpath, rows=rows,
                 copies=copies, workload=workload, kname=kname, fmt=fmt)
@@ -351,6 +365,9 @@ def main() -> int:
     ap.add_argument("--mxfp4", action="store_true",
                     help="quantize the head (or shortlist) to MXFP4 at load and time "
                          "draft_project_argmax_mxfp4 (no CPU baseline)")
+    ap.add_argument("--nvfp4", action="store_true",
+                    help="quantize the head (or shortlist) to NVFP4 at load and time "
+                         "draft_project_argmax_nvfp4 (no CPU baseline)")
     ap.add_argument("--indexed", action="store_true",
                     help="read the shortlist's rows in place from the full head "
                          "(draft_project_argmax_indexed), rotating copies of W past the Infinity Cache")
@@ -361,6 +378,9 @@ def main() -> int:
                     help="time draft_project_logits instead of the argmax: every logit as [M, R] (rows), "
                          "or scattered through d2t into [M, N] with -inf elsewhere (vocab; the full head "
                          "takes d2t = 0..N-1); bf16 heads; whole calls only")
+    ap.add_argument("--onepass", action="store_true",
+                    help="time the argmax as one launch per call (lmhead_bench_argmax_onepass: the last "
+                         "workgroup folds) instead of the projection + fold pair; bf16 heads; whole calls only")
     ap.add_argument("--graph", action="store_true",
                     help="capture the --steps calls of a timed region in one HIP graph and time its replays "
                          "(the calls without the host's launch cost)")
@@ -431,6 +451,13 @@ def main() -> int:
             torch.cuda.synchronize()
         del heads, w
         heads = qheads
+    if a.nvfp4:
+        qheads = []
+        for w in heads:
+            qheads.append(L.lmhead_quantize_nvfp4(w))
+            torch.cuda.synchronize()
+        del heads, w
+        heads = qheads
     torch.cuda.synchronize()
 
     ws = L.new_workspace(dev)
@@ -452,14 +479,22 @@ def main() -> int:
         lg_out = torch.empty((m, lg_cols), dtype=torch.float32, device=dev)
         out_bytes = 4 * m * lg_cols
 
+    if a.onepass:
+        op_ws = L.lmhead_bench_onepass_workspace(dev, m)
+
     def step(i):
-        if a.topk:
+        if a.onepass:
+            L.lmhead_bench_argmax_onepass(h, heads[i % len(heads)], d2t, path, op_ws, out_id, out_logit, launch_on[0])
+        elif a.topk:
             if a.fp8:
                 q, sc = heads[i % len(heads)]
                 L.draft_project_topk_fp8(h, q, sc, d2t, a.topk, tk_id, tk_logit, tk_ws, path, launch_on[0])
             elif a.mxfp4:
                 q, sc = heads[i % len(heads)]
                 L.draft_project_topk_mxfp4(h, q, sc, d2t, a.topk, tk_id, tk_logit, tk_ws, path, launch_on[0])
+            elif a.nvfp4:
+                q, sc, gs = heads[i % len(heads)]
+                L.draft_project_topk_nvfp4(h, q, sc, gs, d2t, a.topk, tk_id, tk_logit, tk_ws, path, launch_on[0])
             else:
                 L.draft_project_topk(h, heads[i % len(heads)], d2t, a.topk, tk_id, tk_logit, tk_ws, path, launch_on[0])
         elif a.logits:
@@ -473,6 +508,9 @@ def main() -> int:
         elif a.mxfp4:
             q, sc = heads[i % len(heads)]
             L.draft_project_argmax_mxfp4(h, q, sc, d2t, path, out_id, out_logit, ws, launch_on[0])
+        elif a.nvfp4:
+            q, sc, gs = heads[i % len(heads)]
+            L.draft_project_argmax_nvfp4(h, q, sc, gs, d2t, path, out_id, out_logit, ws, launch_on[0])
         else:
             L.draft_project_argmax_path(h, heads[i % len(heads)], d2t, path, out_id, out_logit, ws,
                                         launch_on[0])
@@ -525,10 +563,10 @@ def main() -> int:
         torch.cuda.synchronize()
         rates.append(a.steps / (e0.elapsed_time(e1) / 1e3))
 
-    if a.topk or a.logits:
+    if a.topk or a.logits or a.onepass:
         # whole calls only: the kernel-only timer covers the argmax epilogue
         result = {
-            "mode": f"top-{a.topk}" if a.topk else f"logits ({a.logits})",
+            "mode": f"top-{a.topk}" if a.topk else (f"logits ({a.logits})" if a.logits else "argmax, single launch"),
             "workload": workload, "M": m, "K": c.k, "rows": rows, "fmt": d["fmt"], "graph": a.graph,
             "steps": a.steps,
             "warmup": a.warmup, "us_per_call": round(ms_per_step * 1e3, 2),
@@ -550,6 +588,8 @@ def main() -> int:
         proj_ms = L.lmhead_bench_time_argmax_fp8(h, heads, d2t, path, a.steps, out_id, out_logit, ws, stream)
     elif a.mxfp4:
         proj_ms = L.lmhead_bench_time_argmax_mxfp4(h, heads, d2t, path, a.steps, out_id, out_logit, ws, stream)
+    elif a.nvfp4:
+        proj_ms = L.lmhead_bench_time_argmax_nvfp4(h, heads, d2t, path, a.steps, out_id, out_logit, ws, stream)
     else:
         proj_ms = L.lmhead_bench_time_argmax(h, heads, d2t, path, a.steps, out_id, out_logit, ws, stream)
     # a rotated workload also timed on one copy, which the Infinity Cache can hold
@@ -562,6 +602,8 @@ def main() -> int:
             proj_ms_hot = L.lmhead_bench_time_argmax_fp8(h, one, d2t, path, a.steps, out_id, out_logit, ws, stream)
         elif a.mxfp4:
             proj_ms_hot = L.lmhead_bench_time_argmax_mxfp4(h, one, d2t, path, a.steps, out_id, out_logit, ws, stream)
+        elif a.nvfp4:
+            proj_ms_hot = L.lmhead_bench_time_argmax_nvfp4(h, one, d2t, path, a.steps, out_id, out_logit, ws, stream)
         else:
             proj_ms_hot = L.lmhead_bench_time_argmax(h, one, d2t, path, a.steps, out_id, out_logit, ws, stream)
     pbytes = projection_bytes(m, rows, c.k, d["fmt"], a.indexed)
@@ -609,6 +651,7 @@ def main() -> int:
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": {"fp8": "e4m3 W x bf16 h, fp32 accumulate", "mxfp4": "mxfp4 (e2m1 + e8m0) W x bf16 h, fp32 accumulate",
+                  "nvfp4": "nvfp4 (e2m1 + e4m3 per 16 + fp32) W x bf16 h, fp32 accumulate",
                   "bf16": "bf16"}[d["fmt"]],
         "data": "synthetic (seeded bf16 W ~ N(0, 0.02), h ~ N(0, 1))",
         "config": {"workload": workload, "M": m, "K": c.k, "rows": rows, "indexed": a.indexed,

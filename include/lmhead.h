@@ -58,12 +58,12 @@ typedef enum {
 #define LMH_MAX_M 32
 #define LMH_MIN_K 8
 #define LMH_MAX_K 8192
-#define LMH_MAX_R (1 << 30)
+#define LMH_MAX_R ((1 << 30) - 1)  /* rows of a head or entries of a list */
 #define LMH_MAX_TOPK 16
 #define LMH_MAX_OVERWRITE 65536      /* entries per lmhead_shortlist_overwrite call */
 #define LMH_MAX_UNION_VOCAB 524288   /* N of lmhead_shortlist_union (two LDS bitmaps) */
 
-/* Kernel choice for draft_project_argmax_path. */
+/* Kernel choice of the calls that take a `path` argument. */
 #define LMH_PATH_AUTO 0
 #define LMH_PATH_VALU 1  /* hidden rows in registers, packed bf16 dot products */
 #define LMH_PATH_MFMA 2  /* hidden rows in LDS, 16x16x32 bf16 matrix-core tiles */
@@ -98,7 +98,13 @@ int lmhead_trim(const uint16_t* W, int64_t N, int64_t K,
 size_t draft_project_workspace_bytes(int64_t M);
 
 /*
- * draft_project_argmax -- for each hidden row m:
+ * draft_project_argmax -- the draft head's greedy proposal, one draft step:
+ * score the hidden rows against every row of the head and keep the best
+ * (krisbailey.com/articles/shortlist-mtp, "What I was testing": a 2,560-wide
+ * hidden state against the LM head, one row per draft step and three per
+ * MTP2 verify step); over a trimmed head the winning row maps back to its
+ * vocabulary id through d2t (zone-1.cobraproject.com "Masked MTP drafts",
+ * "Two ways to run it").  For each hidden row m:
  *     idx[m]       = the smallest r maximizing  L[m, r] = sum_k h[m, k] * W[r, k]
  *     out_id[m]    = d2t ? d2t[idx[m]] : idx[m]
  *     out_logit[m] = L[m, idx[m]]
@@ -107,7 +113,8 @@ size_t draft_project_workspace_bytes(int64_t M);
  *
  *  h          [M, K] bf16, 16-byte aligned, 1 <= M <= LMH_MAX_M.
  *  W          [R, K] bf16, 16-byte aligned: the full head (R = N) or a
- *             trimmed head from lmhead_trim (R = S).  1 <= R <= 2^30.
+ *             trimmed head from lmhead_trim (R = S).  1 <= R <= LMH_MAX_R
+ *             (2^30 - 1).
  *  d2t        [R] int32 or NULL.  For a trimmed head pass the ids given to
  *             lmhead_trim (absolute vocabulary ids); NULL returns row indices.
  *  out_id     [M] int32.  -1 only if no logit of the row is ordered (NaN).
@@ -134,15 +141,38 @@ int draft_project_argmax(const uint16_t* h, int64_t M, int64_t K,
                          void* stream);
 
 /*
- * draft_project_argmax_path -- draft_project_argmax with the kernel chosen
- * by the caller (LMH_PATH_*), for tests and measurement.  LMH_PATH_VALU
- * accepts M <= 8 with M * ceil(K / 512) <= 40; LMH_PATH_MFMA accepts every
- * shape draft_project_argmax accepts.  Other shapes give LMH_EINVAL.
+ * draft_project_argmax_keys -- the argmax of one slice of a head, as keys
+ * that combine across slices: the unit of work of one GPU when the head is
+ * split by vocabulary rows across GPUs, as a tensor-parallel lm_head is
+ * (ai-muninn.com "Qwen3.8-Flash-Next on two DGX Sparks", kernel table under
+ * "Decode runs at 80-87% of memory bandwidth": the 124,160-row shard of the
+ * 248,320-row head at TP = 2), or when a shortlist is split evenly across
+ * ranks ("Build the draft vocabulary from your own text", same page).  The
+ * argmax is still reduced where it is computed; only M keys leave a slice.
+ *
+ * For each hidden row m, with idx[m] the smallest maximizing row of the
+ * slice W (as for draft_project_argmax):
+ *     out_key[m] = (ord(L[m, idx[m]]) << 32) | (0xFFFFFFFF - (row_base + idx[m]))
+ * where ord is the order-preserving map of an fp32 value to 32 bits
+ * (negative values: all bits inverted; others: sign bit set; -0 taken as
+ * +0).  The unsigned maximum of the keys of all slices of a head is the
+ * whole head's key: its largest logit, and among equal logits the smallest
+ * global row.  Decode it as row = 0xFFFFFFFF - (key & 0xFFFFFFFF) and the
+ * logit from the high word, then map the row through the head's d2t (for a
+ * split list, row is the position in the whole list).  0 means no ordered
+ * logit (NaN inputs).
+ *
+ *  W          [R, K] bf16, the slice (rows row_base .. row_base + R - 1 of
+ *             the whole head or list), 16-byte aligned.
+ *  row_base   >= 0, row_base + R <= 2^32 - 1.
+ *  out_key    [M] uint64 (device, 8-byte aligned).
+ *  workspace, path, h, M, K, R: as for draft_project_argmax_path.
+ * Never synchronizes and never allocates; queues the projection and a
+ * small fold kernel.  Errors as for draft_project_argmax.
  */
-int draft_project_argmax_path(const uint16_t* h, int64_t M, int64_t K,
-                              const uint16_t* W, int64_t R,
-                              const int32_t* d2t,
-                              int32_t* out_id, float* out_logit,
+int draft_project_argmax_keys(const uint16_t* h, int64_t M, int64_t K,
+                              const uint16_t* W, int64_t R, int64_t row_base,
+                              uint64_t* out_key,
                               void* workspace, size_t workspace_bytes,
                               int path, void* stream);
 
@@ -264,7 +294,7 @@ int lmhead_quantize_mxfp4(const uint16_t* W, int64_t R, int64_t K,
 /*
  * lmhead_mxfp4_scale_bytes -- size in bytes of the tiled scale array of an
  * [R, K] MXFP4 head: ceil(R / 16) * ceil(K / 512) * 256.  Host only; -1 for
- * a bad shape (R outside [0, 2^31 - 1), K not a positive multiple of 32 up
+ * a bad shape (R outside [0, LMH_MAX_R], K not a positive multiple of 32 up
  * to the library's limit).
  */
 int64_t lmhead_mxfp4_scale_bytes(int64_t R, int64_t K);
@@ -307,6 +337,90 @@ int draft_project_argmax_mxfp4(const uint16_t* h, int64_t M, int64_t K,
                                int path, void* stream);
 
 /*
+ * lmhead_quantize_nvfp4 -- load-time copy of a bf16 head (W or W_trim) in
+ * NVFP4, the 4-bit format the pages requantize the trimmed draft head to at
+ * no measured acceptance cost (zone-1.cobraproject.com "Masked MTP drafts",
+ * the section of that name) and score a drafter's candidates through
+ * ("Update (November 2026)", same page): E2M1 elements (0, 0.5, 1, 1.5, 2,
+ * 3, 4, 6 and negatives), one E4M3 scale per 16 consecutive elements of a
+ * row, and one fp32 scale g for the whole head, so that element k of row r
+ * stands for e2m1(code) x e4m3(block scale) x g.  The pages do not give the
+ * conversion; the one used here (every division correctly rounded in fp32):
+ *   g          = max |W| / 2688 (448 x 6), or 1 for a head of zeros;
+ *   block code = the E4M3 value nearest to (amax_block / 6) / g, ties to the
+ *                even code, above 448 saturating to 448;
+ *   code       = the E2M1 value nearest to W / (decode(block code) x g),
+ *                ties to the even code, above 6 saturating to 6; a signed
+ *                zero where decode(block code) x g is 0.
+ *
+ *  W       [R, K] bf16 (device, 16-byte aligned); K a multiple of 16.
+ *  Wq      [R, K / 2] uint8 (device, 16-byte aligned): two codes per byte,
+ *          element 2i in the low nibble of byte i.
+ *  scales  lmhead_nvfp4_scale_bytes(R, K) bytes (device) of E4M3 block
+ *          scale codes in the tiled layout: with ng = ceil(K / 512), the
+ *          scale of row r, block j (elements 16 j .. 16 j + 15) is byte
+ *            ((r / 16 * ng + j / 32) * 16 + r % 16) * 32 + j % 32,
+ *          so the scales one 16-row tile needs for 512 elements are 512
+ *          contiguous bytes.  Padding bytes are not written.
+ *  gscale  one float (device, 4-byte aligned): receives g.  While the call
+ *          runs it holds the head's largest magnitude; read it after the
+ *          call's work has completed on `stream`.
+ * R = 0 is a no-op.  Asynchronous on `stream` (four small kernels);
+ * allocates nothing.  Returns LMH_EINVAL for a bad shape, a null or
+ * misaligned pointer.
+ */
+int lmhead_quantize_nvfp4(const uint16_t* W, int64_t R, int64_t K,
+                          uint8_t* Wq, uint8_t* scales, float* gscale,
+                          void* stream);
+
+/*
+ * lmhead_nvfp4_scale_bytes -- size in bytes of the tiled block-scale array
+ * of an [R, K] NVFP4 head: ceil(R / 16) * ceil(K / 512) * 512.  Host only;
+ * -1 for a bad shape (R outside [0, LMH_MAX_R], K not a positive multiple of
+ * 16 up to the library's limit).
+ */
+int64_t lmhead_nvfp4_scale_bytes(int64_t R, int64_t K);
+
+/*
+ * lmhead_nvfp4_tile_scales -- row-major E4M3 block scales [R, K / 16] (a
+ * head quantized elsewhere, with its own g) into the tiled layout of
+ * lmhead_quantize_nvfp4.
+ *
+ *  src     [R, K / 16] uint8 (device).
+ *  scales  lmhead_nvfp4_scale_bytes(R, K) bytes (device); padding bytes are
+ *          not written.
+ * R = 0 is a no-op.  Asynchronous on `stream`; allocates nothing.
+ * Returns LMH_EINVAL for a bad shape or a null pointer.
+ */
+int lmhead_nvfp4_tile_scales(const uint8_t* src, int64_t R, int64_t K, uint8_t* scales, void* stream);
+
+/*
+ * draft_project_argmax_nvfp4 -- draft_project_argmax over an NVFP4 head
+ * from lmhead_quantize_nvfp4: out_logit[m] = max_r g * sum_k h[m, k] *
+ * e2m1(Wq[r, k]) * e4m3(scale of block k / 16 of row r); each element times
+ * its block scale is a bf16 number (at most 6 significant bits), so every
+ * product is exact, the sums are fp32 and g multiplies each row's sum once.
+ * out_id as for draft_project_argmax (first row among equal maxima, mapped
+ * through d2t).  The head streams at 0.5625 bytes per weight (codes and
+ * block scales).  The matrix cores take every M.
+ *
+ *  Wq, scales, gscale  as written by lmhead_quantize_nvfp4 (R rows; scales
+ *                      in the tiled layout, all of which may be read); K a
+ *                      multiple of 512; Wq and scales 16-byte aligned,
+ *                      gscale 4-byte aligned.
+ *  path                LMH_PATH_AUTO or LMH_PATH_MFMA.
+ * Other arguments, workspace, synchronization and errors as for
+ * draft_project_argmax.
+ */
+int draft_project_argmax_nvfp4(const uint16_t* h, int64_t M, int64_t K,
+                               const uint8_t* Wq, const uint8_t* scales,
+                               const float* gscale, int64_t R,
+                               const int32_t* d2t,
+                               int32_t* out_id, float* out_logit,
+                               void* workspace, size_t workspace_bytes,
+                               int path, void* stream);
+
+/*
  * draft_project_topk_fp8, draft_project_topk_mxfp4 -- draft_project_topk
  * over a quantized head: the `topk` best rows of the dequantized FP8 or
  * MXFP4 head per hidden row, best first, mapped through d2t.  The pages
@@ -336,6 +450,20 @@ int draft_project_topk_mxfp4(const uint16_t* h, int64_t M, int64_t K,
                              int path, void* stream);
 
 /*
+ * draft_project_topk_nvfp4 -- the same over an NVFP4 head (Wq, scales,
+ * gscale as for draft_project_argmax_nvfp4): the drafter's candidates
+ * scored through the target's NVFP4 head (zone-1.cobraproject.com "Masked
+ * MTP drafts", "Update (November 2026)").
+ */
+int draft_project_topk_nvfp4(const uint16_t* h, int64_t M, int64_t K,
+                             const uint8_t* Wq, const uint8_t* scales,
+                             const float* gscale, int64_t R,
+                             const int32_t* d2t, int64_t topk,
+                             int32_t* out_id, float* out_logit,
+                             void* workspace, size_t workspace_bytes,
+                             int path, void* stream);
+
+/*
  * draft_project_argmax_indexed -- the shortlisted argmax read straight from
  * the full head: for each hidden row m, over the list entries i with
  * ids[i] in [0, N),
@@ -354,7 +482,7 @@ int draft_project_topk_mxfp4(const uint16_t* h, int64_t M, int64_t K,
  *  h          [M, K] bf16 (device, 16-byte aligned), 1 <= M <= LMH_MAX_M.
  *  W          [N, K] bf16 (device, 16-byte aligned), the full head;
  *             1 <= N <= 2^31 - 1.
- *  ids        [S] int32 (device, 4-byte aligned), 1 <= S <= 2^30, any
+ *  ids        [S] int32 (device, 4-byte aligned), 1 <= S <= LMH_MAX_R, any
  *             order, duplicates allowed.  An entry outside [0, N) is
  *             skipped (never read); if every entry is skipped, out_id = -1
  *             and out_logit is NaN.
@@ -375,8 +503,9 @@ int draft_project_argmax_indexed(const uint16_t* h, int64_t M, int64_t K,
  * lmhead_shortlist_overwrite -- refresh rows of a trimmed head in place:
  * for each entry i, W_trim[rows[i], :] = W[ids[i], :] and d2t[rows[i]] =
  * ids[i].  This is how escaped ids are learned into spare head rows, the
- * pages' fix for a static trim that misses tokens (krisbailey.com/articles/
- * shortlist-mtp, the update in "Re-running the comparison fairly"): keep
+ * pages' fix for a static trim that misses tokens (zone-1.cobraproject.com
+ * "Masked MTP drafts", section "Update (November 2026)", the Gemma 4 31B
+ * case): keep
  * W_trim and d2t with room for `cap` rows, project over the first R, write
  * newly seen ids into rows R, R + 1, ... and project over the grown prefix.
  *
@@ -429,82 +558,6 @@ const char* lmhead_status_str(int status);
 
 /* Text of the last HIP error seen by this thread (empty if none). */
 const char* lmhead_last_error(void);
-
-/*
- * Measurement support (not part of the projection): plain streaming kernels
- * used to find the practical HBM ceiling and to scale hardware counters.
- *
- * lmhead_bench_stream_read: reads `bytes` (a nonzero multiple of 16,
- *   16-byte aligned `src`) with 16-byte non-temporal loads, two groups of
- *   four in flight per lane, and writes one 32-bit checksum word per
- *   workgroup into `sink` (at least lmhead_bench_sink_words() words).
- *   grid 0 = one 256-thread workgroup per CU, the fastest shape measured.
- * lmhead_bench_copy: dst[0:bytes] = src[0:bytes] (16-byte multiples/aligned).
- * `grid` = workgroups to launch (0 = the library's default).
- */
-int lmhead_bench_sink_words(void);
-int lmhead_bench_stream_read(const void* src, size_t bytes, uint32_t* sink,
-                             int grid, void* stream);
-int lmhead_bench_copy(const void* src, void* dst, size_t bytes, int grid,
-                      void* stream);
-
-/*
- * lmhead_bench_time_argmax: mean duration of the projection kernel of
- *   draft_project_argmax_path.  Between two HIP events on `stream` the
- *   library launches that kernel `calls` times back to back, launch i over
- *   heads[i % nheads] (a host array of device pointers, each [R, K]), with
- *   no fold in between; *proj_ms = elapsed milliseconds / calls.  Then one
- *   whole call over heads[0] writes out_id / out_logit.  Only shapes that
- *   take a single projection launch are accepted (LMH_EINVAL otherwise).
- *   Synchronizes; for measurement, not for the decode loop.  Other
- *   arguments as for draft_project_argmax_path.
- */
-int lmhead_bench_time_argmax(const uint16_t* h, int64_t M, int64_t K,
-                             const uint16_t* const* heads, int nheads,
-                             int64_t R, const int32_t* d2t,
-                             int32_t* out_id, float* out_logit,
-                             void* workspace, size_t workspace_bytes,
-                             int path, int calls, double* proj_ms,
-                             void* stream);
-
-/*
- * lmhead_bench_time_argmax_fp8: the same over FP8 heads (draft_project_
- *   argmax_fp8): launch i uses heads[i % nheads] with scales[i % nheads].
- */
-int lmhead_bench_time_argmax_fp8(const uint16_t* h, int64_t M, int64_t K,
-                                 const uint8_t* const* heads,
-                                 const float* const* scales, int nheads,
-                                 int64_t R, const int32_t* d2t,
-                                 int32_t* out_id, float* out_logit,
-                                 void* workspace, size_t workspace_bytes,
-                                 int path, int calls, double* proj_ms,
-                                 void* stream);
-
-/*
- * lmhead_bench_time_argmax_mxfp4: the same over MXFP4 heads (draft_project_
- *   argmax_mxfp4): launch i uses heads[i % nheads] with scales[i % nheads].
- */
-int lmhead_bench_time_argmax_mxfp4(const uint16_t* h, int64_t M, int64_t K,
-                                   const uint8_t* const* heads,
-                                   const uint8_t* const* scales, int nheads,
-                                   int64_t R, const int32_t* d2t,
-                                   int32_t* out_id, float* out_logit,
-                                   void* workspace, size_t workspace_bytes,
-                                   int path, int calls, double* proj_ms,
-                                   void* stream);
-
-/*
- * lmhead_bench_time_argmax_indexed: the same for draft_project_argmax_
- *   indexed: launch i reads full head heads[i % nheads] ([N, K] each)
- *   through the one id list `ids`.
- */
-int lmhead_bench_time_argmax_indexed(const uint16_t* h, int64_t M, int64_t K,
-                                     const uint16_t* const* heads, int nheads,
-                                     int64_t N, const int32_t* ids, int64_t S,
-                                     int32_t* out_id, float* out_logit,
-                                     void* workspace, size_t workspace_bytes,
-                                     int path, int calls, double* proj_ms,
-                                     void* stream);
 
 #ifdef __cplusplus
 }

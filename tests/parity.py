@@ -19,6 +19,8 @@ Two bars are applied to every hidden row:
    rounding multiplies by the row's scale: (K + 2) * 2**-24 * sum_k
    |h_k w_k| with w the dequantized values.  Over an MXFP4 head every
    dequantized value is a bf16 number and the bf16 bound applies unchanged.
+   Over an NVFP4 head every code times its block scale is a bf16 number and
+   the head's scale multiplies each row's sum once: K + 2, as for FP8.
 """
 from __future__ import annotations
 
@@ -100,6 +102,19 @@ def check_mxfp4(h_bits, codes, scales, d2t, gpu_id, gpu_logit, res=None) -> Pari
         res = oracle.oracle_project_argmax_mxfp4(h_bits, codes, scales, d2t, keep_logits=True)
     return _check_core(h_bits, lambda rows: oracle.oracle_dequant_mxfp4(codes[rows], scales[rows]),
                        codes.shape[0], d2t, gpu_id, gpu_logit, res, extra=1)
+
+
+def check_nvfp4(h_bits, codes, scales, g, d2t, gpu_id, gpu_logit, res=None) -> ParityStats:
+    """The same rule over an NVFP4 head (codes [R, K / 2], block scales
+    [R, K / 16], tensor scale g).  Each E2M1 value times its E4M3 block scale
+    is a bf16 number, so the GPU's products are exact; it sums them in fp32
+    and multiplies each row's sum by g once: K + 2 roundings against the
+    dequantized values, as over an FP8 head."""
+    codes, scales = np.asarray(codes), np.asarray(scales)
+    if res is None or res.logits is None:
+        res = oracle.oracle_project_argmax_nvfp4(h_bits, codes, scales, g, d2t, keep_logits=True)
+    return _check_core(h_bits, lambda rows: oracle.oracle_dequant_nvfp4(codes[rows], scales[rows], g),
+                       codes.shape[0], d2t, gpu_id, gpu_logit, res, extra=2)
 
 
 def _check_core(h_bits, w_rows, r, d2t, gpu_id, gpu_logit, res, extra) -> ParityStats:
@@ -192,6 +207,16 @@ def check_topk_mxfp4(h_bits, codes, scales, d2t, gpu_ids, gpu_logits, res=None) 
         res = oracle.oracle_project_topk_mxfp4(h_bits, codes, scales, d2t, np.asarray(gpu_ids).shape[1])
     return _check_topk_core(h_bits, lambda rr: oracle.oracle_dequant_mxfp4(codes[rr], scales[rr]),
                             codes.shape[0], d2t, gpu_ids, gpu_logits, res, extra=1)
+
+
+def check_topk_nvfp4(h_bits, codes, scales, g, d2t, gpu_ids, gpu_logits, res=None) -> ParityStats:
+    """The top-k rule over an NVFP4 head (bound with K + 2 roundings, as in
+    check_nvfp4)."""
+    codes, scales = np.asarray(codes), np.asarray(scales)
+    if res is None:
+        res = oracle.oracle_project_topk_nvfp4(h_bits, codes, scales, g, d2t, np.asarray(gpu_ids).shape[1])
+    return _check_topk_core(h_bits, lambda rr: oracle.oracle_dequant_nvfp4(codes[rr], scales[rr], g),
+                            codes.shape[0], d2t, gpu_ids, gpu_logits, res, extra=2)
 
 
 def _check_topk_core(h_bits, w_rows, r, d2t, gpu_ids, gpu_logits, res, extra) -> ParityStats:

@@ -1,4 +1,4 @@
-"""The C-ABI library loads, exports every symbol include/lmhead.h declares,
+"""The C-ABI library loads, exports every symbol include/*.h declares,
 and rejects bad arguments on the host before touching the GPU (CPU only:
 every call here returns before the first HIP runtime call)."""
 import os
@@ -9,6 +9,8 @@ import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "lmhead.h")
+HEADERS = sorted(os.path.join(ROOT, "include", f) for f in os.listdir(os.path.join(ROOT, "include"))
+                 if f.endswith(".h"))
 
 
 @pytest.fixture(scope="module")
@@ -16,22 +18,31 @@ def L():
     from vocab_shortlisted_lm_amd import lmhead, build
     src = build.SRC
     if (not os.path.exists(lmhead.LIB_PATH)
-            or os.path.getmtime(lmhead.LIB_PATH) < max(os.path.getmtime(src), os.path.getmtime(HEADER))):
+            or os.path.getmtime(lmhead.LIB_PATH) < max(os.path.getmtime(f) for f in [src] + HEADERS)):
         build.build()
     return lmhead
 
 
-def declared_functions():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"^\s*(?:const\s+)?[\w]+\s*\*?\s*(\w+)\s*\(", text, flags=re.M)))
+def declared_functions(headers=None):
+    names = set()
+    for path in headers or HEADERS:
+        text = open(path).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        names |= set(re.findall(r"^\s*(?:const\s+)?[\w]+\s*\*?\s*(\w+)\s*\(", text, flags=re.M))
+    return sorted(names)
 
 
 def test_header_declares_the_boundary():
-    names = declared_functions()
+    names = declared_functions([HEADER])
     for n in ("lmhead_trim", "draft_project_argmax", "draft_project_workspace_bytes",
               "lmhead_status_str"):
         assert n in names
+    # measurement and forced-kernel calls live in lmhead_bench.h, not in the
+    # product header
+    assert not [n for n in names if n.startswith("lmhead_bench_")]
+    assert "draft_project_argmax_path" not in names
+    bench = declared_functions([os.path.join(ROOT, "include", "lmhead_bench.h")])
+    assert "draft_project_argmax_path" in bench and "lmhead_bench_time_argmax" in bench
 
 
 def test_every_declared_symbol_is_exported(L):
@@ -106,7 +117,7 @@ def call(L, h=A, m=1, k=2560, w=B, r=100, d2t=None, oid=C, olog=D, ws=E, wsb=1 <
 @pytest.mark.parametrize("kw,code", [
     (dict(h=None), 1), (dict(w=None), 1), (dict(oid=None), 1), (dict(olog=None), 1),
     (dict(m=0), 1), (dict(m=33), 1), (dict(k=0), 1), (dict(k=12), 1), (dict(k=8200), 1),
-    (dict(r=0), 1), (dict(r=(1 << 30) + 1), 1), (dict(h=A + 2), 1), (dict(w=B + 8), 1),
+    (dict(r=0), 1), (dict(r=1 << 30), 1), (dict(r=(1 << 30) + 1), 1), (dict(h=A + 2), 1), (dict(w=B + 8), 1),
     (dict(path=7), 1), (dict(m=9, path=1), 1), (dict(m=4, k=8192, path=1), 1), (dict(m=8, k=4096, path=1), 1),
     (dict(ws=None), 3), (dict(ws=E + 4), 3), (dict(wsb=16), 3), (dict(wsb=0), 3),
     (dict(m=2, wsb=8 * 1024 * 2 - 8), 3),
@@ -192,6 +203,7 @@ def test_indexed_rejects_on_host(L):
     assert f(A, 3, 2560, B, 1000, C + 2, 100, D, E, E, ws, 0, None) == 1  # ids misaligned
     assert f(A, 3, 2560, B, 1000, C, 0, D, E, E, ws, 0, None) == 1     # S = 0
     assert f(A, 3, 2560, B, 1000, C, (1 << 30) + 1, D, E, E, ws, 0, None) == 1
+    assert f(A, 3, 2560, B, 1000, C, 1 << 30, D, E, E, ws, 0, None) == 1  # 4 * S must stay below 2^32
     assert f(A, 33, 2560, B, 1000, C, 100, D, E, E, ws, 0, None) == 1  # M
     assert f(A, 3, 2560, B + 8, 1000, C, 100, D, E, E, ws, 0, None) == 1  # W misaligned
     assert f(A, 9, 2560, B, 1000, C, 100, D, E, E, ws, 1, None) == 1   # VALU takes M <= 8
@@ -259,6 +271,39 @@ def test_mxfp4_rejects_on_host(L):
     assert f(A, 33, 2560, B, C, 100, None, D, E, E, ws, 0, None) == 1
     assert f(A, 1, 2560, B, C, 0, None, D, E, E, ws, 0, None) == 1     # R = 0
     assert f(A, 4, 2560, B, C, 100, None, D, E, E, 8, 0, None) == 3    # workspace
+
+
+def test_nvfp4_rejects_on_host(L):
+    lib = L.lib()
+    q = lib.lmhead_quantize_nvfp4
+    assert q(A, 0, 2560, B, C, D, None) == 0                      # R = 0: no-op
+    assert q(A, 10, 2568, B, C, D, None) == 1                     # K not a multiple of 16
+    assert q(A, 10, 2560, B + 8, C, D, None) == 1                 # Wq misaligned
+    assert q(A, 10, 2560, B, C, D + 2, None) == 1                 # gscale misaligned
+    assert q(A, 10, 2560, B, C, None, None) == 1
+    assert q(None, 10, 2560, B, C, D, None) == 1
+    assert q(A, 1 << 30, 2560, B, C, D, None) == 1
+    f = lib.draft_project_argmax_nvfp4
+    ws = L.draft_project_workspace_bytes(4)
+    assert f(A, 4, 2592, B, C, D, 100, None, E, E, E, ws, 0, None) == 1   # K % 512
+    assert f(A, 4, 2560, B, C, D, 100, None, E, E, E, ws, 1, None) == 1   # no VALU path
+    assert f(A, 4, 2560, B, C + 4, D, 100, None, E, E, E, ws, 0, None) == 1  # scales misaligned
+    assert f(A, 4, 2560, B, C, None, 100, None, E, E, E, ws, 0, None) == 1   # no head scale
+    assert f(A, 4, 2560, B, C, D + 1, 100, None, E, E, E, ws, 0, None) == 1  # head scale misaligned
+    assert f(A, 33, 2560, B, C, D, 100, None, E, E, E, ws, 0, None) == 1
+    assert f(A, 1, 2560, B, C, D, 0, None, E, E, E, ws, 0, None) == 1     # R = 0
+    assert f(A, 4, 2560, B, C, D, 100, None, E, E, E, 8, 0, None) == 3    # workspace
+    t = lib.draft_project_topk_nvfp4
+    assert t(A, 2, 2560, B, C, D, 100, None, 0, E, E, E, 1 << 24, 0, None) == 1   # topk 0
+    assert t(A, 2, 2560, B, C, D, 100, None, 4, E, E, E, 1 << 24, 1, None) == 1   # no VALU path
+    assert L.lmhead_nvfp4_scale_bytes(17, 2560) == 2 * 5 * 512
+    assert L.lmhead_nvfp4_scale_bytes(16, 16) == 512
+    assert L.lmhead_nvfp4_scale_bytes(16, 24) == -1
+    assert L.nvfp4_scale_shape(17, 2560) == (2, 5, 16, 32)
+    tl = lib.lmhead_nvfp4_tile_scales
+    assert tl(A, 0, 2560, B, None) == 0
+    assert tl(A, 10, 2568, B, None) == 1
+    assert tl(None, 10, 2560, B, None) == 1
 
 
 def test_shortlist_ops_reject_on_host(L):
@@ -347,25 +392,26 @@ def test_build_has_no_scratch_spills():
         assert proc.returncode == 0, proc.stderr[-2000:]
         usage = build.kernel_resources(proc.stderr)
     for kernel in ("proj_valu_tiled", "proj_valu_rows", "proj_mfma", "finalize_topk", "proj_valu_fp8",
-                   "quantize_rows_fp8", "quantize_rows_mxfp4", "tile_mxfp4_scales"):
+                   "quantize_rows_fp8", "quantize_rows_mxfp4", "quantize_rows_nvfp4", "tile_block_scales"):
         assert any(kernel in k for k in usage), kernel
     spills = {k: v["ScratchSize"] for k, v in usage.items() if v.get("ScratchSize", 0)}
     assert not spills, spills
-    # The one-tile matrix-core argmax kernels over FP8 and MXFP4 heads run two
-    # 8-wave workgroups per CU at a few hidden rows (their LDS allows it), so
-    # they must fit 4 waves per SIMD in registers; a larger register peak
-    # silently halves their residency (no parity test can see it)
-    for fmt in (1, 2):
-        name = [k for k in usage if "proj_mfma" in k and f"ILi1ELi{8 * fmt}ELi8ELi3ELi1ELb0ELi{fmt}ELb0E" in k]
+    # The one-tile matrix-core argmax kernels over FP8, MXFP4 and NVFP4 heads
+    # run two 8-wave workgroups per CU at a few hidden rows (their LDS allows
+    # it), so they must fit 4 waves per SIMD in registers; a larger register
+    # peak silently halves their residency (no parity test can see it)
+    for fmt, sb in ((1, 8), (2, 16), (3, 16)):
+        name = [k for k in usage if "proj_mfma" in k and f"ILi1ELi{sb}ELi8ELi3ELi1ELb0ELi{fmt}ELb0E" in k]
         assert len(name) == 1, (fmt, name)
         assert usage[name[0]].get("Occupancy", 0) >= 4, (name[0], usage[name[0]])
 
 
 def test_header_is_plain_c(tmp_path):
-    """include/lmhead.h compiles as strict C99 on its own: the boundary has no
-    C++ or torch types."""
+    """include/lmhead.h and lmhead_bench.h compile as strict C99 on their own:
+    the boundary has no C++ or torch types."""
     src = tmp_path / "uses_header.c"
-    src.write_text('#include "lmhead.h"\nint main(void) { return (int)draft_project_workspace_bytes(1) == 0; }\n')
+    src.write_text('#include "lmhead.h"\n#include "lmhead_bench.h"\n'
+                   'int main(void) { return (int)draft_project_workspace_bytes(1) == 0; }\n')
     proc = subprocess.run(["gcc", "-std=c99", "-pedantic", "-Wall", "-Wextra", "-Werror", "-fsyntax-only",
                            "-I", os.path.join(ROOT, "include"), str(src)], capture_output=True, text=True)
     assert proc.returncode == 0, proc.stderr
@@ -380,3 +426,27 @@ def test_c_consumer_builds_against_the_header_alone(tmp_path):
     ldd = subprocess.run(["ldd", out], capture_output=True, text=True, check=True).stdout
     line = [l for l in ldd.splitlines() if "liblmhead.so" in l]
     assert line and "not found" not in line[0], ldd
+
+
+def test_row_bound_is_below_two_to_the_thirty(L):
+    """Heads and lists are capped at 2^30 - 1 rows on the host, before any
+    launch: the id list of an indexed call is read through a buffer
+    descriptor whose 32-bit byte count, 4 bytes per entry, would wrap to 0 at
+    2^30 entries and make every id read as 0 (a valid row, so a silently
+    wrong answer).  Every entry point that takes a row count rejects 2^30."""
+    lib = L.lib()
+    big = 1 << 30
+    assert L.LMH_MAX_R == big - 1
+    ws = L.draft_project_workspace_bytes(3)
+    assert lib.draft_project_argmax(A, 3, 2560, B, big, None, C, D, E, ws, None) == 1
+    assert lib.draft_project_argmax_indexed(A, 3, 2560, B, 1000, C, big, D, E, E, ws, 0, None) == 1
+    assert lib.draft_project_topk(A, 2, 2560, B, big, None, 4, C, D, E, 1 << 24, 0, None) == 1
+    assert lib.draft_project_logits(A, 1, 2560, B, big, None, 0, D, 0, None) == 1
+    assert lib.draft_project_argmax_fp8(A, 1, 2560, B, E, big, None, C, D, E, ws, 0, None) == 1
+    assert lib.draft_project_argmax_mxfp4(A, 1, 2560, B, E, big, None, C, D, E, ws, 0, None) == 1
+    assert lib.lmhead_quantize_fp8(A, big, 2560, B, E, None) == 1
+    assert lib.lmhead_quantize_mxfp4(A, big, 2560, B, E, None) == 1
+    assert lib.lmhead_mxfp4_scale_bytes(big, 2560) == -1
+    assert lib.lmhead_mxfp4_scale_bytes(big - 1, 2560) == (big // 16) * 5 * 256
+    assert lib.draft_project_auto_path_rows(1, 2560, big) == -1
+    assert lib.draft_project_auto_path_rows(1, 2560, big - 1) in (1, 2)

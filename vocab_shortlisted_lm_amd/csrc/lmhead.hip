@@ -31,7 +31,8 @@
 //   finalize_topk           the same for the top-k lists.
 //   fill_neg_inf            the -inf fill before logits are scattered to
 //                           vocabulary ids.
-//   quantize_rows_fp8, quantize_rows_mxfp4, tile_mxfp4_scales
+//   quantize_rows_fp8, quantize_rows_mxfp4, quantize_rows_nvfp4 (with
+//   nvfp4_slot_zero, nvfp4_head_amax, nvfp4_set_scale), tile_block_scales
 //                           load-time copies of a head in FP8 or MXFP4.
 //   overwrite_rows, union_ids
 //                           shortlist maintenance (escaped ids into spare
@@ -61,6 +62,7 @@
 #include <vector>
 
 #include "lmhead.h"
+#include "lmhead_bench.h"
 
 namespace {
 
@@ -100,6 +102,9 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 #ifndef LMH_RING_MAX_ROWS
 #define LMH_RING_MAX_ROWS 131072  // VALU argmax over fewer head rows than this uses the ring loop
 #endif
+#ifndef LMH_M4_MFMA_MAX_ROWS
+#define LMH_M4_MFMA_MAX_ROWS 131072  // an argmax over 4 hidden rows and fewer head rows takes the matrix cores
+#endif
 #ifndef LMH_VALU_WAVES
 #define LMH_VALU_WAVES 4          // waves per workgroup (VALU path)
 #endif
@@ -121,6 +126,7 @@ constexpr int kValuMaxM = 8;
 constexpr int kFmtBf16 = 0;  // bf16 head
 constexpr int kFmtFp8 = 1;   // E4M3 codes, one fp32 scale per row
 constexpr int kFmtMx4 = 2;   // MXFP4: E2M1 codes, one E8M0 scale per 32 elements
+constexpr int kFmtNv4 = 3;   // NVFP4: E2M1 codes, one E4M3 scale per 16 elements, one fp32 scale per head
 constexpr int kLoopPair = 0;
 constexpr int kLoopUncond = 1;
 constexpr int kLoopRing = 2;
@@ -136,7 +142,13 @@ constexpr int kLdsPerWorkgroup = 160 * 1024;
 // Largest top-k a matrix-core lane keeps in its own registers; larger k
 // keep each column's best 16 over its four lanes.
 constexpr int kLaneListMaxTk = 4;
-constexpr int64_t kMaxRows = (int64_t)1 << 30;  // keeps row arithmetic in int range
+// Largest head (or list) a call takes: row arithmetic stays in int range,
+// and every buffer descriptor's byte count fits its 32-bit field -- the
+// largest is the id list of an indexed call, 4 bytes per entry, so
+// (2^30 - 1) * 4 < 2^32 (at 2^30 entries the count would wrap to 0 and every
+// id would read as 0).  The other descriptors span at most a 16-row tile of a
+// head row, the hidden block, or one tile's scales.
+constexpr int64_t kMaxRows = ((int64_t)1 << 30) - 1;
 constexpr uint32_t kBufferWord3 = 0x00020000u;  // gfx9 raw buffer, 32-bit data
 constexpr uint32_t kOobOffset = 0x80000000u;    // any offset >= num_records reads 0
 // cache-policy operand of buffer loads: bit 1 = nt (streaming).  Every
@@ -147,6 +159,8 @@ constexpr int kPolicyStream = LMH_NT_LOADS ? 2 : 0;
 // ---------------------------------------------------------------------------
 // device helpers
 // ---------------------------------------------------------------------------
+// Raw buffer descriptor over `bytes` bytes from `base`; offsets at or past
+// `bytes` read 0.  Callers keep `bytes` below 2^32 (see kMaxRows).
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
                                            (int)kBufferWord3);
@@ -189,18 +203,56 @@ __device__ __forceinline__ u32x4 fp8x8_to_bf16x8(uint32_t lo, uint32_t hi) {
 }
 
 // Eight E2M1 codes (the nibbles of `packed`, element 2i in the low nibble of
-// byte i) as eight bf16 values times the block scale 2^(e - 127), e the
-// block's E8M0 code.  The gfx950 conversion multiplies by an fp32 scale;
-// every E2M1 value times a power of two in bf16 range is a bf16 number, so
-// the result is exact.  Code 0 is 2^-127 (an fp32 subnormal).
-__device__ __forceinline__ u32x4 fp4x8_to_bf16x8(uint32_t packed, uint32_t e) {
-  const float sc = __builtin_bit_cast(float, e != 0u ? e << 23 : 0x00400000u);
+// byte i) as eight bf16 values times the power-of-two scale `sc`, by the
+// gfx950 conversion: exact, since an E2M1 value times a power of two in bf16
+// range is a bf16 number.  Only for power-of-two scales: on MI355X an E4M3
+// scale with mantissa bits passed as this operand gave NVFP4 logits up to
+// 18% off the exact ones, as if only its exponent were applied.
+__device__ __forceinline__ u32x4 fp4x8_to_bf16x8_scaled(uint32_t packed, float sc) {
   const bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(packed, sc, 0);
   const bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(packed, sc, 1);
   const bf16x2 c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(packed, sc, 2);
   const bf16x2 d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(packed, sc, 3);
   return u32x4{__builtin_bit_cast(uint32_t, a), __builtin_bit_cast(uint32_t, b), __builtin_bit_cast(uint32_t, c),
                __builtin_bit_cast(uint32_t, d)};
+}
+
+// Eight E2M1 codes times an NVFP4 block scale `sc` (a decoded E4M3 value,
+// not a power of two) as eight bf16 values, exactly.  The codes convert at
+// scale 1 to fp32; each product with the scale has at most 6 significant
+// bits (2 of E2M1 times 4 of E4M3), so the fp32 multiply is exact and the
+// product's high 16 bits are its bf16 value (the low 16 are zero), which
+// v_perm_b32 packs two at a time.
+template <int SEL>
+__device__ __forceinline__ uint32_t fp4x2_times_scale_to_bf16x2(uint32_t packed, float sc) {
+  const auto v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(packed, 1.0f, SEL);
+  const uint32_t lo = __builtin_bit_cast(uint32_t, v[0] * sc);
+  const uint32_t hi = __builtin_bit_cast(uint32_t, v[1] * sc);
+  return __builtin_amdgcn_perm(hi, lo, 0x07060302u);  // bytes 2, 3 of lo, then 2, 3 of hi
+}
+__device__ __forceinline__ u32x4 fp4x8_times_scale_to_bf16x8(uint32_t packed, float sc) {
+  return u32x4{fp4x2_times_scale_to_bf16x2<0>(packed, sc), fp4x2_times_scale_to_bf16x2<1>(packed, sc),
+               fp4x2_times_scale_to_bf16x2<2>(packed, sc), fp4x2_times_scale_to_bf16x2<3>(packed, sc)};
+}
+
+// The same with the MXFP4 block scale 2^(e - 127), e the block's E8M0
+// code (code 0 is 2^-127, an fp32 subnormal).
+__device__ __forceinline__ u32x4 fp4x8_to_bf16x8(uint32_t packed, uint32_t e) {
+  return fp4x8_to_bf16x8_scaled(packed, __builtin_bit_cast(float, e != 0u ? e << 23 : 0x00400000u));
+}
+
+// Value of an OCP E4M3 code (the low byte of `code`) as fp32, exactly, from
+// the format: sign, 4 exponent bits with bias 7, 3 mantissa bits; exponent 0
+// is subnormal (m x 2^-9).  The NaN code (S.1111.111) is not given a NaN:
+// the NVFP4 quantizer never writes it, and a caller's scale array holding
+// it gives an unspecified (in-bounds) result.
+__device__ __forceinline__ float e4m3_to_f32(uint32_t code) {
+  const uint32_t e = (code >> 3) & 0xFu;
+  const uint32_t m = code & 0x7u;
+  const uint32_t sign = (code & 0x80u) << 24;
+  const float sub = (float)m * 0x1p-9f;  // exact
+  const uint32_t normal = sign | ((e + 120u) << 23) | (m << 20);
+  return e == 0u ? __builtin_bit_cast(float, sign | __builtin_bit_cast(uint32_t, sub)) : __builtin_bit_cast(float, normal);
 }
 
 // E2M1 code (OCP MX FP4: bias 1, 1 mantissa bit, subnormal 0.5) of an
@@ -595,6 +647,10 @@ __device__ __forceinline__ void publish_workgroup(unsigned long long key, int la
 // head row r of the projection is row rowmap[r] of W, which has nw rows; a
 // row whose id lies outside [0, nw) is never read and takes no part in the
 // result.
+//
+// Single launch (argmax only): with `ticket` set, the workgroup that takes
+// the last ticket folds every workgroup's slot, maps the winner through
+// fold_d2t and writes out_id / out_logit, so no fold kernel follows.
 struct Epi {
   unsigned long long* slots;
   float* logits;
@@ -603,7 +659,56 @@ struct Epi {
   int64_t ncols;
   const int32_t* rowmap = nullptr;
   int nw = 0;
+  unsigned int* ticket = nullptr;
+  const int32_t* fold_d2t = nullptr;
+  int32_t* out_id = nullptr;
+  float* out_logit = nullptr;
 };
+
+// The single-launch hand-off, run by wave 0 of every workgroup after it has
+// stored its keys (lanes m < mcount, hidden rows m_base + m) into its slots.
+// Lane 0 takes a ticket with release ordering at agent scope: the compiler
+// writes the wave's stores back from this chiplet's L2 and waits for them
+// before the atomic, so a workgroup on any other chiplet that takes a later
+// ticket and then acquires sees them.  The workgroup with the last ticket
+// acquires (invalidating its L2's stale lines), folds the slots of every
+// hidden row -- lane m keeps row m's winner -- then lanes m < mcount decode,
+// map through d2t and store, and the ticket goes back to 0 for the next
+// launch on this workspace.
+__device__ __forceinline__ void fold_if_last(const Epi& e, int lane, int mcount, int m_base) {
+  unsigned int t = 0u;
+  if (lane == 0) t = __hip_atomic_fetch_add(e.ticket, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+  t = (unsigned int)__builtin_amdgcn_readfirstlane((int)t);
+  if (t != gridDim.x - 1u) return;
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  unsigned long long mine = 0ull;
+  for (int m = 0; m < mcount; ++m) {
+    const unsigned long long* row = e.slots + (size_t)(m_base + m) * kMaxGrid;
+    unsigned long long k = 0ull;
+    for (int i = lane; i < (int)gridDim.x; i += 64) k = max_u64(k, row[i]);
+#pragma unroll
+    for (int x = 32; x >= 1; x >>= 1) {
+      const uint32_t lo = (uint32_t)__shfl_xor((int)(uint32_t)k, x);
+      const uint32_t hi = (uint32_t)__shfl_xor((int)(uint32_t)(k >> 32), x);
+      k = max_u64(k, ((unsigned long long)hi << 32) | lo);
+    }
+    mine = lane == m ? k : mine;
+  }
+  if (lane < mcount) {
+    const int m = m_base + lane;
+    if (mine == 0ull) {
+      e.out_id[m] = -1;
+      e.out_logit[m] = __builtin_nanf("");
+    } else {
+      float v;
+      int idx;
+      unpack_key(mine, v, idx);
+      e.out_id[m] = e.fold_d2t ? e.fold_d2t[idx] : idx;
+      e.out_logit[m] = v;
+    }
+  }
+  if (lane == 0) __hip_atomic_store(e.ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 
 // Id of list entry r for an indexed kernel, as a plain (unconditional)
 // buffer load; entries past the list (r >= R) read 0, so the caller checks
@@ -681,6 +786,38 @@ finalize_argmax(const unsigned long long* __restrict__ slots, int nslots, int m_
   unpack_key(k, v, idx);
   out_id[m] = d2t ? d2t[idx] : idx;
   out_logit[m] = v;
+}
+
+// Key output for a slice of a head: the same fold, then the winner's key
+// re-packed with its global row row_base + idx (no d2t), so that the maximum
+// over the keys of all slices of a head is the whole head's winner with the
+// smallest-row tie-break.  An empty key (no ordered logit) stays 0.
+__global__ void __launch_bounds__(256)
+finalize_keys(const unsigned long long* __restrict__ slots, int nslots, int m_base, int64_t row_base,
+              unsigned long long* __restrict__ out_key) {
+  __shared__ unsigned long long s_wave[4];
+  const int m = m_base + blockIdx.x;
+  const unsigned long long* row = slots + (size_t)m * kMaxGrid;
+  unsigned long long k = 0ull;
+  for (int i = threadIdx.x; i < nslots; i += 256) k = row[i] > k ? row[i] : k;
+#pragma unroll
+  for (int x = 32; x >= 1; x >>= 1) {
+    const uint32_t lo = (uint32_t)__shfl_xor((int)(uint32_t)k, x);
+    const uint32_t hi = (uint32_t)__shfl_xor((int)(uint32_t)(k >> 32), x);
+    const unsigned long long o = ((unsigned long long)hi << 32) | lo;
+    k = o > k ? o : k;
+  }
+  if ((threadIdx.x & 63) == 0) s_wave[threadIdx.x >> 6] = k;
+  __syncthreads();
+  if (threadIdx.x != 0) return;
+  k = s_wave[0];
+#pragma unroll
+  for (int w = 1; w < 4; ++w) k = s_wave[w] > k ? s_wave[w] : k;
+  if (k != 0ull) {
+    const uint32_t idx = 0xFFFFFFFFu - (uint32_t)k;
+    k = (k & 0xFFFFFFFF00000000ull) | (unsigned long long)(0xFFFFFFFFu - (uint32_t)(row_base + idx));
+  }
+  out_key[m] = k;
 }
 
 // Top-TK version: one workgroup per hidden row merges the sorted TK-key
@@ -763,8 +900,9 @@ gather_rows(const uint16_t* __restrict__ W, int64_t N, int K, const int32_t* __r
 // an entry with a row outside [0, cap) or an id outside [0, N) is skipped,
 // and an entry is dropped when a later valid entry names the same row (the
 // last one wins), so every row has exactly one writer.  Escaped ids learned
-// into spare rows are the pages' fix for a static trim that misses
-// (Shortlist-MTP, the update in "Re-running the comparison fairly").
+// into spare head rows are the pages' fix for a static trim that misses
+// (zone-1.cobraproject.com "Masked MTP drafts", section "Update (November
+// 2026)", the Gemma 4 31B case).
 __global__ void __launch_bounds__(256)
 overwrite_rows(const uint16_t* __restrict__ W, int64_t N, int K, uint16_t* __restrict__ W_trim, int32_t* d2t,
                int64_t cap, const int32_t* __restrict__ rows, const int32_t* __restrict__ ids, int n) {
@@ -914,20 +1052,28 @@ quantize_rows_fp8(const uint16_t* __restrict__ W, int R, int K, uint8_t* __restr
 // 16 bytes, the pieces of a tile in group order and the tiles in row order.
 // With nb = ceil(blocks / 16) groups per row the array holds ceil(R / 16) x
 // nb x 256 bytes; a tile's part starts at r0 x blocks when blocks % 16 == 0.
-__device__ __forceinline__ size_t mx_scale_index(int r, int j, int blocks) {
-  const int nb = (blocks + 15) >> 4;
-  return (((size_t)(r >> 4) * nb + (j >> 4)) * 16 + (r & 15)) * 16 + (j & 15);
+// NVFP4 (blocks of 16 elements) uses the same layout with groups of 32
+// blocks, again 512 elements per group: GROUP = blocks per group, each
+// (tile, group) piece 16 rows x GROUP bytes.
+template <int GROUP>
+__device__ __forceinline__ size_t tiled_scale_index(int r, int j, int blocks) {
+  const int nb = (blocks + GROUP - 1) / GROUP;
+  return (((size_t)(r >> 4) * nb + j / GROUP) * 16 + (r & 15)) * GROUP + (j % GROUP);
 }
+__device__ __forceinline__ size_t mx_scale_index(int r, int j, int blocks) { return tiled_scale_index<16>(r, j, blocks); }
+__device__ __forceinline__ size_t nv_scale_index(int r, int j, int blocks) { return tiled_scale_index<32>(r, j, blocks); }
 
-// Row-major E8M0 scales [R, blocks] into the tiled scale layout, one byte per
-// thread (a load-time conversion of scales written elsewhere).
+// Row-major block scales [R, blocks] into the tiled scale layout (GROUP 16:
+// MXFP4, 32: NVFP4), one byte per thread (a load-time conversion of scales
+// written elsewhere).
+template <int GROUP>
 __global__ void __launch_bounds__(256)
-tile_mxfp4_scales(const uint8_t* __restrict__ src, int R, int blocks, uint8_t* __restrict__ dst) {
+tile_block_scales(const uint8_t* __restrict__ src, int R, int blocks, uint8_t* __restrict__ dst) {
   const int64_t n = (int64_t)R * blocks;
   for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) {
     const int r = (int)(i / blocks);
     const int j = (int)(i - (int64_t)r * blocks);
-    dst[mx_scale_index(r, j, blocks)] = src[i];
+    dst[tiled_scale_index<GROUP>(r, j, blocks)] = src[i];
   }
 }
 
@@ -972,6 +1118,88 @@ quantize_rows_mxfp4(const uint16_t* __restrict__ W, int R, int K, uint8_t* __res
       for (int i = 0; i < 32; ++i) packed[i >> 3] |= e2m1_encode(__builtin_ldexpf(x[i], -s)) << (4 * (i & 7));
       reinterpret_cast<u32x4*>(Wq + (size_t)r * (K >> 1))[blk] = u32x4{packed[0], packed[1], packed[2], packed[3]};
       scales[mx_scale_index(r, blk, blocks)] = (uint8_t)(s + 127);
+    }
+  }
+}
+
+// NVFP4 copy of a bf16 head in three kernels on one stream, with the head's
+// scale slot (one fp32, the caller's) as the only state between them:
+//   nvfp4_head_amax      the head's largest magnitude, as the bits of a
+//                        non-negative fp32 (whose unsigned order is the
+//                        value order), atomicMax'ed into the slot after the
+//                        slot is zeroed by nvfp4_slot_zero;
+//   quantize_rows_nvfp4  per row and 16-element block: block scale and
+//                        codes (below), from g = fp32(amax / 2688) (1 for a
+//                        head of zeros), which every thread derives from the
+//                        slot the same way;
+//   nvfp4_set_scale      replaces the slot's amax by g.
+constexpr float kNvTensorDivisor = 2688.0f;  // largest E4M3 value 448 x largest E2M1 value 6
+
+__global__ void __launch_bounds__(64) nvfp4_slot_zero(float* __restrict__ slot) {
+  if (threadIdx.x == 0) *slot = 0.0f;
+}
+
+__global__ void __launch_bounds__(256)
+nvfp4_head_amax(const uint16_t* __restrict__ W, int64_t n16, float* __restrict__ slot) {
+  uint32_t m = 0u;
+  const u32x4* src = reinterpret_cast<const u32x4*>(W);
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n16; i += (int64_t)gridDim.x * 256) {
+    const u32x4 v = src[i];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) m = max(m, max(v[e] & 0x7FFFu, (v[e] >> 16) & 0x7FFFu));  // |bf16| bits
+  }
+#pragma unroll
+  for (int x = 32; x >= 1; x >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, x));
+  if ((threadIdx.x & 63) == 0) atomicMax(reinterpret_cast<unsigned int*>(slot), m << 16);  // as fp32 bits
+}
+
+__device__ __forceinline__ float nvfp4_tensor_scale(float amax) {
+  return amax > 0.0f ? __fdiv_rn(amax, kNvTensorDivisor) : 1.0f;
+}
+
+__global__ void __launch_bounds__(64) nvfp4_set_scale(float* __restrict__ slot) {
+  if (threadIdx.x == 0) *slot = nvfp4_tensor_scale(*slot);
+}
+
+// One wave per row, one 16-element block per lane at a time: block scale
+// code = E4M3 nearest to fp32(fp32(amax_b / 6) / g) (e4m3_encode: ties to
+// the even code, saturating at 448), then each element's E2M1 code nearest
+// to fp32(x / fp32(decode(code) x g)), a signed zero where that product is
+// 0.  Every division is correctly rounded (__fdiv_rn).  The block's 8 code
+// bytes are one 8-byte store, its scale one byte at nv_scale_index.
+__global__ void __launch_bounds__(256)
+quantize_rows_nvfp4(const uint16_t* __restrict__ W, int R, int K, uint8_t* __restrict__ Wq,
+                    uint8_t* __restrict__ scales, const float* __restrict__ slot) {
+  const int lane = threadIdx.x & 63;
+  const int blocks = K >> 4;
+  const int nwaves = gridDim.x * 4;
+  const float g = nvfp4_tensor_scale(*slot);
+  for (int r = blockIdx.x * 4 + wave_id(); r < R; r += nwaves) {
+    const u32x4* row = reinterpret_cast<const u32x4*>(W + (size_t)r * K);
+    for (int blk = lane; blk < blocks; blk += 64) {
+      float x[16];
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const u32x4 v = row[blk * 2 + j];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          x[8 * j + 2 * e] = __builtin_bit_cast(float, v[e] << 16);
+          x[8 * j + 2 * e + 1] = __builtin_bit_cast(float, v[e] & 0xFFFF0000u);
+        }
+      }
+      float amax = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) amax = __builtin_fmaxf(amax, __builtin_fabsf(x[i]));
+      const uint32_t code = e4m3_encode(__fdiv_rn(__fdiv_rn(amax, 6.0f), g));
+      const float denom = e4m3_to_f32(code) * g;
+      uint32_t packed[2] = {0u, 0u};
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const float q = denom > 0.0f ? __fdiv_rn(x[i], denom) : __builtin_copysignf(0.0f, x[i]);
+        packed[i >> 3] |= e2m1_encode(q) << (4 * (i & 7));
+      }
+      reinterpret_cast<uint2*>(Wq + (size_t)r * (K >> 1))[blk] = uint2{packed[0], packed[1]};
+      scales[nv_scale_index(r, blk, blocks)] = (uint8_t)code;
     }
   }
 }
@@ -1027,6 +1255,7 @@ struct ValuEpilogue {
         for (int w = 0; w < WV; ++w) key = s_key[w][lane] > key ? s_key[w][lane] : key;
       }
       publish_workgroup(key, lane, M, 0, e.slots);
+      if (e.ticket) fold_if_last(e, lane, M, 0);
     } else {
       __shared__ unsigned long long s_list[WV * M * 16];
       const int rho = lane >> 4;
@@ -1244,8 +1473,13 @@ proj_valu_tiled(const uint16_t* __restrict__ h, const uint16_t* __restrict__ W, 
   const int hc = nb * 64;
   const uint32_t row_bytes = (uint32_t)K * 2u;
 
-  stage_hidden<64 * WV>(h, K, M, hc, hc, h_stripes);
-  __syncthreads();
+  // The hidden rows go to LDS once the wave's first weight batch is in
+  // flight (stage_and_sync below), so the two memory latencies at the start
+  // overlap instead of adding up.
+  auto stage_and_sync = [&]() __attribute__((always_inline)) {
+    stage_hidden<64 * WV>(h, K, M, hc, hc, h_stripes);
+    __syncthreads();
+  };
 
   ValuEpilogue<M, WV, TK, LOGITS> ep;
   ep.init();
@@ -1340,7 +1574,7 @@ proj_valu_tiled(const uint16_t* __restrict__ h, const uint16_t* __restrict__ W, 
     const int tile0 = first_unit(wave, WV);
     const int my_tiles = tile0 < ntiles ? (ntiles - 1 - tile0) / tstride + 1 : 0;
     const int count = my_tiles * nb;
-    if (count > 0) {
+    {
       u32x4 ring[D][TR];
       int live[D];
       int vid[IDX ? D : 1];
@@ -1348,13 +1582,6 @@ proj_valu_tiled(const uint16_t* __restrict__ h, const uint16_t* __restrict__ W, 
       int ta = tile0, ja = 0;  // position D ahead of it (IDX ids)
       int tc = tile0, jc = 0;  // next position to consume
       auto id_lane = [&](int tile) { return load_row_id(epi.rowmap, R, tile * TR + (lane < TR ? lane : 0)); };
-      if constexpr (IDX) {
-#pragma unroll
-        for (int q = 0; q < D; ++q) {
-          vid[q] = id_lane(ta);
-          advance(ta, ja);
-        }
-      }
       auto issue_at = [&](auto slot) __attribute__((always_inline)) {
         constexpr int S = decltype(slot)::value;
         const int c = lane + 64 * ji;
@@ -1388,9 +1615,19 @@ proj_valu_tiled(const uint16_t* __restrict__ h, const uint16_t* __restrict__ W, 
         consume(ring[S], live[S], tc, jc);
         advance(tc, jc);
       };
-      [&]<int... J>(std::integer_sequence<int, J...>) {
-        (issue_at(std::integral_constant<int, J>{}), ...);
-      }(std::make_integer_sequence<int, D - 1>{});
+      if (count > 0) {
+        if constexpr (IDX) {
+#pragma unroll
+          for (int q = 0; q < D; ++q) {
+            vid[q] = id_lane(ta);
+            advance(ta, ja);
+          }
+        }
+        [&]<int... J>(std::integer_sequence<int, J...>) {
+          (issue_at(std::integral_constant<int, J>{}), ...);
+        }(std::make_integer_sequence<int, D - 1>{});
+      }
+      stage_and_sync();
       int n = 0;
       for (; n + D <= count; n += D) {
         [&]<int... J>(std::integer_sequence<int, J...>) {
@@ -1416,6 +1653,9 @@ proj_valu_tiled(const uint16_t* __restrict__ h, const uint16_t* __restrict__ W, 
   if (tile < ntiles) {
     if constexpr (IDX) fetch_next_ids(tile);
     issue(wa, la, tile, 0);
+  }
+  stage_and_sync();
+  if (tile < ntiles) {
     while (true) {
       int t1 = tile, j1 = j;
       advance(t1, j1);
@@ -1577,17 +1817,23 @@ proj_valu_fp8(const uint16_t* __restrict__ h, const uint8_t* __restrict__ W, con
 // when read from the stage, and a row's sum is multiplied by its fp32
 // scale); or one of E2M1 codes (kFmtMx4: one E8M0 scale per k-step and row;
 // each batch also loads the 16 scale bytes of each of its 16 rows, staged
-// beside the codes, and the codes become bf16 times the scale, exactly).
+// beside the codes, and the codes become bf16 times the scale, exactly); or
+// NVFP4 (kFmtNv4: as MXFP4, with two E4M3 block scales per k-step and row,
+// 32 scale bytes per row per batch, each code times its decoded block scale
+// exactly in bf16; a row's sum is multiplied once by the head's fp32 scale
+// *gsc).
 template <int NT, int SB, int WV, int D, int TK, bool LOGITS, int FMT, bool IDX = false>
 __global__ void __launch_bounds__(64 * WV)
-proj_mfma(const uint16_t* __restrict__ h, const void* __restrict__ Wv, const void* __restrict__ wsc, int R,
-          int K, int m_base, int mp, Epi epi, int early) {
+proj_mfma(const uint16_t* __restrict__ h, const void* __restrict__ Wv, const void* __restrict__ wsc,
+          const float* __restrict__ gsc, int R, int K, int m_base, int mp, Epi epi, int early) {
   constexpr bool FP8 = FMT == kFmtFp8;
-  constexpr bool MX4 = FMT == kFmtMx4;
+  constexpr bool NV4 = FMT == kFmtNv4;
+  constexpr bool MX4 = FMT == kFmtMx4 || NV4;   // the E2M1 code layout and batch shape
   static_assert(!IDX || (TK == 1 && !LOGITS && FMT == kFmtBf16), "indexed rows: bf16 argmax epilogue");
-  static_assert(!MX4 || SB == 16, "MXFP4: a batch is 16 k-steps, one scale chunk per row");
+  static_assert(!MX4 || SB == 16, "MXFP4 / NVFP4: a batch is 16 k-steps, one scale piece per row");
   const float* wscale = static_cast<const float*>(wsc);     // FP8: [R] fp32
-  const uint8_t* mxscale = static_cast<const uint8_t*>(wsc);  // MX4: [R, K / 32] E8M0 codes
+  const uint8_t* mxscale = static_cast<const uint8_t*>(wsc);  // MX4: E8M0 codes; NV4: E4M3 codes (tiled)
+  constexpr int SPR = NV4 ? 2 : 1;  // MX4 / NV4: 16-byte scale chunks per row per batch
   constexpr int CPS = FP8 ? 2 : (MX4 ? 1 : 4);  // 16-byte chunks per k-step
   constexpr int BC = CPS * SB;      // 16-byte chunks per row per batch
   static_assert(BC == 16 || BC == 32 || BC == 64, "a load instruction covers whole row pieces");
@@ -1613,8 +1859,8 @@ proj_mfma(const uint16_t* __restrict__ h, const void* __restrict__ Wv, const voi
     __syncthreads();
   }
   u32x4* stage = lds + mp * row_chunks + wave * 16 * SC;
-  // MX4: this wave's scale stage, one 16-byte chunk (16 k-steps) per row
-  u32x4* sstage = lds + mp * row_chunks + WV * 16 * SC + wave * 16;
+  // MX4 / NV4: this wave's scale stage, SPR 16-byte chunks (16 k-steps) per row
+  u32x4* sstage = lds + mp * row_chunks + WV * 16 * SC + wave * 16 * SPR;
   const u32x4* bptr[NT];
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
@@ -1649,7 +1895,10 @@ proj_mfma(const uint16_t* __restrict__ h, const void* __restrict__ Wv, const voi
   for (int nt = 0; nt < NT; ++nt) acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   const uint32_t row_bytes = FP8 ? (uint32_t)K : (MX4 ? (uint32_t)K / 2u : (uint32_t)K * 2u);
-  const uint32_t sc_row_bytes = (uint32_t)K / 32u;  // MX4: scale bytes per row (a tile holds 16 rows' worth)
+  // MX4 / NV4: scale bytes per row (a tile holds 16 rows' worth)
+  const uint32_t sc_row_bytes = NV4 ? (uint32_t)K / 16u : (uint32_t)K / 32u;
+  // NV4: the head's fp32 scale, one scalar load
+  const float gscale = NV4 ? *gsc : 1.0f;
   const int ntiles = (R + 15) >> 4;
   const int nbatch = (steps + SB - 1) / SB;
   const int lrow = lane / BC;  // row of this lane within a load instruction
@@ -1663,7 +1912,7 @@ proj_mfma(const uint16_t* __restrict__ h, const void* __restrict__ Wv, const voi
   // FP8: scales of head rows r0 .. r0 + 15 of a tile, read with scalar
   // loads one tile ahead (the wave's next tile), clamped to the last row.
   float sc[FP8 ? 16 : 1];
-  auto load_scales = [&](int tile) {
+  auto load_scales = [&](int tile) __attribute__((always_inline)) {
     if constexpr (FP8) {
       const int r0 = tile * 16;
 #pragma unroll
@@ -1679,14 +1928,14 @@ proj_mfma(const uint16_t* __restrict__ h, const void* __restrict__ Wv, const voi
   const uint8_t* vrow[IDX ? LPB : 1];
   unsigned long long hist = 0ull;
   int pushed = 0;
-  auto fetch_tile_ids = [&](int tile) {
+  auto fetch_tile_ids = [&](int tile) __attribute__((always_inline)) {
     if constexpr (IDX) {
       const int r0 = tile * 16;
 #pragma unroll
       for (int i = 0; i < 16; ++i) snext[i] = epi.rowmap[min(r0 + i, R - 1)];  // checked against R when used
     }
   };
-  auto start_issue_tile = [&](int tile) {
+  auto start_issue_tile = [&](int tile) __attribute__((always_inline)) {
     if constexpr (IDX) {
       int scur[16];
       uint32_t mask = 0u;
@@ -1710,14 +1959,14 @@ proj_mfma(const uint16_t* __restrict__ h, const void* __restrict__ Wv, const voi
   };
   // Rows of tile `tile` (issued at most three tiles ago) that take part,
   // bit i for row i of the tile.
-  auto tile_mask = [&](int tile) -> uint32_t {
+  auto tile_mask = [&](int tile) __attribute__((always_inline)) -> uint32_t {
     const int d = (pushed - tile) / tstride;
     return (uint32_t)(hist >> (16 * d)) & 0xFFFFu;
   };
 
   // Positions past the last tile get a descriptor with no records, so their
   // loads read zero without touching memory (live is clamped at 0).
-  auto issue = [&](u32x4 (&buf)[LPB], u32x4& sbuf, int tile, int b) {
+  auto issue = [&](u32x4 (&buf)[LPB], u32x4& sbuf, int tile, int b) __attribute__((always_inline)) {
     if constexpr (IDX) {
       if (b == 0) start_issue_tile(tile);
       const int cg = b * BC + lc;
@@ -1738,22 +1987,31 @@ proj_mfma(const uint16_t* __restrict__ h, const void* __restrict__ Wv, const voi
 #pragma unroll
     for (int q = 0; q < LPB; ++q) buf[q] = load16<kPolicyStream>(rs, cbase + rowoff[q]);
     if constexpr (MX4) {
-      // lane i16 of the first 16 lanes: scale bytes of k-steps b*16 .. b*16 + 15
-      // of row i16, 16 bytes at (b * 16 + i16) * 16 in the tile's part of the
-      // tiled scale layout (whole 16-row tiles, so one 256-byte piece per batch)
+      // lane (g < SPR, i16): scale chunk g of row i16 for k-steps b*16 ..
+      // b*16 + 15, at ((b * 16 + i16) * SPR + g) * 16 in the tile's part of
+      // the tiled scale layout (whole 16-row tiles, so one piece of 256
+      // (MXFP4) or 512 (NVFP4) contiguous bytes per batch)
       const __amdgpu_buffer_rsrc_t ss =
           make_rsrc(mxscale + (size_t)r0 * sc_row_bytes, live > 0 ? 16u * sc_row_bytes : 0u);
-      const uint32_t soff = g == 0 && i16 < live ? ((uint32_t)b * 16u + (uint32_t)i16) * 16u : kOobOffset;
+      const uint32_t soff = g < SPR && i16 < live
+                                ? (((uint32_t)b * 16u + (uint32_t)i16) * (uint32_t)SPR + (uint32_t)g) * 16u
+                                : kOobOffset;
       sbuf = load16<kPolicyStream>(ss, soff);
     } else {
       (void)sbuf;
     }
   };
   // A operand of k-step sb of the staged batch: 8 elements of row i16
-  auto a_operand = [&](int sb) -> u32x4 {
+  auto a_operand = [&](int sb) __attribute__((always_inline)) -> u32x4 {
     if constexpr (FP8) {
       const uint2 raw = reinterpret_cast<const uint2*>(stage)[(i16 * SC + 2 * sb) * 2 + g];
       return fp8x8_to_bf16x8(raw.x, raw.y);
+    } else if constexpr (NV4) {
+      // the lane's 8 codes (elements 8 g .. 8 g + 7 of the k-step) share the
+      // block scale of block 2 sb + g / 2
+      const uint32_t codes = reinterpret_cast<const uint32_t*>(stage)[(i16 * SC + sb) * 4 + g];
+      const uint32_t e = reinterpret_cast<const uint8_t*>(sstage)[i16 * 32 + 2 * sb + (g >> 1)];
+      return fp4x8_times_scale_to_bf16x8(codes, e4m3_to_f32(e));
     } else if constexpr (MX4) {
       const uint32_t codes = reinterpret_cast<const uint32_t*>(stage)[(i16 * SC + sb) * 4 + g];
       const uint32_t e = reinterpret_cast<const uint8_t*>(sstage)[i16 * 16 + sb];
@@ -1762,7 +2020,7 @@ proj_mfma(const uint16_t* __restrict__ h, const void* __restrict__ Wv, const voi
       return stage[i16 * SC + 4 * sb + g];
     }
   };
-  auto mma_step = [&](const u32x4& a, int s) {
+  auto mma_step = [&](const u32x4& a, int s) __attribute__((always_inline)) {
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
       const u32x4 bf = bptr[nt][s * 4];
@@ -1770,19 +2028,19 @@ proj_mfma(const uint16_t* __restrict__ h, const void* __restrict__ Wv, const voi
                                                         __builtin_bit_cast(bf16x8, bf), acc[nt], 0, 0, 0);
     }
   };
-  auto consume = [&](const u32x4 (&buf)[LPB], const u32x4& sbuf, int b) {
+  auto consume = [&](const u32x4 (&buf)[LPB], const u32x4& sbuf, int b) __attribute__((always_inline)) {
     // IDX: chunks past the row end were loaded from column 0; zero them
     const bool in_row = !IDX || b * BC + lc < wchunks;
 #pragma unroll
     for (int q = 0; q < LPB; ++q) stage[(q * RPI + lrow) * SC + lc] = in_row ? buf[q] : u32x4{0u, 0u, 0u, 0u};
     if constexpr (MX4) {
-      if (g == 0) sstage[i16] = sbuf;
+      if (g < SPR) sstage[i16 * SPR + g] = sbuf;
     }
     // lanes of this wave exchange data through the stage
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    if (MX4 || (b + 1) * SB <= steps) {  // MXFP4 heads hold whole batches (K % 512 == 0)
+    if (MX4 || (b + 1) * SB <= steps) {  // MXFP4 / NVFP4 heads hold whole batches (K % 512 == 0)
       // whole batch: operand reads first, then the matrix instructions, in
       // groups of CH k-steps (MXFP4's 16 k-steps at once would not fit the
       // registers)
@@ -1826,6 +2084,12 @@ proj_mfma(const uint16_t* __restrict__ h, const void* __restrict__ Wv, const voi
         for (int nt = 0; nt < NT; ++nt) acc[nt][v] *= s;
       }
       load_scales(tile + tstride);
+    } else if constexpr (NV4) {
+      // the head's scale, once per row sum
+#pragma unroll
+      for (int v = 0; v < 4; ++v)
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) acc[nt][v] *= gscale;
     }
     if (LOGITS && vec_logits && r0 + 4 * g + 3 < R) {
 #pragma unroll
@@ -1876,7 +2140,7 @@ proj_mfma(const uint16_t* __restrict__ h, const void* __restrict__ Wv, const voi
   // the matrix cores.  The loop is unrolled D times so ring slots are static.
   int ti = first_unit(wave, WV), bi = 0;  // next pair to issue
   int tc = ti, bc = 0;                      // next pair to consume
-  auto advance = [&](int& t, int& bb) {
+  auto advance = [&](int& t, int& bb) __attribute__((always_inline)) {
     if (++bb == nbatch) {
       bb = 0;
       t += tstride;
@@ -1939,6 +2203,7 @@ proj_mfma(const uint16_t* __restrict__ h, const void* __restrict__ Wv, const voi
       for (int w = 0; w < WV; ++w) key = s_key[w][lane] > key ? s_key[w][lane] : key;
     }
     publish_workgroup(key, lane, mp, m_base, epi.slots);
+    if (epi.ticket) fold_if_last(epi, lane, mp, m_base);
   } else if constexpr (kColLists) {
     // every wave is past its main loop: the stage area is free for the lists
     __syncthreads();
@@ -2260,9 +2525,11 @@ int launch_valu(const ValuPlan& p, const uint16_t* h, int K, const uint16_t* W, 
 }
 
 // LDS of the per-wave stages of the matrix-core kernel: a 16-row code
-// stage (and for MXFP4 a 16-chunk scale stage) per wave.
+// stage (and for MXFP4 a 16-chunk, for NVFP4 a 32-chunk scale stage) per
+// wave.
 size_t mfma_stage_bytes(int waves, int fmt) {
-  return (size_t)waves * 16 * (4 * LMH_MFMA_LDS_SB + 1) * 16 + (fmt == kFmtMx4 ? (size_t)waves * 16 * 16 : 0);
+  const size_t scale_chunks = fmt == kFmtMx4 ? 16 : (fmt == kFmtNv4 ? 32 : 0);
+  return (size_t)waves * 16 * (4 * LMH_MFMA_LDS_SB + 1) * 16 + (size_t)waves * scale_chunks * 16;
 }
 
 // Hidden rows one launch of the matrix-core kernel can stage for K with
@@ -2283,20 +2550,22 @@ int mfma_lds_rows_fit(int64_t K, int waves, int fmt = kFmtBf16) {
 // few rows (MXFP4: 3.5% at 1, 3 and 8 rows; FP8: 1% at 1 and 3 rows), where
 // waiting for the early batches delays the start.
 bool mfma_stage_early(int fmt, int mp, int64_t R) {
-  return R >= LMH_RING_MAX_ROWS || mp >= 16 || (mp >= 5 && fmt != kFmtMx4);
+  return R >= LMH_RING_MAX_ROWS || mp >= 16 || (mp >= 5 && fmt != kFmtMx4 && fmt != kFmtNv4);
 }
 
 // One pass of the matrix-core path over hidden rows [m_base, m_base + mp):
 // 8 waves per workgroup when the hidden rows and eight stages fit the LDS
 // and the head has at least 8 tiles per CU, else 4; two 16-column tiles
 // when mp > 16.
-// FP8 heads take twice the k-steps per batch and MXFP4 heads four times, so
-// a batch moves the same code bytes (and the stage has the same size) as for
-// bf16.  `wsc` is the FP8 row scales or the MXFP4 block scales.
+// FP8 heads take twice the k-steps per batch and MXFP4 / NVFP4 heads four
+// times, so a batch moves the same code bytes (and the stage has the same
+// size) as for bf16.  `wsc` is the FP8 row scales or the MXFP4 / NVFP4
+// block scales; `gsc` the NVFP4 head's fp32 scale (else unused).
 template <int TK, bool LOGITS, int FMT, bool IDX = false>
-int launch_mfma_pass(const uint16_t* h, int K, int m_base, int mp, const void* W, const void* wsc, int R,
-                     const Epi& epi, int cus, hipStream_t stream, int* grid_out) {
-  constexpr int SB = FMT == kFmtFp8 ? 2 * LMH_MFMA_LDS_SB : (FMT == kFmtMx4 ? 4 * LMH_MFMA_LDS_SB : LMH_MFMA_LDS_SB);
+int launch_mfma_pass(const uint16_t* h, int K, int m_base, int mp, const void* W, const void* wsc,
+                     const float* gsc, int R, const Epi& epi, int cus, hipStream_t stream, int* grid_out) {
+  constexpr int SB = FMT == kFmtFp8 ? 2 * LMH_MFMA_LDS_SB
+                                    : (FMT == kFmtMx4 || FMT == kFmtNv4 ? 4 * LMH_MFMA_LDS_SB : LMH_MFMA_LDS_SB);
   constexpr int D = LMH_MFMA_RING;
   const void* wscale = wsc;
   const size_t hbytes = (size_t)mp * mfma_row_bytes(K);
@@ -2310,13 +2579,13 @@ int launch_mfma_pass(const uint16_t* h, int K, int m_base, int mp, const void* W
   const int early = mfma_stage_early(FMT, mp, R) ? 1 : 0;
   if (mp <= 16)
     return eight ? launch_persistent(proj_mfma<1, SB, 8, D, TK, LOGITS, FMT, IDX>, 512, lds, tiles, 8, 1 << 20, cus,
-                                     stream, what, grid_out, h, W, wscale, R, K, m_base, mp, epi, early)
+                                     stream, what, grid_out, h, W, wscale, gsc, R, K, m_base, mp, epi, early)
                  : launch_persistent(proj_mfma<1, SB, 4, D, TK, LOGITS, FMT, IDX>, 256, lds, tiles, 4, 1 << 20, cus,
-                                     stream, what, grid_out, h, W, wscale, R, K, m_base, mp, epi, early);
+                                     stream, what, grid_out, h, W, wscale, gsc, R, K, m_base, mp, epi, early);
   return eight ? launch_persistent(proj_mfma<2, SB, 8, D, TK, LOGITS, FMT, IDX>, 512, lds, tiles, 8, 1 << 20, cus,
-                                   stream, what, grid_out, h, W, wscale, R, K, m_base, mp, epi, early)
+                                   stream, what, grid_out, h, W, wscale, gsc, R, K, m_base, mp, epi, early)
                : launch_persistent(proj_mfma<2, SB, 4, D, TK, LOGITS, FMT, IDX>, 256, lds, tiles, 4, 1 << 20, cus,
-                                   stream, what, grid_out, h, W, wscale, R, K, m_base, mp, epi, early);
+                                   stream, what, grid_out, h, W, wscale, gsc, R, K, m_base, mp, epi, early);
 }
 
 // VALU path over an FP8 head: the tiled kernel for every M <= 4.
@@ -2348,6 +2617,13 @@ int launch_finalize_argmax(unsigned long long* slots, int nslots, int m_base, in
   return e == hipSuccess ? LMH_OK : hip_fail(e, "launch finalize_argmax");
 }
 
+int launch_finalize_keys(unsigned long long* slots, int nslots, int m_base, int mcount, int64_t row_base,
+                         unsigned long long* out_key, hipStream_t stream) {
+  hipLaunchKernelGGL(finalize_keys, dim3(mcount), dim3(256), 0, stream, slots, nslots, m_base, row_base, out_key);
+  const hipError_t e = hipGetLastError();
+  return e == hipSuccess ? LMH_OK : hip_fail(e, "launch finalize_keys");
+}
+
 template <int TK>
 int launch_finalize_topk(unsigned long long* slots, int nslots, int m_base, int mcount, int topk,
                          const int32_t* d2t, int32_t* out_id, float* out_logit, hipStream_t stream) {
@@ -2373,6 +2649,9 @@ struct Call {
   const void* wscale = nullptr;
   int fmt = kFmtBf16;
   bool indexed = false;          // W is the whole head, read through epi.rowmap (argmax only)
+  const float* gscale = nullptr; // NVFP4: the head's fp32 scale (device)
+  int64_t row_base = 0;          // keys: global row of the slice's row 0
+  unsigned long long* out_key = nullptr;  // keys: [M] packed keys
 };
 
 int record(hipEvent_t e, hipStream_t s) {
@@ -2380,8 +2659,9 @@ int record(hipEvent_t e, hipStream_t s) {
   return r == hipSuccess ? LMH_OK : hip_fail(r, "hipEventRecord");
 }
 
-// Argmax (TK == 1 with the argmax finalizer), top-TK, or every logit.
-// MODE: 0 = argmax, 1 = top-k, 2 = logits.
+// Argmax (TK == 1 with the argmax finalizer), top-TK, every logit, or the
+// argmax as global-row keys of a head slice.
+// MODE: 0 = argmax, 1 = top-k, 2 = logits, 3 = keys (c.out_key, c.row_base).
 template <int MODE, int TK>
 int run(const Call& c, const Epi& epi, int topk, int32_t* out_id, float* out_logit) {
   constexpr bool LOGITS = MODE == 2;
@@ -2389,23 +2669,27 @@ int run(const Call& c, const Epi& epi, int topk, int32_t* out_id, float* out_log
   int st = cu_count(&cus);
   if (st != LMH_OK) return st;
   auto finalize = [&](int grid, int m_base, int mcount) -> int {
-    if (c.projection_only) return LMH_OK;
+    if (c.projection_only || epi.ticket) return LMH_OK;  // single launch: folded in the kernel
     if constexpr (MODE == 0)
       return launch_finalize_argmax(epi.slots, grid, m_base, mcount, c.d2t, out_id, out_logit, c.stream);
     else if constexpr (MODE == 1)
       return launch_finalize_topk<TK>(epi.slots, grid, m_base, mcount, topk, c.d2t, out_id, out_logit, c.stream);
+    else if constexpr (MODE == 3)
+      return launch_finalize_keys(epi.slots, grid, m_base, mcount, c.row_base, c.out_key, c.stream);
     else
       return LMH_OK;
   };
   const bool fp8 = c.fmt == kFmtFp8;
   const bool mx4 = c.fmt == kFmtMx4;
-  if ((fp8 || mx4) && MODE == 2) return LMH_EINVAL;  // quantized heads: argmax and top k
-  if ((fp8 || mx4) && !c.wscale) return LMH_EINVAL;
+  const bool nv4 = c.fmt == kFmtNv4;
+  if ((fp8 || mx4 || nv4) && MODE == 2) return LMH_EINVAL;  // quantized heads: argmax and top k
+  if ((fp8 || mx4 || nv4) && !c.wscale) return LMH_EINVAL;
+  if (nv4 && !c.gscale) return LMH_EINVAL;
   constexpr bool kIdxOk = MODE == 0 && TK == 1;
   if (c.indexed && (!kIdxOk || c.fmt != kFmtBf16 || !epi.rowmap)) return LMH_EINVAL;
   if (c.path == LMH_PATH_VALU) {
     int grid = 0;
-    if (mx4) return LMH_EINVAL;  // MXFP4 heads take the matrix cores only
+    if (mx4 || nv4) return LMH_EINVAL;  // MXFP4 and NVFP4 heads take the matrix cores only
     if (fp8) {
       if constexpr (MODE != 0) return LMH_EINVAL;  // top k over an FP8 head: matrix cores only
       st = launch_valu_fp8(c.h, c.M, c.K, static_cast<const uint8_t*>(c.W), static_cast<const float*>(c.wscale),
@@ -2429,19 +2713,25 @@ int run(const Call& c, const Epi& epi, int topk, int32_t* out_id, float* out_log
   for (int m0 = 0; m0 < c.M; m0 += per) {
     const int mp = std::min(per, c.M - m0);
     int grid = 0;
-    if (fp8 || mx4) {
+    if (fp8 || mx4 || nv4) {
       if constexpr (MODE != 2) {
-        st = fp8 ? launch_mfma_pass<TK, LOGITS, kFmtFp8>(c.h, c.K, m0, mp, c.W, c.wscale, c.R, epi, cus, c.stream,
-                                                         &grid)
-                 : launch_mfma_pass<TK, LOGITS, kFmtMx4>(c.h, c.K, m0, mp, c.W, c.wscale, c.R, epi, cus, c.stream,
-                                                         &grid);
+        if (fp8)
+          st = launch_mfma_pass<TK, LOGITS, kFmtFp8>(c.h, c.K, m0, mp, c.W, c.wscale, nullptr, c.R, epi, cus,
+                                                     c.stream, &grid);
+        else if (mx4)
+          st = launch_mfma_pass<TK, LOGITS, kFmtMx4>(c.h, c.K, m0, mp, c.W, c.wscale, nullptr, c.R, epi, cus,
+                                                     c.stream, &grid);
+        else
+          st = launch_mfma_pass<TK, LOGITS, kFmtNv4>(c.h, c.K, m0, mp, c.W, c.wscale, c.gscale, c.R, epi, cus,
+                                                     c.stream, &grid);
       }
     } else if (c.indexed) {
       if constexpr (kIdxOk)
-        st = launch_mfma_pass<TK, LOGITS, kFmtBf16, true>(c.h, c.K, m0, mp, c.W, nullptr, c.R, epi, cus, c.stream,
+        st = launch_mfma_pass<TK, LOGITS, kFmtBf16, true>(c.h, c.K, m0, mp, c.W, nullptr, nullptr, c.R, epi, cus, c.stream,
                                                           &grid);
     } else {
-      st = launch_mfma_pass<TK, LOGITS, kFmtBf16>(c.h, c.K, m0, mp, c.W, nullptr, c.R, epi, cus, c.stream, &grid);
+      st = launch_mfma_pass<TK, LOGITS, kFmtBf16>(c.h, c.K, m0, mp, c.W, nullptr, nullptr, c.R, epi, cus, c.stream,
+                                                  &grid);
     }
     if (st != LMH_OK) return st;
     st = finalize(grid, m0, mp);
@@ -2457,7 +2747,7 @@ bool valu_epi_ok(int64_t M, int64_t K) { return M <= 4 && valu_ok(M, K); }
 // argmax, else top k / logits; `indexed`: rows read in place through a
 // list).  VALU up to 4 hidden rows, matrix cores above, measured on the
 // full head.  Exception, measured on the lists: an argmax over 4 hidden
-// rows and a head of fewer than LMH_RING_MAX_ROWS rows runs 1-4% faster on
+// rows and a head of fewer than LMH_M4_MFMA_MAX_ROWS rows runs 1-4% faster on
 // the matrix cores (32,768 rows: 27.24 against 28.37 us; 16,000: 15.39
 // against 15.67; 52,755: 43.09 against 43.60), while on the full head the
 // VALU kernel is 2% faster (179.4 against 183.3 us).  Read in place through
@@ -2465,7 +2755,7 @@ bool valu_epi_ok(int64_t M, int64_t K) { return M <= 4 && valu_ok(M, K); }
 // calls keep the VALU kernel.
 int default_path(int64_t M, int64_t K, int64_t R, int mode, bool indexed) {
   if (M > LMH_VALU_AUTO_MAX_M || !(mode == 0 ? valu_ok(M, K) : valu_epi_ok(M, K))) return LMH_PATH_MFMA;
-  if (mode == 0 && !indexed && M == 4 && R < LMH_RING_MAX_ROWS) return LMH_PATH_MFMA;
+  if (mode == 0 && !indexed && M == 4 && R < LMH_M4_MFMA_MAX_ROWS) return LMH_PATH_MFMA;
   return LMH_PATH_VALU;
 }
 
@@ -2513,11 +2803,21 @@ int check_mx4(const uint16_t* h, int64_t M, int64_t K, const uint8_t* Wq, const 
   return LMH_OK;
 }
 
+// Checks for a call over an NVFP4 head: as check_mx4 (K a multiple of 512,
+// the matrix cores only), plus a 4-byte aligned pointer to the head's fp32
+// scale.
+int check_nv4(const uint16_t* h, int64_t M, int64_t K, const uint8_t* Wq, const uint8_t* scales,
+              const float* gscale, int64_t R, int* path) {
+  if (!gscale || (reinterpret_cast<uintptr_t>(gscale) & 3u) != 0) return LMH_EINVAL;
+  return check_mx4(h, M, K, Wq, scales, R, path);
+}
+
 // Mean projection-kernel time over `calls` back-to-back launches between two
 // events, then one whole call so the outputs hold a result (bench helpers).
 // `scales[i]` goes with `heads[i]` for FP8 and MXFP4 heads.
 int time_projection(Call c, int nheads, const void* const* heads, const void* const* scales, const Epi& epi,
-                    int32_t* out_id, float* out_logit, int calls, double* proj_ms) {
+                    int32_t* out_id, float* out_logit, int calls, double* proj_ms,
+                    const float* const* gscales = nullptr) {
   hipEvent_t ev[2] = {nullptr, nullptr};
   int st = LMH_OK;
   for (auto& e : ev) {
@@ -2536,6 +2836,7 @@ int time_projection(Call c, int nheads, const void* const* heads, const void* co
     Call ci = c;
     ci.W = heads[i % nheads];
     ci.wscale = scales ? scales[i % nheads] : nullptr;
+    ci.gscale = gscales ? gscales[i % nheads] : nullptr;
     ci.projection_only = true;
     st = run<0, 1>(ci, epi, 1, out_id, out_logit);
   }
@@ -2544,6 +2845,7 @@ int time_projection(Call c, int nheads, const void* const* heads, const void* co
     Call c0 = c;
     c0.W = heads[0];
     c0.wscale = scales ? scales[0] : nullptr;
+    c0.gscale = gscales ? gscales[0] : nullptr;
     st = run<0, 1>(c0, epi, 1, out_id, out_logit);
   }
   if (st == LMH_OK) {
@@ -2612,7 +2914,7 @@ size_t draft_project_workspace_bytes(int64_t M) {
 
 int draft_project_auto_path(int64_t M, int64_t K) {
   if (M < 1 || M > LMH_MAX_M || !k_ok(K)) return -1;
-  return default_path(M, K, LMH_RING_MAX_ROWS, 0, false);
+  return default_path(M, K, kMaxRows, 0, false);
 }
 
 int draft_project_auto_path_rows(int64_t M, int64_t K, int64_t R) {
@@ -2810,7 +3112,7 @@ int lmhead_mxfp4_tile_scales(const uint8_t* src, int64_t R, int64_t K, uint8_t* 
   if (st != LMH_OK) return st;
   const int64_t n = R * (K / 32);
   const int grid = (int)std::max<int64_t>(1, std::min<int64_t>((n + 255) / 256, (int64_t)cus * 16));
-  hipLaunchKernelGGL(tile_mxfp4_scales, dim3(grid), dim3(256), 0, static_cast<hipStream_t>(stream), src, (int)R,
+  hipLaunchKernelGGL(tile_block_scales<16>, dim3(grid), dim3(256), 0, static_cast<hipStream_t>(stream), src, (int)R,
                      (int)(K / 32), scales);
   const hipError_t e = hipGetLastError();
   return e == hipSuccess ? LMH_OK : hip_fail(e, "launch tile_mxfp4_scales");
@@ -2842,6 +3144,143 @@ int draft_project_argmax_mxfp4(const uint16_t* h, int64_t M, int64_t K, const ui
   c.wscale = scales;
   c.fmt = kFmtMx4;
   const Epi epi{static_cast<unsigned long long*>(workspace), nullptr, nullptr, 0, 0};
+  return run<0, 1>(c, epi, 1, out_id, out_logit);
+}
+
+int64_t lmhead_nvfp4_scale_bytes(int64_t R, int64_t K) {
+  if (R < 0 || R > kMaxRows || !k_ok(K) || (K % 16) != 0) return -1;
+  return (R + 15) / 16 * ((K / 16 + 31) / 32) * 512;
+}
+
+int lmhead_nvfp4_tile_scales(const uint8_t* src, int64_t R, int64_t K, uint8_t* scales, void* stream) {
+  if (R < 0 || R > kMaxRows || !k_ok(K) || (K % 16) != 0) return LMH_EINVAL;
+  if (R == 0) return LMH_OK;
+  if (!src || !scales) return LMH_EINVAL;
+  int cus = 0;
+  const int st = cu_count(&cus);
+  if (st != LMH_OK) return st;
+  const int64_t n = R * (K / 16);
+  const int grid = (int)std::max<int64_t>(1, std::min<int64_t>((n + 255) / 256, (int64_t)cus * 16));
+  hipLaunchKernelGGL(tile_block_scales<32>, dim3(grid), dim3(256), 0, static_cast<hipStream_t>(stream), src, (int)R,
+                     (int)(K / 16), scales);
+  const hipError_t e = hipGetLastError();
+  return e == hipSuccess ? LMH_OK : hip_fail(e, "launch tile_block_scales");
+}
+
+int lmhead_quantize_nvfp4(const uint16_t* W, int64_t R, int64_t K, uint8_t* Wq, uint8_t* scales, float* gscale,
+                          void* stream) {
+  if (R < 0 || R > kMaxRows || !k_ok(K) || (K % 16) != 0) return LMH_EINVAL;
+  if (R == 0) return LMH_OK;
+  if (!W || !Wq || !scales || !gscale || !aligned16(W) || !aligned16(Wq) ||
+      (reinterpret_cast<uintptr_t>(gscale) & 3u) != 0)
+    return LMH_EINVAL;
+  int cus = 0;
+  const int st = cu_count(&cus);
+  if (st != LMH_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int64_t n16 = R * K / 8;
+  const int agrid = (int)std::max<int64_t>(1, std::min<int64_t>((n16 + 255) / 256, (int64_t)cus * 8));
+  const int qgrid = (int)std::max<int64_t>(1, std::min<int64_t>((R + 3) / 4, (int64_t)cus * 16));
+  hipLaunchKernelGGL(nvfp4_slot_zero, dim3(1), dim3(64), 0, s, gscale);
+  hipLaunchKernelGGL(nvfp4_head_amax, dim3(agrid), dim3(256), 0, s, W, n16, gscale);
+  hipLaunchKernelGGL(quantize_rows_nvfp4, dim3(qgrid), dim3(256), 0, s, W, (int)R, (int)K, Wq, scales,
+                     static_cast<const float*>(gscale));
+  hipLaunchKernelGGL(nvfp4_set_scale, dim3(1), dim3(64), 0, s, gscale);
+  const hipError_t e = hipGetLastError();
+  return e == hipSuccess ? LMH_OK : hip_fail(e, "launch NVFP4 quantization");
+}
+
+int draft_project_argmax_nvfp4(const uint16_t* h, int64_t M, int64_t K, const uint8_t* Wq, const uint8_t* scales,
+                               const float* gscale, int64_t R, const int32_t* d2t, int32_t* out_id,
+                               float* out_logit, void* workspace, size_t workspace_bytes, int path, void* stream) {
+  int st = check_nv4(h, M, K, Wq, scales, gscale, R, &path);
+  if (st != LMH_OK) return st;
+  if (!out_id || !out_logit) return LMH_EINVAL;
+  if (!workspace || !aligned16(workspace)) return LMH_EWORKSPACE;
+  if (workspace_bytes < draft_project_workspace_bytes(M)) return LMH_EWORKSPACE;
+  Call c{h, (int)M, (int)K, Wq, (int)R, d2t, path, static_cast<hipStream_t>(stream)};
+  c.wscale = scales;
+  c.gscale = gscale;
+  c.fmt = kFmtNv4;
+  const Epi epi{static_cast<unsigned long long*>(workspace), nullptr, nullptr, 0, 0};
+  return run<0, 1>(c, epi, 1, out_id, out_logit);
+}
+
+int draft_project_topk_nvfp4(const uint16_t* h, int64_t M, int64_t K, const uint8_t* Wq, const uint8_t* scales,
+                             const float* gscale, int64_t R, const int32_t* d2t, int64_t topk, int32_t* out_id,
+                             float* out_logit, void* workspace, size_t workspace_bytes, int path, void* stream) {
+  int st = check_nv4(h, M, K, Wq, scales, gscale, R, &path);
+  if (st != LMH_OK) return st;
+  if ((st = check_topk_io(M, topk, out_id, out_logit, workspace, workspace_bytes)) != LMH_OK) return st;
+  Call c{h, (int)M, (int)K, Wq, (int)R, d2t, path, static_cast<hipStream_t>(stream)};
+  c.wscale = scales;
+  c.gscale = gscale;
+  c.fmt = kFmtNv4;
+  const Epi epi{static_cast<unsigned long long*>(workspace), nullptr, nullptr, 0, 0};
+  return run_topk(c, epi, topk, out_id, out_logit);
+}
+
+int lmhead_bench_time_argmax_nvfp4(const uint16_t* h, int64_t M, int64_t K, const uint8_t* const* heads,
+                                   const uint8_t* const* scales, const float* const* gscales, int nheads, int64_t R,
+                                   const int32_t* d2t, int32_t* out_id, float* out_logit, void* workspace,
+                                   size_t workspace_bytes, int path, int calls, double* proj_ms, void* stream) {
+  if (!heads || !scales || !gscales || nheads < 1 || calls < 1 || !proj_ms) return LMH_EINVAL;
+  const int path_in = path;
+  int st = LMH_OK;
+  for (int i = 0; i < nheads; ++i) {
+    path = path_in;
+    if ((st = check_nv4(h, M, K, heads[i], scales[i], gscales[i], R, &path)) != LMH_OK) return st;
+  }
+  if (!out_id || !out_logit) return LMH_EINVAL;
+  if (!workspace || !aligned16(workspace)) return LMH_EWORKSPACE;
+  if (workspace_bytes < draft_project_workspace_bytes(M)) return LMH_EWORKSPACE;
+  Call c{h, (int)M, (int)K, heads[0], (int)R, d2t, path, static_cast<hipStream_t>(stream)};
+  c.wscale = scales[0];
+  c.gscale = gscales[0];
+  c.fmt = kFmtNv4;
+  const Epi epi{static_cast<unsigned long long*>(workspace), nullptr, nullptr, 0, 0};
+  return time_projection(c, nheads, reinterpret_cast<const void* const*>(heads),
+                         reinterpret_cast<const void* const*>(scales), epi, out_id, out_logit, calls, proj_ms,
+                         gscales);
+}
+
+int draft_project_argmax_keys(const uint16_t* h, int64_t M, int64_t K, const uint16_t* W, int64_t R,
+                              int64_t row_base, uint64_t* out_key, void* workspace, size_t workspace_bytes,
+                              int path, void* stream) {
+  int st = check_common(h, M, K, W, R, 0, &path);
+  if (st != LMH_OK) return st;
+  if (row_base < 0 || row_base > (int64_t)0xFFFFFFFF - R) return LMH_EINVAL;
+  if (!out_key || (reinterpret_cast<uintptr_t>(out_key) & 7u) != 0) return LMH_EINVAL;
+  if (!workspace || !aligned16(workspace)) return LMH_EWORKSPACE;
+  if (workspace_bytes < draft_project_workspace_bytes(M)) return LMH_EWORKSPACE;
+  Call c{h, (int)M, (int)K, W, (int)R, nullptr, path, static_cast<hipStream_t>(stream)};
+  c.row_base = row_base;
+  c.out_key = reinterpret_cast<unsigned long long*>(out_key);
+  const Epi epi{static_cast<unsigned long long*>(workspace), nullptr, nullptr, 0, 0};
+  return run<3, 1>(c, epi, 1, nullptr, nullptr);
+}
+
+size_t lmhead_bench_onepass_workspace_bytes(int64_t M) {
+  const size_t slots = draft_project_workspace_bytes(M);
+  return slots ? slots + 256 : 0;
+}
+
+int lmhead_bench_argmax_onepass(const uint16_t* h, int64_t M, int64_t K, const uint16_t* W, int64_t R,
+                                const int32_t* d2t, int32_t* out_id, float* out_logit, void* workspace,
+                                size_t workspace_bytes, int path, void* stream) {
+  int st = check_common(h, M, K, W, R, 0, &path);
+  if (st != LMH_OK) return st;
+  if (!out_id || !out_logit) return LMH_EINVAL;
+  if (!workspace || !aligned16(workspace)) return LMH_EWORKSPACE;
+  if (workspace_bytes < lmhead_bench_onepass_workspace_bytes(M)) return LMH_EWORKSPACE;
+  const Call c{h, (int)M, (int)K, W, (int)R, d2t, path, static_cast<hipStream_t>(stream)};
+  // the ticket first, at a place that does not depend on M (calls with any
+  // M may share the workspace), then the slots
+  Epi epi{reinterpret_cast<unsigned long long*>(static_cast<char*>(workspace) + 256), nullptr, nullptr, 0, 0};
+  epi.ticket = static_cast<unsigned int*>(workspace);
+  epi.fold_d2t = d2t;
+  epi.out_id = out_id;
+  epi.out_logit = out_logit;
   return run<0, 1>(c, epi, 1, out_id, out_logit);
 }
 

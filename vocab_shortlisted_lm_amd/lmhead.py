@@ -16,7 +16,7 @@ import torch
 
 __all__ = [
     "LmheadError", "lib", "LMH_OK", "LMH_EINVAL", "LMH_ERANGE", "LMH_EWORKSPACE",
-    "LMH_EHIP", "LMH_MAX_M", "LMH_MIN_K", "LMH_MAX_K", "LMH_PATH_AUTO", "LMH_PATH_VALU",
+    "LMH_EHIP", "LMH_MAX_M", "LMH_MIN_K", "LMH_MAX_K", "LMH_MAX_R", "LMH_PATH_AUTO", "LMH_PATH_VALU",
     "LMH_PATH_MFMA", "lmhead_trim", "draft_project_workspace_bytes", "draft_project_argmax",
     "draft_project_argmax_path", "draft_project_auto_path", "draft_project_auto_path_rows", "lmhead_status_str",
     "lmhead_last_error", "lmhead_bench_sink_words", "lmhead_bench_stream_read",
@@ -28,12 +28,16 @@ __all__ = [
     "lmhead_bench_time_argmax_indexed", "lmhead_quantize_mxfp4", "draft_project_argmax_mxfp4",
     "lmhead_bench_time_argmax_mxfp4", "lmhead_mxfp4_scale_bytes", "lmhead_mxfp4_tile_scales",
     "mxfp4_scale_shape", "draft_project_topk_fp8", "draft_project_topk_mxfp4", "PreparedArgmax",
+    "lmhead_quantize_nvfp4", "lmhead_nvfp4_scale_bytes", "lmhead_nvfp4_tile_scales", "nvfp4_scale_shape",
+    "draft_project_argmax_nvfp4", "draft_project_topk_nvfp4", "lmhead_bench_time_argmax_nvfp4",
+    "lmhead_bench_onepass_workspace", "lmhead_bench_argmax_onepass", "draft_project_argmax_keys",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "liblmhead.so")
 
 LMH_OK, LMH_EINVAL, LMH_ERANGE, LMH_EWORKSPACE, LMH_EHIP = 0, 1, 2, 3, 4
 LMH_MAX_M, LMH_MIN_K, LMH_MAX_K, LMH_MAX_TOPK = 32, 8, 8192, 16
+LMH_MAX_R = (1 << 30) - 1
 LMH_PATH_AUTO, LMH_PATH_VALU, LMH_PATH_MFMA = 0, 1, 2
 LMH_MAX_OVERWRITE, LMH_MAX_UNION_VOCAB = 65536, 524288
 
@@ -42,7 +46,7 @@ _I64 = ctypes.c_int64
 _SZ = ctypes.c_size_t
 _INT = ctypes.c_int
 
-# name -> (restype, argtypes); mirrors include/lmhead.h
+# name -> (restype, argtypes); mirrors include/lmhead.h and include/lmhead_bench.h
 SIGNATURES = {
     "lmhead_trim": (_INT, [_P, _I64, _I64, _P, _I64, _P, _P]),
     "draft_project_workspace_bytes": (_SZ, [_I64]),
@@ -77,6 +81,16 @@ SIGNATURES = {
                                               ctypes.POINTER(ctypes.c_double), _P]),
     "draft_project_topk_fp8": (_INT, [_P, _I64, _I64, _P, _P, _I64, _P, _I64, _P, _P, _P, _SZ, _INT, _P]),
     "draft_project_topk_mxfp4": (_INT, [_P, _I64, _I64, _P, _P, _I64, _P, _I64, _P, _P, _P, _SZ, _INT, _P]),
+    "lmhead_quantize_nvfp4": (_INT, [_P, _I64, _I64, _P, _P, _P, _P]),
+    "lmhead_nvfp4_scale_bytes": (_I64, [_I64, _I64]),
+    "lmhead_nvfp4_tile_scales": (_INT, [_P, _I64, _I64, _P, _P]),
+    "draft_project_argmax_nvfp4": (_INT, [_P, _I64, _I64, _P, _P, _P, _I64, _P, _P, _P, _P, _SZ, _INT, _P]),
+    "draft_project_topk_nvfp4": (_INT, [_P, _I64, _I64, _P, _P, _P, _I64, _P, _I64, _P, _P, _P, _SZ, _INT, _P]),
+    "lmhead_bench_time_argmax_nvfp4": (_INT, [_P, _I64, _I64, _P, _P, _P, _INT, _I64, _P, _P, _P, _P, _SZ, _INT,
+                                              _INT, ctypes.POINTER(ctypes.c_double), _P]),
+    "lmhead_bench_onepass_workspace_bytes": (_SZ, [_I64]),
+    "draft_project_argmax_keys": (_INT, [_P, _I64, _I64, _P, _I64, _I64, _P, _P, _SZ, _INT, _P]),
+    "lmhead_bench_argmax_onepass": (_INT, [_P, _I64, _I64, _P, _I64, _P, _P, _P, _P, _SZ, _INT, _P]),
 }
 
 _lib = None
@@ -752,3 +766,189 @@ def draft_project_topk_mxfp4(h: torch.Tensor, Wq: torch.Tensor, scales: torch.Te
         topk, out_id.data_ptr(), out_logit.data_ptr(), workspace.data_ptr(), _nbytes(workspace), path,
         _stream(stream, h.device)), "draft_project_topk_mxfp4")
     return out_id, out_logit
+
+
+# --------------------------------------------------------------------------
+# NVFP4 heads
+# --------------------------------------------------------------------------
+
+def lmhead_nvfp4_scale_bytes(R: int, K: int) -> int:
+    """Bytes of the tiled block-scale array of an [R, K] NVFP4 head (-1: bad shape)."""
+    return int(lib().lmhead_nvfp4_scale_bytes(R, K))
+
+
+def nvfp4_scale_shape(r: int, k: int) -> tuple:
+    """Shape of the tiled block-scale array of an [R, K] NVFP4 head:
+    (ceil(R / 16), ceil(K / 512), 16, 32) bytes -- [tile][group of 32 blocks]
+    [row in tile][block in group]."""
+    if k % 16 or k <= 0 or r < 0:
+        raise ValueError("K must be a positive multiple of 16")
+    return ((r + 15) // 16, (k // 16 + 31) // 32, 16, 32)
+
+
+def lmhead_quantize_nvfp4(W: torch.Tensor, out: torch.Tensor | None = None, scales: torch.Tensor | None = None,
+                          gscale: torch.Tensor | None = None, stream=None):
+    """(Wq uint8 [R, K / 2] packed E2M1 codes, scales uint8 E4M3 codes in the
+    tiled layout (shape nvfp4_scale_shape(R, K)), gscale float32 [1]) of a
+    bf16 head.  Queues four kernels; never synchronizes."""
+    _dev_tensor(W, "W", _BF16_LIKE, 2)
+    r, k = W.shape
+    if k % 16:
+        raise ValueError("K must be a multiple of 16")
+    if out is None:
+        out = torch.empty((r, k // 2), dtype=torch.uint8, device=W.device)
+    if scales is None:
+        scales = torch.zeros(nvfp4_scale_shape(r, k), dtype=torch.uint8, device=W.device)
+    if gscale is None:
+        gscale = torch.ones(1, dtype=torch.float32, device=W.device)
+    _dev_tensor(out, "Wq", (torch.uint8,), 2, W.device)
+    _dev_tensor(scales, "scales", (torch.uint8,), 4, W.device)
+    _dev_tensor(gscale, "gscale", (torch.float32,), 1, W.device)
+    if tuple(out.shape) != (r, k // 2) or tuple(scales.shape) != nvfp4_scale_shape(r, k):
+        raise ValueError("Wq must be [R, K / 2] and scales of shape nvfp4_scale_shape(R, K)")
+    _check(lib().lmhead_quantize_nvfp4(W.data_ptr(), r, k, out.data_ptr(), scales.data_ptr(), gscale.data_ptr(),
+                                       _stream(stream, W.device)), "lmhead_quantize_nvfp4")
+    return out, scales, gscale
+
+
+def lmhead_nvfp4_tile_scales(src: torch.Tensor, out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """Row-major E4M3 block scales [R, K / 16] (a head quantized elsewhere)
+    into the tiled layout.  Queues one kernel; never synchronizes."""
+    _dev_tensor(src, "src", (torch.uint8,), 2)
+    r, nblk = src.shape
+    k = nblk * 16
+    if out is None:
+        out = torch.zeros(nvfp4_scale_shape(r, k), dtype=torch.uint8, device=src.device)
+    _dev_tensor(out, "scales", (torch.uint8,), 4, src.device)
+    if tuple(out.shape) != nvfp4_scale_shape(r, k):
+        raise ValueError("scales must have shape nvfp4_scale_shape(R, K)")
+    _check(lib().lmhead_nvfp4_tile_scales(src.data_ptr(), r, k, out.data_ptr(), _stream(stream, src.device)),
+           "lmhead_nvfp4_tile_scales")
+    return out
+
+
+def _check_nv4_head(h, Wq, scales, gscale, d2t):
+    _dev_tensor(h, "h", _BF16_LIKE, 2)
+    _dev_tensor(Wq, "Wq", (torch.uint8,), 2, h.device)
+    _dev_tensor(scales, "scales", (torch.uint8,), 4, h.device)
+    _dev_tensor(gscale, "gscale", (torch.float32,), 1, h.device)
+    m, k = h.shape
+    r, half = Wq.shape
+    if k != 2 * half:
+        raise ValueError("Wq must be [R, K / 2] for h [M, K]")
+    if tuple(scales.shape) != nvfp4_scale_shape(r, k):
+        raise ValueError("scales must have shape nvfp4_scale_shape(R, K) (the tiled layout)")
+    _d2t(d2t, r, h.device, "Wq")
+    return m, k, r
+
+
+def draft_project_argmax_nvfp4(h: torch.Tensor, Wq: torch.Tensor, scales: torch.Tensor, gscale: torch.Tensor,
+                               d2t: torch.Tensor | None = None, path: int = LMH_PATH_AUTO,
+                               out_id: torch.Tensor | None = None, out_logit: torch.Tensor | None = None,
+                               workspace: torch.Tensor | None = None, stream=None):
+    """(out_id int32 [M], out_logit float32 [M]) for the best row of the
+    dequantized NVFP4 head per hidden row, mapped through d2t.  Never
+    synchronizes."""
+    m, k, r = _check_nv4_head(h, Wq, scales, gscale, d2t)
+    out_id, out_logit = _outputs(m, out_id, out_logit, h.device)
+    st = _stream(stream, h.device)
+    workspace = _workspace(workspace, h.device, st)
+    _check(lib().draft_project_argmax_nvfp4(
+        h.data_ptr(), m, k, Wq.data_ptr(), scales.data_ptr(), gscale.data_ptr(), r,
+        d2t.data_ptr() if d2t is not None else None, out_id.data_ptr(), out_logit.data_ptr(),
+        workspace.data_ptr(), _nbytes(workspace), path, st), "draft_project_argmax_nvfp4")
+    return out_id, out_logit
+
+
+def draft_project_topk_nvfp4(h: torch.Tensor, Wq: torch.Tensor, scales: torch.Tensor, gscale: torch.Tensor,
+                             d2t: torch.Tensor | None, topk: int, out_id: torch.Tensor | None = None,
+                             out_logit: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
+                             path: int = LMH_PATH_AUTO, stream=None):
+    """(ids int32 [M, topk], logits float32 [M, topk]): the topk best rows of
+    the dequantized NVFP4 head per hidden row, best first, mapped through
+    d2t.  Never synchronizes."""
+    m, k, r = _check_nv4_head(h, Wq, scales, gscale, d2t)
+    out_id, out_logit, workspace = _topk_io(m, topk, out_id, out_logit, workspace, h.device)
+    _check(lib().draft_project_topk_nvfp4(
+        h.data_ptr(), m, k, Wq.data_ptr(), scales.data_ptr(), gscale.data_ptr(), r,
+        d2t.data_ptr() if d2t is not None else None, topk, out_id.data_ptr(), out_logit.data_ptr(),
+        workspace.data_ptr(), _nbytes(workspace), path, _stream(stream, h.device)), "draft_project_topk_nvfp4")
+    return out_id, out_logit
+
+
+def lmhead_bench_time_argmax_nvfp4(h: torch.Tensor, heads: list, d2t: torch.Tensor | None, path: int,
+                                   calls: int, out_id: torch.Tensor, out_logit: torch.Tensor,
+                                   workspace: torch.Tensor, stream=None) -> float:
+    """lmhead_bench_time_argmax over NVFP4 heads: `heads` is a list of
+    (Wq, scales, gscale) triples.  Synchronizes."""
+    if not heads:
+        raise ValueError("at least one head")
+    m, k, r = _check_nv4_head(h, heads[0][0], heads[0][1], heads[0][2], d2t)
+    for wq, sc, gs in heads:
+        _check_nv4_head(h, wq, sc, gs, None)
+        if wq.shape[0] != r:
+            raise ValueError("every head must have the same shape")
+    out_id, out_logit = _outputs(m, out_id, out_logit, h.device)
+    st = _stream(stream, h.device)
+    workspace = _workspace(workspace, h.device, st)
+    qp = (ctypes.c_void_p * len(heads))(*[t[0].data_ptr() for t in heads])
+    sp = (ctypes.c_void_p * len(heads))(*[t[1].data_ptr() for t in heads])
+    gp = (ctypes.c_void_p * len(heads))(*[t[2].data_ptr() for t in heads])
+    out = ctypes.c_double(0.0)
+    _check(lib().lmhead_bench_time_argmax_nvfp4(
+        h.data_ptr(), m, k, qp, sp, gp, len(heads), r, d2t.data_ptr() if d2t is not None else None,
+        out_id.data_ptr(), out_logit.data_ptr(), workspace.data_ptr(), _nbytes(workspace), path, calls,
+        ctypes.byref(out), st), "lmhead_bench_time_argmax_nvfp4")
+    return out.value
+
+
+# --------------------------------------------------------------------------
+# single-launch argmax (measurement)
+# --------------------------------------------------------------------------
+
+def lmhead_bench_onepass_workspace(device=None, M: int = LMH_MAX_M) -> torch.Tensor:
+    """A zeroed workspace for lmhead_bench_argmax_onepass (its ticket must
+    start at zero; every call leaves it zero)."""
+    nbytes = int(lib().lmhead_bench_onepass_workspace_bytes(M))
+    return torch.zeros(nbytes, dtype=torch.uint8, device=device or "cuda")
+
+
+def lmhead_bench_argmax_onepass(h: torch.Tensor, W: torch.Tensor, d2t: torch.Tensor | None, path: int,
+                                workspace: torch.Tensor, out_id: torch.Tensor | None = None,
+                                out_logit: torch.Tensor | None = None, stream=None):
+    """draft_project_argmax_path in one kernel launch (the last workgroup
+    folds); `workspace` from lmhead_bench_onepass_workspace.  Never
+    synchronizes."""
+    m, k, r = _check_hw(h, W, d2t)
+    out_id, out_logit = _outputs(m, out_id, out_logit, h.device)
+    _dev_tensor(workspace, "workspace", None, None, h.device)
+    _check(lib().lmhead_bench_argmax_onepass(
+        h.data_ptr(), m, k, W.data_ptr(), r, d2t.data_ptr() if d2t is not None else None, out_id.data_ptr(),
+        out_logit.data_ptr(), workspace.data_ptr(), _nbytes(workspace), path, _stream(stream, h.device)),
+        "lmhead_bench_argmax_onepass")
+    return out_id, out_logit
+
+
+# --------------------------------------------------------------------------
+# argmax keys of a head slice (vocabulary-parallel split)
+# --------------------------------------------------------------------------
+
+def draft_project_argmax_keys(h: torch.Tensor, W: torch.Tensor, row_base: int = 0, path: int = LMH_PATH_AUTO,
+                              out_key: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
+                              stream=None) -> torch.Tensor:
+    """int64 [M] packed keys (ordered logit << 32 | ~(row_base + row)) of
+    the slice W's argmax per hidden row; the maximum over the slices' keys
+    (compared as unsigned 64-bit) is the whole head's.  Never synchronizes."""
+    m, k, r = _check_hw(h, W, None)
+    if out_key is None:
+        out_key = torch.empty(m, dtype=torch.int64, device=h.device)
+    _dev_tensor(out_key, "out_key", (torch.int64,), 1, h.device)
+    if out_key.shape[0] < m:
+        raise ValueError("out_key must hold M entries")
+    st = _stream(stream, h.device)
+    workspace = _workspace(workspace, h.device, st)
+    _check(lib().draft_project_argmax_keys(h.data_ptr(), m, k, W.data_ptr(), r, row_base, out_key.data_ptr(),
+                                           workspace.data_ptr(), _nbytes(workspace), path, st),
+           "draft_project_argmax_keys")
+    return out_key
+
