@@ -108,8 +108,24 @@ def describe(a, synth, L):
         by_rows = not (a.indexed or a.topk or a.logits)
         chosen = (path if path != L.LMH_PATH_AUTO else
                   L.draft_project_auto_path_rows(m, c.k, rows_now) if by_rows else L.draft_project_auto_path(m, c.k))
+    if a.rows:
+        if ids is not None and not a.full:
+            raise SystemExit("bench.py: --rows slices the full head: use --config 2, or --full")
+        if quantized or a.indexed or a.topk or a.logits or a.onepass:
+            raise SystemExit("bench.py: --rows times the bf16 argmax keys of a head slice")
+        if not 1 <= a.rows <= c.n:
+            raise SystemExit(f"bench.py: --rows must be 1..{c.n}")
+        chosen = path if path != L.LMH_PATH_AUTO else L.draft_project_auto_path_rows(m, c.k, a.rows)
     kpath = {L.LMH_PATH_VALU: "valu", L.LMH_PATH_MFMA: "mfma"}[chosen]
-    if trimmed:
+    if a.rows:
+        rows = a.rows
+        copies = max(1, -(-2 * MALL_BYTES // weight_bytes(rows, c.k)) + 1) if weight_bytes(rows, c.k) < 2 * MALL_BYTES \
+            else 1
+        workload = (f"vocab shard: M={m} K={c.k} rows 0..{rows - 1} of the N={c.n} head, argmax keys "
+                    f"({copies} rotated copies)")
+        trimmed = False
+        ids = None
+    elif trimmed:
         rows = ids.size
         copies = max(1, -(-2 * MALL_BYTES // weight_bytes(rows, c.k)) + 1)
         workload = f"{c.name}: M={m} K={c.k} trimmed to {rows} rows ({copies} rotated copies)"
@@ -378,6 +394,15 @@ def main() -> int:
                     help="time draft_project_logits instead of the argmax: every logit as [M, R] (rows), "
                          "or scattered through d2t into [M, N] with -inf elsewhere (vocab; the full head "
                          "takes d2t = 0..N-1); bf16 heads; whole calls only")
+    ap.add_argument("--sweep-m", default="",
+                    help="comma-separated hidden-row counts: time the projection kernel of the argmax on "
+                         "both kernels (VALU where it takes the shape, matrix cores) at each, on this "
+                         "workload's head, one JSON line per (M, kernel); for locating the crossover under "
+                         "rocprofv3")
+    ap.add_argument("--rows", type=int, default=0,
+                    help="time draft_project_argmax_keys over the first ROWS rows of the full head (one GPU's "
+                         "share of a vocabulary split: 124160 at 2 GPUs, 31040 at 8), rotating copies past "
+                         "the Infinity Cache")
     ap.add_argument("--onepass", action="store_true",
                     help="time the argmax as one launch per call (lmhead_bench_argmax_onepass: the last "
                          "workgroup folds) instead of the projection + fold pair; bf16 heads; whole calls only")
@@ -427,7 +452,13 @@ def main() -> int:
     # writable copies: the seeded arrays are read-only and torch.from_numpy wants a writable buffer
     w_full = torch.from_numpy(np.array(w_np.view(np.int16))).to(dev)
     h = torch.from_numpy(np.array(h_np.view(np.int16))).to(dev)
-    if a.indexed:
+    if a.rows:
+        d2t = None
+        heads = [w_full[:rows].clone() for _ in range(d["copies"])] if d["copies"] > 1 else [w_full[:rows]]
+        if d["copies"] > 1:
+            del w_full
+        out_key = torch.empty(m, dtype=torch.int64, device=dev)
+    elif a.indexed:
         d2t = torch.from_numpy(ids.astype(np.int32)).to(dev)
         heads = [w_full] + [w_full.clone() for _ in range(d["copies"] - 1)]
     elif trimmed:
@@ -461,6 +492,28 @@ def main() -> int:
     torch.cuda.synchronize()
 
     ws = L.new_workspace(dev)
+    if a.sweep_m:
+        if d["fmt"] != "bf16" or a.indexed or a.topk or a.logits or a.onepass or a.rows:
+            raise SystemExit("bench.py: --sweep-m times the bf16 argmax over a full or trimmed head")
+        stream = torch.cuda.current_stream(dev)
+        for ms in [int(x) for x in a.sweep_m.split(",")]:
+            hm = torch.from_numpy(np.array(synth.hidden(c.h_seed[0] + 97, 0, ms, c.k).view(np.int16))).to(dev)
+            oid = torch.empty(ms, dtype=torch.int32, device=dev)
+            olg = torch.empty(ms, dtype=torch.float32, device=dev)
+            for pname, pv in (("valu", L.LMH_PATH_VALU), ("mfma", L.LMH_PATH_MFMA)):
+                if pv == L.LMH_PATH_VALU and not (ms <= 8 and ms * ((c.k // 8 + 63) // 64) <= 40):
+                    continue
+                L.lmhead_bench_time_argmax(hm, heads, d2t, pv, max(1, a.warmup), oid, olg, ws, stream)
+                t = [L.lmhead_bench_time_argmax(hm, heads, d2t, pv, a.steps, oid, olg, ws, stream)
+                     for _ in range(max(1, a.repeats))]
+                print(json.dumps({"mode": "kernel sweep", "workload": workload, "M": ms, "path": pname,
+                                  "kernel": kernel_name(pname, ms), "rows": rows,
+                                  "auto_path": {L.LMH_PATH_VALU: "valu", L.LMH_PATH_MFMA: "mfma"}[
+                                      L.draft_project_auto_path_rows(ms, c.k, rows)],
+                                  "kernel_avg_us": round(float(np.median(t)) * 1e3, 2),
+                                  "spread_us": [round(min(t) * 1e3, 2), round(max(t) * 1e3, 2)],
+                                  "launches": a.steps, "regions": len(t)}), flush=True)
+        return 0
     out_id = torch.empty(m, dtype=torch.int32, device=dev)
     out_logit = torch.empty(m, dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream(dev)
@@ -483,7 +536,9 @@ def main() -> int:
         op_ws = L.lmhead_bench_onepass_workspace(dev, m)
 
     def step(i):
-        if a.onepass:
+        if a.rows:
+            L.draft_project_argmax_keys(h, heads[i % len(heads)], 0, path, out_key, ws, launch_on[0])
+        elif a.onepass:
             L.lmhead_bench_argmax_onepass(h, heads[i % len(heads)], d2t, path, op_ws, out_id, out_logit, launch_on[0])
         elif a.topk:
             if a.fp8:
@@ -612,18 +667,23 @@ def main() -> int:
     traffic = measured_traffic(kpath, workload)
     extra = {}
     if a.stream_read:
+        # the plain streaming read over the same head bytes (codes only for a
+        # quantized head), rotating through the same copies as the calls
         sink = torch.zeros(L.lmhead_bench_sink_words(), dtype=torch.int32, device=dev)
-        buf = heads[0][0] if d["fmt"] != "bf16" else heads[0]
-        for _ in range(3):
-            L.lmhead_bench_stream_read(buf, sink)
+        bufs = [hd[0] if d["fmt"] != "bf16" else hd for hd in heads]
+        n_sr = 20 * len(bufs)
+        for i in range(3):
+            L.lmhead_bench_stream_read(bufs[i % len(bufs)], sink)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(stream)
-        for _ in range(20):
-            L.lmhead_bench_stream_read(buf, sink)
+        for i in range(n_sr):
+            L.lmhead_bench_stream_read(bufs[i % len(bufs)], sink)
         e1.record(stream)
         torch.cuda.synchronize()
-        nb = buf.numel() * buf.element_size()
-        extra["stream_read_gbps"] = round(nb / (e0.elapsed_time(e1) / 20 / 1e3) / 1e9, 1)
+        nb = bufs[0].numel() * bufs[0].element_size()
+        sr_us = e0.elapsed_time(e1) / n_sr * 1e3
+        extra["stream_read"] = {"bytes": nb, "us": round(sr_us, 2), "gbps": round(nb / (sr_us / 1e6) / 1e9, 1),
+                                "copies": len(bufs)}
 
     if a.calibrate:
         nb = 1 << 30
@@ -678,7 +738,7 @@ def main() -> int:
         if a.indexed:
             result["cpu_baseline"] = cpu_baseline(hb, w_np, ids, a.cpu_seconds, indexed=True)
         else:
-            wb = w_np[ids] if trimmed else w_np
+            wb = w_np[ids] if trimmed else (w_np[:rows] if a.rows else w_np)
             result["cpu_baseline"] = cpu_baseline(hb, wb, ids if trimmed else None, a.cpu_seconds)
     print(json.dumps(result), flush=True)
     return 0

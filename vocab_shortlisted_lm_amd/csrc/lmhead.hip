@@ -1842,7 +1842,6 @@ proj_mfma(const uint16_t* __restrict__ h, const void* __restrict__ Wv, const voi
   constexpr int LPB = 16 / RPI;     // load instructions per batch
   const uint8_t* W = static_cast<const uint8_t*>(Wv);
   extern __shared__ u32x4 lds[];  // [mp][row_chunks] hidden rows, then [WV][16][SC] stages
-  __shared__ unsigned long long s_key[TK == 1 && !LOGITS ? WV : 1][32];
   const int lane = threadIdx.x & 63;
   const int wave = wave_id();
   const int i16 = lane & 15;
@@ -2008,10 +2007,13 @@ proj_mfma(const uint16_t* __restrict__ h, const void* __restrict__ Wv, const voi
       return fp8x8_to_bf16x8(raw.x, raw.y);
     } else if constexpr (NV4) {
       // the lane's 8 codes (elements 8 g .. 8 g + 7 of the k-step) share the
-      // block scale of block 2 sb + g / 2
+      // block scale of block 2 sb + g / 2: both of the k-step's scale codes
+      // are read as one 16-bit word and decoded by the gfx950 E4M3
+      // conversion (scale 1: exact)
       const uint32_t codes = reinterpret_cast<const uint32_t*>(stage)[(i16 * SC + sb) * 4 + g];
-      const uint32_t e = reinterpret_cast<const uint8_t*>(sstage)[i16 * 32 + 2 * sb + (g >> 1)];
-      return fp4x8_times_scale_to_bf16x8(codes, e4m3_to_f32(e));
+      const uint32_t pair = reinterpret_cast<const uint16_t*>(sstage)[i16 * 16 + sb];
+      const auto sc2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(pair, 1.0f, false);
+      return fp4x8_times_scale_to_bf16x8(codes, (g >> 1) ? sc2[1] : sc2[0]);
     } else if constexpr (MX4) {
       const uint32_t codes = reinterpret_cast<const uint32_t*>(stage)[(i16 * SC + sb) * 4 + g];
       const uint32_t e = reinterpret_cast<const uint8_t*>(sstage)[i16 * 16 + sb];
@@ -2186,6 +2188,11 @@ proj_mfma(const uint16_t* __restrict__ h, const void* __restrict__ Wv, const voi
   if constexpr (LOGITS) {
     return;
   } else if constexpr (TK == 1) {
+    // the waves' keys go to the stage area once every wave is past its main
+    // loop (a static array there would cost the LDS that lets 24 hidden rows
+    // of an NVFP4 head run 8-wave workgroups)
+    __syncthreads();
+    unsigned long long (*s_key)[32] = reinterpret_cast<unsigned long long (*)[32]>(lds + mp * row_chunks);
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
       unsigned long long k = pack_key(best[nt], bidx[nt]);
@@ -2533,11 +2540,11 @@ size_t mfma_stage_bytes(int waves, int fmt) {
 }
 
 // Hidden rows one launch of the matrix-core kernel can stage for K with
-// `waves` waves (each with its own stages); the static key array of the
-// argmax epilogue is counted too.
+// `waves` waves (each with its own stages; the epilogues reuse the stage
+// area), with 512 bytes to spare.
 int mfma_lds_rows_fit(int64_t K, int waves, int fmt = kFmtBf16) {
   const int64_t stage = (int64_t)mfma_stage_bytes(waves, fmt);
-  const int64_t fixed = stage + (int64_t)waves * 32 * 8 + 512;
+  const int64_t fixed = stage + 512;
   const int64_t rows = (kLdsPerWorkgroup - fixed) / mfma_row_bytes(K);
   return (int)std::max<int64_t>(0, std::min<int64_t>(LMH_MAX_M, rows));
 }

@@ -33,7 +33,9 @@ __all__ = [
     "lmhead_bench_onepass_workspace", "lmhead_bench_argmax_onepass", "draft_project_argmax_keys",
 ]
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "liblmhead.so")
+# The in-tree build; LMHEAD_LIB names another build of the same source to load
+# instead (the host-sanitizer build the CPU tests run under).
+LIB_PATH = os.environ.get("LMHEAD_LIB") or os.path.join(os.path.dirname(os.path.abspath(__file__)), "liblmhead.so")
 
 LMH_OK, LMH_EINVAL, LMH_ERANGE, LMH_EWORKSPACE, LMH_EHIP = 0, 1, 2, 3, 4
 LMH_MAX_M, LMH_MIN_K, LMH_MAX_K, LMH_MAX_TOPK = 32, 8, 8192, 16
@@ -951,4 +953,5 @@ def draft_project_argmax_keys(h: torch.Tensor, W: torch.Tensor, row_base: int = 
                                            workspace.data_ptr(), _nbytes(workspace), path, st),
            "draft_project_argmax_keys")
     return out_key
+
 
