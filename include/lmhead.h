@@ -141,6 +141,31 @@ int draft_project_argmax(const uint16_t* h, int64_t M, int64_t K,
                          void* stream);
 
 /*
+ * draft_project_argmax_noalloc -- draft_project_argmax for callers that
+ * cannot allocate device memory or hold a workspace: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation.  Same
+ * operation, outputs, kernels and errors as draft_project_argmax (library's
+ * own kernel choice), without the workspace arguments: the per-workgroup
+ * key slots live in a static array in the library's device memory (256 KiB
+ * per GPU, held until the process ends), whose address on each device is
+ * looked up once, on the first call on that device.
+ *
+ *  M          1 .. LMH_NOALLOC_MAX_M (= LMH_MAX_M, the rows the array holds);
+ *             more is LMH_EINVAL.
+ * Never allocates and never synchronizes.  The array is shared by every
+ * call on the device and its contents on entry do not matter (nothing in it
+ * needs clearing), but calls that may overlap on one GPU -- on different
+ * streams, or from several threads without ordering -- race on it: order
+ * them on one stream, or use draft_project_argmax with separate workspaces.
+ */
+#define LMH_NOALLOC_MAX_M LMH_MAX_M
+int draft_project_argmax_noalloc(const uint16_t* h, int64_t M, int64_t K,
+                                 const uint16_t* W, int64_t R,
+                                 const int32_t* d2t,
+                                 int32_t* out_id, float* out_logit,
+                                 void* stream);
+
+/*
  * draft_project_argmax_keys -- the argmax of one slice of a head, as keys
  * that combine across slices: the unit of work of one GPU when the head is
  * split by vocabulary rows across GPUs, as a tensor-parallel lm_head is

@@ -427,3 +427,17 @@ def test_row_bound_is_below_two_to_the_thirty(L):
     assert lib.draft_project_auto_path_rows(1, 2560, big) == -1
     assert lib.draft_project_auto_path_rows(1, 2560, big - 1) in (1, 2)
 
+
+def test_noalloc_rejects_on_host(L):
+    """The allocation-free argmax checks its arguments before it looks up
+    its scratch array or launches anything."""
+    f = L.lib().draft_project_argmax_noalloc
+    assert L.LMH_NOALLOC_MAX_M == L.LMH_MAX_M
+    assert f(A, 33, 2560, B, 100, None, C, D, None) == 1          # M above the array's rows
+    assert f(A, 0, 2560, B, 100, None, C, D, None) == 1
+    assert f(A, 2, 2560, B, 0, None, C, D, None) == 1             # R = 0
+    assert f(A, 2, 2560, B, 1 << 30, None, C, D, None) == 1
+    assert f(A, 2, 2564, B, 100, None, C, D, None) == 1           # K % 8
+    assert f(A + 2, 2, 2560, B, 100, None, C, D, None) == 1       # h misaligned
+    assert f(A, 2, 2560, B, 100, None, None, D, None) == 1
+    assert f(A, 2, 2560, B, 100, None, C, None, None) == 1

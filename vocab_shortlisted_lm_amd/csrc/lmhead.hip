@@ -2887,6 +2887,40 @@ int run_topk(const Call& c, const Epi& epi, int64_t topk, int32_t* out_id, float
 
 }  // namespace
 
+// Scratch of the allocation-free argmax (draft_project_argmax_noalloc): the
+// per-workgroup key slots of up to LMH_MAX_M hidden rows, 256 KiB, in the
+// library's own device memory.  Each GPU the library runs on holds its own
+// copy until the process ends.  Host code never passes this name to a kernel
+// (on the host it is only a handle): scratch_on_device() asks the runtime
+// for the address on the current device once and keeps it.
+static __device__ __align__(256) unsigned long long scratch[LMH_MAX_M * kMaxGrid];
+
+namespace {
+
+std::mutex g_scratch_mu;
+std::vector<std::pair<int, void*>> g_scratch_ptrs;  // (device, address of `scratch` there)
+
+int scratch_on_device(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  for (const auto& dp : g_scratch_ptrs)
+    if (dp.first == dev) {
+      *out = dp.second;
+      return LMH_OK;
+    }
+  void* p = nullptr;
+  e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+  if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+  if (!p) return hip_fail(hipErrorInvalidSymbol, "hipGetSymbolAddress(scratch)");
+  g_scratch_ptrs.emplace_back(dev, p);
+  *out = p;
+  return LMH_OK;
+}
+
+}  // namespace
+
 // ---------------------------------------------------------------------------
 // C ABI
 // ---------------------------------------------------------------------------
@@ -3265,6 +3299,20 @@ int draft_project_argmax_keys(const uint16_t* h, int64_t M, int64_t K, const uin
   c.out_key = reinterpret_cast<unsigned long long*>(out_key);
   const Epi epi{static_cast<unsigned long long*>(workspace), nullptr, nullptr, 0, 0};
   return run<3, 1>(c, epi, 1, nullptr, nullptr);
+}
+
+int draft_project_argmax_noalloc(const uint16_t* h, int64_t M, int64_t K, const uint16_t* W, int64_t R,
+                                 const int32_t* d2t, int32_t* out_id, float* out_logit, void* stream) {
+  int path = LMH_PATH_AUTO;
+  int st = check_common(h, M, K, W, R, 0, &path);
+  if (st != LMH_OK) return st;
+  if (M > LMH_NOALLOC_MAX_M) return LMH_EINVAL;  // the scratch holds LMH_NOALLOC_MAX_M rows of slots
+  if (!out_id || !out_logit) return LMH_EINVAL;
+  void* slots = nullptr;
+  if ((st = scratch_on_device(&slots)) != LMH_OK) return st;
+  const Call c{h, (int)M, (int)K, W, (int)R, d2t, path, static_cast<hipStream_t>(stream)};
+  const Epi epi{static_cast<unsigned long long*>(slots), nullptr, nullptr, 0, 0};
+  return run<0, 1>(c, epi, 1, out_id, out_logit);
 }
 
 size_t lmhead_bench_onepass_workspace_bytes(int64_t M) {

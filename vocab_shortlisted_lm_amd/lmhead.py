@@ -16,7 +16,7 @@ import torch
 
 __all__ = [
     "LmheadError", "lib", "LMH_OK", "LMH_EINVAL", "LMH_ERANGE", "LMH_EWORKSPACE",
-    "LMH_EHIP", "LMH_MAX_M", "LMH_MIN_K", "LMH_MAX_K", "LMH_MAX_R", "LMH_PATH_AUTO", "LMH_PATH_VALU",
+    "LMH_EHIP", "LMH_MAX_M", "LMH_MIN_K", "LMH_MAX_K", "LMH_MAX_R", "LMH_NOALLOC_MAX_M", "LMH_PATH_AUTO", "LMH_PATH_VALU",
     "LMH_PATH_MFMA", "lmhead_trim", "draft_project_workspace_bytes", "draft_project_argmax",
     "draft_project_argmax_path", "draft_project_auto_path", "draft_project_auto_path_rows", "lmhead_status_str",
     "lmhead_last_error", "lmhead_bench_sink_words", "lmhead_bench_stream_read",
@@ -31,6 +31,7 @@ __all__ = [
     "lmhead_quantize_nvfp4", "lmhead_nvfp4_scale_bytes", "lmhead_nvfp4_tile_scales", "nvfp4_scale_shape",
     "draft_project_argmax_nvfp4", "draft_project_topk_nvfp4", "lmhead_bench_time_argmax_nvfp4",
     "lmhead_bench_onepass_workspace", "lmhead_bench_argmax_onepass", "draft_project_argmax_keys",
+    "draft_project_argmax_noalloc",
 ]
 
 # The in-tree build; LMHEAD_LIB names another build of the same source to load
@@ -40,6 +41,7 @@ LIB_PATH = os.environ.get("LMHEAD_LIB") or os.path.join(os.path.dirname(os.path.
 LMH_OK, LMH_EINVAL, LMH_ERANGE, LMH_EWORKSPACE, LMH_EHIP = 0, 1, 2, 3, 4
 LMH_MAX_M, LMH_MIN_K, LMH_MAX_K, LMH_MAX_TOPK = 32, 8, 8192, 16
 LMH_MAX_R = (1 << 30) - 1
+LMH_NOALLOC_MAX_M = LMH_MAX_M
 LMH_PATH_AUTO, LMH_PATH_VALU, LMH_PATH_MFMA = 0, 1, 2
 LMH_MAX_OVERWRITE, LMH_MAX_UNION_VOCAB = 65536, 524288
 
@@ -92,6 +94,7 @@ SIGNATURES = {
                                               _INT, ctypes.POINTER(ctypes.c_double), _P]),
     "lmhead_bench_onepass_workspace_bytes": (_SZ, [_I64]),
     "draft_project_argmax_keys": (_INT, [_P, _I64, _I64, _P, _I64, _I64, _P, _P, _SZ, _INT, _P]),
+    "draft_project_argmax_noalloc": (_INT, [_P, _I64, _I64, _P, _I64, _P, _P, _P, _P]),
     "lmhead_bench_argmax_onepass": (_INT, [_P, _I64, _I64, _P, _I64, _P, _P, _P, _P, _SZ, _INT, _P]),
 }
 
@@ -955,3 +958,17 @@ def draft_project_argmax_keys(h: torch.Tensor, W: torch.Tensor, row_base: int = 
     return out_key
 
 
+
+def draft_project_argmax_noalloc(h: torch.Tensor, W: torch.Tensor, d2t: torch.Tensor | None = None,
+                                 out_id: torch.Tensor | None = None, out_logit: torch.Tensor | None = None,
+                                 stream=None):
+    """draft_project_argmax with no workspace: the library's own static
+    device array holds the per-workgroup keys.  Calls that may overlap on one
+    GPU race on that array.  Never synchronizes; the library allocates
+    nothing (outputs are allocated here only when not given)."""
+    m, k, r = _check_hw(h, W, d2t)
+    out_id, out_logit = _outputs(m, out_id, out_logit, h.device)
+    _check(lib().draft_project_argmax_noalloc(
+        h.data_ptr(), m, k, W.data_ptr(), r, d2t.data_ptr() if d2t is not None else None, out_id.data_ptr(),
+        out_logit.data_ptr(), _stream(stream, h.device)), "draft_project_argmax_noalloc")
+    return out_id, out_logit
