@@ -111,7 +111,7 @@ def describe(a, synth, L):
     if a.rows:
         if ids is not None and not a.full:
             raise SystemExit("bench.py: --rows slices the full head: use --config 2, or --full")
-        if quantized or a.indexed or a.topk or a.logits or a.onepass:
+        if quantized or a.indexed or a.topk or a.logits or a.fused:
             raise SystemExit("bench.py: --rows times the bf16 argmax keys of a head slice")
         if not 1 <= a.rows <= c.n:
             raise SystemExit(f"bench.py: --rows must be 1..{c.n}")
@@ -141,8 +141,8 @@ def describe(a, synth, L):
         raise SystemExit("bench.py: --topk and --logits time trimmed or full heads, not --indexed")
     if a.logits and quantized:
         raise SystemExit("bench.py: --logits takes a bf16 head")
-    if a.onepass and (quantized or a.indexed or a.topk or a.logits):
-        raise SystemExit("bench.py: --onepass times the bf16 argmax over a full or trimmed head")
+    if a.fused and (quantized or a.indexed or a.topk or a.logits):
+        raise SystemExit("bench.py: --fused times the bf16 argmax over a full or trimmed head")
     if a.topk and not 1 <= a.topk <= L.LMH_MAX_TOPK:
         raise SystemExit(f"bench.py: --topk must be 1..{L.LMH_MAX_TOPK}")
     if a.indexed:
@@ -403,9 +403,10 @@ def main() -> int:
                     help="time draft_project_argmax_keys over the first ROWS rows of the full head (one GPU's "
                          "share of a vocabulary split: 124160 at 2 GPUs, 31040 at 8), rotating copies past "
                          "the Infinity Cache")
-    ap.add_argument("--onepass", action="store_true",
-                    help="time the argmax as one launch per call (lmhead_bench_argmax_onepass: the last "
-                         "workgroup folds) instead of the projection + fold pair; bf16 heads; whole calls only")
+    ap.add_argument("--fused", action="store_true",
+                    help="time the argmax as one launch per call (draft_project_argmax_fused: workgroups merge "
+                         "their keys with atomics, the last one writes the outputs) instead of the projection + "
+                         "fold pair; bf16 heads; whole calls only")
     ap.add_argument("--graph", action="store_true",
                     help="capture the --steps calls of a timed region in one HIP graph and time its replays "
                          "(the calls without the host's launch cost)")
@@ -493,7 +494,7 @@ def main() -> int:
 
     ws = L.new_workspace(dev)
     if a.sweep_m:
-        if d["fmt"] != "bf16" or a.indexed or a.topk or a.logits or a.onepass or a.rows:
+        if d["fmt"] != "bf16" or a.indexed or a.topk or a.logits or a.fused or a.rows:
             raise SystemExit("bench.py: --sweep-m times the bf16 argmax over a full or trimmed head")
         stream = torch.cuda.current_stream(dev)
         for ms in [int(x) for x in a.sweep_m.split(",")]:
@@ -532,14 +533,15 @@ def main() -> int:
         lg_out = torch.empty((m, lg_cols), dtype=torch.float32, device=dev)
         out_bytes = 4 * m * lg_cols
 
-    if a.onepass:
-        op_ws = L.lmhead_bench_onepass_workspace(dev, m)
+    if a.fused:
+        state = L.new_state(dev)
 
     def step(i):
         if a.rows:
             L.draft_project_argmax_keys(h, heads[i % len(heads)], 0, path, out_key, ws, launch_on[0])
-        elif a.onepass:
-            L.lmhead_bench_argmax_onepass(h, heads[i % len(heads)], d2t, path, op_ws, out_id, out_logit, launch_on[0])
+        elif a.fused:
+            L.draft_project_argmax_fused_path(h, heads[i % len(heads)], d2t, path, state, out_id, out_logit,
+                                              launch_on[0])
         elif a.topk:
             if a.fp8:
                 q, sc = heads[i % len(heads)]
@@ -618,10 +620,10 @@ def main() -> int:
         torch.cuda.synchronize()
         rates.append(a.steps / (e0.elapsed_time(e1) / 1e3))
 
-    if a.topk or a.logits or a.onepass:
+    if a.topk or a.logits or a.fused:
         # whole calls only: the kernel-only timer covers the argmax epilogue
         result = {
-            "mode": f"top-{a.topk}" if a.topk else (f"logits ({a.logits})" if a.logits else "argmax, single launch"),
+            "mode": f"top-{a.topk}" if a.topk else (f"logits ({a.logits})" if a.logits else "argmax, single launch (fused)"),
             "workload": workload, "M": m, "K": c.k, "rows": rows, "fmt": d["fmt"], "graph": a.graph,
             "steps": a.steps,
             "warmup": a.warmup, "us_per_call": round(ms_per_step * 1e3, 2),

@@ -141,6 +141,38 @@ int draft_project_argmax(const uint16_t* h, int64_t M, int64_t K,
                          void* stream);
 
 /*
+ * draft_project_argmax_fused -- draft_project_argmax as ONE kernel launch
+ * (per pass of hidden rows), with a small persistent state in place of the
+ * scratch workspace.  Same operation (see draft_project_argmax: the passages
+ * cited there), arguments, outputs, kernel choice and errors as
+ * draft_project_argmax, except:
+ *
+ *  state        LMH_STATE_BYTES bytes, 16-byte aligned, ALL ZERO before
+ *               the first call that uses it: zero it once when it is
+ *               allocated.  Every call leaves it all zero again (a call
+ *               whose kernel faulted does not).  Calls ordered on one stream
+ *               may share a state; calls that may run concurrently need
+ *               separate ones; nothing else may write it.
+ *  state_bytes  its size; a NULL or misaligned state, or a size below
+ *               LMH_STATE_BYTES, is LMH_EWORKSPACE.
+ *
+ * Never synchronizes and never allocates.  The projection kernel's
+ * workgroups merge their best keys into the state with 64-bit atomic
+ * maxima at agent scope, in two levels (16 groups of workgroups, then the
+ * groups), each level closed by a ticket (a relaxed atomic add taken only
+ * after the wave's maxima are acknowledged); the workgroup that takes the
+ * last ticket decodes the winners, maps them through d2t, writes the
+ * outputs and clears the state.  No fence, no fold kernel.
+ */
+#define LMH_STATE_BYTES 8192
+int draft_project_argmax_fused(const uint16_t* h, int64_t M, int64_t K,
+                               const uint16_t* W, int64_t R,
+                               const int32_t* d2t,
+                               int32_t* out_id, float* out_logit,
+                               void* state, size_t state_bytes,
+                               void* stream);
+
+/*
  * draft_project_argmax_noalloc -- draft_project_argmax for callers that
  * cannot allocate device memory or hold a workspace: code under HIP graph
  * capture, tight serving loops, harnesses that forbid allocation.  Same

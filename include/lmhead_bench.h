@@ -105,28 +105,17 @@ int lmhead_bench_time_argmax_indexed(const uint16_t* h, int64_t M, int64_t K,
                                      void* stream);
 
 /*
- * lmhead_bench_argmax_onepass: draft_project_argmax_path as ONE kernel
- *   launch per pass of hidden rows.  Every workgroup leaves its keys in its
- *   slots and takes a ticket with release ordering at agent scope; the
- *   workgroup with the last ticket acquires, folds every slot, maps the
- *   winner through d2t and writes out_id / out_logit, and resets the ticket.
- *   Against the default's second (fold) kernel this trades the kernel
- *   boundary for one L2 write-back and one atomic per workgroup, measured
- *   here; the default call does not depend on it.
- *   workspace: lmhead_bench_onepass_workspace_bytes(M) bytes, 16-byte
- *   aligned; its first 256 bytes hold the ticket, which must be ZERO before
- *   the first call on this workspace (every call leaves it zero again; a
- *   call that faulted does not), and the slots follow.  Calls sharing a workspace must be ordered
- *   on one stream.  Other arguments and errors as for
- *   draft_project_argmax_path.
+ * draft_project_argmax_fused_path: draft_project_argmax_fused with the
+ *   projection kernel chosen by `path` (LMH_PATH_VALU or LMH_PATH_MFMA; see
+ *   draft_project_argmax_path), so that both kernels' single-launch
+ *   epilogues can be checked and timed.
  */
-size_t lmhead_bench_onepass_workspace_bytes(int64_t M);
-int lmhead_bench_argmax_onepass(const uint16_t* h, int64_t M, int64_t K,
-                                const uint16_t* W, int64_t R,
-                                const int32_t* d2t,
-                                int32_t* out_id, float* out_logit,
-                                void* workspace, size_t workspace_bytes,
-                                int path, void* stream);
+int draft_project_argmax_fused_path(const uint16_t* h, int64_t M, int64_t K,
+                                    const uint16_t* W, int64_t R,
+                                    const int32_t* d2t,
+                                    int32_t* out_id, float* out_logit,
+                                    void* state, size_t state_bytes,
+                                    int path, void* stream);
 
 /*
  * lmhead_bench_time_argmax_nvfp4: the same over NVFP4 heads (draft_project_

@@ -77,6 +77,14 @@ def test_workspace_bytes(L):
         assert ws == m * 1024 * 8 and ws % 16 == 0
 
 
+def test_fused_state_size(L):
+    """The single-launch state holds the tickets and keys of 16 merge groups
+    and of the final level within LMH_STATE_BYTES."""
+    assert L.LMH_STATE_BYTES == 8192
+    src = open(os.path.join(ROOT, "include", "lmhead.h")).read()
+    assert "#define LMH_STATE_BYTES 8192" in src
+
+
 def test_auto_path_by_head_size(L):
     # four hidden rows: matrix cores below 131,072 head rows, VALU above
     assert L.draft_project_auto_path_rows(4, 2560, 32768) == L.LMH_PATH_MFMA
@@ -441,3 +449,22 @@ def test_noalloc_rejects_on_host(L):
     assert f(A + 2, 2, 2560, B, 100, None, C, D, None) == 1       # h misaligned
     assert f(A, 2, 2560, B, 100, None, None, D, None) == 1
     assert f(A, 2, 2560, B, 100, None, C, None, None) == 1
+
+
+def test_fused_rejects_on_host(L):
+    """The single-launch argmax checks its arguments, the state included,
+    before anything is launched."""
+    f = L.lib().draft_project_argmax_fused
+    g = L.lib().draft_project_argmax_fused_path
+    S = L.LMH_STATE_BYTES
+    assert f(A, 2, 2560, B, 100, None, C, D, None, S, None) == 3          # no state
+    assert f(A, 2, 2560, B, 100, None, C, D, E + 8, S, None) == 3         # misaligned state
+    assert f(A, 2, 2560, B, 100, None, C, D, E, S - 1, None) == 3         # state too small
+    assert f(A, 33, 2560, B, 100, None, C, D, E, S, None) == 1
+    assert f(A, 2, 2560, B, 0, None, C, D, E, S, None) == 1
+    assert f(A, 2, 2560, B, 1 << 30, None, C, D, E, S, None) == 1
+    assert f(A, 2, 2564, B, 100, None, C, D, E, S, None) == 1
+    assert f(A, 2, 2560, B, 100, None, None, D, E, S, None) == 1
+    assert f(A, 2, 2560, B, 100, None, C, None, E, S, None) == 1
+    assert g(A, 2, 2560, B, 100, None, C, D, E, S, 3, None) == 1          # no such path
+    assert g(A, 9, 2560, B, 100, None, C, D, E, S, L.LMH_PATH_VALU, None) == 1   # VALU argmax: M <= 8

@@ -648,9 +648,11 @@ __device__ __forceinline__ void publish_workgroup(unsigned long long key, int la
 // row whose id lies outside [0, nw) is never read and takes no part in the
 // result.
 //
-// Single launch (argmax only): with `ticket` set, the workgroup that takes
-// the last ticket folds every workgroup's slot, maps the winner through
-// fold_d2t and writes out_id / out_logit, so no fold kernel follows.
+// Single launch (argmax only): with `state` set, no slots are written:
+// every workgroup merges its keys into per-hidden-row keys in `state` and
+// takes a ticket; the workgroup with the last ticket maps the winners
+// through fold_d2t and writes out_id / out_logit, so no fold kernel
+// follows.
 struct Epi {
   unsigned long long* slots;
   float* logits;
@@ -659,55 +661,95 @@ struct Epi {
   int64_t ncols;
   const int32_t* rowmap = nullptr;
   int nw = 0;
-  unsigned int* ticket = nullptr;
+  char* state = nullptr;
   const int32_t* fold_d2t = nullptr;
   int32_t* out_id = nullptr;
   float* out_logit = nullptr;
 };
 
-// The single-launch hand-off, run by wave 0 of every workgroup after it has
-// stored its keys (lanes m < mcount, hidden rows m_base + m) into its slots.
-// Lane 0 takes a ticket with release ordering at agent scope: the compiler
-// writes the wave's stores back from this chiplet's L2 and waits for them
-// before the atomic, so a workgroup on any other chiplet that takes a later
-// ticket and then acquires sees them.  The workgroup with the last ticket
-// acquires (invalidating its L2's stale lines), folds the slots of every
-// hidden row -- lane m keeps row m's winner -- then lanes m < mcount decode,
-// map through d2t and store, and the ticket goes back to 0 for the next
-// launch on this workspace.
-__device__ __forceinline__ void fold_if_last(const Epi& e, int lane, int mcount, int m_base) {
+// Layout of the single-launch state (all of it zero between launches).
+// Workgroup b belongs to merge group b % kMergeGroups; each group has a
+// ticket and one key per hidden row, and the final level has the same.
+// Tickets sit 128 bytes apart (one L2 line each), so the groups' atomics
+// do not queue on one line.
+constexpr int kMergeGroups = 16;
+constexpr int kStateTicket = 0;                                   // final ticket
+constexpr int kStateGroupTickets = 128;                           // + 128 x group
+constexpr int kStateGroupKeys = kStateGroupTickets + 128 * kMergeGroups;   // [group][LMH_MAX_M]
+constexpr int kStateKeys = kStateGroupKeys + 8 * LMH_MAX_M * kMergeGroups; // [LMH_MAX_M]
+constexpr int kStateBytes = kStateKeys + 8 * LMH_MAX_M;
+static_assert(kStateBytes <= LMH_STATE_BYTES, "the state fits the size the header promises");
+
+// One level of the merge, run by wave 0: lane m < mcount merges `key` (for
+// hidden row m_base + m) into keys[m_base + m] with a 64-bit atomic max at
+// agent scope -- atomics of that scope on one location are coherent across
+// the chiplets with no L2 write-back, which is what a release fence would
+// cost every workgroup.  The wave waits until the memory system has
+// acknowledged every one of them, and only then lane 0 takes a ticket (a
+// relaxed atomic add, same scope): when a ticket is counted, the maxima of
+// its taker are in place.  (An agent-scope release on this target is that
+// same wait plus an L2 write-back, and the write-back only matters for
+// plain stores; here every write before the ticket is such an atomic.)
+// Returns whether this wave took the last of `count` tickets; that wave
+// then resets the ticket to 0.
+__device__ __forceinline__ bool merge_level(unsigned long long* keys, unsigned int* ticket, unsigned int count,
+                                            unsigned long long key, int lane, int mcount, int m_base) {
+  if (lane < mcount && key != 0ull)
+    (void)__hip_atomic_fetch_max(keys + m_base + lane, key, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
   unsigned int t = 0u;
-  if (lane == 0) t = __hip_atomic_fetch_add(e.ticket, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+  if (lane == 0) t = __hip_atomic_fetch_add(ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   t = (unsigned int)__builtin_amdgcn_readfirstlane((int)t);
-  if (t != gridDim.x - 1u) return;
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-  unsigned long long mine = 0ull;
-  for (int m = 0; m < mcount; ++m) {
-    const unsigned long long* row = e.slots + (size_t)(m_base + m) * kMaxGrid;
-    unsigned long long k = 0ull;
-    for (int i = lane; i < (int)gridDim.x; i += 64) k = max_u64(k, row[i]);
-#pragma unroll
-    for (int x = 32; x >= 1; x >>= 1) {
-      const uint32_t lo = (uint32_t)__shfl_xor((int)(uint32_t)k, x);
-      const uint32_t hi = (uint32_t)__shfl_xor((int)(uint32_t)(k >> 32), x);
-      k = max_u64(k, ((unsigned long long)hi << 32) | lo);
-    }
-    mine = lane == m ? k : mine;
-  }
+  if (t != count - 1u) return false;
+  if (lane == 0) __hip_atomic_store(ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return true;
+}
+
+// The last taker of a level reads the level's keys (agent-scope atomic
+// loads: every taker's maxima were acknowledged before its ticket) and puts
+// them back to 0 for the next launch on this state.
+__device__ __forceinline__ unsigned long long take_level_key(unsigned long long* keys, int lane, int mcount,
+                                                             int m_base) {
+  if (lane >= mcount) return 0ull;
+  unsigned long long* p = keys + m_base + lane;
+  const unsigned long long k = __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __hip_atomic_store(p, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return k;
+}
+
+// The single-launch hand-off, run by wave 0 of every workgroup in place of
+// publish_workgroup, with no fence.  Two levels, so that no location takes
+// more than about grid / 16 atomics: the workgroups of a merge group merge
+// into the group's keys; the last of each group merges the group's result
+// into the final keys; the last group's last workgroup decodes the final
+// keys, maps through d2t and stores the outputs.
+__device__ __forceinline__ void merge_and_fold_if_last(const Epi& e, unsigned long long key, int lane, int mcount,
+                                                       int m_base) {
+  const unsigned int grid = gridDim.x;
+  const unsigned int groups = grid < (unsigned)kMergeGroups ? grid : (unsigned)kMergeGroups;
+  const unsigned int x = blockIdx.x % (unsigned)kMergeGroups;
+  const unsigned int members = (grid - 1u - x) / (unsigned)kMergeGroups + 1u;
+  unsigned long long* gkeys = reinterpret_cast<unsigned long long*>(e.state + kStateGroupKeys) + x * LMH_MAX_M;
+  unsigned int* gticket = reinterpret_cast<unsigned int*>(e.state + kStateGroupTickets + 128 * x);
+  if (!merge_level(gkeys, gticket, members, key, lane, mcount, m_base)) return;
+  key = take_level_key(gkeys, lane, mcount, m_base);
+  unsigned long long* keys = reinterpret_cast<unsigned long long*>(e.state + kStateKeys);
+  unsigned int* ticket = reinterpret_cast<unsigned int*>(e.state + kStateTicket);
+  if (!merge_level(keys, ticket, groups, key, lane, mcount, m_base)) return;
+  key = take_level_key(keys, lane, mcount, m_base);
   if (lane < mcount) {
     const int m = m_base + lane;
-    if (mine == 0ull) {
+    if (key == 0ull) {
       e.out_id[m] = -1;
       e.out_logit[m] = __builtin_nanf("");
     } else {
       float v;
       int idx;
-      unpack_key(mine, v, idx);
+      unpack_key(key, v, idx);
       e.out_id[m] = e.fold_d2t ? e.fold_d2t[idx] : idx;
       e.out_logit[m] = v;
     }
   }
-  if (lane == 0) __hip_atomic_store(e.ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // Id of list entry r for an indexed kernel, as a plain (unconditional)
@@ -1254,8 +1296,10 @@ struct ValuEpilogue {
 #pragma unroll
         for (int w = 0; w < WV; ++w) key = s_key[w][lane] > key ? s_key[w][lane] : key;
       }
-      publish_workgroup(key, lane, M, 0, e.slots);
-      if (e.ticket) fold_if_last(e, lane, M, 0);
+      if (e.state)
+        merge_and_fold_if_last(e, key, lane, M, 0);
+      else
+        publish_workgroup(key, lane, M, 0, e.slots);
     } else {
       __shared__ unsigned long long s_list[WV * M * 16];
       const int rho = lane >> 4;
@@ -2209,8 +2253,10 @@ proj_mfma(const uint16_t* __restrict__ h, const void* __restrict__ Wv, const voi
 #pragma unroll
       for (int w = 0; w < WV; ++w) key = s_key[w][lane] > key ? s_key[w][lane] : key;
     }
-    publish_workgroup(key, lane, mp, m_base, epi.slots);
-    if (epi.ticket) fold_if_last(epi, lane, mp, m_base);
+    if (epi.state)
+      merge_and_fold_if_last(epi, key, lane, mp, m_base);
+    else
+      publish_workgroup(key, lane, mp, m_base, epi.slots);
   } else if constexpr (kColLists) {
     // every wave is past its main loop: the stage area is free for the lists
     __syncthreads();
@@ -2676,7 +2722,7 @@ int run(const Call& c, const Epi& epi, int topk, int32_t* out_id, float* out_log
   int st = cu_count(&cus);
   if (st != LMH_OK) return st;
   auto finalize = [&](int grid, int m_base, int mcount) -> int {
-    if (c.projection_only || epi.ticket) return LMH_OK;  // single launch: folded in the kernel
+    if (c.projection_only || epi.state) return LMH_OK;  // single launch: folded in the kernel
     if constexpr (MODE == 0)
       return launch_finalize_argmax(epi.slots, grid, m_base, mcount, c.d2t, out_id, out_logit, c.stream);
     else if constexpr (MODE == 1)
@@ -3315,28 +3361,27 @@ int draft_project_argmax_noalloc(const uint16_t* h, int64_t M, int64_t K, const 
   return run<0, 1>(c, epi, 1, out_id, out_logit);
 }
 
-size_t lmhead_bench_onepass_workspace_bytes(int64_t M) {
-  const size_t slots = draft_project_workspace_bytes(M);
-  return slots ? slots + 256 : 0;
-}
-
-int lmhead_bench_argmax_onepass(const uint16_t* h, int64_t M, int64_t K, const uint16_t* W, int64_t R,
-                                const int32_t* d2t, int32_t* out_id, float* out_logit, void* workspace,
-                                size_t workspace_bytes, int path, void* stream) {
+int draft_project_argmax_fused_path(const uint16_t* h, int64_t M, int64_t K, const uint16_t* W, int64_t R,
+                                    const int32_t* d2t, int32_t* out_id, float* out_logit, void* state,
+                                    size_t state_bytes, int path, void* stream) {
   int st = check_common(h, M, K, W, R, 0, &path);
   if (st != LMH_OK) return st;
   if (!out_id || !out_logit) return LMH_EINVAL;
-  if (!workspace || !aligned16(workspace)) return LMH_EWORKSPACE;
-  if (workspace_bytes < lmhead_bench_onepass_workspace_bytes(M)) return LMH_EWORKSPACE;
+  if (!state || !aligned16(state) || state_bytes < (size_t)LMH_STATE_BYTES) return LMH_EWORKSPACE;
   const Call c{h, (int)M, (int)K, W, (int)R, d2t, path, static_cast<hipStream_t>(stream)};
-  // the ticket first, at a place that does not depend on M (calls with any
-  // M may share the workspace), then the slots
-  Epi epi{reinterpret_cast<unsigned long long*>(static_cast<char*>(workspace) + 256), nullptr, nullptr, 0, 0};
-  epi.ticket = static_cast<unsigned int*>(workspace);
+  Epi epi{nullptr, nullptr, nullptr, 0, 0};
+  epi.state = static_cast<char*>(state);
   epi.fold_d2t = d2t;
   epi.out_id = out_id;
   epi.out_logit = out_logit;
   return run<0, 1>(c, epi, 1, out_id, out_logit);
+}
+
+int draft_project_argmax_fused(const uint16_t* h, int64_t M, int64_t K, const uint16_t* W, int64_t R,
+                               const int32_t* d2t, int32_t* out_id, float* out_logit, void* state,
+                               size_t state_bytes, void* stream) {
+  return draft_project_argmax_fused_path(h, M, K, W, R, d2t, out_id, out_logit, state, state_bytes,
+                                         LMH_PATH_AUTO, stream);
 }
 
 const char* lmhead_status_str(int status) {

@@ -30,7 +30,8 @@ __all__ = [
     "mxfp4_scale_shape", "draft_project_topk_fp8", "draft_project_topk_mxfp4", "PreparedArgmax",
     "lmhead_quantize_nvfp4", "lmhead_nvfp4_scale_bytes", "lmhead_nvfp4_tile_scales", "nvfp4_scale_shape",
     "draft_project_argmax_nvfp4", "draft_project_topk_nvfp4", "lmhead_bench_time_argmax_nvfp4",
-    "lmhead_bench_onepass_workspace", "lmhead_bench_argmax_onepass", "draft_project_argmax_keys",
+    "LMH_STATE_BYTES", "new_state", "draft_project_argmax_fused", "draft_project_argmax_fused_path",
+    "draft_project_argmax_keys",
     "draft_project_argmax_noalloc",
 ]
 
@@ -42,6 +43,7 @@ LMH_OK, LMH_EINVAL, LMH_ERANGE, LMH_EWORKSPACE, LMH_EHIP = 0, 1, 2, 3, 4
 LMH_MAX_M, LMH_MIN_K, LMH_MAX_K, LMH_MAX_TOPK = 32, 8, 8192, 16
 LMH_MAX_R = (1 << 30) - 1
 LMH_NOALLOC_MAX_M = LMH_MAX_M
+LMH_STATE_BYTES = 8192
 LMH_PATH_AUTO, LMH_PATH_VALU, LMH_PATH_MFMA = 0, 1, 2
 LMH_MAX_OVERWRITE, LMH_MAX_UNION_VOCAB = 65536, 524288
 
@@ -92,10 +94,10 @@ SIGNATURES = {
     "draft_project_topk_nvfp4": (_INT, [_P, _I64, _I64, _P, _P, _P, _I64, _P, _I64, _P, _P, _P, _SZ, _INT, _P]),
     "lmhead_bench_time_argmax_nvfp4": (_INT, [_P, _I64, _I64, _P, _P, _P, _INT, _I64, _P, _P, _P, _P, _SZ, _INT,
                                               _INT, ctypes.POINTER(ctypes.c_double), _P]),
-    "lmhead_bench_onepass_workspace_bytes": (_SZ, [_I64]),
     "draft_project_argmax_keys": (_INT, [_P, _I64, _I64, _P, _I64, _I64, _P, _P, _SZ, _INT, _P]),
     "draft_project_argmax_noalloc": (_INT, [_P, _I64, _I64, _P, _I64, _P, _P, _P, _P]),
-    "lmhead_bench_argmax_onepass": (_INT, [_P, _I64, _I64, _P, _I64, _P, _P, _P, _P, _SZ, _INT, _P]),
+    "draft_project_argmax_fused": (_INT, [_P, _I64, _I64, _P, _I64, _P, _P, _P, _P, _SZ, _P]),
+    "draft_project_argmax_fused_path": (_INT, [_P, _I64, _I64, _P, _I64, _P, _P, _P, _P, _SZ, _INT, _P]),
 }
 
 _lib = None
@@ -280,17 +282,25 @@ class PreparedArgmax:
     makes one C call per step; the tensors must keep their storage
     (no resize or reallocation) while it is used, and it holds references so
     they stay alive.  Calling it queues the step on the stream given here
-    and returns (out_id, out_logit)."""
+    and returns (out_id, out_logit).  Given a `state` (new_state), each step
+    is the single-launch draft_project_argmax_fused_path instead, and no
+    workspace is used."""
 
     def __init__(self, h: torch.Tensor, W: torch.Tensor, d2t: torch.Tensor | None = None,
                  path: int = LMH_PATH_AUTO, out_id: torch.Tensor | None = None,
-                 out_logit: torch.Tensor | None = None, workspace: torch.Tensor | None = None, stream=None):
+                 out_logit: torch.Tensor | None = None, workspace: torch.Tensor | None = None, stream=None,
+                 state: torch.Tensor | None = None):
         m, k, r = _check_hw(h, W, d2t)
         self.out_id, self.out_logit = _outputs(m, out_id, out_logit, h.device)
         st = _stream(stream, h.device)
-        self.workspace = _workspace(workspace, h.device, st)
+        if state is not None:
+            _check_state(state, h.device)
+            self.workspace = state
+            self._fn = lib().draft_project_argmax_fused_path
+        else:
+            self.workspace = _workspace(workspace, h.device, st)
+            self._fn = lib().draft_project_argmax_path
         self._keep = (h, W, d2t)
-        self._fn = lib().draft_project_argmax_path
         self._args = (h.data_ptr(), m, k, W.data_ptr(), r, d2t.data_ptr() if d2t is not None else None,
                       self.out_id.data_ptr(), self.out_logit.data_ptr(), self.workspace.data_ptr(),
                       _nbytes(self.workspace), path, st)
@@ -908,30 +918,42 @@ def lmhead_bench_time_argmax_nvfp4(h: torch.Tensor, heads: list, d2t: torch.Tens
 
 
 # --------------------------------------------------------------------------
-# single-launch argmax (measurement)
+# single-launch argmax
 # --------------------------------------------------------------------------
 
-def lmhead_bench_onepass_workspace(device=None, M: int = LMH_MAX_M) -> torch.Tensor:
-    """A zeroed workspace for lmhead_bench_argmax_onepass (its ticket must
-    start at zero; every call leaves it zero)."""
-    nbytes = int(lib().lmhead_bench_onepass_workspace_bytes(M))
-    return torch.zeros(nbytes, dtype=torch.uint8, device=device or "cuda")
+def new_state(device=None) -> torch.Tensor:
+    """A zeroed state for draft_project_argmax_fused (it must start at zero;
+    every call leaves it zero).  One per stream that calls concurrently."""
+    return torch.zeros(LMH_STATE_BYTES, dtype=torch.uint8, device=device or "cuda")
 
 
-def lmhead_bench_argmax_onepass(h: torch.Tensor, W: torch.Tensor, d2t: torch.Tensor | None, path: int,
-                                workspace: torch.Tensor, out_id: torch.Tensor | None = None,
-                                out_logit: torch.Tensor | None = None, stream=None):
-    """draft_project_argmax_path in one kernel launch (the last workgroup
-    folds); `workspace` from lmhead_bench_onepass_workspace.  Never
-    synchronizes."""
+def _check_state(state, device) -> None:
+    _dev_tensor(state, "state", (torch.uint8,), 1, device)
+    if state.numel() < LMH_STATE_BYTES:
+        raise ValueError(f"state must hold {LMH_STATE_BYTES} bytes")
+
+
+def draft_project_argmax_fused_path(h: torch.Tensor, W: torch.Tensor, d2t: torch.Tensor | None, path: int,
+                                    state: torch.Tensor, out_id: torch.Tensor | None = None,
+                                    out_logit: torch.Tensor | None = None, stream=None):
+    """draft_project_argmax_path in one kernel launch per pass: the
+    workgroups merge their keys into `state` (from new_state) with atomics
+    and the last one writes the outputs.  Never synchronizes."""
     m, k, r = _check_hw(h, W, d2t)
     out_id, out_logit = _outputs(m, out_id, out_logit, h.device)
-    _dev_tensor(workspace, "workspace", None, None, h.device)
-    _check(lib().lmhead_bench_argmax_onepass(
+    _check_state(state, h.device)
+    _check(lib().draft_project_argmax_fused_path(
         h.data_ptr(), m, k, W.data_ptr(), r, d2t.data_ptr() if d2t is not None else None, out_id.data_ptr(),
-        out_logit.data_ptr(), workspace.data_ptr(), _nbytes(workspace), path, _stream(stream, h.device)),
-        "lmhead_bench_argmax_onepass")
+        out_logit.data_ptr(), state.data_ptr(), _nbytes(state), path, _stream(stream, h.device)),
+        "draft_project_argmax_fused")
     return out_id, out_logit
+
+
+def draft_project_argmax_fused(h, W, d2t=None, state=None, out_id=None, out_logit=None, stream=None):
+    """draft_project_argmax_fused_path with the library's own kernel choice."""
+    if state is None:
+        raise ValueError("draft_project_argmax_fused needs a state (new_state) that persists across calls")
+    return draft_project_argmax_fused_path(h, W, d2t, LMH_PATH_AUTO, state, out_id, out_logit, stream)
 
 
 # --------------------------------------------------------------------------
