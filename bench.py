@@ -262,6 +262,30 @@ def record_traffic(a, d, fetch_csv: str, write_csv: str) -> int:
     return 0
 
 
+def traffic_table() -> int:
+    """profiles/traffic.json as a markdown table: per workload, the median
+    counter values per dispatch, the scaled HBM bytes of one projection
+    launch against the algorithmic bytes, and whether the entry was taken on
+    the kernel source as it stands."""
+    with open(TRAFFIC_FILE) as f:
+        table = json.load(f)
+    digest = source_digest()
+    print("| Workload | Kernel | FETCH_SIZE KiB | WRITE_SIZE KiB | HBM bytes (scaled) | Algorithmic bytes "
+          "| Excess | Current source |")
+    print("|---|---|---|---|---|---|---|---|")
+    for e in table.get("entries", []):
+        alg = e["algorithmic_bytes_projection_kernel"]
+        got = e["bytes_projection_kernel"]
+        print(f"| {e['workload']} | `{e['kernel']}` | {e['fetch_kib_per_dispatch']:,.1f} | "
+              f"{e['write_kib_per_dispatch']:,.1f} | {got:,} | {alg:,} | {100 * (got / alg - 1):+.3f}% | "
+              f"{'yes' if e['source_sha256_16'] == digest else 'no'} |")
+    e0 = (table.get("entries") or [{}])[0]
+    if e0:
+        print(f"\nScale factors from copy16 over 1 GiB in each run: FETCH_SIZE x {e0['fetch_scale']}, "
+              f"WRITE_SIZE x {e0['write_scale']}.")
+    return 0
+
+
 def blas_threads() -> dict:
     """The BLAS library numpy calls (name and version, from threadpoolctl)
     and the threads it runs: the cores the oracle's fp64 matrix products
@@ -413,6 +437,8 @@ def main() -> int:
     ap.add_argument("--shortlist-ops", action="store_true",
                     help="instead of the projection: time the list gathers, the device union of two lists "
                          "and 600 escaped ids written into spare rows (one JSON line)")
+    ap.add_argument("--traffic-table", action="store_true",
+                    help="no GPU: print profiles/traffic.json as a markdown table (one row per workload)")
     ap.add_argument("--record-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="no GPU: write this workload's entry of profiles/traffic.json from the "
                          "counter_collection.csv files of two rocprofv3 --pmc runs (FETCH_SIZE, "
@@ -424,6 +450,9 @@ def main() -> int:
               "(the projection shards by vocabulary rows with one small all-reduce, "
               "which is not built here)", file=sys.stderr)
         return 2
+
+    if a.traffic_table:
+        return traffic_table()
 
     import numpy as np
     import torch

@@ -4,6 +4,7 @@ committed HBM counters to the kernel code, and the counter bookkeeping
 (scaling by the copy kernel, lookup, staleness)."""
 import json
 import os
+import re
 import subprocess
 import sys
 
@@ -74,17 +75,24 @@ def test_digest_ignores_comments_and_whitespace_only(tmp_path, monkeypatch):
 
 def test_committed_counters_are_consistent_and_never_stale():
     """profiles/traffic.json: an entry taken on the kernel code as it stands
-    is reported by the benchmark line and shows W read once (within 1% of
-    the algorithmic bytes); an entry taken on other kernel code is never
-    reported (the line's `traffic` is then null, not an old figure)."""
+    is reported by the benchmark line and shows the head read once: at most
+    2% above the algorithmic bytes, beyond the hidden rows fetched once more
+    by each further chiplet's L2 (7 x M x K x 2 bytes) and one 32-byte write
+    per key slot (M x 1,024 x 32 bytes at most).  A second read of the head
+    would add 100%.  An entry taken on other kernel code is never reported
+    (the line's `traffic` is then null, not an old figure)."""
     with open(bench.TRAFFIC_FILE) as f:
         table = json.load(f)
     assert table["entries"], "no counter entries"
     digest = bench.source_digest()
     for e in table["entries"]:
-        assert e["bytes_projection_kernel"] >= e["algorithmic_bytes_projection_kernel"], e["workload"]
+        alg = e["algorithmic_bytes_projection_kernel"]
+        m = int(re.search(r"M=(\d+)", e["workload"]).group(1))
+        k = int(re.search(r"K=(\d+)", e["workload"]).group(1))
+        allowance = 7 * m * k * 2 + m * 1024 * 32
+        assert e["bytes_projection_kernel"] >= alg, e["workload"]
         if e["source_sha256_16"] == digest:
-            assert e["bytes_projection_kernel"] < 1.01 * e["algorithmic_bytes_projection_kernel"], e["workload"]
+            assert e["bytes_projection_kernel"] < 1.02 * alg + allowance, e["workload"]
             assert bench.measured_traffic(e["path"], e["workload"]) == e["bytes_projection_kernel"]
         else:
             assert bench.measured_traffic(e["path"], e["workload"]) is None, e["workload"]
@@ -144,3 +152,17 @@ def test_cpu_baseline_names_its_cores_and_blas():
     assert rec["cores"] == rec["blas_threads"] >= 1
     assert rec["blas"] != "unknown" and rec["blas"] in rec["sample"]
     assert np.isfinite(rec["value"])
+
+
+def test_traffic_table_lists_every_entry():
+    """`bench.py --traffic-table` (no GPU) prints one markdown row per entry
+    of profiles/traffic.json, with its excess over the algorithmic bytes."""
+    with open(bench.TRAFFIC_FILE) as f:
+        entries = json.load(f)["entries"]
+    p = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--traffic-table"],
+                       capture_output=True, text=True, timeout=120)
+    assert p.returncode == 0, p.stderr
+    rows = [ln for ln in p.stdout.splitlines() if ln.startswith("| ") and "`" in ln]
+    assert len(rows) == len(entries)
+    for e, ln in zip(entries, rows):
+        assert e["workload"] in ln and f"{e['bytes_projection_kernel']:,}" in ln
