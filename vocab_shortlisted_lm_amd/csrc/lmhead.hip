@@ -118,7 +118,7 @@ constexpr int kValuMaxM = 8;
 //                batch it scores;
 //   kLoopRing    a branch-free ring of kRingDepth batches, unrolled so the
 //                slots are static: exact waits, one batch always in flight.
-// Measured on MI355X (interleaved runs, same box): on the full 248,320-row
+// Measured on MI355X (interleaved runs on one machine): on the full 248,320-row
 // head the draining loop is best for M = 2..4 and the unconditional one for
 // M = 1 (174.6 against 177.7 us); on shortlists of 16k-53k rows the ring
 // is 3-16% faster than either (the ramp and tail dominate there).
@@ -1519,7 +1519,7 @@ proj_valu_tiled(const uint16_t* __restrict__ h, const uint16_t* __restrict__ W, 
 
   // The hidden rows go to LDS once the wave's first weight batch is in
   // flight (stage_and_sync below), so the two memory latencies at the start
-  // overlap instead of adding up.
+  // overlap instead of adding up (except in the draining loop, below).
   auto stage_and_sync = [&]() __attribute__((always_inline)) {
     stage_hidden<64 * WV>(h, K, M, hc, hc, h_stripes);
     __syncthreads();
@@ -1694,11 +1694,15 @@ proj_valu_tiled(const uint16_t* __restrict__ h, const uint16_t* __restrict__ W, 
   int j = 0;
   u32x4 wa[TR], wb[TR];
   int la = 0, lb = 0;
+  // the draining loop (top k and logits at M = 1 on the full head, M = 2-4
+  // there) stages first: staged after its first issue, the logits calls
+  // measured 6% slower (188 against 177 us at M = 1), the rest unchanged
+  if constexpr (LOOP == kLoopPair) stage_and_sync();
   if (tile < ntiles) {
     if constexpr (IDX) fetch_next_ids(tile);
     issue(wa, la, tile, 0);
   }
-  stage_and_sync();
+  if constexpr (LOOP != kLoopPair) stage_and_sync();
   if (tile < ntiles) {
     while (true) {
       int t1 = tile, j1 = j;
@@ -2597,7 +2601,7 @@ int mfma_lds_rows_fit(int64_t K, int waves, int fmt = kFmtBf16) {
 
 // Whether the matrix-core kernel stages the hidden rows after issuing its
 // first batches (so the two latencies overlap) rather than before.  Measured
-// on MI355X, interleaved builds on one box: after wins at 16 and more hidden
+// on MI355X, interleaved builds on one machine: after wins at 16 and more hidden
 // rows (the staging is long: 1-4% at 24 rows on the 52,755-row list) and on
 // the full head in every format; before wins on short quantized lists at a
 // few rows (MXFP4: 3.5% at 1, 3 and 8 rows; FP8: 1% at 1 and 3 rows), where
