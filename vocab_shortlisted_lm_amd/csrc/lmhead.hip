@@ -95,6 +95,32 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 #ifndef LMH_MFMA_RING
 #define LMH_MFMA_RING 3          // batches in the register ring of the coalesced matrix-core kernel
 #endif
+// LDS row padding of the matrix-core kernel, in 16-byte chunks.  Measured
+// with SQ_LDS_BANK_CONFLICT over row strides and lane offsets on gfx950: a
+// 16-byte read serves a half-wave at a time and is conflict-free when the
+// half-wave's 32 chunk indices are distinct modulo 32.  The hidden rows are
+// read as [column = lane % 16][chunk lane / 16 + 4 k], so a row stride of
+// 2 (mod 4) chunks keeps 16 columns x 2 lane groups apart, while a stride of
+// 1 (mod 4) makes column c of one group collide with column c + 1 of the
+// next (3.6 extra cycles per read).  Those reads matter where the kernel is
+// bound by its LDS traffic, the 4-bit heads at more than 16 hidden rows:
+// the 2-chunk pad took the MXFP4 head at 24 rows from 74.5 to 70.7 us (the
+// bank-conflict count from 12.4M to 2.5M per launch) and NVFP4 1.2% faster.
+// The bf16 and FP8 heads are bound by HBM: a conflict-free layout there
+// (hidden rows and the bf16 stage at 2, which removed every conflict of the
+// bf16 kernel) changed bf16 by under 0.2% and left FP8 0.5-2.5% slower, so
+// they keep the 1-chunk pads.  The FP8 stage (8-byte reads) is
+// conflict-free at odd strides; the 4-bit stages (4-byte reads) reach the
+// floor of such reads, 2 cycles each, at odd strides.
+#ifndef LMH_MFMA_HPAD
+#define LMH_MFMA_HPAD 1          // hidden rows, bf16 and FP8 heads
+#endif
+#ifndef LMH_MFMA_HPAD4
+#define LMH_MFMA_HPAD4 2         // hidden rows, MXFP4 and NVFP4 heads
+#endif
+#ifndef LMH_MFMA_SPAD
+#define LMH_MFMA_SPAD 1          // stages (A operand)
+#endif
 
 #ifndef LMH_WAVE_MAJOR
 #define LMH_WAVE_MAJOR 0          // 1: hand out work units wave-major (see first_unit)
@@ -1885,7 +1911,7 @@ proj_mfma(const uint16_t* __restrict__ h, const void* __restrict__ Wv, const voi
   constexpr int CPS = FP8 ? 2 : (MX4 ? 1 : 4);  // 16-byte chunks per k-step
   constexpr int BC = CPS * SB;      // 16-byte chunks per row per batch
   static_assert(BC == 16 || BC == 32 || BC == 64, "a load instruction covers whole row pieces");
-  constexpr int SC = BC + 1;        // stage row stride in chunks (padded against bank conflicts)
+  constexpr int SC = BC + LMH_MFMA_SPAD;  // stage row stride in chunks
   constexpr int RPI = 64 / BC;      // rows per load instruction
   constexpr int LPB = 16 / RPI;     // load instructions per batch
   const uint8_t* W = static_cast<const uint8_t*>(Wv);
@@ -1897,7 +1923,7 @@ proj_mfma(const uint16_t* __restrict__ h, const void* __restrict__ Wv, const voi
   const int wchunks = FP8 ? (K >> 4) : (MX4 ? (K >> 5) : (K >> 3));  // 16-byte chunks of a head row
   const int steps = (K + 31) >> 5;
   const int s4 = steps * 4;
-  const int row_chunks = s4 + 1;
+  const int row_chunks = s4 + (MX4 ? LMH_MFMA_HPAD4 : LMH_MFMA_HPAD);
 
   // The hidden rows go to LDS either first, or (early != 0) once the
   // wave's first batches are in flight: see mfma_stage_early.
@@ -2437,7 +2463,11 @@ bool valu_ok(int64_t M, int64_t K) {
   return M >= 1 && M <= kValuMaxM && k_ok(K) && M * chunks_per_lane(K) <= kValuMaxChunksTimesM;
 }
 
-int mfma_row_bytes(int64_t K) { return (int)((((K + 31) / 32) * 4 + 1) * 16); }
+// LDS bytes of one hidden row in the matrix-core kernel for a head format
+int mfma_row_bytes(int64_t K, int fmt) {
+  const int pad = fmt == kFmtMx4 || fmt == kFmtNv4 ? LMH_MFMA_HPAD4 : LMH_MFMA_HPAD;
+  return (int)((((K + 31) / 32) * 4 + pad) * 16);
+}
 
 
 typedef void (*proj_fn)(const uint16_t*, const uint16_t*, int, int, Epi);
@@ -2586,7 +2616,7 @@ int launch_valu(const ValuPlan& p, const uint16_t* h, int K, const uint16_t* W, 
 // wave.
 size_t mfma_stage_bytes(int waves, int fmt) {
   const size_t scale_chunks = fmt == kFmtMx4 ? 16 : (fmt == kFmtNv4 ? 32 : 0);
-  return (size_t)waves * 16 * (4 * LMH_MFMA_LDS_SB + 1) * 16 + (size_t)waves * scale_chunks * 16;
+  return (size_t)waves * 16 * (4 * LMH_MFMA_LDS_SB + LMH_MFMA_SPAD) * 16 + (size_t)waves * scale_chunks * 16;
 }
 
 // Hidden rows one launch of the matrix-core kernel can stage for K with
@@ -2595,7 +2625,7 @@ size_t mfma_stage_bytes(int waves, int fmt) {
 int mfma_lds_rows_fit(int64_t K, int waves, int fmt = kFmtBf16) {
   const int64_t stage = (int64_t)mfma_stage_bytes(waves, fmt);
   const int64_t fixed = stage + 512;
-  const int64_t rows = (kLdsPerWorkgroup - fixed) / mfma_row_bytes(K);
+  const int64_t rows = (kLdsPerWorkgroup - fixed) / mfma_row_bytes(K, fmt);
   return (int)std::max<int64_t>(0, std::min<int64_t>(LMH_MAX_M, rows));
 }
 
@@ -2625,7 +2655,7 @@ int launch_mfma_pass(const uint16_t* h, int K, int m_base, int mp, const void* W
                                     : (FMT == kFmtMx4 || FMT == kFmtNv4 ? 4 * LMH_MFMA_LDS_SB : LMH_MFMA_LDS_SB);
   constexpr int D = LMH_MFMA_RING;
   const void* wscale = wsc;
-  const size_t hbytes = (size_t)mp * mfma_row_bytes(K);
+  const size_t hbytes = (size_t)mp * mfma_row_bytes(K, FMT);
   const int64_t tiles = (R + 15) / 16;
   // 8 waves per workgroup only when there are tiles for 8 waves on every CU:
   // a shorter head in 8-wave workgroups would leave CUs idle (a 16,000-row
