@@ -20,7 +20,9 @@
  *    device, unless it is documented otherwise.
  *  - Matrices are row-major and contiguous: element (r, k) of an [R, K]
  *    matrix is at index r * K + k.
- *  - `stream` is a hipStream_t passed as void*; NULL means the null stream.
+ *  - `stream` is a hipStream_t passed as void*, created on the current
+ *    device; NULL means the null stream.  Launch settings (CU count,
+ *    occupancy) are those of the current device.
  *    Work is queued on `stream` and the call returns without waiting, except
  *    where a call says it synchronizes.  A call that neither synchronizes
  *    nor allocates only launches kernels, so it may be captured in a HIP
@@ -28,7 +30,9 @@
  *    shapes first, so that the per-kernel launch settings are cached outside
  *    the capture.
  *  - The caller owns every buffer.  The library never allocates or frees
- *    device memory and keeps no device state between calls.
+ *    device memory and keeps no device state between calls, except the
+ *    static slot array of draft_project_argmax_noalloc (loaded with the
+ *    library; nothing in it carries from one call to the next).
  *  - Return value: an lmh_status code.  A call that returns LMH_EINVAL,
  *    LMH_ERANGE or LMH_EWORKSPACE has launched nothing and written nothing.
  *    LMH_EHIP means a HIP runtime call failed; lmhead_last_error() gives its
