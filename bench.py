@@ -431,6 +431,9 @@ def main() -> int:
                     help="time the argmax as one launch per call (draft_project_argmax_fused: workgroups merge "
                          "their keys with atomics, the last one writes the outputs) instead of the projection + "
                          "fold pair; bf16 heads; whole calls only")
+    ap.add_argument("--unprepared", action="store_true",
+                    help="call the bf16 argmax through the plain binding (every tensor checked on every call) "
+                         "instead of PreparedArgmax")
     ap.add_argument("--graph", action="store_true",
                     help="capture the --steps calls of a timed region in one HIP graph and time its replays "
                          "(the calls without the host's launch cost)")
@@ -565,9 +568,26 @@ def main() -> int:
     if a.fused:
         state = L.new_state(dev)
 
+    # The bf16 argmax (and its single-launch form) goes through
+    # PreparedArgmax, as a decode loop would call it: the buffers are checked
+    # once, then each step is one C call.  One prepared step per rotated head
+    # copy and per stream (the capture stream under --graph is another).
+    prepared: dict = {}
+
+    def prepared_step(i):
+        st = launch_on[0]
+        steps_ = prepared.get(id(st))
+        if steps_ is None:
+            steps_ = [L.PreparedArgmax(h, w, d2t, path, out_id, out_logit, ws, st, state=state if a.fused else None)
+                      for w in heads]
+            prepared[id(st)] = steps_
+        steps_[i % len(steps_)]()
+
     def step(i):
         if a.rows:
             L.draft_project_argmax_keys(h, heads[i % len(heads)], 0, path, out_key, ws, launch_on[0])
+        elif a.fused and not a.unprepared:
+            prepared_step(i)
         elif a.fused:
             L.draft_project_argmax_fused_path(h, heads[i % len(heads)], d2t, path, state, out_id, out_logit,
                                               launch_on[0])
@@ -597,6 +617,8 @@ def main() -> int:
         elif a.nvfp4:
             q, sc, gs = heads[i % len(heads)]
             L.draft_project_argmax_nvfp4(h, q, sc, gs, d2t, path, out_id, out_logit, ws, launch_on[0])
+        elif not a.unprepared:
+            prepared_step(i)
         else:
             L.draft_project_argmax_path(h, heads[i % len(heads)], d2t, path, out_id, out_logit, ws,
                                         launch_on[0])

@@ -203,8 +203,15 @@ def _d2t(d2t, r: int, device, rows_of: str = "W"):
             raise ValueError(f"d2t must have one entry per row of {rows_of}")
 
 
+# The current stream's raw handle without building a torch Stream object
+# (1.8 us per call through torch.cuda.current_stream, 0.07 us this way).
+_raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+
+
 def _stream(stream, device) -> int:
     if stream is None:
+        if _raw_stream is not None:
+            return int(_raw_stream(_index(device)))
         stream = torch.cuda.current_stream(device)
     return int(stream.cuda_stream) if hasattr(stream, "cuda_stream") else int(stream)
 
