@@ -1734,9 +1734,9 @@ proj_valu_tiled(const uint16_t* __restrict__ h, const uint16_t* __restrict__ W, 
   int j = 0;
   u32x4 wa[TR], wb[TR];
   int la = 0, lb = 0;
-  // the draining loop (top k and logits at M = 1 on the full head, M = 2-4
-  // there) stages first: staged after its first issue, the logits calls
-  // measured 6% slower (188 against 177 us at M = 1), the rest unchanged
+  // the draining loop (top k and logits at M = 1) stages first: staged
+  // after its first issue, the logits calls measured 6% slower (188 against
+  // 177 us on the full head), top k unchanged
   if constexpr (LOOP == kLoopPair) stage_and_sync();
   if (tile < ntiles) {
     if constexpr (IDX) fetch_next_ids(tile);
