@@ -104,8 +104,9 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 // 1 (mod 4) makes column c of one group collide with column c + 1 of the
 // next (3.6 extra cycles per read).  Those reads matter where the kernel is
 // bound by its LDS traffic, the 4-bit heads at more than 16 hidden rows:
-// the 2-chunk pad took the MXFP4 head at 24 rows from 74.5 to 70.7 us (the
-// bank-conflict count from 12.4M to 2.5M per launch) and NVFP4 1.2% faster.
+// the 2-chunk pad took the MXFP4 head at 24 rows from 74.1 to 69.9 us (the
+// bank-conflict count from 12.4M to 2.5M per launch) and NVFP4 1.5-1.8%
+// faster.
 // The bf16 and FP8 heads are bound by HBM: a conflict-free layout there
 // (hidden rows and the bf16 stage at 2, which removed every conflict of the
 // bf16 kernel) changed bf16 by under 0.2% and left FP8 0.5-2.5% slower, so
