@@ -221,3 +221,72 @@ def test_random_shape_quantized_topk(L, case):
                                               torch.from_numpy(_tile_scales(scales)).cuda(), d2t_dev, topk)
         st = check_topk_mxfp4(h, codes, scales, d2t, ids.cpu().numpy(), lgs.cpu().numpy(), res)
     log(f"[random quantized top-k {i}] max_err={st.max_err:.2e} err/bound={st.max_err_over_bound:.3f}")
+
+
+# --------------------------------------------------------------------------
+# NVFP4 heads: argmax and top k over random shapes
+# --------------------------------------------------------------------------
+
+def _nv_cases(n=40, seed=20261205):
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        m = int(rng.choice(MS))
+        kmax = 1024 if rng.random() < 0.5 else 8192
+        k = 512 * int(rng.integers(1, kmax // 512 + 1))
+        rmax = max(1, min(40_000, 12_000_000 // k))
+        r = int(rng.integers(1, min(rmax, 600) + 1)) if rng.random() < 0.5 or rmax <= 600 else \
+            int(np.exp(rng.uniform(np.log(600), np.log(rmax))))
+        topk = int(rng.integers(1, 17)) if i % 2 else 0           # every other case a top-k call
+        out.append((i, m, k, r, bool(rng.random() < 0.5), topk))
+    return out
+
+
+NV_CASES = _nv_cases()
+
+
+def _nv_tile_scales(sc):
+    """Row-major E4M3 block scales [R, K / 16] -> the library's tiled layout
+    (16-row tiles, groups of 32 blocks, 512 bytes per tile and group)."""
+    r, nblk = sc.shape
+    t, ng = (r + 15) // 16, (nblk + 31) // 32
+    pad = np.zeros((t * 16, ng * 32), dtype=np.uint8)
+    pad[:r, :nblk] = sc
+    return np.ascontiguousarray(pad.reshape(t, 16, ng, 32).transpose(0, 2, 1, 3))
+
+
+@pytest.mark.parametrize("case", NV_CASES,
+                         ids=[f"{c[0]}-nv4-M{c[1]}-K{c[2]}-R{c[3]}{'-d2t' if c[4] else ''}"
+                              f"{'-k' + str(c[5]) if c[5] else ''}" for c in NV_CASES])
+def test_random_shape_nvfp4(L, case):
+    """NVFP4 heads quantized by the oracle (codes, tiled E4M3 scales, g): the
+    argmax on the library's kernel choice and the matrix-core path, or the
+    top k, against the oracle over the dequantized head."""
+    from parity import check_nvfp4, check_topk_nvfp4
+    import oracle.nvfp4_head as nv
+    i, m, k, r, with_d2t, topk = case
+    log(f"[random nvfp4 {i}] M={m} K={k} R={r} d2t={with_d2t} topk={topk}")
+    rng = np.random.default_rng(11000 + i)
+    w = synth.normal_bf16(11100 + i, r, k, 0.02)
+    hs = [synth.hidden(11200 + i, d, m, k) for d in range(2)]
+    stack = np.concatenate(hs)
+    d2t = _ids(rng, r, r + int(rng.integers(0, 2 * r + 1))) if with_d2t else None
+    d2t_dev = dev_i32(d2t) if d2t is not None else None
+    codes, scales, g = nv.oracle_quantize_nvfp4(w)
+    q_dev = torch.from_numpy(codes).cuda()
+    s_dev = torch.from_numpy(_nv_tile_scales(scales)).cuda()
+    g_dev = torch.tensor([float(g)], dtype=torch.float32, device="cuda")
+    if topk:
+        res = oracle.oracle_project_topk_nvfp4(stack, codes, scales, g, d2t, topk)
+        got = [L.draft_project_topk_nvfp4(dev_bf16(h), q_dev, s_dev, g_dev, d2t_dev, topk) for h in hs]
+        st = check_topk_nvfp4(stack, codes, scales, g, d2t, np.concatenate([x[0].cpu().numpy() for x in got]),
+                              np.concatenate([x[1].cpu().numpy() for x in got]), res)
+    else:
+        res = oracle.oracle_project_argmax_nvfp4(stack, codes, scales, g, d2t, keep_logits=True)
+        st = ParityStats()
+        for p in (L.LMH_PATH_AUTO, L.LMH_PATH_MFMA):
+            got = [L.draft_project_argmax_nvfp4(dev_bf16(h), q_dev, s_dev, g_dev, d2t_dev, p) for h in hs]
+            st.add(check_nvfp4(stack, codes, scales, g, d2t, np.concatenate([x[0].cpu().numpy() for x in got]),
+                               np.concatenate([x[1].cpu().numpy() for x in got]), res))
+        st.assert_exempt_bound()
+    log(f"[random nvfp4 {i}] max_err={st.max_err:.2e} err/bound={st.max_err_over_bound:.3f}")
