@@ -211,3 +211,41 @@ def test_fused_rejects_and_writes_nothing(L):
     torch.cuda.synchronize()
     assert bool((oid == 7).all()) and bool((olg == 5.0).all())
     assert nonzero_bytes(state) == 0
+
+
+def _random_cases(n=30, seed=20261206):
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        m = int(rng.choice([1, 2, 3, 4, 5, 8, 12, 16, 17, 24, 31, 32]))
+        k = 8 * int(rng.integers(1, (1024 if rng.random() < 0.5 else 8192) // 8 + 1))
+        rmax = max(1, min(70_000, 16_000_000 // k))
+        r = int(rng.integers(1, min(rmax, 600) + 1)) if rng.random() < 0.5 or rmax <= 600 else \
+            int(np.exp(rng.uniform(np.log(600), np.log(rmax))))
+        out.append((i, m, k, r, bool(rng.random() < 0.5)))
+    return out
+
+
+@pytest.mark.parametrize("case", _random_cases(),
+                         ids=lambda c: f"{c[0]}-M{c[1]}-K{c[2]}-R{c[3]}{'-d2t' if c[4] else ''}")
+def test_fused_random_shapes(L, case):
+    """Seeded random shapes (M, K, R, d2t) on every kernel that takes them:
+    the single launch equals the two-kernel call bit for bit and leaves the
+    state at zero."""
+    i, m, k, r, with_d2t = case
+    rng = np.random.default_rng(12000 + i)
+    w_dev = dev_bf16(synth.normal_bf16(12100 + i, r, k, 0.02))
+    h_dev = dev_bf16(synth.hidden(12200 + i, 0, m, k))
+    d2t = dev_i32(rng.permutation(r + int(rng.integers(0, 2 * r + 1)))[:r].astype(np.int32)) if with_d2t else None
+    state = L.new_state("cuda")
+    paths = [L.LMH_PATH_AUTO, L.LMH_PATH_MFMA]
+    if L.lib().draft_project_auto_path_rows(m, k, r) == L.LMH_PATH_VALU or m <= 8:
+        paths.append(L.LMH_PATH_VALU)
+    for p in paths:
+        try:
+            b = L.draft_project_argmax_path(h_dev, w_dev, d2t, p)
+        except L.LmheadError:
+            continue                                   # this kernel does not take the shape
+        a = L.draft_project_argmax_fused_path(h_dev, w_dev, d2t, p, state)
+        assert same(a, b), (case, p)
+        assert nonzero_bytes(state) == 0, (case, p)
