@@ -1,8 +1,12 @@
 """The boundary from C: tests/c_consumer/lmhead_consumer owns its device
 buffers, gathers a shortlist (lmhead_trim) and runs the argmax over the
 trimmed head with d2t and over the full head without it
-(draft_project_argmax), with no Python or torch in the process.  Its
-outputs are checked against the fp64 oracle with the parity rule."""
+(draft_project_argmax), the first as single launches on a state it zeroes
+once (draft_project_argmax_fused) and the second without a workspace
+(draft_project_argmax_noalloc), with no Python or torch in the process.
+Its outputs are checked against the fp64 oracle with the parity rule, and
+the single-launch and no-workspace outputs against the ordinary calls bit
+for bit."""
 import os
 import subprocess
 
@@ -43,7 +47,9 @@ def test_c_program_matches_the_oracle(consumer, tmp_path, m):
     assert proc.returncode == 0, proc.stderr
     assert "ok" in proc.stdout
     out = np.fromfile(files["out"], dtype=np.dtype([("id", "<i4"), ("logit", "<f4")]))
-    assert out.size == 2 * m
-    trimmed, full = out[:m], out[m:]
+    assert out.size == 4 * m
+    trimmed, full, fused, noalloc = out[:m], out[m:2 * m], out[2 * m:3 * m], out[3 * m:]
     check(h, oracle.oracle_trim(w, ids), ids, trimmed["id"], trimmed["logit"])
     check(h, w, None, full["id"], full["logit"])
+    assert np.array_equal(fused.view(np.uint64), trimmed.view(np.uint64))
+    assert np.array_equal(noalloc.view(np.uint64), full.view(np.uint64))
