@@ -317,9 +317,12 @@ def cpu_baseline(h_np, w_np, d2t_np, budget_s: float, indexed: bool = False):
         el = time.perf_counter() - t0
         if el >= budget_s or calls >= 50:
             break
+    rows = d2t_np.size if indexed else w_np.shape[0]
     return {"value": calls / el, "unit": "calls/s", "cores": threads, "kind": "oracle",
             "host_cpus": os.cpu_count(), "host_cpus_usable": len(os.sched_getaffinity(0)),
             "blas": blas["library"], "blas_threads": threads,
+            "seconds_per_call": el / calls,
+            "gbps": round(rows * w_np.shape[1] * 2 * calls / el / 1e9, 3),  # bf16 head bytes per second
             "sample": f"{calls} whole oracle calls (fp64, M={h_np.shape[0]}, "
                       f"{d2t_np.size if indexed else w_np.shape[0]} rows x K={w_np.shape[1]}) in {el:.1f} s; "
                       f"numpy + {blas['library']} with {threads} threads"}

@@ -140,7 +140,8 @@ def test_record_and_look_up_traffic(tmp_path, monkeypatch):
 
 def test_cpu_baseline_names_its_cores_and_blas():
     """The CPU baseline record states the threads the oracle ran on, the
-    host's CPU count and the BLAS library, each as its own field."""
+    host's CPU count and the BLAS library, each as its own field, and the
+    time per call and effective rate over the head's bytes."""
     import numpy as np
     import synth
     inp = synth.make_config(1)
@@ -152,6 +153,9 @@ def test_cpu_baseline_names_its_cores_and_blas():
     assert rec["cores"] == rec["blas_threads"] >= 1
     assert rec["blas"] != "unknown" and rec["blas"] in rec["sample"]
     assert np.isfinite(rec["value"])
+    # seconds per call and the bf16 head bytes it reads per second
+    assert abs(rec["seconds_per_call"] * rec["value"] - 1.0) < 1e-9
+    assert abs(rec["gbps"] - 4096 * 256 * 2 * rec["value"] / 1e9) <= 1e-3
 
 
 def test_traffic_table_lists_every_entry():
