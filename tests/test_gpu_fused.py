@@ -249,3 +249,39 @@ def test_fused_random_shapes(L, case):
         a = L.draft_project_argmax_fused_path(h_dev, w_dev, d2t, p, state)
         assert same(a, b), (case, p)
         assert nonzero_bytes(state) == 0, (case, p)
+
+
+@pytest.mark.parametrize("m,cfg", [(1, 2), (3, 3), (24, 5)])
+def test_fused_many_calls_back_to_back(L, m, cfg):
+    """400 single launches queued back to back on one state (each with
+    its own hidden rows and output slot, no synchronization between them),
+    against the two-kernel call on the same inputs, bit for bit: every
+    launch's merge must see every workgroup's maxima and leave the state
+    clean for the next one.  The full head at one hidden row has the most
+    workgroups per launch (the most atomics per ticket)."""
+    inp = config_inputs(cfg)
+    if cfg == 2:
+        w = device_weights(2)
+        d2t = None
+    else:
+        w = L.lmhead_trim(device_weights(cfg), dev_i32(inp["ids"]))
+        d2t = dev_i32(inp["ids"])
+    n = 400
+    k = inp["config"].k
+    hs = dev_bf16(np.concatenate([synth.hidden(13000 + m, d, m, k) for d in range(n)]))  # [n * m, K]
+    state = L.new_state("cuda")
+    fid = torch.empty((n, m), dtype=torch.int32, device="cuda")
+    flg = torch.empty((n, m), dtype=torch.float32, device="cuda")
+    rid = torch.empty((n, m), dtype=torch.int32, device="cuda")
+    rlg = torch.empty((n, m), dtype=torch.float32, device="cuda")
+    ws = L.new_workspace(M=m)
+    for i in range(n):
+        h = hs[i * m:(i + 1) * m]
+        L.draft_project_argmax_fused(h, w, d2t, state, fid[i], flg[i])
+    for i in range(n):
+        h = hs[i * m:(i + 1) * m]
+        L.draft_project_argmax(h, w, d2t, rid[i], rlg[i], ws)
+    torch.cuda.synchronize()
+    assert torch.equal(fid, rid)
+    assert torch.equal(flg.view(torch.int32), rlg.view(torch.int32))
+    assert nonzero_bytes(state) == 0
