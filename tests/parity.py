@@ -19,8 +19,16 @@ Two bars are applied to every hidden row:
    rounding multiplies by the row's scale: (K + 2) * 2**-24 * sum_k
    |h_k w_k| with w the dequantized values.  Over an MXFP4 head every
    dequantized value is a bf16 number and the bf16 bound applies unchanged.
-   Over an NVFP4 head every code times its block scale is a bf16 number and
-   the head's scale multiplies each row's sum once: K + 2, as for FP8.
+   Over an NVFP4 head every code times its block scale is an f16 number
+   (E2M1 x E4M3: at most 6 significant bits, within f16's normal range) and
+   the head's scale multiplies each row's sum once: K + 2, as for FP8.  The
+   kernel takes those products against hidden rows in f16, each row scaled
+   by a power of two that puts its largest magnitude in [2^15, 2^16): a
+   value within 2^29 of the largest is exact, a smaller one may be rounded
+   or flushed, an error of at most its own magnitude.  So the NVFP4 bound
+   adds sum_k |h_k w_k| over the hidden row's values below 2^(E - 29), E
+   the exponent of its largest magnitude (zero on every row where no value
+   is that small).
 """
 from __future__ import annotations
 
@@ -65,8 +73,21 @@ class ParityStats:
             f"{self.exempt} of {self.rows} rows took another near-tied id")
 
 
-def _row_bound(h_row: np.ndarray, w_row: np.ndarray, k: int, extra: int = 1) -> float:
-    return (k + extra) * U32 * float(np.abs(h_row * w_row).sum()) + 1e-30
+def f16_hidden_slack(h: np.ndarray) -> np.ndarray:
+    """|h| where a hidden value lies more than 2^29 below its row's largest
+    magnitude (below 2^(E - 29), E = floor(log2 max |h|)), else 0: the most
+    the power-of-two-scaled f16 copy of a row can be off by, per element."""
+    a = np.abs(np.atleast_2d(h))
+    amax = a.max(axis=1, keepdims=True)
+    e = np.floor(np.log2(np.where(amax > 0, amax, 1.0)))
+    return np.where((amax > 0) & (a < np.exp2(e - 29)), a, 0.0).reshape(np.shape(h))
+
+
+def _row_bound(h_row: np.ndarray, w_row: np.ndarray, k: int, extra: int = 1, f16_hidden: bool = False) -> float:
+    b = (k + extra) * U32 * float(np.abs(h_row * w_row).sum()) + 1e-30
+    if f16_hidden:
+        b += float((f16_hidden_slack(h_row) * np.abs(w_row)).sum())
+    return b
 
 
 def check(h_bits, w_bits, d2t, gpu_id, gpu_logit, res=None) -> ParityStats:
@@ -107,17 +128,18 @@ def check_mxfp4(h_bits, codes, scales, d2t, gpu_id, gpu_logit, res=None) -> Pari
 def check_nvfp4(h_bits, codes, scales, g, d2t, gpu_id, gpu_logit, res=None) -> ParityStats:
     """The same rule over an NVFP4 head (codes [R, K / 2], block scales
     [R, K / 16], tensor scale g).  Each E2M1 value times its E4M3 block scale
-    is a bf16 number, so the GPU's products are exact; it sums them in fp32
+    is an f16 number, so the GPU's products are exact; it sums them in fp32
     and multiplies each row's sum by g once: K + 2 roundings against the
-    dequantized values, as over an FP8 head."""
+    dequantized values, as over an FP8 head, plus the f16 hidden rows'
+    slack (f16_hidden_slack)."""
     codes, scales = np.asarray(codes), np.asarray(scales)
     if res is None or res.logits is None:
         res = oracle.oracle_project_argmax_nvfp4(h_bits, codes, scales, g, d2t, keep_logits=True)
     return _check_core(h_bits, lambda rows: oracle.oracle_dequant_nvfp4(codes[rows], scales[rows], g),
-                       codes.shape[0], d2t, gpu_id, gpu_logit, res, extra=2)
+                       codes.shape[0], d2t, gpu_id, gpu_logit, res, extra=2, f16_hidden=True)
 
 
-def _check_core(h_bits, w_rows, r, d2t, gpu_id, gpu_logit, res, extra) -> ParityStats:
+def _check_core(h_bits, w_rows, r, d2t, gpu_id, gpu_logit, res, extra, f16_hidden=False) -> ParityStats:
     h_bits = np.asarray(h_bits)
     gpu_id = np.asarray(gpu_id).astype(np.int64)
     gpu_logit = np.asarray(gpu_logit).astype(np.float64)
@@ -137,8 +159,8 @@ def _check_core(h_bits, w_rows, r, d2t, gpu_id, gpu_logit, res, extra) -> Parity
         lg = res.logits[i, rows[i]]
         wg = w_rows(np.array([rows[i]]))[0]
         wb = w_rows(np.array([res.idx[i]]))[0]
-        b_g = _row_bound(h[i], wg, k, extra)
-        b_best = _row_bound(h[i], wb, k, extra)
+        b_g = _row_bound(h[i], wg, k, extra, f16_hidden)
+        b_best = _row_bound(h[i], wb, k, extra, f16_hidden)
         err = abs(gpu_logit[i] - lg)
         st.max_err = max(st.max_err, err)
         st.max_err_over_bound = max(st.max_err_over_bound, err / b_g)
@@ -159,11 +181,13 @@ def _check_core(h_bits, w_rows, r, d2t, gpu_id, gpu_logit, res, extra) -> Parity
     return st
 
 
-def row_bounds(h_bits, w_bits, rows=None, w_rows=None, extra: int = 1) -> np.ndarray:
+def row_bounds(h_bits, w_bits, rows=None, w_rows=None, extra: int = 1, f16_hidden: bool = False) -> np.ndarray:
     """(K + extra) * 2**-24 * sum_k |h[m,k] W[r,k]| for every (m, r) (or the
     given rows): the fp32 error bound of any summation order, as in check().
-    `w_rows(rows)` gives fp64 rows of a quantized head instead of w_bits."""
+    `w_rows(rows)` gives fp64 rows of a quantized head instead of w_bits;
+    f16_hidden adds the f16 hidden rows' slack, as in check_nvfp4."""
     h = np.abs(oracle.bf16_bits_to_f64(np.asarray(h_bits)))
+    slack = f16_hidden_slack(h) if f16_hidden else None
     if w_rows is None:
         w_bits = np.asarray(w_bits)
         rows = np.arange(w_bits.shape[0]) if rows is None else np.asarray(rows)
@@ -173,7 +197,12 @@ def row_bounds(h_bits, w_bits, rows=None, w_rows=None, extra: int = 1) -> np.nda
     for r0 in range(0, len(rows), 8192):
         wb = np.abs(w_rows(rows[r0:r0 + 8192]))
         out[:, r0:r0 + wb.shape[0]] = h @ wb.T
-    return (k + extra) * U32 * out + 1e-30
+    out = (k + extra) * U32 * out + 1e-30
+    if slack is not None:
+        for r0 in range(0, len(rows), 8192):
+            wb = np.abs(w_rows(rows[r0:r0 + 8192]))
+            out[:, r0:r0 + wb.shape[0]] += slack @ wb.T
+    return out
 
 
 def check_topk(h_bits, w_bits, d2t, gpu_ids, gpu_logits, res=None) -> ParityStats:
@@ -210,16 +239,16 @@ def check_topk_mxfp4(h_bits, codes, scales, d2t, gpu_ids, gpu_logits, res=None) 
 
 
 def check_topk_nvfp4(h_bits, codes, scales, g, d2t, gpu_ids, gpu_logits, res=None) -> ParityStats:
-    """The top-k rule over an NVFP4 head (bound with K + 2 roundings, as in
-    check_nvfp4)."""
+    """The top-k rule over an NVFP4 head (bound with K + 2 roundings and
+    the f16 hidden rows' slack, as in check_nvfp4)."""
     codes, scales = np.asarray(codes), np.asarray(scales)
     if res is None:
         res = oracle.oracle_project_topk_nvfp4(h_bits, codes, scales, g, d2t, np.asarray(gpu_ids).shape[1])
     return _check_topk_core(h_bits, lambda rr: oracle.oracle_dequant_nvfp4(codes[rr], scales[rr], g),
-                            codes.shape[0], d2t, gpu_ids, gpu_logits, res, extra=2)
+                            codes.shape[0], d2t, gpu_ids, gpu_logits, res, extra=2, f16_hidden=True)
 
 
-def _check_topk_core(h_bits, w_rows, r, d2t, gpu_ids, gpu_logits, res, extra) -> ParityStats:
+def _check_topk_core(h_bits, w_rows, r, d2t, gpu_ids, gpu_logits, res, extra, f16_hidden=False) -> ParityStats:
     h_bits = np.asarray(h_bits)
     gpu_ids = np.asarray(gpu_ids).astype(np.int64)
     gpu_logits = np.asarray(gpu_logits).astype(np.float64)
@@ -240,8 +269,8 @@ def _check_topk_core(h_bits, w_rows, r, d2t, gpu_ids, gpu_logits, res, extra) ->
         assert np.unique(rows).size == kk, f"row {i}: repeated candidates"
         gl = gpu_logits[i, :kk]
         assert np.all(gl[:-1] >= gl[1:]), f"row {i}: logits not in descending order"
-        bnd = row_bounds(h_bits[i:i + 1], None, rows, w_rows, extra)[0]
-        bnd_ref = row_bounds(h_bits[i:i + 1], None, res.idx[i, :kk], w_rows, extra)[0]
+        bnd = row_bounds(h_bits[i:i + 1], None, rows, w_rows, extra, f16_hidden)[0]
+        bnd_ref = row_bounds(h_bits[i:i + 1], None, res.idx[i, :kk], w_rows, extra, f16_hidden)[0]
         srt = res.sorted_logits[i]
         bmax = 2 * float(max(bnd.max(), bnd_ref.max()))
         for j in range(kk):

@@ -301,6 +301,43 @@ def test_nvfp4_wide_block_scales(L):
     run_and_check(L, hs, codes, scales, g, None, "nvfp4 wide block scales")
 
 
+@pytest.mark.parametrize("k", [512, 2560])
+def test_nvfp4_hidden_rows_across_the_bf16_range(L, k):
+    """The kernel takes NVFP4 products against hidden rows in f16, each row
+    scaled by a power of two that moves its largest magnitude to [2^15,
+    2^16) and taken off again from the row's sums.  So a hidden row times
+    2^j must give the same ids and exactly 2^j times the logits, for rows
+    far above and below 1 (bf16's range, not f16's).  A row with values
+    more than 2^29 below its largest (which the f16 copy may round or
+    flush) and an all-zero row meet the parity rule with that slack."""
+    from parity import f16_hidden_slack
+    w = synth.normal_bf16(41000 + k, 3001, k, 0.02)
+    codes, scales, g = nv.oracle_quantize_nvfp4(w)
+    dev = (dev_u8(codes), dev_u8(tile_scales(scales)), dev_f32([g]))
+    base = oracle.bf16_bits_to_f64(synth.hidden(42000 + k, 0, 4, k))
+    ids0, lg0 = (x.cpu().numpy() for x in L.draft_project_argmax_nvfp4(dev_bf16(synth.bf16_from_f32(
+        base.astype(np.float32))), *dev, None, L.LMH_PATH_MFMA))
+    for j in (-100, -40, -7, 9, 40, 100):
+        hj = base * 2.0 ** j
+        bits = synth.bf16_from_f32(hj.astype(np.float32))
+        assert np.array_equal(oracle.bf16_bits_to_f64(bits), hj)        # the scaling is exact in bf16
+        for p in (L.LMH_PATH_AUTO, L.LMH_PATH_MFMA):
+            i, lg = (x.cpu().numpy() for x in L.draft_project_argmax_nvfp4(dev_bf16(bits), *dev, None, p))
+            assert np.array_equal(i, ids0), (j, p)
+            assert np.array_equal(lg, np.ldexp(lg0, j).astype(np.float32)), (j, p)
+    # a row spanning more than 2^29, and a zero row
+    wide = base.copy()
+    wide[0, ::7] *= 2.0 ** -40
+    wide[1, 5::11] *= 2.0 ** -33
+    wide[2] = 0.0
+    bits = synth.bf16_from_f32(wide.astype(np.float32))
+    assert np.all(f16_hidden_slack(oracle.bf16_bits_to_f64(bits))[:2].sum(axis=1) > 0)
+    run_and_check(L, [bits], codes, scales, g, None, f"nvfp4 hidden beyond f16 K={k}", dev)
+    res = oracle.oracle_project_argmax_nvfp4(bits, codes, scales, g)
+    i, lg = (x.cpu().numpy() for x in L.draft_project_argmax_nvfp4(dev_bf16(bits), *dev, None, L.LMH_PATH_MFMA))
+    assert i[2] == 0 and lg[2] == 0.0 and res.id[2] == 0
+
+
 def _tie_head(rng, r, k, m, vals, planted, big):
     """E2M1 values with every block's maximum 6 (block scale 1), a row
     holding 2,688 in a column every hidden row zeroes (head scale 1, logit

@@ -70,6 +70,8 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 
 // ---------------------------------------------------------------------------
 // tunables (compile-time)
@@ -244,22 +246,21 @@ __device__ __forceinline__ u32x4 fp4x8_to_bf16x8_scaled(uint32_t packed, float s
                __builtin_bit_cast(uint32_t, d)};
 }
 
-// Eight E2M1 codes times an NVFP4 block scale `sc` (a decoded E4M3 value,
-// not a power of two) as eight bf16 values, exactly.  The codes convert at
-// scale 1 to fp32; each product with the scale has at most 6 significant
-// bits (2 of E2M1 times 4 of E4M3), so the fp32 multiply is exact and the
-// product's high 16 bits are its bf16 value (the low 16 are zero), which
-// v_perm_b32 packs two at a time.
-template <int SEL>
-__device__ __forceinline__ uint32_t fp4x2_times_scale_to_bf16x2(uint32_t packed, float sc) {
-  const auto v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(packed, 1.0f, SEL);
-  const uint32_t lo = __builtin_bit_cast(uint32_t, v[0] * sc);
-  const uint32_t hi = __builtin_bit_cast(uint32_t, v[1] * sc);
-  return __builtin_amdgcn_perm(hi, lo, 0x07060302u);  // bytes 2, 3 of lo, then 2, 3 of hi
-}
-__device__ __forceinline__ u32x4 fp4x8_times_scale_to_bf16x8(uint32_t packed, float sc) {
-  return u32x4{fp4x2_times_scale_to_bf16x2<0>(packed, sc), fp4x2_times_scale_to_bf16x2<1>(packed, sc),
-               fp4x2_times_scale_to_bf16x2<2>(packed, sc), fp4x2_times_scale_to_bf16x2<3>(packed, sc)};
+// Eight E2M1 codes times an NVFP4 block scale as eight f16 values, exactly:
+// the codes convert at scale 1 to f16, and one packed f16 multiply per two
+// takes the block scale `sc` (a decoded E4M3 value, exact in f16).  Every
+// product has at most 6 significant bits and lies in [2^-10, 2688] or is
+// zero, so it is a normal f16 number.  Two VALU operations per two
+// elements, against four for the same products as bf16 (gfx950 has no
+// packed bf16 multiply).
+__device__ __forceinline__ u32x4 fp4x8_times_scale_to_f16x8(uint32_t packed, _Float16 sc) {
+  const f16x2 s2 = f16x2{sc, sc};
+  const f16x2 a = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(packed, 1.0f, 0) * s2;
+  const f16x2 b = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(packed, 1.0f, 1) * s2;
+  const f16x2 c = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(packed, 1.0f, 2) * s2;
+  const f16x2 d = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(packed, 1.0f, 3) * s2;
+  return u32x4{__builtin_bit_cast(uint32_t, a), __builtin_bit_cast(uint32_t, b), __builtin_bit_cast(uint32_t, c),
+               __builtin_bit_cast(uint32_t, d)};
 }
 
 // The same with the MXFP4 block scale 2^(e - 127), e the block's E8M0
@@ -1883,6 +1884,121 @@ proj_valu_fp8(const uint16_t* __restrict__ h, const uint8_t* __restrict__ W, con
 // ---------------------------------------------------------------------------
 // matrix-core path
 // ---------------------------------------------------------------------------
+// NVFP4 heads take the f16 matrix instruction (see
+// fp4x8_times_scale_to_f16x8), so their hidden rows go to LDS as f16.
+// Hidden row m is stored as h * 2^n with n = 15 - E, E the exponent of the
+// row's largest magnitude, which then lies in [2^15, 2^16); n goes to the
+// row's first pad chunk (past `width`, never read as an operand).  A value
+// within 2^29 of the largest becomes a normal f16 number with at most 8
+// significant bits: exact.  Smaller ones are rounded to f16's subnormal
+// step or flushed, an error of at most their own magnitude.  Since 2^n is
+// exact, the row's sums times 2^-n are what bf16 operands would give.
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false));   // quad_perm [1,0,3,2]
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false));   // quad_perm [2,3,0,1]
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x124, 0xF, 0xF, false));  // row_ror:4
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x128, 0xF, 0xF, false));  // row_ror:8
+  const int row = (int)(threadIdx.x & 63) >> 4;
+  v = max(v, xrow_u32<16>(v, row));
+  return max(v, xrow_u32<32>(v, row));
+}
+
+// n of a row from the wave's per-lane maxima of its |bf16| bits: frexp
+// gives e with amax = f * 2^e, f in [0.5, 1), so E = e - 1 and n = 16 - e
+// (a zero row gives e = 0 and n = 16, which scales nothing).
+__device__ __forceinline__ int f16_row_shift(uint32_t lane_max) {
+  return 16 - __builtin_amdgcn_frexp_expf(__builtin_bit_cast(float, wave_max_u32(lane_max) << 16));
+}
+
+__device__ __forceinline__ u32x4 bf16x8_to_f16x8_shifted(const u32x4& v, int n) {
+  u32x4 o;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const float lo = __builtin_ldexpf(__builtin_bit_cast(float, v[e] << 16), n);
+    const float hi = __builtin_ldexpf(__builtin_bit_cast(float, v[e] & 0xFFFF0000u), n);
+    o[e] = __builtin_bit_cast(uint32_t, f16x2{(_Float16)lo, (_Float16)hi});
+  }
+  return o;
+}
+
+// Stages hidden rows [0, mp) of h ([mp, K] bf16) into LDS rows of `stride`
+// chunks as above: `width` 16-byte chunks of 8 values, zero past K.  Wave w owns
+// rows w, w + WV, ... and reads them straight from memory: with K <= 2,560
+// (at most 5 chunks per lane and row), GR of its rows at a time with all
+// their loads in flight at once, then each row's maximum (one DPP
+// reduction), the conversion in registers and one LDS write per chunk.
+// Longer rows go one at a time in pieces of 8 chunks per lane, read twice
+// (maximum, then conversion).  The caller synchronizes afterwards.
+template <int WV, int GR>
+__device__ __forceinline__ void stage_hidden_f16(const uint16_t* __restrict__ h, int K, int mp, int width, int stride,
+                                                 u32x4* __restrict__ lds) {
+  constexpr int CPL = 5;  // chunks per lane and row on the fast path
+  const int lane = threadIdx.x & 63;
+  const int w = wave_id();
+  const __amdgpu_buffer_rsrc_t hs = make_rsrc(h, (uint32_t)mp * (uint32_t)K * 2u);
+  if (width <= 64 * CPL) {
+    for (int m0 = w; m0 < mp; m0 += GR * WV) {
+      u32x4 v[GR][CPL];
+#pragma unroll
+      for (int r = 0; r < GR; ++r) {
+        const int m = m0 + r * WV;
+#pragma unroll
+        for (int j = 0; j < CPL; ++j) {
+          const int c = lane + 64 * j;
+          v[r][j] = load16<0>(hs, m < mp && c * 8 < K ? (uint32_t)(m * K + c * 8) * 2u : kOobOffset);
+        }
+      }
+#pragma unroll
+      for (int r = 0; r < GR; ++r) {
+        const int m = m0 + r * WV;
+        if (m >= mp) break;
+        uint32_t mx = 0u;
+#pragma unroll
+        for (int j = 0; j < CPL; ++j) mx = abs_bits_max(mx, v[r][j]);
+        const int n = f16_row_shift(mx);
+        u32x4* row = lds + m * stride;
+#pragma unroll
+        for (int j = 0; j < CPL; ++j) {
+          const int c = lane + 64 * j;
+          if (c < width) row[c] = bf16x8_to_f16x8_shifted(v[r][j], n);
+        }
+        if (lane == 0) reinterpret_cast<int*>(row + width)[0] = n;
+      }
+    }
+    return;
+  }
+  constexpr int P = 8;  // chunks per lane and piece on the long-row path
+  for (int m = w; m < mp; m += WV) {
+    uint32_t mx = 0u;
+    for (int c0 = 0; c0 < width; c0 += 64 * P) {
+      u32x4 v[P];
+#pragma unroll
+      for (int j = 0; j < P; ++j) {
+        const int c = c0 + lane + 64 * j;
+        v[j] = load16<0>(hs, c * 8 < K ? (uint32_t)(m * K + c * 8) * 2u : kOobOffset);
+      }
+#pragma unroll
+      for (int j = 0; j < P; ++j) mx = abs_bits_max(mx, v[j]);
+    }
+    const int n = f16_row_shift(mx);
+    u32x4* row = lds + m * stride;
+    for (int c0 = 0; c0 < width; c0 += 64 * P) {
+      u32x4 v[P];
+#pragma unroll
+      for (int j = 0; j < P; ++j) {
+        const int c = c0 + lane + 64 * j;
+        v[j] = load16<0>(hs, c * 8 < K ? (uint32_t)(m * K + c * 8) * 2u : kOobOffset);
+      }
+#pragma unroll
+      for (int j = 0; j < P; ++j) {
+        const int c = c0 + lane + 64 * j;
+        if (c < width) row[c] = bf16x8_to_f16x8_shifted(v[j], n);
+      }
+    }
+    if (lane == 0) reinterpret_cast<int*>(row + width)[0] = n;
+  }
+}
+
 // Matrix-core path with coalesced loads.  The MFMA operand layout wants the
 // 16 lanes of a k-group to hold 16 different head rows, which makes every
 // load instruction touch 16 rows x 64 bytes; HBM streams such loads at
@@ -1908,9 +2024,11 @@ proj_valu_fp8(const uint16_t* __restrict__ h, const uint8_t* __restrict__ W, con
 // each batch also loads the 16 scale bytes of each of its 16 rows, staged
 // beside the codes, and the codes become bf16 times the scale, exactly); or
 // NVFP4 (kFmtNv4: as MXFP4, with two E4M3 block scales per k-step and row,
-// 32 scale bytes per row per batch, each code times its decoded block scale
-// exactly in bf16; a row's sum is multiplied once by the head's fp32 scale
-// *gsc).
+// 32 scale bytes per row per batch; each code times its decoded block scale
+// exactly in f16, against hidden rows in f16 scaled by a power of two per
+// row (hidden_rows_to_f16), on the f16 matrix instruction; a row's sum is
+// multiplied by the inverse power of two, then once by the head's fp32
+// scale *gsc).
 template <int NT, int SB, int WV, int D, int TK, bool LOGITS, int FMT, bool IDX = false>
 __global__ void __launch_bounds__(64 * WV)
 proj_mfma(const uint16_t* __restrict__ h, const void* __restrict__ Wv, const void* __restrict__ wsc,
@@ -1941,11 +2059,25 @@ proj_mfma(const uint16_t* __restrict__ h, const void* __restrict__ Wv, const voi
   const int row_chunks = s4 + (MX4 ? LMH_MFMA_HPAD4 : LMH_MFMA_HPAD);
 
   // The hidden rows go to LDS either first, or (early != 0) once the
-  // wave's first batches are in flight: see mfma_stage_early.
-  if (!early) {
-    stage_hidden<64 * WV, NT == 2 ? 16 : 8>(h + (size_t)m_base * K, K, mp, s4, row_chunks, lds);
+  // wave's first batches are in flight: see mfma_stage_early.  NV4: as f16
+  // (stage_hidden_f16), and each lane takes its columns' power-of-two
+  // exponents.
+  int hexp[NV4 ? NT : 1];
+  auto load_hidden = [&]() __attribute__((always_inline)) {
+    if constexpr (NV4)
+      stage_hidden_f16<WV, (NT * 16 / WV < 3 ? NT * 16 / WV : 3)>(h + (size_t)m_base * K, K, mp, s4, row_chunks, lds);
+    else
+      stage_hidden<64 * WV, NT == 2 ? 16 : 8>(h + (size_t)m_base * K, K, mp, s4, row_chunks, lds);
     __syncthreads();
-  }
+    if constexpr (NV4) {
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        const int col = nt * 16 + i16;
+        hexp[nt] = reinterpret_cast<const int*>(lds + (col < mp ? col : mp - 1) * row_chunks + s4)[0];
+      }
+    }
+  };
+  if (!early) load_hidden();
   u32x4* stage = lds + mp * row_chunks + wave * 16 * SC;
   // MX4 / NV4: this wave's scale stage, SPR 16-byte chunks (16 k-steps) per row
   u32x4* sstage = lds + mp * row_chunks + WV * 16 * SC + wave * 16 * SPR;
@@ -2097,12 +2229,12 @@ proj_mfma(const uint16_t* __restrict__ h, const void* __restrict__ Wv, const voi
     } else if constexpr (NV4) {
       // the lane's 8 codes (elements 8 g .. 8 g + 7 of the k-step) share the
       // block scale of block 2 sb + g / 2: both of the k-step's scale codes
-      // are read as one 16-bit word and decoded by the gfx950 E4M3
-      // conversion (scale 1: exact)
+      // are read as one 16-bit word and decoded to f16 by the gfx950 E4M3
+      // conversion (scale 1: exact, every E4M3 value is a normal f16 number)
       const uint32_t codes = reinterpret_cast<const uint32_t*>(stage)[(i16 * SC + sb) * 4 + g];
       const uint32_t pair = reinterpret_cast<const uint16_t*>(sstage)[i16 * 16 + sb];
-      const auto sc2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(pair, 1.0f, false);
-      return fp4x8_times_scale_to_bf16x8(codes, (g >> 1) ? sc2[1] : sc2[0]);
+      const f16x2 sc2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(pair, 1.0f, false);
+      return fp4x8_times_scale_to_f16x8(codes, (g >> 1) ? sc2[1] : sc2[0]);
     } else if constexpr (MX4) {
       const uint32_t codes = reinterpret_cast<const uint32_t*>(stage)[(i16 * SC + sb) * 4 + g];
       const uint32_t e = reinterpret_cast<const uint8_t*>(sstage)[i16 * 16 + sb];
@@ -2115,8 +2247,12 @@ proj_mfma(const uint16_t* __restrict__ h, const void* __restrict__ Wv, const voi
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
       const u32x4 bf = bptr[nt][s * 4];
-      acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
-                                                        __builtin_bit_cast(bf16x8, bf), acc[nt], 0, 0, 0);
+      if constexpr (NV4)
+        acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
+                                                         __builtin_bit_cast(f16x8, bf), acc[nt], 0, 0, 0);
+      else
+        acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                          __builtin_bit_cast(bf16x8, bf), acc[nt], 0, 0, 0);
     }
   };
   auto consume = [&](const u32x4 (&buf)[LPB], const u32x4& sbuf, int b) __attribute__((always_inline)) {
@@ -2176,11 +2312,12 @@ proj_mfma(const uint16_t* __restrict__ h, const void* __restrict__ Wv, const voi
       }
       load_scales(tile + tstride);
     } else if constexpr (NV4) {
-      // the head's scale, once per row sum
+      // the hidden row's power of two off (exact), then the head's scale,
+      // once per row sum
 #pragma unroll
       for (int v = 0; v < 4; ++v)
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt) acc[nt][v] *= gscale;
+        for (int nt = 0; nt < NT; ++nt) acc[nt][v] = __builtin_ldexpf(acc[nt][v], -hexp[nt]) * gscale;
     }
     if (LOGITS && vec_logits && r0 + 4 * g + 3 < R) {
 #pragma unroll
@@ -2250,10 +2387,7 @@ proj_mfma(const uint16_t* __restrict__ h, const void* __restrict__ Wv, const voi
     advance(ti, bi);
   }
 
-  if (early) {
-    stage_hidden<64 * WV, NT == 2 ? 16 : 8>(h + (size_t)m_base * K, K, mp, s4, row_chunks, lds);
-    __syncthreads();
-  }
+  if (early) load_hidden();
 
   auto step = [&](auto jc) __attribute__((always_inline)) {
     constexpr int j = decltype(jc)::value;
