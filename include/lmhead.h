@@ -458,9 +458,14 @@ int lmhead_nvfp4_tile_scales(const uint8_t* src, int64_t R, int64_t K, uint8_t* 
 /*
  * draft_project_argmax_nvfp4 -- draft_project_argmax over an NVFP4 head
  * from lmhead_quantize_nvfp4: out_logit[m] = max_r g * sum_k h[m, k] *
- * e2m1(Wq[r, k]) * e4m3(scale of block k / 16 of row r); each element times
- * its block scale is a bf16 number (at most 6 significant bits), so every
- * product is exact, the sums are fp32 and g multiplies each row's sum once.
+ * e2m1(Wq[r, k]) * e4m3(scale of block k / 16 of row r).  Each element
+ * times its block scale is a normal f16 number (at most 6 significant bits)
+ * and each hidden row is taken as f16 times a power of two that puts its
+ * largest magnitude in [2^15, 2^16), so every product of an element and a
+ * hidden value within 2^29 of its row's largest is exact (a smaller hidden
+ * value may be rounded or flushed in f16, an error of at most its own
+ * magnitude); the sums are fp32, the power of two comes off exactly and g
+ * multiplies each row's sum once.
  * out_id as for draft_project_argmax (first row among equal maxima, mapped
  * through d2t).  The head streams at 0.5625 bytes per weight (codes and
  * block scales).  The matrix cores take every M.
