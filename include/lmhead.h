@@ -609,14 +609,14 @@ int lmhead_shortlist_union(const int32_t* a, int64_t na, const int32_t* b,
                            int64_t nb, int64_t N, int32_t* out,
                            int64_t out_cap, int32_t* counts, void* stream);
 
-/* Which kernel draft_project_argmax picks for (M, K) over a head of at
- * least 131,072 rows (the full head): an LMH_PATH_* value, or -1 if the
- * shape is not accepted. */
+/* Which kernel draft_project_argmax picks for (M, K): an LMH_PATH_* value
+ * (the VALU kernels up to 4 hidden rows where they accept K, the matrix
+ * cores above), or -1 if the shape is not accepted.  The same for every
+ * head size and for rows read in place through a list. */
 int draft_project_auto_path(int64_t M, int64_t K);
 
-/* The same for a head of R rows (the choice depends on the head size at
- * M = 4: the matrix cores below 131,072 rows).  -1 if the shape is not
- * accepted.  Indexed calls keep the VALU kernel up to M = 4. */
+/* The same, also checking a head of R rows: -1 if (M, K, R) is not
+ * accepted (R outside [1, LMH_MAX_R]). */
 int draft_project_auto_path_rows(int64_t M, int64_t K, int64_t R);
 
 /* Static text for a status code. */

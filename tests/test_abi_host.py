@@ -86,14 +86,18 @@ def test_fused_state_size(L):
 
 
 def test_auto_path_by_head_size(L):
-    # four hidden rows: matrix cores below 131,072 head rows, VALU above
-    assert L.draft_project_auto_path_rows(4, 2560, 32768) == L.LMH_PATH_MFMA
-    assert L.draft_project_auto_path_rows(4, 2560, 131071) == L.LMH_PATH_MFMA
+    # the head's size does not change the choice: VALU up to four hidden
+    # rows, matrix cores from five, on lists and on the full head
+    assert L.draft_project_auto_path_rows(4, 2560, 32768) == L.LMH_PATH_VALU
+    assert L.draft_project_auto_path_rows(4, 2560, 131071) == L.LMH_PATH_VALU
     assert L.draft_project_auto_path_rows(4, 2560, 131072) == L.LMH_PATH_VALU
     assert L.draft_project_auto_path_rows(4, 2560, 248320) == L.LMH_PATH_VALU
     for m in (1, 2, 3):
         assert L.draft_project_auto_path_rows(m, 2560, 16000) == L.LMH_PATH_VALU
     assert L.draft_project_auto_path_rows(5, 2560, 248320) == L.LMH_PATH_MFMA
+    assert L.draft_project_auto_path_rows(5, 2560, 16000) == L.LMH_PATH_MFMA
+    assert L.draft_project_auto_path_rows(4, 2560, (1 << 30) - 1) == L.LMH_PATH_VALU
+    assert L.draft_project_auto_path_rows(4, 2560, 1 << 30) == -1
     assert L.draft_project_auto_path_rows(4, 2560, 0) == -1
     assert L.draft_project_auto_path_rows(0, 2560, 100) == -1
 

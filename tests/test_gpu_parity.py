@@ -159,16 +159,18 @@ def test_full_head_two_and_three_rows(L, m):
 
 @pytest.mark.parametrize("r", [131_071, 131_072])
 def test_four_rows_at_the_head_size_boundary(L, r):
-    """The argmax at M = 4 takes the matrix cores below 131,072 head rows
-    and VALU from there on: on both sides of the boundary the default call
-    matches the oracle and, bit for bit, the kernel that the rule names."""
+    """The argmax at M = 4 takes the VALU kernel on both sides of 131,072
+    head rows (the size where the one- and two-row argmax change their load
+    loop): on both sides the default call matches the oracle and, bit for
+    bit, the VALU kernel, and the matrix-core kernel meets the parity rule
+    too."""
     inp = config_inputs(2)
     c = inp["config"]
     w_np, w_dev = inp["W"][:r], device_weights(2)[:r]
-    want = L.LMH_PATH_MFMA if r < 131_072 else L.LMH_PATH_VALU
+    want = L.LMH_PATH_VALU
     assert L.draft_project_auto_path_rows(4, c.k, r) == want
     hs = [synth.hidden(4040, d, 4, c.k) for d in range(16)]
-    run_and_check(L, hs, w_np, w_dev, None, [L.LMH_PATH_AUTO], f"{r} rows M=4")
+    run_and_check(L, hs, w_np, w_dev, None, [L.LMH_PATH_AUTO, L.LMH_PATH_MFMA], f"{r} rows M=4")
     for h in hs:
         a = L.draft_project_argmax_path(dev_bf16(h), w_dev, None, L.LMH_PATH_AUTO)
         b = L.draft_project_argmax_path(dev_bf16(h), w_dev, None, want)

@@ -129,10 +129,7 @@ typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 #define LMH_WAVE_MAJOR 0          // 1: hand out work units wave-major (see first_unit)
 #endif
 #ifndef LMH_RING_MAX_ROWS
-#define LMH_RING_MAX_ROWS 131072  // VALU argmax over fewer head rows than this uses the ring loop
-#endif
-#ifndef LMH_M4_MFMA_MAX_ROWS
-#define LMH_M4_MFMA_MAX_ROWS 131072  // an argmax over 4 hidden rows and fewer head rows takes the matrix cores
+#define LMH_RING_MAX_ROWS 131072  // VALU argmax at 1-2 hidden rows over fewer head rows than this: ring loop
 #endif
 #ifndef LMH_VALU_WAVES
 #define LMH_VALU_WAVES 4          // waves per workgroup (VALU path)
@@ -2638,8 +2635,13 @@ template <int M, int CPL, int WV, int TK, bool LOGITS, bool IDX, int LOOP>
 void row_plan(ValuPlan& p) {
   if constexpr (M * CPL <= kValuMaxChunksTimesM) {
     // rows per step: keep each of the two row buffers at <= 10 chunks/lane,
-    // and one row per step once h alone takes more than 80 registers
-    constexpr int U0 = M * CPL > 20 ? 1 : (CPL * LMH_VALU_ROWS <= 10 ? LMH_VALU_ROWS : (CPL <= 10 ? 10 / CPL : 1));
+    // and one row per step once h alone takes more than 80 registers.  The
+    // ring loop at 3 and 4 hidden rows takes one row per step: 1.4-5.2%
+    // faster on the 16,000-, 32,768- and 52,755-row lists and 1.1-4.5% on
+    // lists read in place (interleaved builds on one machine); the pair loop
+    // at those M is 8-17% slower so.
+    constexpr bool kOne = M * CPL > 20 || (LOOP == kLoopRing && (M == 3 || M == 4));
+    constexpr int U0 = kOne ? 1 : (CPL * LMH_VALU_ROWS <= 10 ? LMH_VALU_ROWS : (CPL <= 10 ? 10 / CPL : 1));
     constexpr int U = U0 < 1 ? 1 : U0;
     p.fn = proj_valu_rows<M, CPL, U, WV, TK, LOGITS, IDX, LOOP>;
     p.waves = WV;
@@ -2664,14 +2666,16 @@ ValuPlan tiled_plan(int K) {
   return p;
 }
 
-// Row-order plan for M = 1..4 with the argmax loop chosen by the head's row
-// count (the ring below LMH_RING_MAX_ROWS rows); other epilogues keep the
-// two-buffer loop.
+// Row-order plan for M = 1..4.  The argmax takes the ring loop at 3 and 4
+// hidden rows on every head (with one row per step: 1.6-2.8% faster than
+// the two-buffer loop on heads of 131,072-248,320 rows at three rows, up to
+// 1.7% at four), and at 1 and 2 rows below LMH_RING_MAX_ROWS head rows;
+// other epilogues keep the two-buffer loop.
 template <int M, int TK, bool LOGITS, bool IDX>
 void row_plan_m(ValuPlan& p, int cpl, int64_t R) {
   using seq = std::make_integer_sequence<int, 16>;
   if constexpr (TK == 1 && !LOGITS) {
-    if (R < LMH_RING_MAX_ROWS) {
+    if (M >= 3 || R < LMH_RING_MAX_ROWS) {
       row_plan_cpl<M, TK, LOGITS, IDX, kLoopRing>(p, cpl, seq{});
       return;
     }
@@ -2979,30 +2983,25 @@ int run(const Call& c, const Epi& epi, int topk, int32_t* out_id, float* out_log
 bool valu_epi_ok(int64_t M, int64_t K) { return M <= 4 && valu_ok(M, K); }
 
 // Shared argument checks; returns LMH_OK and the resolved path, or a status.
-// The default kernel of a call with M hidden rows over R head rows (mode 0:
-// argmax, else top k / logits; `indexed`: rows read in place through a
-// list).  VALU up to 4 hidden rows, matrix cores above, measured on the
-// full head.  Exception, measured on the lists: an argmax over 4 hidden
-// rows and a head of fewer than LMH_M4_MFMA_MAX_ROWS rows runs 1-4% faster on
-// the matrix cores (32,768 rows: 27.24 against 28.37 us; 16,000: 15.39
-// against 15.67; 52,755: 43.09 against 43.60), while on the full head the
-// VALU kernel is 2% faster (179.4 against 183.3 us).  Read in place through
-// a list the matrix cores are slower at 16,000 and 52,755 rows, so indexed
-// calls keep the VALU kernel.
-int default_path(int64_t M, int64_t K, int64_t R, int mode, bool indexed) {
+// The default kernel of a call with M hidden rows (mode 0: argmax, else top
+// k / logits): VALU up to 4 hidden rows, matrix cores above.  Measured under
+// rocprofv3 on the full head and the 16,000-, 32,768- and 52,755-row lists
+// at 3, 4, 5 and 8 hidden rows: the VALU kernel is 0.6-4.5% faster at 3
+// and 4 rows on every head (one row per step in the ring loop of the
+// lists), the matrix cores 2.1-10.6% faster at 5.  The head's size does
+// not enter the choice, nor whether its rows are read in place.
+int default_path(int64_t M, int64_t K, int mode) {
   if (M > LMH_VALU_AUTO_MAX_M || !(mode == 0 ? valu_ok(M, K) : valu_epi_ok(M, K))) return LMH_PATH_MFMA;
-  if (mode == 0 && !indexed && M == 4 && R < LMH_M4_MFMA_MAX_ROWS) return LMH_PATH_MFMA;
   return LMH_PATH_VALU;
 }
 
-int check_common(const uint16_t* h, int64_t M, int64_t K, const uint16_t* W, int64_t R, int mode, int* path,
-                 bool indexed = false) {
+int check_common(const uint16_t* h, int64_t M, int64_t K, const uint16_t* W, int64_t R, int mode, int* path) {
   if (!h || !W) return LMH_EINVAL;
   if (M < 1 || M > LMH_MAX_M || !k_ok(K)) return LMH_EINVAL;
   if (R < 1 || R > kMaxRows) return LMH_EINVAL;
   if (!aligned16(h) || !aligned16(W)) return LMH_EINVAL;
   if (*path != LMH_PATH_AUTO && *path != LMH_PATH_VALU && *path != LMH_PATH_MFMA) return LMH_EINVAL;
-  if (*path == LMH_PATH_AUTO) *path = default_path(M, K, R, mode, indexed);
+  if (*path == LMH_PATH_AUTO) *path = default_path(M, K, mode);
   if (*path == LMH_PATH_VALU && !(mode == 0 ? valu_ok(M, K) : valu_epi_ok(M, K))) return LMH_EINVAL;
   return LMH_OK;
 }
@@ -3184,12 +3183,12 @@ size_t draft_project_workspace_bytes(int64_t M) {
 
 int draft_project_auto_path(int64_t M, int64_t K) {
   if (M < 1 || M > LMH_MAX_M || !k_ok(K)) return -1;
-  return default_path(M, K, kMaxRows, 0, false);
+  return default_path(M, K, 0);
 }
 
 int draft_project_auto_path_rows(int64_t M, int64_t K, int64_t R) {
   if (M < 1 || M > LMH_MAX_M || !k_ok(K) || R < 1 || R > kMaxRows) return -1;
-  return default_path(M, K, R, 0, false);
+  return default_path(M, K, 0);
 }
 
 int draft_project_argmax_path(const uint16_t* h, int64_t M, int64_t K, const uint16_t* W, int64_t R,
@@ -3215,7 +3214,7 @@ int draft_project_argmax(const uint16_t* h, int64_t M, int64_t K, const uint16_t
 int draft_project_argmax_indexed(const uint16_t* h, int64_t M, int64_t K, const uint16_t* W, int64_t N,
                                  const int32_t* ids, int64_t S, int32_t* out_id, float* out_logit, void* workspace,
                                  size_t workspace_bytes, int path, void* stream) {
-  int st = check_common(h, M, K, W, S, 0, &path, true);
+  int st = check_common(h, M, K, W, S, 0, &path);
   if (st != LMH_OK) return st;
   if (N < 1 || N > (int64_t)0x7FFFFFFF || !ids || (reinterpret_cast<uintptr_t>(ids) & 3u) != 0) return LMH_EINVAL;
   if (!out_id || !out_logit) return LMH_EINVAL;
@@ -3668,7 +3667,7 @@ int lmhead_bench_time_argmax_indexed(const uint16_t* h, int64_t M, int64_t K, co
   int st = LMH_OK;
   for (int i = 0; i < nheads; ++i) {
     path = path_in;
-    if ((st = check_common(h, M, K, heads[i], S, 0, &path, true)) != LMH_OK) return st;
+    if ((st = check_common(h, M, K, heads[i], S, 0, &path)) != LMH_OK) return st;
   }
   if (N < 1 || N > (int64_t)0x7FFFFFFF || !ids || (reinterpret_cast<uintptr_t>(ids) & 3u) != 0) return LMH_EINVAL;
   if (!out_id || !out_logit) return LMH_EINVAL;
