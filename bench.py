@@ -83,11 +83,13 @@ def source_digest() -> str:
     return hashlib.sha256(code.encode("utf-8")).hexdigest()[:16]
 
 
-def kernel_name(path: str, m: int) -> str:
-    """The projection kernel a call runs (the plan in the library's host code)."""
+def kernel_name(path: str, m: int, indexed: bool = False) -> str:
+    """The projection kernel a call runs (the plan in the library's host code:
+    the tiled kernel at one and two hidden rows, except over rows read in
+    place through a list, which take the row-order kernel)."""
     if path == "mfma":
         return "proj_mfma"
-    return "proj_valu_tiled" if m <= 2 else "proj_valu_rows"
+    return "proj_valu_tiled" if m <= 2 and not indexed else "proj_valu_rows"
 
 
 def describe(a, synth, L):
@@ -171,7 +173,7 @@ def describe(a, synth, L):
             workload = f"{c.name}: M={m} K={c.k} trimmed to {rows} rows ({copies} rotated copies)"
         workload += ", NVFP4 head (E2M1, E4M3 scale per 16, fp32 head scale)"
     fmt = "fp8" if a.fp8 else ("mxfp4" if a.mxfp4 else ("nvfp4" if a.nvfp4 else "bf16"))
-    kname = kernel_name(kpath, m) if fmt == "bf16" else ("proj_mfma" if kpath == "mfma" else "proj_valu_fp8")
+    kname = kernel_name(kpath, m, a.indexed) if fmt == "bf16" else ("proj_mfma" if kpath == "mfma" else "proj_valu_fp8")
     return dict(inp=inp, c=c, m=m, ids=ids, trimmed=trimmed, path=path, kpath=kpath, rows=rows,
                 copies=copies, workload=workload, kname=kname, fmt=fmt)
 

@@ -107,7 +107,7 @@ def _counter_csv(path, counter, rows):
 
 def test_record_and_look_up_traffic(tmp_path, monkeypatch):
     monkeypatch.setattr(bench, "TRAFFIC_FILE", str(tmp_path / "traffic.json"))
-    kern = "void (anonymous namespace)::proj_valu_tiled<1, 4, 4, 1, false, false, 1>(unsigned short const*)"
+    kern = "void (anonymous namespace)::proj_valu_tiled<1, 4, 4, 1, false, 1>(unsigned short const*)"
     fold = "(anonymous namespace)::finalize_argmax(unsigned long long const*, int)"
     gib_kib = (1 << 30) / 1024
     # the fetch counter reads half the bytes (as on MI355X), the write counter all of them
@@ -170,3 +170,15 @@ def test_traffic_table_lists_every_entry():
     assert len(rows) == len(entries)
     for e, ln in zip(entries, rows):
         assert e["workload"] in ln and f"{e['bytes_projection_kernel']:,}" in ln
+
+
+def test_kernel_name_follows_the_library_plan():
+    """The kernel whose counters and times a bench line reports: the tiled
+    VALU kernel at one and two hidden rows over a head or trimmed list, the
+    row-order kernel from three rows and for rows read in place."""
+    assert bench.kernel_name("valu", 1) == "proj_valu_tiled"
+    assert bench.kernel_name("valu", 2) == "proj_valu_tiled"
+    assert bench.kernel_name("valu", 1, True) == "proj_valu_rows"
+    assert bench.kernel_name("valu", 2, True) == "proj_valu_rows"
+    assert bench.kernel_name("valu", 3) == "proj_valu_rows"
+    assert bench.kernel_name("mfma", 1) == "proj_mfma"

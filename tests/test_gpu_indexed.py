@@ -256,9 +256,10 @@ def test_indexed_bench_helper_matches_call(L):
 
 @pytest.mark.parametrize("m", [1, 3, 24])
 def test_indexed_long_list_takes_the_large_head_loops(L, m):
-    """A list of at least 131,072 entries takes the loops chosen for large
-    heads (unconditional issue at M = 1, the two-buffer loop at M = 2-4):
-    a shuffled 150,000-id list of the full head, with a few invalid ids."""
+    """A list of at least 131,072 entries (the size where trimmed heads at
+    one and two hidden rows change their load loop; lists read in place
+    keep the row-order kernel's ring loop): a shuffled 150,000-id list of
+    the full head, with a few invalid ids."""
     inp = config_inputs(2)
     c = inp["config"]
     rng = np.random.default_rng(91 + m)

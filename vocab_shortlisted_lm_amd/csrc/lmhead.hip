@@ -1537,17 +1537,11 @@ proj_valu_rows(const uint16_t* __restrict__ h, const uint16_t* __restrict__ W, i
 // row) in its lanes.  One batch is TR rows x 1 KiB; the next batch is in
 // flight while this one is scored.  Hidden rows live in LDS, zero-padded to
 // whole stripes, so the batch loop is a plain runtime loop.  The epilogue
-// (argmax, top-TK or every logit) is chosen by TK and LOGITS.
-//
-// IDX: the tile's rows are list entries; row q of a tile is row
-// epi.rowmap[tile * TR + q] of W, each with its own descriptor.  The ids of
-// the wave's next tile are fetched with a vector load when a tile starts,
-// so they have long arrived (loads complete in order) when that tile starts;
-// a row with an id outside [0, nw) reads nothing and is left out.
-template <int M, int TR, int WV, int TK, bool LOGITS, bool IDX = false, int LOOP = kLoopPair>
+// (argmax, top-TK or every logit) is chosen by TK and LOGITS.  Rows read in
+// place through a list take the row-order kernel.
+template <int M, int TR, int WV, int TK, bool LOGITS, int LOOP = kLoopPair>
 __global__ void __launch_bounds__(64 * WV)
 proj_valu_tiled(const uint16_t* __restrict__ h, const uint16_t* __restrict__ W, int R, int K, Epi epi) {
-  static_assert(!IDX || (TK == 1 && !LOGITS && TR <= 64), "indexed rows: argmax epilogue");
   extern __shared__ u32x4 h_stripes[];  // [M][nb * 64] chunks, zero past K
   const int lane = threadIdx.x & 63;
   const int wave = wave_id();
@@ -1575,49 +1569,21 @@ proj_valu_tiled(const uint16_t* __restrict__ h, const uint16_t* __restrict__ W, 
   const int ntiles = (R + TR - 1) / TR;
   const int tstride = gridDim.x * WV;
 
-  // IDX: ids of the rows being issued (wave-uniform) and, in lane q < TR,
-  // the id of row q of the wave's next tile.
-  int rid[IDX ? TR : 1];
-  int vnext = -1;
-  auto fetch_next_ids = [&](int tile) {
-    vnext = load_row_id(epi.rowmap, R, tile * TR + (lane < TR ? lane : 0));
-  };
-
   // One descriptor per tile covering its live rows: offsets of rows past R
-  // (and of chunks past K) are >= num_records and read as zero.  IDX: one
-  // descriptor per row; `live` gets bit q for each row that takes part.
-  auto issue = [&](u32x4 (&w)[TR], int& live, int tile, int j) {
+  // (and of chunks past K) are >= num_records and read as zero.
+  auto issue = [&](u32x4 (&w)[TR], int tile, int j) {
     const int c = lane + 64 * j;
     const int r0 = tile * TR;
     const uint32_t off = c < chunks ? (uint32_t)c * 16u : kOobOffset;
-    if constexpr (IDX) {
-      if (j == 0) {
+    // past the last tile (unconditional issue) the descriptor has no records
+    constexpr bool kUncond = LOOP == kLoopUncond;
+    const int nlive = kUncond ? __builtin_amdgcn_readfirstlane(max(0, min(TR, R - r0))) : min(TR, R - r0);
+    const int rbase = kUncond ? __builtin_amdgcn_readfirstlane(nlive == 0 ? 0 : r0) : r0;
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(W + (size_t)rbase * (size_t)K, (uint32_t)nlive * row_bytes);
 #pragma unroll
-        for (int q = 0; q < TR; ++q) rid[q] = __builtin_amdgcn_readlane(vnext, q);
-        fetch_next_ids(tile + tstride);
-      }
-      int bits = 0;
-#pragma unroll
-      for (int q = 0; q < TR; ++q) {
-        const bool ok = r0 + q < R && row_id_ok(rid[q], epi.nw);
-        bits |= ok ? (1 << q) : 0;
-        const __amdgpu_buffer_rsrc_t rs =
-            make_rsrc(W + (size_t)(ok ? rid[q] : 0) * (size_t)K, ok ? row_bytes : 0u);
-        w[q] = load16(rs, off);
-      }
-      live = bits;
-    } else {
-      // past the last tile (unconditional issue) the descriptor has no records
-      constexpr bool kUncond = LOOP == kLoopUncond;
-      const int nlive = kUncond ? __builtin_amdgcn_readfirstlane(max(0, min(TR, R - r0))) : min(TR, R - r0);
-      const int rbase = kUncond ? __builtin_amdgcn_readfirstlane(nlive == 0 ? 0 : r0) : r0;
-      const __amdgpu_buffer_rsrc_t rs = make_rsrc(W + (size_t)rbase * (size_t)K, (uint32_t)nlive * row_bytes);
-#pragma unroll
-      for (int q = 0; q < TR; ++q) w[q] = load16(rs, off + (uint32_t)q * row_bytes);
-      live = (1 << TR) - 1;
-    }
+    for (int q = 0; q < TR; ++q) w[q] = load16(rs, off + (uint32_t)q * row_bytes);
   };
-  auto consume = [&](const u32x4 (&w)[TR], int live, int tile, int j) {
+  auto consume = [&](const u32x4 (&w)[TR], int tile, int j) {
 #pragma unroll
     for (int m = 0; m < M; ++m) {
       const u32x4 hv = h_stripes[m * hc + j * 64 + lane];
@@ -1634,7 +1600,7 @@ proj_valu_tiled(const uint16_t* __restrict__ h, const uint16_t* __restrict__ W, 
           sum[m] = wave_sum(acc[q][m]);
           acc[q][m] = 0.0f;
         }
-        if (r0 + q < R && (!IDX || ((live >> q) & 1))) ep.row(sum, r0 + q, lane, epi);
+        if (r0 + q < R) ep.row(sum, r0 + q, lane, epi);
       }
     }
   };
@@ -1650,62 +1616,33 @@ proj_valu_tiled(const uint16_t* __restrict__ h, const uint16_t* __restrict__ W, 
     // batches: D - 1 are in flight while one is scored.  The steady state is
     // unrolled D times so ring slots are static and every slot issues and
     // consumes without conditions; positions past the wave's last one read
-    // through descriptors with no records (nothing is fetched).  IDX: ring
-    // slot S also keeps, in lane q < TR, the ids of the tile its next
-    // position will read, loaded D positions ahead.
+    // through descriptors with no records (nothing is fetched).
     constexpr int D = kRingDepth;
     const int tile0 = first_unit(wave, WV);
     const int my_tiles = tile0 < ntiles ? (ntiles - 1 - tile0) / tstride + 1 : 0;
     const int count = my_tiles * nb;
     {
       u32x4 ring[D][TR];
-      int live[D];
-      int vid[IDX ? D : 1];
       int ti = tile0, ji = 0;  // next position to issue
-      int ta = tile0, ja = 0;  // position D ahead of it (IDX ids)
       int tc = tile0, jc = 0;  // next position to consume
-      auto id_lane = [&](int tile) { return load_row_id(epi.rowmap, R, tile * TR + (lane < TR ? lane : 0)); };
       auto issue_at = [&](auto slot) __attribute__((always_inline)) {
         constexpr int S = decltype(slot)::value;
         const int c = lane + 64 * ji;
         const uint32_t off = c < chunks ? (uint32_t)c * 16u : kOobOffset;
         const int r0 = ti * TR;
-        if constexpr (IDX) {
-          int bits = 0;
+        const int nlive = __builtin_amdgcn_readfirstlane(max(0, min(TR, R - r0)));
+        const int rbase = __builtin_amdgcn_readfirstlane(nlive > 0 ? r0 : 0);
+        const __amdgpu_buffer_rsrc_t rs = make_rsrc(W + (size_t)rbase * (size_t)K, (uint32_t)nlive * row_bytes);
 #pragma unroll
-          for (int q = 0; q < TR; ++q) {
-            const int id = __builtin_amdgcn_readlane(vid[S], q);
-            const bool ok = r0 + q < R && row_id_ok(id, epi.nw);
-            bits |= ok ? (1 << q) : 0;
-            const __amdgpu_buffer_rsrc_t rs = make_rsrc(W + (size_t)(ok ? id : 0) * (size_t)K, ok ? row_bytes : 0u);
-            ring[S][q] = load16(rs, off);
-          }
-          live[S] = bits;
-          vid[S] = id_lane(ta);
-          advance(ta, ja);
-        } else {
-          const int nlive = __builtin_amdgcn_readfirstlane(max(0, min(TR, R - r0)));
-          const int rbase = __builtin_amdgcn_readfirstlane(nlive > 0 ? r0 : 0);
-          const __amdgpu_buffer_rsrc_t rs = make_rsrc(W + (size_t)rbase * (size_t)K, (uint32_t)nlive * row_bytes);
-#pragma unroll
-          for (int q = 0; q < TR; ++q) ring[S][q] = load16(rs, off + (uint32_t)q * row_bytes);
-          live[S] = (1 << TR) - 1;
-        }
+        for (int q = 0; q < TR; ++q) ring[S][q] = load16(rs, off + (uint32_t)q * row_bytes);
         advance(ti, ji);
       };
       auto consume_at = [&](auto slot) __attribute__((always_inline)) {
         constexpr int S = decltype(slot)::value;
-        consume(ring[S], live[S], tc, jc);
+        consume(ring[S], tc, jc);
         advance(tc, jc);
       };
       if (count > 0) {
-        if constexpr (IDX) {
-#pragma unroll
-          for (int q = 0; q < D; ++q) {
-            vid[q] = id_lane(ta);
-            advance(ta, ja);
-          }
-        }
         [&]<int... J>(std::integer_sequence<int, J...>) {
           (issue_at(std::integral_constant<int, J>{}), ...);
         }(std::make_integer_sequence<int, D - 1>{});
@@ -1732,30 +1669,26 @@ proj_valu_tiled(const uint16_t* __restrict__ h, const uint16_t* __restrict__ W, 
   int tile = first_unit(wave, WV);
   int j = 0;
   u32x4 wa[TR], wb[TR];
-  int la = 0, lb = 0;
   // the draining loop (top k and logits at M = 1) stages first: staged
   // after its first issue, the logits calls measured 6% slower (188 against
   // 177 us on the full head), top k unchanged
   if constexpr (LOOP == kLoopPair) stage_and_sync();
-  if (tile < ntiles) {
-    if constexpr (IDX) fetch_next_ids(tile);
-    issue(wa, la, tile, 0);
-  }
+  if (tile < ntiles) issue(wa, tile, 0);
   if constexpr (LOOP != kLoopPair) stage_and_sync();
   if (tile < ntiles) {
     while (true) {
       int t1 = tile, j1 = j;
       advance(t1, j1);
       bool more = t1 < ntiles;
-      if (LOOP == kLoopUncond || more) issue(wb, lb, t1, j1);
-      consume(wa, la, tile, j);
+      if (LOOP == kLoopUncond || more) issue(wb, t1, j1);
+      consume(wa, tile, j);
       if (!more) break;
       tile = t1;
       j = j1;
       advance(t1, j1);
       more = t1 < ntiles;
-      if (LOOP == kLoopUncond || more) issue(wa, la, t1, j1);
-      consume(wb, lb, tile, j);
+      if (LOOP == kLoopUncond || more) issue(wa, t1, j1);
+      consume(wb, tile, j);
       if (!more) break;
       tile = t1;
       j = j1;
@@ -2636,11 +2569,11 @@ void row_plan(ValuPlan& p) {
   if constexpr (M * CPL <= kValuMaxChunksTimesM) {
     // rows per step: keep each of the two row buffers at <= 10 chunks/lane,
     // and one row per step once h alone takes more than 80 registers.  The
-    // ring loop at 3 and 4 hidden rows takes one row per step: 1.4-5.2%
-    // faster on the 16,000-, 32,768- and 52,755-row lists and 1.1-4.5% on
-    // lists read in place (interleaved builds on one machine); the pair loop
-    // at those M is 8-17% slower so.
-    constexpr bool kOne = M * CPL > 20 || (LOOP == kLoopRing && (M == 3 || M == 4));
+    // ring loop at 3 and 4 hidden rows, and over rows read in place, takes
+    // one row per step: 1.4-5.2% faster on the 16,000-, 32,768- and
+    // 52,755-row lists and 1.1-4.5% on lists read in place (interleaved
+    // builds on one machine); the pair loop at those M is 8-17% slower so.
+    constexpr bool kOne = M * CPL > 20 || (LOOP == kLoopRing && (M == 3 || M == 4 || IDX));
     constexpr int U0 = kOne ? 1 : (CPL * LMH_VALU_ROWS <= 10 ? LMH_VALU_ROWS : (CPL <= 10 ? 10 / CPL : 1));
     constexpr int U = U0 < 1 ? 1 : U0;
     p.fn = proj_valu_rows<M, CPL, U, WV, TK, LOGITS, IDX, LOOP>;
@@ -2656,10 +2589,10 @@ void row_plan_cpl(ValuPlan& p, int cpl, std::integer_sequence<int, C...>) {
   ((cpl == C + 1 ? (row_plan<M, C + 1, WV, TK, LOGITS, IDX, LOOP>(p), 0) : 0), ...);
 }
 
-template <int M, int TK, bool LOGITS, bool IDX, int LOOP>
+template <int M, int TK, bool LOGITS, int LOOP>
 ValuPlan tiled_plan(int K) {
   ValuPlan p;
-  p.fn = proj_valu_tiled<M, LMH_VALU_TILE_ROWS, LMH_VALU_WAVES, TK, LOGITS, IDX, LOOP>;
+  p.fn = proj_valu_tiled<M, LMH_VALU_TILE_ROWS, LMH_VALU_WAVES, TK, LOGITS, LOOP>;
   p.waves = LMH_VALU_WAVES;
   p.rows_per_wave = LMH_VALU_TILE_ROWS;
   p.lds = (size_t)M * chunks_per_lane(K) * 64 * 16;
@@ -2669,13 +2602,13 @@ ValuPlan tiled_plan(int K) {
 // Row-order plan for M = 1..4.  The argmax takes the ring loop at 3 and 4
 // hidden rows on every head (with one row per step: 1.6-2.8% faster than
 // the two-buffer loop on heads of 131,072-248,320 rows at three rows, up to
-// 1.7% at four), and at 1 and 2 rows below LMH_RING_MAX_ROWS head rows;
-// other epilogues keep the two-buffer loop.
+// 1.7% at four), over rows read in place, and at 1 and 2 rows below
+// LMH_RING_MAX_ROWS head rows; other epilogues keep the two-buffer loop.
 template <int M, int TK, bool LOGITS, bool IDX>
 void row_plan_m(ValuPlan& p, int cpl, int64_t R) {
   using seq = std::make_integer_sequence<int, 16>;
   if constexpr (TK == 1 && !LOGITS) {
-    if (M >= 3 || R < LMH_RING_MAX_ROWS) {
+    if (M >= 3 || IDX || R < LMH_RING_MAX_ROWS) {
       row_plan_cpl<M, TK, LOGITS, IDX, kLoopRing>(p, cpl, seq{});
       return;
     }
@@ -2689,18 +2622,25 @@ ValuPlan valu_plan(int M, int K, int64_t R) {
   // Two hidden rows (the verify step of a depth-1 draft): the tiled kernel
   // measured 2.2% faster than the row-order one on the full head (181.0
   // against 185.1 us) and level on lists; from three rows on it is slower
-  // (198.2 against 183.5 us at three, 229.6 against 178.6 at four).
-  if constexpr (TK == 1 && !LOGITS) {
-    if (M == 2 && LMH_VALU_TILE_ROWS > 0)
-      return R < LMH_RING_MAX_ROWS ? tiled_plan<2, TK, LOGITS, IDX, kLoopRing>(K)
-                                   : tiled_plan<2, TK, LOGITS, IDX, kLoopUncond>(K);
-  }
-  if (M == 1 && LMH_VALU_TILE_ROWS > 0) {
-    if constexpr (TK == 1 && !LOGITS)
-      return R < LMH_RING_MAX_ROWS ? tiled_plan<1, TK, LOGITS, IDX, kLoopRing>(K)
-                                   : tiled_plan<1, TK, LOGITS, IDX, kLoopUncond>(K);
-    else
-      return tiled_plan<1, TK, LOGITS, IDX, kLoopPair>(K);
+  // (198.2 against 183.5 us at three, 229.6 against 178.6 at four).  Rows
+  // read in place through a list (IDX) take the row-order kernel's ring
+  // loop with one row per step at one and two hidden rows too: 6-9% faster
+  // than the tiled kernel on the 16,000- and 32,768-row lists at M = 1,
+  // 10-11% at M = 2, 2.6% on the 52,755-row list at M = 1 (interleaved
+  // builds on one machine).
+  if constexpr (!IDX) {
+    if constexpr (TK == 1 && !LOGITS) {
+      if (M == 2 && LMH_VALU_TILE_ROWS > 0)
+        return R < LMH_RING_MAX_ROWS ? tiled_plan<2, TK, LOGITS, kLoopRing>(K)
+                                     : tiled_plan<2, TK, LOGITS, kLoopUncond>(K);
+    }
+    if (M == 1 && LMH_VALU_TILE_ROWS > 0) {
+      if constexpr (TK == 1 && !LOGITS)
+        return R < LMH_RING_MAX_ROWS ? tiled_plan<1, TK, LOGITS, kLoopRing>(K)
+                                     : tiled_plan<1, TK, LOGITS, kLoopUncond>(K);
+      else
+        return tiled_plan<1, TK, LOGITS, kLoopPair>(K);
+    }
   }
   const int cpl = chunks_per_lane(K);
   using seq = std::make_integer_sequence<int, 16>;
