@@ -2603,12 +2603,19 @@ ValuPlan tiled_plan(int K) {
 // hidden rows on every head (with one row per step: 1.6-2.8% faster than
 // the two-buffer loop on heads of 131,072-248,320 rows at three rows, up to
 // 1.7% at four), over rows read in place, and at 1 and 2 rows below
-// LMH_RING_MAX_ROWS head rows; other epilogues keep the two-buffer loop.
+// LMH_RING_MAX_ROWS head rows.  Top k takes it at 3 and 4 rows (the
+// 16,000-row list at M = 3 5% faster, the full head 1.3-1.5%); logits keep
+// the two-buffer loop (the ring made them 2-27% slower on the full head).
 template <int M, int TK, bool LOGITS, bool IDX>
 void row_plan_m(ValuPlan& p, int cpl, int64_t R) {
   using seq = std::make_integer_sequence<int, 16>;
   if constexpr (TK == 1 && !LOGITS) {
     if (M >= 3 || IDX || R < LMH_RING_MAX_ROWS) {
+      row_plan_cpl<M, TK, LOGITS, IDX, kLoopRing>(p, cpl, seq{});
+      return;
+    }
+  } else if constexpr (!LOGITS) {
+    if (M >= 3) {
       row_plan_cpl<M, TK, LOGITS, IDX, kLoopRing>(p, cpl, seq{});
       return;
     }
