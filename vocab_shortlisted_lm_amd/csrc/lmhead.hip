@@ -1295,6 +1295,14 @@ struct ValuEpilogue {
   float best[M];
   int bidx[M];
   RowTop16 top;
+  // LOGITS: lane i keeps the logits of the wave's i-th pending row; every
+  // 64 rows the wave stores them with M full-wave stores.  One store per
+  // row and hidden row from a single lane counted towards the same wait
+  // counter as the weight loads, and the loops' waits then covered them
+  // (logits at 3 and 4 hidden rows took 11% longer than the argmax).
+  float pend[LOGITS ? M : 1];
+  int prow;
+  int npend;
 
   __device__ __forceinline__ void init() {
 #pragma unroll
@@ -1303,14 +1311,24 @@ struct ValuEpilogue {
       bidx[m] = -1;
     }
     top.clear();
+    prow = -1;
+    npend = 0;
+  }
+  __device__ __forceinline__ void flush_logits(int lane, const Epi& e) {
+    if (lane < npend) {
+#pragma unroll
+      for (int m = 0; m < M; ++m) store_logit(e, m, prow, pend[m]);
+    }
+    npend = 0;
   }
   // head row r (< R) has logit sum[m] against hidden row m
   __device__ __forceinline__ void row(const float (&sum)[M], int r, int lane, const Epi& e) {
     if constexpr (LOGITS) {
-      if (lane == 0) {
+      const bool mine = lane == npend;
 #pragma unroll
-        for (int m = 0; m < M; ++m) store_logit(e, m, r, sum[m]);
-      }
+      for (int m = 0; m < M; ++m) pend[m] = mine ? sum[m] : pend[m];
+      prow = mine ? r : prow;
+      if (++npend == 64) flush_logits(lane, e);
     } else if constexpr (TK == 1) {
 #pragma unroll
       for (int m = 0; m < M; ++m) take_best(sum[m], r, best[m], bidx[m]);
@@ -1321,7 +1339,7 @@ struct ValuEpilogue {
   // fold the waves of the workgroup and publish its keys
   __device__ __forceinline__ void finish(int lane, int wave, const Epi& e) {
     if constexpr (LOGITS) {
-      return;
+      flush_logits(lane, e);
     } else if constexpr (TK == 1) {
       __shared__ unsigned long long s_key[WV][M];
       if (lane == 0) {
@@ -2604,8 +2622,9 @@ ValuPlan tiled_plan(int K) {
 // the two-buffer loop on heads of 131,072-248,320 rows at three rows, up to
 // 1.7% at four), over rows read in place, and at 1 and 2 rows below
 // LMH_RING_MAX_ROWS head rows.  Top k takes it at 3 and 4 rows (the
-// 16,000-row list at M = 3 5% faster, the full head 1.3-1.5%); logits keep
-// the two-buffer loop (the ring made them 2-27% slower on the full head).
+// 16,000-row list at M = 3 5% faster, the full head 1.3-1.5%); logits take
+// it below LMH_RING_MAX_ROWS head rows (2-6% faster on the lists, 1.7%
+// slower on the full head at 3 and 4 rows, with their stores batched).
 template <int M, int TK, bool LOGITS, bool IDX>
 void row_plan_m(ValuPlan& p, int cpl, int64_t R) {
   using seq = std::make_integer_sequence<int, 16>;
@@ -2616,6 +2635,11 @@ void row_plan_m(ValuPlan& p, int cpl, int64_t R) {
     }
   } else if constexpr (!LOGITS) {
     if (M >= 3) {
+      row_plan_cpl<M, TK, LOGITS, IDX, kLoopRing>(p, cpl, seq{});
+      return;
+    }
+  } else {
+    if (R < LMH_RING_MAX_ROWS) {
       row_plan_cpl<M, TK, LOGITS, IDX, kLoopRing>(p, cpl, seq{});
       return;
     }
@@ -2645,6 +2669,9 @@ ValuPlan valu_plan(int M, int K, int64_t R) {
       if constexpr (TK == 1 && !LOGITS)
         return R < LMH_RING_MAX_ROWS ? tiled_plan<1, TK, LOGITS, kLoopRing>(K)
                                      : tiled_plan<1, TK, LOGITS, kLoopUncond>(K);
+      else if constexpr (LOGITS)
+        return R < LMH_RING_MAX_ROWS ? tiled_plan<1, TK, LOGITS, kLoopRing>(K)
+                                     : tiled_plan<1, TK, LOGITS, kLoopPair>(K);
       else
         return tiled_plan<1, TK, LOGITS, kLoopPair>(K);
     }
