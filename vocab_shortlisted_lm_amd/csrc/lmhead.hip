@@ -413,6 +413,43 @@ __device__ __forceinline__ unsigned long long xrow_u64(unsigned long long k, int
   return ((unsigned long long)hi << 32) | lo;
 }
 
+// Four wave sums at once, each with wave_sum's association, so every
+// result equals wave_sum of that value bit for bit: lane pairs, then quads,
+// with the four values merged into one register by lane bits 0-1 (lane
+// 4 i + p of a quad ends up holding value p's quad sum), then the row
+// rotations and the row swaps (xor 16, xor 32) that wave_sum's reads of
+// lanes 0, 16, 32 and 48 and its (a + b) + (c + d) amount to.  About 21
+// instructions for four values against four times 14.
+__device__ __forceinline__ void wave_sum4(float x0, float x1, float x2, float x3, float (&out)[4]) {
+  const int lane = threadIdx.x & 63;
+  const bool b0 = (lane & 1) != 0, b1 = (lane & 2) != 0;
+  // even lanes keep value 0 (or 2) plus its odd neighbour's, odd lanes value 1 (or 3)
+  const float p01 = (b0 ? x1 : x0) + dpp<0xB1>(b0 ? x0 : x1);  // quad_perm [1,0,3,2]
+  const float p23 = (b0 ? x3 : x2) + dpp<0xB1>(b0 ? x2 : x3);
+  float q = (b1 ? p23 : p01) + dpp<0x4E>(b1 ? p01 : p23);     // quad_perm [2,3,0,1]
+  q += dpp<0x124>(q);  // row_ror:4
+  q += dpp<0x128>(q);  // row_ror:8  -> lane p of every 16-lane row: value p's row sum
+  const int row = lane >> 4;
+  q += __builtin_bit_cast(float, xrow_u32<16>(__builtin_bit_cast(uint32_t, q), row));
+  q += __builtin_bit_cast(float, xrow_u32<32>(__builtin_bit_cast(uint32_t, q), row));
+#pragma unroll
+  for (int p = 0; p < 4; ++p)
+    out[p] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, q), p));
+}
+
+// The wave sums of N values, four at a time (the last group padded).
+template <int N>
+__device__ __forceinline__ void wave_sums(const float (&x)[N], float (&out)[N]) {
+#pragma unroll
+  for (int g = 0; g < N; g += 4) {
+    float o[4];
+    wave_sum4(x[g], g + 1 < N ? x[g + 1] : 0.0f, g + 2 < N ? x[g + 2] : 0.0f, g + 3 < N ? x[g + 3] : 0.0f, o);
+#pragma unroll
+    for (int p = 0; p < 4; ++p)
+      if (g + p < N) out[g + p] = o[p];
+  }
+}
+
 // A lane's running top-TK: keys in descending order, 0 = empty slot.
 // push() inserts without branches over the list: position j takes
 // max(old[j], min(old[j - 1], x)), which shifts every key below x down one
@@ -1434,6 +1471,9 @@ proj_valu_rows(const uint16_t* __restrict__ h, const uint16_t* __restrict__ W, i
     }
     live = bits;
   };
+  // one wave_sum per row and hidden row: these independent chains measured
+  // 0.4-0.7% faster on the full head at 3 and 4 hidden rows than wave_sums'
+  // longer four-value chain
   auto score_rows = [&](const u32x4 (&w)[U][CPL], int live, int r0) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -1610,14 +1650,29 @@ proj_valu_tiled(const uint16_t* __restrict__ h, const uint16_t* __restrict__ W, 
     }
     if (j == nb - 1) {
       const int r0 = tile * TR;
+      // the tile's TR x M sums: one row at a time at M = 1 (four
+      // interleaved chains; one chain of four values measured 0.35% slower
+      // on the full head), else four at a time (the same bits; at M = 2 the
+      // full head 183.8 -> 180.2 us and the 32,768-row list 27.1 -> 26.8)
+      float part[TR * M], tot[TR * M];
+#pragma unroll
+      for (int q = 0; q < TR; ++q)
+#pragma unroll
+        for (int m = 0; m < M; ++m) {
+          part[q * M + m] = acc[q][m];
+          acc[q][m] = 0.0f;
+        }
+      if constexpr (M == 1) {
+#pragma unroll
+        for (int q = 0; q < TR; ++q) tot[q] = wave_sum(part[q]);
+      } else {
+        wave_sums<TR * M>(part, tot);
+      }
 #pragma unroll
       for (int q = 0; q < TR; ++q) {
         float sum[M];
 #pragma unroll
-        for (int m = 0; m < M; ++m) {
-          sum[m] = wave_sum(acc[q][m]);
-          acc[q][m] = 0.0f;
-        }
+        for (int m = 0; m < M; ++m) sum[m] = tot[q * M + m];
         if (r0 + q < R) ep.row(sum, r0 + q, lane, epi);
       }
     }
