@@ -2296,9 +2296,11 @@ proj_mfma(const uint16_t* __restrict__ h, const void* __restrict__ Wv, const voi
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   };
   // Logits without d2t: lane (g, i16) holds head rows 4 g .. 4 g + 3 of its
-  // column, one 16-byte store where the row block is whole and aligned.
-  // Whole tiles are held in a shift register of kLogitTiles tiles and
-  // stored together when it fills and at the end: on this chip stores count
+  // column, one 16-byte store where the row block is whole and aligned;
+  // through d2t, one store per row and column.  Whole tiles are held in a
+  // shift register of kLogitTiles tiles and stored together when it fills
+  // and at the end (through d2t a tile at a time, after loading its
+  // columns): on this chip stores count
   // towards the same wait counter as the weight loads, so a store after
   // every tile made later waits stall on its acknowledgement (the full head
   // at 16 and 24 hidden rows took 28 and 36 us longer than without the
@@ -2310,14 +2312,39 @@ proj_mfma(const uint16_t* __restrict__ h, const void* __restrict__ Wv, const voi
   int lbase[kLogitTiles];
   int nbuf = 0;
   auto flush_logits = [&]() __attribute__((always_inline)) {
+    if (epi.d2t) {
+      // scattered through d2t, a tile at a time: its rows' vocabulary
+      // columns, then its stores (the first wait drains the loads in
+      // flight once per flush, the later ones only these columns)
 #pragma unroll
-    for (int k = 0; k < kLogitTiles; ++k) {
-      if (k < nbuf) {
+      for (int k = 0; k < kLogitTiles; ++k) {
+        if (k < nbuf) {
+          int dcol[4];
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt) {
-          const int col = nt * 16 + i16;
-          if (col < mp)
-            *reinterpret_cast<f32x4*>(epi.logits + (int64_t)(m_base + col) * epi.ld + lbase[k] + 4 * g) = lbuf[k][nt];
+          for (int v = 0; v < 4; ++v) dcol[v] = epi.d2t[lbase[k] + 4 * g + v];
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            if (dcol[v] >= 0 && dcol[v] < epi.ncols) {
+#pragma unroll
+              for (int nt = 0; nt < NT; ++nt) {
+                const int col = nt * 16 + i16;
+                if (col < mp) epi.logits[(int64_t)(m_base + col) * epi.ld + dcol[v]] = lbuf[k][nt][v];
+              }
+            }
+          }
+        }
+      }
+    } else {
+#pragma unroll
+      for (int k = 0; k < kLogitTiles; ++k) {
+        if (k < nbuf) {
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt) {
+            const int col = nt * 16 + i16;
+            if (col < mp)
+              *reinterpret_cast<f32x4*>(epi.logits + (int64_t)(m_base + col) * epi.ld + lbase[k] + 4 * g) =
+                  lbuf[k][nt];
+          }
         }
       }
     }
@@ -2346,7 +2373,7 @@ proj_mfma(const uint16_t* __restrict__ h, const void* __restrict__ Wv, const voi
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) acc[nt][v] = __builtin_ldexpf(acc[nt][v], -hexp[nt]) * gscale;
     }
-    if (LOGITS && vec_logits && r0 + 15 < R) {
+    if (LOGITS && (vec_logits || epi.d2t) && r0 + 15 < R) {
       // a whole tile: into the shift register (static moves, no indexing)
 #pragma unroll
       for (int k = kLogitTiles - 1; k > 0; --k) {
