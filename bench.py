@@ -437,8 +437,8 @@ def main() -> int:
                          "their keys with atomics, the last one writes the outputs) instead of the projection + "
                          "fold pair; bf16 heads; whole calls only")
     ap.add_argument("--unprepared", action="store_true",
-                    help="call the bf16 argmax through the plain binding (every tensor checked on every call) "
-                         "instead of PreparedArgmax")
+                    help="call the argmax through the plain binding (every tensor checked on every call) "
+                         "instead of the prepared calls (PreparedArgmax and its FP8 / MXFP4 / NVFP4 forms)")
     ap.add_argument("--graph", action="store_true",
                     help="capture the --steps calls of a timed region in one HIP graph and time its replays "
                          "(the calls without the host's launch cost)")
@@ -573,18 +573,27 @@ def main() -> int:
     if a.fused:
         state = L.new_state(dev)
 
-    # The bf16 argmax (and its single-launch form) goes through
-    # PreparedArgmax, as a decode loop would call it: the buffers are checked
-    # once, then each step is one C call.  One prepared step per rotated head
-    # copy and per stream (the capture stream under --graph is another).
+    # The argmax (bf16, its single-launch form, and over quantized heads)
+    # goes through the prepared calls, as a decode loop would make them: the
+    # buffers are checked once, then each step is one C call.  One prepared
+    # step per rotated head copy and per stream (the capture stream under
+    # --graph is another).
     prepared: dict = {}
+
+    def make_prepared(w, st):
+        if a.fp8:
+            return L.PreparedArgmaxFp8(h, w[0], w[1], d2t, path, out_id, out_logit, ws, st)
+        if a.mxfp4:
+            return L.PreparedArgmaxMxfp4(h, w[0], w[1], d2t, path, out_id, out_logit, ws, st)
+        if a.nvfp4:
+            return L.PreparedArgmaxNvfp4(h, w[0], w[1], w[2], d2t, path, out_id, out_logit, ws, st)
+        return L.PreparedArgmax(h, w, d2t, path, out_id, out_logit, ws, st, state=state if a.fused else None)
 
     def prepared_step(i):
         st = launch_on[0]
         steps_ = prepared.get(id(st))
         if steps_ is None:
-            steps_ = [L.PreparedArgmax(h, w, d2t, path, out_id, out_logit, ws, st, state=state if a.fused else None)
-                      for w in heads]
+            steps_ = [make_prepared(w, st) for w in heads]
             prepared[id(st)] = steps_
         steps_[i % len(steps_)]()
 
@@ -613,6 +622,8 @@ def main() -> int:
                                    lg_out, path, launch_on[0])
         elif a.indexed:
             L.draft_project_argmax_indexed(h, heads[i % len(heads)], d2t, path, out_id, out_logit, ws, launch_on[0])
+        elif (a.fp8 or a.mxfp4 or a.nvfp4) and not a.unprepared:
+            prepared_step(i)
         elif a.fp8:
             q, sc = heads[i % len(heads)]
             L.draft_project_argmax_fp8(h, q, sc, d2t, path, out_id, out_logit, ws, launch_on[0])

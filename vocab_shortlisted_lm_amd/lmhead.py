@@ -28,6 +28,7 @@ __all__ = [
     "lmhead_bench_time_argmax_indexed", "lmhead_quantize_mxfp4", "draft_project_argmax_mxfp4",
     "lmhead_bench_time_argmax_mxfp4", "lmhead_mxfp4_scale_bytes", "lmhead_mxfp4_tile_scales",
     "mxfp4_scale_shape", "draft_project_topk_fp8", "draft_project_topk_mxfp4", "PreparedArgmax",
+    "PreparedArgmaxFp8", "PreparedArgmaxMxfp4", "PreparedArgmaxNvfp4",
     "lmhead_quantize_nvfp4", "lmhead_nvfp4_scale_bytes", "lmhead_nvfp4_tile_scales", "nvfp4_scale_shape",
     "draft_project_argmax_nvfp4", "draft_project_topk_nvfp4", "lmhead_bench_time_argmax_nvfp4",
     "LMH_STATE_BYTES", "new_state", "draft_project_argmax_fused", "draft_project_argmax_fused_path",
@@ -317,6 +318,72 @@ class PreparedArgmax:
         if code != LMH_OK:
             raise LmheadError(code, "draft_project_argmax")
         return self.out_id, self.out_logit
+
+
+class _PreparedQuant:
+    """One argmax C call over a quantized head, its arguments checked and
+    fixed at construction (the contract of PreparedArgmax: the tensors keep
+    their storage while it is used; calling it queues the step and returns
+    (out_id, out_logit))."""
+
+    def __init__(self, fn, name, args, keep, out_id, out_logit):
+        self._fn, self._name, self._args, self._keep = fn, name, args, keep
+        self.out_id, self.out_logit = out_id, out_logit
+
+    def __call__(self):
+        code = self._fn(*self._args)
+        if code != LMH_OK:
+            raise LmheadError(code, self._name)
+        return self.out_id, self.out_logit
+
+
+class PreparedArgmaxFp8(_PreparedQuant):
+    """draft_project_argmax_fp8 with its tensors checked once."""
+
+    def __init__(self, h: torch.Tensor, Wq: torch.Tensor, scale: torch.Tensor, d2t: torch.Tensor | None = None,
+                 path: int = LMH_PATH_AUTO, out_id: torch.Tensor | None = None,
+                 out_logit: torch.Tensor | None = None, workspace: torch.Tensor | None = None, stream=None):
+        m, k, r = _check_fp8_head(h, Wq, scale, d2t)
+        out_id, out_logit = _outputs(m, out_id, out_logit, h.device)
+        st = _stream(stream, h.device)
+        ws = _workspace(workspace, h.device, st)
+        super().__init__(lib().draft_project_argmax_fp8, "draft_project_argmax_fp8",
+                         (h.data_ptr(), m, k, Wq.data_ptr(), scale.data_ptr(), r,
+                          d2t.data_ptr() if d2t is not None else None, out_id.data_ptr(), out_logit.data_ptr(),
+                          ws.data_ptr(), _nbytes(ws), path, st), (h, Wq, scale, d2t, ws), out_id, out_logit)
+
+
+class PreparedArgmaxMxfp4(_PreparedQuant):
+    """draft_project_argmax_mxfp4 with its tensors checked once."""
+
+    def __init__(self, h: torch.Tensor, Wq: torch.Tensor, scales: torch.Tensor, d2t: torch.Tensor | None = None,
+                 path: int = LMH_PATH_AUTO, out_id: torch.Tensor | None = None,
+                 out_logit: torch.Tensor | None = None, workspace: torch.Tensor | None = None, stream=None):
+        m, k, r = _check_mx4_head(h, Wq, scales, d2t)
+        out_id, out_logit = _outputs(m, out_id, out_logit, h.device)
+        st = _stream(stream, h.device)
+        ws = _workspace(workspace, h.device, st)
+        super().__init__(lib().draft_project_argmax_mxfp4, "draft_project_argmax_mxfp4",
+                         (h.data_ptr(), m, k, Wq.data_ptr(), scales.data_ptr(), r,
+                          d2t.data_ptr() if d2t is not None else None, out_id.data_ptr(), out_logit.data_ptr(),
+                          ws.data_ptr(), _nbytes(ws), path, st), (h, Wq, scales, d2t, ws), out_id, out_logit)
+
+
+class PreparedArgmaxNvfp4(_PreparedQuant):
+    """draft_project_argmax_nvfp4 with its tensors checked once."""
+
+    def __init__(self, h: torch.Tensor, Wq: torch.Tensor, scales: torch.Tensor, gscale: torch.Tensor,
+                 d2t: torch.Tensor | None = None, path: int = LMH_PATH_AUTO, out_id: torch.Tensor | None = None,
+                 out_logit: torch.Tensor | None = None, workspace: torch.Tensor | None = None, stream=None):
+        m, k, r = _check_nv4_head(h, Wq, scales, gscale, d2t)
+        out_id, out_logit = _outputs(m, out_id, out_logit, h.device)
+        st = _stream(stream, h.device)
+        ws = _workspace(workspace, h.device, st)
+        super().__init__(lib().draft_project_argmax_nvfp4, "draft_project_argmax_nvfp4",
+                         (h.data_ptr(), m, k, Wq.data_ptr(), scales.data_ptr(), gscale.data_ptr(), r,
+                          d2t.data_ptr() if d2t is not None else None, out_id.data_ptr(), out_logit.data_ptr(),
+                          ws.data_ptr(), _nbytes(ws), path, st), (h, Wq, scales, gscale, d2t, ws),
+                         out_id, out_logit)
 
 
 def draft_project_argmax(h, W, d2t=None, out_id=None, out_logit=None, workspace=None,
