@@ -2224,20 +2224,29 @@ proj_mfma(const uint16_t* __restrict__ h, const void* __restrict__ Wv, const voi
       (void)sbuf;
     }
   };
-  // A operand of k-step sb of the staged batch: 8 elements of row i16
-  auto a_operand = [&](int sb) __attribute__((always_inline)) -> u32x4 {
+  // NV4: the lane's 8 codes of k-step sb (elements 8 g .. 8 g + 7) share
+  // the block scale of block 2 sb + g / 2, byte 2 sb + g / 2 of row i16's
+  // 32 scale bytes.  nv4_scales gathers that byte for 4 k-steps at once with
+  // one byte permute (selector bytes g / 2, 2 + g / 2, 4 + g / 2, 6 + g / 2
+  // over the 8 bytes of k-steps c0 .. c0 + 3) and decodes them to f16 with
+  // two gfx950 E4M3 conversions (scale 1: exact, every E4M3 value is a
+  // normal f16 number).
+  const uint32_t nv_sel = 0x06040200u + (uint32_t)(g >> 1) * 0x01010101u;
+  auto nv4_scales = [&](int c0, f16x2& lo, f16x2& hi) __attribute__((always_inline)) {
+    const uint2 w = reinterpret_cast<const uint2*>(sstage)[i16 * 4 + (c0 >> 2)];
+    const uint32_t s4 = __builtin_amdgcn_perm(w.y, w.x, nv_sel);
+    lo = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(s4, 1.0f, false);
+    hi = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(s4, 1.0f, true);
+  };
+  // A operand of k-step sb of the staged batch: 8 elements of row i16 (NV4:
+  // times the block scale `nsc` from nv4_scales)
+  auto a_operand = [&](int sb, _Float16 nsc = (_Float16)0) __attribute__((always_inline)) -> u32x4 {
     if constexpr (FP8) {
       const uint2 raw = reinterpret_cast<const uint2*>(stage)[(i16 * SC + 2 * sb) * 2 + g];
       return fp8x8_to_bf16x8(raw.x, raw.y);
     } else if constexpr (NV4) {
-      // the lane's 8 codes (elements 8 g .. 8 g + 7 of the k-step) share the
-      // block scale of block 2 sb + g / 2: both of the k-step's scale codes
-      // are read as one 16-bit word and decoded to f16 by the gfx950 E4M3
-      // conversion (scale 1: exact, every E4M3 value is a normal f16 number)
       const uint32_t codes = reinterpret_cast<const uint32_t*>(stage)[(i16 * SC + sb) * 4 + g];
-      const uint32_t pair = reinterpret_cast<const uint16_t*>(sstage)[i16 * 16 + sb];
-      const f16x2 sc2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(pair, 1.0f, false);
-      return fp4x8_times_scale_to_f16x8(codes, (g >> 1) ? sc2[1] : sc2[0]);
+      return fp4x8_times_scale_to_f16x8(codes, nsc);
     } else if constexpr (MX4) {
       const uint32_t codes = reinterpret_cast<const uint32_t*>(stage)[(i16 * SC + sb) * 4 + g];
       const uint32_t e = reinterpret_cast<const uint8_t*>(sstage)[i16 * 16 + sb];
@@ -2278,12 +2287,22 @@ proj_mfma(const uint16_t* __restrict__ h, const void* __restrict__ Wv, const voi
 #pragma unroll
       for (int c0 = 0; c0 < SB; c0 += CH) {
         u32x4 a[CH];
+        if constexpr (NV4) {
+          static_assert(CH == 4, "NV4: one scale gather per 4 k-steps");
+          f16x2 lo, hi;
+          nv4_scales(c0, lo, hi);
+          a[0] = a_operand(c0, lo[0]);
+          a[1] = a_operand(c0 + 1, lo[1]);
+          a[2] = a_operand(c0 + 2, hi[0]);
+          a[3] = a_operand(c0 + 3, hi[1]);
+        } else {
 #pragma unroll
-        for (int sb = 0; sb < CH; ++sb) a[sb] = a_operand(c0 + sb);
+          for (int sb = 0; sb < CH; ++sb) a[sb] = a_operand(c0 + sb);
+        }
 #pragma unroll
         for (int sb = 0; sb < CH; ++sb) mma_step(a[sb], b * SB + c0 + sb);
       }
-    } else {
+    } else if constexpr (!MX4) {
 #pragma unroll
       for (int sb = 0; sb < SB; ++sb) {
         const int s = b * SB + sb;
