@@ -261,9 +261,12 @@ __device__ __forceinline__ u32x4 fp4x8_times_scale_to_f16x8(uint32_t packed, _Fl
 }
 
 // The same with the MXFP4 block scale 2^(e - 127), e the block's E8M0
-// code (code 0 is 2^-127, an fp32 subnormal).
+// code, placed in the exponent field of the scale operand.  The conversion
+// reads only that field, as an E8M0 exponent: code 0 stands for 2^-127
+// there too (blocks at that scale take part in the projection parity tests
+// at full weight), so no case needs the fp32 subnormal 2^-127.
 __device__ __forceinline__ u32x4 fp4x8_to_bf16x8(uint32_t packed, uint32_t e) {
-  return fp4x8_to_bf16x8_scaled(packed, __builtin_bit_cast(float, e != 0u ? e << 23 : 0x00400000u));
+  return fp4x8_to_bf16x8_scaled(packed, __builtin_bit_cast(float, e << 23));
 }
 
 // Value of an OCP E4M3 code (the low byte of `code`) as fp32, exactly, from
